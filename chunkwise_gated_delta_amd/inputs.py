@@ -1,0 +1,190 @@
+"""Seeded synthetic inputs for the gated delta-rule forward pass.
+
+This module only draws random numbers and shapes them; it holds none of the
+method's arithmetic, so both the CPU oracle tests and the GPU tests can use it.
+
+Five workloads are defined, each a sampled stand-in for the shapes and value
+ranges used to study the method (the pages report no dataset for this path):
+
+1. ``deltanet_f32``  DeltaNet, no gate, fp32:   B=1  H=2  T=256   dk=dv=64
+2. ``gdn``           Gated DeltaNet, head gate:  B=4  H=16 T=4096  dk=dv=128
+3. ``kda``           KDA, per-channel gate:      B=2  H=32 T=8192  dk=dv=128
+4. ``dplr``          gated DPLR, distinct a, b:  B=1  H=16 T=16384 dk=dv=128
+5. ``kda_varlen``    KDA, 8 packed sequences:    32768 tokens, H=32, dk=dv=128
+
+Draw order (fixed, so every consumer sees the same bytes): [lengths], q, k, v,
+beta, log_alpha, [a_raw, b_noise], [S0].  All draws are float32; q and k (and a,
+b) are L2-normalised over the head dimension in float32, then rounded to the
+input dtype (bf16 by round-to-nearest-even) where the workload says so.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+GATE_NONE, GATE_HEAD, GATE_CHANNEL = 0, 1, 2
+
+
+@dataclasses.dataclass
+class Problem:
+    """One forward-pass problem. Tensors are CPU torch tensors.
+
+    Layout: q, k, a, b ``[B, T, H, dk]``; v ``[B, T, H, dv]``;
+    log_alpha ``[B, T, H]`` (head gate) or ``[B, T, H, dk]`` (channel gate) fp32;
+    beta ``[B, T, H]`` fp32; S0 ``[N, H, dv, dk]`` fp32 where N is B, or the number
+    of packed sequences when ``cu_seqlens`` is given (then B == 1).
+    """
+
+    name: str
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    beta: torch.Tensor
+    log_alpha: Optional[torch.Tensor]
+    a: Optional[torch.Tensor]
+    b: Optional[torch.Tensor]
+    S0: Optional[torch.Tensor]
+    cu_seqlens: Optional[torch.Tensor]
+    gate: int
+    chunk: int = 64
+
+    @property
+    def B(self):
+        return self.q.shape[0]
+
+    @property
+    def T(self):
+        return self.q.shape[1]
+
+    @property
+    def H(self):
+        return self.q.shape[2]
+
+    @property
+    def dk(self):
+        return self.q.shape[3]
+
+    @property
+    def dv(self):
+        return self.v.shape[3]
+
+    @property
+    def n_seq(self):
+        return self.B if self.cu_seqlens is None else self.cu_seqlens.numel() - 1
+
+    @property
+    def dtype(self):
+        return self.q.dtype
+
+    def tokens(self):
+        return self.B * self.T
+
+    def seq_bounds(self):
+        """(start, end) token offsets into the flattened [B*T] token axis."""
+        if self.cu_seqlens is None:
+            return [(i * self.T, (i + 1) * self.T) for i in range(self.B)]
+        cu = self.cu_seqlens.tolist()
+        return [(cu[i], cu[i + 1]) for i in range(len(cu) - 1)]
+
+
+def _l2n(x: np.ndarray) -> np.ndarray:
+    n = np.sqrt(np.sum(x.astype(np.float32) ** 2, axis=-1, keepdims=True, dtype=np.float32))
+    return (x / n).astype(np.float32)
+
+
+def _cast(x: np.ndarray, dtype) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dtype)
+
+
+def dirichlet_lengths(rng: np.random.Generator, n_seq: int, total: int, min_len: int) -> np.ndarray:
+    """Split ``total`` tokens into ``n_seq`` lengths, each >= ``min_len``.
+
+    p ~ Dirichlet(1); L_i = min_len + floor(p_i * (total - n_seq*min_len)); the
+    remaining tokens go one each to the largest fractional parts (ties to the
+    lower index), so the lengths sum to ``total`` exactly.
+    """
+    p = rng.dirichlet(np.ones(n_seq))
+    spare = total - n_seq * min_len
+    assert spare >= 0
+    raw = p * spare
+    base = np.floor(raw).astype(np.int64)
+    rem = int(spare - base.sum())
+    frac = raw - base
+    order = sorted(range(n_seq), key=lambda i: (-frac[i], i))
+    for i in order[:rem]:
+        base[i] += 1
+    return (base + min_len).astype(np.int64)
+
+
+def make_problem(kind: str, *, seed: Optional[int] = None, B=None, H=None, T=None, dk=None,
+                 dv=None, n_seq=None, total=None, min_len=None, dtype=None,
+                 s0_scale=None, chunk: int = 64) -> Problem:
+    """Build a seeded problem of workload ``kind`` (see module doc).
+
+    Keyword overrides shrink or reshape a workload while keeping its value
+    distributions, so small parity cases and the full-size workloads share one
+    recipe.
+    """
+    spec = dict(WORKLOADS[kind])
+    spec.update({k: v for k, v in dict(B=B, H=H, T=T, dk=dk, dv=dv, n_seq=n_seq, total=total,
+                                        min_len=min_len, dtype=dtype, s0_scale=s0_scale).items()
+                 if v is not None})
+    if seed is None:
+        seed = spec["seed"]
+    rng = np.random.default_rng(seed)
+    dt = spec["dtype"]
+    H_, dk_, dv_ = spec["H"], spec["dk"], spec["dv"]
+    cu = None
+    if spec.get("varlen"):
+        lens = dirichlet_lengths(rng, spec["n_seq"], spec["total"], spec["min_len"])
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        B_, T_ = 1, int(spec["total"])
+    else:
+        B_, T_ = spec["B"], spec["T"]
+    shp = (B_, T_, H_)
+    q = _l2n(rng.standard_normal(shp + (dk_,), dtype=np.float32))
+    k = _l2n(rng.standard_normal(shp + (dk_,), dtype=np.float32))
+    v = rng.standard_normal(shp + (dv_,), dtype=np.float32)
+    beta = rng.random(shp, dtype=np.float32)
+    gate = spec["gate"]
+    log_alpha = None
+    if gate == GATE_HEAD:
+        log_alpha = rng.uniform(*spec["la_range"], size=shp).astype(np.float32)
+    elif gate == GATE_CHANNEL:
+        log_alpha = rng.uniform(*spec["la_range"], size=shp + (dk_,)).astype(np.float32)
+    a = b = None
+    if spec.get("dplr"):
+        a32 = _l2n(rng.standard_normal(shp + (dk_,), dtype=np.float32))
+        noise = rng.standard_normal(shp + (dk_,), dtype=np.float32)
+        b32 = (beta[..., None] * _l2n(a32 + np.float32(0.1) * noise)).astype(np.float32)
+        a, b = _cast(a32, dt), _cast(b32, dt)
+    S0 = None
+    if spec.get("s0_scale"):
+        n = len(cu) - 1 if cu is not None else B_
+        S0 = torch.from_numpy(
+            (np.float32(spec["s0_scale"]) * rng.standard_normal((n, H_, dv_, dk_), dtype=np.float32)))
+    return Problem(
+        name=kind, q=_cast(q, dt), k=_cast(k, dt), v=_cast(v, dt), beta=torch.from_numpy(beta),
+        log_alpha=None if log_alpha is None else torch.from_numpy(log_alpha), a=a, b=b, S0=S0,
+        cu_seqlens=None if cu is None else torch.from_numpy(cu), gate=gate, chunk=chunk)
+
+
+WORKLOADS = {
+    "deltanet_f32": dict(seed=1, B=1, H=2, T=256, dk=64, dv=64, dtype=torch.float32,
+                         gate=GATE_NONE),
+    "gdn": dict(seed=2, B=4, H=16, T=4096, dk=128, dv=128, dtype=torch.bfloat16,
+                gate=GATE_HEAD, la_range=(-0.1, -0.001)),
+    "kda": dict(seed=3, B=2, H=32, T=8192, dk=128, dv=128, dtype=torch.bfloat16,
+                gate=GATE_CHANNEL, la_range=(-0.2, -0.001)),
+    "dplr": dict(seed=4, B=1, H=16, T=16384, dk=128, dv=128, dtype=torch.bfloat16,
+                 gate=GATE_CHANNEL, la_range=(-0.1, -0.001), dplr=True),
+    "kda_varlen": dict(seed=5, varlen=True, n_seq=8, total=32768, min_len=256, H=32, dk=128,
+                       dv=128, dtype=torch.bfloat16, gate=GATE_CHANNEL, la_range=(-0.2, -0.001),
+                       s0_scale=0.1),
+}
+
+# The tolerance on max|X - X_ref| / max|X_ref| for O and for the final state.
+TOLERANCE = {torch.float32: 1e-4, torch.bfloat16: 1e-2}

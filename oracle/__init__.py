@@ -1,0 +1,113 @@
+"""CPU oracle for the gated delta-rule forward pass.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only users.  Nothing here is imported by, or imports,
+the GPU library; inputs arrive as plain numpy arrays.
+
+* ``recurrence``        -- the definition: fp64 token-by-token recurrence (C, OpenMP),
+                           built from ``gdr_ref.c``.
+* ``spectral_norm_rank1`` -- closed form of ||I - eta k j^T||_2 for unit k, j
+                           ("How to make GDN2 more stable", eq. 4).
+* ``chunk_mirror``      -- the chunk-form algebra of the pages in fp64 numpy, used to
+                           pin the chunk rewrite against the definition.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        path = os.path.join(_HERE, "libgdr_ref.so")
+        if not os.path.exists(path):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        lib.gdr_ref_fwd.restype = I
+        lib.gdr_ref_fwd.argtypes = [P, P, P, P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, P, I, I]
+        lib.gdr_ref_max_threads.restype = I
+        lib.gdr_ref_max_threads.argtypes = []
+        _LIB = lib
+    return _LIB
+
+
+def max_threads() -> int:
+    return int(_lib().gdr_ref_max_threads())
+
+
+def _f64(x):
+    if x is None:
+        return None
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def recurrence(q, k, v, beta, log_alpha=None, a=None, b=None, S0=None, cu_seqlens=None,
+               chains=None, n_threads: int = 0, want_state: bool = True):
+    """Run the fp64 recurrence.
+
+    q, k, a, b: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H];
+    log_alpha: None (no gate), [B, T, H] (head gate) or [B, T, H, dk] (channel gate);
+    S0: None or [N, H, dv, dk]; cu_seqlens: None or int [N+1] (then B == 1).
+    chains: None (all) or a list of (sequence, head) pairs to compute; the other
+    entries of O and S_final are left as NaN.
+    Returns (O [B, T, H, dv], S_final [N, H, dv, dk] or None), float64.
+    """
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    a, b, log_alpha, S0 = _f64(a), _f64(b), _f64(log_alpha), _f64(S0)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape[:3] == q.shape[:3] and beta.shape == q.shape[:3]
+    if log_alpha is None:
+        gate = 0
+    elif log_alpha.ndim == 3:
+        gate = 1
+        assert log_alpha.shape == q.shape[:3]
+    else:
+        gate = 2
+        assert log_alpha.shape == q.shape
+    if a is not None:
+        assert a.shape == q.shape and b.shape == q.shape
+    cu = None
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        N = cu.size - 1
+    else:
+        N = B
+    if S0 is not None:
+        assert S0.shape == (N, H, dv, dk)
+    O = np.full((B, T, H, dv), np.nan)
+    Sf = np.full((N, H, dv, dk), np.nan) if want_state else None
+    ch = None
+    n_ch = 0
+    if chains is not None:
+        ch = np.ascontiguousarray(np.asarray(chains, dtype=np.int32).reshape(-1, 2))
+        n_ch = ch.shape[0]
+    rc = _lib().gdr_ref_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha), gate,
+                            _ptr(beta), _ptr(S0), _ptr(O), _ptr(Sf), _ptr(cu), N, B, H, T, dk,
+                            dv, _ptr(ch), n_ch, int(n_threads))
+    if rc != 0:
+        raise ValueError(f"gdr_ref_fwd rejected its arguments (code {rc})")
+    return O, Sf
+
+
+def spectral_norm_rank1(eta: float, k: np.ndarray, j: np.ndarray) -> float:
+    """||I - eta k j^T||_2 for unit vectors k, j: (eta + sqrt(eta^2 - 4 eta k.j + 4)) / 2.
+
+    "How to make GDN2 more stable", eq. 4 (proved there by reducing to the 2x2
+    block on span{k, j} and using ||B||_F^2 and |det B|, eqs. 8-12).
+    """
+    c = float(np.dot(k, j))
+    return 0.5 * (eta + np.sqrt(eta * eta - 4.0 * eta * c + 4.0))

@@ -1,0 +1,144 @@
+"""Invariants of the recurrence that pin the oracle's boundary handling (initial
+state, final state, packed sequences, head indexing), plus checks of the seeded
+input generators."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunkwise_gated_delta_amd import inputs
+from helpers import f64, oracle_of, rel_err
+
+
+def _small(kind, **kw):
+    base = dict(kda=dict(B=2, H=3, T=150, dk=16, dv=8), gdn=dict(B=2, H=2, T=130, dk=16, dv=16),
+                dplr=dict(B=1, H=2, T=140, dk=16, dv=16),
+                deltanet_f32=dict(B=1, H=2, T=90, dk=8, dv=8),
+                kda_varlen=dict(n_seq=3, total=400, min_len=40, H=2, dk=16, dv=8))[kind]
+    base.update(kw)
+    return inputs.make_problem(kind, **base)
+
+
+def _args(P):
+    return dict(q=f64(P.q), k=f64(P.k), v=f64(P.v), beta=f64(P.beta), log_alpha=f64(P.log_alpha),
+                a=f64(P.a), b=f64(P.b), S0=f64(P.S0))
+
+
+@pytest.mark.parametrize("kind", ["kda", "gdn", "dplr", "deltanet_f32"])
+@pytest.mark.parametrize("split", [1, 64, 77])
+def test_state_passing(kind, split):
+    """Running [0, s) and then [s, T) from the carried state equals one run."""
+    P = _small(kind)
+    c = _args(P)
+    O, Sf = oracle.recurrence(**c)
+    head = {k: (v[:, :split] if (v is not None and k != "S0") else v) for k, v in c.items()}
+    tail = {k: (v[:, split:] if (v is not None and k != "S0") else v) for k, v in c.items()}
+    O1, S1 = oracle.recurrence(**head)
+    tail["S0"] = S1
+    O2, S2 = oracle.recurrence(**tail)
+    np.testing.assert_allclose(np.concatenate([O1, O2], axis=1), O, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(S2, Sf, rtol=0, atol=1e-12)
+
+
+def test_varlen_equals_separate_runs():
+    P = _small("kda_varlen")
+    O, Sf = oracle_of(P)
+    c = _args(P)
+    for n, (t0, t1) in enumerate(P.seq_bounds()):
+        part = {k: (v[:, t0:t1] if (v is not None and k != "S0") else v) for k, v in c.items()}
+        part["S0"] = c["S0"][n:n + 1]
+        On, Sn = oracle.recurrence(**part)
+        np.testing.assert_allclose(On, O[:, t0:t1], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(Sn[0], Sf[n], rtol=0, atol=1e-12)
+
+
+def test_linear_in_values_and_initial_state():
+    """For fixed keys, gates and beta the map (v, S0) -> (O, S_final) is linear."""
+    P = _small("kda", B=1)
+    c = _args(P)
+    rng = np.random.default_rng(1)
+    c["S0"] = rng.standard_normal((1, P.H, P.dv, P.dk))
+    O, Sf = oracle.recurrence(**c)
+    c2 = dict(c, v=2.5 * c["v"], S0=2.5 * c["S0"])
+    O2, S2 = oracle.recurrence(**c2)
+    np.testing.assert_allclose(O2, 2.5 * O, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S2, 2.5 * Sf, rtol=1e-12, atol=1e-12)
+    v1 = rng.standard_normal(c["v"].shape)
+    Oa, _ = oracle.recurrence(**dict(c, v=c["v"] + v1))
+    Ob, _ = oracle.recurrence(**dict(c, v=v1, S0=np.zeros_like(c["S0"])))
+    np.testing.assert_allclose(Oa, O + Ob, rtol=0, atol=1e-11)
+
+
+def test_head_permutation_equivariance():
+    P = _small("dplr", H=4)
+    c = _args(P)
+    perm = np.array([2, 0, 3, 1])
+    O, Sf = oracle.recurrence(**c)
+    cp = {k: (v[:, :, perm] if (v is not None and k != "S0") else v) for k, v in c.items()}
+    Op, Sp = oracle.recurrence(**cp)
+    np.testing.assert_allclose(Op, O[:, :, perm], rtol=0, atol=0)
+    np.testing.assert_allclose(Sp, Sf[:, perm], rtol=0, atol=0)
+
+
+def test_identity_padding():
+    """Tokens with k = v = a = b = 0, beta = 0 and log alpha = 0 leave the state unchanged."""
+    P = _small("dplr")
+    c = _args(P)
+    O, Sf = oracle.recurrence(**c)
+    pad = 5
+    cp = {}
+    for k, v in c.items():
+        if v is None or k == "S0":
+            cp[k] = v
+        else:
+            z = np.zeros((v.shape[0], pad) + v.shape[2:])
+            cp[k] = np.concatenate([v, z], axis=1)
+    Op, Sp = oracle.recurrence(**cp)
+    np.testing.assert_allclose(Sp, Sf, rtol=0, atol=0)
+    np.testing.assert_allclose(Op[:, :P.T], O, rtol=0, atol=0)
+
+
+def test_chain_subset_matches_full_run():
+    P = _small("kda")
+    O, Sf = oracle_of(P)
+    chains = [(1, 2), (0, 0)]
+    Os, Ss = oracle_of(P, chains=chains)
+    for n, h in chains:
+        np.testing.assert_array_equal(Os[n, :, h], O[n, :, h])
+        np.testing.assert_array_equal(Ss[n, h], Sf[n, h])
+    assert np.isnan(Os[0, :, 1]).all()
+
+
+def test_rel_err_metric():
+    ref = np.array([1.0, -4.0, 2.0])
+    assert rel_err(ref + np.array([0.0, 0.04, 0.0]), ref) == pytest.approx(0.01)
+
+
+# ---------------------------------------------------------------------------
+# Seeded input generators.
+# ---------------------------------------------------------------------------
+def test_generators_are_deterministic_and_shaped():
+    P1 = inputs.make_problem("dplr", T=64)
+    P2 = inputs.make_problem("dplr", T=64)
+    assert torch.equal(P1.q, P2.q) and torch.equal(P1.b, P2.b)
+    assert P1.q.dtype == torch.bfloat16 and P1.log_alpha.shape == (1, 64, 16, 128)
+    nq = torch.linalg.vector_norm(P1.q.float(), dim=-1)
+    assert torch.all((nq - 1).abs() < 1e-2)
+    assert float(P1.log_alpha.max()) <= -0.001 and float(P1.log_alpha.min()) >= -0.1
+    assert float(P1.beta.min()) >= 0 and float(P1.beta.max()) < 1
+
+
+def test_dirichlet_split_full_size():
+    P = inputs.make_problem("kda_varlen", H=1, dk=8, dv=8)
+    cu = P.cu_seqlens.numpy()
+    lens = np.diff(cu)
+    assert cu[0] == 0 and cu[-1] == 32768 and len(lens) == 8
+    assert lens.min() >= 256
+    assert P.S0.shape == (8, 1, 8, 8)
+
+
+def test_workload_shapes():
+    spec = inputs.WORKLOADS
+    assert spec["kda"]["B"] * spec["kda"]["T"] == 16384
+    assert spec["gdn"]["gate"] == inputs.GATE_HEAD
+    assert spec["deltanet_f32"]["dtype"] == torch.float32
