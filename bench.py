@@ -1,0 +1,168 @@
+"""Benchmark: chunkwise KDA forward, B=2 H=32 T=8192 dk=dv=128 C=64, bf16, one MI355X.
+
+One step = one gdr_chunk_fwd call over the whole batch (all of the hot path:
+gate prefix sums, UT transform, WY factors, serial state pass and output), on
+seeded synthetic inputs already resident in HBM.  Prints one JSON line.
+
+Throughput is tokens/s (B*T / step time; a token carries all H heads).  The
+roofline entry is for the fused KDA kernel: algorithmic bytes per launch
+(read q, k, v, log alpha, beta; write O and S_final) over its mean duration
+measured with HIP events on the launch stream, against 8 TB/s.  The CPU
+baseline is the fp64 oracle timed on the host cores on the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+WORKLOAD = "kda"
+
+
+def algorithmic_counts(P):
+    """(bytes, flops) one launch must move / perform at the algorithmic minimum.
+
+    Bytes per token-head: q, k, v, O at 2*d each (bf16), log alpha 4*dk, beta 4;
+    plus S_final (and S0 if given) once per (sequence, head).
+    FLOP per token-head: 10*C*d + 6*d^2 -- five C x C x d products (K<-K->^T,
+    At K<-, At V, Q<-K->^T, A_qk V_new) and three C x d x d products (W S^T,
+    V_new^T K^, Q<- S^T), counted as full tiles.
+    """
+    th = P.B * P.T * P.H
+    d, C = P.dk, P.chunk
+    es = 2 if P.dtype.itemsize == 2 else 4
+    per_th = es * (2 * P.dk + 2 * P.dv) + 4 * P.dk + 4
+    state = P.n_seq * P.H * P.dv * P.dk * 4 * (1 + (P.S0 is not None))
+    flops = th * (10 * C * d + 6 * d * d)
+    return th * per_th + state, flops
+
+
+def time_gpu(P, steps, warmup):
+    import torch
+
+    from chunkwise_gated_delta_amd import gdr
+
+    dev = torch.device("cuda", 0)
+    to = lambda t: None if t is None else t.to(dev)
+    q, k, v, beta, la = to(P.q), to(P.k), to(P.v), to(P.beta), to(P.log_alpha)
+    S0, cu = to(P.S0), to(P.cu_seqlens)
+    out = torch.empty((P.B, P.T, P.H, P.dv), dtype=P.dtype, device=dev)
+    fin = torch.empty((P.n_seq, P.H, P.dv, P.dk), dtype=torch.float32, device=dev)
+    call = lambda: gdr.chunk_fwd(q, k, v, beta, log_alpha=la, S0=S0, cu_seqlens=cu,
+                                 chunk_size=P.chunk, out=out, final_state=fin)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = []
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        per.append((e0, e1))
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = ev0.elapsed_time(ev1)
+    launch_ms = sorted(a.elapsed_time(b) for a, b in per)
+    return total_ms / steps, launch_ms, t_wall, out, fin
+
+
+def cpu_baseline(P, n_threads):
+    import numpy as np
+    import torch
+
+    import oracle
+
+    f64 = lambda t: None if t is None else t.to(torch.float64).numpy()
+    args = dict(q=f64(P.q), k=f64(P.k), v=f64(P.v), beta=f64(P.beta),
+                log_alpha=f64(P.log_alpha), S0=f64(P.S0),
+                cu_seqlens=None if P.cu_seqlens is None else P.cu_seqlens.numpy())
+    t = time.perf_counter()
+    O, Sf = oracle.recurrence(**args, n_threads=n_threads)
+    dt = time.perf_counter() - t
+    return dt, O, Sf, args
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); each (sequence, head) "
+              "chain is independent, so N GPUs would each run this kernel on H/N heads.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from chunkwise_gated_delta_amd import inputs
+
+    P = inputs.make_problem(WORKLOAD)
+    alg_bytes, alg_flops = algorithmic_counts(P)
+    ms, launch_ms, wall, out, fin = time_gpu(P, args.steps, args.warmup)
+    kern_ms = float(np.mean(launch_ms))
+    tokens = P.B * P.T
+    achieved_gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
+    tflops = alg_flops / (kern_ms * 1e-3) / 1e12
+
+    result = {
+        "metric": "tokens/s + MFMA util % for KDA chunk fwd, T=8192 H=32 d=128, 1xMI355X",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "KDA chunkwise forward (per-channel gate), B=2 H=32 T=8192 "
+                               "dk=dv=128 C=64, bf16 q/k/v, fp32 gate/beta/state, S0=0",
+                   "global_batch": P.B, "seq_len": P.T, "heads": P.H, "dk": P.dk, "dv": P.dv,
+                   "chunk": P.chunk, "parallelism": "none (one GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kda_mfma_kernel<128, channel gate>",
+                     "kernel_ms_mean": kern_ms, "kernel_ms_p10": launch_ms[len(launch_ms) // 10],
+                     "kernel_ms_p90": launch_ms[(9 * len(launch_ms)) // 10],
+                     "alg_bytes_per_launch": alg_bytes},
+        "mfma": {"alg_flops_per_launch": alg_flops, "achieved_tflops": tflops,
+                 "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "frac": tflops / BF16_MFMA_PEAK_TFLOPS},
+    }
+    if not args.no_cpu:
+        import oracle
+
+        n_threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or oracle.max_threads()
+        dt, Oref, Sref, _ = cpu_baseline(P, n_threads)
+        Og = out.to(torch.float64).cpu().numpy()
+        Sg = fin.to(torch.float64).cpu().numpy()
+        result["cpu_baseline"] = {
+            "value": tokens / dt, "unit": "tokens/s", "cores": n_threads, "kind": "oracle",
+            "sample": f"the whole workload ({P.B * P.H} (sequence, head) chains x {P.T} tokens), "
+                      f"fp64 token recurrence, {dt:.2f} s"}
+        result["parity"] = {
+            "O_rel_err": float(np.max(np.abs(Og - Oref)) / np.max(np.abs(Oref))),
+            "S_final_rel_err": float(np.max(np.abs(Sg - Sref)) / np.max(np.abs(Sref))),
+            "tol": 1e-2}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+// Host side of libgdr: argument validation, workspace sizing and kernel choice
+// behind the C ABI declared in include/gdr.h.
+#include "../../include/gdr.h"
+#include "gdr_common.h"
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+namespace {
+
+using gdr::FwdArgs;
+
+bool trace_enabled() {
+    static const int on = [] {
+        const char *s = std::getenv("GDR_TRACE");
+        return (s && s[0] == '1') ? 1 : 0;
+    }();
+    return on != 0;
+}
+
+size_t elem_size(int dtype) { return dtype == GDR_F32 ? 4 : 2; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const void *p, size_t bytes) {
+    const uintptr_t a = (uintptr_t)p;
+    return Range{a, a + bytes};
+}
+
+bool overlaps(Range a, Range b) { return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+bool shape_ok(int B, int H, int T, int dk, int dv, int n_seq, bool varlen) {
+    if (B < 1 || H < 1 || T < 1) return false;
+    if (varlen && (B != 1 || n_seq < 1)) return false;
+    const long long tokens = (long long)B * T;
+    if (tokens * H * (long long)(dk > dv ? dk : dv) >= (1LL << 40)) return false;
+    if (dk < 1 || dv < 1) return false;
+    return true;
+}
+
+int supported(int dtype, int dk, int dv, int C, bool has_ab) {
+    if (dtype != GDR_F32 && dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
+    if (dk != 64 && dk != 128) return GDR_ERR_UNSUPPORTED;
+    if (dv % 32 != 0 || dv > 256) return GDR_ERR_UNSUPPORTED;
+    if (dtype == GDR_BF16 && !has_ab) return C == 64 ? GDR_OK : GDR_ERR_UNSUPPORTED;
+    return (C == 16 || C == 32 || C == 64) ? GDR_OK : GDR_ERR_UNSUPPORTED;
+}
+
+FwdArgs make_args(int B, int H, int T, int dk, int dv, int C, int n_seq, int dtype, int gate,
+                  bool has_ab) {
+    FwdArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.B = B; a.H = H; a.T = T; a.dk = dk; a.dv = dv; a.C = C; a.n_seq = n_seq;
+    a.dtype = dtype; a.gate = gate;
+    static const char dummy = 0;
+    if (has_ab) a.a = a.b = &dummy;
+    return a;
+}
+
+size_t workspace_for(const FwdArgs &a, int n_seq_eff) {
+    if (gdr::kda_mfma_supported(a)) return gdr::kWorkspaceHeader;
+    return gdr::generic_workspace_bytes(a, n_seq_eff);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdr_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int C, int n_seq, int dtype,
+                               int gate, int has_ab) {
+    const bool varlen = n_seq > 0;
+    if (!shape_ok(B, H, T, dk, dv, n_seq, varlen)) return 0;
+    if (gate < GDR_GATE_NONE || gate > GDR_GATE_CHANNEL) return 0;
+    if (supported(dtype, dk, dv, C, has_ab != 0) != GDR_OK) return 0;
+    const FwdArgs a = make_args(B, H, T, dk, dv, C, n_seq, dtype, gate, has_ab != 0);
+    return workspace_for(a, varlen ? n_seq : B);
+}
+
+int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, const void *b,
+                  const float *log_alpha, const float *beta, const float *S0, void *O,
+                  float *S_final, const int32_t *cu_seqlens, int n_seq, int B, int H, int T,
+                  int dk, int dv, int C, int dtype, int gate, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    if (!q || !k || !v || !beta || !O) return GDR_ERR_NULL;
+    if ((a == nullptr) != (b == nullptr)) return GDR_ERR_NULL;
+    if (gate < GDR_GATE_NONE || gate > GDR_GATE_CHANNEL) return GDR_ERR_SHAPE;
+    if ((gate == GDR_GATE_NONE) != (log_alpha == nullptr)) return GDR_ERR_NULL;
+    const bool varlen = cu_seqlens != nullptr;
+    if (!shape_ok(B, H, T, dk, dv, n_seq, varlen)) return GDR_ERR_SHAPE;
+    const bool has_ab = a != nullptr;
+    const int sup = supported(dtype, dk, dv, C, has_ab);
+    if (sup != GDR_OK) return sup;
+    const int N = varlen ? n_seq : B;
+
+    // Bytes of every tensor, for the alias check.
+    const size_t tokens = (size_t)B * T, es = elem_size(dtype);
+    const Range rq = range(q, tokens * H * dk * es), rk = range(k, tokens * H * dk * es);
+    const Range rv = range(v, tokens * H * dv * es);
+    const Range ra = range(a, has_ab ? tokens * H * dk * es : 0);
+    const Range rb = range(b, has_ab ? tokens * H * dk * es : 0);
+    const size_t la_elems = gate == GDR_GATE_CHANNEL ? tokens * H * dk : (gate == GDR_GATE_HEAD ? tokens * H : 0);
+    const Range rla = range(log_alpha, la_elems * 4), rbeta = range(beta, tokens * H * 4);
+    const size_t sbytes = (size_t)N * H * dv * dk * 4;
+    const Range rs0 = range(S0, S0 ? sbytes : 0), rO = range(O, tokens * H * dv * es);
+    const Range rsf = range(S_final, S_final ? sbytes : 0);
+    const Range rcu = range(cu_seqlens, varlen ? (size_t)(n_seq + 1) * 4 : 0);
+    const Range inputs[] = {rq, rk, rv, ra, rb, rla, rbeta, rs0, rcu};
+    for (const Range &r : inputs)
+        if (overlaps(rO, r)) return GDR_ERR_ALIAS;
+    for (const Range &r : inputs) {
+        if (&r == &inputs[7]) continue;  // S_final may be S0 exactly ...
+        if (overlaps(rsf, r)) return GDR_ERR_ALIAS;
+    }
+    if (overlaps(rsf, rO)) return GDR_ERR_ALIAS;
+    if (S0 && S_final && overlaps(rsf, rs0) && (const void *)S_final != (const void *)S0)
+        return GDR_ERR_ALIAS;  // ... but not partly overlap it
+
+    FwdArgs args = make_args(B, H, T, dk, dv, C, n_seq, dtype, gate, has_ab);
+    args.q = q; args.k = k; args.v = v; args.a = a; args.b = b;
+    args.log_alpha = log_alpha; args.beta = beta; args.S0 = S0;
+    args.O = O; args.S_final = S_final; args.cu_seqlens = cu_seqlens;
+    args.workspace = workspace; args.workspace_bytes = workspace_bytes;
+    const size_t need = workspace_for(args, N);
+    if (!workspace || workspace_bytes < need) return GDR_ERR_WORKSPACE;
+    const Range rws = range(workspace, need);
+    for (const Range &r : inputs)
+        if (overlaps(rws, r)) return GDR_ERR_ALIAS;
+    if (overlaps(rws, rO) || overlaps(rws, rsf)) return GDR_ERR_ALIAS;
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool mfma = gdr::kda_mfma_supported(args);
+    if (trace_enabled())
+        std::fprintf(stderr, "[gdr] %s B=%d H=%d T=%d N=%d dk=%d dv=%d C=%d dtype=%d gate=%d ws=%zu\n",
+                     mfma ? "kda_mfma" : "generic", B, H, T, N, dk, dv, C, dtype, gate, need);
+    const int rc = mfma ? gdr::launch_kda_mfma(args, N, s) : gdr::launch_generic(args, N, s);
+    return rc == 0 ? GDR_OK : GDR_ERR_HIP;
+}
+
+int gdr_workspace_error(void *workspace, void *stream) {
+    if (!workspace) return GDR_ERR_NULL;
+    hipStream_t s = (hipStream_t)stream;
+    if (hipStreamSynchronize(s) != hipSuccess) return GDR_ERR_HIP;
+    int flag = 0;
+    if (hipMemcpy(&flag, workspace, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return GDR_ERR_HIP;
+    if (flag != 0) {
+        const int zero = 0;
+        if (hipMemcpy(workspace, &zero, sizeof(int), hipMemcpyHostToDevice) != hipSuccess)
+            return GDR_ERR_HIP;
+    }
+    return flag;
+}
+
+const char *gdr_status_string(int status) {
+    switch (status) {
+        case GDR_OK: return "ok";
+        case GDR_ERR_NULL: return "required pointer is NULL (or only one of a, b given)";
+        case GDR_ERR_SHAPE: return "size out of range or inconsistent";
+        case GDR_ERR_UNSUPPORTED: return "unsupported dtype, head size or chunk size";
+        case GDR_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDR_ERR_ALIAS: return "output overlaps an input or the workspace";
+        case GDR_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int gdr_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Shared device helpers and launch interfaces of libgdr (internal header).
+#pragma once
+
+#include <hip/hip_bf16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef __hip_bfloat16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGateNone = 0, kGateHead = 1, kGateChannel = 2;
+
+// Bytes at the start of every workspace reserved for the device error flag.
+constexpr size_t kWorkspaceHeader = 256;
+
+__device__ __forceinline__ float ld(const float *p, size_t i) { return p[i]; }
+__device__ __forceinline__ float ld(const bf16 *p, size_t i) { return __bfloat162float(p[i]); }
+__device__ __forceinline__ void st(float *p, size_t i, float x) { p[i] = x; }
+__device__ __forceinline__ void st(bf16 *p, size_t i, float x) { p[i] = __float2bfloat16(x); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Two floats -> two bf16 (round to nearest even) packed low-first in one word.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16 l = __float2bfloat16(lo), h = __float2bfloat16(hi);
+    return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+
+// Sequence bounds [t0, t1) of sequence n on the flattened token axis.  Packed
+// offsets are clamped into [0, total] and made non-decreasing so that nothing
+// is read or written outside the buffers; a clamp raises the error flag.
+__device__ __forceinline__ void seq_bounds(const int32_t *cu, int n, int T, long total, long &t0,
+                                           long &t1, int *err_flag) {
+    if (cu == nullptr) {
+        t0 = (long)n * T;
+        t1 = t0 + T;
+        return;
+    }
+    long a = cu[n], b = cu[n + 1];
+    long ca = a < 0 ? 0 : (a > total ? total : a);
+    long cb = b < ca ? ca : (b > total ? total : b);
+    if ((ca != a || cb != b) && err_flag != nullptr) atomicOr(err_flag, 1);
+    t0 = ca;
+    t1 = cb;
+}
+
+// Workgroup id -> linear work index so that consecutive indices (the dv-tiles of
+// one (sequence, head) pair) land on the same XCD: workgroups are dispatched
+// round-robin over the 8 XCDs, so ids that are equal mod 8 share an L2.
+__device__ __forceinline__ int xcd_linear_index(int bid, int nblocks) {
+    if ((nblocks & 7) != 0) return bid;
+    return (bid & 7) * (nblocks >> 3) + (bid >> 3);
+}
+
+struct FwdArgs {
+    const void *q, *k, *v, *a, *b;
+    const float *log_alpha, *beta, *S0;
+    void *O;
+    float *S_final;
+    const int32_t *cu_seqlens;
+    int n_seq, B, H, T, dk, dv, C, dtype, gate;
+    void *workspace;
+    size_t workspace_bytes;
+};
+
+// Launchers (return a hipError_t as int).  Each enqueues on `stream`.
+size_t generic_workspace_bytes(const FwdArgs &a, int n_seq_eff);
+int launch_generic(const FwdArgs &a, int n_seq_eff, hipStream_t stream);
+bool kda_mfma_supported(const FwdArgs &a);
+int launch_kda_mfma(const FwdArgs &a, int n_seq_eff, hipStream_t stream);
+
+}  // namespace gdr

@@ -1,0 +1,124 @@
+/*
+ * gdr.h -- C ABI of libgdr.so: the chunkwise-parallel forward pass of the
+ * gated delta-rule family of linear attention on AMD MI355X (gfx950).
+ *
+ * The operation (per sequence n and head h; "Diagonal Plus Low Rank" notes,
+ * section 2, the original gated DPLR formula, with the write term scaled by
+ * beta as in eq. 1 of "How to make GDN2 more stable"):
+ *
+ *     S = S0[n,h]                                   (dv x dk, zero if S0 == NULL)
+ *     for each token t of the sequence, in order:
+ *         S    = S Diag(alpha_t) (I - b_t a_t^T) + beta_t v_t k_t^T
+ *         O[t] = S q_t
+ *     S_final[n,h] = S
+ *
+ * alpha_t = exp(log_alpha) per key channel (GDR_GATE_CHANNEL), one value per
+ * head (GDR_GATE_HEAD), or 1 (GDR_GATE_NONE).  With a == b == NULL the library
+ * uses a = k, b = beta k: this is KDA (channel gate), Gated DeltaNet (head gate)
+ * and DeltaNet (no gate) -- the special cases listed under "relation to KDA" in
+ * the same notes.  With a and b given it is gated DPLR; pass beta = 1 for the
+ * unscaled write term.
+ *
+ * The library evaluates this with the chunkwise rewrite of the pages: the UT
+ * transform and WY factors inside each chunk of C tokens ("Kimi Delta
+ * Attention backward" notes, forward recap; "DeltaNet" notes, section 4.1),
+ * the triangular inverse of section 4.2 of the DeltaNet notes, and a serial
+ * state pass across chunks.  Results equal the recurrence up to rounding.
+ *
+ * Memory: every tensor pointer is a DEVICE pointer to contiguous row-major,
+ * 16-byte aligned memory owned by the caller.  The library allocates nothing, frees nothing
+ * and keeps no pointer after a call returns.  All work is enqueued on
+ * `stream` (a hipStream_t; NULL is the default stream) and the call returns
+ * without synchronising: buffers must stay valid until that work completes.
+ * The library keeps no state; concurrent calls on different streams with
+ * disjoint outputs and workspaces are safe.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes.  Validation happens on the host before anything is enqueued,
+ * so a non-zero code means no GPU work was launched (except GDR_ERR_HIP,
+ * which reports a failed launch). */
+typedef enum {
+    GDR_OK = 0,
+    GDR_ERR_NULL = -1,        /* a required pointer is NULL, or exactly one of a/b is NULL */
+    GDR_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+    GDR_ERR_UNSUPPORTED = -3, /* valid, but no kernel for this dtype/shape/chunk size */
+    GDR_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than gdr_chunk_fwd_workspace() */
+    GDR_ERR_ALIAS = -5,       /* O or S_final overlaps an input it must not overwrite */
+    GDR_ERR_HIP = -6          /* a HIP runtime call failed */
+} gdr_status;
+
+/* Element type of q, k, v, a, b and O.  log_alpha, beta, S0 and S_final are
+ * always fp32. */
+typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+/* Gate layout. NONE: alpha = 1 (log_alpha must be NULL).  HEAD: log_alpha is
+ * [tokens, H].  CHANNEL: log_alpha is [tokens, H, dk]. */
+typedef enum { GDR_GATE_NONE = 0, GDR_GATE_HEAD = 1, GDR_GATE_CHANNEL = 2 } gdr_gate;
+
+/* Bytes of device workspace gdr_chunk_fwd needs for these arguments (n_seq:
+ * the number of packed sequences, or 0 without cu_seqlens; has_ab: non-zero
+ * when a and b are given).  Returns 0 when the arguments are invalid
+ * or unsupported.  The first 256 bytes of a workspace hold a sticky device
+ * error flag (see gdr_workspace_error); zero-fill a workspace before its first
+ * use. */
+size_t gdr_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int C, int n_seq,
+                               int dtype, int gate, int has_ab);
+
+/* The forward pass.
+ *
+ *   q, k        [B, T, H, dk]  dtype          queries, keys
+ *   v           [B, T, H, dv]  dtype          values
+ *   a, b        [B, T, H, dk]  dtype or NULL  the rank-one factor I - b a^T
+ *                                             (both NULL: a = k, b = beta k)
+ *   log_alpha   see gdr_gate, fp32            log of the forget gate (<= 0 expected)
+ *   beta        [B, T, H]      fp32           write strength
+ *   S0          [N, H, dv, dk] fp32 or NULL   initial state per sequence (NULL: zero)
+ *   O           [B, T, H, dv]  dtype          output, o_t = S_t q_t
+ *   S_final     [N, H, dv, dk] fp32 or NULL   final state per sequence
+ *   cu_seqlens  [n_seq + 1]    int32 or NULL  packed sequences: sequence n is tokens
+ *                                             [cu[n], cu[n+1]) of the B*T token axis;
+ *                                             requires B == 1; N = n_seq.  Without it
+ *                                             N = B and sequence n is batch row n.
+ *               n_seq is ignored when cu_seqlens is NULL.
+ *   C           chunk size (tokens per chunk).  The result does not depend on it
+ *               beyond rounding.  Supported: 64 (bf16); 16, 32, 64 (fp32, with
+ *               C*dk <= 8192).
+ *   dk, dv      head sizes; dk in {64, 128}; dv a multiple of 32 up to 256.
+ *
+ * S_final may equal S0 (in-place state update).  O must not overlap any input.
+ * cu_seqlens lives in device memory and is not read on the host: malformed
+ * offsets (decreasing, or beyond B*T) are clamped on the device, so no access
+ * leaves the buffers, and raise the workspace error flag.  NaN or Inf inputs
+ * propagate; they are not checked.
+ */
+int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, const void *b,
+                  const float *log_alpha, const float *beta, const float *S0, void *O,
+                  float *S_final, const int32_t *cu_seqlens, int n_seq, int B, int H, int T,
+                  int dk, int dv, int C, int dtype, int gate, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/* Synchronises `stream`, returns the sticky device error flag of `workspace`
+ * (0: none; 1: malformed cu_seqlens were clamped) and clears it.  Returns
+ * GDR_ERR_NULL or GDR_ERR_HIP on failure. */
+int gdr_workspace_error(void *workspace, void *stream);
+
+/* Human-readable text for a gdr_status value (static storage). */
+const char *gdr_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int gdr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

@@ -1,0 +1,105 @@
+"""C-ABI contract tests that run without a GPU: the library loads, exports
+every function include/gdr.h declares, sizes workspaces, and rejects bad
+arguments on the host before anything is enqueued.
+
+Every call below that passes non-NULL pointers is one that validation rejects,
+so no kernel is ever launched with them."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunkwise_gated_delta_amd import gdr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+P = ctypes.c_void_p
+FAKE = 1 << 40  # never dereferenced: every such call fails validation first
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gdr.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = _header_functions()
+    assert set(names) == set(gdr.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gdr_version() >= 100
+    for code in range(-6, 1):
+        s = lib.gdr_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.gdr_status_string(-99).decode() == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    ws = gdr.workspace_bytes
+    # the fused KDA-family kernel needs only the error-flag header
+    assert ws(2, 32, 8192, 128, 128) == 256
+    assert ws(4, 16, 4096, 128, 128, gate=gdr.GATE_HEAD) == 256
+    # the generic fp32 / DPLR kernel needs per-workgroup scratch
+    g = ws(1, 16, 16384, 128, 128, has_ab=True)
+    assert g == 256 + 1 * 16 * 4 * 7 * 64 * 128 * 4
+    assert ws(1, 2, 256, 64, 64, dtype=__import__("torch").float32, gate=0) > 256
+    # unsupported / invalid -> 0
+    assert ws(1, 2, 256, 96, 64) == 0
+    assert ws(1, 2, 256, 128, 48) == 0
+    assert ws(1, 2, 256, 128, 128, C=32) == 0           # bf16 KDA family: C = 64 only
+    assert ws(0, 2, 256, 128, 128) == 0
+    assert ws(2, 2, 256, 128, 128, n_seq=3) == 0        # packed sequences need B == 1
+
+
+def _call(lib, q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), a=None, b=None,
+          la=FAKE + (3 << 30), beta=FAKE + (4 << 30), S0=None, O=FAKE + (5 << 30),
+          Sf=FAKE + (6 << 30), cu=None, n_seq=0, B=1, H=2, T=64, dk=128, dv=128, C=64,
+          dtype=1, gate=2, ws=FAKE + (7 << 30), ws_bytes=256):
+    return lib.gdr_chunk_fwd(P(q), P(k), P(v), P(a), P(b), P(la), P(beta), P(S0), P(O), P(Sf),
+                             P(cu), n_seq, B, H, T, dk, dv, C, dtype, gate, P(ws), ws_bytes, None)
+
+
+def test_null_pointers_rejected(lib):
+    assert _call(lib, q=None) == -1
+    assert _call(lib, O=None) == -1
+    assert _call(lib, beta=None) == -1
+    assert _call(lib, a=FAKE + (9 << 30)) == -1           # only one of a, b
+    assert _call(lib, la=None, gate=2) == -1              # gate without log_alpha
+    assert _call(lib, gate=0) == -1                       # log_alpha without a gate
+
+
+def test_bad_shapes_rejected(lib):
+    assert _call(lib, T=0) == -2
+    assert _call(lib, B=0) == -2
+    assert _call(lib, gate=3) == -2
+    assert _call(lib, cu=FAKE + (8 << 30), n_seq=2, B=2) == -2
+    assert _call(lib, cu=FAKE + (8 << 30), n_seq=0) == -2
+
+
+def test_unsupported_rejected(lib):
+    assert _call(lib, dk=96) == -3
+    assert _call(lib, dv=40) == -3
+    assert _call(lib, C=32) == -3
+    assert _call(lib, dtype=5) == -3
+
+
+def test_workspace_checked(lib):
+    assert _call(lib, ws=None) == -4
+    assert _call(lib, ws_bytes=100) == -4
+
+
+def test_aliasing_rejected(lib):
+    assert _call(lib, O=FAKE) == -5                       # O on top of q
+    assert _call(lib, Sf=FAKE + (2 << 30)) == -5          # S_final on top of v
+    assert _call(lib, S0=FAKE + (10 << 30), Sf=FAKE + (10 << 30) + 64) == -5  # partial overlap
+    assert _call(lib, ws=FAKE + (5 << 30)) == -5          # workspace on top of O

@@ -1,0 +1,184 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bar: max|X - X_ref| / max|X_ref| <= 1e-4 for fp32 inputs and <= 1e-2 for bf16
+inputs, separately for O and S_final.  Small cases compare every element and
+span several chunks plus a ragged tail; the full-size workloads run exactly
+as the benchmark launches them and are compared on sampled (sequence, head)
+chains, which the oracle computes independently of the others.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from chunkwise_gated_delta_amd import gdr, inputs
+from helpers import compare, gpu_run
+
+pytestmark = pytest.mark.gpu
+
+TOL = inputs.TOLERANCE
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-case] {request.node.nodeid}", file=sys.__stderr__, flush=True)
+    yield
+
+
+def _check(P, O, Sf, chains=None, tol=None):
+    tol = TOL[P.dtype] if tol is None else tol
+    eo, es = compare(P, O, Sf, chains=chains)
+    print(f"[gpu-case] rel err O {eo:.3e} S_final {es if es is None else f'{es:.3e}'} tol {tol}",
+          file=sys.__stderr__, flush=True)
+    assert np.isfinite(O).all()
+    assert eo <= tol, f"O rel err {eo:.3e} > {tol}"
+    if Sf is not None:
+        assert es <= tol, f"S_final rel err {es:.3e} > {tol}"
+    return eo, es
+
+
+SMALL = {
+    "deltanet_f32": dict(),  # the full workload is already small
+    "gdn": dict(B=2, H=3, T=333),
+    "kda": dict(B=2, H=3, T=333),
+    "dplr": dict(B=1, H=2, T=300),
+    "kda_varlen": dict(n_seq=4, total=700, min_len=40, H=3),
+}
+
+
+@pytest.mark.parametrize("kind", list(SMALL))
+def test_small_full_compare(kind):
+    P = inputs.make_problem(kind, **SMALL[kind])
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+
+
+FULL_CHAINS = {
+    "gdn": [(0, 0), (3, 15), (1, 7)],
+    "kda": [(0, 0), (1, 31), (0, 17)],
+    "dplr": [(0, 0), (0, 11)],
+    "kda_varlen": None,  # filled in: shortest and longest sequence
+}
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda", "dplr", "kda_varlen"])
+def test_full_size_sampled(kind):
+    P = inputs.make_problem(kind)
+    chains = FULL_CHAINS[kind]
+    if chains is None:
+        lens = np.diff(P.cu_seqlens.numpy())
+        chains = [(int(np.argmin(lens)), 0), (int(np.argmax(lens)), 31), (3, 9)]
+    # NaN canary: every output element must be written.
+    out = torch.full((P.B, P.T, P.H, P.dv), float("nan"), dtype=P.dtype, device="cuda")
+    O, Sf = gpu_run(P, out=out)
+    assert np.isfinite(O).all() and np.isfinite(Sf).all()
+    _check(P, O, Sf, chains=chains)
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [1, 17, 64, 65, 128, 191])
+def test_ragged_lengths_kda(T):
+    P = inputs.make_problem("kda", B=2, H=2, T=T)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+
+
+@pytest.mark.parametrize("gate", [0, 1, 2])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 256), (64, 32)])
+def test_head_sizes_and_gates_bf16(gate, dk, dv):
+    kind = {0: "deltanet_f32", 1: "gdn", 2: "kda"}[gate]
+    P = inputs.make_problem(kind, B=1, H=2, T=150, dk=dk, dv=dv, dtype=torch.bfloat16)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+
+
+@pytest.mark.parametrize("kind", ["deltanet_f32", "gdn", "kda", "dplr"])
+@pytest.mark.parametrize("C", [16, 32, 64])
+def test_fp32_all_modes_and_chunks(kind, C):
+    P = inputs.make_problem(kind, B=1, H=2, T=150, dk=64, dv=64, dtype=torch.float32, chunk=C)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf, tol=TOL[torch.float32])
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+def test_dplr_bf16_chunks(C):
+    P = inputs.make_problem("dplr", B=1, H=2, T=200, chunk=C)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+
+
+def test_nonzero_initial_state_and_inplace_final_state():
+    P = inputs.make_problem("kda", B=2, H=2, T=130, s0_scale=0.3)
+    assert P.S0 is not None
+    dev = "cuda"
+    S = P.S0.to(dev).clone()
+    to = lambda t: None if t is None else t.to(dev)
+    O, Sf = gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), log_alpha=to(P.log_alpha),
+                          S0=S, final_state=S)
+    torch.cuda.synchronize()
+    assert Sf.data_ptr() == S.data_ptr()
+    _check(P, O.double().cpu().numpy(), Sf.double().cpu().numpy())
+
+
+def test_no_final_state():
+    P = inputs.make_problem("gdn", B=1, H=2, T=100)
+    O, Sf = gpu_run(P, output_final_state=False)
+    assert Sf is None
+    _check(P, O, None)
+
+
+def test_varlen_with_empty_and_short_sequences():
+    P = inputs.make_problem("kda_varlen", n_seq=3, total=300, min_len=20, H=2)
+    cu = torch.tensor([0, 10, 10, 75, 300], dtype=torch.int32)
+    P.cu_seqlens = cu
+    P.S0 = torch.randn(4, 2, P.dv, P.dk, generator=torch.Generator().manual_seed(0)) * 0.1
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+    # the empty sequence returns its initial state unchanged
+    np.testing.assert_array_equal(Sf[1], P.S0[1].double().numpy())
+
+
+def test_state_passing_on_gpu():
+    """Splitting a sequence and carrying S_final into S0 equals one call."""
+    P = inputs.make_problem("kda", B=1, H=2, T=256)
+    O, Sf = gpu_run(P)
+    cut = 128
+    P1 = inputs.make_problem("kda", B=1, H=2, T=256)
+    for name in ("q", "k", "v", "beta", "log_alpha"):
+        setattr(P1, name, getattr(P, name)[:, :cut].contiguous())
+    O1, S1 = gpu_run(P1)
+    P2 = inputs.make_problem("kda", B=1, H=2, T=256)
+    for name in ("q", "k", "v", "beta", "log_alpha"):
+        setattr(P2, name, getattr(P, name)[:, cut:].contiguous())
+    P2.S0 = torch.from_numpy(S1).float()
+    O2, S2 = gpu_run(P2)
+    assert np.max(np.abs(np.concatenate([O1, O2], axis=1) - O)) <= 1e-2 * np.max(np.abs(O))
+    assert np.max(np.abs(S2 - Sf)) <= 1e-2 * np.max(np.abs(Sf))
+
+
+def test_deterministic():
+    P = inputs.make_problem("kda", B=1, H=4, T=300)
+    O1, S1 = gpu_run(P)
+    O2, S2 = gpu_run(P)
+    np.testing.assert_array_equal(O1, O2)
+    np.testing.assert_array_equal(S1, S2)
+
+
+def test_malformed_cu_seqlens_clamped_and_flagged():
+    P = inputs.make_problem("kda_varlen", n_seq=3, total=300, min_len=20, H=2)
+    P.cu_seqlens = torch.tensor([0, 100, 50, 5000], dtype=torch.int32)
+    P.S0 = None
+    gdr.check_workspace_error()  # clear anything left from earlier calls
+    O, Sf = gpu_run(P)
+    assert np.isfinite(O[:, :300]).all()
+    assert gdr.check_workspace_error() == 1
+    assert gdr.check_workspace_error() == 0
+
+
+def test_rejects_cpu_tensors():
+    P = inputs.make_problem("kda", B=1, H=1, T=10)
+    with pytest.raises(RuntimeError):
+        gdr.chunk_fwd(P.q, P.k, P.v, P.beta, log_alpha=P.log_alpha)
