@@ -29,6 +29,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
 }
 
+// Workgroup barrier that orders LDS traffic only.  __syncthreads() also waits for
+// every outstanding global load and store, which would stall on loads issued
+// early on purpose (prefetch of the next chunk).  Every barrier in the kernels
+// here exists to hand LDS data between waves, so waiting on the LDS counter
+// (lgkmcnt = 0, vmcnt and expcnt left at their maxima) before s_barrier is
+// enough; the empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Sequence bounds [t0, t1) of sequence n on the flattened token axis.  Packed
 // offsets are clamped into [0, total] and made non-decreasing so that nothing
 // is read or written outside the buffers; a clamp raises the error flag.
