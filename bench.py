@@ -100,7 +100,21 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--copy-cal", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (calibrates the HBM "
+                         "traffic counters: FETCH_SIZE/WRITE_SIZE per byte actually moved)")
     args = ap.parse_args()
+    if args.copy_cal:
+        import torch
+
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": args.steps}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); each (sequence, head) "
               "chain is independent, so N GPUs would each run this kernel on H/N heads.",

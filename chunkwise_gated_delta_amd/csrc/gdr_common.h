@@ -23,10 +23,12 @@ __device__ __forceinline__ void st(bf16 *p, size_t i, float x) { p[i] = __float2
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-// Two floats -> two bf16 (round to nearest even) packed low-first in one word.
+// Two floats -> two bf16 (round to nearest even) packed low-first in one word
+// (a single v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    bf16 l = __float2bfloat16(lo), h = __float2bfloat16(hi);
-    return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Workgroup barrier that orders LDS traffic only.  __syncthreads() also waits for

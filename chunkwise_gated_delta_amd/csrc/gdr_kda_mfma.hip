@@ -7,26 +7,31 @@
 // KDA chunk form ("Kimi Delta Attention backward" notes, forward recap):
 //
 //   gate  g = in-chunk inclusive prefix sum of log alpha (per channel or head);
-//         Q<- = Q e^g, K<- = K e^g, K-> = K e^-g, K^ = K e^(g_C - g) -> LDS (bf16)
+//         Q<- = Q e^g, K<- = K e^g, K-> = K e^-g            -> LDS (bf16)
 //   gram  L = Diag(beta)(K<- K->^T, strictly lower) (fp32) and
-//         A_qk = Q<- K->^T on and below the diagonal (bf16), bf16 MFMA
+//         A_qk = Q<- K->^T on and below the diagonal (bf16)
 //   inv   At = (I + L)^-1 by 16x16 blocks ("DeltaNet" notes, section 4.2):
-//         diagonal blocks by forward substitution, then the two-block form
-//         [A11 0; A21 A22]^-1 = [A11^-1 0; -A22^-1 A21 A11^-1  A22^-1]
-//         at 32 rows and at 64 rows, with fp32 MFMA
+//         the four diagonal blocks by forward substitution (fp32), then the
+//         two-block form [A11 0; A21 A22]^-1 = [A11^-1 0; -A22^-1 A21 A11^-1  A22^-1]
+//         at 32 rows and at 64 rows, with bf16 MFMA products
 //   wy    W = At Diag(beta) K<-,  U = At Diag(beta) V
 //   state V_new = U - W S^T,  O = Q<- S^T + A_qk V_new,
-//         S = S Diag(gamma_C) + V_new^T K^
+//         S = (S + V_new^T K->) Diag(gamma_C)        (gamma_C = e^(g at the last row))
+//
+// The last line is the pages' S Diag(gamma_C) + V_new^T K-> Diag(gamma_C) with the
+// gate applied once to the fp32 accumulator.
 //
 // MFMA operand layout (v_mfma_f32_16x16x32_bf16): lane l feeds A[l%16][8(l/16)+0..7]
-// and B[8(l/16)+0..7][l%16] and receives D[4(l/16)+0..3][l%16].  Operands that
-// are contiguous along the contraction are read as 16-byte rows; operands whose
-// rows run along the contraction (a contraction over chunk rows of a row-major
-// array) are read with the LDS transpose read, so every LDS array is stored
-// row-major only.  Products are oriented so that each lane's four outputs are
-// contiguous in the array they are stored to.
+// and B[8(l/16)+0..7][l%16] and receives D[4(l/16)+0..3][l%16] (the 16x16x16 form
+// feeds 4 contraction elements per lane, A[l%16][4(l/16)+0..3]).  Operands that are
+// contiguous along the contraction are read as 16-byte rows; operands whose rows
+// run along the contraction (a contraction over chunk rows of a row-major array)
+// are read with the LDS transpose read, so every LDS operand array is row-major.
+// Products are oriented so that each lane's four outputs are contiguous where
+// they are stored.
 //
-// The inputs of chunk t+1 are loaded into registers while chunk t is computed.
+// The inputs of chunk t+1 are loaded into registers while chunk t is computed,
+// and every barrier orders LDS traffic only (see lds_barrier).
 #include "gdr_common.h"
 
 namespace gdr {
@@ -36,9 +41,10 @@ constexpr int kC = 64;        // chunk size
 constexpr int kDVT = 32;      // dv columns per workgroup
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kRPW = kC / kWaves;  // gate-stage rows per wave
 constexpr int kCS = kC + 8;   // bf16 row stride of [*][64] arrays
 constexpr int kLS = kC + 4;   // fp32 row stride of the 64x64 inverse (16-byte rows)
-constexpr int kTS = 33;       // fp32 row stride of the inverse's temporaries
+constexpr int kTS = 33;       // fp32 row stride of the 32x32 temporary
 constexpr int kVS = kDVT + 8; // bf16 row stride of the value tile
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -60,13 +66,14 @@ template <int DK>
 struct Smem {
     static constexpr int KS = DK + 8;                      // bf16 row stride of [*][DK] arrays
     static constexpr int oKl = 0;                          // K<-  [64][KS]
-    static constexpr int oKr = oKl + kC * KS * 2;          // K->  [64][KS]; W after the gram
+    static constexpr int oKr = oKl + kC * KS * 2;          // K->  [64][KS]
     static constexpr int oQl = oKr + kC * KS * 2;          // Q<-  [64][KS]
-    static constexpr int oKh = oQl + kC * KS * 2;          // K^   [64][KS]
-    static constexpr int oV = oKh + kC * KS * 2;           // V    [64][kVS]
-    static constexpr int oL = oV + kC * kVS * 2;           // fp32 [64][kLS]: totals, L, At
-    static constexpr int oT = oL + kC * kLS * 4;           // fp32 [32][kTS] temporaries
-    static constexpr int oAb = oT + 32 * kTS * 4;          // At Diag(beta) bf16 [64][kCS]
+    static constexpr int oW = oQl + kC * KS * 2;           // W    [64][KS]
+    static constexpr int oV = oW + kC * KS * 2;            // V    [64][kVS]
+    static constexpr int oL = oV + kC * kVS * 2;           // fp32 [64][kLS]: L, then At
+    static constexpr int oT = oL + kC * kLS * 4;           // fp32 [32][kTS]
+    static constexpr int oTot = oT + 32 * kTS * 4;         // fp32 [8][DK] gate partial sums
+    static constexpr int oAb = oTot + kWaves * DK * 4;     // At Diag(beta) bf16 [64][kCS]
     static constexpr int oAqk = oAb + kC * kCS * 2;        // A_qk bf16 [64][kCS]
     static constexpr int oS = oAqk + kC * kCS * 2;         // S bf16 [32][KS]
     static constexpr int oVnT = oS + kDVT * KS * 2;        // V_new^T bf16 [32][kCS]
@@ -75,13 +82,14 @@ struct Smem {
     static constexpr int oRow = oGC + DK * 4;              // fp32 [3][64] (head gate)
     static constexpr int bytes = oRow + 3 * kC * 4;
     static_assert(bytes <= 160 * 1024, "LDS budget");
-    static_assert(oKr % 16 == 0 && oQl % 16 == 0 && oKh % 16 == 0 && oV % 16 == 0 &&
-                      oL % 16 == 0 && oT % 16 == 0 && oAb % 16 == 0 && oAqk % 16 == 0 &&
-                      oS % 16 == 0 && oVnT % 16 == 0 && oBeta % 16 == 0 && oGC % 16 == 0,
+    static_assert(oKr % 16 == 0 && oQl % 16 == 0 && oW % 16 == 0 && oV % 16 == 0 &&
+                      oL % 16 == 0 && oT % 16 == 0 && oTot % 16 == 0 && oAb % 16 == 0 &&
+                      oAqk % 16 == 0 && oS % 16 == 0 && oVnT % 16 == 0 && oBeta % 16 == 0 &&
+                      oGC % 16 == 0,
                   "16-byte aligned arrays");
 };
 
-// A-operand (or B-operand) fragment whose 8 contraction elements are contiguous.
+// Fragment whose 8 contraction elements are contiguous in a row.
 __device__ __forceinline__ bf16x8 frag(const uint16_t *base, int row, int stride, int col) {
     return *(const bf16x8 *)(base + row * stride + col);
 }
@@ -103,10 +111,22 @@ __device__ __forceinline__ bf16x8 frag_tr(const uint16_t *base, int k0, int stri
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+// 32x32x16: lane l feeds A[l%32][8(l/32)+0..7] and B[8(l/32)+0..7][l%32] and receives
+// D[8q + 4(l/32) + e][l%32] in register 4q + e.
+__device__ __forceinline__ f32x16 mfma32x32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 
-// fp32 16x16x4: lane l feeds A[l%16][l/16] and B[l/16][l%16].
-__device__ __forceinline__ f32x4 mfma32(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+__device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
+    return bf16x4{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+}
+__device__ __forceinline__ bf16x8 to_bf16x8(float4 a, float4 b) {
+    return bf16x8{(__bf16)a.x, (__bf16)a.y, (__bf16)a.z, (__bf16)a.w,
+                  (__bf16)b.x, (__bf16)b.y, (__bf16)b.z, (__bf16)b.w};
 }
 
 __device__ __forceinline__ void store4(uint16_t *dst, float x0, float x1, float x2, float x3) {
@@ -122,24 +142,21 @@ template <int DK, int GATE>
 __global__ __launch_bounds__(kThreads) void kda_mfma_kernel(KdaParams p) {
     using L = Smem<DK>;
     constexpr int KS = L::KS;
-    constexpr int NCB = DK / 4;                  // 4-channel blocks in the gate stage
-    constexpr int NRB = kThreads / NCB;          // row blocks in the gate stage
-    constexpr int RPT = kC / NRB;                // rows per thread in the gate stage
-    constexpr int NST = (DK / 16) * 2 / kWaves;  // state tiles per wave
-    constexpr int NWT = (DK / 16) * 4 / kWaves;  // W tiles per wave
-    static_assert(RPT == 2 || RPT == 4, "gate-stage layout");
+    constexpr int CPL = DK / 64;                 // gate-stage channels per lane
+    constexpr int NST = (DK / 16) * 2 / kWaves;  // S^T tiles per wave
+    constexpr int NWT = (DK / 16) * 4 / kWaves;  // W^T tiles per wave
+    static_assert(CPL == 1 || CPL == 2, "gate-stage layout");
     static_assert(NST >= 1 && NWT >= 1, "tiling");
 
     __shared__ __attribute__((aligned(16))) char smem[L::bytes];
     uint16_t *sKl = (uint16_t *)(smem + L::oKl);
     uint16_t *sKr = (uint16_t *)(smem + L::oKr);
-    uint16_t *sW = sKr;  // K-> is dead once the gram is formed
     uint16_t *sQl = (uint16_t *)(smem + L::oQl);
-    uint16_t *sKh = (uint16_t *)(smem + L::oKh);
+    uint16_t *sW = (uint16_t *)(smem + L::oW);
     uint16_t *sV = (uint16_t *)(smem + L::oV);
     float *sL = (float *)(smem + L::oL);
-    float *sTot = sL;    // gate-stage partial sums, before L is formed
     float *sT = (float *)(smem + L::oT);
+    float *sTot = (float *)(smem + L::oTot);
     uint16_t *sAb = (uint16_t *)(smem + L::oAb);
     uint16_t *sAqk = (uint16_t *)(smem + L::oAqk);
     uint16_t *sS = (uint16_t *)(smem + L::oS);
@@ -150,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void kda_mfma_kernel(KdaParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
     const int l16 = lane & 15;
     const int lg = lane >> 4;
 
@@ -180,71 +197,89 @@ __global__ __launch_bounds__(kThreads) void kda_mfma_kernel(KdaParams p) {
         }
         store4(sS + dvr * KS + dkc, Sacc[i][0], Sacc[i][1], Sacc[i][2], Sacc[i][3]);
     }
-    // A_qk tiles above the diagonal inside the used 32-wide contraction blocks stay zero.
+    // Tiles above the diagonal inside the 32-wide contraction blocks that the products
+    // read, (rows 0-15, cols 16-31) and (rows 32-47, cols 48-63), stay zero: in A_qk
+    // for O, and in the fp32 inverse for its 32-wide level-2 products.  Nothing else
+    // ever writes them.
     for (int idx = tid; idx < 2 * 256; idx += kThreads) {
         const int blk = idx >> 8, e = idx & 255;
-        sAqk[((blk ? 32 : 0) + (e >> 4)) * kCS + (blk ? 48 : 16) + (e & 15)] = 0;
+        const int r = (blk ? 32 : 0) + (e >> 4), c = (blk ? 48 : 16) + (e & 15);
+        sAqk[r * kCS + c] = 0;
+        sL[r * kLS + c] = 0.f;
     }
 
     // ---- register prefetch of one chunk's inputs ----------------------------------
-    const int gcb = tid % NCB, grb = tid / NCB;
-    const int gc0 = 4 * gcb, gr0 = RPT * grb;
-    const int vr = tid >> 3, vj = 4 * (tid & 7);
-    uint2 pk[RPT], pq[RPT], pv;
-    float4 pla[RPT];
+    // gate stage: wave w owns chunk rows 8w..8w+7, lane l owns channels CPL*l..+CPL-1
+    const int gc0 = CPL * lane;
+    const int vr = tid >> 3, vj = 4 * (tid & 7);  // value-tile loader: one row, 4 columns
+    uint32_t pk[kRPW], pq[kRPW];
+    float2 pla[kRPW];
+    uint2 pv;
     float pbeta = 0.f, plah = 0.f;
+    // Rows at or beyond the end of the sequence are filled with zeros here (an exact
+    // identity step), so the stages below need no masking.  The chunk's base address
+    // is wave-uniform; a row adds a 32-bit byte offset (a chunk spans well under 4 GB).
+    const uint32_t rstride = (uint32_t)(H * DK);   // elements between consecutive tokens
     auto prefetch = [&](long c) {
         const int mc = (int)((t1 - c) < kC ? (t1 - c) : kC);
+        const size_t cbase = ((size_t)c * H + h) * DK;
+        const char *kc = (const char *)(p.k + cbase), *qc = (const char *)(p.q + cbase);
+        const char *lc = (const char *)(p.la + cbase);
 #pragma unroll
-        for (int rr = 0; rr < RPT; ++rr) {
-            const int r = gr0 + rr < mc ? gr0 + rr : mc - 1;
-            const size_t base = ((size_t)(c + r) * H + h) * DK + gc0;
-            pk[rr] = *(const uint2 *)(p.k + base);
-            pq[rr] = *(const uint2 *)(p.q + base);
-            if (GATE == kGateChannel) pla[rr] = *(const float4 *)(p.la + base);
+        for (int rr = 0; rr < kRPW; ++rr) {
+            const int r = kRPW * wave + rr;
+            if (r < mc) {
+                const uint32_t o2 = ((uint32_t)r * rstride + gc0) * 2u, o4 = 2u * o2;
+                if (CPL == 2) {
+                    pk[rr] = *(const uint32_t *)(kc + o2);
+                    pq[rr] = *(const uint32_t *)(qc + o2);
+                    if (GATE == kGateChannel) pla[rr] = *(const float2 *)(lc + o4);
+                } else {
+                    pk[rr] = *(const uint16_t *)(kc + o2);
+                    pq[rr] = *(const uint16_t *)(qc + o2);
+                    if (GATE == kGateChannel) pla[rr] = make_float2(*(const float *)(lc + o4), 0.f);
+                }
+            } else {
+                pk[rr] = pq[rr] = 0u;
+                pla[rr] = make_float2(0.f, 0.f);
+            }
         }
-        const int rv = vr < mc ? vr : mc - 1;
-        pv = *(const uint2 *)(p.v + ((size_t)(c + rv) * H + h) * DV + j0 + vj);
+        pv = vr < mc ? *(const uint2 *)(p.v + ((size_t)(c + vr) * H + h) * DV + j0 + vj)
+                     : make_uint2(0u, 0u);
         if (tid < kC) {
-            const int rb = tid < mc ? tid : mc - 1;
-            pbeta = p.beta[(size_t)(c + rb) * H + h];
-            if (GATE == kGateHead) plah = p.la[(size_t)(c + rb) * H + h];
+            pbeta = tid < mc ? p.beta[(size_t)(c + tid) * H + h] : 0.f;
+            if (GATE == kGateHead) plah = tid < mc ? p.la[(size_t)(c + tid) * H + h] : 0.f;
         }
     };
     if (t0 < t1) prefetch(t0);
 
-    // serial-stage tiles of this wave
-    const int vib = wave >> 1, vjb = wave & 1;  // V_new / U: chunk-row block, dv block
-    const int ocb = wave >> 1, odb = wave & 1;  // O^T: chunk-row block, dv block
+    const int vib = wave >> 1, vjb = wave & 1;  // V_new / U tile: chunk-row block, dv block
+    const int ocb = wave >> 1, odb = wave & 1;  // O^T tile: chunk-row block, dv block
 
     for (long c0 = t0; c0 < t1; c0 += kC) {
         const int m = (int)((t1 - c0) < kC ? (t1 - c0) : kC);
 
-        // ============ gate, part 1: local prefix sums, beta, values ===================
-        float kf[RPT][4], qf[RPT][4], g[RPT][4];
+        // ============ gate, part 1: in-wave prefix sums, beta, values =================
+        float gl[kRPW][CPL];
         {
-            float run[4] = {0.f, 0.f, 0.f, 0.f};
+            float run[CPL];
 #pragma unroll
-            for (int rr = 0; rr < RPT; ++rr) {
-                const bool ok = gr0 + rr < m;
-                kf[rr][0] = bf16_lo(pk[rr].x); kf[rr][1] = bf16_hi(pk[rr].x);
-                kf[rr][2] = bf16_lo(pk[rr].y); kf[rr][3] = bf16_hi(pk[rr].y);
-                qf[rr][0] = bf16_lo(pq[rr].x); qf[rr][1] = bf16_hi(pq[rr].x);
-                qf[rr][2] = bf16_lo(pq[rr].y); qf[rr][3] = bf16_hi(pq[rr].y);
-                if (GATE == kGateChannel && ok) {
-                    run[0] += pla[rr].x * kLog2e; run[1] += pla[rr].y * kLog2e;
-                    run[2] += pla[rr].z * kLog2e; run[3] += pla[rr].w * kLog2e;
+            for (int e = 0; e < CPL; ++e) run[e] = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < kRPW; ++rr) {
+                if (GATE == kGateChannel) {
+                    run[0] += pla[rr].x * kLog2e;
+                    if (CPL == 2) run[CPL - 1] += pla[rr].y * kLog2e;
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (!ok) kf[rr][e] = qf[rr][e] = 0.f;
-                    g[rr][e] = run[e];
-                }
+                for (int e = 0; e < CPL; ++e) gl[rr][e] = run[e];
             }
-            if (GATE == kGateChannel)
-                *(float4 *)(sTot + grb * DK + gc0) = make_float4(run[0], run[1], run[2], run[3]);
+            if (GATE == kGateChannel) {
+                if (CPL == 2) *(float2 *)(sTot + wave * DK + gc0) = make_float2(run[0], run[CPL - 1]);
+                else sTot[wave * DK + gc0] = run[0];
+            }
             if (GATE == kGateHead && wave == 0) {
-                float x = lane < m ? plah * kLog2e : 0.f;
+                float x = plah * kLog2e;
 #pragma unroll
                 for (int off = 1; off < 64; off <<= 1) {
                     const float y = __shfl_up(x, off, 64);
@@ -255,176 +290,190 @@ __global__ __launch_bounds__(kThreads) void kda_mfma_kernel(KdaParams p) {
                 sRow[64 + lane] = exp2_fast(-x);
                 if (lane == 0) sRow[128] = exp2_fast(gc);
             }
-            if (tid < kC) sBeta[tid] = tid < m ? pbeta : 0.f;
-            *(uint2 *)(sV + vr * kVS + vj) = vr < m ? pv : make_uint2(0u, 0u);
+            if (tid < kC) sBeta[tid] = pbeta;
+            *(uint2 *)(sV + vr * kVS + vj) = pv;
         }
         lds_barrier();
         // ============ gate, part 2: scaled operands ===================================
         {
-            float eg[RPT][4], eig[RPT][4], egc[4];
+            float carry[CPL], egc[CPL];
             if (GATE == kGateChannel) {
-                float carry[4] = {0.f, 0.f, 0.f, 0.f}, gcv[4] = {0.f, 0.f, 0.f, 0.f};
+                float tot[CPL];
 #pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) {
-                    const float4 t4 = *(const float4 *)(sTot + rb * DK + gc0);
-                    const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+                for (int e = 0; e < CPL; ++e) carry[e] = tot[e] = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        gcv[e] += tv[e];
-                        if (rb < grb) carry[e] += tv[e];
+                for (int w2 = 0; w2 < kWaves; ++w2) {
+                    float tv[CPL];
+                    if (CPL == 2) {
+                        const float2 t2 = *(const float2 *)(sTot + w2 * DK + gc0);
+                        tv[0] = t2.x;
+                        tv[CPL - 1] = t2.y;
+                    } else {
+                        tv[0] = sTot[w2 * DK + gc0];
+                    }
+#pragma unroll
+                    for (int e = 0; e < CPL; ++e) {
+                        tot[e] += tv[e];
+                        if (w2 < wave) carry[e] += tv[e];  // wave-uniform
                     }
                 }
 #pragma unroll
-                for (int rr = 0; rr < RPT; ++rr)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float gg = g[rr][e] + carry[e];
-                        eg[rr][e] = exp2_fast(gg);
-                        eig[rr][e] = exp2_fast(-gg);
-                    }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) egc[e] = exp2_fast(gcv[e]);
-                if (grb == 0)
-                    *(float4 *)(sGC + gc0) = make_float4(egc[0], egc[1], egc[2], egc[3]);
-            } else if (GATE == kGateHead) {
-#pragma unroll
-                for (int rr = 0; rr < RPT; ++rr) {
-                    const float a0 = sRow[gr0 + rr], a1 = sRow[64 + gr0 + rr];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) { eg[rr][e] = a0; eig[rr][e] = a1; }
-                }
-                const float ec = sRow[128];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) egc[e] = ec;
-                if (grb == 0) *(float4 *)(sGC + gc0) = make_float4(ec, ec, ec, ec);
+                for (int e = 0; e < CPL; ++e) egc[e] = exp2_fast(tot[e]);
             } else {
+                const float ec = GATE == kGateHead ? sRow[128] : 1.f;
 #pragma unroll
-                for (int rr = 0; rr < RPT; ++rr)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) eg[rr][e] = eig[rr][e] = 1.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) egc[e] = 1.f;
-                if (grb == 0) *(float4 *)(sGC + gc0) = make_float4(1.f, 1.f, 1.f, 1.f);
+                for (int e = 0; e < CPL; ++e) carry[e] = 0.f, egc[e] = ec;
+            }
+            if (wave == 0) {
+                if (CPL == 2) *(float2 *)(sGC + gc0) = make_float2(egc[0], egc[CPL - 1]);
+                else sGC[gc0] = egc[0];
             }
 #pragma unroll
-            for (int rr = 0; rr < RPT; ++rr) {
-                const int r = gr0 + rr;
-                float kl[4], kr[4], ql[4], kh[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kl[e] = kf[rr][e] * eg[rr][e];
-                    kr[e] = kf[rr][e] * eig[rr][e];
-                    ql[e] = qf[rr][e] * eg[rr][e];
-                    kh[e] = kr[e] * egc[e];
+            for (int rr = 0; rr < kRPW; ++rr) {
+                const int r = kRPW * wave + rr;
+                float kv[CPL], qv[CPL], eg[CPL], eig[CPL];
+                kv[0] = bf16_lo(pk[rr]);
+                qv[0] = bf16_lo(pq[rr]);
+                if (CPL == 2) {
+                    kv[CPL - 1] = bf16_hi(pk[rr]);
+                    qv[CPL - 1] = bf16_hi(pq[rr]);
                 }
-                store4(sKl + r * KS + gc0, kl[0], kl[1], kl[2], kl[3]);
-                store4(sKr + r * KS + gc0, kr[0], kr[1], kr[2], kr[3]);
-                store4(sQl + r * KS + gc0, ql[0], ql[1], ql[2], ql[3]);
-                store4(sKh + r * KS + gc0, kh[0], kh[1], kh[2], kh[3]);
+#pragma unroll
+                for (int e = 0; e < CPL; ++e) {
+                    if (GATE == kGateChannel) {
+                        const float gg = gl[rr][e] + carry[e];
+                        eg[e] = exp2_fast(gg);
+                        eig[e] = exp2_fast(-gg);
+                    } else if (GATE == kGateHead) {
+                        eg[e] = sRow[r];
+                        eig[e] = sRow[64 + r];
+                    } else {
+                        eg[e] = eig[e] = 1.f;
+                    }
+                }
+                if (CPL == 2) {
+                    *(uint32_t *)(sKl + r * KS + gc0) = pack_bf16x2(kv[0] * eg[0], kv[CPL - 1] * eg[CPL - 1]);
+                    *(uint32_t *)(sKr + r * KS + gc0) = pack_bf16x2(kv[0] * eig[0], kv[CPL - 1] * eig[CPL - 1]);
+                    *(uint32_t *)(sQl + r * KS + gc0) = pack_bf16x2(qv[0] * eg[0], qv[CPL - 1] * eg[CPL - 1]);
+                } else {
+                    sKl[r * KS + gc0] = __builtin_bit_cast(uint16_t, __float2bfloat16(kv[0] * eg[0]));
+                    sKr[r * KS + gc0] = __builtin_bit_cast(uint16_t, __float2bfloat16(kv[0] * eig[0]));
+                    sQl[r * KS + gc0] = __builtin_bit_cast(uint16_t, __float2bfloat16(qv[0] * eg[0]));
+                }
             }
         }
         if (c0 + kC < t1) prefetch(c0 + kC);
         lds_barrier();
 
         // ============ gram: L = Diag(beta) K<- K->^T (strictly lower), A_qk ===========
-        // Tile (rb, cb), cb <= rb, computed transposed (D[c][r]) so each lane holds
-        // four consecutive columns of one row.
-        for (int job = wave; job < 10; job += kWaves) {
-            const int rb = job >= 6 ? 3 : (job >= 3 ? 2 : (job >= 1 ? 1 : 0));
-            const int cb = job - rb * (rb + 1) / 2;
-            f32x4 gacc = {0.f, 0.f, 0.f, 0.f}, aacc = {0.f, 0.f, 0.f, 0.f};
+        // 32x32 tiles (RB, CB) in {(0,0), (1,0), (1,1)}; waves 2j, 2j+1 form tile j of
+        // L and of A_qk.  Each is computed transposed, D[c][r], so a lane holds four
+        // consecutive columns of one row (32x32x16 layout: lane l holds rows
+        // 8q + 4(l/32) + 0..3, column l%32, q = 0..3).  The diagonal tiles write the
+        // zeros above the diagonal as well.
+        if (wave < 6) {
+            const int job = wave >> 1, RB = job >= 1 ? 1 : 0, CB = job == 2 ? 1 : 0;
+            const bool isA = wave & 1;
+            const uint16_t *src = isA ? sQl : sKl;
+            const int l32 = lane & 31, lh = lane >> 5;
+            bf16x8 fa[DK / 16], fb[DK / 16];
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                const bf16x8 a = frag(sKr, 16 * cb + l16, KS, 32 * kk + 8 * lg);
-                gacc = mfma(a, frag(sKl, 16 * rb + l16, KS, 32 * kk + 8 * lg), gacc);
-                aacc = mfma(a, frag(sQl, 16 * rb + l16, KS, 32 * kk + 8 * lg), aacc);
+            for (int s16 = 0; s16 < DK / 16; ++s16) {
+                fa[s16] = frag(sKr, 32 * CB + l32, KS, 16 * s16 + 8 * lh);
+                fb[s16] = frag(src, 32 * RB + l32, KS, 16 * s16 + 8 * lh);
             }
-            const int r = 16 * rb + l16, c = 16 * cb + 4 * lg;
+            f32x16 acc = {};
+#pragma unroll
+            for (int s16 = 0; s16 < DK / 16; ++s16) acc = mfma32x32(fa[s16], fb[s16], acc);
+            const int r = 32 * RB + l32;
             const float br = sBeta[r];
-            float gl[4], al[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                gl[e] = c + e < r ? br * gacc[e] : 0.f;
-                al[e] = c + e <= r ? aacc[e] : 0.f;
+            for (int q = 0; q < 4; ++q) {
+                const int c = 32 * CB + 8 * q + 4 * lh;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = acc[4 * q + e];
+                    v[e] = isA ? (c + e <= r ? x : 0.f) : (c + e < r ? br * x : 0.f);
+                }
+                if (isA) store4(sAqk + r * kCS + c, v[0], v[1], v[2], v[3]);
+                else *(float4 *)(sL + r * kLS + c) = make_float4(v[0], v[1], v[2], v[3]);
             }
-            *(float4 *)(sL + r * kLS + c) = make_float4(gl[0], gl[1], gl[2], gl[3]);
-            store4(sAqk + r * kCS + c, al[0], al[1], al[2], al[3]);
         }
         lds_barrier();
 
-        // ============ inverse, diagonal 16x16 blocks (wave 0) ==========================
-        if (wave == 0) {
-            const int o = 16 * lg, col = l16;  // block lg, column col
+        // ============ inverse: diagonal 16x16 blocks, one per wave =====================
+        // x = column l16 of (I + L_bb)^-1:  x_r = [r == col] - sum_{i<r} L[r][i] x_i,
+        // which leaves x_r = 0 for r < col without any masking.
+        if (wave < 4) {
+            const int o = 16 * wave;
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float s0 = 0.f, s1 = 0.f;
+                float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
                     const float4 Lv = *(const float4 *)(sL + (o + r) * kLS + o + 4 * i4);
                     const float lv[4] = {Lv.x, Lv.y, Lv.z, Lv.w};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 4 * i4 + e;
-                        if (i < r) {
-                            if (e & 1) s1 += lv[e] * x[i];
-                            else s0 += lv[e] * x[i];
-                        }
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * i4 + e < r) ps[e] += lv[e] * x[4 * i4 + e];
                 }
-                x[r] = r < col ? 0.f : (r == col ? 1.f : -(s0 + s1));
+                x[r] = (r == l16 ? 1.f : 0.f) - ((ps[0] + ps[1]) + (ps[2] + ps[3]));
             }
+            if (lane < 16) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (r >= col) sL[(o + r) * kLS + o + col] = x[r];
+                for (int r = 0; r < 16; ++r) sL[(o + r) * kLS + o + l16] = x[r];
+            }
         }
         lds_barrier();
-        // ============ inverse, 32-row level: X[p+1][p] = -X[p+1][p+1] L[p+1][p] X[p][p] ==
+        // ============ inverse, 32-row level: X[p+1][p] = -X[p+1][p+1] (L[p+1][p] X[p][p]) ==
         if (wave < 2) {
-            const int q0 = 32 * wave;  // rows/cols of block p = 2*wave
-            f32x4 t = {0.f, 0.f, 0.f, 0.f};
+            const int a0 = 32 * wave, a1 = a0 + 16;
+            const float4 la4 = *(const float4 *)(sL + (a1 + l16) * kLS + a0 + 4 * lg);
+            const bf16x4 fL = to_bf16x4(la4.x, la4.y, la4.z, la4.w);
+            const bf16x4 fX = to_bf16x4(sL[(a0 + 4 * lg + 0) * kLS + a0 + l16], sL[(a0 + 4 * lg + 1) * kLS + a0 + l16],
+                                        sL[(a0 + 4 * lg + 2) * kLS + a0 + l16], sL[(a0 + 4 * lg + 3) * kLS + a0 + l16]);
+            const f32x4 t = mfma16(fL, fX, f32x4{0.f, 0.f, 0.f, 0.f});  // t[e] = T[4lg+e][l16]
+            const float4 xa = *(const float4 *)(sL + (a1 + l16) * kLS + a1 + 4 * lg);
+            const f32x4 x = mfma16(to_bf16x4(xa.x, xa.y, xa.z, xa.w), to_bf16x4(t[0], t[1], t[2], t[3]),
+                                   f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                t = mfma32(sL[(q0 + 16 + l16) * kLS + q0 + 4 * s + lg],
-                           sL[(q0 + 4 * s + lg) * kLS + q0 + l16], t);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sT[wave * 16 * 17 + (4 * lg + e) * 17 + l16] = t[e];
-        }
-        lds_barrier();
-        if (wave < 2) {
-            const int q0 = 32 * wave;
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                x = mfma32(sL[(q0 + 16 + l16) * kLS + q0 + 16 + 4 * s + lg],
-                           sT[wave * 16 * 17 + (4 * s + lg) * 17 + l16], x);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sL[(q0 + 16 + 4 * lg + e) * kLS + q0 + l16] = -x[e];
+            for (int e = 0; e < 4; ++e) sL[(a1 + 4 * lg + e) * kLS + a0 + l16] = -x[e];
         }
         lds_barrier();
         // ============ inverse, 64-row level: X_BA = -X_BB (L_BA X_AA) ==================
-        if (wave < 4) {
-            const int ti = wave >> 1, tj = wave & 1;
-            f32x4 t = {0.f, 0.f, 0.f, 0.f};
-            for (int kb = tj; kb < 2; ++kb)
+        // Tile (ti, tj) of the 32x32 lower-left block; the contraction runs over 32 with
+        // the zero tiles above the diagonal filling the unused half.
+        {
+            const int ti = (wave >> 1) & 1, tj = wave & 1;
+            if (wave < 4) {
+                const float4 l0 = *(const float4 *)(sL + (32 + 16 * ti + l16) * kLS + 8 * lg);
+                const float4 l1 = *(const float4 *)(sL + (32 + 16 * ti + l16) * kLS + 8 * lg + 4);
+                float xb[8];
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    t = mfma32(sL[(32 + 16 * ti + l16) * kLS + 16 * kb + 4 * s + lg],
-                               sL[(16 * kb + 4 * s + lg) * kLS + 16 * tj + l16], t);
+                for (int e = 0; e < 8; ++e) xb[e] = sL[(8 * lg + e) * kLS + 16 * tj + l16];
+                const f32x4 t = mfma(to_bf16x8(l0, l1),
+                                     to_bf16x8(make_float4(xb[0], xb[1], xb[2], xb[3]),
+                                               make_float4(xb[4], xb[5], xb[6], xb[7])),
+                                     f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sT[(16 * ti + 4 * lg + e) * kTS + 16 * tj + l16] = t[e];
-        }
-        lds_barrier();
-        if (wave < 4) {
-            const int ti = wave >> 1, tj = wave & 1;
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-            for (int kb = 0; kb <= ti; ++kb)
+                for (int e = 0; e < 4; ++e) sT[(16 * ti + 4 * lg + e) * kTS + 16 * tj + l16] = t[e];
+            }
+            lds_barrier();
+            if (wave < 4) {
+                const float4 x0 = *(const float4 *)(sL + (32 + 16 * ti + l16) * kLS + 32 + 8 * lg);
+                const float4 x1 = *(const float4 *)(sL + (32 + 16 * ti + l16) * kLS + 32 + 8 * lg + 4);
+                float tb[8];
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    x = mfma32(sL[(32 + 16 * ti + l16) * kLS + 32 + 16 * kb + 4 * s + lg],
-                               sT[(16 * kb + 4 * s + lg) * kTS + 16 * tj + l16], x);
+                for (int e = 0; e < 8; ++e) tb[e] = sT[(8 * lg + e) * kTS + 16 * tj + l16];
+                const f32x4 x = mfma(to_bf16x8(x0, x1),
+                                     to_bf16x8(make_float4(tb[0], tb[1], tb[2], tb[3]),
+                                               make_float4(tb[4], tb[5], tb[6], tb[7])),
+                                     f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sL[(32 + 16 * ti + 4 * lg + e) * kLS + 16 * tj + l16] = -x[e];
+                for (int e = 0; e < 4; ++e) sL[(32 + 16 * ti + 4 * lg + e) * kLS + 16 * tj + l16] = -x[e];
+            }
         }
         lds_barrier();
         // At Diag(beta) -> bf16 (zero above the diagonal)
@@ -447,41 +496,49 @@ __global__ __launch_bounds__(kThreads) void kda_mfma_kernel(KdaParams p) {
 
         // ============ WY factors and the state-independent part of O ==================
         // W^T tile (dk block ib, chunk block jb) = K<-^T (At Diag(beta))^T
+        f32x4 U = {0.f, 0.f, 0.f, 0.f}, Ot = {0.f, 0.f, 0.f, 0.f};
+        {
 #pragma unroll
-        for (int i = 0; i < NWT; ++i) {
-            const int t = wave * NWT + i, ib = t >> 2, jb = t & 3;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma(frag_tr(sKl, 0, KS, 16 * ib, lane), frag(sAb, 16 * jb + l16, kCS, 8 * lg), acc);
-            if (jb >= 2)
-                acc = mfma(frag_tr(sKl, 32, KS, 16 * ib, lane),
-                           frag(sAb, 16 * jb + l16, kCS, 32 + 8 * lg), acc);
-            store4(sW + (16 * jb + l16) * KS + 16 * ib + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
+            for (int i = 0; i < NWT; ++i) {
+                const int t = wave * NWT + i, ib = t >> 2, jb = t & 3;
+                f32x4 acc = mfma(frag_tr(sKl, 0, KS, 16 * ib, lane),
+                                 frag(sAb, 16 * jb + l16, kCS, 8 * lg), f32x4{0.f, 0.f, 0.f, 0.f});
+                if (jb >= 2)
+                    acc = mfma(frag_tr(sKl, 32, KS, 16 * ib, lane),
+                               frag(sAb, 16 * jb + l16, kCS, 32 + 8 * lg), acc);
+                store4(sW + (16 * jb + l16) * KS + 16 * ib + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
+            }
+            U = mfma(frag(sAb, 16 * vib + l16, kCS, 8 * lg), frag_tr(sV, 0, kVS, 16 * vjb, lane), U);
+            if (vib >= 2)
+                U = mfma(frag(sAb, 16 * vib + l16, kCS, 32 + 8 * lg), frag_tr(sV, 32, kVS, 16 * vjb, lane), U);
+            bf16x8 fs[DK / 32], fq[DK / 32];
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                fs[kk] = frag(sS, 16 * odb + l16, KS, 32 * kk + 8 * lg);
+                fq[kk] = frag(sQl, 16 * ocb + l16, KS, 32 * kk + 8 * lg);
+            }
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) Ot = mfma(fs[kk], fq[kk], Ot);
         }
-        f32x4 U = {0.f, 0.f, 0.f, 0.f};
-        U = mfma(frag(sAb, 16 * vib + l16, kCS, 8 * lg), frag_tr(sV, 0, kVS, 16 * vjb, lane), U);
-        if (vib >= 2)
-            U = mfma(frag(sAb, 16 * vib + l16, kCS, 32 + 8 * lg), frag_tr(sV, 32, kVS, 16 * vjb, lane), U);
-        // O^T tile (dv block odb, chunk block ocb): S Q<-^T
-        f32x4 Ot = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk)
-            Ot = mfma(frag(sS, 16 * odb + l16, KS, 32 * kk + 8 * lg),
-                      frag(sQl, 16 * ocb + l16, KS, 32 * kk + 8 * lg), Ot);
         lds_barrier();
 
         // ============ V_new = U - W S^T =================================================
         {
+            bf16x8 fw[DK / 32], fs[DK / 32];
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                fw[kk] = frag(sW, 16 * vib + l16, KS, 32 * kk + 8 * lg);
+                fs[kk] = frag(sS, 16 * vjb + l16, KS, 32 * kk + 8 * lg);
+            }
             f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk)
-                P = mfma(frag(sW, 16 * vib + l16, KS, 32 * kk + 8 * lg),
-                         frag(sS, 16 * vjb + l16, KS, 32 * kk + 8 * lg), P);
+            for (int kk = 0; kk < DK / 32; ++kk) P = mfma(fw[kk], fs[kk], P);
             store4(sVnT + (16 * vjb + l16) * kCS + 16 * vib + 4 * lg, U[0] - P[0], U[1] - P[1],
                    U[2] - P[2], U[3] - P[3]);
         }
         lds_barrier();
 
-        // ============ O += A_qk V_new ;  S = S Diag(gamma_C) + V_new^T K^ ==============
+        // ============ O += A_qk V_new ;  S = (S + V_new^T K->) Diag(gamma_C) ===========
         Ot = mfma(frag(sVnT, 16 * odb + l16, kCS, 8 * lg), frag(sAqk, 16 * ocb + l16, kCS, 8 * lg), Ot);
         if (ocb >= 2)
             Ot = mfma(frag(sVnT, 16 * odb + l16, kCS, 32 + 8 * lg),
@@ -497,20 +554,21 @@ __global__ __launch_bounds__(kThreads) void kda_mfma_kernel(KdaParams p) {
         }
 #pragma unroll
         for (int i = 0; i < NST; ++i) {
+            Sacc[i] = mfma(frag_tr(sKr, 0, KS, 16 * sib[i], lane),
+                           frag(sVnT, 16 * sjb[i] + l16, kCS, 8 * lg), Sacc[i]);
+            Sacc[i] = mfma(frag_tr(sKr, 32, KS, 16 * sib[i], lane),
+                           frag(sVnT, 16 * sjb[i] + l16, kCS, 32 + 8 * lg), Sacc[i]);
             const float4 gc = *(const float4 *)(sGC + 16 * sib[i] + 4 * lg);
             Sacc[i][0] *= gc.x; Sacc[i][1] *= gc.y; Sacc[i][2] *= gc.z; Sacc[i][3] *= gc.w;
-            Sacc[i] = mfma(frag_tr(sKh, 0, KS, 16 * sib[i], lane),
-                           frag(sVnT, 16 * sjb[i] + l16, kCS, 8 * lg), Sacc[i]);
-            Sacc[i] = mfma(frag_tr(sKh, 32, KS, 16 * sib[i], lane),
-                           frag(sVnT, 16 * sjb[i] + l16, kCS, 32 + 8 * lg), Sacc[i]);
         }
         // The old bf16 state was last read before the barrier above.
 #pragma unroll
         for (int i = 0; i < NST; ++i)
             store4(sS + (16 * sjb[i] + l16) * KS + 16 * sib[i] + 4 * lg, Sacc[i][0], Sacc[i][1],
                    Sacc[i][2], Sacc[i][3]);
-        // No barrier here: the next chunk's first writes (totals, beta, values) touch
-        // nothing read above, and its second stage starts after a barrier.
+        // No barrier here: the next chunk's first stage writes only the gate partial
+        // sums, beta, the value tile and (head gate) the row gates, none of which is
+        // read above; its second stage starts after a barrier.
     }
 
     if (p.Sf) {
