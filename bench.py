@@ -23,6 +23,33 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 WORKLOAD = "kda"
+KERNEL_SOURCES = ["chunkwise_gated_delta_amd/csrc/gdr_kda_mfma.hip"]
+COUNTERS_FILE = "profiles/kda_mfma_kernel__kda_B2_H32_T8192_d128__counters.md"
+
+
+def counter_traffic():
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary.
+
+    The summary records the sha256 of the kernel source it was measured on; when the
+    source has changed since, the figure no longer describes this kernel and None is
+    returned.
+    """
+    import hashlib
+    import re
+
+    try:
+        text = open(os.path.join(ROOT, COUNTERS_FILE)).read()
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    m_sha = re.search(r"Kernel source sha256 `([0-9a-f]{64})`", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    if not (m_sha and m_bytes) or m_sha.group(1) != h.hexdigest():
+        return None
+    return int(m_bytes.group(1))
 
 
 def algorithmic_counts(P):
@@ -152,9 +179,12 @@ def main():
                    "global_batch": P.B, "seq_len": P.T, "heads": P.H, "dk": P.dk, "dv": P.dv,
                    "chunk": P.chunk, "parallelism": "none (one GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": counter_traffic(),
                      "kernel": "kda_mfma_kernel<128, channel gate>",
-                     "kernel_ms_mean": kern_ms, "kernel_ms_p10": launch_ms[len(launch_ms) // 10],
+                     "kernel_ms_mean": kern_ms,
+                     "kernel_ms_median": launch_ms[len(launch_ms) // 2],
+                     "kernel_ms_p10": launch_ms[len(launch_ms) // 10],
                      "kernel_ms_p90": launch_ms[(9 * len(launch_ms)) // 10],
                      "alg_bytes_per_launch": alg_bytes},
         "mfma": {"alg_flops_per_launch": alg_flops, "achieved_tflops": tflops,

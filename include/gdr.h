@@ -90,8 +90,8 @@ size_t gdr_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int C, int n
  *                                             N = B and sequence n is batch row n.
  *               n_seq is ignored when cu_seqlens is NULL.
  *   C           chunk size (tokens per chunk).  The result does not depend on it
- *               beyond rounding.  Supported: 64 (bf16); 16, 32, 64 (fp32, with
- *               C*dk <= 8192).
+ *               beyond rounding.  Supported: 64 for bf16 without a, b; 16, 32 or
+ *               64 for fp32 inputs and for bf16 with a, b (DPLR).
  *   dk, dv      head sizes; dk in {64, 128}; dv a multiple of 32 up to 256.
  *
  * S_final may equal S0 (in-place state update).  O must not overlap any input.
