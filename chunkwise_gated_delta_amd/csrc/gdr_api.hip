@@ -56,12 +56,22 @@ FwdArgs make_args(int B, int H, int T, int dk, int dv, int C, int n_seq, int dty
     a.B = B; a.H = H; a.T = T; a.dk = dk; a.dv = dv; a.C = C; a.n_seq = n_seq;
     a.dtype = dtype; a.gate = gate;
     static const char dummy = 0;
+    static const int32_t dummy_cu = 0;
     if (has_ab) a.a = a.b = &dummy;
+    if (n_seq > 0) a.cu_seqlens = &dummy_cu;  // marks packed sequences for the size query
     return a;
 }
 
+bool use_fused() {
+    static const int on = [] {
+        const char *s = std::getenv("GDR_KDA_FUSED");
+        return (s && s[0] == '1') ? 1 : 0;
+    }();
+    return on != 0;
+}
+
 size_t workspace_for(const FwdArgs &a, int n_seq_eff) {
-    if (gdr::kda_mfma_supported(a)) return gdr::kWorkspaceHeader;
+    if (gdr::kda_split_supported(a)) return gdr::kda_split_workspace_bytes(a, n_seq_eff);
     return gdr::generic_workspace_bytes(a, n_seq_eff);
 }
 
@@ -118,7 +128,7 @@ int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
     if (S0 && S_final && overlaps(rsf, rs0) && (const void *)S_final != (const void *)S0)
         return GDR_ERR_ALIAS;  // ... but not partly overlap it
 
-    FwdArgs args = make_args(B, H, T, dk, dv, C, n_seq, dtype, gate, has_ab);
+    FwdArgs args = make_args(B, H, T, dk, dv, C, varlen ? n_seq : 0, dtype, gate, has_ab);
     args.q = q; args.k = k; args.v = v; args.a = a; args.b = b;
     args.log_alpha = log_alpha; args.beta = beta; args.S0 = S0;
     args.O = O; args.S_final = S_final; args.cu_seqlens = cu_seqlens;
@@ -131,11 +141,14 @@ int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
     if (overlaps(rws, rO) || overlaps(rws, rsf)) return GDR_ERR_ALIAS;
 
     hipStream_t s = (hipStream_t)stream;
-    const bool mfma = gdr::kda_mfma_supported(args);
+    const bool split = gdr::kda_split_supported(args);
+    const bool fused = split && use_fused();
     if (trace_enabled())
         std::fprintf(stderr, "[gdr] %s B=%d H=%d T=%d N=%d dk=%d dv=%d C=%d dtype=%d gate=%d ws=%zu\n",
-                     mfma ? "kda_mfma" : "generic", B, H, T, N, dk, dv, C, dtype, gate, need);
-    const int rc = mfma ? gdr::launch_kda_mfma(args, N, s) : gdr::launch_generic(args, N, s);
+                     fused ? "kda_fused" : (split ? "kda_split" : "generic"), B, H, T, N, dk, dv, C,
+                     dtype, gate, need);
+    const int rc = fused ? gdr::launch_kda_mfma(args, N, s)
+                         : (split ? gdr::launch_kda_split(args, N, s) : gdr::launch_generic(args, N, s));
     return rc == 0 ? GDR_OK : GDR_ERR_HIP;
 }
 

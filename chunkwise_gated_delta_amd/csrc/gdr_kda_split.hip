@@ -1,0 +1,855 @@
+// Chunkwise forward for the KDA family (a = k, b = beta k) with bf16 inputs, as two
+// kernels on gfx950 matrix cores (fp32 accumulate).
+//
+// Per chunk of 64 tokens the KDA chunk form ("Kimi Delta Attention backward" notes,
+// forward recap) splits into work that does not depend on the state and a short
+// serial remainder:
+//
+//   kda_prep_kernel   one workgroup per (chunk, head), every chunk at once
+//     g      in-chunk inclusive prefix sum of log alpha (per channel or head)
+//     Q<- = Q e^g, K<- = K e^g, K-> = K e^-g, K^ = K e^(g_C - g), gamma_C = e^g_C
+//     L      = Diag(beta)(K<- K->^T strictly lower),  A_qk = Q<- K->^T on and below
+//              the diagonal
+//     At     = (I + L)^-1 by 16x16 blocks ("DeltaNet" notes, section 4.2): diagonal
+//              blocks by forward substitution, then the two-block form
+//              [A 0; C B]^-1 = [A^-1 0; -B^-1 C A^-1  B^-1] at 32 and 64 rows
+//     Ab     = At Diag(beta),  Ao = A_qk Ab
+//     W'     = -Ab K<-,  Q~ = Q<- - Ao K<-
+//   kda_state_kernel  one workgroup per (sequence, head, 32-wide dv tile), serial
+//                     over the sequence's chunks, state tile in registers
+//     V_new  = Ab V + W' S^T                 (= U - W S^T)
+//     O      = Ao V + Q~ S^T                 (= Q<- S^T + A_qk V_new)
+//     S      = S Diag(gamma_C) + V_new^T K^  (= (S + V_new^T K->) Diag(gamma_C))
+//
+// The two right-hand forms of O are equal because A_qk V_new = A_qk Ab V - A_qk Ab
+// K<- S^T; with them the output no longer waits for V_new, and the serial kernel's
+// chain per chunk is two products.  The prep kernel hands its results over in the
+// operand order of v_mfma_f32_32x32x16_bf16, so the state kernel loads them straight
+// into registers with whole-wave contiguous loads.
+#include "gdr_mfma.h"
+
+namespace gdr {
+namespace {
+
+constexpr int kC = 64;         // chunk size
+constexpr int kDVT = 32;       // dv columns per state workgroup
+constexpr int kThreads = 256;  // 4 waves, both kernels
+constexpr int kCS = kC + 8;    // bf16 row stride of [*][64] arrays
+constexpr int kDS = 20;        // fp32 row stride of the 16x16 diagonal blocks
+constexpr int kTS = 32 + 8;    // bf16 row stride of the 32x32 level temporary
+constexpr int kVS = kDVT + 8;  // bf16 row stride of the value tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+// One (chunk, head) block of the workspace.  A "fragment tile" of 32 rows and K
+// contraction columns is stored as K/16 steps x 64 lanes x 16 bytes; lane l of
+// step s holds row l%32, columns 16s + 8(l/32) + 0..7 -- the A-operand registers of
+// v_mfma_f32_32x32x16_bf16, so one wave-wide load of a step is one contiguous KiB.
+template <int DK>
+struct Blk {
+    static constexpr int oW = 0;                // W' = -Ab K<-: row tiles 0-31, 32-63, K = DK
+    static constexpr int oQ = oW + 128 * DK;    // Q~ = Q<- - Ao K<-: same
+    static constexpr int oK = oQ + 128 * DK;    // K^ transposed: tiles of dk rows 32w.., K = 64 tokens
+    static constexpr int oAb = oK + 128 * DK;   // Ab: 32x32 tiles (0,0), (1,0), (1,1), K = 32
+    static constexpr int oAo = oAb + 6144;      // Ao: same tiles
+    static constexpr int oG = oAo + 6144;       // gamma_C [DK] fp32
+    static constexpr int bytes = oG + 4 * DK;
+    static_assert(bytes % 256 == 0, "block alignment");
+};
+
+struct SplitParams {
+    const bf16 *q, *k, *v;
+    const float *la, *beta, *S0;
+    bf16 *O;
+    float *Sf;
+    const int32_t *cu;
+    int32_t *coff;  // first chunk of each packed sequence (with cu_seqlens), else NULL
+    int *err;
+    char *blk;      // (chunk, head) blocks
+    long total;
+    int H, T, dv, n_seq, n_tiles;
+    int nc;          // chunks per sequence (fixed-length batch)
+    int max_chunks;  // blocks per head in the workspace
+};
+
+// ---------------------------------------------------------------------------------
+// Chunk offsets of packed sequences: coff[n] = sum over m < n of ceil(len_m / 64).
+// Malformed offsets are clamped here (and flagged) exactly as the other kernels clamp
+// them, so all three agree on every sequence's bounds.
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void kda_plan_kernel(SplitParams p) {
+    __shared__ int part[kThreads];
+    const int tid = threadIdx.x, N = p.n_seq;
+    const int per = (N + kThreads - 1) / kThreads;
+    const int a = min(N, tid * per), b = min(N, a + per);
+    int s = 0;
+    for (int n = a; n < b; ++n) {
+        long t0, t1;
+        seq_bounds(p.cu, n, p.T, p.total, t0, t1, p.err);
+        s += (int)((t1 - t0 + kC - 1) / kC);
+    }
+    part[tid] = s;
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int i = 0; i < kThreads; ++i) {
+            const int x = part[i];
+            part[i] = acc;
+            acc += x;
+        }
+        p.coff[N] = acc;
+    }
+    __syncthreads();
+    s = part[tid];
+    for (int n = a; n < b; ++n) {
+        p.coff[n] = s;
+        long t0, t1;
+        seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
+        s += (int)((t1 - t0 + kC - 1) / kC);
+    }
+}
+
+// Sequence n and chunk c of global chunk j; false when j is past the last chunk.
+__device__ __forceinline__ bool chunk_of(const SplitParams &p, int j, int &n, int &c) {
+    if (p.coff == nullptr) {
+        n = j / p.nc;
+        c = j - n * p.nc;
+        return true;
+    }
+    const int last = min(p.coff[p.n_seq], p.max_chunks);
+    if (j >= last) return false;
+    int lo = 0, hi = p.n_seq - 1;  // last n with coff[n] <= j
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.coff[mid] <= j) lo = mid;
+        else hi = mid - 1;
+    }
+    n = lo;
+    c = j - p.coff[lo];
+    return true;
+}
+
+// ---------------------------------------------------------------------------------
+// Prep kernel
+// ---------------------------------------------------------------------------------
+template <int DK>
+struct PrepSmem {
+    static constexpr int KS = DK + 8;                   // bf16 row stride of [64][DK] arrays
+    static constexpr int oKl = 0;                       // K<-
+    static constexpr int oKr = oKl + kC * KS * 2;       // K->, then W'
+    static constexpr int oQl = oKr + kC * KS * 2;       // Q<-, then Q~
+    static constexpr int oX = oQl + kC * KS * 2;        // bf16 [64][kCS]: L off the diagonal blocks -> At -> Ab
+    static constexpr int oAqk = oX + kC * kCS * 2;      // bf16 [64][kCS]: A_qk -> Ao
+    static constexpr int oLd = oAqk + kC * kCS * 2;     // fp32 4 x [16][kDS]: diagonal blocks of L -> of At
+    static constexpr int oT = oLd + 4 * 16 * kDS * 4;   // bf16 [32][kTS]
+    static constexpr int oTot = oLd;                    // fp32 [8][DK] gate partial sums (before oLd is used)
+    static constexpr int oBeta = oT + 32 * kTS * 2;     // fp32 [64]
+    static constexpr int oG = oBeta + kC * 4;           // fp32 [65]: head-gate prefix sums and total
+    static constexpr int bytes = oG + 80 * 4;
+    static_assert(8 * DK * 4 <= oBeta - oLd, "gate partial sums fit");
+    static_assert(bytes <= 80 * 1024, "two workgroups per CU");
+};
+
+template <int DK, int GATE>
+__global__ __launch_bounds__(kThreads) void kda_prep_kernel(SplitParams p) {
+    using L = PrepSmem<DK>;
+    using Bk = Blk<DK>;
+    constexpr int KS = L::KS;
+    constexpr int CPT = DK / 32;  // gate stage: channels per thread
+    constexpr int WPR = CPT / 2;  // 32-bit words of bf16 per row per thread
+
+    __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+    uint16_t *sKl = (uint16_t *)(smem + L::oKl);
+    uint16_t *sKr = (uint16_t *)(smem + L::oKr);
+    uint16_t *sQl = (uint16_t *)(smem + L::oQl);
+    uint16_t *sX = (uint16_t *)(smem + L::oX);
+    uint16_t *sAqk = (uint16_t *)(smem + L::oAqk);
+    float *sLd = (float *)(smem + L::oLd);
+    uint16_t *sT = (uint16_t *)(smem + L::oT);
+    float *sTot = (float *)(smem + L::oTot);
+    float *sBeta = (float *)(smem + L::oBeta);
+    float *sG = (float *)(smem + L::oG);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int H = p.H;
+    const int h = blockIdx.x % H;
+    const int j = blockIdx.x / H;
+    int n, c;
+    if (!chunk_of(p, j, n, c)) return;  // workgroup-uniform
+    long t0, t1;
+    seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
+    const long tok0 = t0 + (long)c * kC;
+    const int m = (int)((t1 - tok0) < kC ? (t1 - tok0) : kC);  // >= 1
+    char *bp = p.blk + ((size_t)j * H + h) * Bk::bytes;
+
+    // ---- loads: thread (rg, cg) owns rows 8rg..8rg+7, channels CPT*cg..+CPT-1 ------
+    // Every load is issued unconditionally (rows past the end of the sequence re-read
+    // the last row) so that all of them are in flight at once; those rows are then
+    // zeroed, which makes them exact identity steps.
+    const int rg = tid >> 5, cg = tid & 31, c0 = CPT * cg;
+    uint32_t kw[8][WPR], qw[8][WPR];
+    float lw[8][CPT];
+    {
+        const size_t rs = (size_t)H * DK;
+        const bf16 *kb = p.k + ((size_t)tok0 * H + h) * DK + c0;
+        const bf16 *qb = p.q + ((size_t)tok0 * H + h) * DK + c0;
+        const float *lb = p.la + ((size_t)tok0 * H + h) * DK + c0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * rg + i, rr = r < m ? r : m - 1;
+            if constexpr (WPR == 2) {
+                const uint2 xk = *(const uint2 *)(kb + rr * rs), xq = *(const uint2 *)(qb + rr * rs);
+                kw[i][0] = xk.x; kw[i][WPR - 1] = xk.y;
+                qw[i][0] = xq.x; qw[i][WPR - 1] = xq.y;
+            } else {
+                kw[i][0] = *(const uint32_t *)(kb + rr * rs);
+                qw[i][0] = *(const uint32_t *)(qb + rr * rs);
+            }
+            if constexpr (GATE == kGateChannel) {
+                if constexpr (CPT == 4) {
+                    const float4 x = *(const float4 *)(lb + rr * rs);
+                    lw[i][0] = x.x; lw[i][1] = x.y; lw[i][2] = x.z; lw[i][3] = x.w;
+                } else {
+                    const float2 x = *(const float2 *)(lb + rr * rs);
+                    lw[i][0] = x.x; lw[i][1] = x.y;
+                }
+            }
+        }
+    }
+    const int rb0 = tid < kC ? (tid < m ? tid : m - 1) : 0;
+    float beta_r = p.beta[(size_t)(tok0 + rb0) * H + h];
+    float lah = 0.f;
+    if (GATE == kGateHead) lah = p.la[(size_t)(tok0 + (lane < m ? lane : m - 1)) * H + h];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (8 * rg + i >= m) {
+#pragma unroll
+            for (int w = 0; w < WPR; ++w) kw[i][w] = qw[i][w] = 0u;
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) lw[i][e] = 0.f;
+        }
+    }
+    if (tid < kC) sBeta[tid] = tid < m ? beta_r : 0.f;
+    if (GATE == kGateHead && wave == 0) {
+        float x = lane < m ? lah * kLog2e : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        sG[lane] = x;
+        if (lane == 63) sG[64] = x;
+    }
+    // The products read whole 32-wide contraction blocks of X and A_qk, so everything
+    // not written below (above the diagonal) must be zero.
+    for (int i = tid; i < 2 * kC * kCS * 2 / 16; i += kThreads)
+        ((uint4 *)(smem + L::oX))[i] = make_uint4(0u, 0u, 0u, 0u);
+
+    // ---- gate: prefix sums (log2 domain) -------------------------------------------
+    float g[8][CPT], gC[CPT];
+    if (GATE == kGateChannel) {
+        float run[CPT];
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) run[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) {
+                run[e] += lw[i][e] * kLog2e;
+                g[i][e] = run[e];
+            }
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) sTot[rg * DK + c0 + e] = run[e];
+    }
+    lds_barrier();
+    if (GATE == kGateChannel) {
+        float carry[CPT], tot[CPT];
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) carry[e] = tot[e] = 0.f;
+#pragma unroll
+        for (int r2 = 0; r2 < 8; ++r2)
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) {
+                const float t = sTot[r2 * DK + c0 + e];
+                tot[e] += t;
+                carry[e] += r2 < rg ? t : 0.f;
+            }
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+            gC[e] = tot[e];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) g[i][e] += carry[e];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+            gC[e] = GATE == kGateHead ? sG[64] : 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) g[i][e] = GATE == kGateHead ? sG[8 * rg + i] : 0.f;
+        }
+    }
+
+    // ---- scaled operands: Q<-, K<-, K-> to LDS; K^ and gamma_C to the block ---------
+    {
+        float kh[CPT][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * rg + i;
+            float kv[CPT], qv[CPT], a[CPT], b[CPT], cq[CPT];
+#pragma unroll
+            for (int w = 0; w < WPR; ++w) {
+                kv[2 * w] = bf16_lo(kw[i][w]); kv[2 * w + 1] = bf16_hi(kw[i][w]);
+                qv[2 * w] = bf16_lo(qw[i][w]); qv[2 * w + 1] = bf16_hi(qw[i][w]);
+            }
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) {
+                const float eg = GATE == kGateNone ? 1.f : exp2_fast(g[i][e]);
+                const float eig = GATE == kGateNone ? 1.f : exp2_fast(-g[i][e]);
+                const float egc = GATE == kGateNone ? 1.f : exp2_fast(gC[e] - g[i][e]);
+                a[e] = kv[e] * eg;
+                b[e] = kv[e] * eig;
+                cq[e] = qv[e] * eg;
+                kh[e][i] = kv[e] * egc;
+            }
+            uint32_t wa[WPR], wb[WPR], wq[WPR];
+#pragma unroll
+            for (int w = 0; w < WPR; ++w) {
+                wa[w] = pack_bf16x2(a[2 * w], a[2 * w + 1]);
+                wb[w] = pack_bf16x2(b[2 * w], b[2 * w + 1]);
+                wq[w] = pack_bf16x2(cq[2 * w], cq[2 * w + 1]);
+            }
+            if constexpr (WPR == 2) {
+                *(uint2 *)(sKl + r * KS + c0) = make_uint2(wa[0], wa[1]);
+                *(uint2 *)(sKr + r * KS + c0) = make_uint2(wb[0], wb[1]);
+                *(uint2 *)(sQl + r * KS + c0) = make_uint2(wq[0], wq[1]);
+            } else {
+                *(uint32_t *)(sKl + r * KS + c0) = wa[0];
+                *(uint32_t *)(sKr + r * KS + c0) = wb[0];
+                *(uint32_t *)(sQl + r * KS + c0) = wq[0];
+            }
+        }
+        // K^ transposed: channel cc is row cc%32 of fragment tile cc/32; this thread's
+        // 8 rows are one 16-byte piece (step rg/2, lane half rg%2).
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+            const int cc = c0 + e;
+            const int pc = (cc >> 5) * 4 * 64 + (rg >> 1) * 64 + (cc & 31) + 32 * (rg & 1);
+            uint4 w;
+            w.x = pack_bf16x2(kh[e][0], kh[e][1]);
+            w.y = pack_bf16x2(kh[e][2], kh[e][3]);
+            w.z = pack_bf16x2(kh[e][4], kh[e][5]);
+            w.w = pack_bf16x2(kh[e][6], kh[e][7]);
+            ((uint4 *)(bp + Bk::oK))[pc] = w;
+        }
+        if (rg == 0) {
+#pragma unroll
+            for (int e = 0; e < CPT; ++e)
+                ((float *)(bp + Bk::oG))[c0 + e] = GATE == kGateNone ? 1.f : exp2_fast(gC[e]);
+        }
+    }
+    lds_barrier();
+
+    // ---- L and A_qk: the 10 lower-triangle 16x16 tiles of each (20 jobs) -----------
+    // Computed transposed, D[c][r] = K->[c] . (K<- or Q<-)[r], so that each lane holds
+    // four consecutive columns of one row.
+    for (int jb = wave; jb < 20; jb += 4) {
+        const bool isA = jb >= 10;
+        const int t = isA ? jb - 10 : jb;
+        const int ti = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
+        const int tj = t - ti * (ti + 1) / 2;
+        const uint16_t *src = isA ? sQl : sKl;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s)
+            d = mfma(frag(sKr, 16 * tj + l16, KS, 32 * s + 8 * lg),
+                     frag(src, 16 * ti + l16, KS, 32 * s + 8 * lg), d);
+        const int r = 16 * ti + l16, cb = 16 * tj + 4 * lg;
+        if (isA) {
+            store4(sAqk + r * kCS + cb, cb + 0 <= r ? d[0] : 0.f, cb + 1 <= r ? d[1] : 0.f,
+                   cb + 2 <= r ? d[2] : 0.f, cb + 3 <= r ? d[3] : 0.f);
+        } else {
+            const float br = sBeta[r];
+            const float v0 = cb + 0 < r ? br * d[0] : 0.f, v1 = cb + 1 < r ? br * d[1] : 0.f;
+            const float v2 = cb + 2 < r ? br * d[2] : 0.f, v3 = cb + 3 < r ? br * d[3] : 0.f;
+            if (ti == tj) *(float4 *)(sLd + (16 * ti + l16) * kDS + 4 * lg) = make_float4(v0, v1, v2, v3);
+            else store4(sX + r * kCS + cb, v0, v1, v2, v3);
+        }
+    }
+    lds_barrier();
+
+    // ---- At, diagonal blocks: forward substitution (wave 0) ------------------------
+    // Lane (block lg, column l16): x_r = [r == col] - sum_{i<r} L[r][i] x_i, which
+    // leaves x_r = 0 for r < col without any masking.
+    if (wave == 0) {
+        const float *Lb = sLd + 16 * lg * kDS;
+        float x[16];
+        float4 cur[4], nxt[4];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if (r + 1 < 16) {
+#pragma unroll
+                for (int i4 = 0; i4 < (r + 4) / 4; ++i4) nxt[i4] = *(const float4 *)(Lb + (r + 1) * kDS + 4 * i4);
+            }
+            float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
+                const float lv[4] = {cur[i4].x, cur[i4].y, cur[i4].z, cur[i4].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * i4 + e < r) ps[e] += lv[e] * x[4 * i4 + e];
+            }
+            x[r] = (r == l16 ? 1.f : 0.f) - ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) cur[i4] = nxt[i4];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            sLd[(16 * lg + r) * kDS + l16] = x[r];
+            sX[(16 * lg + r) * kCS + 16 * lg + l16] = __builtin_bit_cast(uint16_t, (__bf16)x[r]);
+        }
+    }
+    lds_barrier();
+
+    // ---- At, 32-row level (waves 0, 1): X_BA = -X_BB (L_BA X_AA) --------------------
+    if (wave < 2) {
+        const int a0 = 32 * wave, a1 = a0 + 16;
+        const bf16x4 fL = *(const bf16x4 *)(sX + (a1 + l16) * kCS + a0 + 4 * lg);
+        bf16x4 fXa;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            fXa[e] = __builtin_bit_cast(__bf16, sX[(a0 + 4 * lg + e) * kCS + a0 + l16]);
+        const f32x4 t = mfma16(fL, fXa, f32x4{0.f, 0.f, 0.f, 0.f});  // t[e] = T[4lg+e][l16]
+        const bf16x4 fXb = *(const bf16x4 *)(sX + (a1 + l16) * kCS + a1 + 4 * lg);
+        const f32x4 x = mfma16(fXb, to_bf16x4(t[0], t[1], t[2], t[3]), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            sX[(a1 + 4 * lg + e) * kCS + a0 + l16] = __builtin_bit_cast(uint16_t, (__bf16)(-x[e]));
+    }
+    lds_barrier();
+
+    // ---- At, 64-row level (waves 0-3, one 16x16 tile each) -------------------------
+    {
+        const int ti = wave >> 1, tj = wave & 1;
+        const f32x4 t = mfma(frag(sX, 32 + 16 * ti + l16, kCS, 8 * lg), frag_tr(sX, 0, kCS, 16 * tj, lane),
+                             f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            sT[(16 * ti + 4 * lg + e) * kTS + 16 * tj + l16] = __builtin_bit_cast(uint16_t, (__bf16)t[e]);
+        lds_barrier();
+        const f32x4 x = mfma(frag(sX, 32 + 16 * ti + l16, kCS, 32 + 8 * lg), frag_tr(sT, 0, kTS, 16 * tj, lane),
+                             f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            sX[(32 + 16 * ti + 4 * lg + e) * kCS + 16 * tj + l16] = __builtin_bit_cast(uint16_t, (__bf16)(-x[e]));
+    }
+    lds_barrier();
+
+    // ---- Ab = At Diag(beta), in place (diagonal blocks from the fp32 copy) ---------
+    {
+        const int r = tid >> 2, cbk = tid & 3, cb = 16 * cbk, b = r >> 4;
+        float a[16];
+        if (cbk == b) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const float4 x = *(const float4 *)(sLd + (16 * b + (r & 15)) * kDS + 4 * i4);
+                a[4 * i4 + 0] = x.x; a[4 * i4 + 1] = x.y; a[4 * i4 + 2] = x.z; a[4 * i4 + 3] = x.w;
+            }
+        } else if (cbk < b) {
+            const uint4 x0 = *(const uint4 *)(sX + r * kCS + cb), x1 = *(const uint4 *)(sX + r * kCS + cb + 8);
+            const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a[2 * i] = bf16_lo(w[i]), a[2 * i + 1] = bf16_hi(w[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) a[i] = 0.f;
+        }
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int ca = cb + 2 * i;
+            const float x0 = ca <= r ? a[2 * i] * sBeta[ca] : 0.f;
+            const float x1 = ca + 1 <= r ? a[2 * i + 1] * sBeta[ca + 1] : 0.f;
+            w[i] = pack_bf16x2(x0, x1);
+        }
+        *(uint4 *)(sX + r * kCS + cb) = make_uint4(w[0], w[1], w[2], w[3]);
+        *(uint4 *)(sX + r * kCS + cb + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+    lds_barrier();
+
+    // ---- Ao = A_qk Ab, in place: wave ti owns 16-row block ti ----------------------
+    {
+        const int ti = wave;
+        const bf16x8 b0 = frag(sAqk, 16 * ti + l16, kCS, 8 * lg);
+        const bf16x8 b1 = frag(sAqk, 16 * ti + l16, kCS, 32 + 8 * lg);
+        for (int tj = 0; tj <= ti; ++tj) {  // wave-uniform
+            f32x4 d = mfma(frag_tr(sX, 0, kCS, 16 * tj, lane), b0, f32x4{0.f, 0.f, 0.f, 0.f});
+            d = mfma(frag_tr(sX, 32, kCS, 16 * tj, lane), b1, d);
+            store4(sAqk + (16 * ti + l16) * kCS + 16 * tj + 4 * lg, d[0], d[1], d[2], d[3]);
+        }
+    }
+    lds_barrier();
+
+    // ---- W' = -Ab K<- (into the K-> array), Q~ = Q<- - Ao K<- (in place) ------------
+    {
+        bf16x8 fab[4][2], fao[4][2];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                fab[ti][s] = frag(sX, 16 * ti + l16, kCS, 32 * s + 8 * lg);
+                fao[ti][s] = frag(sAqk, 16 * ti + l16, kCS, 32 * s + 8 * lg);
+            }
+#pragma unroll
+        for (int tt = 0; tt < DK / 64; ++tt) {
+            const int tn = wave * (DK / 64) + tt;
+            const bf16x8 k0 = frag_tr(sKl, 0, KS, 16 * tn, lane);
+            const bf16x8 k1 = frag_tr(sKl, 32, KS, 16 * tn, lane);
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                f32x4 w = mfma(k0, fab[ti][0], f32x4{0.f, 0.f, 0.f, 0.f});
+                w = mfma(k1, fab[ti][1], w);
+                f32x4 o = mfma(k0, fao[ti][0], f32x4{0.f, 0.f, 0.f, 0.f});
+                o = mfma(k1, fao[ti][1], o);
+                const int r = 16 * ti + l16, cc = 16 * tn + 4 * lg;
+                store4(sKr + r * KS + cc, -w[0], -w[1], -w[2], -w[3]);
+                const uint2 qv = *(const uint2 *)(sQl + r * KS + cc);
+                store4(sQl + r * KS + cc, bf16_lo(qv.x) - o[0], bf16_hi(qv.x) - o[1],
+                       bf16_lo(qv.y) - o[2], bf16_hi(qv.y) - o[3]);
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- fragment tiles out: W', Q~ (2 row tiles x DK/16 steps), Ab, Ao (3 tiles) ---
+    constexpr int NPW = 2 * (DK / 16) * 64;
+    for (int pc = tid; pc < NPW; pc += kThreads) {
+        const int t = pc / ((DK / 16) * 64), s = (pc >> 6) % (DK / 16), ln = pc & 63;
+        const int r = 32 * t + (ln & 31), cc = 16 * s + 8 * (ln >> 5);
+        ((uint4 *)(bp + Bk::oW))[pc] = *(const uint4 *)(sKr + r * KS + cc);
+        ((uint4 *)(bp + Bk::oQ))[pc] = *(const uint4 *)(sQl + r * KS + cc);
+    }
+    for (int pc = tid; pc < 3 * 128; pc += kThreads) {
+        const int tau = pc >> 7, s = (pc >> 6) & 1, ln = pc & 63;
+        const int r = (tau ? 32 : 0) + (ln & 31), cc = (tau == 2 ? 32 : 0) + 16 * s + 8 * (ln >> 5);
+        ((uint4 *)(bp + Bk::oAb))[pc] = *(const uint4 *)(sX + r * kCS + cc);
+        ((uint4 *)(bp + Bk::oAo))[pc] = *(const uint4 *)(sAqk + r * kCS + cc);
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// State kernel
+// ---------------------------------------------------------------------------------
+template <int DK>
+struct StateSmem {
+    static constexpr int KS = DK + 8;
+    static constexpr int oS = 0;                   // S bf16 [32 dv][KS]
+    static constexpr int oV = oS + kDVT * KS * 2;  // V bf16 [64][kVS]
+    static constexpr int oVn = oV + kC * kVS * 2;  // V_new^T bf16 [32 dv][kCS]
+    static constexpr int oO = oVn + kDVT * kCS * 2;  // output staging, 2 x bf16 [32][kVS]
+    static constexpr int oG = oO + 2 * 32 * kVS * 2;  // gamma_C, 2 x fp32 [DK] (chunk parity)
+    static constexpr int bytes = oG + 2 * DK * 4;
+};
+
+// Operands of one chunk for one wave, loaded two chunks ahead.
+template <int DK>
+struct Pre {
+    uint4 P[DK / 16];  // W' (waves 0, 1) or Q~ (waves 2, 3): this wave's 32 rows
+    uint4 A[4];        // Ab or Ao tiles of those rows (2 steps for rows 0-31, 4 for 32-63)
+    uint4 K[4];        // K^ tile of dk rows 32w.. (waves w < DK/32)
+    uint4 V;           // one 16-byte piece of the value tile
+    float4 G;          // wave 0, lanes 0..DK/4-1: gamma_C[4 lane..+3]
+};
+// Fewest loads any wave issues per chunk (rows 0-31 take two A steps; waves past
+// DK/32 take no K^ tile); waiting until at most this many are in flight therefore
+// completes every load of the chunk before, whatever the wave.
+template <int DK>
+constexpr int kMinLoadsPerChunk = DK / 16 + 2 + (DK / 32 >= 4 ? 4 : 0) + 1;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// vmcnt(N) alone (expcnt and lgkmcnt left at their maxima), gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
+// Chunks whose operands are in flight ahead of the one being computed.
+constexpr int kDepth = 2;
+
+template <int DK>
+__global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
+    using L = StateSmem<DK>;
+    using Bk = Blk<DK>;
+    constexpr int KS = L::KS;
+    constexpr int NSW = DK / 32;  // waves owning a 32x32 S^T tile
+
+    __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+    uint16_t *sS = (uint16_t *)(smem + L::oS);
+    uint16_t *sV = (uint16_t *)(smem + L::oV);
+    uint16_t *sVn = (uint16_t *)(smem + L::oVn);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int H = p.H, DV = p.dv;
+    const int lin = xcd_linear_index(blockIdx.x, gridDim.x);
+    const int tile = lin % p.n_tiles;
+    const int h = (lin / p.n_tiles) % H;
+    const int n = lin / (p.n_tiles * H);
+    const int j0 = tile * kDVT;
+    long t0, t1;
+    seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
+    int nck = (int)((t1 - t0 + kC - 1) / kC);
+    long cbase;
+    if (p.coff) {
+        cbase = p.coff[n];
+        const long room = p.max_chunks - cbase;  // only short of nck for malformed offsets
+        nck = (int)(room < 0 ? 0 : (room < nck ? room : nck));
+    } else {
+        cbase = (long)n * p.nc;
+    }
+
+    const int rt = wave & 1;      // 32-row tile of the chunk
+    const bool vw = wave < 2;     // V_new waves (W', Ab); waves 2, 3: output (Q~, Ao)
+    uint16_t *sO = (uint16_t *)(smem + L::oO) + (wave & 1) * 32 * kVS;
+
+    // state: wave w < NSW holds S^T[dk 32w..+31][dv 0..31]; register 4q+e is
+    // S[dv l32][dk 32w + 8q + 4lh + e]
+    f32x16 ST = {};
+    if (wave < NSW) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int dk = 32 * wave + 8 * q + 4 * lh;
+            float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (p.S0) s4 = *(const float4 *)(p.S0 + (((size_t)n * H + h) * DV + j0 + l32) * DK + dk);
+            ST[4 * q + 0] = s4.x; ST[4 * q + 1] = s4.y; ST[4 * q + 2] = s4.z; ST[4 * q + 3] = s4.w;
+            store4(sS + l32 * KS + dk, s4.x, s4.y, s4.z, s4.w);
+        }
+    }
+
+    const int vr = tid >> 2, vc = 8 * (tid & 3);
+    // Loads of one chunk in two batches: the W'/Q~ tile first, the rest later in the
+    // step, so that the memory pipeline is fed while the wave computes.
+    auto load_p = [&](Pre<DK> &x, int c) {
+        const char *bp = p.blk + ((size_t)(cbase + c) * H + h) * Bk::bytes;
+        const uint4 *pw = (const uint4 *)(bp + (vw ? Bk::oW : Bk::oQ)) + rt * (DK / 16) * 64 + lane;
+#pragma unroll
+        for (int s = 0; s < DK / 16; ++s) x.P[s] = pw[s * 64];
+    };
+    auto load_rest = [&](Pre<DK> &x, int c) {
+        const char *bp = p.blk + ((size_t)(cbase + c) * H + h) * Bk::bytes;
+        const uint4 *pa = (const uint4 *)(bp + (vw ? Bk::oAb : Bk::oAo)) + rt * 128 + lane;
+        x.A[0] = pa[0];
+        x.A[1] = pa[64];
+        if (rt) {
+            x.A[2] = pa[128];
+            x.A[3] = pa[192];
+        }
+        if (wave < NSW) {
+            const uint4 *pk = (const uint4 *)(bp + Bk::oK) + wave * 256 + lane;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) x.K[s] = pk[s * 64];
+        }
+        const long tok = t0 + (long)c * kC + vr;
+        x.V = *(const uint4 *)(p.v + ((size_t)(tok < t1 ? tok : t1 - 1) * H + h) * DV + j0 + vc);
+        if (wave == 0 && lane < DK / 4) x.G = ((const float4 *)(bp + Bk::oG))[lane];
+    };
+
+    // Output rows of the previous chunk, staged in LDS by this wave: 16 rows x 64 bytes
+    // per store instruction.
+    auto store_out = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = 16 * i + (lane >> 2), q4 = lane & 3;
+            const long tok = t0 + (long)c * kC + 32 * rt + r;
+            const uint4 o = *(const uint4 *)(sO + r * kVS + 8 * q4);
+            if (tok < t1) *(uint4 *)(p.O + ((size_t)tok * H + h) * DV + j0 + 8 * q4) = o;
+        }
+    };
+
+    auto step = [&](int c, Pre<DK> &x, Pre<DK> &nx) {
+        wait_vmcnt<(kDepth - 1) * kMinLoadsPerChunk<DK>>();  // operands of chunk c have arrived
+        float *sG = (float *)(smem + L::oG) + (c & 1) * DK;
+        if (wave == 0 && lane < DK / 4) ((float4 *)sG)[lane] = x.G;
+        {
+            // rows past the end of the sequence are zero (branch-free: a lane mask)
+            const uint32_t keep = 0u - (uint32_t)(t0 + (long)c * kC + vr < t1);
+            *(uint4 *)(sV + vr * kVS + vc) = make_uint4(x.V.x & keep, x.V.y & keep, x.V.z & keep, x.V.w & keep);
+        }
+        if (!vw && c > 0) store_out(c - 1);
+        const int cn = c + kDepth < nck ? c + kDepth : nck - 1;
+        load_p(nx, cn);
+        lds_barrier();  // value tile, gamma_C and S of chunk c visible
+
+        // LDS operands are all read before the products so that their latency overlaps.
+        bf16x8 fv[4], fs[DK / 16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (i < 2 || rt) fv[i] = frag_tr32(sV, 16 * i, kVS, 0, lane);
+#pragma unroll
+        for (int s = 0; s < DK / 16; ++s) fs[s] = frag(sS, l32, KS, 16 * s + 8 * lh);
+        f32x16 acc = {};
+        if (vw) {
+            // V_new = Ab V + W' S^T; register 4q+e is V_new[row 32rt + 8q + 4lh + e][dv l32]
+            acc = mfma32x32(as_bf16x8(x.A[0]), fv[0], acc);
+            acc = mfma32x32(as_bf16x8(x.A[1]), fv[1], acc);
+            if (rt) {
+                acc = mfma32x32(as_bf16x8(x.A[2]), fv[2], acc);
+                acc = mfma32x32(as_bf16x8(x.A[3]), fv[3], acc);
+            }
+#pragma unroll
+            for (int s = 0; s < DK / 16; ++s) acc = mfma32x32(as_bf16x8(x.P[s]), fs[s], acc);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                store4(sVn + l32 * kCS + 32 * rt + 8 * q + 4 * lh, acc[4 * q + 0], acc[4 * q + 1],
+                       acc[4 * q + 2], acc[4 * q + 3]);
+        } else {
+            // O^T = V^T Ao^T + S Q~^T (operands swapped); register 4q+e is
+            // O[row 32rt + l32][dv 8q + 4lh + e]
+            acc = mfma32x32(fv[0], as_bf16x8(x.A[0]), acc);
+            acc = mfma32x32(fv[1], as_bf16x8(x.A[1]), acc);
+            if (rt) {
+                acc = mfma32x32(fv[2], as_bf16x8(x.A[2]), acc);
+                acc = mfma32x32(fv[3], as_bf16x8(x.A[3]), acc);
+            }
+#pragma unroll
+            for (int s = 0; s < DK / 16; ++s) acc = mfma32x32(fs[s], as_bf16x8(x.P[s]), acc);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                store4(sO + l32 * kVS + 8 * q + 4 * lh, acc[4 * q + 0], acc[4 * q + 1],
+                       acc[4 * q + 2], acc[4 * q + 3]);
+        }
+        load_rest(nx, cn);
+        lds_barrier();  // V_new^T visible
+
+        // S <- S Diag(gamma_C) + V_new^T K^ (transposed: S^T tile = K^T-tile V_new)
+        if (wave < NSW) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 g = *(const float4 *)(sG + 32 * wave + 8 * q + 4 * lh);
+                ST[4 * q + 0] *= g.x; ST[4 * q + 1] *= g.y;
+                ST[4 * q + 2] *= g.z; ST[4 * q + 3] *= g.w;
+            }
+            bf16x8 fn[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) fn[s] = frag(sVn, l32, kCS, 16 * s + 8 * lh);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ST = mfma32x32(as_bf16x8(x.K[s]), fn[s], ST);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                store4(sS + l32 * KS + 32 * wave + 8 * q + 4 * lh, ST[4 * q + 0], ST[4 * q + 1],
+                       ST[4 * q + 2], ST[4 * q + 3]);
+        }
+    };
+
+    if (nck > 0) {
+        Pre<DK> buf[kDepth + 1];
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) {
+            load_p(buf[u], u < nck ? u : nck - 1);
+            load_rest(buf[u], u < nck ? u : nck - 1);
+            asm volatile("" ::: "memory");  // keep the chunks' loads in chunk order
+        }
+        static_assert(kDepth == 2, "the unrolled loop below rotates three operand sets");
+        // Whole triples of steps, then the tail: every path through this code runs the
+        // steps in order with nothing skipped, so the compiler's count of memory
+        // operations in flight stays exact and the waits above are the only ones.
+        int c = 0;
+        for (; c + 3 <= nck; c += 3) {
+            step(c, buf[0], buf[2]);
+            step(c + 1, buf[1], buf[0]);
+            step(c + 2, buf[2], buf[1]);
+        }
+        if (c < nck) {
+            step(c, buf[0], buf[2]);
+            if (c + 1 < nck) step(c + 1, buf[1], buf[0]);
+        }
+        if (!vw) store_out(nck - 1);
+    }
+
+    if (p.Sf && wave < NSW) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int dk = 32 * wave + 8 * q + 4 * lh;
+            *(float4 *)(p.Sf + (((size_t)n * H + h) * DV + j0 + l32) * DK + dk) =
+                make_float4(ST[4 * q + 0], ST[4 * q + 1], ST[4 * q + 2], ST[4 * q + 3]);
+        }
+    }
+}
+
+int blk_bytes(int dk) { return dk == 128 ? Blk<128>::bytes : Blk<64>::bytes; }
+
+// Workspace: [error flag header][chunk offsets (packed sequences)][blocks].
+void split_layout(const FwdArgs &a, int N, bool varlen, size_t &coff_off, size_t &blk_off,
+                  int &nc, int &max_chunks, size_t &total) {
+    const int ncT = (a.T + kC - 1) / kC;
+    coff_off = kWorkspaceHeader;
+    if (varlen) {
+        nc = 0;
+        max_chunks = ncT + N;
+        blk_off = coff_off + (((size_t)(N + 1) * 4 + 255) / 256) * 256;
+    } else {
+        nc = ncT;
+        max_chunks = N * ncT;
+        blk_off = coff_off;
+    }
+    total = blk_off + (size_t)a.H * max_chunks * blk_bytes(a.dk);
+}
+
+}  // namespace
+
+bool kda_split_supported(const FwdArgs &a) {
+    return a.dtype == 1 && a.a == nullptr && a.b == nullptr && a.C == kC &&
+           (a.dk == 64 || a.dk == 128) && a.dv % kDVT == 0;
+}
+
+size_t kda_split_workspace_bytes(const FwdArgs &a, int n_seq_eff) {
+    size_t coff_off, blk_off, total;
+    int nc, max_chunks;
+    split_layout(a, n_seq_eff, a.cu_seqlens != nullptr, coff_off, blk_off, nc, max_chunks, total);
+    return total;
+}
+
+int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
+    const bool varlen = a.cu_seqlens != nullptr;
+    size_t coff_off, blk_off, total;
+    int nc, max_chunks;
+    split_layout(a, n_seq_eff, varlen, coff_off, blk_off, nc, max_chunks, total);
+    SplitParams sp;
+    sp.q = (const bf16 *)a.q; sp.k = (const bf16 *)a.k; sp.v = (const bf16 *)a.v;
+    sp.la = a.log_alpha; sp.beta = a.beta; sp.S0 = a.S0;
+    sp.O = (bf16 *)a.O; sp.Sf = a.S_final; sp.cu = a.cu_seqlens;
+    char *ws = (char *)a.workspace;
+    sp.err = (int *)ws;
+    sp.coff = varlen ? (int32_t *)(ws + coff_off) : nullptr;
+    sp.blk = ws + blk_off;
+    sp.total = (long)a.B * a.T;
+    sp.H = a.H; sp.T = a.T; sp.dv = a.dv; sp.n_seq = n_seq_eff; sp.n_tiles = a.dv / kDVT;
+    sp.nc = nc; sp.max_chunks = max_chunks;
+
+    if (varlen) hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kThreads), 0, s, sp);
+    const dim3 grid_prep((unsigned)a.H * (unsigned)max_chunks);
+    const dim3 grid_state((unsigned)(n_seq_eff * a.H * sp.n_tiles));
+#define GDR_PREP(DK, G) hipLaunchKernelGGL((kda_prep_kernel<DK, G>), grid_prep, dim3(kThreads), 0, s, sp)
+    if (a.dk == 128) {
+        if (a.gate == kGateChannel) GDR_PREP(128, kGateChannel);
+        else if (a.gate == kGateHead) GDR_PREP(128, kGateHead);
+        else GDR_PREP(128, kGateNone);
+        hipLaunchKernelGGL((kda_state_kernel<128>), grid_state, dim3(kThreads), 0, s, sp);
+    } else {
+        if (a.gate == kGateChannel) GDR_PREP(64, kGateChannel);
+        else if (a.gate == kGateHead) GDR_PREP(64, kGateHead);
+        else GDR_PREP(64, kGateNone);
+        hipLaunchKernelGGL((kda_state_kernel<64>), grid_state, dim3(kThreads), 0, s, sp);
+    }
+#undef GDR_PREP
+    return (int)hipGetLastError();
+}
+
+}  // namespace gdr

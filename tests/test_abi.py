@@ -46,9 +46,14 @@ def test_version_and_status_strings(lib):
 
 def test_workspace_sizes(lib):
     ws = gdr.workspace_bytes
-    # the fused KDA-family kernel needs only the error-flag header
-    assert ws(2, 32, 8192, 128, 128) == 256
-    assert ws(4, 16, 4096, 128, 128, gate=gdr.GATE_HEAD) == 256
+    # KDA family (bf16): the error-flag header plus one 61952-byte block per
+    # (chunk, head) at dk = 128 (37120 at dk = 64) ...
+    assert ws(2, 32, 8192, 128, 128) == 256 + 32 * (2 * 128) * 61952
+    assert ws(4, 16, 4096, 128, 128, gate=gdr.GATE_HEAD) == 256 + 16 * (4 * 64) * 61952
+    assert ws(1, 2, 100, 64, 64, gate=gdr.GATE_NONE) == 256 + 2 * 2 * 37120
+    # ... and, for packed sequences, the chunk offsets and room for every sequence
+    # to end in a partial chunk
+    assert ws(1, 32, 32768, 128, 128, n_seq=8) == 256 + 256 + 32 * (512 + 8) * 61952
     # the generic fp32 / DPLR kernel needs per-workgroup scratch
     g = ws(1, 16, 16384, 128, 128, has_ab=True)
     assert g == 256 + 1 * 16 * 4 * 7 * 64 * 128 * 4
@@ -64,7 +69,7 @@ def test_workspace_sizes(lib):
 def _call(lib, q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), a=None, b=None,
           la=FAKE + (3 << 30), beta=FAKE + (4 << 30), S0=None, O=FAKE + (5 << 30),
           Sf=FAKE + (6 << 30), cu=None, n_seq=0, B=1, H=2, T=64, dk=128, dv=128, C=64,
-          dtype=1, gate=2, ws=FAKE + (7 << 30), ws_bytes=256):
+          dtype=1, gate=2, ws=FAKE + (7 << 30), ws_bytes=1 << 20):
     return lib.gdr_chunk_fwd(P(q), P(k), P(v), P(a), P(b), P(la), P(beta), P(S0), P(O), P(Sf),
                              P(cu), n_seq, B, H, T, dk, dv, C, dtype, gate, P(ws), ws_bytes, None)
 
