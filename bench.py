@@ -1,18 +1,24 @@
 """Benchmark: chunkwise KDA forward, B=2 H=32 T=8192 dk=dv=128 C=64, bf16, one MI355X.
 
-One step = one gdr_chunk_fwd call over the whole batch (all of the hot path:
-gate prefix sums, UT transform, WY factors, serial state pass and output), on
-seeded synthetic inputs already resident in HBM.  Prints one JSON line.
+One step = one gdr_chunk_fwd call over the whole batch: the whole hot path (gate
+prefix sums, UT transform and WY factors in the chunk-parallel kernel; the serial
+state pass and the output in the state kernel), on seeded synthetic inputs already
+resident in HBM.  Prints one JSON line.
 
-Throughput is tokens/s (B*T / step time; a token carries all H heads).  The
-roofline entry is for the fused KDA kernel: algorithmic bytes per launch
-(read q, k, v, log alpha, beta; write O and S_final) over its mean duration
-measured with HIP events on the launch stream, against 8 TB/s.  The CPU
-baseline is the fp64 oracle timed on the host cores on the same workload.
+Throughput is tokens/s (B*T / mean step time; a token carries all H heads).  The
+roofline entry treats the call (its two kernels) as the unit: algorithmic bytes
+per call (read q, k, v, log alpha, beta; write O and S_final) over the mean call
+duration measured with HIP events on the launch stream, against 8 TB/s.  HBM
+traffic and MFMA-busy figures come from the committed rocprofv3 counter summary,
+and only while the kernel source still matches the one it was measured on.  The
+CPU baseline is the fp64 oracle on the host cores.
 """
 import argparse
+import hashlib
 import json
 import os
+import platform
+import re
 import sys
 import time
 
@@ -23,37 +29,41 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 WORKLOAD = "kda"
-KERNEL_SOURCES = ["chunkwise_gated_delta_amd/csrc/gdr_kda_mfma.hip"]
-COUNTERS_FILE = "profiles/kda_mfma_kernel__kda_B2_H32_T8192_d128__counters.md"
+KERNEL_SOURCES = ["chunkwise_gated_delta_amd/csrc/gdr_kda_split.hip"]
+COUNTERS_FILE = "profiles/kda_split__kda_B2_H32_T8192_d128__counters.md"
 
 
-def counter_traffic():
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary.
-
-    The summary records the sha256 of the kernel source it was measured on; when the
-    source has changed since, the figure no longer describes this kernel and None is
-    returned.
-    """
-    import hashlib
-    import re
-
-    try:
-        text = open(os.path.join(ROOT, COUNTERS_FILE)).read()
-    except OSError:
-        return None
+def kernel_source_sha():
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_counters():
+    """Figures from the committed counter summary, or {} when the kernels changed since.
+
+    The summary records the sha256 of the kernel source it was measured on and a few
+    machine-readable lines `key: value`.
+    """
+    try:
+        text = open(os.path.join(ROOT, COUNTERS_FILE)).read()
+    except OSError:
+        return {}
     m_sha = re.search(r"Kernel source sha256 `([0-9a-f]{64})`", text)
-    m_bytes = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    if not (m_sha and m_bytes) or m_sha.group(1) != h.hexdigest():
-        return None
-    return int(m_bytes.group(1))
+    if not m_sha or m_sha.group(1) != kernel_source_sha():
+        return {}
+    out = {}
+    for key in ("traffic_bytes_per_launch", "mfma_busy_frac"):
+        m = re.search(rf"^{key}: ([0-9.eE+-]+)$", text, re.M)
+        if m:
+            out[key] = float(m.group(1))
+    return out
 
 
 def algorithmic_counts(P):
-    """(bytes, flops) one launch must move / perform at the algorithmic minimum.
+    """(bytes, flops) one call must move / perform at the algorithmic minimum.
 
     Bytes per token-head: q, k, v, O at 2*d each (bf16), log alpha 4*dk, beta 4;
     plus S_final (and S0 if given) once per (sequence, head).
@@ -70,7 +80,7 @@ def algorithmic_counts(P):
     return th * per_th + state, flops
 
 
-def time_gpu(P, steps, warmup):
+def time_gpu(P, steps, warmup, cold_steps):
     import torch
 
     from chunkwise_gated_delta_amd import gdr
@@ -87,25 +97,71 @@ def time_gpu(P, steps, warmup):
         call()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    ev0, ev1 = ev(), ev()
     per = []
-    t_wall = time.perf_counter()
     ev0.record(stream)
     for _ in range(steps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = ev(), ev()
         e0.record(stream)
         call()
         e1.record(stream)
         per.append((e0, e1))
     ev1.record(stream)
     torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
     total_ms = ev0.elapsed_time(ev1)
     launch_ms = sorted(a.elapsed_time(b) for a, b in per)
-    return total_ms / steps, launch_ms, t_wall, out, fin
+    # cold: a 512 MB write between calls evicts the 256 MB memory-side cache
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(cold_steps):
+        scrub.fill_(i & 0xFF)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        cold.append((e0, e1))
+    torch.cuda.synchronize()
+    cold_ms = sorted(a.elapsed_time(b) for a, b in cold)
+    del scrub
+    return total_ms / steps, launch_ms, cold_ms, out, fin
+
+
+def machine_context():
+    """Measured bf16 GEMM rate and device copy bandwidth on this GPU (context only)."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    return {"bf16_gemm_8192_tflops": gemm_tflops, "copy_1GiB_read_plus_write_gbs": copy_gbs}
 
 
 def cpu_baseline(P, n_threads):
+    """fp64 oracle on the whole workload (all host threads) and on a 2-chain sample (1 thread)."""
     import numpy as np
     import torch
 
@@ -118,15 +174,31 @@ def cpu_baseline(P, n_threads):
     t = time.perf_counter()
     O, Sf = oracle.recurrence(**args, n_threads=n_threads)
     dt = time.perf_counter() - t
-    return dt, O, Sf, args
+    t = time.perf_counter()
+    oracle.recurrence(**args, chains=[(0, 0), (1, 5)], n_threads=1)
+    dt1 = time.perf_counter() - t
+    return dt, dt1, O, Sf
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cold-steps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the GEMM / copy context measurements")
     ap.add_argument("--copy-cal", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (calibrates the HBM "
                          "traffic counters: FETCH_SIZE/WRITE_SIZE per byte actually moved)")
@@ -144,7 +216,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); each (sequence, head) "
-              "chain is independent, so N GPUs would each run this kernel on H/N heads.",
+              "chain is independent, so N GPUs would each run this path on H/N heads.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -155,11 +227,14 @@ def main():
 
     P = inputs.make_problem(WORKLOAD)
     alg_bytes, alg_flops = algorithmic_counts(P)
-    ms, launch_ms, wall, out, fin = time_gpu(P, args.steps, args.warmup)
-    kern_ms = float(np.mean(launch_ms))
+    ms, launch_ms, cold_ms, out, fin = time_gpu(P, args.steps, args.warmup, args.cold_steps)
+    call_ms = float(np.mean(launch_ms))
     tokens = P.B * P.T
-    achieved_gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
-    tflops = alg_flops / (kern_ms * 1e-3) / 1e12
+    achieved_gbs = alg_bytes / (call_ms * 1e-3) / 1e9
+    tflops = alg_flops / (call_ms * 1e-3) / 1e12
+    cc = committed_counters()
+    traffic = cc.get("traffic_bytes_per_launch")
+    pct = lambda xs, f: xs[min(len(xs) - 1, int(f * len(xs)))]
 
     result = {
         "metric": "tokens/s + MFMA util % for KDA chunk fwd, T=8192 H=32 d=128, 1xMI355X",
@@ -180,27 +255,33 @@ def main():
                    "chunk": P.chunk, "parallelism": "none (one GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": counter_traffic(),
-                     "kernel": "kda_mfma_kernel<128, channel gate>",
-                     "kernel_ms_mean": kern_ms,
-                     "kernel_ms_median": launch_ms[len(launch_ms) // 2],
-                     "kernel_ms_p10": launch_ms[len(launch_ms) // 10],
-                     "kernel_ms_p90": launch_ms[(9 * len(launch_ms)) // 10],
+                     "traffic": None if traffic is None else int(traffic),
+                     "kernel": "gdr_chunk_fwd call: kda_prep_kernel<128, channel gate> + "
+                               "kda_state_kernel<128>",
+                     "call_ms_mean": call_ms, "call_ms_median": pct(launch_ms, 0.5),
+                     "call_ms_p10": pct(launch_ms, 0.1), "call_ms_p90": pct(launch_ms, 0.9),
+                     "call_ms_cold_mean": float(np.mean(cold_ms)) if cold_ms else None,
                      "alg_bytes_per_launch": alg_bytes},
         "mfma": {"alg_flops_per_launch": alg_flops, "achieved_tflops": tflops,
-                 "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "frac": tflops / BF16_MFMA_PEAK_TFLOPS},
+                 "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "frac": tflops / BF16_MFMA_PEAK_TFLOPS,
+                 "counter_busy_frac": cc.get("mfma_busy_frac")},
     }
+    if not args.no_context:
+        result["context"] = machine_context()
     if not args.no_cpu:
         import oracle
 
         n_threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or oracle.max_threads()
-        dt, Oref, Sref, _ = cpu_baseline(P, n_threads)
+        dt, dt1, Oref, Sref = cpu_baseline(P, n_threads)
         Og = out.to(torch.float64).cpu().numpy()
         Sg = fin.to(torch.float64).cpu().numpy()
         result["cpu_baseline"] = {
             "value": tokens / dt, "unit": "tokens/s", "cores": n_threads, "kind": "oracle",
             "sample": f"the whole workload ({P.B * P.H} (sequence, head) chains x {P.T} tokens), "
-                      f"fp64 token recurrence, {dt:.2f} s"}
+                      f"fp64 token recurrence, {dt:.2f} s on {n_threads} threads; one thread: "
+                      f"2 chains in {dt1:.2f} s = {2 * P.T / dt1 / P.H:.0f} tokens/s "
+                      f"(a token = all {P.H} heads)",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count()}
         result["parity"] = {
             "O_rel_err": float(np.max(np.abs(Og - Oref)) / np.max(np.abs(Oref))),
             "S_final_rel_err": float(np.max(np.abs(Sg - Sref)) / np.max(np.abs(Sref))),

@@ -62,14 +62,6 @@ FwdArgs make_args(int B, int H, int T, int dk, int dv, int C, int n_seq, int dty
     return a;
 }
 
-bool use_fused() {
-    static const int on = [] {
-        const char *s = std::getenv("GDR_KDA_FUSED");
-        return (s && s[0] == '1') ? 1 : 0;
-    }();
-    return on != 0;
-}
-
 size_t workspace_for(const FwdArgs &a, int n_seq_eff) {
     if (gdr::kda_split_supported(a)) return gdr::kda_split_workspace_bytes(a, n_seq_eff);
     return gdr::generic_workspace_bytes(a, n_seq_eff);
@@ -142,13 +134,10 @@ int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
 
     hipStream_t s = (hipStream_t)stream;
     const bool split = gdr::kda_split_supported(args);
-    const bool fused = split && use_fused();
     if (trace_enabled())
         std::fprintf(stderr, "[gdr] %s B=%d H=%d T=%d N=%d dk=%d dv=%d C=%d dtype=%d gate=%d ws=%zu\n",
-                     fused ? "kda_fused" : (split ? "kda_split" : "generic"), B, H, T, N, dk, dv, C,
-                     dtype, gate, need);
-    const int rc = fused ? gdr::launch_kda_mfma(args, N, s)
-                         : (split ? gdr::launch_kda_split(args, N, s) : gdr::launch_generic(args, N, s));
+                     split ? "kda_split" : "generic", B, H, T, N, dk, dv, C, dtype, gate, need);
+    const int rc = split ? gdr::launch_kda_split(args, N, s) : gdr::launch_generic(args, N, s);
     return rc == 0 ? GDR_OK : GDR_ERR_HIP;
 }
 

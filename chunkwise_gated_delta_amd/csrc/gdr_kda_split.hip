@@ -150,7 +150,7 @@ struct PrepSmem {
 };
 
 template <int DK, int GATE>
-__global__ __launch_bounds__(kThreads) void kda_prep_kernel(SplitParams p) {
+__global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
     using L = PrepSmem<DK>;
     using Bk = Blk<DK>;
     constexpr int KS = L::KS;
@@ -174,31 +174,49 @@ __global__ __launch_bounds__(kThreads) void kda_prep_kernel(SplitParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
     const int H = p.H;
-    const int h = blockIdx.x % H;
-    const int j = blockIdx.x / H;
-    int n, c;
-    if (!chunk_of(p, j, n, c)) return;  // workgroup-uniform
-    long t0, t1;
-    seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
-    const long tok0 = t0 + (long)c * kC;
-    const int m = (int)((t1 - tok0) < kC ? (t1 - tok0) : kC);  // >= 1
-    char *bp = p.blk + ((size_t)j * H + h) * Bk::bytes;
-
-    // ---- loads: thread (rg, cg) owns rows 8rg..8rg+7, channels CPT*cg..+CPT-1 ------
-    // Every load is issued unconditionally (rows past the end of the sequence re-read
-    // the last row) so that all of them are in flight at once; those rows are then
-    // zeroed, which makes them exact identity steps.
+    const int njobs = H * p.max_chunks;
     const int rg = tid >> 5, cg = tid & 31, c0 = CPT * cg;
+
+    // The workgroup is persistent: it walks jobs (chunk j, head h), job g = j H + h,
+    // with stride gridDim.x.  The raw inputs of the next job are loaded while the
+    // current one is processed (from the moment its own inputs have been consumed).
+    struct Job {
+        int g, m;
+        long tok0;
+        bool ok;
+    };
+    auto decode = [&](int g) {
+        Job J;
+        J.g = g;
+        J.tok0 = 0;
+        J.m = 1;
+        int n = 0, c = 0;
+        J.ok = g < njobs && chunk_of(p, g / H, n, c);
+        if (J.ok) {
+            long t0, t1;
+            seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
+            J.tok0 = t0 + (long)c * kC;
+            J.m = (int)((t1 - J.tok0) < kC ? (t1 - J.tok0) : kC);  // >= 1
+        }
+        return J;
+    };
+
+    // Thread (rg, cg) owns rows 8rg..8rg+7, channels CPT*cg..+CPT-1.  Every load is
+    // issued unconditionally (rows past the end of the sequence re-read its last row)
+    // so that all of them are in flight at once; those rows are zeroed when consumed,
+    // which makes them exact identity steps.
     uint32_t kw[8][WPR], qw[8][WPR];
     float lw[8][CPT];
-    {
+    float beta_r = 0.f, lah = 0.f;
+    auto issue = [&](const Job &J) {
+        const int h = J.g % H;
         const size_t rs = (size_t)H * DK;
-        const bf16 *kb = p.k + ((size_t)tok0 * H + h) * DK + c0;
-        const bf16 *qb = p.q + ((size_t)tok0 * H + h) * DK + c0;
-        const float *lb = p.la + ((size_t)tok0 * H + h) * DK + c0;
+        const bf16 *kb = p.k + ((size_t)J.tok0 * H + h) * DK + c0;
+        const bf16 *qb = p.q + ((size_t)J.tok0 * H + h) * DK + c0;
+        const float *lb = p.la + ((size_t)J.tok0 * H + h) * DK + c0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int r = 8 * rg + i, rr = r < m ? r : m - 1;
+            const int r = 8 * rg + i, rr = r < J.m ? r : J.m - 1;
             if constexpr (WPR == 2) {
                 const uint2 xk = *(const uint2 *)(kb + rr * rs), xq = *(const uint2 *)(qb + rr * rs);
                 kw[i][0] = xk.x; kw[i][WPR - 1] = xk.y;
@@ -217,324 +235,345 @@ __global__ __launch_bounds__(kThreads) void kda_prep_kernel(SplitParams p) {
                 }
             }
         }
-    }
-    const int rb0 = tid < kC ? (tid < m ? tid : m - 1) : 0;
-    float beta_r = p.beta[(size_t)(tok0 + rb0) * H + h];
-    float lah = 0.f;
-    if (GATE == kGateHead) lah = p.la[(size_t)(tok0 + (lane < m ? lane : m - 1)) * H + h];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (8 * rg + i >= m) {
-#pragma unroll
-            for (int w = 0; w < WPR; ++w) kw[i][w] = qw[i][w] = 0u;
-#pragma unroll
-            for (int e = 0; e < CPT; ++e) lw[i][e] = 0.f;
-        }
-    }
-    if (tid < kC) sBeta[tid] = tid < m ? beta_r : 0.f;
-    if (GATE == kGateHead && wave == 0) {
-        float x = lane < m ? lah * kLog2e : 0.f;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
-        }
-        sG[lane] = x;
-        if (lane == 63) sG[64] = x;
-    }
-    // The products read whole 32-wide contraction blocks of X and A_qk, so everything
-    // not written below (above the diagonal) must be zero.
-    for (int i = tid; i < 2 * kC * kCS * 2 / 16; i += kThreads)
-        ((uint4 *)(smem + L::oX))[i] = make_uint4(0u, 0u, 0u, 0u);
+        const int rb0 = tid < kC ? (tid < J.m ? tid : J.m - 1) : 0;
+        beta_r = p.beta[(size_t)(J.tok0 + rb0) * H + h];
+        if (GATE == kGateHead) lah = p.la[(size_t)(J.tok0 + (lane < J.m ? lane : J.m - 1)) * H + h];
+    };
 
-    // ---- gate: prefix sums (log2 domain) -------------------------------------------
-    float g[8][CPT], gC[CPT];
-    if (GATE == kGateChannel) {
-        float run[CPT];
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) run[e] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int e = 0; e < CPT; ++e) {
-                run[e] += lw[i][e] * kLog2e;
-                g[i][e] = run[e];
-            }
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) sTot[rg * DK + c0 + e] = run[e];
-    }
-    lds_barrier();
-    if (GATE == kGateChannel) {
-        float carry[CPT], tot[CPT];
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) carry[e] = tot[e] = 0.f;
-#pragma unroll
-        for (int r2 = 0; r2 < 8; ++r2)
-#pragma unroll
-            for (int e = 0; e < CPT; ++e) {
-                const float t = sTot[r2 * DK + c0 + e];
-                tot[e] += t;
-                carry[e] += r2 < rg ? t : 0.f;
-            }
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) {
-            gC[e] = tot[e];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) g[i][e] += carry[e];
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) {
-            gC[e] = GATE == kGateHead ? sG[64] : 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) g[i][e] = GATE == kGateHead ? sG[8 * rg + i] : 0.f;
-        }
-    }
-
-    // ---- scaled operands: Q<-, K<-, K-> to LDS; K^ and gamma_C to the block ---------
-    {
-        float kh[CPT][8];
+    Job cur = decode(blockIdx.x);
+    if (cur.ok) issue(cur);
+    while (cur.ok) {  // workgroup-uniform
+        // Thread-index values are re-derived from an opaque copy each job: otherwise the
+        // compiler hoists every per-lane LDS address of the body out of the loop and
+        // keeps them all live, which costs more registers than the body itself.
+        int tidv = threadIdx.x;
+        asm volatile("" : "+v"(tidv));
+        const int tid = tidv;
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int l16 = lane & 15, lg = lane >> 4;
+        const int rg = tid >> 5, cg = tid & 31, c0 = CPT * cg;
+        const int m = cur.m;
+        char *bp = p.blk + (size_t)cur.g * Bk::bytes;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int r = 8 * rg + i;
-            float kv[CPT], qv[CPT], a[CPT], b[CPT], cq[CPT];
+            if (8 * rg + i >= m) {
 #pragma unroll
-            for (int w = 0; w < WPR; ++w) {
-                kv[2 * w] = bf16_lo(kw[i][w]); kv[2 * w + 1] = bf16_hi(kw[i][w]);
-                qv[2 * w] = bf16_lo(qw[i][w]); qv[2 * w + 1] = bf16_hi(qw[i][w]);
+                for (int w = 0; w < WPR; ++w) kw[i][w] = qw[i][w] = 0u;
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) lw[i][e] = 0.f;
             }
+        }
+        if (tid < kC) sBeta[tid] = tid < m ? beta_r : 0.f;
+        if (GATE == kGateHead && wave == 0) {
+            float x = lane < m ? lah * kLog2e : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off, 64);
+                if (lane >= off) x += y;
+            }
+            sG[lane] = x;
+            if (lane == 63) sG[64] = x;
+        }
+        // The products read whole 32-wide contraction blocks of X and A_qk, so everything
+        // not written below (above the diagonal) must be zero.
+        for (int i = tid; i < 2 * kC * kCS * 2 / 16; i += kThreads)
+            ((uint4 *)(smem + L::oX))[i] = make_uint4(0u, 0u, 0u, 0u);
+
+        // ---- gate: prefix sums (log2 domain) -------------------------------------------
+        float g[8][CPT], gC[CPT];
+        if (GATE == kGateChannel) {
+            float run[CPT];
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) run[e] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) {
+                    run[e] += lw[i][e] * kLog2e;
+                    g[i][e] = run[e];
+                }
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) sTot[rg * DK + c0 + e] = run[e];
+        }
+        lds_barrier();
+        if (GATE == kGateChannel) {
+            float carry[CPT], tot[CPT];
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) carry[e] = tot[e] = 0.f;
+#pragma unroll
+            for (int r2 = 0; r2 < 8; ++r2)
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) {
+                    const float t = sTot[r2 * DK + c0 + e];
+                    tot[e] += t;
+                    carry[e] += r2 < rg ? t : 0.f;
+                }
 #pragma unroll
             for (int e = 0; e < CPT; ++e) {
-                const float eg = GATE == kGateNone ? 1.f : exp2_fast(g[i][e]);
-                const float eig = GATE == kGateNone ? 1.f : exp2_fast(-g[i][e]);
-                const float egc = GATE == kGateNone ? 1.f : exp2_fast(gC[e] - g[i][e]);
-                a[e] = kv[e] * eg;
-                b[e] = kv[e] * eig;
-                cq[e] = qv[e] * eg;
-                kh[e][i] = kv[e] * egc;
+                gC[e] = tot[e];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) g[i][e] += carry[e];
             }
-            uint32_t wa[WPR], wb[WPR], wq[WPR];
-#pragma unroll
-            for (int w = 0; w < WPR; ++w) {
-                wa[w] = pack_bf16x2(a[2 * w], a[2 * w + 1]);
-                wb[w] = pack_bf16x2(b[2 * w], b[2 * w + 1]);
-                wq[w] = pack_bf16x2(cq[2 * w], cq[2 * w + 1]);
-            }
-            if constexpr (WPR == 2) {
-                *(uint2 *)(sKl + r * KS + c0) = make_uint2(wa[0], wa[1]);
-                *(uint2 *)(sKr + r * KS + c0) = make_uint2(wb[0], wb[1]);
-                *(uint2 *)(sQl + r * KS + c0) = make_uint2(wq[0], wq[1]);
-            } else {
-                *(uint32_t *)(sKl + r * KS + c0) = wa[0];
-                *(uint32_t *)(sKr + r * KS + c0) = wb[0];
-                *(uint32_t *)(sQl + r * KS + c0) = wq[0];
-            }
-        }
-        // K^ transposed: channel cc is row cc%32 of fragment tile cc/32; this thread's
-        // 8 rows are one 16-byte piece (step rg/2, lane half rg%2).
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) {
-            const int cc = c0 + e;
-            const int pc = (cc >> 5) * 4 * 64 + (rg >> 1) * 64 + (cc & 31) + 32 * (rg & 1);
-            uint4 w;
-            w.x = pack_bf16x2(kh[e][0], kh[e][1]);
-            w.y = pack_bf16x2(kh[e][2], kh[e][3]);
-            w.z = pack_bf16x2(kh[e][4], kh[e][5]);
-            w.w = pack_bf16x2(kh[e][6], kh[e][7]);
-            ((uint4 *)(bp + Bk::oK))[pc] = w;
-        }
-        if (rg == 0) {
-#pragma unroll
-            for (int e = 0; e < CPT; ++e)
-                ((float *)(bp + Bk::oG))[c0 + e] = GATE == kGateNone ? 1.f : exp2_fast(gC[e]);
-        }
-    }
-    lds_barrier();
-
-    // ---- L and A_qk: the 10 lower-triangle 16x16 tiles of each (20 jobs) -----------
-    // Computed transposed, D[c][r] = K->[c] . (K<- or Q<-)[r], so that each lane holds
-    // four consecutive columns of one row.
-    for (int jb = wave; jb < 20; jb += 4) {
-        const bool isA = jb >= 10;
-        const int t = isA ? jb - 10 : jb;
-        const int ti = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
-        const int tj = t - ti * (ti + 1) / 2;
-        const uint16_t *src = isA ? sQl : sKl;
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < DK / 32; ++s)
-            d = mfma(frag(sKr, 16 * tj + l16, KS, 32 * s + 8 * lg),
-                     frag(src, 16 * ti + l16, KS, 32 * s + 8 * lg), d);
-        const int r = 16 * ti + l16, cb = 16 * tj + 4 * lg;
-        if (isA) {
-            store4(sAqk + r * kCS + cb, cb + 0 <= r ? d[0] : 0.f, cb + 1 <= r ? d[1] : 0.f,
-                   cb + 2 <= r ? d[2] : 0.f, cb + 3 <= r ? d[3] : 0.f);
         } else {
-            const float br = sBeta[r];
-            const float v0 = cb + 0 < r ? br * d[0] : 0.f, v1 = cb + 1 < r ? br * d[1] : 0.f;
-            const float v2 = cb + 2 < r ? br * d[2] : 0.f, v3 = cb + 3 < r ? br * d[3] : 0.f;
-            if (ti == tj) *(float4 *)(sLd + (16 * ti + l16) * kDS + 4 * lg) = make_float4(v0, v1, v2, v3);
-            else store4(sX + r * kCS + cb, v0, v1, v2, v3);
-        }
-    }
-    lds_barrier();
-
-    // ---- At, diagonal blocks: forward substitution (wave 0) ------------------------
-    // Lane (block lg, column l16): x_r = [r == col] - sum_{i<r} L[r][i] x_i, which
-    // leaves x_r = 0 for r < col without any masking.
-    if (wave == 0) {
-        const float *Lb = sLd + 16 * lg * kDS;
-        float x[16];
-        float4 cur[4], nxt[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            if (r + 1 < 16) {
+            for (int e = 0; e < CPT; ++e) {
+                gC[e] = GATE == kGateHead ? sG[64] : 0.f;
 #pragma unroll
-                for (int i4 = 0; i4 < (r + 4) / 4; ++i4) nxt[i4] = *(const float4 *)(Lb + (r + 1) * kDS + 4 * i4);
+                for (int i = 0; i < 8; ++i) g[i][e] = GATE == kGateHead ? sG[8 * rg + i] : 0.f;
             }
-            float ps[4] = {0.f, 0.f, 0.f, 0.f};
+        }
+
+        // ---- scaled operands: Q<-, K<-, K-> to LDS; K^ and gamma_C to the block ---------
+        {
+            float kh[CPT][8], gam[CPT];
 #pragma unroll
-            for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
-                const float lv[4] = {cur[i4].x, cur[i4].y, cur[i4].z, cur[i4].w};
+            for (int e = 0; e < CPT; ++e) gam[e] = GATE == kGateNone ? 1.f : exp2_fast(gC[e]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (4 * i4 + e < r) ps[e] += lv[e] * x[4 * i4 + e];
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * rg + i;
+                float kv[CPT], qv[CPT], a[CPT], b[CPT], cq[CPT];
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) {
+                    kv[2 * w] = bf16_lo(kw[i][w]); kv[2 * w + 1] = bf16_hi(kw[i][w]);
+                    qv[2 * w] = bf16_lo(qw[i][w]); qv[2 * w + 1] = bf16_hi(qw[i][w]);
+                }
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) {
+                    const float eg = GATE == kGateNone ? 1.f : exp2_fast(g[i][e]);
+                    const float eig = GATE == kGateNone ? 1.f : exp2_fast(-g[i][e]);
+                    const float egc = eig * gam[e];  // e^(g_C - g)
+                    a[e] = kv[e] * eg;
+                    b[e] = kv[e] * eig;
+                    cq[e] = qv[e] * eg;
+                    kh[e][i] = kv[e] * egc;
+                }
+                uint32_t wa[WPR], wb[WPR], wq[WPR];
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) {
+                    wa[w] = pack_bf16x2(a[2 * w], a[2 * w + 1]);
+                    wb[w] = pack_bf16x2(b[2 * w], b[2 * w + 1]);
+                    wq[w] = pack_bf16x2(cq[2 * w], cq[2 * w + 1]);
+                }
+                if constexpr (WPR == 2) {
+                    *(uint2 *)(sKl + r * KS + c0) = make_uint2(wa[0], wa[1]);
+                    *(uint2 *)(sKr + r * KS + c0) = make_uint2(wb[0], wb[1]);
+                    *(uint2 *)(sQl + r * KS + c0) = make_uint2(wq[0], wq[1]);
+                } else {
+                    *(uint32_t *)(sKl + r * KS + c0) = wa[0];
+                    *(uint32_t *)(sKr + r * KS + c0) = wb[0];
+                    *(uint32_t *)(sQl + r * KS + c0) = wq[0];
+                }
             }
-            x[r] = (r == l16 ? 1.f : 0.f) - ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+            // K^ transposed: channel cc is row cc%32 of fragment tile cc/32; this thread's
+            // 8 rows are one 16-byte piece (step rg/2, lane half rg%2).
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) cur[i4] = nxt[i4];
+            for (int e = 0; e < CPT; ++e) {
+                const int cc = c0 + e;
+                const int pc = (cc >> 5) * 4 * 64 + (rg >> 1) * 64 + (cc & 31) + 32 * (rg & 1);
+                uint4 w;
+                w.x = pack_bf16x2(kh[e][0], kh[e][1]);
+                w.y = pack_bf16x2(kh[e][2], kh[e][3]);
+                w.z = pack_bf16x2(kh[e][4], kh[e][5]);
+                w.w = pack_bf16x2(kh[e][6], kh[e][7]);
+                ((uint4 *)(bp + Bk::oK))[pc] = w;
+            }
+            if (rg == 0) {
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) ((float *)(bp + Bk::oG))[c0 + e] = gam[e];
+            }
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            sLd[(16 * lg + r) * kDS + l16] = x[r];
-            sX[(16 * lg + r) * kCS + 16 * lg + l16] = __builtin_bit_cast(uint16_t, (__bf16)x[r]);
-        }
-    }
-    lds_barrier();
-
-    // ---- At, 32-row level (waves 0, 1): X_BA = -X_BB (L_BA X_AA) --------------------
-    if (wave < 2) {
-        const int a0 = 32 * wave, a1 = a0 + 16;
-        const bf16x4 fL = *(const bf16x4 *)(sX + (a1 + l16) * kCS + a0 + 4 * lg);
-        bf16x4 fXa;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            fXa[e] = __builtin_bit_cast(__bf16, sX[(a0 + 4 * lg + e) * kCS + a0 + l16]);
-        const f32x4 t = mfma16(fL, fXa, f32x4{0.f, 0.f, 0.f, 0.f});  // t[e] = T[4lg+e][l16]
-        const bf16x4 fXb = *(const bf16x4 *)(sX + (a1 + l16) * kCS + a1 + 4 * lg);
-        const f32x4 x = mfma16(fXb, to_bf16x4(t[0], t[1], t[2], t[3]), f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            sX[(a1 + 4 * lg + e) * kCS + a0 + l16] = __builtin_bit_cast(uint16_t, (__bf16)(-x[e]));
-    }
-    lds_barrier();
-
-    // ---- At, 64-row level (waves 0-3, one 16x16 tile each) -------------------------
-    {
-        const int ti = wave >> 1, tj = wave & 1;
-        const f32x4 t = mfma(frag(sX, 32 + 16 * ti + l16, kCS, 8 * lg), frag_tr(sX, 0, kCS, 16 * tj, lane),
-                             f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            sT[(16 * ti + 4 * lg + e) * kTS + 16 * tj + l16] = __builtin_bit_cast(uint16_t, (__bf16)t[e]);
+        // this job's raw inputs are consumed: the next job's start loading
+        const Job nxt = decode(cur.g + gridDim.x);
+        if (nxt.ok) issue(nxt);
         lds_barrier();
-        const f32x4 x = mfma(frag(sX, 32 + 16 * ti + l16, kCS, 32 + 8 * lg), frag_tr(sT, 0, kTS, 16 * tj, lane),
-                             f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            sX[(32 + 16 * ti + 4 * lg + e) * kCS + 16 * tj + l16] = __builtin_bit_cast(uint16_t, (__bf16)(-x[e]));
-    }
-    lds_barrier();
 
-    // ---- Ab = At Diag(beta), in place (diagonal blocks from the fp32 copy) ---------
-    {
-        const int r = tid >> 2, cbk = tid & 3, cb = 16 * cbk, b = r >> 4;
-        float a[16];
-        if (cbk == b) {
+        // ---- L and A_qk: the 10 lower-triangle 16x16 tiles of each (20 jobs) -----------
+        // Computed transposed, D[c][r] = K->[c] . (K<- or Q<-)[r], so that each lane holds
+        // four consecutive columns of one row.
+        for (int jb = wave; jb < 20; jb += 4) {
+            const bool isA = jb >= 10;
+            const int t = isA ? jb - 10 : jb;
+            const int ti = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
+            const int tj = t - ti * (ti + 1) / 2;
+            const uint16_t *src = isA ? sQl : sKl;
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < DK / 32; ++s)
+                d = mfma(frag(sKr, 16 * tj + l16, KS, 32 * s + 8 * lg),
+                         frag(src, 16 * ti + l16, KS, 32 * s + 8 * lg), d);
+            const int r = 16 * ti + l16, cb = 16 * tj + 4 * lg;
+            if (isA) {
+                store4(sAqk + r * kCS + cb, cb + 0 <= r ? d[0] : 0.f, cb + 1 <= r ? d[1] : 0.f,
+                       cb + 2 <= r ? d[2] : 0.f, cb + 3 <= r ? d[3] : 0.f);
+            } else {
+                const float br = sBeta[r];
+                const float v0 = cb + 0 < r ? br * d[0] : 0.f, v1 = cb + 1 < r ? br * d[1] : 0.f;
+                const float v2 = cb + 2 < r ? br * d[2] : 0.f, v3 = cb + 3 < r ? br * d[3] : 0.f;
+                if (ti == tj) *(float4 *)(sLd + (16 * ti + l16) * kDS + 4 * lg) = make_float4(v0, v1, v2, v3);
+                else store4(sX + r * kCS + cb, v0, v1, v2, v3);
+            }
+        }
+        lds_barrier();
+
+        // ---- At, diagonal blocks: forward substitution (wave 0) ------------------------
+        // Lane (block lg, column l16): x_r = [r == col] - sum_{i<r} L[r][i] x_i, which
+        // leaves x_r = 0 for r < col without any masking.
+        if (wave == 0) {
+            const float *Lb = sLd + 16 * lg * kDS;
+            float x[16];
+            float4 cur[4], nxt[4];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (r + 1 < 16) {
+#pragma unroll
+                    for (int i4 = 0; i4 < (r + 4) / 4; ++i4) nxt[i4] = *(const float4 *)(Lb + (r + 1) * kDS + 4 * i4);
+                }
+                float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
+                    const float lv[4] = {cur[i4].x, cur[i4].y, cur[i4].z, cur[i4].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * i4 + e < r) ps[e] += lv[e] * x[4 * i4 + e];
+                }
+                x[r] = (r == l16 ? 1.f : 0.f) - ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) cur[i4] = nxt[i4];
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sLd[(16 * lg + r) * kDS + l16] = x[r];
+                sX[(16 * lg + r) * kCS + 16 * lg + l16] = __builtin_bit_cast(uint16_t, (__bf16)x[r]);
+            }
+        }
+        lds_barrier();
+
+        // ---- At, 32-row level (waves 0, 1): X_BA = -X_BB (L_BA X_AA) --------------------
+        if (wave < 2) {
+            const int a0 = 32 * wave, a1 = a0 + 16;
+            const bf16x4 fL = *(const bf16x4 *)(sX + (a1 + l16) * kCS + a0 + 4 * lg);
+            bf16x4 fXa;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                fXa[e] = __builtin_bit_cast(__bf16, sX[(a0 + 4 * lg + e) * kCS + a0 + l16]);
+            const f32x4 t = mfma16(fL, fXa, f32x4{0.f, 0.f, 0.f, 0.f});  // t[e] = T[4lg+e][l16]
+            const bf16x4 fXb = *(const bf16x4 *)(sX + (a1 + l16) * kCS + a1 + 4 * lg);
+            const f32x4 x = mfma16(fXb, to_bf16x4(t[0], t[1], t[2], t[3]), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sX[(a1 + 4 * lg + e) * kCS + a0 + l16] = __builtin_bit_cast(uint16_t, (__bf16)(-x[e]));
+        }
+        lds_barrier();
+
+        // ---- At, 64-row level (waves 0-3, one 16x16 tile each) -------------------------
+        {
+            const int ti = wave >> 1, tj = wave & 1;
+            const f32x4 t = mfma(frag(sX, 32 + 16 * ti + l16, kCS, 8 * lg), frag_tr(sX, 0, kCS, 16 * tj, lane),
+                                 f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sT[(16 * ti + 4 * lg + e) * kTS + 16 * tj + l16] = __builtin_bit_cast(uint16_t, (__bf16)t[e]);
+            lds_barrier();
+            const f32x4 x = mfma(frag(sX, 32 + 16 * ti + l16, kCS, 32 + 8 * lg), frag_tr(sT, 0, kTS, 16 * tj, lane),
+                                 f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sX[(32 + 16 * ti + 4 * lg + e) * kCS + 16 * tj + l16] = __builtin_bit_cast(uint16_t, (__bf16)(-x[e]));
+        }
+        lds_barrier();
+
+        // ---- Ab = At Diag(beta), in place (diagonal blocks from the fp32 copy) ---------
+        // Thread: row r, 16 columns from cb.  Both sources are read and one is selected,
+        // so that the lanes of a wave do not diverge.
+        {
+            const int r = tid >> 2, cbk = tid & 3, cb = 16 * cbk, b = r >> 4;
+            const uint4 x0 = *(const uint4 *)(sX + r * kCS + cb), x1 = *(const uint4 *)(sX + r * kCS + cb + 8);
+            const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            const float *dr = sLd + (16 * b + (r & 15)) * kDS;
+            const bool diag = cbk == b;
+            uint32_t w[8];
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                const float4 x = *(const float4 *)(sLd + (16 * b + (r & 15)) * kDS + 4 * i4);
-                a[4 * i4 + 0] = x.x; a[4 * i4 + 1] = x.y; a[4 * i4 + 2] = x.z; a[4 * i4 + 3] = x.w;
+                const float4 d = *(const float4 *)(dr + 4 * i4);
+                const float4 be = *(const float4 *)(sBeta + cb + 4 * i4);
+                const float dv[4] = {d.x, d.y, d.z, d.w}, bv[4] = {be.x, be.y, be.z, be.w};
+                float x[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * i4 + e, ca = cb + i;
+                    const uint32_t word = xw[i >> 1];
+                    const float a = diag ? dv[e] : ((i & 1) ? bf16_hi(word) : bf16_lo(word));
+                    x[e] = ca <= r ? a * bv[e] : 0.f;
+                }
+                w[2 * i4] = pack_bf16x2(x[0], x[1]);
+                w[2 * i4 + 1] = pack_bf16x2(x[2], x[3]);
             }
-        } else if (cbk < b) {
-            const uint4 x0 = *(const uint4 *)(sX + r * kCS + cb), x1 = *(const uint4 *)(sX + r * kCS + cb + 8);
-            const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) a[2 * i] = bf16_lo(w[i]), a[2 * i + 1] = bf16_hi(w[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) a[i] = 0.f;
+            *(uint4 *)(sX + r * kCS + cb) = make_uint4(w[0], w[1], w[2], w[3]);
+            *(uint4 *)(sX + r * kCS + cb + 8) = make_uint4(w[4], w[5], w[6], w[7]);
         }
-        uint32_t w[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int ca = cb + 2 * i;
-            const float x0 = ca <= r ? a[2 * i] * sBeta[ca] : 0.f;
-            const float x1 = ca + 1 <= r ? a[2 * i + 1] * sBeta[ca + 1] : 0.f;
-            w[i] = pack_bf16x2(x0, x1);
-        }
-        *(uint4 *)(sX + r * kCS + cb) = make_uint4(w[0], w[1], w[2], w[3]);
-        *(uint4 *)(sX + r * kCS + cb + 8) = make_uint4(w[4], w[5], w[6], w[7]);
-    }
-    lds_barrier();
+        lds_barrier();
 
-    // ---- Ao = A_qk Ab, in place: wave ti owns 16-row block ti ----------------------
-    {
-        const int ti = wave;
-        const bf16x8 b0 = frag(sAqk, 16 * ti + l16, kCS, 8 * lg);
-        const bf16x8 b1 = frag(sAqk, 16 * ti + l16, kCS, 32 + 8 * lg);
-        for (int tj = 0; tj <= ti; ++tj) {  // wave-uniform
-            f32x4 d = mfma(frag_tr(sX, 0, kCS, 16 * tj, lane), b0, f32x4{0.f, 0.f, 0.f, 0.f});
-            d = mfma(frag_tr(sX, 32, kCS, 16 * tj, lane), b1, d);
-            store4(sAqk + (16 * ti + l16) * kCS + 16 * tj + 4 * lg, d[0], d[1], d[2], d[3]);
-        }
-    }
-    lds_barrier();
-
-    // ---- W' = -Ab K<- (into the K-> array), Q~ = Q<- - Ao K<- (in place) ------------
-    {
-        bf16x8 fab[4][2], fao[4][2];
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                fab[ti][s] = frag(sX, 16 * ti + l16, kCS, 32 * s + 8 * lg);
-                fao[ti][s] = frag(sAqk, 16 * ti + l16, kCS, 32 * s + 8 * lg);
-            }
-#pragma unroll
-        for (int tt = 0; tt < DK / 64; ++tt) {
-            const int tn = wave * (DK / 64) + tt;
-            const bf16x8 k0 = frag_tr(sKl, 0, KS, 16 * tn, lane);
-            const bf16x8 k1 = frag_tr(sKl, 32, KS, 16 * tn, lane);
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                f32x4 w = mfma(k0, fab[ti][0], f32x4{0.f, 0.f, 0.f, 0.f});
-                w = mfma(k1, fab[ti][1], w);
-                f32x4 o = mfma(k0, fao[ti][0], f32x4{0.f, 0.f, 0.f, 0.f});
-                o = mfma(k1, fao[ti][1], o);
-                const int r = 16 * ti + l16, cc = 16 * tn + 4 * lg;
-                store4(sKr + r * KS + cc, -w[0], -w[1], -w[2], -w[3]);
-                const uint2 qv = *(const uint2 *)(sQl + r * KS + cc);
-                store4(sQl + r * KS + cc, bf16_lo(qv.x) - o[0], bf16_hi(qv.x) - o[1],
-                       bf16_lo(qv.y) - o[2], bf16_hi(qv.y) - o[3]);
+        // ---- Ao = A_qk Ab, in place: wave ti owns 16-row block ti ----------------------
+        {
+            const int ti = wave;
+            const bf16x8 b0 = frag(sAqk, 16 * ti + l16, kCS, 8 * lg);
+            const bf16x8 b1 = frag(sAqk, 16 * ti + l16, kCS, 32 + 8 * lg);
+            for (int tj = 0; tj <= ti; ++tj) {  // wave-uniform
+                f32x4 d = mfma(frag_tr(sX, 0, kCS, 16 * tj, lane), b0, f32x4{0.f, 0.f, 0.f, 0.f});
+                d = mfma(frag_tr(sX, 32, kCS, 16 * tj, lane), b1, d);
+                store4(sAqk + (16 * ti + l16) * kCS + 16 * tj + 4 * lg, d[0], d[1], d[2], d[3]);
             }
         }
-    }
-    lds_barrier();
+        lds_barrier();
 
-    // ---- fragment tiles out: W', Q~ (2 row tiles x DK/16 steps), Ab, Ao (3 tiles) ---
-    constexpr int NPW = 2 * (DK / 16) * 64;
-    for (int pc = tid; pc < NPW; pc += kThreads) {
-        const int t = pc / ((DK / 16) * 64), s = (pc >> 6) % (DK / 16), ln = pc & 63;
-        const int r = 32 * t + (ln & 31), cc = 16 * s + 8 * (ln >> 5);
-        ((uint4 *)(bp + Bk::oW))[pc] = *(const uint4 *)(sKr + r * KS + cc);
-        ((uint4 *)(bp + Bk::oQ))[pc] = *(const uint4 *)(sQl + r * KS + cc);
-    }
-    for (int pc = tid; pc < 3 * 128; pc += kThreads) {
-        const int tau = pc >> 7, s = (pc >> 6) & 1, ln = pc & 63;
-        const int r = (tau ? 32 : 0) + (ln & 31), cc = (tau == 2 ? 32 : 0) + 16 * s + 8 * (ln >> 5);
-        ((uint4 *)(bp + Bk::oAb))[pc] = *(const uint4 *)(sX + r * kCS + cc);
-        ((uint4 *)(bp + Bk::oAo))[pc] = *(const uint4 *)(sAqk + r * kCS + cc);
+        // ---- W' = -Ab K<- (into the K-> array), Q~ = Q<- - Ao K<- (in place) ------------
+        {
+            bf16x8 fab[4][2], fao[4][2];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    fab[ti][s] = frag(sX, 16 * ti + l16, kCS, 32 * s + 8 * lg);
+                    fao[ti][s] = frag(sAqk, 16 * ti + l16, kCS, 32 * s + 8 * lg);
+                }
+#pragma unroll
+            for (int tt = 0; tt < DK / 64; ++tt) {
+                const int tn = wave * (DK / 64) + tt;
+                const bf16x8 k0 = frag_tr(sKl, 0, KS, 16 * tn, lane);
+                const bf16x8 k1 = frag_tr(sKl, 32, KS, 16 * tn, lane);
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    f32x4 w = mfma(k0, fab[ti][0], f32x4{0.f, 0.f, 0.f, 0.f});
+                    w = mfma(k1, fab[ti][1], w);
+                    f32x4 o = mfma(k0, fao[ti][0], f32x4{0.f, 0.f, 0.f, 0.f});
+                    o = mfma(k1, fao[ti][1], o);
+                    const int r = 16 * ti + l16, cc = 16 * tn + 4 * lg;
+                    store4(sKr + r * KS + cc, -w[0], -w[1], -w[2], -w[3]);
+                    const uint2 qv = *(const uint2 *)(sQl + r * KS + cc);
+                    store4(sQl + r * KS + cc, bf16_lo(qv.x) - o[0], bf16_hi(qv.x) - o[1],
+                           bf16_lo(qv.y) - o[2], bf16_hi(qv.y) - o[3]);
+                }
+            }
+        }
+        lds_barrier();
+
+        // ---- fragment tiles out: W', Q~ (2 row tiles x DK/16 steps), Ab, Ao (3 tiles) ---
+        constexpr int NPW = 2 * (DK / 16) * 64;
+        for (int pc = tid; pc < NPW; pc += kThreads) {
+            const int t = pc / ((DK / 16) * 64), s = (pc >> 6) % (DK / 16), ln = pc & 63;
+            const int r = 32 * t + (ln & 31), cc = 16 * s + 8 * (ln >> 5);
+            ((uint4 *)(bp + Bk::oW))[pc] = *(const uint4 *)(sKr + r * KS + cc);
+            ((uint4 *)(bp + Bk::oQ))[pc] = *(const uint4 *)(sQl + r * KS + cc);
+        }
+        for (int pc = tid; pc < 3 * 128; pc += kThreads) {
+            const int tau = pc >> 7, s = (pc >> 6) & 1, ln = pc & 63;
+            const int r = (tau ? 32 : 0) + (ln & 31), cc = (tau == 2 ? 32 : 0) + 16 * s + 8 * (ln >> 5);
+            ((uint4 *)(bp + Bk::oAb))[pc] = *(const uint4 *)(sX + r * kCS + cc);
+            ((uint4 *)(bp + Bk::oAo))[pc] = *(const uint4 *)(sAqk + r * kCS + cc);
+        }
+        lds_barrier();  // every LDS array is free for the next job
+        cur = nxt;
     }
 }
 
@@ -783,6 +822,20 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     }
 }
 
+// Compute units of the current device (cached per device).
+int compute_units() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 int blk_bytes(int dk) { return dk == 128 ? Blk<128>::bytes : Blk<64>::bytes; }
 
 // Workspace: [error flag header][chunk offsets (packed sequences)][blocks].
@@ -834,7 +887,10 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     sp.nc = nc; sp.max_chunks = max_chunks;
 
     if (varlen) hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kThreads), 0, s, sp);
-    const dim3 grid_prep((unsigned)a.H * (unsigned)max_chunks);
+    // persistent prep workgroups: two per CU (their LDS allows no more)
+    const long njobs = (long)a.H * max_chunks;
+    const long slots = 2L * compute_units();
+    const dim3 grid_prep((unsigned)(njobs < slots ? njobs : slots));
     const dim3 grid_state((unsigned)(n_seq_eff * a.H * sp.n_tiles));
 #define GDR_PREP(DK, G) hipLaunchKernelGGL((kda_prep_kernel<DK, G>), grid_prep, dim3(kThreads), 0, s, sp)
     if (a.dk == 128) {
