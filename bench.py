@@ -69,15 +69,20 @@ def algorithmic_counts(P):
     plus S_final (and S0 if given) once per (sequence, head).
     FLOP per token-head: 10*C*d + 6*d^2 -- five C x C x d products (K<-K->^T,
     At K<-, At V, Q<-K->^T, A_qk V_new) and three C x d x d products (W S^T,
-    V_new^T K^, Q<- S^T), counted as full tiles.
+    V_new^T K^, Q<- S^T), counted as full tiles.  With a and b (DPLR) the call also
+    reads a, b (2*dk each) and does 18*C*d + 8*d^2.
     """
     th = P.B * P.T * P.H
     d, C = P.dk, P.chunk
     es = 2 if P.dtype.itemsize == 2 else 4
-    per_th = es * (2 * P.dk + 2 * P.dv) + 4 * P.dk + 4
+    gate_bytes = {0: 0, 1: 4, 2: 4 * P.dk}[P.gate]
+    per_th = es * (2 * P.dk + 2 * P.dv) + gate_bytes + 4
+    flops_th = 10 * C * d + 6 * d * d
+    if P.a is not None:
+        per_th += 2 * es * P.dk
+        flops_th = 18 * C * d + 8 * d * d
     state = P.n_seq * P.H * P.dv * P.dk * 4 * (1 + (P.S0 is not None))
-    flops = th * (10 * C * d + 6 * d * d)
-    return th * per_th + state, flops
+    return th * per_th + state, th * flops_th
 
 
 def time_gpu(P, steps, warmup, cold_steps):
@@ -88,10 +93,10 @@ def time_gpu(P, steps, warmup, cold_steps):
     dev = torch.device("cuda", 0)
     to = lambda t: None if t is None else t.to(dev)
     q, k, v, beta, la = to(P.q), to(P.k), to(P.v), to(P.beta), to(P.log_alpha)
-    S0, cu = to(P.S0), to(P.cu_seqlens)
+    a, b, S0, cu = to(P.a), to(P.b), to(P.S0), to(P.cu_seqlens)
     out = torch.empty((P.B, P.T, P.H, P.dv), dtype=P.dtype, device=dev)
     fin = torch.empty((P.n_seq, P.H, P.dv, P.dk), dtype=torch.float32, device=dev)
-    call = lambda: gdr.chunk_fwd(q, k, v, beta, log_alpha=la, S0=S0, cu_seqlens=cu,
+    call = lambda: gdr.chunk_fwd(q, k, v, beta, log_alpha=la, a=a, b=b, S0=S0, cu_seqlens=cu,
                                  chunk_size=P.chunk, out=out, final_state=fin)
     for _ in range(warmup):
         call()
@@ -169,13 +174,13 @@ def cpu_baseline(P, n_threads):
 
     f64 = lambda t: None if t is None else t.to(torch.float64).numpy()
     args = dict(q=f64(P.q), k=f64(P.k), v=f64(P.v), beta=f64(P.beta),
-                log_alpha=f64(P.log_alpha), S0=f64(P.S0),
+                log_alpha=f64(P.log_alpha), a=f64(P.a), b=f64(P.b), S0=f64(P.S0),
                 cu_seqlens=None if P.cu_seqlens is None else P.cu_seqlens.numpy())
     t = time.perf_counter()
     O, Sf = oracle.recurrence(**args, n_threads=n_threads)
     dt = time.perf_counter() - t
     t = time.perf_counter()
-    oracle.recurrence(**args, chains=[(0, 0), (1, 5)], n_threads=1)
+    oracle.recurrence(**args, chains=[(0, 0), (min(1, P.n_seq - 1), min(5, P.H - 1))], n_threads=1)
     dt1 = time.perf_counter() - t
     return dt, dt1, O, Sf
 
@@ -193,6 +198,10 @@ def cpu_model():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", default=WORKLOAD, choices=["kda", "gdn", "dplr", "kda_varlen",
+                                                              "deltanet_f32"],
+                    help="the benchmark line is for kda; the others time the same call on the "
+                         "other workloads (reported under the same keys, metric named per workload)")
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cold-steps", type=int, default=10)
@@ -225,19 +234,21 @@ def main():
 
     from chunkwise_gated_delta_amd import inputs
 
-    P = inputs.make_problem(WORKLOAD)
+    P = inputs.make_problem(args.workload)
     alg_bytes, alg_flops = algorithmic_counts(P)
     ms, launch_ms, cold_ms, out, fin = time_gpu(P, args.steps, args.warmup, args.cold_steps)
     call_ms = float(np.mean(launch_ms))
-    tokens = P.B * P.T
+    tokens = P.B * P.T  # packed total for the varlen workload (B = 1)
     achieved_gbs = alg_bytes / (call_ms * 1e-3) / 1e9
     tflops = alg_flops / (call_ms * 1e-3) / 1e12
-    cc = committed_counters()
+    headline = args.workload == WORKLOAD
+    cc = committed_counters() if headline else {}
     traffic = cc.get("traffic_bytes_per_launch")
     pct = lambda xs, f: xs[min(len(xs) - 1, int(f * len(xs)))]
 
     result = {
-        "metric": "tokens/s + MFMA util % for KDA chunk fwd, T=8192 H=32 d=128, 1xMI355X",
+        "metric": ("tokens/s + MFMA util % for KDA chunk fwd, T=8192 H=32 d=128, 1xMI355X"
+                   if headline else f"tokens/s, {args.workload} chunk fwd, 1xMI355X"),
         "value": tokens / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -247,17 +258,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if P.dtype == torch.float32 else "bf16",
         "data": "synthetic",
-        "config": {"workload": "KDA chunkwise forward (per-channel gate), B=2 H=32 T=8192 "
-                               "dk=dv=128 C=64, bf16 q/k/v, fp32 gate/beta/state, S0=0",
+        "config": {"workload": ("KDA chunkwise forward (per-channel gate), B=2 H=32 T=8192 "
+                                "dk=dv=128 C=64, bf16 q/k/v, fp32 gate/beta/state, S0=0"
+                                if headline else f"{args.workload}: B={P.B} H={P.H} T={P.T} "
+                                f"dk={P.dk} dv={P.dv} C={P.chunk} n_seq={P.n_seq}"),
                    "global_batch": P.B, "seq_len": P.T, "heads": P.H, "dk": P.dk, "dv": P.dv,
                    "chunk": P.chunk, "parallelism": "none (one GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": None if traffic is None else int(traffic),
-                     "kernel": "gdr_chunk_fwd call: kda_prep_kernel<128, channel gate> + "
-                               "kda_state_kernel<128>",
+                     "kernel": ("gdr_chunk_fwd call: kda_prep_kernel<128, channel gate> + "
+                                "kda_state_kernel<128>" if headline else "gdr_chunk_fwd call"),
                      "call_ms_mean": call_ms, "call_ms_median": pct(launch_ms, 0.5),
                      "call_ms_p10": pct(launch_ms, 0.1), "call_ms_p90": pct(launch_ms, 0.9),
                      "call_ms_cold_mean": float(np.mean(cold_ms)) if cold_ms else None,

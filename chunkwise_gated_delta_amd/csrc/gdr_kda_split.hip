@@ -62,7 +62,8 @@ struct SplitParams {
     bf16 *O;
     float *Sf;
     const int32_t *cu;
-    int32_t *coff;  // first chunk of each packed sequence (with cu_seqlens), else NULL
+    int32_t *coff;   // first chunk of each packed sequence (with cu_seqlens), else NULL
+    int32_t *order;  // packed sequences, longest first (with cu_seqlens), else NULL
     int *err;
     char *blk;      // (chunk, head) blocks
     long total;
@@ -72,9 +73,12 @@ struct SplitParams {
 };
 
 // ---------------------------------------------------------------------------------
-// Chunk offsets of packed sequences: coff[n] = sum over m < n of ceil(len_m / 64).
-// Malformed offsets are clamped here (and flagged) exactly as the other kernels clamp
-// them, so all three agree on every sequence's bounds.
+// Chunk offsets of packed sequences: coff[n] = sum over m < n of ceil(len_m / 64);
+// and the sequences ordered longest first (ties by index), so that the state
+// kernel, whose work per sequence is serial, starts the longest ones first when
+// there are more (sequence, head, tile) triples than CUs.  Malformed offsets are
+// clamped here (and flagged) exactly as the other kernels clamp them, so all three
+// agree on every sequence's bounds.
 // ---------------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void kda_plan_kernel(SplitParams p) {
     __shared__ int part[kThreads];
@@ -105,6 +109,17 @@ __global__ __launch_bounds__(kThreads) void kda_plan_kernel(SplitParams p) {
         long t0, t1;
         seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
         s += (int)((t1 - t0 + kC - 1) / kC);
+    }
+    __syncthreads();
+    // rank of sequence n: how many sequences are longer, or as long with a lower index
+    for (int n = tid; n < N; n += kThreads) {
+        const int cn = p.coff[n + 1] - p.coff[n];
+        int rank = 0;
+        for (int m2 = 0; m2 < N; ++m2) {
+            const int cm = p.coff[m2 + 1] - p.coff[m2];
+            rank += (cm > cn) || (cm == cn && m2 < n);
+        }
+        p.order[rank] = n;
     }
 }
 
@@ -637,10 +652,18 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, lh = lane >> 5;
     const int H = p.H, DV = p.dv;
-    const int lin = xcd_linear_index(blockIdx.x, gridDim.x);
-    const int tile = lin % p.n_tiles;
-    const int h = (lin / p.n_tiles) % H;
-    const int n = lin / (p.n_tiles * H);
+    // Workgroups go to the 8 XCDs round-robin by block index.  A (sequence, head)
+    // group is the n_tiles workgroups that read the same chunk operands, so they are
+    // kept on one XCD (one L2); groups, longest sequence first, are dealt to the XCDs
+    // in turn so that every XCD gets an equal share of the long ones.  The grid is
+    // padded to a multiple of 8 groups; the padding exits at once.
+    const int pos = blockIdx.x >> 3;
+    const int grp = (pos / p.n_tiles) * 8 + (blockIdx.x & 7);
+    if (grp >= p.n_seq * H) return;
+    const int tile = pos % p.n_tiles;
+    const int h = grp % H;
+    const int rank = grp / H;
+    const int n = p.order ? p.order[rank] : rank;
     const int j0 = tile * kDVT;
     long t0, t1;
     seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
@@ -846,7 +869,7 @@ void split_layout(const FwdArgs &a, int N, bool varlen, size_t &coff_off, size_t
     if (varlen) {
         nc = 0;
         max_chunks = ncT + N;
-        blk_off = coff_off + (((size_t)(N + 1) * 4 + 255) / 256) * 256;
+        blk_off = coff_off + (((size_t)(2 * N + 1) * 4 + 255) / 256) * 256;  // coff, order
     } else {
         nc = ncT;
         max_chunks = N * ncT;
@@ -881,6 +904,7 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     char *ws = (char *)a.workspace;
     sp.err = (int *)ws;
     sp.coff = varlen ? (int32_t *)(ws + coff_off) : nullptr;
+    sp.order = varlen ? sp.coff + n_seq_eff + 1 : nullptr;
     sp.blk = ws + blk_off;
     sp.total = (long)a.B * a.T;
     sp.H = a.H; sp.T = a.T; sp.dv = a.dv; sp.n_seq = n_seq_eff; sp.n_tiles = a.dv / kDVT;
@@ -891,7 +915,7 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     const long njobs = (long)a.H * max_chunks;
     const long slots = 2L * compute_units();
     const dim3 grid_prep((unsigned)(njobs < slots ? njobs : slots));
-    const dim3 grid_state((unsigned)(n_seq_eff * a.H * sp.n_tiles));
+    const dim3 grid_state((unsigned)(((n_seq_eff * a.H + 7) / 8) * 8 * sp.n_tiles));
 #define GDR_PREP(DK, G) hipLaunchKernelGGL((kda_prep_kernel<DK, G>), grid_prep, dim3(kThreads), 0, s, sp)
     if (a.dk == 128) {
         if (a.gate == kGateChannel) GDR_PREP(128, kGateChannel);
