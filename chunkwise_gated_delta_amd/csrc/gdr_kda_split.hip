@@ -23,7 +23,18 @@
 //
 // The two right-hand forms of O are equal because A_qk V_new = A_qk Ab V - A_qk Ab
 // K<- S^T; with them the output no longer waits for V_new, and the serial kernel's
-// chain per chunk is two products.  The prep kernel hands its results over in the
+// chain per chunk is two products.
+//
+// With distinct a, b (the gated DPLR form, "Diagonal Plus Low Rank" notes, section 2,
+// matrix form, write term scaled by beta) the same two kernels run with DP set:
+//   prep   A-> = A e^-g, B<- = B e^g, A^ = A e^(g_C - g), K^b = Diag(beta) K^
+//          E   = (I + (B<- A->^T strictly lower))^-1        (same blocked inverse)
+//          Ec' = -E (B<- K->^T strictly lower) Diag(beta),  W' = -E B<-
+//          Ao' = A_qk Diag(beta) + (Q<- A->^T on and below the diagonal) Ec'
+//          Q~  = Q<- + (Q<- A->^T ...) W'
+//   state  N = Ec' V + W' S^T,  O = Ao' V + Q~ S^T,  S = S Diag(gamma_C) + N^T A^ + V^T K^b
+// which expands the pages' N = C - W S^T, O = Q<- S^T + (Q<- K->^T)V' + (Q<- A->^T)N and
+// S = (S + V'^T K-> + N^T A->) Diag(gamma_C), with V' = Diag(beta) V.  The prep kernel hands its results over in the
 // operand order of v_mfma_f32_32x32x16_bf16, so the state kernel loads them straight
 // into registers with whole-wave contiguous loads.
 #include "gdr_mfma.h"
@@ -44,20 +55,23 @@ constexpr float kLog2e = 1.4426950408889634f;
 // contraction columns is stored as K/16 steps x 64 lanes x 16 bytes; lane l of
 // step s holds row l%32, columns 16s + 8(l/32) + 0..7 -- the A-operand registers of
 // v_mfma_f32_32x32x16_bf16, so one wave-wide load of a step is one contiguous KiB.
-template <int DK>
+// With DP (distinct a, b) the slots hold the DPLR counterparts named after the slash.
+template <int DK, bool DP = false>
 struct Blk {
-    static constexpr int oW = 0;                // W' = -Ab K<-: row tiles 0-31, 32-63, K = DK
-    static constexpr int oQ = oW + 128 * DK;    // Q~ = Q<- - Ao K<-: same
-    static constexpr int oK = oQ + 128 * DK;    // K^ transposed: tiles of dk rows 32w.., K = 64 tokens
-    static constexpr int oAb = oK + 128 * DK;   // Ab: 32x32 tiles (0,0), (1,0), (1,1), K = 32
-    static constexpr int oAo = oAb + 6144;      // Ao: same tiles
+    static constexpr int oW = 0;                // W' = -Ab K<- / -E B<-: row tiles 0-31, 32-63, K = DK
+    static constexpr int oQ = oW + 128 * DK;    // Q~ = Q<- - Ao K<- / Q<- + Aqa W': same
+    static constexpr int oK = oQ + 128 * DK;    // K^ / A^ transposed: tiles of dk rows 32w.., K = 64 tokens
+    static constexpr int oAb = oK + 128 * DK;   // Ab / Ec': 32x32 tiles (0,0), (1,0), (1,1), K = 32
+    static constexpr int oAo = oAb + 6144;      // Ao / Ao': same tiles
     static constexpr int oG = oAo + 6144;       // gamma_C [DK] fp32
-    static constexpr int bytes = oG + 4 * DK;
+    static constexpr int oKb = oG + 4 * DK;     // DP only: Diag(beta) K^ transposed, as oK
+    static constexpr int bytes = oKb + (DP ? 128 * DK : 0);
     static_assert(bytes % 256 == 0, "block alignment");
 };
 
 struct SplitParams {
     const bf16 *q, *k, *v;
+    const bf16 *a, *b;  // DPLR low-rank vectors, or NULL (a = k, b = beta k)
     const float *la, *beta, *S0;
     bf16 *O;
     float *Sf;
@@ -146,28 +160,35 @@ __device__ __forceinline__ bool chunk_of(const SplitParams &p, int j, int &n, in
 // ---------------------------------------------------------------------------------
 // Prep kernel
 // ---------------------------------------------------------------------------------
-template <int DK>
+template <int DK, bool DP>
 struct PrepSmem {
     static constexpr int KS = DK + 8;                   // bf16 row stride of [64][DK] arrays
-    static constexpr int oKl = 0;                       // K<-
+    static constexpr int CCB = kC * kCS * 2;            // bytes of one bf16 [64][kCS] array
+    static constexpr int oKl = 0;                       // K<- (DP: B<-)
     static constexpr int oKr = oKl + kC * KS * 2;       // K->, then W'
     static constexpr int oQl = oKr + kC * KS * 2;       // Q<-, then Q~
-    static constexpr int oX = oQl + kC * KS * 2;        // bf16 [64][kCS]: L off the diagonal blocks -> At -> Ab
-    static constexpr int oAqk = oX + kC * kCS * 2;      // bf16 [64][kCS]: A_qk -> Ao
-    static constexpr int oLd = oAqk + kC * kCS * 2;     // fp32 4 x [16][kDS]: diagonal blocks of L -> of At
+    static constexpr int oAr = oQl + kC * KS * 2;       // DP only: A->
+    static constexpr int oX = oAr + (DP ? kC * KS * 2 : 0);  // L off the diagonal blocks -> At -> Ab (DP: -> E)
+    static constexpr int oAqk = oX + CCB;               // A_qk -> Ao (DP: A_qk Diag(beta) -> Ao')
+    static constexpr int oBK = oAqk + CCB;              // DP only: B<- K->^T strictly lower, Diag(beta)
+    static constexpr int oAqa = oBK + (DP ? CCB : 0);   // DP only: Q<- A->^T on and below the diagonal
+    static constexpr int oEc = oAqa + (DP ? CCB : 0);   // DP only: Ec'
+    static constexpr int nCC = DP ? 5 : 2;              // [64][kCS] arrays from oX, cleared per job
+    static constexpr int oLd = oX + nCC * CCB;          // fp32 4 x [16][kDS]: diagonal blocks of L -> of At
     static constexpr int oT = oLd + 4 * 16 * kDS * 4;   // bf16 [32][kTS]
     static constexpr int oTot = oLd;                    // fp32 [8][DK] gate partial sums (before oLd is used)
     static constexpr int oBeta = oT + 32 * kTS * 2;     // fp32 [64]
     static constexpr int oG = oBeta + kC * 4;           // fp32 [65]: head-gate prefix sums and total
     static constexpr int bytes = oG + 80 * 4;
     static_assert(8 * DK * 4 <= oBeta - oLd, "gate partial sums fit");
-    static_assert(bytes <= 80 * 1024, "two workgroups per CU");
+    static_assert(DP || bytes <= 80 * 1024, "two workgroups per CU");
+    static_assert(bytes <= 160 * 1024, "one workgroup per CU");
 };
 
-template <int DK, int GATE>
-__global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
-    using L = PrepSmem<DK>;
-    using Bk = Blk<DK>;
+template <int DK, int GATE, bool DP>
+__global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitParams p) {
+    using L = PrepSmem<DK, DP>;
+    using Bk = Blk<DK, DP>;
     constexpr int KS = L::KS;
     constexpr int CPT = DK / 32;  // gate stage: channels per thread
     constexpr int WPR = CPT / 2;  // 32-bit words of bf16 per row per thread
@@ -178,6 +199,10 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
     uint16_t *sQl = (uint16_t *)(smem + L::oQl);
     uint16_t *sX = (uint16_t *)(smem + L::oX);
     uint16_t *sAqk = (uint16_t *)(smem + L::oAqk);
+    uint16_t *sAr = (uint16_t *)(smem + L::oAr);
+    uint16_t *sBK = (uint16_t *)(smem + L::oBK);
+    uint16_t *sAqa = (uint16_t *)(smem + L::oAqa);
+    uint16_t *sEc = (uint16_t *)(smem + L::oEc);
     float *sLd = (float *)(smem + L::oLd);
     uint16_t *sT = (uint16_t *)(smem + L::oT);
     float *sTot = (float *)(smem + L::oTot);
@@ -220,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
     // issued unconditionally (rows past the end of the sequence re-read its last row)
     // so that all of them are in flight at once; those rows are zeroed when consumed,
     // which makes them exact identity steps.
-    uint32_t kw[8][WPR], qw[8][WPR];
+    uint32_t kw[8][WPR], qw[8][WPR], aw[8][WPR], bw[8][WPR];
     float lw[8][CPT];
     float beta_r = 0.f, lah = 0.f;
     auto issue = [&](const Job &J) {
@@ -229,6 +254,8 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
         const bf16 *kb = p.k + ((size_t)J.tok0 * H + h) * DK + c0;
         const bf16 *qb = p.q + ((size_t)J.tok0 * H + h) * DK + c0;
         const float *lb = p.la + ((size_t)J.tok0 * H + h) * DK + c0;
+        const bf16 *ab = DP ? p.a + ((size_t)J.tok0 * H + h) * DK + c0 : nullptr;
+        const bf16 *bb = DP ? p.b + ((size_t)J.tok0 * H + h) * DK + c0 : nullptr;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * rg + i, rr = r < J.m ? r : J.m - 1;
@@ -236,9 +263,18 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
                 const uint2 xk = *(const uint2 *)(kb + rr * rs), xq = *(const uint2 *)(qb + rr * rs);
                 kw[i][0] = xk.x; kw[i][WPR - 1] = xk.y;
                 qw[i][0] = xq.x; qw[i][WPR - 1] = xq.y;
+                if constexpr (DP) {
+                    const uint2 xa = *(const uint2 *)(ab + rr * rs), xb = *(const uint2 *)(bb + rr * rs);
+                    aw[i][0] = xa.x; aw[i][WPR - 1] = xa.y;
+                    bw[i][0] = xb.x; bw[i][WPR - 1] = xb.y;
+                }
             } else {
                 kw[i][0] = *(const uint32_t *)(kb + rr * rs);
                 qw[i][0] = *(const uint32_t *)(qb + rr * rs);
+                if constexpr (DP) {
+                    aw[i][0] = *(const uint32_t *)(ab + rr * rs);
+                    bw[i][0] = *(const uint32_t *)(bb + rr * rs);
+                }
             }
             if constexpr (GATE == kGateChannel) {
                 if constexpr (CPT == 4) {
@@ -253,6 +289,86 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
         const int rb0 = tid < kC ? (tid < J.m ? tid : J.m - 1) : 0;
         beta_r = p.beta[(size_t)(J.tok0 + rb0) * H + h];
         if (GATE == kGateHead) lah = p.la[(size_t)(J.tok0 + (lane < J.m ? lane : J.m - 1)) * H + h];
+    };
+
+    // DPLR after the inverse (E in sX as bf16, unit diagonal, zero above it):
+    //   stage 1  Ec' = -E BK' (wave ti: row block ti),  W' = -E B<- (into the K-> array)
+    //   stage 2  Ao' = A_qk' + Aqa Ec' (in place),      Q~ = Q<- + Aqa W' (in place)
+    // where BK' = (B<- K->^T strictly lower) Diag(beta), A_qk' = (Q<- K->^T) Diag(beta)
+    // and Aqa = Q<- A->^T, both on and below the diagonal.
+    auto dplr_products = [&]() {
+        int tidv = threadIdx.x;
+        asm volatile("" : "+v"(tidv));
+        const int lane = tidv & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tidv >> 6);
+        const int l16 = lane & 15, lg = lane >> 4;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        {
+            const int ti = wave;
+            const bf16x8 e0 = frag(sX, 16 * ti + l16, kCS, 8 * lg);
+            const bf16x8 e1 = frag(sX, 16 * ti + l16, kCS, 32 + 8 * lg);
+            for (int tj = 0; tj <= ti; ++tj) {  // wave-uniform
+                f32x4 d = mfma(frag_tr(sBK, 0, kCS, 16 * tj, lane), e0, zero);
+                d = mfma(frag_tr(sBK, 32, kCS, 16 * tj, lane), e1, d);
+                store4(sEc + (16 * ti + l16) * kCS + 16 * tj + 4 * lg, -d[0], -d[1], -d[2], -d[3]);
+            }
+        }
+        {
+            bf16x8 fe[4][2];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) fe[ti][s] = frag(sX, 16 * ti + l16, kCS, 32 * s + 8 * lg);
+#pragma unroll
+            for (int tt = 0; tt < DK / 64; ++tt) {
+                const int tn = wave * (DK / 64) + tt;
+                const bf16x8 b0 = frag_tr(sKl, 0, KS, 16 * tn, lane);
+                const bf16x8 b1 = frag_tr(sKl, 32, KS, 16 * tn, lane);
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    f32x4 w = mfma(b0, fe[ti][0], zero);
+                    w = mfma(b1, fe[ti][1], w);
+                    store4(sKr + (16 * ti + l16) * KS + 16 * tn + 4 * lg, -w[0], -w[1], -w[2], -w[3]);
+                }
+            }
+        }
+        lds_barrier();
+        {
+            const int ti = wave;
+            const bf16x8 a0 = frag(sAqa, 16 * ti + l16, kCS, 8 * lg);
+            const bf16x8 a1 = frag(sAqa, 16 * ti + l16, kCS, 32 + 8 * lg);
+            for (int tj = 0; tj <= ti; ++tj) {  // wave-uniform
+                uint16_t *dst = sAqk + (16 * ti + l16) * kCS + 16 * tj + 4 * lg;
+                const uint2 o = *(const uint2 *)dst;
+                f32x4 d = {bf16_lo(o.x), bf16_hi(o.x), bf16_lo(o.y), bf16_hi(o.y)};
+                d = mfma(frag_tr(sEc, 0, kCS, 16 * tj, lane), a0, d);
+                d = mfma(frag_tr(sEc, 32, kCS, 16 * tj, lane), a1, d);
+                store4(dst, d[0], d[1], d[2], d[3]);
+            }
+        }
+        {
+            bf16x8 fa[4][2];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) fa[ti][s] = frag(sAqa, 16 * ti + l16, kCS, 32 * s + 8 * lg);
+#pragma unroll
+            for (int tt = 0; tt < DK / 64; ++tt) {
+                const int tn = wave * (DK / 64) + tt;
+                const bf16x8 w0 = frag_tr(sKr, 0, KS, 16 * tn, lane);
+                const bf16x8 w1 = frag_tr(sKr, 32, KS, 16 * tn, lane);
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    f32x4 o = mfma(w0, fa[ti][0], zero);
+                    o = mfma(w1, fa[ti][1], o);
+                    const int r = 16 * ti + l16, cc = 16 * tn + 4 * lg;
+                    const uint2 qv = *(const uint2 *)(sQl + r * KS + cc);
+                    store4(sQl + r * KS + cc, bf16_lo(qv.x) + o[0], bf16_hi(qv.x) + o[1],
+                           bf16_lo(qv.y) + o[2], bf16_hi(qv.y) + o[3]);
+                }
+            }
+        }
+        lds_barrier();
     };
 
     Job cur = decode(blockIdx.x);
@@ -274,7 +390,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
         for (int i = 0; i < 8; ++i) {
             if (8 * rg + i >= m) {
 #pragma unroll
-                for (int w = 0; w < WPR; ++w) kw[i][w] = qw[i][w] = 0u;
+                for (int w = 0; w < WPR; ++w) kw[i][w] = qw[i][w] = aw[i][w] = bw[i][w] = 0u;
 #pragma unroll
                 for (int e = 0; e < CPT; ++e) lw[i][e] = 0.f;
             }
@@ -292,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
         }
         // The products read whole 32-wide contraction blocks of X and A_qk, so everything
         // not written below (above the diagonal) must be zero.
-        for (int i = tid; i < 2 * kC * kCS * 2 / 16; i += kThreads)
+        for (int i = tid; i < L::nCC * L::CCB / 16; i += kThreads)
             ((uint4 *)(smem + L::oX))[i] = make_uint4(0u, 0u, 0u, 0u);
 
         // ---- gate: prefix sums (log2 domain) -------------------------------------------
@@ -340,44 +456,57 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
         }
 
         // ---- scaled operands: Q<-, K<-, K-> to LDS; K^ and gamma_C to the block ---------
+        // (DP: Q<-, B<-, K->, A-> to LDS; A^, Diag(beta) K^ and gamma_C to the block)
         {
-            float kh[CPT][8], gam[CPT];
+            float kh[CPT][8], kb[CPT][8], gam[CPT];
 #pragma unroll
             for (int e = 0; e < CPT; ++e) gam[e] = GATE == kGateNone ? 1.f : exp2_fast(gC[e]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int r = 8 * rg + i;
-                float kv[CPT], qv[CPT], a[CPT], b[CPT], cq[CPT];
+                const float br = DP ? sBeta[r] : 0.f;
+                float kv[CPT], qv[CPT], av[CPT], bv[CPT], a[CPT], b[CPT], cq[CPT], ar[CPT];
 #pragma unroll
                 for (int w = 0; w < WPR; ++w) {
                     kv[2 * w] = bf16_lo(kw[i][w]); kv[2 * w + 1] = bf16_hi(kw[i][w]);
                     qv[2 * w] = bf16_lo(qw[i][w]); qv[2 * w + 1] = bf16_hi(qw[i][w]);
+                    if constexpr (DP) {
+                        av[2 * w] = bf16_lo(aw[i][w]); av[2 * w + 1] = bf16_hi(aw[i][w]);
+                        bv[2 * w] = bf16_lo(bw[i][w]); bv[2 * w + 1] = bf16_hi(bw[i][w]);
+                    }
                 }
 #pragma unroll
                 for (int e = 0; e < CPT; ++e) {
                     const float eg = GATE == kGateNone ? 1.f : exp2_fast(g[i][e]);
                     const float eig = GATE == kGateNone ? 1.f : exp2_fast(-g[i][e]);
                     const float egc = eig * gam[e];  // e^(g_C - g)
-                    a[e] = kv[e] * eg;
+                    a[e] = (DP ? bv[e] : kv[e]) * eg;
                     b[e] = kv[e] * eig;
                     cq[e] = qv[e] * eg;
-                    kh[e][i] = kv[e] * egc;
+                    kh[e][i] = (DP ? av[e] : kv[e]) * egc;
+                    if constexpr (DP) {
+                        ar[e] = av[e] * eig;
+                        kb[e][i] = br * kv[e] * egc;
+                    }
                 }
-                uint32_t wa[WPR], wb[WPR], wq[WPR];
+                uint32_t wa[WPR], wb[WPR], wq[WPR], wr[WPR];
 #pragma unroll
                 for (int w = 0; w < WPR; ++w) {
                     wa[w] = pack_bf16x2(a[2 * w], a[2 * w + 1]);
                     wb[w] = pack_bf16x2(b[2 * w], b[2 * w + 1]);
                     wq[w] = pack_bf16x2(cq[2 * w], cq[2 * w + 1]);
+                    if constexpr (DP) wr[w] = pack_bf16x2(ar[2 * w], ar[2 * w + 1]);
                 }
                 if constexpr (WPR == 2) {
                     *(uint2 *)(sKl + r * KS + c0) = make_uint2(wa[0], wa[1]);
                     *(uint2 *)(sKr + r * KS + c0) = make_uint2(wb[0], wb[1]);
                     *(uint2 *)(sQl + r * KS + c0) = make_uint2(wq[0], wq[1]);
+                    if constexpr (DP) *(uint2 *)(sAr + r * KS + c0) = make_uint2(wr[0], wr[1]);
                 } else {
                     *(uint32_t *)(sKl + r * KS + c0) = wa[0];
                     *(uint32_t *)(sKr + r * KS + c0) = wb[0];
                     *(uint32_t *)(sQl + r * KS + c0) = wq[0];
+                    if constexpr (DP) *(uint32_t *)(sAr + r * KS + c0) = wr[0];
                 }
             }
             // K^ transposed: channel cc is row cc%32 of fragment tile cc/32; this thread's
@@ -392,6 +521,13 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
                 w.z = pack_bf16x2(kh[e][4], kh[e][5]);
                 w.w = pack_bf16x2(kh[e][6], kh[e][7]);
                 ((uint4 *)(bp + Bk::oK))[pc] = w;
+                if constexpr (DP) {
+                    w.x = pack_bf16x2(kb[e][0], kb[e][1]);
+                    w.y = pack_bf16x2(kb[e][2], kb[e][3]);
+                    w.z = pack_bf16x2(kb[e][4], kb[e][5]);
+                    w.w = pack_bf16x2(kb[e][6], kb[e][7]);
+                    ((uint4 *)(bp + Bk::oKb))[pc] = w;
+                }
             }
             if (rg == 0) {
 #pragma unroll
@@ -404,25 +540,36 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
         lds_barrier();
 
         // ---- L and A_qk: the 10 lower-triangle 16x16 tiles of each (20 jobs) -----------
+        // (DP: B<- A->^T, B<- K->^T, Q<- K->^T, Q<- A->^T; 40 jobs.)
         // Computed transposed, D[c][r] = K->[c] . (K<- or Q<-)[r], so that each lane holds
         // four consecutive columns of one row.
-        for (int jb = wave; jb < 20; jb += 4) {
-            const bool isA = jb >= 10;
-            const int t = isA ? jb - 10 : jb;
+        for (int jb = wave; jb < (DP ? 40 : 20); jb += 4) {
+            const int pr = jb / 10;  // product
+            const bool isA = !DP && pr == 1;
+            const int t = jb - 10 * pr;
             const int ti = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
             const int tj = t - ti * (ti + 1) / 2;
-            const uint16_t *src = isA ? sQl : sKl;
+            const uint16_t *src = DP ? (pr < 2 ? sKl : sQl) : (isA ? sQl : sKl);
+            const uint16_t *col = DP && (pr == 0 || pr == 3) ? sAr : sKr;
             f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < DK / 32; ++s)
-                d = mfma(frag(sKr, 16 * tj + l16, KS, 32 * s + 8 * lg),
+                d = mfma(frag(col, 16 * tj + l16, KS, 32 * s + 8 * lg),
                          frag(src, 16 * ti + l16, KS, 32 * s + 8 * lg), d);
             const int r = 16 * ti + l16, cb = 16 * tj + 4 * lg;
-            if (isA) {
+            if (DP && pr > 0) {
+                // B<- K->^T (strictly lower) and Q<- K->^T (with the diagonal) take the
+                // column scaling Diag(beta) of the value they multiply; Q<- A->^T does not.
+                const float4 be = pr < 3 ? *(const float4 *)(sBeta + cb) : make_float4(1.f, 1.f, 1.f, 1.f);
+                const int lim = pr == 1 ? r : r + 1;  // columns below lim are kept
+                uint16_t *dst = pr == 1 ? sBK : (pr == 2 ? sAqk : sAqa);
+                store4(dst + r * kCS + cb, cb + 0 < lim ? be.x * d[0] : 0.f, cb + 1 < lim ? be.y * d[1] : 0.f,
+                       cb + 2 < lim ? be.z * d[2] : 0.f, cb + 3 < lim ? be.w * d[3] : 0.f);
+            } else if (isA) {
                 store4(sAqk + r * kCS + cb, cb + 0 <= r ? d[0] : 0.f, cb + 1 <= r ? d[1] : 0.f,
                        cb + 2 <= r ? d[2] : 0.f, cb + 3 <= r ? d[3] : 0.f);
             } else {
-                const float br = sBeta[r];
+                const float br = DP ? 1.f : sBeta[r];  // DP: E's system has no beta
                 const float v0 = cb + 0 < r ? br * d[0] : 0.f, v1 = cb + 1 < r ? br * d[1] : 0.f;
                 const float v2 = cb + 2 < r ? br * d[2] : 0.f, v3 = cb + 3 < r ? br * d[3] : 0.f;
                 if (ti == tj) *(float4 *)(sLd + (16 * ti + l16) * kDS + 4 * lg) = make_float4(v0, v1, v2, v3);
@@ -498,6 +645,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
         }
         lds_barrier();
 
+        if constexpr (DP) {
+            dplr_products();
+        } else {
         // ---- Ab = At Diag(beta), in place (diagonal blocks from the fp32 copy) ---------
         // Thread: row r, 16 columns from cb.  Both sources are read and one is selected,
         // so that the lanes of a wave do not diverge.
@@ -572,6 +722,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
             }
         }
         lds_barrier();
+        }
 
         // ---- fragment tiles out: W', Q~ (2 row tiles x DK/16 steps), Ab, Ao (3 tiles) ---
         constexpr int NPW = 2 * (DK / 16) * 64;
@@ -584,7 +735,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(SplitParams p) {
         for (int pc = tid; pc < 3 * 128; pc += kThreads) {
             const int tau = pc >> 7, s = (pc >> 6) & 1, ln = pc & 63;
             const int r = (tau ? 32 : 0) + (ln & 31), cc = (tau == 2 ? 32 : 0) + 16 * s + 8 * (ln >> 5);
-            ((uint4 *)(bp + Bk::oAb))[pc] = *(const uint4 *)(sX + r * kCS + cc);
+            ((uint4 *)(bp + Bk::oAb))[pc] = *(const uint4 *)((DP ? sEc : sX) + r * kCS + cc);
             ((uint4 *)(bp + Bk::oAo))[pc] = *(const uint4 *)(sAqk + r * kCS + cc);
         }
         lds_barrier();  // every LDS array is free for the next job
@@ -611,15 +762,16 @@ template <int DK>
 struct Pre {
     uint4 P[DK / 16];  // W' (waves 0, 1) or Q~ (waves 2, 3): this wave's 32 rows
     uint4 A[4];        // Ab or Ao tiles of those rows (2 steps for rows 0-31, 4 for 32-63)
-    uint4 K[4];        // K^ tile of dk rows 32w.. (waves w < DK/32)
+    uint4 K[4];        // K^ (DPLR: A^) tile of dk rows 32w.. (waves w < DK/32)
+    uint4 Kb[4];       // DPLR only: Diag(beta) K^ tile of the same rows
     uint4 V;           // one 16-byte piece of the value tile
     float4 G;          // wave 0, lanes 0..DK/4-1: gamma_C[4 lane..+3]
 };
 // Fewest loads any wave issues per chunk (rows 0-31 take two A steps; waves past
 // DK/32 take no K^ tile); waiting until at most this many are in flight therefore
 // completes every load of the chunk before, whatever the wave.
-template <int DK>
-constexpr int kMinLoadsPerChunk = DK / 16 + 2 + (DK / 32 >= 4 ? 4 : 0) + 1;
+template <int DK, bool DP>
+constexpr int kMinLoadsPerChunk = DK / 16 + 2 + (DK / 32 >= 4 ? (DP ? 8 : 4) : 0) + 1;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -635,10 +787,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Chunks whose operands are in flight ahead of the one being computed.
 constexpr int kDepth = 2;
 
-template <int DK>
+template <int DK, bool DP>
 __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     using L = StateSmem<DK>;
-    using Bk = Blk<DK>;
+    using Bk = Blk<DK, DP>;
     constexpr int KS = L::KS;
     constexpr int NSW = DK / 32;  // waves owning a 32x32 S^T tile
 
@@ -717,6 +869,11 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
             const uint4 *pk = (const uint4 *)(bp + Bk::oK) + wave * 256 + lane;
 #pragma unroll
             for (int s = 0; s < 4; ++s) x.K[s] = pk[s * 64];
+            if constexpr (DP) {
+                const uint4 *pkb = (const uint4 *)(bp + Bk::oKb) + wave * 256 + lane;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) x.Kb[s] = pkb[s * 64];
+            }
         }
         const long tok = t0 + (long)c * kC + vr;
         x.V = *(const uint4 *)(p.v + ((size_t)(tok < t1 ? tok : t1 - 1) * H + h) * DV + j0 + vc);
@@ -736,7 +893,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     };
 
     auto step = [&](int c, Pre<DK> &x, Pre<DK> &nx) {
-        wait_vmcnt<(kDepth - 1) * kMinLoadsPerChunk<DK>>();  // operands of chunk c have arrived
+        wait_vmcnt<(kDepth - 1) * kMinLoadsPerChunk<DK, DP>>();  // operands of chunk c have arrived
         float *sG = (float *)(smem + L::oG) + (c & 1) * DK;
         if (wave == 0 && lane < DK / 4) ((float4 *)sG)[lane] = x.G;
         {
@@ -753,7 +910,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
         bf16x8 fv[4], fs[DK / 16];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if (i < 2 || rt) fv[i] = frag_tr32(sV, 16 * i, kVS, 0, lane);
+            if (i < 2 || rt || DP) fv[i] = frag_tr32(sV, 16 * i, kVS, 0, lane);
 #pragma unroll
         for (int s = 0; s < DK / 16; ++s) fs[s] = frag(sS, l32, KS, 16 * s + 8 * lh);
         f32x16 acc = {};
@@ -791,6 +948,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
         lds_barrier();  // V_new^T visible
 
         // S <- S Diag(gamma_C) + V_new^T K^ (transposed: S^T tile = K^T-tile V_new)
+        // (DP: + N^T A^ + V^T Diag(beta) K^)
         if (wave < NSW) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -803,6 +961,10 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
             for (int s = 0; s < 4; ++s) fn[s] = frag(sVn, l32, kCS, 16 * s + 8 * lh);
 #pragma unroll
             for (int s = 0; s < 4; ++s) ST = mfma32x32(as_bf16x8(x.K[s]), fn[s], ST);
+            if constexpr (DP) {  // + V^T Diag(beta) K^
+#pragma unroll
+                for (int s = 0; s < 4; ++s) ST = mfma32x32(as_bf16x8(x.Kb[s]), fv[s], ST);
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 store4(sS + l32 * KS + 32 * wave + 8 * q + 4 * lh, ST[4 * q + 0], ST[4 * q + 1],
@@ -859,7 +1021,10 @@ int compute_units() {
     return cached[dev];
 }
 
-int blk_bytes(int dk) { return dk == 128 ? Blk<128>::bytes : Blk<64>::bytes; }
+int blk_bytes(int dk, bool dp) {
+    if (dp) return dk == 128 ? Blk<128, true>::bytes : Blk<64, true>::bytes;
+    return dk == 128 ? Blk<128>::bytes : Blk<64>::bytes;
+}
 
 // Workspace: [error flag header][chunk offsets (packed sequences)][blocks].
 void split_layout(const FwdArgs &a, int N, bool varlen, size_t &coff_off, size_t &blk_off,
@@ -875,13 +1040,13 @@ void split_layout(const FwdArgs &a, int N, bool varlen, size_t &coff_off, size_t
         max_chunks = N * ncT;
         blk_off = coff_off;
     }
-    total = blk_off + (size_t)a.H * max_chunks * blk_bytes(a.dk);
+    total = blk_off + (size_t)a.H * max_chunks * blk_bytes(a.dk, a.a != nullptr);
 }
 
 }  // namespace
 
 bool kda_split_supported(const FwdArgs &a) {
-    return a.dtype == 1 && a.a == nullptr && a.b == nullptr && a.C == kC &&
+    return a.dtype == 1 && (a.a == nullptr) == (a.b == nullptr) && a.C == kC &&
            (a.dk == 64 || a.dk == 128) && a.dv % kDVT == 0;
 }
 
@@ -899,6 +1064,8 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     split_layout(a, n_seq_eff, varlen, coff_off, blk_off, nc, max_chunks, total);
     SplitParams sp;
     sp.q = (const bf16 *)a.q; sp.k = (const bf16 *)a.k; sp.v = (const bf16 *)a.v;
+    sp.a = (const bf16 *)a.a; sp.b = (const bf16 *)a.b;
+    const bool dp = a.a != nullptr;
     sp.la = a.log_alpha; sp.beta = a.beta; sp.S0 = a.S0;
     sp.O = (bf16 *)a.O; sp.Sf = a.S_final; sp.cu = a.cu_seqlens;
     char *ws = (char *)a.workspace;
@@ -911,23 +1078,27 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     sp.nc = nc; sp.max_chunks = max_chunks;
 
     if (varlen) hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kThreads), 0, s, sp);
-    // persistent prep workgroups: two per CU (their LDS allows no more)
+    // persistent prep workgroups: two per CU (one with a, b: their LDS allows no more)
     const long njobs = (long)a.H * max_chunks;
-    const long slots = 2L * compute_units();
+    const long slots = (dp ? 1L : 2L) * compute_units();
     const dim3 grid_prep((unsigned)(njobs < slots ? njobs : slots));
     const dim3 grid_state((unsigned)(((n_seq_eff * a.H + 7) / 8) * 8 * sp.n_tiles));
-#define GDR_PREP(DK, G) hipLaunchKernelGGL((kda_prep_kernel<DK, G>), grid_prep, dim3(kThreads), 0, s, sp)
+#define GDR_PREP(DK, G, D) hipLaunchKernelGGL((kda_prep_kernel<DK, G, D>), grid_prep, dim3(kThreads), 0, s, sp)
+#define GDR_PATH(DK, D)                                                                     \
+    do {                                                                                    \
+        if (a.gate == kGateChannel) GDR_PREP(DK, kGateChannel, D);                          \
+        else if (a.gate == kGateHead) GDR_PREP(DK, kGateHead, D);                           \
+        else GDR_PREP(DK, kGateNone, D);                                                    \
+        hipLaunchKernelGGL((kda_state_kernel<DK, D>), grid_state, dim3(kThreads), 0, s, sp); \
+    } while (0)
     if (a.dk == 128) {
-        if (a.gate == kGateChannel) GDR_PREP(128, kGateChannel);
-        else if (a.gate == kGateHead) GDR_PREP(128, kGateHead);
-        else GDR_PREP(128, kGateNone);
-        hipLaunchKernelGGL((kda_state_kernel<128>), grid_state, dim3(kThreads), 0, s, sp);
+        if (dp) GDR_PATH(128, true);
+        else GDR_PATH(128, false);
     } else {
-        if (a.gate == kGateChannel) GDR_PREP(64, kGateChannel);
-        else if (a.gate == kGateHead) GDR_PREP(64, kGateHead);
-        else GDR_PREP(64, kGateNone);
-        hipLaunchKernelGGL((kda_state_kernel<64>), grid_state, dim3(kThreads), 0, s, sp);
+        if (dp) GDR_PATH(64, true);
+        else GDR_PATH(64, false);
     }
+#undef GDR_PATH
 #undef GDR_PREP
     return (int)hipGetLastError();
 }

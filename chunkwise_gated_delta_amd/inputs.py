@@ -121,16 +121,18 @@ def dirichlet_lengths(rng: np.random.Generator, n_seq: int, total: int, min_len:
 
 def make_problem(kind: str, *, seed: Optional[int] = None, B=None, H=None, T=None, dk=None,
                  dv=None, n_seq=None, total=None, min_len=None, dtype=None,
-                 s0_scale=None, chunk: int = 64) -> Problem:
+                 s0_scale=None, gate=None, dplr=None, chunk: int = 64) -> Problem:
     """Build a seeded problem of workload ``kind`` (see module doc).
 
     Keyword overrides shrink or reshape a workload while keeping its value
     distributions, so small parity cases and the full-size workloads share one
-    recipe.
+    recipe.  ``gate`` swaps the gate mode (the log-decay range stays the
+    workload's); ``dplr=True`` adds distinct a, b drawn as in the ``dplr`` workload.
     """
     spec = dict(WORKLOADS[kind])
     spec.update({k: v for k, v in dict(B=B, H=H, T=T, dk=dk, dv=dv, n_seq=n_seq, total=total,
-                                        min_len=min_len, dtype=dtype, s0_scale=s0_scale).items()
+                                        min_len=min_len, dtype=dtype, s0_scale=s0_scale,
+                                        gate=gate, dplr=dplr).items()
                  if v is not None})
     if seed is None:
         seed = spec["seed"]

@@ -54,9 +54,12 @@ def test_workspace_sizes(lib):
     # ... and, for packed sequences, the chunk offsets and room for every sequence
     # to end in a partial chunk
     assert ws(1, 32, 32768, 128, 128, n_seq=8) == 256 + 256 + 32 * (512 + 8) * 61952
-    # the generic fp32 / DPLR kernel needs per-workgroup scratch
-    g = ws(1, 16, 16384, 128, 128, has_ab=True)
-    assert g == 256 + 1 * 16 * 4 * 7 * 64 * 128 * 4
+    # DPLR (bf16, distinct a, b, C = 64): the same blocks plus Diag(beta) K^ (16 KiB)
+    assert ws(1, 16, 16384, 128, 128, has_ab=True) == 256 + 16 * 256 * (61952 + 16384)
+    assert ws(1, 2, 100, 64, 64, has_ab=True) == 256 + 2 * 2 * (37120 + 8192)
+    # the generic kernel (fp32 inputs, or other chunk sizes with a, b) needs
+    # per-workgroup scratch
+    assert ws(1, 16, 16384, 128, 128, C=32, has_ab=True) > 256
     assert ws(1, 2, 256, 64, 64, dtype=__import__("torch").float32, gate=0) > 256
     # unsupported / invalid -> 0
     assert ws(1, 2, 256, 96, 64) == 0

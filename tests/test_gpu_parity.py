@@ -110,6 +110,30 @@ def test_dplr_bf16_chunks(C):
     _check(P, O, Sf)
 
 
+@pytest.mark.parametrize("T", [1, 17, 64, 65, 191])
+def test_ragged_lengths_dplr(T):
+    P = inputs.make_problem("dplr", B=2, H=2, T=T)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+
+
+@pytest.mark.parametrize("gate", [0, 1, 2])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 256), (64, 32)])
+def test_dplr_head_sizes_and_gates(gate, dk, dv):
+    P = inputs.make_problem("dplr", B=1, H=2, T=150, dk=dk, dv=dv, gate=gate)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+
+
+def test_dplr_varlen_with_initial_state():
+    # packed sequences down to a single token, per-sequence initial state
+    P = inputs.make_problem("kda_varlen", n_seq=6, total=520, min_len=1, H=3, dplr=True)
+    P.cu_seqlens = torch.tensor([0, 1, 65, 66, 200, 329, 520], dtype=torch.int32)
+    assert P.a is not None and P.S0 is not None
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+
+
 def test_nonzero_initial_state_and_inplace_final_state():
     P = inputs.make_problem("kda", B=2, H=2, T=130, s0_scale=0.3)
     assert P.S0 is not None
