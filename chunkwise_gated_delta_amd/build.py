@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgdr.so")
-SOURCES = ["gdr_api.hip", "gdr_generic.hip", "gdr_kda_split.hip"]
+SOURCES = ["gdr_api.hip", "gdr_f32_split.hip", "gdr_kda_split.hip"]
 
 # Packed fp32 ops stay off: the compiler must not form v_pk_* fp32 instructions.
 HIPCC_FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-shared", "-std=c++17",

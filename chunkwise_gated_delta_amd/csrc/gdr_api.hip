@@ -64,7 +64,8 @@ FwdArgs make_args(int B, int H, int T, int dk, int dv, int C, int n_seq, int dty
 
 size_t workspace_for(const FwdArgs &a, int n_seq_eff) {
     if (gdr::kda_split_supported(a)) return gdr::kda_split_workspace_bytes(a, n_seq_eff);
-    return gdr::generic_workspace_bytes(a, n_seq_eff);
+    if (gdr::f32_split_supported(a)) return gdr::f32_split_workspace_bytes(a, n_seq_eff);
+    return 0;
 }
 
 }  // namespace
@@ -136,8 +137,9 @@ int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
     const bool split = gdr::kda_split_supported(args);
     if (trace_enabled())
         std::fprintf(stderr, "[gdr] %s B=%d H=%d T=%d N=%d dk=%d dv=%d C=%d dtype=%d gate=%d ws=%zu\n",
-                     split ? "kda_split" : "generic", B, H, T, N, dk, dv, C, dtype, gate, need);
-    const int rc = split ? gdr::launch_kda_split(args, N, s) : gdr::launch_generic(args, N, s);
+                     split ? "kda_split" : "f32_split", B, H, T, N, dk, dv, C, dtype, gate, need);
+    if (!split && !gdr::f32_split_supported(args)) return GDR_ERR_UNSUPPORTED;
+    const int rc = split ? gdr::launch_kda_split(args, N, s) : gdr::launch_f32_split(args, N, s);
     return rc == 0 ? GDR_OK : GDR_ERR_HIP;
 }
 

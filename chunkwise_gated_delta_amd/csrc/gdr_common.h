@@ -83,8 +83,9 @@ struct FwdArgs {
 };
 
 // Launchers (return a hipError_t as int).  Each enqueues on `stream`.
-size_t generic_workspace_bytes(const FwdArgs &a, int n_seq_eff);
-int launch_generic(const FwdArgs &a, int n_seq_eff, hipStream_t stream);
+bool f32_split_supported(const FwdArgs &a);
+size_t f32_split_workspace_bytes(const FwdArgs &a, int n_seq_eff);
+int launch_f32_split(const FwdArgs &a, int n_seq_eff, hipStream_t stream);
 bool kda_split_supported(const FwdArgs &a);
 size_t kda_split_workspace_bytes(const FwdArgs &a, int n_seq_eff);
 int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t stream);

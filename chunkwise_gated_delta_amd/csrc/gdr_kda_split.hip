@@ -38,6 +38,7 @@
 // operand order of v_mfma_f32_32x32x16_bf16, so the state kernel loads them straight
 // into registers with whole-wave contiguous loads.
 #include "gdr_mfma.h"
+#include "gdr_split_common.h"
 
 namespace gdr {
 namespace {
@@ -82,80 +83,10 @@ struct SplitParams {
     char *blk;      // (chunk, head) blocks
     long total;
     int H, T, dv, n_seq, n_tiles;
+    int C;           // chunk size (always kC here)
     int nc;          // chunks per sequence (fixed-length batch)
     int max_chunks;  // blocks per head in the workspace
 };
-
-// ---------------------------------------------------------------------------------
-// Chunk offsets of packed sequences: coff[n] = sum over m < n of ceil(len_m / 64);
-// and the sequences ordered longest first (ties by index), so that the state
-// kernel, whose work per sequence is serial, starts the longest ones first when
-// there are more (sequence, head, tile) triples than CUs.  Malformed offsets are
-// clamped here (and flagged) exactly as the other kernels clamp them, so all three
-// agree on every sequence's bounds.
-// ---------------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void kda_plan_kernel(SplitParams p) {
-    __shared__ int part[kThreads];
-    const int tid = threadIdx.x, N = p.n_seq;
-    const int per = (N + kThreads - 1) / kThreads;
-    const int a = min(N, tid * per), b = min(N, a + per);
-    int s = 0;
-    for (int n = a; n < b; ++n) {
-        long t0, t1;
-        seq_bounds(p.cu, n, p.T, p.total, t0, t1, p.err);
-        s += (int)((t1 - t0 + kC - 1) / kC);
-    }
-    part[tid] = s;
-    __syncthreads();
-    if (tid == 0) {
-        int acc = 0;
-        for (int i = 0; i < kThreads; ++i) {
-            const int x = part[i];
-            part[i] = acc;
-            acc += x;
-        }
-        p.coff[N] = acc;
-    }
-    __syncthreads();
-    s = part[tid];
-    for (int n = a; n < b; ++n) {
-        p.coff[n] = s;
-        long t0, t1;
-        seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
-        s += (int)((t1 - t0 + kC - 1) / kC);
-    }
-    __syncthreads();
-    // rank of sequence n: how many sequences are longer, or as long with a lower index
-    for (int n = tid; n < N; n += kThreads) {
-        const int cn = p.coff[n + 1] - p.coff[n];
-        int rank = 0;
-        for (int m2 = 0; m2 < N; ++m2) {
-            const int cm = p.coff[m2 + 1] - p.coff[m2];
-            rank += (cm > cn) || (cm == cn && m2 < n);
-        }
-        p.order[rank] = n;
-    }
-}
-
-// Sequence n and chunk c of global chunk j; false when j is past the last chunk.
-__device__ __forceinline__ bool chunk_of(const SplitParams &p, int j, int &n, int &c) {
-    if (p.coff == nullptr) {
-        n = j / p.nc;
-        c = j - n * p.nc;
-        return true;
-    }
-    const int last = min(p.coff[p.n_seq], p.max_chunks);
-    if (j >= last) return false;
-    int lo = 0, hi = p.n_seq - 1;  // last n with coff[n] <= j
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (p.coff[mid] <= j) lo = mid;
-        else hi = mid - 1;
-    }
-    n = lo;
-    c = j - p.coff[lo];
-    return true;
-}
 
 // ---------------------------------------------------------------------------------
 // Prep kernel
@@ -1026,23 +957,6 @@ int blk_bytes(int dk, bool dp) {
     return dk == 128 ? Blk<128>::bytes : Blk<64>::bytes;
 }
 
-// Workspace: [error flag header][chunk offsets (packed sequences)][blocks].
-void split_layout(const FwdArgs &a, int N, bool varlen, size_t &coff_off, size_t &blk_off,
-                  int &nc, int &max_chunks, size_t &total) {
-    const int ncT = (a.T + kC - 1) / kC;
-    coff_off = kWorkspaceHeader;
-    if (varlen) {
-        nc = 0;
-        max_chunks = ncT + N;
-        blk_off = coff_off + (((size_t)(2 * N + 1) * 4 + 255) / 256) * 256;  // coff, order
-    } else {
-        nc = ncT;
-        max_chunks = N * ncT;
-        blk_off = coff_off;
-    }
-    total = blk_off + (size_t)a.H * max_chunks * blk_bytes(a.dk, a.a != nullptr);
-}
-
 }  // namespace
 
 bool kda_split_supported(const FwdArgs &a) {
@@ -1051,17 +965,13 @@ bool kda_split_supported(const FwdArgs &a) {
 }
 
 size_t kda_split_workspace_bytes(const FwdArgs &a, int n_seq_eff) {
-    size_t coff_off, blk_off, total;
-    int nc, max_chunks;
-    split_layout(a, n_seq_eff, a.cu_seqlens != nullptr, coff_off, blk_off, nc, max_chunks, total);
-    return total;
+    return split_layout(a, n_seq_eff, blk_bytes(a.dk, a.a != nullptr)).total;
 }
 
 int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     const bool varlen = a.cu_seqlens != nullptr;
-    size_t coff_off, blk_off, total;
-    int nc, max_chunks;
-    split_layout(a, n_seq_eff, varlen, coff_off, blk_off, nc, max_chunks, total);
+    const SplitLayout lay = split_layout(a, n_seq_eff, blk_bytes(a.dk, a.a != nullptr));
+    const int max_chunks = lay.max_chunks;
     SplitParams sp;
     sp.q = (const bf16 *)a.q; sp.k = (const bf16 *)a.k; sp.v = (const bf16 *)a.v;
     sp.a = (const bf16 *)a.a; sp.b = (const bf16 *)a.b;
@@ -1070,14 +980,14 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     sp.O = (bf16 *)a.O; sp.Sf = a.S_final; sp.cu = a.cu_seqlens;
     char *ws = (char *)a.workspace;
     sp.err = (int *)ws;
-    sp.coff = varlen ? (int32_t *)(ws + coff_off) : nullptr;
+    sp.coff = varlen ? (int32_t *)(ws + lay.coff_off) : nullptr;
     sp.order = varlen ? sp.coff + n_seq_eff + 1 : nullptr;
-    sp.blk = ws + blk_off;
+    sp.blk = ws + lay.blk_off;
     sp.total = (long)a.B * a.T;
     sp.H = a.H; sp.T = a.T; sp.dv = a.dv; sp.n_seq = n_seq_eff; sp.n_tiles = a.dv / kDVT;
-    sp.nc = nc; sp.max_chunks = max_chunks;
+    sp.nc = lay.nc; sp.max_chunks = max_chunks; sp.C = kC;
 
-    if (varlen) hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kThreads), 0, s, sp);
+    if (varlen) hipLaunchKernelGGL((chunk_plan_kernel<SplitParams>), dim3(1), dim3(kPlanThreads), 0, s, sp);
     // persistent prep workgroups: two per CU (one with a, b: their LDS allows no more)
     const long njobs = (long)a.H * max_chunks;
     const long slots = (dp ? 1L : 2L) * compute_units();

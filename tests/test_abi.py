@@ -57,10 +57,12 @@ def test_workspace_sizes(lib):
     # DPLR (bf16, distinct a, b, C = 64): the same blocks plus Diag(beta) K^ (16 KiB)
     assert ws(1, 16, 16384, 128, 128, has_ab=True) == 256 + 16 * 256 * (61952 + 16384)
     assert ws(1, 2, 100, 64, 64, has_ab=True) == 256 + 2 * 2 * (37120 + 8192)
-    # the generic kernel (fp32 inputs, or other chunk sizes with a, b) needs
-    # per-workgroup scratch
-    assert ws(1, 16, 16384, 128, 128, C=32, has_ab=True) > 256
-    assert ws(1, 2, 256, 64, 64, dtype=__import__("torch").float32, gate=0) > 256
+    # the fp32 kernels (fp32 inputs, or other chunk sizes with a, b) keep one fp32 block
+    # per (chunk, head): W', Q~, K^ (+ Diag(beta) K^) [C][dk], two [C][C], gamma [dk],
+    # rounded up to 64 floats
+    blk = lambda C, dk, dp: -(-((4 if dp else 3) * C * dk + 2 * C * C + dk) // 64) * 64 * 4
+    assert ws(1, 2, 256, 64, 64, dtype=__import__("torch").float32, gate=0) == 256 + 2 * 4 * blk(64, 64, False)
+    assert ws(1, 16, 16384, 128, 128, C=32, has_ab=True) == 256 + 16 * 512 * blk(32, 128, True)
     # unsupported / invalid -> 0
     assert ws(1, 2, 256, 96, 64) == 0
     assert ws(1, 2, 256, 128, 48) == 0
