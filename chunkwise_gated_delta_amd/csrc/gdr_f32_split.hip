@@ -501,10 +501,193 @@ __global__ __launch_bounds__(kFT) void f32_state_kernel(F32Params p) {
     }
 }
 
+// At dk = 64 the whole fp32 block of a chunk fits in LDS next to the state: the staged
+// variant copies each chunk's block (rows padded by 4 floats) and value tile into LDS
+// and loads the next chunk's into registers while it computes, so a chunk costs one
+// memory latency hidden behind the previous chunk instead of several exposed ones.
+template <int C, bool DP>
+struct F32StagedSmem {  // offsets in floats; dk = 64
+    static constexpr int RS = 64 + 4;                  // row stride of [C][dk] matrices
+    static constexpr int CS = C + 4;                   // row stride of [C][C] matrices
+    static constexpr int VS = kFDVT + 4;               // row stride of [*][32] tiles
+    static constexpr int oW = 0;
+    static constexpr int oQ = oW + C * RS;
+    static constexpr int oK = oQ + C * RS;
+    static constexpr int oKb = oK + C * RS;            // DP only
+    static constexpr int oAb = oKb + (DP ? C * RS : 0);
+    static constexpr int oAo = oAb + C * CS;
+    static constexpr int oG = oAo + C * CS;
+    static constexpr int oDump = oG + 64;              // 4 floats: target of the padding copies
+    static constexpr int oST = oDump + 4;              // S^T [64][VS]
+    static constexpr int oV = oST + 64 * VS;           // V [C][VS]
+    static constexpr int oVn = oV + C * VS;            // V_new (N) [C][VS]
+    static constexpr int floats = oVn + C * VS;
+    static_assert(floats * 4 <= 160 * 1024, "LDS");
+};
+
+template <typename Tin, int C, bool DP>
+__global__ __launch_bounds__(kFT) void f32_state_staged_kernel(F32Params p) {
+    using L = F32StagedSmem<C, DP>;
+    constexpr int DK = 64;
+    constexpr int VS = L::VS;
+    constexpr int TPR = kFT / C;       // phase 1: threads per chunk row
+    constexpr int JW = kFDVT / TPR;    // phase 1: dv columns per thread
+    constexpr int kJS = 8;             // phase 2: dv columns per item
+    constexpr int NB4 = ((DP ? 4 : 3) * C * DK + 2 * C * C + DK) / 4;  // float4 of a block's data
+    constexpr int NPF = (NB4 + kFT - 1) / kFT;                          // per thread
+    constexpr int NPV = C * kFDVT / kFT;                                // value elements per thread
+    __shared__ __attribute__((aligned(16))) float smem[L::floats];
+    float *sST = smem + L::oST, *sV = smem + L::oV, *sVn = smem + L::oVn;
+
+    const Tin *v = (const Tin *)p.v;
+    Tin *O = (Tin *)p.O;
+    const int tid = threadIdx.x, H = p.H, DV = p.dv;
+    const int lin = blockIdx.x;
+    const int tile = lin % p.n_tiles;
+    const int h = (lin / p.n_tiles) % H;
+    const int rank = lin / (p.n_tiles * H);
+    const int n = p.order ? p.order[rank] : rank;
+    const int j0 = tile * kFDVT;
+    long t0, t1;
+    seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
+    int nck = (int)((t1 - t0 + C - 1) / C);
+    long cbase;
+    if (p.coff) {
+        cbase = p.coff[n];
+        const long room = p.max_chunks - cbase;
+        nck = (int)(room < 0 ? 0 : (room < nck ? room : nck));
+    } else {
+        cbase = (long)n * p.nc;
+    }
+
+    for (int idx = tid; idx < DK * kFDVT; idx += kFT) {
+        const int j = idx / DK, d = idx % DK;
+        sST[d * VS + j] = p.S0 ? p.S0[(((size_t)n * H + h) * DV + j0 + j) * DK + d] : 0.f;
+    }
+
+    // LDS position of the block's float4 number e4 (block order: W', Q~, K^, [K^b],
+    // Ab, Ao, gamma_C; each matrix row-major, rows padded in LDS).
+    // Float4 numbers past the block's data go to a dump slot, so every thread stores
+    // the same number of values with no branch.
+    auto lds_pos = [&](int e4) __attribute__((always_inline)) {
+        const int e = 4 * e4;
+        constexpr int nm = DP ? 4 : 3;
+        const int f = e - nm * C * DK;
+        const int pm = L::oW + (e / DK) * L::RS + e % DK;  // the [C][dk] matrices are stacked
+        const int pc = L::oAb + (f / C) * L::CS + f % C;    // so are the two [C][C] ones
+        const int pg = L::oG + (f - 2 * C * C);
+        return e4 >= NB4 ? L::oDump : (f < 0 ? pm : (f < 2 * C * C ? pc : pg));
+    };
+    // Loads of chunk c's block and value tile into registers (native vector type: HIP's
+    // float4 class is copied through memory, which would put these registers in scratch).
+#define GDR_F32_FETCH(c)                                                                            \
+    do {                                                                                            \
+        const f32x4 *bp_ = (const f32x4 *)(p.blk + ((size_t)(cbase + (c)) * H + h) * p.bf);         \
+        _Pragma("unroll") for (int u = 0; u < NPF; ++u) {                                           \
+            const int e4 = tid + kFT * u;                                                           \
+            pf[u] = bp_[e4 < NB4 ? e4 : 0];                                                         \
+        }                                                                                           \
+        const long tc0_ = t0 + (long)(c) * C;                                                       \
+        _Pragma("unroll") for (int u = 0; u < NPV; ++u) {                                           \
+            const int idx = tid + kFT * u, r = idx / kFDVT, j = idx % kFDVT;                        \
+            const long tok = tc0_ + r < t1 ? tc0_ + r : t1 - 1;                                     \
+            pv[u] = ld(v, ((size_t)tok * H + h) * DV + j0 + j);                                     \
+        }                                                                                           \
+    } while (0)
+    f32x4 pf[NPF];
+    float pv[NPV];
+    if (nck > 0) GDR_F32_FETCH(0);
+
+    const int r1 = tid / TPR, jc = JW * (tid % TPR);  // phase 1
+    for (int c = 0; c < nck; ++c) {
+        const long tc0 = t0 + (long)c * C;
+        const int m = (int)((t1 - tc0) < C ? (t1 - tc0) : C);
+#pragma unroll
+        for (int u = 0; u < NPF; ++u) *(f32x4 *)(smem + lds_pos(tid + kFT * u)) = pf[u];
+#pragma unroll
+        for (int u = 0; u < NPV; ++u) {
+            const int idx = tid + kFT * u, r = idx / kFDVT, j = idx % kFDVT;
+            sV[r * VS + j] = r < m ? pv[u] : 0.f;
+        }
+        lds_barrier();  // chunk c in LDS; S^T of chunk c visible
+        if (c + 1 < nck) GDR_F32_FETCH(c + 1);
+
+        // V_new (N) and O rows: row r1, columns jc..jc+JW-1
+        {
+            float vn[JW] = {}, o[JW] = {};
+            const float *ab = smem + L::oAb + r1 * L::CS, *ao = smem + L::oAo + r1 * L::CS;
+            for (int i4 = 0; i4 < C / 4; ++i4) {
+                const float4 x = *(const float4 *)(ab + 4 * i4), y = *(const float4 *)(ao + 4 * i4);
+                const float xv[4] = {x.x, x.y, x.z, x.w}, yv[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int jj = 0; jj < JW; ++jj) {
+                        const float vv = sV[(4 * i4 + e) * VS + jc + jj];
+                        vn[jj] += xv[e] * vv;
+                        o[jj] += yv[e] * vv;
+                    }
+            }
+            const float *wr = smem + L::oW + r1 * L::RS, *qr = smem + L::oQ + r1 * L::RS;
+            for (int d4 = 0; d4 < DK / 4; ++d4) {
+                const float4 x = *(const float4 *)(wr + 4 * d4), y = *(const float4 *)(qr + 4 * d4);
+                const float xv[4] = {x.x, x.y, x.z, x.w}, yv[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int jj = 0; jj < JW; ++jj) {
+                        const float s = sST[(4 * d4 + e) * VS + jc + jj];
+                        vn[jj] += xv[e] * s;
+                        o[jj] += yv[e] * s;
+                    }
+            }
+#pragma unroll
+            for (int jj = 0; jj < JW; ++jj) sVn[r1 * VS + jc + jj] = vn[jj];
+            if (r1 < m) {
+#pragma unroll
+                for (int jj = 0; jj < JW; ++jj) st(O, ((size_t)(tc0 + r1) * H + h) * DV + j0 + jc + jj, o[jj]);
+            }
+        }
+        lds_barrier();
+
+        // S^T[d][js..] = gamma_C S^T + K^^T V_new (+ (Diag(beta) K^)^T V); one item per thread
+        {
+            const int d2 = tid % DK, js = kJS * (tid / DK);
+            float acc[kJS];
+            const float gm = smem[L::oG + d2];
+#pragma unroll
+            for (int jj = 0; jj < kJS; ++jj) acc[jj] = gm * sST[d2 * VS + js + jj];
+            for (int r = 0; r < C; ++r) {
+                const float kh = smem[L::oK + r * L::RS + d2];
+                const float kb = DP ? smem[L::oKb + r * L::RS + d2] : 0.f;
+#pragma unroll
+                for (int jj = 0; jj < kJS; ++jj) {
+                    acc[jj] += kh * sVn[r * VS + js + jj];
+                    if (DP) acc[jj] += kb * sV[r * VS + js + jj];
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < kJS; ++jj) sST[d2 * VS + js + jj] = acc[jj];
+        }
+        lds_barrier();  // before the next chunk overwrites the block, V and V_new
+    }
+
+    if (p.Sf) {
+        for (int idx = tid; idx < DK * kFDVT; idx += kFT) {
+            const int j = idx / DK, d = idx % DK;
+            p.Sf[(((size_t)n * H + h) * DV + j0 + j) * DK + d] = sST[d * VS + j];
+        }
+    }
+#undef GDR_F32_FETCH
+}
+
 template <typename Tin, int C, bool DP>
 void f32_launch(const F32Params &fp, dim3 gp, dim3 gs, hipStream_t s) {
     hipLaunchKernelGGL((f32_prep_kernel<Tin, C, DP>), gp, dim3(kFT), 0, s, fp);
-    hipLaunchKernelGGL((f32_state_kernel<Tin, C, DP>), gs, dim3(kFT), 0, s, fp);
+    if (fp.dk == 64)
+        hipLaunchKernelGGL((f32_state_staged_kernel<Tin, C, DP>), gs, dim3(kFT), 0, s, fp);
+    else
+        hipLaunchKernelGGL((f32_state_kernel<Tin, C, DP>), gs, dim3(kFT), 0, s, fp);
 }
 
 }  // namespace
