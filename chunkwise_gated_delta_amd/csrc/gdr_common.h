@@ -63,14 +63,6 @@ __device__ __forceinline__ void seq_bounds(const int32_t *cu, int n, int T, long
     t1 = cb;
 }
 
-// Workgroup id -> linear work index so that consecutive indices (the dv-tiles of
-// one (sequence, head) pair) land on the same XCD: workgroups are dispatched
-// round-robin over the 8 XCDs, so ids that are equal mod 8 share an L2.
-__device__ __forceinline__ int xcd_linear_index(int bid, int nblocks) {
-    if ((nblocks & 7) != 0) return bid;
-    return (bid & 7) * (nblocks >> 3) + (bid >> 3);
-}
-
 struct FwdArgs {
     const void *q, *k, *v, *a, *b;
     const float *log_alpha, *beta, *S0;

@@ -142,8 +142,6 @@ __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitPar
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15, lg = lane >> 4;
     const int H = p.H;
     const int njobs = H * p.max_chunks;
     const int rg = tid >> 5, cg = tid & 31, c0 = CPT * cg;

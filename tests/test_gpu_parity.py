@@ -103,6 +103,16 @@ def test_fp32_all_modes_and_chunks(kind, C):
     _check(P, O, Sf, tol=TOL[torch.float32])
 
 
+@pytest.mark.parametrize("kind", ["deltanet_f32", "gdn", "kda", "dplr"])
+@pytest.mark.parametrize("C", [32, 64])
+def test_fp32_dk128(kind, C):
+    # dk = 128: two 64-channel operand blocks in the fp32 prep kernel and the streaming
+    # (unstaged) fp32 state kernel; ragged length
+    P = inputs.make_problem(kind, B=1, H=2, T=150, dk=128, dv=64, dtype=torch.float32, chunk=C)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf, tol=TOL[torch.float32])
+
+
 @pytest.mark.parametrize("C", [16, 32, 64])
 def test_dplr_bf16_chunks(C):
     P = inputs.make_problem("dplr", B=1, H=2, T=200, chunk=C)
