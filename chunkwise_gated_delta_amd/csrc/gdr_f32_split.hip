@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
         }
         if (tid < C) sGh[tid] = x;
     }
-    __syncthreads();
+    lds_barrier();
 
     // Operands of channel block db into LDS: thread (channel d, row group rg).  With
     // `first`, also K->, A-> and the block's K^ / A^ / Diag(beta) K^ / gamma_C.
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
         float gC = 0.f;
         if (p.gate == kGateChannel) {
             sTot[rg * kDB + d] = run;
-            __syncthreads();
+            lds_barrier();
             float carry = 0.f;
 #pragma unroll
             for (int r2 = 0; r2 < 4; ++r2) {
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
             }
         }
         if (first && rg == 0) bp[B.oG + col] = expf(gC);
-        __syncthreads();
+        lds_barrier();
     };
 
     // C x C products accumulate over the channel blocks; thread tile rows R0.., cols I0..
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
                     }
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 #pragma unroll
     for (int x = 0; x < TR; ++x)
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
                 sAqk[r * CS + i] = i <= r ? accQ[x][y] : 0.f;
             }
         }
-    __syncthreads();
+    lds_barrier();
 
     // (I + L)^-1: thread c solves column c, x_r = [r == c] - sum_{i<r} L[r][i] x_i
     // (x_r = 0 above the diagonal follows without masking).
@@ -239,12 +239,12 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
                 x[r] = (r == tid ? 1.f : 0.f) - (s0 + s1);
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < C) {
 #pragma unroll
             for (int r = 0; r < C; ++r) sL[r * CS + tid] = x[r];
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // C x C x C products on thread tiles: acc = sum_k A[R0+x][k] Bm[k][I0+y]
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
         for (int x = 0; x < TR; ++x)
 #pragma unroll
             for (int y = 0; y < TR; ++y) sEc[(R0 + x) * CS + I0 + y] = -acc[x][y];
-        __syncthreads();
+        lds_barrier();
         float acc2[TR][TR];
 #pragma unroll
         for (int x = 0; x < TR; ++x)
@@ -280,21 +280,21 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
         for (int x = 0; x < TR; ++x)
 #pragma unroll
             for (int y = 0; y < TR; ++y) sAqk[(R0 + x) * CS + I0 + y] = acc2[x][y];
-        __syncthreads();
+        lds_barrier();
     } else {
         for (int idx = tid; idx < C * C; idx += kFT) {  // Ab = At Diag(beta)
             const int r = idx / C, i = idx % C;
             sL[r * CS + i] *= sBeta[i];
         }
-        __syncthreads();
+        lds_barrier();
         float acc[TR][TR] = {};
         mm(sAqk, sL, acc);  // Ao = A_qk Ab
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int x = 0; x < TR; ++x)
 #pragma unroll
             for (int y = 0; y < TR; ++y) sAqk[(R0 + x) * CS + I0 + y] = acc[x][y];
-        __syncthreads();
+        lds_barrier();
     }
     for (int idx = tid; idx < C * C; idx += kFT) {
         const int r = idx / C, i = idx % C;
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
                 bp[B.oW + r * dk + col] = -w[x][y];
                 if (DP) sKr[r * kOS + 4 * tc + y] = -w[x][y];
             }
-        if (DP) __syncthreads();
+        if (DP) lds_barrier();
         float o[TR][4] = {};
         const float *Am = DP ? sAqa : sAqk;  // Q~ = Q<- + Aqa W'  |  Q<- - Ao K<-
         const float *Bm = DP ? sKr : sKl;
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
                 const float ql = sQl[r * kOS + cc];
                 bp[B.oQ + r * dk + db * kDB + cc] = DP ? ql + o[x][y] : ql - o[x][y];
             }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kFT) void f32_state_kernel(F32Params p) {
             sV[r * VS + j] = r < m ? ld(v, ((size_t)(tc0 + r) * H + h) * DV + j0 + j) : 0.f;
         }
         for (int d = tid; d < dk; d += kFT) sGam[d] = bp[B.oG + d];
-        __syncthreads();
+        lds_barrier();
 
         // V_new (N) and O rows: row r1, columns jc..jc+JW-1
         {
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kFT) void f32_state_kernel(F32Params p) {
                 for (int jj = 0; jj < JW; ++jj) st(O, ((size_t)(tc0 + r1) * H + h) * DV + j0 + jc + jj, o[jj]);
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // S^T[d][js..] = gamma_C S^T + K^^T V_new (+ (Diag(beta) K^)^T V), items of one
         // channel and 8 dv columns (1 per thread at dk = 64, 2 at dk = 128)
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(kFT) void f32_state_kernel(F32Params p) {
 #pragma unroll
             for (int jj = 0; jj < kJS; ++jj) sST[d2 * VS + js + jj] = acc[jj];
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     if (p.Sf) {
@@ -505,11 +505,11 @@ __global__ __launch_bounds__(kFT) void f32_state_kernel(F32Params p) {
 // variant copies each chunk's block (rows padded by 4 floats) and value tile into LDS
 // and loads the next chunk's into registers while it computes, so a chunk costs one
 // memory latency hidden behind the previous chunk instead of several exposed ones.
-template <int C, bool DP>
+template <int C, bool DP, int DVT>
 struct F32StagedSmem {  // offsets in floats; dk = 64
     static constexpr int RS = 64 + 4;                  // row stride of [C][dk] matrices
     static constexpr int CS = C + 4;                   // row stride of [C][C] matrices
-    static constexpr int VS = kFDVT + 4;               // row stride of [*][32] tiles
+    static constexpr int VS = DVT + 4;                 // row stride of [*][DVT] tiles
     static constexpr int oW = 0;
     static constexpr int oQ = oW + C * RS;
     static constexpr int oK = oQ + C * RS;
@@ -525,17 +525,21 @@ struct F32StagedSmem {  // offsets in floats; dk = 64
     static_assert(floats * 4 <= 160 * 1024, "LDS");
 };
 
-template <typename Tin, int C, bool DP>
+// DVT (dv columns per workgroup) is 32, or 8 for problems too small to fill the GPU.
+template <typename Tin, int C, bool DP, int DVT>
 __global__ __launch_bounds__(kFT) void f32_state_staged_kernel(F32Params p) {
-    using L = F32StagedSmem<C, DP>;
+    using L = F32StagedSmem<C, DP, DVT>;
     constexpr int DK = 64;
     constexpr int VS = L::VS;
-    constexpr int TPR = kFT / C;       // phase 1: threads per chunk row
-    constexpr int JW = kFDVT / TPR;    // phase 1: dv columns per thread
-    constexpr int kJS = 8;             // phase 2: dv columns per item
+    constexpr int TPR = kFT / C < DVT ? kFT / C : DVT;  // phase 1: threads per chunk row
+    constexpr int JW = DVT / TPR;                       // phase 1: dv columns per thread
+    constexpr int NT1 = C * TPR;                        // phase 1: busy threads
+    constexpr int kJS = DVT < 8 ? DVT : 8;              // phase 2: dv columns per item
+    constexpr int NT2 = DK * (DVT / kJS);               // phase 2: items (<= threads)
+    static_assert(NT1 <= kFT && NT2 <= kFT, "one item per thread");
     constexpr int NB4 = ((DP ? 4 : 3) * C * DK + 2 * C * C + DK) / 4;  // float4 of a block's data
     constexpr int NPF = (NB4 + kFT - 1) / kFT;                          // per thread
-    constexpr int NPV = C * kFDVT / kFT;                                // value elements per thread
+    constexpr int NPV = (C * DVT + kFT - 1) / kFT;                      // value elements per thread
     __shared__ __attribute__((aligned(16))) float smem[L::floats];
     float *sST = smem + L::oST, *sV = smem + L::oV, *sVn = smem + L::oVn;
 
@@ -547,7 +551,7 @@ __global__ __launch_bounds__(kFT) void f32_state_staged_kernel(F32Params p) {
     const int h = (lin / p.n_tiles) % H;
     const int rank = lin / (p.n_tiles * H);
     const int n = p.order ? p.order[rank] : rank;
-    const int j0 = tile * kFDVT;
+    const int j0 = tile * DVT;
     long t0, t1;
     seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
     int nck = (int)((t1 - t0 + C - 1) / C);
@@ -560,7 +564,7 @@ __global__ __launch_bounds__(kFT) void f32_state_staged_kernel(F32Params p) {
         cbase = (long)n * p.nc;
     }
 
-    for (int idx = tid; idx < DK * kFDVT; idx += kFT) {
+    for (int idx = tid; idx < DK * DVT; idx += kFT) {
         const int j = idx / DK, d = idx % DK;
         sST[d * VS + j] = p.S0 ? p.S0[(((size_t)n * H + h) * DV + j0 + j) * DK + d] : 0.f;
     }
@@ -589,7 +593,7 @@ __global__ __launch_bounds__(kFT) void f32_state_staged_kernel(F32Params p) {
         }                                                                                           \
         const long tc0_ = t0 + (long)(c) * C;                                                       \
         _Pragma("unroll") for (int u = 0; u < NPV; ++u) {                                           \
-            const int idx = tid + kFT * u, r = idx / kFDVT, j = idx % kFDVT;                        \
+            const int idx = (tid + kFT * u) % (C * DVT), r = idx / DVT, j = idx % DVT;              \
             const long tok = tc0_ + r < t1 ? tc0_ + r : t1 - 1;                                     \
             pv[u] = ld(v, ((size_t)tok * H + h) * DV + j0 + j);                                     \
         }                                                                                           \
@@ -606,16 +610,17 @@ __global__ __launch_bounds__(kFT) void f32_state_staged_kernel(F32Params p) {
         for (int u = 0; u < NPF; ++u) *(f32x4 *)(smem + lds_pos(tid + kFT * u)) = pf[u];
 #pragma unroll
         for (int u = 0; u < NPV; ++u) {
-            const int idx = tid + kFT * u, r = idx / kFDVT, j = idx % kFDVT;
-            sV[r * VS + j] = r < m ? pv[u] : 0.f;
+            const int idx = tid + kFT * u, r = (idx % (C * DVT)) / DVT, j = idx % DVT;
+            if (idx < C * DVT) sV[r * VS + j] = r < m ? pv[u] : 0.f;
         }
         lds_barrier();  // chunk c in LDS; S^T of chunk c visible
         if (c + 1 < nck) GDR_F32_FETCH(c + 1);
 
         // V_new (N) and O rows: row r1, columns jc..jc+JW-1
-        {
+        if (tid < NT1) {
             float vn[JW] = {}, o[JW] = {};
             const float *ab = smem + L::oAb + r1 * L::CS, *ao = smem + L::oAo + r1 * L::CS;
+#pragma unroll 4
             for (int i4 = 0; i4 < C / 4; ++i4) {
                 const float4 x = *(const float4 *)(ab + 4 * i4), y = *(const float4 *)(ao + 4 * i4);
                 const float xv[4] = {x.x, x.y, x.z, x.w}, yv[4] = {y.x, y.y, y.z, y.w};
@@ -629,6 +634,7 @@ __global__ __launch_bounds__(kFT) void f32_state_staged_kernel(F32Params p) {
                     }
             }
             const float *wr = smem + L::oW + r1 * L::RS, *qr = smem + L::oQ + r1 * L::RS;
+#pragma unroll 4
             for (int d4 = 0; d4 < DK / 4; ++d4) {
                 const float4 x = *(const float4 *)(wr + 4 * d4), y = *(const float4 *)(qr + 4 * d4);
                 const float xv[4] = {x.x, x.y, x.z, x.w}, yv[4] = {y.x, y.y, y.z, y.w};
@@ -651,12 +657,13 @@ __global__ __launch_bounds__(kFT) void f32_state_staged_kernel(F32Params p) {
         lds_barrier();
 
         // S^T[d][js..] = gamma_C S^T + K^^T V_new (+ (Diag(beta) K^)^T V); one item per thread
-        {
+        if (tid < NT2) {
             const int d2 = tid % DK, js = kJS * (tid / DK);
             float acc[kJS];
             const float gm = smem[L::oG + d2];
 #pragma unroll
             for (int jj = 0; jj < kJS; ++jj) acc[jj] = gm * sST[d2 * VS + js + jj];
+#pragma unroll 8
             for (int r = 0; r < C; ++r) {
                 const float kh = smem[L::oK + r * L::RS + d2];
                 const float kb = DP ? smem[L::oKb + r * L::RS + d2] : 0.f;
@@ -673,7 +680,7 @@ __global__ __launch_bounds__(kFT) void f32_state_staged_kernel(F32Params p) {
     }
 
     if (p.Sf) {
-        for (int idx = tid; idx < DK * kFDVT; idx += kFT) {
+        for (int idx = tid; idx < DK * DVT; idx += kFT) {
             const int j = idx / DK, d = idx % DK;
             p.Sf[(((size_t)n * H + h) * DV + j0 + j) * DK + d] = sST[d * VS + j];
         }
@@ -681,11 +688,19 @@ __global__ __launch_bounds__(kFT) void f32_state_staged_kernel(F32Params p) {
 #undef GDR_F32_FETCH
 }
 
+// dv columns per state workgroup at dk = 64: 8 when 32 would leave most of the GPU idle.
+int f32_dvt(const FwdArgs &a, int n_seq_eff) {
+    return a.dk == 64 && (long)n_seq_eff * a.H * (a.dv / kFDVT) < 64 ? 8 : kFDVT;
+}
+
 template <typename Tin, int C, bool DP>
-void f32_launch(const F32Params &fp, dim3 gp, dim3 gs, hipStream_t s) {
+void f32_launch(const F32Params &fp, dim3 gp, hipStream_t s, int dvt) {
     hipLaunchKernelGGL((f32_prep_kernel<Tin, C, DP>), gp, dim3(kFT), 0, s, fp);
-    if (fp.dk == 64)
-        hipLaunchKernelGGL((f32_state_staged_kernel<Tin, C, DP>), gs, dim3(kFT), 0, s, fp);
+    const dim3 gs((unsigned)(fp.n_seq * fp.H * fp.n_tiles));
+    if (fp.dk == 64 && dvt == 8)
+        hipLaunchKernelGGL((f32_state_staged_kernel<Tin, C, DP, 8>), gs, dim3(kFT), 0, s, fp);
+    else if (fp.dk == 64)
+        hipLaunchKernelGGL((f32_state_staged_kernel<Tin, C, DP, kFDVT>), gs, dim3(kFT), 0, s, fp);
     else
         hipLaunchKernelGGL((f32_state_kernel<Tin, C, DP>), gs, dim3(kFT), 0, s, fp);
 }
@@ -720,25 +735,25 @@ int launch_f32_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     fp.blk = (float *)(ws + lay.blk_off);
     fp.total = (long)a.B * a.T;
     fp.H = a.H; fp.T = a.T; fp.dk = a.dk; fp.dv = a.dv; fp.n_seq = n_seq_eff;
-    fp.n_tiles = a.dv / kFDVT; fp.C = a.C; fp.gate = a.gate;
+    const int dvt = f32_dvt(a, n_seq_eff);
+    fp.n_tiles = a.dv / dvt; fp.C = a.C; fp.gate = a.gate;
     fp.nc = lay.nc; fp.max_chunks = lay.max_chunks; fp.bf = B.floats;
 
     if (varlen) hipLaunchKernelGGL((chunk_plan_kernel<F32Params>), dim3(1), dim3(kPlanThreads), 0, s, fp);
     const dim3 gp((unsigned)((long)a.H * lay.max_chunks));
-    const dim3 gs((unsigned)(n_seq_eff * a.H * fp.n_tiles));
     if (a.dtype == 0) {
         if (dp) {
-            if (a.C == 16) f32_launch<float, 16, true>(fp, gp, gs, s);
-            else if (a.C == 32) f32_launch<float, 32, true>(fp, gp, gs, s);
-            else f32_launch<float, 64, true>(fp, gp, gs, s);
+            if (a.C == 16) f32_launch<float, 16, true>(fp, gp, s, dvt);
+            else if (a.C == 32) f32_launch<float, 32, true>(fp, gp, s, dvt);
+            else f32_launch<float, 64, true>(fp, gp, s, dvt);
         } else {
-            if (a.C == 16) f32_launch<float, 16, false>(fp, gp, gs, s);
-            else if (a.C == 32) f32_launch<float, 32, false>(fp, gp, gs, s);
-            else f32_launch<float, 64, false>(fp, gp, gs, s);
+            if (a.C == 16) f32_launch<float, 16, false>(fp, gp, s, dvt);
+            else if (a.C == 32) f32_launch<float, 32, false>(fp, gp, s, dvt);
+            else f32_launch<float, 64, false>(fp, gp, s, dvt);
         }
     } else {
-        if (a.C == 16) f32_launch<bf16, 16, true>(fp, gp, gs, s);
-        else f32_launch<bf16, 32, true>(fp, gp, gs, s);
+        if (a.C == 16) f32_launch<bf16, 16, true>(fp, gp, s, dvt);
+        else f32_launch<bf16, 32, true>(fp, gp, s, dvt);
     }
     return (int)hipGetLastError();
 }

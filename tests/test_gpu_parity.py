@@ -113,6 +113,14 @@ def test_fp32_dk128(kind, C):
     _check(P, O, Sf, tol=TOL[torch.float32])
 
 
+@pytest.mark.parametrize("kind", ["kda", "dplr"])
+def test_fp32_dk64_wide_tiles(kind):
+    # enough (sequence, head) pairs for the 32-column tiles of the staged fp32 state kernel
+    P = inputs.make_problem(kind, B=2, H=16, T=130, dk=64, dv=64, dtype=torch.float32)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf, tol=TOL[torch.float32])
+
+
 @pytest.mark.parametrize("C", [16, 32, 64])
 def test_dplr_bf16_chunks(C):
     P = inputs.make_problem("dplr", B=1, H=2, T=200, chunk=C)
