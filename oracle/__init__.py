@@ -33,7 +33,7 @@ def _lib():
         P = ctypes.c_void_p
         I = ctypes.c_int
         lib.gdr_ref_fwd.restype = I
-        lib.gdr_ref_fwd.argtypes = [P, P, P, P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, P, I, I]
+        lib.gdr_ref_fwd.argtypes = [P, P, P, P, P, P, I, I, P, P, P, P, P, I, I, I, I, I, I, P, I, I]
         lib.gdr_ref_max_threads.restype = I
         lib.gdr_ref_max_threads.argtypes = []
         _LIB = lib
@@ -55,8 +55,12 @@ def _ptr(x):
 
 
 def recurrence(q, k, v, beta, log_alpha=None, a=None, b=None, S0=None, cu_seqlens=None,
-               chains=None, n_threads: int = 0, want_state: bool = True):
+               chains=None, n_threads: int = 0, want_state: bool = True, clip: bool = False):
     """Run the fp64 recurrence.
+
+    clip: spectral clipping of the gate, alpha_t <- min(alpha_t, 1/||I - b_t a_t^T||_2)
+    per token ("How to make GDN2 more stable", eq. 7; also without a gate, where
+    alpha_t = 1/rho_t).
 
     q, k, a, b: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H];
     log_alpha: None (no gate), [B, T, H] (head gate) or [B, T, H, dk] (channel gate);
@@ -96,8 +100,8 @@ def recurrence(q, k, v, beta, log_alpha=None, a=None, b=None, S0=None, cu_seqlen
         ch = np.ascontiguousarray(np.asarray(chains, dtype=np.int32).reshape(-1, 2))
         n_ch = ch.shape[0]
     rc = _lib().gdr_ref_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha), gate,
-                            _ptr(beta), _ptr(S0), _ptr(O), _ptr(Sf), _ptr(cu), N, B, H, T, dk,
-                            dv, _ptr(ch), n_ch, int(n_threads))
+                            int(bool(clip)), _ptr(beta), _ptr(S0), _ptr(O), _ptr(Sf), _ptr(cu), N,
+                            B, H, T, dk, dv, _ptr(ch), n_ch, int(n_threads))
     if rc != 0:
         raise ValueError(f"gdr_ref_fwd rejected its arguments (code {rc})")
     return O, Sf

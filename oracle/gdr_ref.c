@@ -27,6 +27,14 @@
  * in the GDN2 form (eq. 1 of "How to make GDN2 more stable"); passing
  * beta = 1 recovers the unscaled DPLR formula.
  *
+ * clip != 0 adds the spectral clipping of the forget gate from "How to make
+ * GDN2 more stable" (eq. 7): per token, rho = ||I - b_t a_t^T||_2 and the gate
+ * becomes alpha = min(alpha, 1/rho) channel by channel before it is applied, so
+ * that ||Diag(alpha)(I - b a^T)||_2 <= 1.  rho has the closed form of eq. 4;
+ * vectors of any length are reduced to that unit-vector form by moving their
+ * norms into eta (the page's remark under eq. 4).  With no gate alpha = 1 is
+ * clipped like any other gate, giving alpha = 1/rho.
+ *
  * Layouts (row-major, contiguous): tokens are the flattened [B*T] axis.
  *   q, k, a, b : [tokens, H, dk]      v : [tokens, H, dv]
  *   log_alpha  : [tokens, H] (gate 1) or [tokens, H, dk] (gate 2); unused for 0
@@ -45,11 +53,28 @@
 #include <omp.h>
 #endif
 
+/* ||I - b a^T||_2 for vectors a, b of length d ("How to make GDN2 more stable",
+ * eq. 4): with eta = |b| |a| and c the cosine between b and a, that is the
+ * norm of I - eta u w^T for unit u, w, namely (eta + sqrt(eta^2 - 4 eta c + 4)) / 2.
+ * eta c = b.a, and eta^2 - 4 eta c + 4 >= (eta - 2)^2 >= 0 (the max() only
+ * absorbs rounding). */
+static double rank1_spectral_norm(const double *a, const double *b, int d) {
+    double aa = 0.0, bb = 0.0, ab = 0.0;
+    for (int j = 0; j < d; ++j) {
+        aa += a[j] * a[j];
+        bb += b[j] * b[j];
+        ab += a[j] * b[j];
+    }
+    const double eta = sqrt(aa) * sqrt(bb);
+    const double disc = eta * eta - 4.0 * ab + 4.0;
+    return 0.5 * (eta + sqrt(disc > 0.0 ? disc : 0.0));
+}
+
 static void run_chain(int n, int h, const double *q, const double *k, const double *v,
                       const double *a, const double *b, const double *log_alpha, int gate,
-                      const double *beta, const double *S0, double *O, double *S_final,
+                      int clip, const double *beta, const double *S0, double *O, double *S_final,
                       long t0, long t1, int H, int dk, int dv, double *S, double *alpha,
-                      double *xb) {
+                      double *xb, double *bk) {
     if (S0)
         memcpy(S, S0 + ((size_t)n * H + h) * dv * dk, sizeof(double) * dv * dk);
     else
@@ -63,6 +88,16 @@ static void run_chain(int n, int h, const double *q, const double *k, const doub
             if (gate == 2) alpha[j] = exp(log_alpha[th * dk + j]);
             else if (gate == 1) alpha[j] = exp(log_alpha[th]);
             else alpha[j] = 1.0;
+        }
+        /* spectral clipping: alpha = min(alpha, 1 / ||I - b a^T||_2) */
+        if (clip) {
+            const double *a_t = a ? a + th * dk : kt;
+            const double *b_t = bk;
+            if (b) b_t = b + th * dk;
+            else for (int j = 0; j < dk; ++j) bk[j] = bt * kt[j];
+            const double inv_rho = 1.0 / rank1_spectral_norm(a_t, b_t, dk);
+            for (int j = 0; j < dk; ++j)
+                if (alpha[j] > inv_rho) alpha[j] = inv_rho;
         }
         /* X = S Diag(alpha): scale column j of S by alpha_j */
         for (int i = 0; i < dv; ++i)
@@ -93,7 +128,7 @@ static void run_chain(int n, int h, const double *q, const double *k, const doub
 }
 
 int gdr_ref_fwd(const double *q, const double *k, const double *v, const double *a,
-                const double *b, const double *log_alpha, int gate, const double *beta,
+                const double *b, const double *log_alpha, int gate, int clip, const double *beta,
                 const double *S0, double *O, double *S_final, const int32_t *cu_seqlens,
                 int n_seq, int B, int H, int T, int dk, int dv, const int32_t *chains,
                 int n_chains, int n_threads) {
@@ -119,7 +154,8 @@ int gdr_ref_fwd(const double *q, const double *k, const double *v, const double 
         double *S = (double *)malloc(sizeof(double) * (size_t)dv * dk);
         double *alpha = (double *)malloc(sizeof(double) * (size_t)dk);
         double *xb = (double *)malloc(sizeof(double) * (size_t)dv);
-        if (!S || !alpha || !xb) {
+        double *bk = (double *)malloc(sizeof(double) * (size_t)dk);
+        if (!S || !alpha || !xb || !bk) {
 #pragma omp atomic write
             err = -7;
         } else {
@@ -146,13 +182,14 @@ int gdr_ref_fwd(const double *q, const double *k, const double *v, const double 
                     t0 = (long)n * T;
                     t1 = t0 + T;
                 }
-                run_chain(n, h, q, k, v, a, b, log_alpha, gate, beta, S0, O, S_final, t0, t1, H,
-                          dk, dv, S, alpha, xb);
+                run_chain(n, h, q, k, v, a, b, log_alpha, gate, clip, beta, S0, O, S_final, t0,
+                          t1, H, dk, dv, S, alpha, xb, bk);
             }
         }
         free(S);
         free(alpha);
         free(xb);
+        free(bk);
     }
     return err;
 }

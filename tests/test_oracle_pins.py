@@ -226,6 +226,124 @@ def test_spectral_norm_exceeds_one_unless_aligned():
 
 
 # ---------------------------------------------------------------------------
+# 4b. Spectral clipping of the gate inside the recurrence ("How to make GDN2
+#     more stable", eq. 7): alpha <- min(alpha, 1/rho), rho = ||I - b a^T||_2.
+#     The expected rho always comes from numpy's SVD, never from eq. 4.
+# ---------------------------------------------------------------------------
+def _rank1_case(rng, d, eta, spread):
+    """a unit, b = eta * unit(a + spread * noise): GDN2's j = a and eta k = b."""
+    a = _unit(rng.standard_normal(d))
+    b = eta * _unit(a + spread * rng.standard_normal(d))
+    return a, b
+
+
+@pytest.mark.parametrize("dplr", [False, True])
+@pytest.mark.parametrize("gate", [0, 1, 2])
+def test_clip_single_step_gate_is_min_with_inverse_norm(gate, dplr):
+    """T = 1, S0 = I, no write: S1 = Diag(alpha')(I - b a^T).  Row j of S1 is alpha'_j
+    times row j of I - b a^T; alpha'_j must be min(alpha_j, 1/sigma_max(I - b a^T))
+    and ||S1||_2 <= 1 (eq. 2)."""
+    rng = np.random.default_rng(300 + gate + 3 * dplr)
+    d = 6
+    c = _rand_case(rng, B=1, T=1, H=1, dk=d, dv=d, gate=gate, dplr=dplr, s0=False)
+    c["S0"] = np.eye(d)[None, None]
+    c["v"] = np.zeros_like(c["v"])
+    if dplr:
+        a, b = _rank1_case(rng, d, 1.6, 0.8)
+        c["a"], c["b"] = a[None, None, None], b[None, None, None]
+        c["beta"] = np.zeros_like(c["beta"])  # no write; b carries its own scale
+    else:
+        c["beta"] = np.full_like(c["beta"], 2.6)  # eta = beta |k|^2 > 2: rho = eta - 1
+        a, b = c["k"][0, 0, 0], 2.6 * c["k"][0, 0, 0]
+    if gate == 2:
+        c["log_alpha"] = np.linspace(-1.5, -0.001, d)[None, None, None]
+    elif gate == 1:
+        c["log_alpha"] = np.full((1, 1, 1), -0.01)
+    M = np.eye(d) - np.outer(b, a)
+    rho = np.linalg.norm(M, 2)
+    assert rho > 1.1
+    alpha = _alpha_full(c["log_alpha"], c["q"].shape)[0, 0, 0]
+    want = np.minimum(alpha, 1.0 / rho)
+    if gate == 2:
+        assert (alpha < 1 / rho).any() and (alpha > 1 / rho).any()  # both sides of the clip
+    O, Sf = oracle.recurrence(**c, clip=True)
+    S1 = Sf[0, 0]
+    got = np.einsum("jk,jk->j", S1, M) / np.einsum("jk,jk->j", M, M)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(S1, np.diag(want) @ M, rtol=0, atol=1e-13)
+    assert np.linalg.norm(S1, 2) <= 1.0 + 1e-12
+    np.testing.assert_allclose(O[0, 0, 0], S1 @ c["q"][0, 0, 0], rtol=0, atol=1e-13)
+    if not dplr:
+        assert abs(rho - 1.6) < 1e-12  # KDA form: max(eta, 2) - 1 (eq. 5)
+
+
+@pytest.mark.parametrize("gate", [0, 1, 2])
+def test_clip_is_identity_when_the_factor_does_not_expand(gate):
+    """Eq. 6: with a = k unit and eta = beta <= 2 the norm is 1, so clipping changes nothing."""
+    rng = np.random.default_rng(320 + gate)
+    c = _rand_case(rng, B=2, T=30, H=2, dk=5, dv=4, gate=gate, dplr=False)
+    O0, S0_ = oracle.recurrence(**c)
+    O1, S1 = oracle.recurrence(**c, clip=True)
+    np.testing.assert_allclose(O1, O0, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(S1, S0_, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("gate", [0, 2])
+def test_clip_makes_the_state_non_expansive(gate):
+    """Without writes, S_t = S_{t-1} M_t with ||M_t||_2 <= 1 after clipping, so every
+    ||S_t||_2 <= ||S0||_2 and |o_t| <= ||S0||_2 for unit q.  Unclipped, the same
+    transitions blow the state up (so the check has teeth)."""
+    rng = np.random.default_rng(340 + gate)
+    d, T = 8, 60
+    c = _rand_case(rng, B=1, T=T, H=1, dk=d, dv=d, gate=gate, dplr=True, la=(-0.02, -0.001))
+    a = np.stack([_rank1_case(rng, d, float(rng.uniform(1.0, 3.0)), 1.0) for _ in range(T)])
+    c["a"] = a[:, 0][None, :, None]
+    c["b"] = a[:, 1][None, :, None]
+    c["beta"] = np.zeros_like(c["beta"])
+    s0 = np.linalg.norm(c["S0"][0, 0], 2)
+    _, Sraw = oracle.recurrence(**c)
+    assert np.linalg.norm(Sraw[0, 0], 2) > 10 * s0
+    O, Sf = oracle.recurrence(**c, clip=True)
+    assert np.linalg.norm(Sf[0, 0], 2) <= s0 * (1 + 1e-12)
+    assert np.max(np.linalg.norm(O[0, :, 0], axis=-1)) <= s0 * (1 + 1e-12)
+
+
+@pytest.mark.parametrize("dplr", [False, True])
+@pytest.mark.parametrize("gate", [0, 1, 2])
+def test_clip_equals_unclipped_run_on_the_clipped_gate(gate, dplr):
+    """The clip acts token by token and head by head: the clipped run equals an
+    unclipped run whose gate is replaced by min(alpha_t, 1/rho_t), rho_t from the SVD
+    of each token's I - b_t a_t^T (packed sequences, several heads, initial state)."""
+    rng = np.random.default_rng(360 + gate + 3 * dplr)
+    B, T, H, d, dv = 1, 37, 3, 5, 4
+    c = _rand_case(rng, B=B, T=T, H=H, dk=d, dv=dv, gate=gate, dplr=dplr, s0=False)
+    c["beta"] = rng.uniform(0.0, 4.0, size=(B, T, H))
+    if dplr:
+        c["b"] = c["beta"][..., None] * _unit(c["a"] + 0.7 * rng.standard_normal(c["a"].shape))
+    cu = np.array([0, 11, 11, 30, 37], dtype=np.int32)
+    c["cu_seqlens"] = cu
+    c["S0"] = rng.standard_normal((len(cu) - 1, H, dv, d)) * 0.5
+    k = c["k"][0]
+    A = k if c["a"] is None else c["a"][0]
+    Bv = c["beta"][0][..., None] * k if c["b"] is None else c["b"][0]
+    inv_rho = np.empty((T, H))
+    for t in range(T):
+        for h in range(H):
+            inv_rho[t, h] = 1.0 / np.linalg.norm(np.eye(d) - np.outer(Bv[t, h], A[t, h]), 2)
+    alpha = _alpha_full(c["log_alpha"], c["q"].shape)[0]
+    clipped = np.minimum(alpha, inv_rho[..., None])
+    assert (alpha > inv_rho[..., None]).mean() > 0.2  # the clip is active often
+    if gate == 2:
+        la = np.log(clipped)[None]
+    else:
+        la = np.log(clipped[..., 0])[None]  # one value per token and head
+    O1, S1 = oracle.recurrence(**c, clip=True)
+    O2, S2 = oracle.recurrence(**dict(c, log_alpha=la))
+    np.testing.assert_allclose(O1, O2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(S1, S2, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # 5. The chunk rewrite against the definition, and its inverse's closed form.
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("C", [1, 7, 16, 64])
