@@ -101,7 +101,7 @@ def time_gpu(P, steps, warmup, cold_steps):
     out = torch.empty((P.B, P.T, P.H, P.dv), dtype=P.dtype, device=dev)
     fin = torch.empty((P.n_seq, P.H, P.dv, P.dk), dtype=torch.float32, device=dev)
     call = lambda: gdr.chunk_fwd(q, k, v, beta, log_alpha=la, a=a, b=b, S0=S0, cu_seqlens=cu,
-                                 chunk_size=P.chunk, out=out, final_state=fin)
+                                 chunk_size=P.chunk, out=out, final_state=fin, clip=P.clip)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -179,7 +179,7 @@ def cpu_baseline(P, n_threads):
     f64 = lambda t: None if t is None else t.to(torch.float64).numpy()
     args = dict(q=f64(P.q), k=f64(P.k), v=f64(P.v), beta=f64(P.beta),
                 log_alpha=f64(P.log_alpha), a=f64(P.a), b=f64(P.b), S0=f64(P.S0),
-                cu_seqlens=None if P.cu_seqlens is None else P.cu_seqlens.numpy())
+                cu_seqlens=None if P.cu_seqlens is None else P.cu_seqlens.numpy(), clip=P.clip)
     # The whole workload, repeated until at least a second has passed (small workloads).
     reps, t = 0, time.perf_counter()
     while True:
@@ -218,7 +218,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default=WORKLOAD, choices=["kda", "gdn", "dplr", "kda_varlen",
-                                                              "deltanet_f32"],
+                                                              "deltanet_f32", "gdn2_clip"],
                     help="the benchmark line is for kda; the others time the same call on the "
                          "other workloads (reported under the same keys, metric named per workload)")
     ap.add_argument("--steps", type=int, default=100)

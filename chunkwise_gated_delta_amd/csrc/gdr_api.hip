@@ -49,12 +49,18 @@ int supported(int dtype, int dk, int dv, int C, bool has_ab) {
     return (C == 16 || C == 32 || C == 64) ? GDR_OK : GDR_ERR_UNSUPPORTED;
 }
 
+// The gate argument: a layout (GDR_GATE_NONE/HEAD/CHANNEL), optionally with GDR_GATE_CLIP.
+bool gate_ok(int gate) {
+    const int layout = gate & ~GDR_GATE_CLIP;
+    return layout >= GDR_GATE_NONE && layout <= GDR_GATE_CHANNEL;
+}
+
 FwdArgs make_args(int B, int H, int T, int dk, int dv, int C, int n_seq, int dtype, int gate,
                   bool has_ab) {
     FwdArgs a;
     std::memset(&a, 0, sizeof(a));
     a.B = B; a.H = H; a.T = T; a.dk = dk; a.dv = dv; a.C = C; a.n_seq = n_seq;
-    a.dtype = dtype; a.gate = gate;
+    a.dtype = dtype; a.gate = gate & ~GDR_GATE_CLIP; a.clip = (gate & GDR_GATE_CLIP) != 0;
     static const char dummy = 0;
     static const int32_t dummy_cu = 0;
     if (has_ab) a.a = a.b = &dummy;
@@ -76,7 +82,7 @@ size_t gdr_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int C, int n
                                int gate, int has_ab) {
     const bool varlen = n_seq > 0;
     if (!shape_ok(B, H, T, dk, dv, n_seq, varlen)) return 0;
-    if (gate < GDR_GATE_NONE || gate > GDR_GATE_CHANNEL) return 0;
+    if (!gate_ok(gate)) return 0;
     if (supported(dtype, dk, dv, C, has_ab != 0) != GDR_OK) return 0;
     const FwdArgs a = make_args(B, H, T, dk, dv, C, n_seq, dtype, gate, has_ab != 0);
     return workspace_for(a, varlen ? n_seq : B);
@@ -89,8 +95,9 @@ int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
                   size_t workspace_bytes, void *stream) {
     if (!q || !k || !v || !beta || !O) return GDR_ERR_NULL;
     if ((a == nullptr) != (b == nullptr)) return GDR_ERR_NULL;
-    if (gate < GDR_GATE_NONE || gate > GDR_GATE_CHANNEL) return GDR_ERR_SHAPE;
-    if ((gate == GDR_GATE_NONE) != (log_alpha == nullptr)) return GDR_ERR_NULL;
+    if (!gate_ok(gate)) return GDR_ERR_SHAPE;
+    const int layout = gate & ~GDR_GATE_CLIP;
+    if ((layout == GDR_GATE_NONE) != (log_alpha == nullptr)) return GDR_ERR_NULL;
     const bool varlen = cu_seqlens != nullptr;
     if (!shape_ok(B, H, T, dk, dv, n_seq, varlen)) return GDR_ERR_SHAPE;
     const bool has_ab = a != nullptr;
@@ -104,7 +111,8 @@ int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
     const Range rv = range(v, tokens * H * dv * es);
     const Range ra = range(a, has_ab ? tokens * H * dk * es : 0);
     const Range rb = range(b, has_ab ? tokens * H * dk * es : 0);
-    const size_t la_elems = gate == GDR_GATE_CHANNEL ? tokens * H * dk : (gate == GDR_GATE_HEAD ? tokens * H : 0);
+    const size_t la_elems =
+        layout == GDR_GATE_CHANNEL ? tokens * H * dk : (layout == GDR_GATE_HEAD ? tokens * H : 0);
     const Range rla = range(log_alpha, la_elems * 4), rbeta = range(beta, tokens * H * 4);
     const size_t sbytes = (size_t)N * H * dv * dk * 4;
     const Range rs0 = range(S0, S0 ? sbytes : 0), rO = range(O, tokens * H * dv * es);
@@ -136,8 +144,9 @@ int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
     hipStream_t s = (hipStream_t)stream;
     const bool split = gdr::kda_split_supported(args);
     if (trace_enabled())
-        std::fprintf(stderr, "[gdr] %s B=%d H=%d T=%d N=%d dk=%d dv=%d C=%d dtype=%d gate=%d ws=%zu\n",
-                     split ? "kda_split" : "f32_split", B, H, T, N, dk, dv, C, dtype, gate, need);
+        std::fprintf(stderr, "[gdr] %s B=%d H=%d T=%d N=%d dk=%d dv=%d C=%d dtype=%d gate=%d clip=%d ws=%zu\n",
+                     split ? "kda_split" : "f32_split", B, H, T, N, dk, dv, C, dtype, layout,
+                     (int)args.clip, need);
     if (!split && !gdr::f32_split_supported(args)) return GDR_ERR_UNSUPPORTED;
     const int rc = split ? gdr::launch_kda_split(args, N, s) : gdr::launch_f32_split(args, N, s);
     return rc == 0 ? GDR_OK : GDR_ERR_HIP;

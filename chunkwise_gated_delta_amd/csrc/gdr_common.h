@@ -45,6 +45,45 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Cross-lane moves.  DPP forms are VALU operand modifiers (no LDS round trip):
+// quad_perm xor 1 / xor 2, row_half_mirror (lane i <-> 7 - i within 8) and
+// row_mirror (i <-> 15 - i within 16).  Across the two 16-lane rows of a
+// 32-lane group, ds_swizzle in its bit mode (offset = xor_mask << 10 | 0x1f).
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float swizzle_xor16(float x) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (16 << 10) | 0x1f));
+}
+
+// Sum of x over each group of G consecutive lanes (G a power of two, <= 32).
+// After the quad steps every lane of a quad holds the quad sum, so the mirror
+// steps pair whole quads (and then whole 8-lane halves).
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(G >= 1 && G <= 32 && (G & (G - 1)) == 0, "group of 1..32 lanes");
+    if constexpr (G >= 2) x += dpp<kDppXor1>(x);
+    if constexpr (G >= 4) x += dpp<kDppXor2>(x);
+    if constexpr (G >= 8) x += dpp<kDppHalfMirror>(x);
+    if constexpr (G >= 16) x += dpp<kDppMirror>(x);
+    if constexpr (G >= 32) x += swizzle_xor16(x);
+    return x;
+}
+
+// Spectral clip bound of one token ("How to make GDN2 more stable", eqs. 4 and 7):
+// the gate is limited to 1 / rho with rho = ||I - b a^T||_2.  With eta = |a| |b|
+// and cosine c, eq. 4 gives rho = (eta + sqrt(eta^2 - 4 eta c + 4)) / 2, and
+// eta c = a.b.  The radicand is >= (eta - 2)^2 >= 0; max() absorbs rounding.
+// Returns -log(rho) in the base the caller asks for (scale = log_base(2) factor:
+// 1 for log2, ln 2 for the natural log).  Zero vectors give rho = 1, bound 0.
+__device__ __forceinline__ float clip_bound(float aa, float bb, float ab, float scale) {
+    const float eta = sqrtf(aa) * sqrtf(bb);
+    const float disc = fmaxf(eta * eta - 4.f * ab + 4.f, 0.f);
+    return -scale * __log2f(0.5f * (eta + sqrtf(disc)));
+}
+
 // Sequence bounds [t0, t1) of sequence n on the flattened token axis.  Packed
 // offsets are clamped into [0, total] and made non-decreasing so that nothing
 // is read or written outside the buffers; a clamp raises the error flag.
@@ -69,7 +108,8 @@ struct FwdArgs {
     void *O;
     float *S_final;
     const int32_t *cu_seqlens;
-    int n_seq, B, H, T, dk, dv, C, dtype, gate;
+    int n_seq, B, H, T, dk, dv, C, dtype, gate;  // gate: the layout only (kGate*)
+    bool clip;  // spectral clipping of the gate, alpha <- min(alpha, 1 / ||I - b a^T||_2)
     void *workspace;
     size_t workspace_bytes;
 };

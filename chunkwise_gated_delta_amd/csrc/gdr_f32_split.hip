@@ -36,6 +36,7 @@ constexpr int kDB = 64;        // dk channels per operand block of the prep kern
 constexpr int kOS = kDB + 1;   // row stride (floats) of [C][kDB] operand arrays
 constexpr int kFDVT = 32;      // dv columns per state workgroup
 constexpr int kMaxDK = 128;
+constexpr float kLn2 = 0.6931471805599453f;
 
 struct F32Params {
     const void *q, *k, *v, *a, *b;  // a, b: DPLR low-rank vectors, or NULL
@@ -48,6 +49,7 @@ struct F32Params {
     float *blk;  // (chunk, head) blocks of bf floats
     long total;
     int H, T, dk, dv, n_seq, n_tiles, C, gate;
+    int clip;  // spectral clipping of the gate: alpha <- min(alpha, 1 / ||I - b a^T||_2)
     int nc, max_chunks, bf;
 };
 
@@ -83,7 +85,8 @@ struct F32PrepSmem {  // offsets in floats
     static constexpr int oBeta = oEc + (DP ? C * CS : 0);
     static constexpr int oTot = oBeta + C;            // gate partial sums [4][kDB]
     static constexpr int oGh = oTot + 4 * kDB;        // head gate prefix sums [C]
-    static constexpr int floats = oGh + C;
+    static constexpr int oClip = oGh + C;             // clip bound -ln rho per row [C]
+    static constexpr int floats = oClip + C;
     static_assert(floats * 4 <= 160 * 1024, "LDS");
 };
 
@@ -97,6 +100,7 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
     float *sQl = smem + L::oQl, *sKl = smem + L::oKl, *sKr = smem + L::oKr, *sAr = smem + L::oAr;
     float *sL = smem + L::oL, *sAqk = smem + L::oAqk, *sBK = smem + L::oBK, *sAqa = smem + L::oAqa;
     float *sEc = smem + L::oEc, *sBeta = smem + L::oBeta, *sTot = smem + L::oTot, *sGh = smem + L::oGh;
+    float *sClip = smem + L::oClip;
 
     const Tin *q = (const Tin *)p.q, *k = (const Tin *)p.k, *a = (const Tin *)p.a, *b = (const Tin *)p.b;
     const int tid = threadIdx.x, H = p.H, dk = p.dk;
@@ -111,8 +115,40 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
     float *bp = p.blk + (size_t)g * p.bf;
 
     if (tid < C) sBeta[tid] = tid < m ? p.beta[(size_t)(tok0 + tid) * H + h] : 0.f;
-    if (p.gate == kGateHead && tid < 64) {
-        float x = tid < m && tid < C ? p.la[(size_t)(tok0 + tid) * H + h] : 0.f;
+    if (p.clip) {  // workgroup-uniform
+        // Spectral clip bound per row, -ln ||I - b a^T||_2, from |a|^2, |b|^2 and a.b
+        // (without a, b: a = k, b = beta k), kFT / C threads per row.
+        constexpr int TPR = kFT / C;
+        const int r = tid / TPR, j = tid % TPR;
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+        if (r < m) {
+            const size_t base = ((size_t)(tok0 + r) * H + h) * dk;
+            for (int d = j; d < dk; d += TPR) {
+                if (DP) {
+                    const float av = ld(a, base + d), bv = ld(b, base + d);
+                    s0 += av * av;
+                    s1 += bv * bv;
+                    s2 += av * bv;
+                } else {
+                    const float kv = ld(k, base + d);
+                    s0 += kv * kv;
+                }
+            }
+        }
+        s0 = group_sum<TPR>(s0);
+        s1 = group_sum<TPR>(s1);
+        s2 = group_sum<TPR>(s2);
+        if (j == 0) {
+            const float br = r < m ? p.beta[(size_t)(tok0 + r) * H + h] : 0.f;
+            sClip[r] = DP ? clip_bound(s0, s1, s2, kLn2) : clip_bound(s0, br * br * s0, br * s0, kLn2);
+        }
+        lds_barrier();
+    }
+    // A clipped gate without a gate input is one value per row, like a head gate.
+    const bool head_scan = p.gate == kGateHead || (p.clip && p.gate == kGateNone);
+    if (head_scan && tid < 64) {
+        float x = tid < m && tid < C && p.gate == kGateHead ? p.la[(size_t)(tok0 + tid) * H + h] : 0.f;
+        if (p.clip && tid < C) x = fminf(x, sClip[tid]);
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(x, off, 64);
             if (tid >= off) x += y;
@@ -136,7 +172,11 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
             kv[i] = ok ? ld(k, e) : 0.f;
             av[i] = DP && ok ? ld(a, e) : 0.f;
             bv[i] = DP && ok ? ld(b, e) : 0.f;
-            if (p.gate == kGateChannel) run += ok ? p.la[e] : 0.f;
+            if (p.gate == kGateChannel) {
+                float x = ok ? p.la[e] : 0.f;
+                if (p.clip) x = fminf(x, sClip[r]);
+                run += x;
+            }
             gv[i] = run;
         }
         float gC = 0.f;
@@ -152,7 +192,7 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
             }
 #pragma unroll
             for (int i = 0; i < RPG; ++i) gv[i] += carry;
-        } else if (p.gate == kGateHead) {
+        } else if (head_scan) {
             gC = sGh[C - 1];
 #pragma unroll
             for (int i = 0; i < RPG; ++i) gv[i] = sGh[rg * RPG + i];
@@ -736,7 +776,7 @@ int launch_f32_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     fp.total = (long)a.B * a.T;
     fp.H = a.H; fp.T = a.T; fp.dk = a.dk; fp.dv = a.dv; fp.n_seq = n_seq_eff;
     const int dvt = f32_dvt(a, n_seq_eff);
-    fp.n_tiles = a.dv / dvt; fp.C = a.C; fp.gate = a.gate;
+    fp.n_tiles = a.dv / dvt; fp.C = a.C; fp.gate = a.gate; fp.clip = a.clip ? 1 : 0;
     fp.nc = lay.nc; fp.max_chunks = lay.max_chunks; fp.bf = B.floats;
 
     if (varlen) hipLaunchKernelGGL((chunk_plan_kernel<F32Params>), dim3(1), dim3(kPlanThreads), 0, s, fp);

@@ -37,6 +37,8 @@
 // S = (S + V'^T K-> + N^T A->) Diag(gamma_C), with V' = Diag(beta) V.  The prep kernel hands its results over in the
 // operand order of v_mfma_f32_32x32x16_bf16, so the state kernel loads them straight
 // into registers with whole-wave contiguous loads.
+#include <type_traits>
+
 #include "gdr_mfma.h"
 #include "gdr_split_common.h"
 
@@ -116,13 +118,16 @@ struct PrepSmem {
     static_assert(bytes <= 160 * 1024, "one workgroup per CU");
 };
 
-template <int DK, int GATE, bool DP>
+template <int DK, int GATE, bool DP, bool CLIP>
 __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitParams p) {
     using L = PrepSmem<DK, DP>;
     using Bk = Blk<DK, DP>;
     constexpr int KS = L::KS;
     constexpr int CPT = DK / 32;  // gate stage: channels per thread
     constexpr int WPR = CPT / 2;  // 32-bit words of bf16 per row per thread
+    // The gate is summed per (row, channel) in registers for a channel gate, and for
+    // every gate when it is clipped (the clip bound differs from row to row).
+    constexpr bool kRowGate = GATE == kGateChannel || CLIP;
 
     __shared__ __attribute__((aligned(16))) char smem[L::bytes];
     uint16_t *sKl = (uint16_t *)(smem + L::oKl);
@@ -213,11 +218,13 @@ __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitPar
                     const float2 x = *(const float2 *)(lb + rr * rs);
                     lw[i][0] = x.x; lw[i][1] = x.y;
                 }
+            } else if constexpr (CLIP && GATE == kGateHead) {
+                lw[i][0] = p.la[(size_t)(J.tok0 + rr) * H + h];
             }
         }
         const int rb0 = tid < kC ? (tid < J.m ? tid : J.m - 1) : 0;
         beta_r = p.beta[(size_t)(J.tok0 + rb0) * H + h];
-        if (GATE == kGateHead) lah = p.la[(size_t)(J.tok0 + (lane < J.m ? lane : J.m - 1)) * H + h];
+        if (GATE == kGateHead && !CLIP) lah = p.la[(size_t)(J.tok0 + (lane < J.m ? lane : J.m - 1)) * H + h];
     };
 
     // DPLR after the inverse (E in sX as bf16, unit diagonal, zero above it):
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitPar
             }
         }
         if (tid < kC) sBeta[tid] = tid < m ? beta_r : 0.f;
-        if (GATE == kGateHead && wave == 0) {
+        if (GATE == kGateHead && !CLIP && wave == 0) {
             float x = lane < m ? lah * kLog2e : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -340,9 +347,77 @@ __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitPar
         for (int i = tid; i < L::nCC * L::CCB / 16; i += kThreads)
             ((uint4 *)(smem + L::oX))[i] = make_uint4(0u, 0u, 0u, 0u);
 
+        // ---- spectral clip bound per row: log2 (1 / ||I - b a^T||_2) ----------------------
+        // Per row |a|^2, |b|^2 and a.b (without a, b: a = k, b = beta k, so |k|^2 alone),
+        // summed over this thread's channels and then over the 32 lanes of the row group
+        // by a reduce-scatter: three exchange steps each halve the rows a lane keeps
+        // (lane bit 3 picks rows 0-3 or 4-7, then bit 2, then bit 1), two full steps finish
+        // the sums, and lane l ends with row (l >> 1) & 7.  Its bound is then read back
+        // from lane 2 i of the half-wave for each row i.
+        float lc[8];
+        if constexpr (CLIP) {
+            if constexpr (!DP) lds_barrier();  // sBeta of this job
+            constexpr int Q = DP ? 3 : 1;
+            float sq[8 * Q];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) {
+                    if constexpr (DP) {
+                        const float a0 = bf16_lo(aw[i][w]), a1 = bf16_hi(aw[i][w]);
+                        const float b0 = bf16_lo(bw[i][w]), b1 = bf16_hi(bw[i][w]);
+                        s0 += a0 * a0 + a1 * a1;
+                        s1 += b0 * b0 + b1 * b1;
+                        s2 += a0 * b0 + a1 * b1;
+                    } else {
+                        const float k0 = bf16_lo(kw[i][w]), k1 = bf16_hi(kw[i][w]);
+                        s0 += k0 * k0 + k1 * k1;
+                    }
+                }
+                sq[Q * i] = s0;
+                if constexpr (DP) {
+                    sq[Q * i + 1] = s1;
+                    sq[Q * i + 2] = s2;
+                }
+            }
+            const int l = lane & 31;
+            auto half_step = [&](auto ctrl, int n, bool hi) {
+#pragma unroll
+                for (int v = 0; v < 4 * Q; ++v) {
+                    if (v < n) {
+                        const float keep = hi ? sq[v + n] : sq[v], send = hi ? sq[v] : sq[v + n];
+                        sq[v] = keep + dpp<decltype(ctrl)::value>(send);
+                    }
+                }
+            };
+            half_step(std::integral_constant<int, kDppMirror>(), 4 * Q, (l >> 3) & 1);      // partner 15 - l
+            half_step(std::integral_constant<int, kDppHalfMirror>(), 2 * Q, (l >> 2) & 1);  // partner l ^ 7
+            half_step(std::integral_constant<int, kDppXor2>(), Q, (l >> 1) & 1);            // partner l ^ 2
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                sq[q] += dpp<kDppXor1>(sq[q]);
+                sq[q] += swizzle_xor16(sq[q]);
+            }
+            float mine;
+            if constexpr (DP) {
+                mine = clip_bound(sq[0], sq[1], sq[2], 1.f);
+            } else {
+                const float br = sBeta[8 * rg + ((l >> 1) & 7)];
+                mine = clip_bound(sq[0], br * br * sq[0], br * sq[0], 1.f);
+            }
+            const int mb = __float_as_int(mine);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float lo = __int_as_float(__builtin_amdgcn_readlane(mb, 2 * i));
+                const float hi = __int_as_float(__builtin_amdgcn_readlane(mb, 32 + 2 * i));
+                lc[i] = lane < 32 ? lo : hi;
+            }
+        }
+
         // ---- gate: prefix sums (log2 domain) -------------------------------------------
         float g[8][CPT], gC[CPT];
-        if (GATE == kGateChannel) {
+        if (kRowGate) {
             float run[CPT];
 #pragma unroll
             for (int e = 0; e < CPT; ++e) run[e] = 0.f;
@@ -350,14 +425,17 @@ __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitPar
             for (int i = 0; i < 8; ++i)
 #pragma unroll
                 for (int e = 0; e < CPT; ++e) {
-                    run[e] += lw[i][e] * kLog2e;
+                    float x = GATE == kGateChannel ? lw[i][e] * kLog2e
+                                                   : (GATE == kGateHead ? lw[i][0] * kLog2e : 0.f);
+                    if (CLIP) x = fminf(x, lc[i]);
+                    run[e] += x;
                     g[i][e] = run[e];
                 }
 #pragma unroll
             for (int e = 0; e < CPT; ++e) sTot[rg * DK + c0 + e] = run[e];
         }
         lds_barrier();
-        if (GATE == kGateChannel) {
+        if (kRowGate) {
             float carry[CPT], tot[CPT];
 #pragma unroll
             for (int e = 0; e < CPT; ++e) carry[e] = tot[e] = 0.f;
@@ -389,7 +467,7 @@ __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitPar
         {
             float kh[CPT][8], kb[CPT][8], gam[CPT];
 #pragma unroll
-            for (int e = 0; e < CPT; ++e) gam[e] = GATE == kGateNone ? 1.f : exp2_fast(gC[e]);
+            for (int e = 0; e < CPT; ++e) gam[e] = GATE == kGateNone && !CLIP ? 1.f : exp2_fast(gC[e]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int r = 8 * rg + i;
@@ -406,8 +484,8 @@ __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitPar
                 }
 #pragma unroll
                 for (int e = 0; e < CPT; ++e) {
-                    const float eg = GATE == kGateNone ? 1.f : exp2_fast(g[i][e]);
-                    const float eig = GATE == kGateNone ? 1.f : exp2_fast(-g[i][e]);
+                    const float eg = GATE == kGateNone && !CLIP ? 1.f : exp2_fast(g[i][e]);
+                    const float eig = GATE == kGateNone && !CLIP ? 1.f : exp2_fast(-g[i][e]);
                     const float egc = eig * gam[e];  // e^(g_C - g)
                     a[e] = (DP ? bv[e] : kv[e]) * eg;
                     b[e] = kv[e] * eig;
@@ -991,12 +1069,18 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     const long slots = (dp ? 1L : 2L) * compute_units();
     const dim3 grid_prep((unsigned)(njobs < slots ? njobs : slots));
     const dim3 grid_state((unsigned)(((n_seq_eff * a.H + 7) / 8) * 8 * sp.n_tiles));
-#define GDR_PREP(DK, G, D) hipLaunchKernelGGL((kda_prep_kernel<DK, G, D>), grid_prep, dim3(kThreads), 0, s, sp)
+#define GDR_PREP(DK, G, D, CL) \
+    hipLaunchKernelGGL((kda_prep_kernel<DK, G, D, CL>), grid_prep, dim3(kThreads), 0, s, sp)
+#define GDR_GATES(DK, D, CL)                                 \
+    do {                                                     \
+        if (a.gate == kGateChannel) GDR_PREP(DK, kGateChannel, D, CL); \
+        else if (a.gate == kGateHead) GDR_PREP(DK, kGateHead, D, CL);  \
+        else GDR_PREP(DK, kGateNone, D, CL);                 \
+    } while (0)
 #define GDR_PATH(DK, D)                                                                     \
     do {                                                                                    \
-        if (a.gate == kGateChannel) GDR_PREP(DK, kGateChannel, D);                          \
-        else if (a.gate == kGateHead) GDR_PREP(DK, kGateHead, D);                           \
-        else GDR_PREP(DK, kGateNone, D);                                                    \
+        if (a.clip) GDR_GATES(DK, D, true);                                                 \
+        else GDR_GATES(DK, D, false);                                                       \
         hipLaunchKernelGGL((kda_state_kernel<DK, D>), grid_state, dim3(kThreads), 0, s, sp); \
     } while (0)
     if (a.dk == 128) {
@@ -1007,6 +1091,7 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
         else GDR_PATH(64, false);
     }
 #undef GDR_PATH
+#undef GDR_GATES
 #undef GDR_PREP
     return (int)hipGetLastError();
 }

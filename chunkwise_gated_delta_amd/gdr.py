@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
 GDR_F32, GDR_BF16 = 0, 1
 GATE_NONE, GATE_HEAD, GATE_CHANNEL = 0, 1, 2
+GATE_CLIP = 4  # flag: spectral clipping of the gate, alpha <- min(alpha, 1/||I - b a^T||_2)
 STATUS = {0: "GDR_OK", -1: "GDR_ERR_NULL", -2: "GDR_ERR_SHAPE", -3: "GDR_ERR_UNSUPPORTED",
           -4: "GDR_ERR_WORKSPACE", -5: "GDR_ERR_ALIAS", -6: "GDR_ERR_HIP"}
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_workspace", "gdr_workspace_error",
@@ -72,6 +73,7 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 def workspace_bytes(B, H, T, dk, dv, C=64, n_seq=0, dtype=torch.bfloat16, gate=GATE_CHANNEL,
                     has_ab=False) -> int:
+    """Workspace bytes for these arguments (gate may carry GATE_CLIP); 0 if unsupported."""
     lib = load_library()
     return int(lib.gdr_chunk_fwd_workspace(B, H, T, dk, dv, C, n_seq, _dtype_code(dtype), gate,
                                            int(bool(has_ab))))
@@ -92,8 +94,12 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
               cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
               output_final_state: bool = True, out: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              workspace: Optional[torch.Tensor] = None,
+              clip: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise forward of S_t = S_{t-1} Diag(alpha_t)(I - b_t a_t^T) + beta_t v_t k_t^T, o_t = S_t q_t.
+
+    clip=True clips the gate per token to min(alpha_t, 1/||I - b_t a_t^T||_2)
+    (spectral clipping of the GDN2 stability notes, eq. 7; GATE_CLIP in the C ABI).
 
     q, k, (a, b): [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H] fp32;
     log_alpha: None, [B, T, H] (head gate) or [B, T, H, dk] (channel gate), fp32;
@@ -133,6 +139,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
         raise ValueError("log_alpha must be [B, T, H] or [B, T, H, dk]")
     if log_alpha is not None and log_alpha.dtype != torch.float32:
         raise ValueError("log_alpha must be float32")
+    if clip:
+        gate |= GATE_CLIP
     n_seq = 0
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32:

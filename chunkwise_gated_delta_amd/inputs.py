@@ -11,11 +11,15 @@ ranges used to study the method (the pages report no dataset for this path):
 3. ``kda``           KDA, per-channel gate:      B=2  H=32 T=8192  dk=dv=128
 4. ``dplr``          gated DPLR, distinct a, b:  B=1  H=16 T=16384 dk=dv=128
 5. ``kda_varlen``    KDA, 8 packed sequences:    32768 tokens, H=32, dk=dv=128
+6. ``gdn2_clip``     GDN2 form with the spectral gate clip: the ``dplr`` shapes, with
+                     the write key tied to b (b = beta k, as in the GDN2 form)
 
 Draw order (fixed, so every consumer sees the same bytes): [lengths], q, k, v,
 beta, log_alpha, [a_raw, b_noise], [S0].  All draws are float32; q and k (and a,
 b) are L2-normalised over the head dimension in float32, then rounded to the
-input dtype (bf16 by round-to-nearest-even) where the workload says so.
+input dtype (bf16 by round-to-nearest-even) where the workload says so.  In the
+GDN2 form (``gdn2``) the drawn k is discarded for k = unit(a + 0.1 noise), so
+that b = beta k carries the same key as the write term.
 """
 from __future__ import annotations
 
@@ -50,6 +54,7 @@ class Problem:
     cu_seqlens: Optional[torch.Tensor]
     gate: int
     chunk: int = 64
+    clip: bool = False  # spectral clipping of the gate, alpha <- min(alpha, 1/||I - b a^T||)
 
     @property
     def B(self):
@@ -121,18 +126,19 @@ def dirichlet_lengths(rng: np.random.Generator, n_seq: int, total: int, min_len:
 
 def make_problem(kind: str, *, seed: Optional[int] = None, B=None, H=None, T=None, dk=None,
                  dv=None, n_seq=None, total=None, min_len=None, dtype=None,
-                 s0_scale=None, gate=None, dplr=None, chunk: int = 64) -> Problem:
+                 s0_scale=None, gate=None, dplr=None, clip=None, chunk: int = 64) -> Problem:
     """Build a seeded problem of workload ``kind`` (see module doc).
 
     Keyword overrides shrink or reshape a workload while keeping its value
     distributions, so small parity cases and the full-size workloads share one
     recipe.  ``gate`` swaps the gate mode (the log-decay range stays the
-    workload's); ``dplr=True`` adds distinct a, b drawn as in the ``dplr`` workload.
+    workload's); ``dplr=True`` adds distinct a, b drawn as in the ``dplr`` workload;
+    ``clip`` turns the spectral gate clipping on or off.
     """
     spec = dict(WORKLOADS[kind])
     spec.update({k: v for k, v in dict(B=B, H=H, T=T, dk=dk, dv=dv, n_seq=n_seq, total=total,
                                         min_len=min_len, dtype=dtype, s0_scale=s0_scale,
-                                        gate=gate, dplr=dplr).items()
+                                        gate=gate, dplr=dplr, clip=clip).items()
                  if v is not None})
     if seed is None:
         seed = spec["seed"]
@@ -161,8 +167,11 @@ def make_problem(kind: str, *, seed: Optional[int] = None, B=None, H=None, T=Non
     if spec.get("dplr"):
         a32 = _l2n(rng.standard_normal(shp + (dk_,), dtype=np.float32))
         noise = rng.standard_normal(shp + (dk_,), dtype=np.float32)
-        b32 = (beta[..., None] * _l2n(a32 + np.float32(0.1) * noise)).astype(np.float32)
+        kb = _l2n(a32 + np.float32(0.1) * noise)
+        b32 = (beta[..., None] * kb).astype(np.float32)
         a, b = _cast(a32, dt), _cast(b32, dt)
+        if spec.get("gdn2"):
+            k = kb
     S0 = None
     if spec.get("s0_scale"):
         n = len(cu) - 1 if cu is not None else B_
@@ -171,7 +180,8 @@ def make_problem(kind: str, *, seed: Optional[int] = None, B=None, H=None, T=Non
     return Problem(
         name=kind, q=_cast(q, dt), k=_cast(k, dt), v=_cast(v, dt), beta=torch.from_numpy(beta),
         log_alpha=None if log_alpha is None else torch.from_numpy(log_alpha), a=a, b=b, S0=S0,
-        cu_seqlens=None if cu is None else torch.from_numpy(cu), gate=gate, chunk=chunk)
+        cu_seqlens=None if cu is None else torch.from_numpy(cu), gate=gate, chunk=chunk,
+        clip=bool(spec.get("clip", False)))
 
 
 WORKLOADS = {
@@ -186,6 +196,8 @@ WORKLOADS = {
     "kda_varlen": dict(seed=5, varlen=True, n_seq=8, total=32768, min_len=256, H=32, dk=128,
                        dv=128, dtype=torch.bfloat16, gate=GATE_CHANNEL, la_range=(-0.2, -0.001),
                        s0_scale=0.1),
+    "gdn2_clip": dict(seed=6, B=1, H=16, T=16384, dk=128, dv=128, dtype=torch.bfloat16,
+                      gate=GATE_CHANNEL, la_range=(-0.1, -0.001), dplr=True, gdn2=True, clip=True),
 }
 
 # The tolerance on max|X - X_ref| / max|X_ref| for O and for the final state.

@@ -61,8 +61,22 @@ typedef enum {
 typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
 
 /* Gate layout. NONE: alpha = 1 (log_alpha must be NULL).  HEAD: log_alpha is
- * [tokens, H].  CHANNEL: log_alpha is [tokens, H, dk]. */
-typedef enum { GDR_GATE_NONE = 0, GDR_GATE_HEAD = 1, GDR_GATE_CHANNEL = 2 } gdr_gate;
+ * [tokens, H].  CHANNEL: log_alpha is [tokens, H, dk].
+ *
+ * GDR_GATE_CLIP may be OR-ed into any layout: the spectral clipping of the
+ * forget gate from "How to make GDN2 more stable" (eq. 7).  Per token and head,
+ * rho_t = ||I - b_t a_t^T||_2 (closed form of eq. 4, the vector norms moved into
+ * eta: rho = (|a||b| + sqrt(|a|^2 |b|^2 - 4 a.b + 4)) / 2) and the gate becomes
+ * alpha_t = min(alpha_t, 1 / rho_t) channel by channel before it is applied,
+ * which bounds ||Diag(alpha_t)(I - b_t a_t^T)||_2 by 1 (eq. 2).  With
+ * GDR_GATE_NONE the clipped gate is 1 / rho_t.  With a == b == NULL the factor is
+ * a = k, b = beta k.  The clip is computed in fp32 from the input values. */
+typedef enum {
+    GDR_GATE_NONE = 0,
+    GDR_GATE_HEAD = 1,
+    GDR_GATE_CHANNEL = 2,
+    GDR_GATE_CLIP = 4
+} gdr_gate;
 
 /* Bytes of device workspace gdr_chunk_fwd needs for these arguments (n_seq:
  * the number of packed sequences, or 0 without cu_seqlens; has_ab: non-zero
@@ -80,6 +94,7 @@ size_t gdr_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int C, int n
  *   a, b        [B, T, H, dk]  dtype or NULL  the rank-one factor I - b a^T
  *                                             (both NULL: a = k, b = beta k)
  *   log_alpha   see gdr_gate, fp32            log of the forget gate (<= 0 expected)
+ *   gate        a gdr_gate layout, optionally | GDR_GATE_CLIP
  *   beta        [B, T, H]      fp32           write strength
  *   S0          [N, H, dv, dk] fp32 or NULL   initial state per sequence (NULL: zero)
  *   O           [B, T, H, dv]  dtype          output, o_t = S_t q_t

@@ -14,7 +14,7 @@ def oracle_of(P, chains=None, n_threads=0):
     return oracle.recurrence(f64(P.q), f64(P.k), f64(P.v), f64(P.beta), log_alpha=f64(P.log_alpha),
                              a=f64(P.a), b=f64(P.b), S0=f64(P.S0),
                              cu_seqlens=None if P.cu_seqlens is None else P.cu_seqlens.numpy(),
-                             chains=chains, n_threads=n_threads)
+                             chains=chains, n_threads=n_threads, clip=P.clip)
 
 
 def rel_err(x, ref):
@@ -34,7 +34,7 @@ def gpu_run(P, device="cuda", **kw):
     to = lambda t: None if t is None else t.to(device)
     O, Sf = gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), log_alpha=to(P.log_alpha),
                           a=to(P.a), b=to(P.b), S0=to(P.S0), cu_seqlens=to(P.cu_seqlens),
-                          chunk_size=P.chunk, **kw)
+                          chunk_size=P.chunk, clip=P.clip, **kw)
     torch.cuda.synchronize()
     return (O.to(torch.float64).cpu().numpy(),
             None if Sf is None else Sf.to(torch.float64).cpu().numpy())

@@ -79,6 +79,18 @@ def _call(lib, q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), a=None, b=None,
                              P(cu), n_seq, B, H, T, dk, dv, C, dtype, gate, P(ws), ws_bytes, None)
 
 
+def test_clip_flag_accepted_with_every_layout(lib):
+    # the clip flag changes no buffer size: same workspace as the plain layout
+    for dt, C, ab in [(1, 64, 0), (1, 64, 1), (0, 32, 0), (1, 16, 1)]:
+        for layout in (0, 1, 2):
+            plain = lib.gdr_chunk_fwd_workspace(2, 4, 300, 128, 128, C, 0, dt, layout, ab)
+            assert plain > 0
+            assert lib.gdr_chunk_fwd_workspace(2, 4, 300, 128, 128, C, 0, dt,
+                                               layout | gdr.GATE_CLIP, ab) == plain
+    assert lib.gdr_chunk_fwd_workspace(2, 4, 300, 128, 128, 64, 0, 1, 3 | gdr.GATE_CLIP, 0) == 0
+    assert lib.gdr_chunk_fwd_workspace(2, 4, 300, 128, 128, 64, 0, 1, 16, 0) == 0
+
+
 def test_null_pointers_rejected(lib):
     assert _call(lib, q=None) == -1
     assert _call(lib, O=None) == -1
@@ -86,12 +98,17 @@ def test_null_pointers_rejected(lib):
     assert _call(lib, a=FAKE + (9 << 30)) == -1           # only one of a, b
     assert _call(lib, la=None, gate=2) == -1              # gate without log_alpha
     assert _call(lib, gate=0) == -1                       # log_alpha without a gate
+    assert _call(lib, gate=0 | gdr.GATE_CLIP) == -1       # ... also with the clip flag
+    assert _call(lib, la=None, gate=2 | gdr.GATE_CLIP) == -1
 
 
 def test_bad_shapes_rejected(lib):
     assert _call(lib, T=0) == -2
     assert _call(lib, B=0) == -2
     assert _call(lib, gate=3) == -2
+    assert _call(lib, gate=3 | gdr.GATE_CLIP) == -2
+    assert _call(lib, gate=8 | 2) == -2                   # unknown flag bit
+    assert _call(lib, gate=-1) == -2
     assert _call(lib, cu=FAKE + (8 << 30), n_seq=2, B=2) == -2
     assert _call(lib, cu=FAKE + (8 << 30), n_seq=0) == -2
 

@@ -6,6 +6,7 @@ span several chunks plus a ragged tail; the full-size workloads run exactly
 as the benchmark launches them and are compared on sampled (sequence, head)
 chains, which the oracle computes independently of the others.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -13,7 +14,7 @@ import pytest
 import torch
 
 from chunkwise_gated_delta_amd import gdr, inputs
-from helpers import compare, gpu_run
+from helpers import compare, gpu_run, oracle_of, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +45,7 @@ SMALL = {
     "kda": dict(B=2, H=3, T=333),
     "dplr": dict(B=1, H=2, T=300),
     "kda_varlen": dict(n_seq=4, total=700, min_len=40, H=3),
+    "gdn2_clip": dict(B=1, H=2, T=300),
 }
 
 
@@ -59,10 +61,11 @@ FULL_CHAINS = {
     "kda": [(0, 0), (1, 31), (0, 17)],
     "dplr": [(0, 0), (0, 11)],
     "kda_varlen": None,  # filled in: shortest and longest sequence
+    "gdn2_clip": [(0, 0), (0, 13)],
 }
 
 
-@pytest.mark.parametrize("kind", ["gdn", "kda", "dplr", "kda_varlen"])
+@pytest.mark.parametrize("kind", ["gdn", "kda", "dplr", "kda_varlen", "gdn2_clip"])
 def test_full_size_sampled(kind):
     P = inputs.make_problem(kind)
     chains = FULL_CHAINS[kind]
@@ -224,3 +227,74 @@ def test_rejects_cpu_tensors():
     P = inputs.make_problem("kda", B=1, H=1, T=10)
     with pytest.raises(RuntimeError):
         gdr.chunk_fwd(P.q, P.k, P.v, P.beta, log_alpha=P.log_alpha)
+
+
+# ---------------------------------------------------------------------------
+# Spectral clipping of the gate (GDR_GATE_CLIP)
+# ---------------------------------------------------------------------------
+def _check_clip(P):
+    """Parity of a clipped run, plus proof that the clip changes the result here
+    (the unclipped oracle is further than the tolerance from the GPU output)."""
+    assert P.clip
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+    O_free, _ = oracle_of(dataclasses.replace(P, clip=False))
+    d = rel_err(O, O_free)
+    print(f"[gpu-case] distance to the unclipped result {d:.3e}", file=sys.__stderr__, flush=True)
+    assert d > 5 * TOL[P.dtype]
+
+
+def _kda_form(kind, beta_scale=3.0, **kw):
+    # a = k, b = beta k with unit k: the factor expands only where beta > 2
+    # (||I - beta k k^T|| = max(beta, 2) - 1), so beta is stretched to [0, 3).
+    P = inputs.make_problem(kind, clip=True, **kw)
+    P.beta = P.beta * beta_scale
+    return P
+
+
+@pytest.mark.parametrize("gate", [0, 1, 2])
+@pytest.mark.parametrize("dk", [64, 128])
+def test_clip_kda_forms_bf16(gate, dk):
+    kind = {0: "deltanet_f32", 1: "gdn", 2: "kda"}[gate]
+    P = _kda_form(kind, B=2, H=2, T=150, dk=dk, dv=64, dtype=torch.bfloat16)
+    _check_clip(P)
+
+
+@pytest.mark.parametrize("gate", [0, 1, 2])
+@pytest.mark.parametrize("dk", [64, 128])
+def test_clip_gdn2_gates(gate, dk):
+    P = inputs.make_problem("gdn2_clip", B=2, H=2, T=150, dk=dk, dv=64, gate=gate)
+    _check_clip(P)
+
+
+@pytest.mark.parametrize("C", [16, 32])
+def test_clip_gdn2_bf16_small_chunks(C):
+    P = inputs.make_problem("gdn2_clip", B=1, H=2, T=200, chunk=C)
+    _check_clip(P)
+
+
+@pytest.mark.parametrize("kind", ["deltanet_f32", "gdn", "kda", "gdn2_clip"])
+@pytest.mark.parametrize("C", [16, 32, 64])
+def test_clip_fp32(kind, C):
+    kw = dict(B=1, H=2, T=150, dk=64, dv=64, dtype=torch.float32, chunk=C)
+    if kind == "gdn2_clip":
+        P = inputs.make_problem(kind, **kw)
+    else:
+        P = _kda_form(kind, **kw)
+    _check_clip(P)
+
+
+@pytest.mark.parametrize("kind", ["kda", "gdn2_clip"])
+def test_clip_fp32_dk128(kind):
+    kw = dict(B=1, H=2, T=150, dk=128, dv=64, dtype=torch.float32)
+    P = inputs.make_problem(kind, **kw) if kind == "gdn2_clip" else _kda_form(kind, **kw)
+    _check_clip(P)
+
+
+def test_clip_varlen_with_initial_state():
+    # packed sequences down to a single token, per-sequence initial state, GDN2 form
+    P = inputs.make_problem("kda_varlen", n_seq=6, total=520, min_len=1, H=3, dplr=True,
+                            clip=True)
+    P.cu_seqlens = torch.tensor([0, 1, 65, 66, 200, 329, 520], dtype=torch.int32)
+    assert P.a is not None and P.S0 is not None
+    _check_clip(P)
