@@ -6,6 +6,8 @@ the GPU library; inputs arrive as plain numpy arrays.
 
 * ``recurrence``        -- the definition: fp64 token-by-token recurrence (C, OpenMP),
                            built from ``gdr_ref.c``.
+* ``recurrence_bwd``    -- its gradients: reverse-mode differentiation of the same
+                           recurrence, written out by hand (``gdr_ref_bwd.c``).
 * ``spectral_norm_rank1`` -- closed form of ||I - eta k j^T||_2 for unit k, j
                            ("How to make GDN2 more stable", eq. 4).
 * ``chunk_mirror``      -- the chunk-form algebra of the pages in fp64 numpy, used to
@@ -34,6 +36,8 @@ def _lib():
         I = ctypes.c_int
         lib.gdr_ref_fwd.restype = I
         lib.gdr_ref_fwd.argtypes = [P, P, P, P, P, P, I, I, P, P, P, P, P, I, I, I, I, I, I, P, I, I]
+        lib.gdr_ref_bwd.restype = I
+        lib.gdr_ref_bwd.argtypes = [P] * 6 + [I] + [P] * 12 + [P, I, I, I, I, I, I, P, I, I]
         lib.gdr_ref_max_threads.restype = I
         lib.gdr_ref_max_threads.argtypes = []
         _LIB = lib
@@ -105,6 +109,54 @@ def recurrence(q, k, v, beta, log_alpha=None, a=None, b=None, S0=None, cu_seqlen
     if rc != 0:
         raise ValueError(f"gdr_ref_fwd rejected its arguments (code {rc})")
     return O, Sf
+
+
+def recurrence_bwd(q, k, v, beta, dO, log_alpha=None, a=None, b=None, S0=None, dS_final=None,
+                   cu_seqlens=None, chains=None, n_threads: int = 0):
+    """Gradients of L = <dO, O> + <dS_final, S_final> for the fp64 recurrence.
+
+    Shapes as in ``recurrence``; dO has O's shape, dS_final S_final's (None: zero).
+    Returns a dict with dq, dk, dv, dbeta, dS0 and, when given, da, db and
+    dlog_alpha (same shapes as the inputs).  Entries of chains that are not
+    computed are NaN.
+    """
+    q, k, v, beta, dO = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(dO)
+    a, b, log_alpha, S0, dSf = _f64(a), _f64(b), _f64(log_alpha), _f64(S0), _f64(dS_final)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert dO.shape == v.shape
+    gate = 0 if log_alpha is None else (1 if log_alpha.ndim == 3 else 2)
+    cu = None
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        N = cu.size - 1
+    else:
+        N = B
+    if S0 is not None:
+        assert S0.shape == (N, H, dv, dk)
+    if dSf is not None:
+        assert dSf.shape == (N, H, dv, dk)
+    g = {"dq": np.full(q.shape, np.nan), "dk": np.full(q.shape, np.nan),
+         "dv": np.full(v.shape, np.nan), "dbeta": np.full(beta.shape, np.nan),
+         "dS0": np.full((N, H, dv, dk), np.nan)}
+    if a is not None:
+        g["da"] = np.full(q.shape, np.nan)
+        g["db"] = np.full(q.shape, np.nan)
+    if log_alpha is not None:
+        g["dlog_alpha"] = np.full(log_alpha.shape, np.nan)
+    ch = None
+    n_ch = 0
+    if chains is not None:
+        ch = np.ascontiguousarray(np.asarray(chains, dtype=np.int32).reshape(-1, 2))
+        n_ch = ch.shape[0]
+    rc = _lib().gdr_ref_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha), gate,
+                            _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dSf), _ptr(g["dq"]),
+                            _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g.get("da")), _ptr(g.get("db")),
+                            _ptr(g.get("dlog_alpha")), _ptr(g["dbeta"]), _ptr(g["dS0"]),
+                            _ptr(cu), N, B, H, T, dk, dv, _ptr(ch), n_ch, int(n_threads))
+    if rc != 0:
+        raise ValueError(f"gdr_ref_bwd rejected its arguments (code {rc})")
+    return g
 
 
 def spectral_norm_rank1(eta: float, k: np.ndarray, j: np.ndarray) -> float:

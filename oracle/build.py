@@ -8,9 +8,9 @@ LIB = os.path.join(HERE, "libgdr_ref.so")
 
 
 def build(verbose: bool = False) -> str:
-    src = os.path.join(HERE, "gdr_ref.c")
+    srcs = [os.path.join(HERE, f) for f in ("gdr_ref.c", "gdr_ref_bwd.c")]
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall", "-Wextra",
-           "-o", LIB + ".tmp", src, "-lm"]
+           "-o", LIB + ".tmp", *srcs, "-lm"]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.check_call(cmd)

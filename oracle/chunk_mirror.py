@@ -112,3 +112,102 @@ def chunk_forward(q, k, v, beta, log_alpha=None, a=None, b=None, S0=None, cu_seq
             Sf[n, h] = S
             records.append(rec)
     return O.reshape(B, T, H, dv), Sf, records
+
+
+def chunk_bwd(q, k, v, beta, dO, log_alpha=None, S0=None, dS_final=None, cu_seqlens=None,
+              C: int = 64, a=None, b=None):
+    """Gradients of <dO, O> + <dS_final, S_final> by the chunk-form backward of the
+    "Kimi Delta Attention backward" notes (KDA form only: a = k, b = beta k), fp64.
+
+    Notation as above, with the notes' state convention S_[t] = S_[t-1] Diag(gamma_C)
+    + V_new^T K-> Diag(gamma_C).  Per chunk, with dS = dL/dS_[t] at its end:
+      dU = dV_new = K-> Diag(gamma_C) dS^T + (Q<- K->^T * M)^T dO
+      dW = -dU S_[t-1]
+      dQ<- = dO S_[t-1] + (dO V_new^T * M) K->,             dQ = dQ<- * Gamma
+      dV = Diag(beta) At^T dU
+      dAt = dW K<-^T Diag(beta) + dU V^T Diag(beta),          dXt = -At^T dAt At^T
+      dK<- = Diag(beta) At^T dW + (Diag(beta) dXt * M_1) K->
+      dK-> = V_new dS Diag(gamma_C) + (dO V_new^T * M)^T Q<- + (Diag(beta) dXt * M_1)^T K<-
+      dK = dK<- * Gamma + dK-> / Gamma
+      dbeta = diag(At^T dW K<-^T + At^T dU V^T + dXt (K<- K->^T * M_1)^T)
+      dlog Gamma = dQ * Q + (dK<- * Gamma) * K - (dK-> / Gamma) * K, plus
+                   diag(S_[t]^T dS) on the chunk's last row
+      dS_[t-1] = dS Diag(gamma_C) + dO^T Q<- - dU^T W
+    and dlog alpha is the suffix sum of dlog Gamma inside the chunk (g is the prefix
+    sum of log alpha), summed over channels for a head gate.  beta is not divided
+    out: the notes' diag(At^T dAt) / beta is written as the diagonal of the first
+    line of their derivation, which is the same number and is defined at beta = 0.
+    """
+    assert a is None and b is None, "chunk_bwd covers the KDA form only"
+    q, k, v, beta, dO = (np.asarray(x, dtype=np.float64) for x in (q, k, v, beta, dO))
+    la = None if log_alpha is None else np.asarray(log_alpha, dtype=np.float64)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    flat = lambda x: None if x is None else x.reshape((B * T,) + x.shape[2:])
+    qf, kf, vf, bf, laf, dOf = map(flat, (q, k, v, beta, la, dO))
+    if cu_seqlens is None:
+        bounds = [(n * T, (n + 1) * T) for n in range(B)]
+    else:
+        cu = list(np.asarray(cu_seqlens).tolist())
+        bounds = [(cu[i], cu[i + 1]) for i in range(len(cu) - 1)]
+    N = len(bounds)
+    out = {"dq": np.zeros((B * T, H, dk)), "dk": np.zeros((B * T, H, dk)),
+           "dv": np.zeros((B * T, H, dv)), "dbeta": np.zeros((B * T, H)),
+           "dS0": np.zeros((N, H, dv, dk))}
+    if la is not None:
+        out["dlog_alpha"] = np.zeros((B * T,) + la.shape[2:])
+    M = np.tril(np.ones((C, C)))
+    M1 = np.tril(np.ones((C, C)), -1)
+    for n, (t0, t1) in enumerate(bounds):
+        for h in range(H):
+            # forward over the chunks, keeping what the backward needs
+            S = np.zeros((dv, dk)) if S0 is None else np.array(S0[n, h], dtype=np.float64)
+            chunks = []
+            for c0 in range(t0, t1, C):
+                c1 = min(c0 + C, t1)
+                m = c1 - c0
+                Q, K, V, dOc = qf[c0:c1, h], kf[c0:c1, h], vf[c0:c1, h], dOf[c0:c1, h]
+                bet = bf[c0:c1, h]
+                Gam = np.exp(_g(None if laf is None else laf[c0:c1, h], m, dk))
+                gC = Gam[-1]
+                Ql, Kl, Kr = Q * Gam, K * Gam, K / Gam
+                At = _unit_lower_inverse(np.eye(m) + bet[:, None] * ((Kl @ Kr.T) * M1[:m, :m]))
+                W = At @ (bet[:, None] * Kl)
+                U = At @ (bet[:, None] * V)
+                Vn = U - W @ S.T
+                Sn = (S + Vn.T @ Kr) * gC[None, :]
+                chunks.append(dict(c0=c0, c1=c1, m=m, Q=Q, K=K, V=V, dO=dOc, bet=bet, Gam=Gam,
+                                   gC=gC, Ql=Ql, Kl=Kl, Kr=Kr, At=At, W=W, Vn=Vn, Sp=S, Sn=Sn))
+                S = Sn
+            dS = np.zeros((dv, dk)) if dS_final is None else np.array(dS_final[n, h], dtype=np.float64)
+            for ch in reversed(chunks):
+                m = ch["m"]
+                Mm, M1m = M[:m, :m], M1[:m, :m]
+                Ql, Kl, Kr, Gam, gC = ch["Ql"], ch["Kl"], ch["Kr"], ch["Gam"], ch["gC"]
+                At, W, Vn, Sp, V, G, bet = ch["At"], ch["W"], ch["Vn"], ch["Sp"], ch["V"], ch["dO"], ch["bet"]
+                dU = (Kr * gC[None, :]) @ dS.T + ((Ql @ Kr.T) * Mm).T @ G
+                dW = -dU @ Sp
+                dOV = (G @ Vn.T) * Mm
+                dQl = G @ Sp + dOV @ Kr
+                dV = bet[:, None] * (At.T @ dU)
+                dAt = (dW @ Kl.T + dU @ V.T) * bet[None, :]
+                dXt = -At.T @ dAt @ At.T
+                dXm = bet[:, None] * dXt * M1m
+                dKl = bet[:, None] * (At.T @ dW) + dXm @ Kr
+                dKr = Vn @ dS * gC[None, :] + dOV.T @ Ql + dXm.T @ Kl
+                dbeta = np.diag(At.T @ dW @ Kl.T + At.T @ dU @ V.T + dXt @ ((Kl @ Kr.T) * M1m).T)
+                dlg = dQl * Ql + dKl * Kl - dKr * Kr
+                dlg[-1] += np.sum(ch["Sn"] * dS, axis=0)
+                sl = slice(ch["c0"], ch["c1"])
+                out["dq"][sl, h] = dQl * Gam
+                out["dk"][sl, h] = dKl * Gam + dKr / Gam
+                out["dv"][sl, h] = dV
+                out["dbeta"][sl, h] = dbeta
+                if la is not None:
+                    suffix = np.cumsum(dlg[::-1], axis=0)[::-1]
+                    out["dlog_alpha"][sl, h] = suffix if la.ndim == 4 else suffix.sum(axis=1)
+                dS = dS * gC[None, :] + G.T @ Ql - dU.T @ W
+            out["dS0"][n, h] = dS
+    res = {key: val.reshape((B, T) + val.shape[1:]) for key, val in out.items() if key != "dS0"}
+    res["dS0"] = out["dS0"]
+    return res
