@@ -114,6 +114,18 @@ struct FwdArgs {
     size_t workspace_bytes;
 };
 
+// Arguments of the backward pass (KDA form: a = k, b = beta k).
+struct BwdArgs {
+    const void *q, *k, *v, *dO;
+    const float *log_alpha, *beta, *S0, *dS_final;
+    void *grad_q, *grad_k, *grad_v;            // dL/dq, dL/dk, dL/dv
+    float *grad_la, *grad_beta, *grad_S0;      // dL/dlog_alpha, dL/dbeta, dL/dS0
+    const int32_t *cu_seqlens;
+    int n_seq, B, H, T, dk, dv, C, dtype, gate;
+    void *workspace;
+    size_t workspace_bytes;
+};
+
 // Launchers (return a hipError_t as int).  Each enqueues on `stream`.
 bool f32_split_supported(const FwdArgs &a);
 size_t f32_split_workspace_bytes(const FwdArgs &a, int n_seq_eff);
@@ -121,5 +133,8 @@ int launch_f32_split(const FwdArgs &a, int n_seq_eff, hipStream_t stream);
 bool kda_split_supported(const FwdArgs &a);
 size_t kda_split_workspace_bytes(const FwdArgs &a, int n_seq_eff);
 int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t stream);
+bool kda_bwd_supported(const BwdArgs &a);
+size_t kda_bwd_workspace_bytes(const BwdArgs &a, int n_seq_eff);
+int launch_kda_bwd(const BwdArgs &a, int n_seq_eff, hipStream_t stream);
 
 }  // namespace gdr

@@ -1,0 +1,589 @@
+// Backward pass of the chunkwise KDA form (internal header, included by
+// gdr_kda_split.hip after the forward kernels).
+//
+// Gradients of L = <dO, O> + <dS_final, S_final> ("Kimi Delta Attention backward"
+// notes), per chunk of C = 64 tokens with the notation of the forward kernels:
+//   g = in-chunk prefix sum of log alpha, Gamma = e^g, gamma_C = Gamma[last row]
+//   Q<- = Q Gamma, K<- = K Gamma, K-> = K / Gamma
+//   KK = K<- K->^T strictly lower, At = (I + Diag(beta) KK)^-1, Ab = At Diag(beta)
+//   A_qk = Q<- K->^T on and below the diagonal, W = Ab K<-, U = Ab V
+//   V_new = U - W S_p^T,  O = Q<- S_p^T + A_qk V_new,  S_n = (S_p + V_new^T K->) Diag(gamma_C)
+// Three passes produce the states the per-chunk gradients need:
+//   forward   the forward state kernel, saving S_p (the state entering each chunk)
+//   reverse   dS_p = dS_n Diag(gamma_C) + (K^ dS_n^T)^T W' + dO^T Q~ over the chunks in
+//             reverse order (the forward state kernel on a reordered block), saving
+//             dS_n (the gradient of the state leaving each chunk); K^ = K-> gamma_C,
+//             W' = -W and Q~ = Q<- - A_qk W come from the forward prep blocks
+//   post      one workgroup per (chunk, head), with dSg = dS_n Diag(gamma_C):
+//     dV_new = K-> dSg^T + A_qk^T dO                  dV = Diag(beta) At^T dV_new
+//     dW = -dV_new S_p,   dA = dO V_new^T (lower),    dKg = V_new dSg
+//     Y = dW K<-^T + dV_new V^T,  Z = At^T Y,  dXt = -Z Ab^T
+//     dbeta = diag(Z) + rowsum(dXt * KK),             dXm = Diag(beta) dXt (strictly lower)
+//     dK<- = Diag(beta) At^T dW + dXm K->
+//     dK-> = dKg + dA^T Q<- + dXm^T K<-
+//     dQ<- = dO S_p + dA K->
+//     dQ = dQ<- Gamma,  dK = dK<- Gamma + dK-> / Gamma
+//     dg = dQ<- Q<- + dK<- K<- - dK-> K->, plus sum_i S_n[i][j] dS_n[i][j] on the last row,
+//          which is sum_i S_p dSg + sum_r K-> dKg by the state update
+//     dlog alpha = suffix sum of dg over the chunk's rows (summed over channels for a
+//     head gate)
+// The notes' dbeta divides diag(At^T dAt) by beta; diag(Z) is the same number written
+// without the division (it is the diagonal of the first line of their derivation).
+#pragma once
+
+namespace gdr {
+namespace {
+
+// ---------------------------------------------------------------------------------
+// Reordering of the forward blocks into the slots the reverse state pass reads.
+// ---------------------------------------------------------------------------------
+// Byte offset of element (row r, contraction column d) in a row-tile fragment slot
+// (W', Q~: rows = tokens, K = DK), and of element (dk row d, token t) in a
+// transposed slot (K^: rows = dk, K = 64 tokens).  See Blk.
+template <int DK>
+__device__ __forceinline__ int nat_off(int r, int d) {
+    const int rt = r >> 5, s = d >> 4, l = (r & 31) + 32 * ((d & 15) >> 3);
+    return (((rt * (DK / 16) + s) * 64 + l) * 8 + (d & 7)) * 2;
+}
+__device__ __forceinline__ int tr_off(int d, int t) {
+    const int w = d >> 5, s = t >> 4, l = (d & 31) + 32 * ((t & 15) >> 3);
+    return (((w * 4 + s) * 64 + l) * 8 + (t & 7)) * 2;
+}
+
+// Backward block of job j: W' slot <- K^ (natural layout), A^ slot <- W' (transposed),
+// K^b slot <- Q~ (transposed), gamma_C copied.  One workgroup per block; the other
+// slots are left as they are (the reverse pass does not use them).
+template <int DK>
+__global__ __launch_bounds__(kThreads) void kda_bwd_reorder_kernel(const char *fwd, char *bwd, int nblk) {
+    using F = Blk<DK, false>;
+    using R = Blk<DK, true>;
+    const int j = blockIdx.x;
+    if (j >= nblk) return;
+    const char *src = fwd + (size_t)j * F::bytes;
+    char *dst = bwd + (size_t)j * R::bytes;
+    constexpr int kPieces = 8 * DK;  // 16-byte pieces per slot
+    for (int u = threadIdx.x; u < 3 * kPieces; u += kThreads) {
+        const int slot = u / kPieces, pc = u % kPieces;
+        const int l = pc & 63, st = pc >> 6;
+        uint16_t v[8];
+        if (slot == 0) {
+            // destination natural (row r, cols d..d+7); source K^ transposed (d + e, r)
+            const int rt = st / (DK / 16), s = st % (DK / 16);
+            const int r = 32 * rt + (l & 31), d = 16 * s + 8 * (l >> 5);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = *(const uint16_t *)(src + F::oK + tr_off(d + e, r));
+        } else {
+            // destination transposed (dk row d, tokens t..t+7); source natural (t + e, d)
+            const int w = st >> 2, s = st & 3;
+            const int d = 32 * w + (l & 31), t = 16 * s + 8 * (l >> 5);
+            const int so = slot == 1 ? F::oW : F::oQ;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = *(const uint16_t *)(src + so + nat_off<DK>(t + e, d));
+        }
+        const int dso = slot == 0 ? R::oW : (slot == 1 ? R::oK : R::oKb);
+        uint4 o;
+        o.x = v[0] | ((uint32_t)v[1] << 16);
+        o.y = v[2] | ((uint32_t)v[3] << 16);
+        o.z = v[4] | ((uint32_t)v[5] << 16);
+        o.w = v[6] | ((uint32_t)v[7] << 16);
+        ((uint4 *)(dst + dso))[pc] = o;
+    }
+    for (int i = threadIdx.x; i < DK; i += kThreads)
+        ((float *)(dst + R::oG))[i] = ((const float *)(src + F::oG))[i];
+}
+
+// ---------------------------------------------------------------------------------
+// Per-chunk gradients.
+// ---------------------------------------------------------------------------------
+struct BwdParams {
+    const bf16 *q, *k, *v, *dO;
+    const float *la, *beta;
+    const uint16_t *S, *dS;  // bf16 [chunk][head][dv][dk]: S_p, dS_n
+    bf16 *dq, *dk, *dv;
+    float *dla, *dbeta;
+    const int32_t *cu;
+    const int32_t *coff;
+    long total;
+    int H, T, dv_, n_seq, nc, max_chunks, C;
+};
+
+// One 16x16 output tile of A B on the 16x16x32 MFMA: lane l ends with
+// D[m0 + l%16][n0 + 4(l/16) + e] in register e.  A is read from a row-major [m][k]
+// array (AT = false) or from one stored [k][m] (AT = true); B from [k][n] (BT =
+// false) or [n][k] (BT = true).  The contraction runs over [k0, k1) in steps of 32.
+template <bool AT, bool BT>
+__device__ __forceinline__ f32x4 mma_tile(const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                                          int m0, int n0, int k0, int k1, f32x4 acc, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    for (int k = k0; k < k1; k += 32) {
+        const bf16x8 fa = AT ? frag_tr(A, k, lda, m0, lane) : frag(A, m0 + r, lda, k + 8 * g);
+        const bf16x8 fb = BT ? frag(B, n0 + r, ldb, k + 8 * g) : frag_tr(B, k, ldb, n0, lane);
+        acc = mfma(fb, fa, acc);
+    }
+    return acc;
+}
+
+template <int DK>
+struct BwdSmem {
+    static constexpr int KS = DK + 8;           // bf16 stride of [64][DK] arrays
+    static constexpr int CS = kC + 8;           // bf16 stride of [64][64] arrays
+    static constexpr int VS = 32 + 8;           // bf16 stride of [64][32] value tiles
+    static constexpr int QK = kC * KS * 2;      // bytes of one [64][KS] array
+    static constexpr int CC = kC * CS * 2;      // bytes of one [64][CS] array
+    static constexpr int oQl = 0;               // Q<-
+    static constexpr int oKl = oQl + QK;        // K<-
+    static constexpr int oKr = oKl + QK;        // K->
+    static constexpr int oA = oKr + QK;         // At
+    static constexpr int oAb = oA + CC;         // Ab
+    static constexpr int oAqk = oAb + CC;       // A_qk
+    static constexpr int oW = oAqk + CC;        // W, then dW
+    static constexpr int oT = oW + QK;          // per-dv-tile region, reused below
+    //   dv tile: S_p [32][KS], dSg [32][KS], V, dO, V_new, dV_new [64][VS]
+    static constexpr int tSp = 0, tdS = tSp + 32 * KS * 2, tV = tdS + 32 * KS * 2;
+    static constexpr int tdO = tV + kC * VS * 2, tVn = tdO + kC * VS * 2, tdVn = tVn + kC * VS * 2;
+    static constexpr int tEnd = tdVn + kC * VS * 2;
+    //   after the dv loop: dA, dXm (Y first), Z at tSp..; the inverse's KK fp32 [64][68] at 0
+    static constexpr int tdA = 0, tY = CC, tZ = 2 * CC;
+    static constexpr int Tbytes = (tEnd > 3 * CC ? tEnd : 3 * CC) > kC * 68 * 4
+                                      ? (tEnd > 3 * CC ? tEnd : 3 * CC) : kC * 68 * 4;
+    static constexpr int oBeta = oT + Tbytes;   // fp32 [64]
+    static constexpr int oGam = oBeta + kC * 4; // fp32 [DK] gamma_C
+    static constexpr int oGp = oGam + DK * 4;   // fp32 [8][DK] gate partial sums
+    static constexpr int oDb = oGp + 8 * DK * 4;  // fp32 [64] dbeta
+    static constexpr int oDg = oDb + kC * 4;    // fp32 [DK] last-row term of dg
+    static constexpr int bytes = oDg + DK * 4;
+    // final stage: Gamma fp32 [64][DK] over Q<-..K-> (free by then), dg fp32 [64][DK] over T
+    static_assert(kC * DK * 4 <= 3 * QK, "Gamma fits over the operand arrays");
+    static_assert(kC * DK * 4 <= Tbytes, "dg fits over the tile region");
+    static_assert(bytes <= 160 * 1024, "LDS");
+};
+
+template <int DK, int GATE>
+__global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) {
+    using L = BwdSmem<DK>;
+    constexpr int KS = L::KS, CS = L::CS, VS = L::VS;
+    constexpr int NT = DK / 16;   // 16-column tiles of dk
+    constexpr int CPT = DK / 32;  // gate stage: channels per thread
+    __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+    uint16_t *sQl = (uint16_t *)(smem + L::oQl), *sKl = (uint16_t *)(smem + L::oKl);
+    uint16_t *sKr = (uint16_t *)(smem + L::oKr), *sA = (uint16_t *)(smem + L::oA);
+    uint16_t *sAb = (uint16_t *)(smem + L::oAb), *sAqk = (uint16_t *)(smem + L::oAqk);
+    uint16_t *sW = (uint16_t *)(smem + L::oW);
+    char *sT = smem + L::oT;
+    uint16_t *sSp = (uint16_t *)(sT + L::tSp), *sdS = (uint16_t *)(sT + L::tdS);
+    uint16_t *sV = (uint16_t *)(sT + L::tV), *sdO = (uint16_t *)(sT + L::tdO);
+    uint16_t *sVn = (uint16_t *)(sT + L::tVn), *sdVn = (uint16_t *)(sT + L::tdVn);
+    float *sBeta = (float *)(smem + L::oBeta), *sGam = (float *)(smem + L::oGam);
+    float *sGp = (float *)(smem + L::oGp), *sDb = (float *)(smem + L::oDb);
+    float *sDg = (float *)(smem + L::oDg);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int H = p.H, DV = p.dv_;
+    const int job = blockIdx.x;
+    const int h = job % H;
+    int n = 0, c = 0;
+    if (!chunk_of(p, job / H, n, c)) return;  // workgroup-uniform
+    long t0, t1;
+    seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
+    const long tok0 = t0 + (long)c * kC;
+    const int m = (int)((t1 - tok0) < kC ? (t1 - tok0) : kC);
+    const size_t sbase = (size_t)(job / H) * H + h;  // (chunk, head) index of the state buffers
+    const int R0 = 16 * wave;                        // this wave's 16 rows of every row-block output
+
+    // ---- gate: g for rows 8rg + i, channels c0 + e (natural log, inclusive prefix) ----
+    const int rg = tid >> 5, c0 = CPT * (tid & 31);
+    auto gate = [&](float (&g)[8][CPT]) {
+        float run[CPT];
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) run[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * rg + i;
+            const size_t th = (size_t)(tok0 + r) * H + h;
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) {
+                float x = 0.f;
+                if (r < m) {
+                    if (GATE == kGateChannel) x = p.la[th * DK + c0 + e];
+                    else if (GATE == kGateHead) x = p.la[th];
+                }
+                run[e] += x;
+                g[i][e] = run[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) sGp[rg * DK + c0 + e] = run[e];
+        lds_barrier();
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+            float carry = 0.f;
+            for (int r2 = 0; r2 < rg; ++r2) carry += sGp[r2 * DK + c0 + e];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) g[i][e] += carry;
+        }
+        lds_barrier();  // sGp may be reused
+    };
+
+    // ---- stage 0: scaled operands ---------------------------------------------------
+    {
+        float g[8][CPT];
+        gate(g);
+        if (tid < kC) sBeta[tid] = tid < m ? p.beta[(size_t)(tok0 + tid) * H + h] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * rg + i;
+            const size_t th = (size_t)(tok0 + r) * H + h;
+            float qv[CPT], kv[CPT];
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) {
+                qv[e] = r < m ? __bfloat162float(p.q[th * DK + c0 + e]) : 0.f;
+                kv[e] = r < m ? __bfloat162float(p.k[th * DK + c0 + e]) : 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) {
+                const float G = expf(g[i][e]), iG = expf(-g[i][e]);
+                sQl[r * KS + c0 + e] = __builtin_bit_cast(uint16_t, (__bf16)(qv[e] * G));
+                sKl[r * KS + c0 + e] = __builtin_bit_cast(uint16_t, (__bf16)(kv[e] * G));
+                sKr[r * KS + c0 + e] = __builtin_bit_cast(uint16_t, (__bf16)(kv[e] * iG));
+                if (r == kC - 1) sGam[c0 + e] = G;
+            }
+        }
+        for (int i = tid; i < kC; i += kThreads) sDb[i] = 0.f;
+        for (int i = tid; i < DK; i += kThreads) sDg[i] = 0.f;
+    }
+    lds_barrier();
+
+    // ---- stage 1: KK (fp32, for the inverse) and A_qk --------------------------------
+    float *sKK = (float *)sT;  // [64][68]
+    {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        for (int tj = 0; tj < 4; ++tj) {
+            f32x4 kk = z, aq = z;
+            if (tj <= wave) {
+                kk = mma_tile<false, true>(sKl, KS, sKr, KS, R0, 16 * tj, 0, DK, z, lane);
+                aq = mma_tile<false, true>(sQl, KS, sKr, KS, R0, 16 * tj, 0, DK, z, lane);
+            }
+            const int row = R0 + r16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int col = 16 * tj + 4 * g4 + e;
+                sKK[row * 68 + col] = col < row ? kk[e] : 0.f;
+                sAqk[row * CS + col] = __builtin_bit_cast(uint16_t, (__bf16)(col <= row ? aq[e] : 0.f));
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- stage 2: At = (I + Diag(beta) KK)^-1 by forward substitution, lane j = column j
+    if (wave == 0) {
+        const int j = lane;
+        float x[kC];
+#pragma unroll
+        for (int i = 0; i < kC; ++i) {
+            float acc = i == j ? 1.f : 0.f;
+            const float bi = sBeta[i];
+            float s = 0.f;
+#pragma unroll
+            for (int k2 = 0; k2 < i; ++k2) s += sKK[i * 68 + k2] * x[k2];
+            x[i] = acc - bi * s;
+        }
+        const float bj = sBeta[j];
+#pragma unroll
+        for (int i = 0; i < kC; ++i) {
+            sA[i * CS + j] = __builtin_bit_cast(uint16_t, (__bf16)x[i]);
+            sAb[i * CS + j] = __builtin_bit_cast(uint16_t, (__bf16)(x[i] * bj));
+        }
+    }
+    lds_barrier();
+
+    // ---- stage 3: W = Ab K<- ---------------------------------------------------------
+    {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const int k1 = R0 + 16 <= 32 ? 32 : 64;  // Ab is lower triangular
+        for (int tn = 0; tn < NT; ++tn) {
+            const f32x4 w = mma_tile<false, false>(sAb, CS, sKl, KS, R0, 16 * tn, 0, k1, z, lane);
+            store4(sW + (R0 + r16) * KS + 16 * tn + 4 * g4, w[0], w[1], w[2], w[3]);
+        }
+    }
+    lds_barrier();
+
+    // ---- stage 4: the dv tiles ---------------------------------------------------------
+    f32x4 aQ[NT], aW[NT], aKg[NT], aA[4], aY[4];
+    {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) aQ[t] = aW[t] = aKg[t] = z;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) aA[t] = aY[t] = z;
+    }
+    float gpart = 0.f;  // sum over dv of S_p * dSg, column tid % DK
+    const int lo_k = R0 >= 32 ? 32 : 0;  // At^T / A_qk^T rows R0..: contraction over j >= R0
+    for (int j0 = 0; j0 < DV; j0 += 32) {
+        // loads: state tiles (dv rows j0..j0+31), value and dO tiles (64 x 32)
+        {
+            const uint16_t *ps = p.S + (sbase * DV + j0) * DK;
+            const uint16_t *pd = p.dS + (sbase * DV + j0) * DK;
+#pragma unroll
+            for (int i = 0; i < 32 * DK / 8 / kThreads; ++i) {
+                const int idx = tid + kThreads * i, r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+                *(uint4 *)(sSp + r * KS + c8) = *(const uint4 *)(ps + (size_t)r * DK + c8);
+                const uint4 dw = *(const uint4 *)(pd + (size_t)r * DK + c8);
+                const uint32_t w4[4] = {dw.x, dw.y, dw.z, dw.w};
+                uint32_t o4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o4[e] = pack_bf16x2(bf16_lo(w4[e]) * sGam[c8 + 2 * e], bf16_hi(w4[e]) * sGam[c8 + 2 * e + 1]);
+                *(uint4 *)(sdS + r * KS + c8) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+            }
+            const int r = tid >> 2, c8 = 8 * (tid & 3);
+            uint4 vv = make_uint4(0u, 0u, 0u, 0u), dd = vv;
+            if (r < m) {
+                const size_t off = ((size_t)(tok0 + r) * H + h) * DV + j0 + c8;
+                vv = *(const uint4 *)(p.v + off);
+                dd = *(const uint4 *)(p.dO + off);
+            }
+            *(uint4 *)(sV + r * VS + c8) = vv;
+            *(uint4 *)(sdO + r * VS + c8) = dd;
+        }
+        lds_barrier();
+        // V_new = Ab V - W S_p^T and dV_new = K-> dSg^T + A_qk^T dO, rows R0..R0+15
+        {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const int k1 = R0 + 16 <= 32 ? 32 : 64;
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn) {
+                f32x4 u = mma_tile<false, false>(sAb, CS, sV, VS, R0, 16 * tn, 0, k1, z, lane);
+                const f32x4 ws = mma_tile<false, true>(sW, KS, sSp, KS, R0, 16 * tn, 0, DK, z, lane);
+                f32x4 dv = mma_tile<false, true>(sKr, KS, sdS, KS, R0, 16 * tn, 0, DK, z, lane);
+                dv = mma_tile<true, false>(sAqk, CS, sdO, VS, R0, 16 * tn, lo_k, kC, dv, lane);
+                store4(sVn + (R0 + r16) * VS + 16 * tn + 4 * g4, u[0] - ws[0], u[1] - ws[1],
+                       u[2] - ws[2], u[3] - ws[3]);
+                store4(sdVn + (R0 + r16) * VS + 16 * tn + 4 * g4, dv[0], dv[1], dv[2], dv[3]);
+            }
+        }
+        lds_barrier();
+        {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const int row = R0 + r16;
+            const float br = sBeta[row];
+            // dV = Diag(beta) At^T dV_new
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn) {
+                const f32x4 d = mma_tile<true, false>(sA, CS, sdVn, VS, R0, 16 * tn, lo_k, kC, z, lane);
+                if (row < m) {
+                    uint2 o;
+                    o.x = pack_bf16x2(br * d[0], br * d[1]);
+                    o.y = pack_bf16x2(br * d[2], br * d[3]);
+                    *(uint2 *)(p.dv + ((size_t)(tok0 + row) * H + h) * DV + j0 + 16 * tn + 4 * g4) = o;
+                }
+            }
+            // contraction over this dv tile: dQ<- += dO S_p, dW += dV_new S_p, dKg += V_new dSg
+            const bf16x8 fdo = frag(sdO, R0 + r16, VS, 8 * g4);
+            const bf16x8 fdv = frag(sdVn, R0 + r16, VS, 8 * g4);
+            const bf16x8 fvn = frag(sVn, R0 + r16, VS, 8 * g4);
+#pragma unroll
+            for (int tn = 0; tn < NT; ++tn) {
+                const bf16x8 fs = frag_tr(sSp, 0, KS, 16 * tn, lane);
+                const bf16x8 fd = frag_tr(sdS, 0, KS, 16 * tn, lane);
+                aQ[tn] = mfma(fs, fdo, aQ[tn]);
+                aW[tn] = mfma(fs, fdv, aW[tn]);
+                aKg[tn] = mfma(fd, fvn, aKg[tn]);
+            }
+            // dA += dO V_new^T (lower tiles), Y += dV_new V^T
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj) {
+                if (tj <= wave) aA[tj] = mfma(frag(sVn, 16 * tj + r16, VS, 8 * g4), fdo, aA[tj]);
+                aY[tj] = mfma(frag(sV, 16 * tj + r16, VS, 8 * g4), fdv, aY[tj]);
+            }
+            // sum_i S_p[i][j] dSg[i][j] over the tile's 32 rows
+            {
+                const int col = tid % DK, half = tid / DK;  // DK = 128: 2 halves; DK = 64: 4
+                constexpr int NH = kThreads / DK;
+                for (int r = half; r < 32; r += NH)
+                    gpart += bf16_lo(sSp[r * KS + col]) * bf16_lo(sdS[r * KS + col]);
+            }
+        }
+        lds_barrier();  // the tile buffers are reloaded
+    }
+
+    // ---- stage 5: dW, dA, Y, Z, dXt, dbeta --------------------------------------------
+    uint16_t *sdW = sW;
+    uint16_t *sdA = (uint16_t *)(sT + L::tdA), *sY = (uint16_t *)(sT + L::tY);
+    uint16_t *sZ = (uint16_t *)(sT + L::tZ), *sdXm = sY;
+    {
+        const int row = R0 + r16;
+#pragma unroll
+        for (int tn = 0; tn < NT; ++tn)
+            store4(sdW + row * KS + 16 * tn + 4 * g4, -aW[tn][0], -aW[tn][1], -aW[tn][2], -aW[tn][3]);
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+            float d[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[e] = (16 * tj + 4 * g4 + e <= row) ? aA[tj][e] : 0.f;
+            store4(sdA + row * CS + 16 * tj + 4 * g4, d[0], d[1], d[2], d[3]);
+        }
+        atomicAdd(&sDg[tid % DK], gpart);
+    }
+    lds_barrier();
+    {
+        const int row = R0 + r16;
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+            aY[tj] = mma_tile<false, true>(sdW, KS, sKl, KS, R0, 16 * tj, 0, DK, aY[tj], lane);
+            store4(sY + row * CS + 16 * tj + 4 * g4, aY[tj][0], aY[tj][1], aY[tj][2], aY[tj][3]);
+        }
+    }
+    lds_barrier();
+    {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const int row = R0 + r16;
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+            const f32x4 zt = mma_tile<true, false>(sA, CS, sY, CS, R0, 16 * tj, lo_k, kC, z, lane);
+            store4(sZ + row * CS + 16 * tj + 4 * g4, zt[0], zt[1], zt[2], zt[3]);
+            if (tj == wave && (r16 >> 2) == g4) sDb[row] = zt[r16 & 3];  // diag(Z)
+        }
+    }
+    lds_barrier();
+    {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const int row = R0 + r16;
+        const float br = sBeta[row];
+        float db2 = 0.f;
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+            f32x4 dx = z;
+            if (tj <= wave) {
+                dx = mma_tile<false, true>(sZ, CS, sAb, CS, R0, 16 * tj, 0, kC, z, lane);
+                const f32x4 kk = mma_tile<false, true>(sKl, KS, sKr, KS, R0, 16 * tj, 0, DK, z, lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int col = 16 * tj + 4 * g4 + e;
+                    dx[e] = col < row ? -dx[e] : 0.f;  // dXt, strictly lower
+                    db2 += dx[e] * kk[e];
+                }
+            }
+            store4(sdXm + row * CS + 16 * tj + 4 * g4, br * dx[0], br * dx[1], br * dx[2], br * dx[3]);
+        }
+        db2 += __shfl_xor(db2, 16);
+        db2 += __shfl_xor(db2, 32);
+        // (sdXm overwrites Y: every wave finished reading Y, for Z, before the barrier
+        // above; diag(Z) went into sDb before it too)
+        if (g4 == 0) sDb[row] += db2;
+    }
+    lds_barrier();
+
+    // ---- stage 6: dK<-, dK->, dQ<- ------------------------------------------------------
+    f32x4 gKl[NT], gKr[NT], gQl[NT];
+    {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const int row = R0 + r16;
+        const float br = sBeta[row];
+        float dgp[NT][4];
+#pragma unroll
+        for (int tn = 0; tn < NT; ++tn) {
+            f32x4 a = mma_tile<true, false>(sA, CS, sdW, KS, R0, 16 * tn, lo_k, kC, z, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] *= br;
+            gKl[tn] = mma_tile<false, false>(sdXm, CS, sKr, KS, R0, 16 * tn, 0, kC, a, lane);
+            f32x4 b = mma_tile<true, false>(sdA, CS, sQl, KS, R0, 16 * tn, lo_k, kC, aKg[tn], lane);
+            gKr[tn] = mma_tile<true, false>(sdXm, CS, sKl, KS, R0, 16 * tn, lo_k, kC, b, lane);
+            gQl[tn] = mma_tile<false, false>(sdA, CS, sKr, KS, R0, 16 * tn, 0, kC, aQ[tn], lane);
+            // last-row term: sum over rows of K-> dKg, per column
+            const uint2 kr = *(const uint2 *)(sKr + row * KS + 16 * tn + 4 * g4);
+            dgp[tn][0] = bf16_lo(kr.x) * aKg[tn][0];
+            dgp[tn][1] = bf16_hi(kr.x) * aKg[tn][1];
+            dgp[tn][2] = bf16_lo(kr.y) * aKg[tn][2];
+            dgp[tn][3] = bf16_hi(kr.y) * aKg[tn][3];
+        }
+#pragma unroll
+        for (int tn = 0; tn < NT; ++tn)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float s = group_sum<16>(dgp[tn][e]);
+                if (r16 == 0) atomicAdd(&sDg[16 * tn + 4 * g4 + e], s);
+            }
+    }
+    lds_barrier();  // the operand arrays are free: Gamma goes over them
+
+    // ---- stage 7: chain rule through Gamma, suffix sums ------------------------------
+    float *sGm = (float *)(smem + L::oQl);  // fp32 [64][DK] Gamma
+    float *sDl = (float *)sT;               // fp32 [64][DK] dg
+    {
+        float g[8][CPT];
+        gate(g);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) sGm[(8 * rg + i) * DK + c0 + e] = g[i][e];
+    }
+    lds_barrier();
+    {
+        const int row = R0 + r16;
+        const bool ok = row < m;
+        const size_t th = (size_t)(tok0 + (ok ? row : 0)) * H + h;
+#pragma unroll
+        for (int tn = 0; tn < NT; ++tn) {
+            const int col = 16 * tn + 4 * g4;
+            float qv[4] = {0.f, 0.f, 0.f, 0.f}, kv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (ok) {
+                const uint2 qw = *(const uint2 *)(p.q + th * DK + col);
+                const uint2 kw = *(const uint2 *)(p.k + th * DK + col);
+                qv[0] = bf16_lo(qw.x); qv[1] = bf16_hi(qw.x); qv[2] = bf16_lo(qw.y); qv[3] = bf16_hi(qw.y);
+                kv[0] = bf16_lo(kw.x); kv[1] = bf16_hi(kw.x); kv[2] = bf16_lo(kw.y); kv[3] = bf16_hi(kw.y);
+            }
+            float dq4[4], dk4[4], dl4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float gv = sGm[row * DK + col + e];
+                const float G = expf(gv), iG = expf(-gv);
+                dq4[e] = gQl[tn][e] * G;
+                dk4[e] = gKl[tn][e] * G + gKr[tn][e] * iG;
+                dl4[e] = gQl[tn][e] * qv[e] * G + gKl[tn][e] * kv[e] * G - gKr[tn][e] * kv[e] * iG;
+            }
+            if (ok) {
+                uint2 o;
+                o.x = pack_bf16x2(dq4[0], dq4[1]);
+                o.y = pack_bf16x2(dq4[2], dq4[3]);
+                *(uint2 *)(p.dq + th * DK + col) = o;
+                o.x = pack_bf16x2(dk4[0], dk4[1]);
+                o.y = pack_bf16x2(dk4[2], dk4[3]);
+                *(uint2 *)(p.dk + th * DK + col) = o;
+            }
+            *(float4 *)(sDl + row * DK + col) = make_float4(dl4[0], dl4[1], dl4[2], dl4[3]);
+        }
+        if (tid < kC && tid < m) p.dbeta[(size_t)(tok0 + tid) * H + h] = sDb[tid];
+    }
+    lds_barrier();
+    if (GATE == kGateChannel) {
+        for (int col = tid; col < DK; col += kThreads) {
+            float acc = sDg[col];  // the last-row term
+            for (int r = kC - 1; r >= 0; --r) {
+                acc += sDl[r * DK + col];
+                if (r < m) p.dla[((size_t)(tok0 + r) * H + h) * DK + col] = acc;
+            }
+        }
+    } else if (GATE == kGateHead) {
+        // row sums (and the last-row term) into sGp, then the suffix sum by one thread
+        if (tid < kC) {
+            float s = 0.f;
+            for (int col = 0; col < DK; ++col) s += sDl[tid * DK + col];
+            if (tid == kC - 1)
+                for (int col = 0; col < DK; ++col) s += sDg[col];
+            sGp[tid] = s;
+        }
+        lds_barrier();
+        if (tid == 0) {
+            float acc = 0.f;
+            for (int r = kC - 1; r >= 0; --r) {
+                acc += sGp[r];
+                if (r < m) p.dla[(size_t)(tok0 + r) * H + h] = acc;
+            }
+        }
+    }
+}
+
+}  // namespace
+}  // namespace gdr

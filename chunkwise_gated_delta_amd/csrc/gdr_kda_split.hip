@@ -37,6 +37,7 @@
 // S = (S + V'^T K-> + N^T A->) Diag(gamma_C), with V' = Diag(beta) V.  The prep kernel hands its results over in the
 // operand order of v_mfma_f32_32x32x16_bf16, so the state kernel loads them straight
 // into registers with whole-wave contiguous loads.
+#include <cstring>
 #include <type_traits>
 
 #include "gdr_mfma.h"
@@ -83,6 +84,7 @@ struct SplitParams {
     int32_t *order;  // packed sequences, longest first (with cu_seqlens), else NULL
     int *err;
     char *blk;      // (chunk, head) blocks
+    uint16_t *states;  // state kernel modes 1, 2: bf16 [chunk][head][dv][dk], the state entering each step
     long total;
     int H, T, dv, n_seq, n_tiles;
     int C;           // chunk size (always kC here)
@@ -794,7 +796,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Chunks whose operands are in flight ahead of the one being computed.
 constexpr int kDepth = 2;
 
-template <int DK, bool DP>
+// Modes of the state kernel.  Forward: the forward pass.  SaveStates: the forward
+// recurrence without the output, writing the state that enters each chunk (bf16)
+// to p.states.  Reverse: the chunks in reverse order, no output and no Ab V term,
+// writing the state entering each step to p.states; with the slots of a backward
+// block (W' slot: K^, A^ slot: W', K^b slot: Q~, value tile: dO) and DP set this is
+// the backward state pass dS <- dS Diag(gamma_C) + (K^ dS^T)^T W' + dO^T Q~.
+constexpr int kForward = 0, kSaveStates = 1, kReverse = 2;
+
+template <int DK, bool DP, int MODE = kForward>
 __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     using L = StateSmem<DK>;
     using Bk = Blk<DK, DP>;
@@ -838,6 +848,8 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
 
     const int rt = wave & 1;      // 32-row tile of the chunk
     const bool vw = wave < 2;     // V_new waves (W', Ab); waves 2, 3: output (Q~, Ao)
+    // chunk of the sequence that step c works on
+    auto cid = [&](int c) { return MODE == kReverse ? nck - 1 - c : c; };
     uint16_t *sO = (uint16_t *)(smem + L::oO) + (wave & 1) * 32 * kVS;
 
     // state: wave w < NSW holds S^T[dk 32w..+31][dv 0..31]; register 4q+e is
@@ -858,13 +870,13 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     // Loads of one chunk in two batches: the W'/Q~ tile first, the rest later in the
     // step, so that the memory pipeline is fed while the wave computes.
     auto load_p = [&](Pre<DK> &x, int c) {
-        const char *bp = p.blk + ((size_t)(cbase + c) * H + h) * Bk::bytes;
+        const char *bp = p.blk + ((size_t)(cbase + cid(c)) * H + h) * Bk::bytes;
         const uint4 *pw = (const uint4 *)(bp + (vw ? Bk::oW : Bk::oQ)) + rt * (DK / 16) * 64 + lane;
 #pragma unroll
         for (int s = 0; s < DK / 16; ++s) x.P[s] = pw[s * 64];
     };
     auto load_rest = [&](Pre<DK> &x, int c) {
-        const char *bp = p.blk + ((size_t)(cbase + c) * H + h) * Bk::bytes;
+        const char *bp = p.blk + ((size_t)(cbase + cid(c)) * H + h) * Bk::bytes;
         const uint4 *pa = (const uint4 *)(bp + (vw ? Bk::oAb : Bk::oAo)) + rt * 128 + lane;
         x.A[0] = pa[0];
         x.A[1] = pa[64];
@@ -882,7 +894,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
                 for (int s = 0; s < 4; ++s) x.Kb[s] = pkb[s * 64];
             }
         }
-        const long tok = t0 + (long)c * kC + vr;
+        const long tok = t0 + (long)cid(c) * kC + vr;
         x.V = *(const uint4 *)(p.v + ((size_t)(tok < t1 ? tok : t1 - 1) * H + h) * DV + j0 + vc);
         if (wave == 0 && lane < DK / 4) x.G = ((const float4 *)(bp + Bk::oG))[lane];
     };
@@ -905,13 +917,22 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
         if (wave == 0 && lane < DK / 4) ((float4 *)sG)[lane] = x.G;
         {
             // rows past the end of the sequence are zero (branch-free: a lane mask)
-            const uint32_t keep = 0u - (uint32_t)(t0 + (long)c * kC + vr < t1);
+            const uint32_t keep = 0u - (uint32_t)(t0 + (long)cid(c) * kC + vr < t1);
             *(uint4 *)(sV + vr * kVS + vc) = make_uint4(x.V.x & keep, x.V.y & keep, x.V.z & keep, x.V.w & keep);
         }
-        if (!vw && c > 0) store_out(c - 1);
+        if (MODE == kForward && !vw && c > 0) store_out(c - 1);
         const int cn = c + kDepth < nck ? c + kDepth : nck - 1;
         load_p(nx, cn);
         lds_barrier();  // value tile, gamma_C and S of chunk c visible
+        if constexpr (MODE != kForward) {
+            // the state entering this step, bf16, 16 bytes per thread and pass
+            uint16_t *dst = p.states + (((size_t)(cbase + cid(c)) * H + h) * DV + j0) * DK;
+#pragma unroll
+            for (int i = 0; i < kDVT * DK / 8 / kThreads; ++i) {
+                const int idx = tid + kThreads * i, r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+                *(uint4 *)(dst + (size_t)r * DK + c8) = *(const uint4 *)(sS + r * KS + c8);
+            }
+        }
 
         // LDS operands are all read before the products so that their latency overlaps.
         bf16x8 fv[4], fs[DK / 16];
@@ -923,11 +944,13 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
         f32x16 acc = {};
         if (vw) {
             // V_new = Ab V + W' S^T; register 4q+e is V_new[row 32rt + 8q + 4lh + e][dv l32]
-            acc = mfma32x32(as_bf16x8(x.A[0]), fv[0], acc);
-            acc = mfma32x32(as_bf16x8(x.A[1]), fv[1], acc);
-            if (rt) {
-                acc = mfma32x32(as_bf16x8(x.A[2]), fv[2], acc);
-                acc = mfma32x32(as_bf16x8(x.A[3]), fv[3], acc);
+            if constexpr (MODE != kReverse) {
+                acc = mfma32x32(as_bf16x8(x.A[0]), fv[0], acc);
+                acc = mfma32x32(as_bf16x8(x.A[1]), fv[1], acc);
+                if (rt) {
+                    acc = mfma32x32(as_bf16x8(x.A[2]), fv[2], acc);
+                    acc = mfma32x32(as_bf16x8(x.A[3]), fv[3], acc);
+                }
             }
 #pragma unroll
             for (int s = 0; s < DK / 16; ++s) acc = mfma32x32(as_bf16x8(x.P[s]), fs[s], acc);
@@ -935,7 +958,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
             for (int q = 0; q < 4; ++q)
                 store4(sVn + l32 * kCS + 32 * rt + 8 * q + 4 * lh, acc[4 * q + 0], acc[4 * q + 1],
                        acc[4 * q + 2], acc[4 * q + 3]);
-        } else {
+        } else if constexpr (MODE == kForward) {
             // O^T = V^T Ao^T + S Q~^T (operands swapped); register 4q+e is
             // O[row 32rt + l32][dv 8q + 4lh + e]
             acc = mfma32x32(fv[0], as_bf16x8(x.A[0]), acc);
@@ -1001,7 +1024,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
             step(c, buf[0], buf[2]);
             if (c + 1 < nck) step(c + 1, buf[1], buf[0]);
         }
-        if (!vw) store_out(nck - 1);
+        if (MODE == kForward && !vw) store_out(nck - 1);
     }
 
     if (p.Sf && wave < NSW) {
@@ -1031,6 +1054,44 @@ int compute_units() {
 int blk_bytes(int dk, bool dp) {
     if (dp) return dk == 128 ? Blk<128, true>::bytes : Blk<64, true>::bytes;
     return dk == 128 ? Blk<128>::bytes : Blk<64>::bytes;
+}
+
+}  // namespace
+}  // namespace gdr
+
+#include "gdr_kda_bwd.h"
+
+namespace gdr {
+namespace {
+
+// Forward-pass view of the backward arguments (for the shared sizing and planning).
+FwdArgs fwd_view(const BwdArgs &b) {
+    FwdArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = b.q; a.k = b.k; a.v = b.v; a.log_alpha = b.log_alpha; a.beta = b.beta; a.S0 = b.S0;
+    a.cu_seqlens = b.cu_seqlens;
+    a.n_seq = b.n_seq; a.B = b.B; a.H = b.H; a.T = b.T; a.dk = b.dk; a.dv = b.dv; a.C = b.C;
+    a.dtype = b.dtype; a.gate = b.gate;
+    return a;
+}
+
+// Backward workspace: [header][packed-sequence plan][forward blocks][backward blocks]
+// [S_p states][dS_n states], the states bf16 [chunk][head][dv][dk].
+struct BwdLayout {
+    SplitLayout fw;
+    size_t bwd_off, s_off, ds_off, total;
+};
+
+BwdLayout bwd_layout(const BwdArgs &b, int N) {
+    BwdLayout L;
+    const FwdArgs a = fwd_view(b);
+    L.fw = split_layout(a, N, blk_bytes(b.dk, false));
+    const size_t nblk = (size_t)b.H * L.fw.max_chunks;
+    L.bwd_off = L.fw.total;
+    L.s_off = L.bwd_off + nblk * blk_bytes(b.dk, true);
+    L.ds_off = L.s_off + nblk * b.dv * b.dk * 2;
+    L.total = L.ds_off + nblk * b.dv * b.dk * 2;
+    return L;
 }
 
 }  // namespace
@@ -1093,6 +1154,80 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
 #undef GDR_PATH
 #undef GDR_GATES
 #undef GDR_PREP
+    return (int)hipGetLastError();
+}
+
+}  // namespace gdr
+
+namespace gdr {
+
+bool kda_bwd_supported(const BwdArgs &a) {
+    return a.dtype == 1 && a.C == kC && (a.dk == 64 || a.dk == 128) && a.dv % kDVT == 0 &&
+           a.dv <= 256 && a.gate >= kGateNone && a.gate <= kGateChannel;
+}
+
+size_t kda_bwd_workspace_bytes(const BwdArgs &a, int n_seq_eff) { return bwd_layout(a, n_seq_eff).total; }
+
+int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
+    const bool varlen = b.cu_seqlens != nullptr;
+    const BwdLayout lay = bwd_layout(b, n_seq_eff);
+    const int max_chunks = lay.fw.max_chunks;
+    char *ws = (char *)b.workspace;
+    SplitParams sp;
+    std::memset(&sp, 0, sizeof(sp));
+    sp.q = (const bf16 *)b.q; sp.k = (const bf16 *)b.k; sp.v = (const bf16 *)b.v;
+    sp.la = b.log_alpha; sp.beta = b.beta; sp.S0 = b.S0; sp.cu = b.cu_seqlens;
+    sp.err = (int *)ws;
+    sp.coff = varlen ? (int32_t *)(ws + lay.fw.coff_off) : nullptr;
+    sp.order = varlen ? sp.coff + n_seq_eff + 1 : nullptr;
+    sp.blk = ws + lay.fw.blk_off;
+    sp.states = (uint16_t *)(ws + lay.s_off);
+    sp.total = (long)b.B * b.T;
+    sp.H = b.H; sp.T = b.T; sp.dv = b.dv; sp.n_seq = n_seq_eff; sp.n_tiles = b.dv / kDVT;
+    sp.nc = lay.fw.nc; sp.max_chunks = max_chunks; sp.C = kC;
+    // the reverse pass: backward blocks, dO as the value tile, dS_final in, dS0 out
+    SplitParams rp = sp;
+    rp.blk = ws + lay.bwd_off;
+    rp.v = (const bf16 *)b.dO;
+    rp.S0 = b.dS_final;
+    rp.Sf = b.grad_S0;
+    rp.states = (uint16_t *)(ws + lay.ds_off);
+    BwdParams bp;
+    std::memset(&bp, 0, sizeof(bp));
+    bp.q = (const bf16 *)b.q; bp.k = (const bf16 *)b.k; bp.v = (const bf16 *)b.v;
+    bp.dO = (const bf16 *)b.dO; bp.la = b.log_alpha; bp.beta = b.beta;
+    bp.S = (const uint16_t *)(ws + lay.s_off); bp.dS = (const uint16_t *)(ws + lay.ds_off);
+    bp.dq = (bf16 *)b.grad_q; bp.dk = (bf16 *)b.grad_k; bp.dv = (bf16 *)b.grad_v;
+    bp.dla = b.grad_la; bp.dbeta = b.grad_beta;
+    bp.cu = b.cu_seqlens; bp.coff = sp.coff; bp.total = sp.total;
+    bp.H = b.H; bp.T = b.T; bp.dv_ = b.dv; bp.n_seq = n_seq_eff; bp.nc = lay.fw.nc;
+    bp.max_chunks = max_chunks; bp.C = kC;
+
+    if (varlen) hipLaunchKernelGGL((chunk_plan_kernel<SplitParams>), dim3(1), dim3(kPlanThreads), 0, s, sp);
+    const long njobs = (long)b.H * max_chunks;
+    const long slots = 2L * compute_units();
+    const dim3 grid_prep((unsigned)(njobs < slots ? njobs : slots));
+    const dim3 grid_state((unsigned)(((n_seq_eff * b.H + 7) / 8) * 8 * sp.n_tiles));
+    const dim3 grid_jobs((unsigned)njobs);
+#define GDR_BWD(DK, G)                                                                             \
+    do {                                                                                           \
+        hipLaunchKernelGGL((kda_prep_kernel<DK, G, false, false>), grid_prep, dim3(kThreads), 0, s, sp); \
+        hipLaunchKernelGGL((kda_state_kernel<DK, false, kSaveStates>), grid_state, dim3(kThreads), 0, s, sp); \
+        hipLaunchKernelGGL((kda_bwd_reorder_kernel<DK>), grid_jobs, dim3(kThreads), 0, s,             \
+                           (const char *)sp.blk, rp.blk, (int)njobs);                              \
+        hipLaunchKernelGGL((kda_state_kernel<DK, true, kReverse>), grid_state, dim3(kThreads), 0, s, rp); \
+        hipLaunchKernelGGL((kda_bwd_post_kernel<DK, G>), grid_jobs, dim3(kThreads), 0, s, bp);      \
+    } while (0)
+#define GDR_BWD_GATES(DK)                                            \
+    do {                                                             \
+        if (b.gate == kGateChannel) GDR_BWD(DK, kGateChannel);       \
+        else if (b.gate == kGateHead) GDR_BWD(DK, kGateHead);        \
+        else GDR_BWD(DK, kGateNone);                                 \
+    } while (0)
+    if (b.dk == 128) GDR_BWD_GATES(128);
+    else GDR_BWD_GATES(64);
+#undef GDR_BWD_GATES
+#undef GDR_BWD
     return (int)hipGetLastError();
 }
 

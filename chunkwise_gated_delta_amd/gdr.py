@@ -21,8 +21,8 @@ GATE_NONE, GATE_HEAD, GATE_CHANNEL = 0, 1, 2
 GATE_CLIP = 4  # flag: spectral clipping of the gate, alpha <- min(alpha, 1/||I - b a^T||_2)
 STATUS = {0: "GDR_OK", -1: "GDR_ERR_NULL", -2: "GDR_ERR_SHAPE", -3: "GDR_ERR_UNSUPPORTED",
           -4: "GDR_ERR_WORKSPACE", -5: "GDR_ERR_ALIAS", -6: "GDR_ERR_HIP"}
-EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_workspace", "gdr_workspace_error",
-           "gdr_status_string", "gdr_version")
+EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_workspace", "gdr_chunk_bwd", "gdr_chunk_bwd_workspace",
+           "gdr_workspace_error", "gdr_status_string", "gdr_version")
 
 _lib = None
 _lock = threading.Lock()
@@ -49,6 +49,10 @@ def load_library(path: str = LIB_PATH):
         lib.gdr_chunk_fwd.argtypes = [P] * 11 + [I] * 9 + [P, Z, P]
         lib.gdr_chunk_fwd_workspace.restype = Z
         lib.gdr_chunk_fwd_workspace.argtypes = [I] * 10
+        lib.gdr_chunk_bwd.restype = I
+        lib.gdr_chunk_bwd.argtypes = [P] * 15 + [I] * 9 + [P, Z, P]
+        lib.gdr_chunk_bwd_workspace.restype = Z
+        lib.gdr_chunk_bwd_workspace.argtypes = [I] * 9
         lib.gdr_workspace_error.restype = I
         lib.gdr_workspace_error.argtypes = [P, P]
         lib.gdr_status_string.restype = ctypes.c_char_p
@@ -182,3 +186,87 @@ def check_workspace_error(workspace: Optional[torch.Tensor] = None, device=None)
             return 0
     stream = torch.cuda.current_stream(workspace.device).cuda_stream
     return int(lib.gdr_workspace_error(_ptr(workspace), ctypes.c_void_p(stream)))
+
+
+def bwd_workspace_bytes(B, H, T, dk, dv, C=64, n_seq=0, dtype=torch.bfloat16,
+                        gate=GATE_CHANNEL) -> int:
+    """Workspace bytes of chunk_bwd for these arguments; 0 if unsupported."""
+    lib = load_library()
+    return int(lib.gdr_chunk_bwd_workspace(B, H, T, dk, dv, C, n_seq, _dtype_code(dtype), gate))
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+              dO: torch.Tensor, log_alpha: Optional[torch.Tensor] = None,
+              S0: Optional[torch.Tensor] = None, dS_final: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+              want_dS0: bool = True, workspace: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of <dO, O> + <dS_final, S_final> for chunk_fwd in its KDA form (a = b = None).
+
+    Shapes as in chunk_fwd; dO like O, dS_final like S_final (None: zero).
+    Returns a dict with dq, dk, dv (q's dtype), dbeta, dlog_alpha (when a gate is
+    given) and dS0 (fp32, when want_dS0).
+    """
+    lib = load_library()
+    if not q.is_cuda:
+        raise RuntimeError("chunk_bwd runs on the GPU only; move the tensors to a cuda device")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    tensors = dict(q=q, k=k, v=v, beta=beta, dO=dO, log_alpha=log_alpha, S0=S0,
+                   dS_final=dS_final, cu_seqlens=cu_seqlens)
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("k must match q in shape and dtype")
+    if v.shape[:3] != q.shape[:3] or v.dtype != q.dtype:
+        raise ValueError("v must be [B, T, H, dv] in q's dtype")
+    if dO.shape != v.shape or dO.dtype != q.dtype:
+        raise ValueError("dO must match v in shape and dtype")
+    if beta.shape != q.shape[:3] or beta.dtype != torch.float32:
+        raise ValueError("beta must be [B, T, H] float32")
+    if log_alpha is None:
+        gate = GATE_NONE
+    elif log_alpha.dim() == 3 and log_alpha.shape == q.shape[:3]:
+        gate = GATE_HEAD
+    elif log_alpha.shape == q.shape:
+        gate = GATE_CHANNEL
+    else:
+        raise ValueError("log_alpha must be [B, T, H] or [B, T, H, dk]")
+    if log_alpha is not None and log_alpha.dtype != torch.float32:
+        raise ValueError("log_alpha must be float32")
+    n_seq = 0
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise ValueError("cu_seqlens must be int32")
+        n_seq = cu_seqlens.numel() - 1
+    N = n_seq if cu_seqlens is not None else B
+    for name, t in (("S0", S0), ("dS_final", dS_final)):
+        if t is not None and (t.shape != (N, H, dv, dk) or t.dtype != torch.float32):
+            raise ValueError(f"{name} must be [{N}, {H}, {dv}, {dk}] float32")
+    need = int(lib.gdr_chunk_bwd_workspace(B, H, T, dk, dv, chunk_size, n_seq, dt, gate))
+    if need == 0:
+        raise GdrError(-3, f"no backward kernel for dtype={q.dtype} dk={dk} dv={dv} C={chunk_size}")
+    if workspace is None:
+        workspace = _workspace(q.device, need)
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dbeta": torch.empty_like(beta)}
+    if log_alpha is not None:
+        out["dlog_alpha"] = torch.empty_like(log_alpha)
+    if want_dS0:
+        out["dS0"] = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        rc = lib.gdr_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                               _ptr(dO), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]),
+                               _ptr(out["dv"]), _ptr(out.get("dlog_alpha")), _ptr(out["dbeta"]),
+                               _ptr(out.get("dS0")), _ptr(cu_seqlens), n_seq, B, H, T, dk, dv,
+                               chunk_size, dt, gate, _ptr(workspace), workspace.numel(),
+                               ctypes.c_void_p(stream))
+    if rc != 0:
+        raise GdrError(rc, lib.gdr_status_string(rc).decode())
+    return out
