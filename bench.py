@@ -214,6 +214,118 @@ def cpu_model():
     return platform.processor() or "unknown"
 
 
+def backward_counts(P):
+    """(bytes, flops) of one backward call at the algorithmic minimum.
+
+    Bytes per token-head: read q, k, v, dO (es*d each), log alpha (4*dk channel gate,
+    4 head gate), beta 4; write dq, dk, dv (es*d each), dlog alpha (as log alpha),
+    dbeta 4; plus S0, dS_final read and dS0 written once per (sequence, head).
+    FLOP per token-head, the chunk products of the backward notes as full tiles:
+    30*C*d + 10*d^2 + 4*C^2 (the per-chunk gradients: fifteen C x C x d and five
+    C x d x d products, two C x C x C), 6*d^2 (the reverse state pass) and the
+    forward quantities it recomputes, 10*C*d + 6*d^2.
+    """
+    th = P.B * P.T * P.H
+    d, C = P.dk, P.chunk
+    es = 2 if P.dtype.itemsize == 2 else 4
+    gate_bytes = {0: 0, 1: 4, 2: 4 * P.dk}[P.gate]
+    per_th = es * (2 * P.dk + 2 * P.dv) + es * (2 * P.dk + P.dv) + 2 * gate_bytes + 8
+    state = P.n_seq * P.H * P.dv * P.dk * 4 * (2 + (P.S0 is not None))
+    flops_th = 30 * C * d + 10 * d * d + 4 * C * C + 6 * d * d + 10 * C * d + 6 * d * d
+    return th * per_th + state, th * flops_th
+
+
+def bench_backward(args):
+    """Time gdr_chunk_bwd on a workload; one JSON line."""
+    import numpy as np
+    import torch
+
+    from chunkwise_gated_delta_amd import gdr, inputs
+
+    P = inputs.make_problem(args.workload)
+    dO, dSf = inputs.make_cotangents(P, seed=100)
+    dev = torch.device("cuda", 0)
+    to = lambda t: None if t is None else t.to(dev)
+    q, k, v, beta, la = to(P.q), to(P.k), to(P.v), to(P.beta), to(P.log_alpha)
+    S0, cu, dOd, dSd = to(P.S0), to(P.cu_seqlens), to(dO), to(dSf)
+    call = lambda: gdr.chunk_bwd(q, k, v, beta, dOd, log_alpha=la, S0=S0, dS_final=dSd,
+                                 cu_seqlens=cu, chunk_size=P.chunk)
+    for _ in range(args.warmup):
+        g = call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    ev0, ev1 = ev(), ev()
+    per = []
+    ev0.record(stream)
+    for _ in range(args.steps):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        g = call()
+        e1.record(stream)
+        per.append((e0, e1))
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    launch_ms = sorted(a.elapsed_time(b) for a, b in per)
+    call_ms = float(np.mean(launch_ms))
+    alg_bytes, alg_flops = backward_counts(P)
+    tokens = P.B * P.T
+    gbs = alg_bytes / (call_ms * 1e-3) / 1e9
+    tflops = alg_flops / (call_ms * 1e-3) / 1e12
+    result = {
+        "metric": f"tokens/s, {args.workload} chunk bwd (all input gradients), 1xMI355X",
+        "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload} backward: B={P.B} H={P.H} T={P.T} dk={P.dk} "
+                               f"dv={P.dv} C={P.chunk} n_seq={P.n_seq}, seeded dO and dS_final"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gdr_chunk_bwd call (all launches)", "call_ms_mean": call_ms,
+                     "alg_bytes_per_launch": alg_bytes},
+        "mfma": {"alg_flops_per_launch": alg_flops, "achieved_tflops": tflops,
+                 "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "frac": tflops / BF16_MFMA_PEAK_TFLOPS},
+    }
+    if not args.no_cpu:
+        import oracle
+
+        f64 = lambda t: None if t is None else t.to(torch.float64).numpy()
+        chains = [(0, 0), (min(1, P.n_seq - 1), min(5, P.H - 1))]
+        cu_np = None if P.cu_seqlens is None else P.cu_seqlens.numpy()
+        t = time.perf_counter()
+        ref = oracle.recurrence_bwd(f64(P.q), f64(P.k), f64(P.v), f64(P.beta), f64(dO),
+                                    log_alpha=f64(P.log_alpha), S0=f64(P.S0), dS_final=f64(dSf),
+                                    cu_seqlens=cu_np, chains=chains, n_threads=2)
+        dt = time.perf_counter() - t
+        if cu_np is None:
+            chain_tokens = len(chains) * P.T
+        else:
+            lens = np.diff(cu_np)
+            chain_tokens = int(sum(lens[n] for n, _ in chains))
+        # a token carries all H heads: chain tokens / H of them per second, scaled to the
+        # two threads that ran the two chains
+        result["cpu_baseline"] = {
+            "value": chain_tokens / dt / P.H, "unit": "tokens/s", "cores": 2, "kind": "oracle",
+            "sample": f"2 (sequence, head) chains ({chain_tokens} token-heads) of the workload, "
+                      f"fp64 reverse pass with checkpoint replay, {dt:.2f} s on 2 threads"}
+        errs = {}
+        for key, val in g.items():
+            gk = val.to(torch.float64).cpu().numpy()
+            if key == "dS0":
+                a = np.concatenate([gk[n, h].ravel() for n, h in chains])
+                b = np.concatenate([ref[key][n, h].ravel() for n, h in chains])
+            elif P.cu_seqlens is None:
+                a = np.concatenate([gk[n, :, h].ravel() for n, h in chains])
+                b = np.concatenate([ref[key][n, :, h].ravel() for n, h in chains])
+            else:
+                a = np.concatenate([gk[0, cu_np[n]:cu_np[n + 1], h].ravel() for n, h in chains])
+                b = np.concatenate([ref[key][0, cu_np[n]:cu_np[n + 1], h].ravel() for n, h in chains])
+            errs[key + "_rel_err"] = float(np.max(np.abs(a - b)) / np.max(np.abs(b)))
+        result["parity"] = dict(errs, tol=inputs.TOLERANCE[P.dtype], chains=chains)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +339,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the GEMM / copy context measurements")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (gdr_chunk_bwd) on the workload instead")
     ap.add_argument("--copy-cal", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (calibrates the HBM "
                          "traffic counters: FETCH_SIZE/WRITE_SIZE per byte actually moved)")
@@ -247,6 +361,10 @@ def main():
               "chain is independent, so N GPUs would each run this path on H/N heads.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.backward:
+        bench_backward(args)
+        return
 
     import numpy as np
     import torch

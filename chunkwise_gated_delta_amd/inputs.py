@@ -184,6 +184,16 @@ def make_problem(kind: str, *, seed: Optional[int] = None, B=None, H=None, T=Non
         clip=bool(spec.get("clip", False)))
 
 
+def make_cotangents(P: Problem, seed: int, ds_scale: float = 0.1):
+    """Seeded dO (P's dtype, shape of O) and dS_final (fp32, shape of S_final) for the
+    backward pass: dO ~ N(0, 1), dS_final ~ ds_scale N(0, 1), drawn in that order."""
+    rng = np.random.default_rng(seed)
+    dO = _cast(rng.standard_normal((P.B, P.T, P.H, P.dv), dtype=np.float32), P.dtype)
+    dSf = torch.from_numpy(np.float32(ds_scale) *
+                           rng.standard_normal((P.n_seq, P.H, P.dv, P.dk), dtype=np.float32))
+    return dO, dSf
+
+
 WORKLOADS = {
     "deltanet_f32": dict(seed=1, B=1, H=2, T=256, dk=64, dv=64, dtype=torch.float32,
                          gate=GATE_NONE),
