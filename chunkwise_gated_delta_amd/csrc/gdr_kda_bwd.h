@@ -110,17 +110,39 @@ struct BwdParams {
 // One 16x16 output tile of A B on the 16x16x32 MFMA: lane l ends with
 // D[m0 + l%16][n0 + 4(l/16) + e] in register e.  A is read from a row-major [m][k]
 // array (AT = false) or from one stored [k][m] (AT = true); B from [k][n] (BT =
-// false) or [n][k] (BT = true).  The contraction runs over [k0, k1) in steps of 32.
-template <bool AT, bool BT>
+// false) or [n][k] (BT = true).  The contraction runs over [k0, k1) (at most KMAX
+// long) in steps of 32; every step's operands are read before the first product so
+// that the LDS latency is paid once per tile.
+template <bool AT, bool BT, int KMAX>
 __device__ __forceinline__ f32x4 mma_tile(const uint16_t *A, int lda, const uint16_t *B, int ldb,
                                           int m0, int n0, int k0, int k1, f32x4 acc, int lane) {
+    constexpr int NS = KMAX / 32;
     const int r = lane & 15, g = lane >> 4;
-    for (int k = k0; k < k1; k += 32) {
-        const bf16x8 fa = AT ? frag_tr(A, k, lda, m0, lane) : frag(A, m0 + r, lda, k + 8 * g);
-        const bf16x8 fb = BT ? frag(B, n0 + r, ldb, k + 8 * g) : frag_tr(B, k, ldb, n0, lane);
-        acc = mfma(fb, fa, acc);
+    bf16x8 fa[NS], fb[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        const int k = k0 + 32 * st;
+        if (k < k1) {
+            fa[st] = AT ? frag_tr(A, k, lda, m0, lane) : frag(A, m0 + r, lda, k + 8 * g);
+            fb[st] = BT ? frag(B, n0 + r, ldb, k + 8 * g) : frag_tr(B, k, ldb, n0, lane);
+        }
     }
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+        if (k0 + 32 * st < k1) acc = mfma(fb[st], fa[st], acc);
     return acc;
+}
+
+// Operand fragments of v_mfma_f32_16x16x16_bf16 (lane l: index l%16, contraction
+// 4(l/16)+0..3): from a row-major [m][k] array (8-byte read) or, gathered with one
+// LDS transpose read, from an array whose rows run along the contraction.
+__device__ __forceinline__ bf16x4 frag4(const uint16_t *base, int row, int stride, int col) {
+    return *(const bf16x4 *)(base + row * stride + col);
+}
+__device__ __forceinline__ bf16x4 frag4_tr(const uint16_t *base, int k0, int stride, int col0, int lane) {
+    const int G = lane >> 4, q = lane & 15;
+    const uint16_t *ptr = base + (k0 + 4 * G + (q >> 2)) * stride + col0 + 4 * (q & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)ptr);
 }
 
 template <int DK>
@@ -144,8 +166,9 @@ struct BwdSmem {
     static constexpr int tEnd = tdVn + kC * VS * 2;
     //   after the dv loop: dA, dXm (Y first), Z at tSp..; the inverse's KK fp32 [64][68] at 0
     static constexpr int tdA = 0, tY = CC, tZ = 2 * CC;
-    static constexpr int Tbytes = (tEnd > 3 * CC ? tEnd : 3 * CC) > kC * 68 * 4
-                                      ? (tEnd > 3 * CC ? tEnd : 3 * CC) : kC * 68 * 4;
+    //   the inverse: KK fp32 [64][68], then L and the middle factor bf16 [64][CS] each
+    static constexpr int tInv = kC * 68 * 4 + 2 * CC;
+    static constexpr int Tbytes = tEnd > 3 * CC ? (tEnd > tInv ? tEnd : tInv) : (3 * CC > tInv ? 3 * CC : tInv);
     static constexpr int oBeta = oT + Tbytes;   // fp32 [64]
     static constexpr int oGam = oBeta + kC * 4; // fp32 [DK] gamma_C
     static constexpr int oGp = oGam + DK * 4;   // fp32 [8][DK] gate partial sums
@@ -192,27 +215,67 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     const size_t sbase = (size_t)(job / H) * H + h;  // (chunk, head) index of the state buffers
     const int R0 = 16 * wave;                        // this wave's 16 rows of every row-block output
 
+    // Global loads of one dv tile (S_p and dS_n rows j0..j0+31, value and dO tiles),
+    // issued a tile ahead so that their latency overlaps the previous tile's products.
+    constexpr int kSPT = 32 * DK / 8 / kThreads;  // 16-byte pieces of a state tile per thread
+    struct Tile {
+        uint4 s[kSPT], d[kSPT], v, o;
+    } pf;
+    auto issue = [&](int j0) {
+        const uint16_t *ps = p.S + (sbase * DV + j0) * DK;
+        const uint16_t *pd = p.dS + (sbase * DV + j0) * DK;
+#pragma unroll
+        for (int i = 0; i < kSPT; ++i) {
+            const int idx = tid + kThreads * i, r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+            pf.s[i] = *(const uint4 *)(ps + (size_t)r * DK + c8);
+            pf.d[i] = *(const uint4 *)(pd + (size_t)r * DK + c8);
+        }
+        const int r = tid >> 2, c8 = 8 * (tid & 3);
+        const size_t off = ((size_t)(tok0 + (r < m ? r : 0)) * H + h) * DV + j0 + c8;
+        pf.v = *(const uint4 *)(p.v + off);  // rows past the end are zeroed when stored
+        pf.o = *(const uint4 *)(p.dO + off);
+    };
+    issue(0);
+
     // ---- gate: g for rows 8rg + i, channels c0 + e (natural log, inclusive prefix) ----
     const int rg = tid >> 5, c0 = CPT * (tid & 31);
     auto gate = [&](float (&g)[8][CPT]) {
+        // all eight rows' log alpha are loaded before the sums use them
+        float la[8][CPT];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * rg + i;
+            const size_t th = (size_t)(tok0 + (r < m ? r : 0)) * H + h;
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) la[i][e] = 0.f;
+            if (GATE == kGateChannel) {
+                if constexpr (CPT == 4) {
+                    const float4 x = *(const float4 *)(p.la + th * DK + c0);
+                    la[i][0] = x.x; la[i][CPT > 1 ? 1 : 0] = x.y;
+                    la[i][CPT > 2 ? 2 : 0] = x.z; la[i][CPT > 3 ? 3 : 0] = x.w;
+                } else {
+                    const float2 x = *(const float2 *)(p.la + th * DK + c0);
+                    la[i][0] = x.x; la[i][CPT > 1 ? 1 : 0] = x.y;
+                }
+            } else if (GATE == kGateHead) {
+                const float x = p.la[th];
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) la[i][e] = x;
+            }
+            if (r >= m)
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) la[i][e] = 0.f;
+        }
         float run[CPT];
 #pragma unroll
         for (int e = 0; e < CPT; ++e) run[e] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 8 * rg + i;
-            const size_t th = (size_t)(tok0 + r) * H + h;
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int e = 0; e < CPT; ++e) {
-                float x = 0.f;
-                if (r < m) {
-                    if (GATE == kGateChannel) x = p.la[th * DK + c0 + e];
-                    else if (GATE == kGateHead) x = p.la[th];
-                }
-                run[e] += x;
+                run[e] += la[i][e];
                 g[i][e] = run[e];
             }
-        }
 #pragma unroll
         for (int e = 0; e < CPT; ++e) sGp[rg * DK + c0 + e] = run[e];
         lds_barrier();
@@ -227,27 +290,52 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     };
 
     // ---- stage 0: scaled operands ---------------------------------------------------
+    float g[8][CPT];  // kept for the chain rule at the end
     {
-        float g[8][CPT];
         gate(g);
         if (tid < kC) sBeta[tid] = tid < m ? p.beta[(size_t)(tok0 + tid) * H + h] : 0.f;
+        constexpr int WPR = CPT / 2;  // bf16 words per row and thread
+        uint32_t qw[8][WPR], kw[8][WPR];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * rg + i;
-            const size_t th = (size_t)(tok0 + r) * H + h;
-            float qv[CPT], kv[CPT];
-#pragma unroll
-            for (int e = 0; e < CPT; ++e) {
-                qv[e] = r < m ? __bfloat162float(p.q[th * DK + c0 + e]) : 0.f;
-                kv[e] = r < m ? __bfloat162float(p.k[th * DK + c0 + e]) : 0.f;
+            const size_t th = (size_t)(tok0 + (r < m ? r : 0)) * H + h;
+            if constexpr (WPR == 2) {
+                const uint2 a = *(const uint2 *)(p.q + th * DK + c0), b = *(const uint2 *)(p.k + th * DK + c0);
+                qw[i][0] = a.x; qw[i][WPR - 1] = a.y; kw[i][0] = b.x; kw[i][WPR - 1] = b.y;
+            } else {
+                qw[i][0] = *(const uint32_t *)(p.q + th * DK + c0);
+                kw[i][0] = *(const uint32_t *)(p.k + th * DK + c0);
             }
+            if (r >= m)
 #pragma unroll
-            for (int e = 0; e < CPT; ++e) {
-                const float G = expf(g[i][e]), iG = expf(-g[i][e]);
-                sQl[r * KS + c0 + e] = __builtin_bit_cast(uint16_t, (__bf16)(qv[e] * G));
-                sKl[r * KS + c0 + e] = __builtin_bit_cast(uint16_t, (__bf16)(kv[e] * G));
-                sKr[r * KS + c0 + e] = __builtin_bit_cast(uint16_t, (__bf16)(kv[e] * iG));
-                if (r == kC - 1) sGam[c0 + e] = G;
+                for (int w = 0; w < WPR; ++w) qw[i][w] = kw[i][w] = 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * rg + i;
+            uint32_t oq[WPR], ol[WPR], orr[WPR];
+#pragma unroll
+            for (int w = 0; w < WPR; ++w) {
+                const float G0 = exp2_fast(g[i][2 * w] * kLog2e), G1 = exp2_fast(g[i][2 * w + 1] * kLog2e);
+                const float q0 = bf16_lo(qw[i][w]), q1 = bf16_hi(qw[i][w]);
+                const float k0 = bf16_lo(kw[i][w]), k1 = bf16_hi(kw[i][w]);
+                oq[w] = pack_bf16x2(q0 * G0, q1 * G1);
+                ol[w] = pack_bf16x2(k0 * G0, k1 * G1);
+                orr[w] = pack_bf16x2(k0 * exp2_fast(-g[i][2 * w] * kLog2e), k1 * exp2_fast(-g[i][2 * w + 1] * kLog2e));
+                if (r == kC - 1) {
+                    sGam[c0 + 2 * w] = G0;
+                    sGam[c0 + 2 * w + 1] = G1;
+                }
+            }
+            if constexpr (WPR == 2) {
+                *(uint2 *)(sQl + r * KS + c0) = make_uint2(oq[0], oq[WPR - 1]);
+                *(uint2 *)(sKl + r * KS + c0) = make_uint2(ol[0], ol[WPR - 1]);
+                *(uint2 *)(sKr + r * KS + c0) = make_uint2(orr[0], orr[WPR - 1]);
+            } else {
+                *(uint32_t *)(sQl + r * KS + c0) = oq[0];
+                *(uint32_t *)(sKl + r * KS + c0) = ol[0];
+                *(uint32_t *)(sKr + r * KS + c0) = orr[0];
             }
         }
         for (int i = tid; i < kC; i += kThreads) sDb[i] = 0.f;
@@ -257,13 +345,14 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
 
     // ---- stage 1: KK (fp32, for the inverse) and A_qk --------------------------------
     float *sKK = (float *)sT;  // [64][68]
+    for (int idx = tid; idx < kC * CS / 8; idx += kThreads) ((uint4 *)sA)[idx] = make_uint4(0u, 0u, 0u, 0u);
     {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         for (int tj = 0; tj < 4; ++tj) {
             f32x4 kk = z, aq = z;
             if (tj <= wave) {
-                kk = mma_tile<false, true>(sKl, KS, sKr, KS, R0, 16 * tj, 0, DK, z, lane);
-                aq = mma_tile<false, true>(sQl, KS, sKr, KS, R0, 16 * tj, 0, DK, z, lane);
+                kk = mma_tile<false, true, DK>(sKl, KS, sKr, KS, R0, 16 * tj, 0, DK, z, lane);
+                aq = mma_tile<false, true, DK>(sQl, KS, sKr, KS, R0, 16 * tj, 0, DK, z, lane);
             }
             const int row = R0 + r16;
 #pragma unroll
@@ -276,25 +365,66 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     }
     lds_barrier();
 
-    // ---- stage 2: At = (I + Diag(beta) KK)^-1 by forward substitution, lane j = column j
-    if (wave == 0) {
-        const int j = lane;
-        float x[kC];
+    // ---- stage 2: At = (I + L)^-1, L = Diag(beta) KK, blocked ----------------------------
+    // (a) wave w inverts the diagonal 16x16 block w by forward substitution (fp32; four
+    //     lanes per column, lane part s keeps x_k for k = s mod 4, quad sums complete the
+    //     rows; x_k = 0 for k < j and KK is zero on and above the diagonal: no masks);
+    //     every thread also writes L in bf16 for the off-diagonal products;
+    // (b) [A 0; C B]^-1 = [A^-1 0; -B^-1 C A^-1 B^-1] for the 32x32 blocks (16x16x16
+    //     MFMA, waves 0 and 2), then (c) for the whole 64x64 (16x16x32 MFMA, all waves).
+    uint16_t *sL = (uint16_t *)(sT + kC * 68 * 4);  // bf16 [64][CS]: L, strictly lower
+    uint16_t *sTm = sL + kC * CS;                     // bf16 [64][CS]: the products' middle factor
+    {
+        const int jl = lane >> 2, s = lane & 3, j = R0 + jl;
+        float xs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < kC; ++i) {
-            float acc = i == j ? 1.f : 0.f;
-            const float bi = sBeta[i];
-            float s = 0.f;
+        for (int i = 0; i < 16; ++i) {
+            float acc = 0.f;
 #pragma unroll
-            for (int k2 = 0; k2 < i; ++k2) s += sKK[i * 68 + k2] * x[k2];
-            x[i] = acc - bi * s;
+            for (int u = 0; u < (i + 3) / 4; ++u) acc += sKK[(R0 + i) * 68 + R0 + 4 * u + s] * xs[u];
+            acc += dpp<kDppXor1>(acc);
+            acc += dpp<kDppXor2>(acc);
+            const float xi = (i == jl ? 1.f : 0.f) - sBeta[R0 + i] * acc;
+            if (s == (i & 3)) xs[i >> 2] = xi;
         }
-        const float bj = sBeta[j];
 #pragma unroll
-        for (int i = 0; i < kC; ++i) {
-            sA[i * CS + j] = __builtin_bit_cast(uint16_t, (__bf16)x[i]);
-            sAb[i * CS + j] = __builtin_bit_cast(uint16_t, (__bf16)(x[i] * bj));
+        for (int u = 0; u < 4; ++u) sA[(R0 + 4 * u + s) * CS + j] = __builtin_bit_cast(uint16_t, (__bf16)xs[u]);
+        for (int idx = tid; idx < kC * kC; idx += kThreads) {
+            const int i = idx >> 6, k2 = idx & 63;
+            sL[i * CS + k2] = __builtin_bit_cast(uint16_t, (__bf16)(sBeta[i] * sKK[i * 68 + k2]));
         }
+    }
+    lds_barrier();
+    if (wave == 0 || wave == 2) {
+        // blocks rows 16..31 x cols 0..15 (wave 0) and rows 48..63 x cols 32..47 (wave 2)
+        const int o = wave == 0 ? 0 : 32;
+        const int r = lane & 15, g = lane >> 4;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        // T = L[o+16..][o..o+15] A[o..][o..]
+        f32x4 t = mfma16(frag4_tr(sA + o, o, CS, 0, lane), frag4(sL + o, o + 16 + r, CS, 4 * g), z);
+        store4(sTm + (o + 16 + r) * CS + o + 4 * g, t[0], t[1], t[2], t[3]);
+        asm volatile("" ::: "memory");
+        // C-block of the inverse = -A[o+16..][o+16..] T  (same wave: the LDS writes above
+        // are seen by its reads below)
+        t = mfma16(frag4_tr(sTm + o, o + 16, CS, 0, lane), frag4(sA + o + 16, o + 16 + r, CS, 4 * g), z);
+        store4(sA + (o + 16 + r) * CS + o + 4 * g, -t[0], -t[1], -t[2], -t[3]);
+    }
+    lds_barrier();
+    {
+        // rows 32..63 x cols 0..31: T = L[32..][0..31] A[0..31][0..31], then -A[32..][32..] T
+        const int m0 = 32 + 16 * (wave >> 1), n0 = 16 * (wave & 1);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 t = mma_tile<false, false, kC>(sL, CS, sA, CS, m0, n0, 0, 32, z, lane);
+        store4(sTm + (m0 + r16) * CS + n0 + 4 * g4, t[0], t[1], t[2], t[3]);
+        lds_barrier();
+        const f32x4 c = mma_tile<false, false, kC>(sA + 32, CS, sTm + 32 * CS, CS, m0, n0, 0, 32, z, lane);
+        lds_barrier();  // every wave has read its A and T operands
+        store4(sA + (m0 + r16) * CS + n0 + 4 * g4, -c[0], -c[1], -c[2], -c[3]);
+    }
+    lds_barrier();
+    for (int idx = tid; idx < kC * kC; idx += kThreads) {
+        const int i = idx >> 6, j = idx & 63;
+        sAb[i * CS + j] = __builtin_bit_cast(uint16_t, (__bf16)(bf16_lo(sA[i * CS + j]) * sBeta[j]));
     }
     lds_barrier();
 
@@ -303,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         const int k1 = R0 + 16 <= 32 ? 32 : 64;  // Ab is lower triangular
         for (int tn = 0; tn < NT; ++tn) {
-            const f32x4 w = mma_tile<false, false>(sAb, CS, sKl, KS, R0, 16 * tn, 0, k1, z, lane);
+            const f32x4 w = mma_tile<false, false, kC>(sAb, CS, sKl, KS, R0, 16 * tn, 0, k1, z, lane);
             store4(sW + (R0 + r16) * KS + 16 * tn + 4 * g4, w[0], w[1], w[2], w[3]);
         }
     }
@@ -318,35 +448,36 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
 #pragma unroll
         for (int t = 0; t < 4; ++t) aA[t] = aY[t] = z;
     }
-    float gpart = 0.f;  // sum over dv of S_p * dSg, column tid % DK
+    // sum over dv of S_p * dSg for this thread's 8 columns 8 (tid % (DK / 8)) + 0..7 (the
+    // same columns for every piece it stores)
+    float gpart[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const int lo_k = R0 >= 32 ? 32 : 0;  // At^T / A_qk^T rows R0..: contraction over j >= R0
     for (int j0 = 0; j0 < DV; j0 += 32) {
-        // loads: state tiles (dv rows j0..j0+31), value and dO tiles (64 x 32)
+        // the tile's loads were issued one tile earlier (the first at the kernel's start);
+        // into LDS, dS scaled by gamma_C per column
         {
-            const uint16_t *ps = p.S + (sbase * DV + j0) * DK;
-            const uint16_t *pd = p.dS + (sbase * DV + j0) * DK;
 #pragma unroll
-            for (int i = 0; i < 32 * DK / 8 / kThreads; ++i) {
+            for (int i = 0; i < kSPT; ++i) {
                 const int idx = tid + kThreads * i, r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
-                *(uint4 *)(sSp + r * KS + c8) = *(const uint4 *)(ps + (size_t)r * DK + c8);
-                const uint4 dw = *(const uint4 *)(pd + (size_t)r * DK + c8);
-                const uint32_t w4[4] = {dw.x, dw.y, dw.z, dw.w};
+                *(uint4 *)(sSp + r * KS + c8) = pf.s[i];
+                const uint32_t w4[4] = {pf.d[i].x, pf.d[i].y, pf.d[i].z, pf.d[i].w};
+                const uint32_t s4[4] = {pf.s[i].x, pf.s[i].y, pf.s[i].z, pf.s[i].w};
                 uint32_t o4[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    o4[e] = pack_bf16x2(bf16_lo(w4[e]) * sGam[c8 + 2 * e], bf16_hi(w4[e]) * sGam[c8 + 2 * e + 1]);
+                for (int e = 0; e < 4; ++e) {
+                    const float d0 = bf16_lo(w4[e]) * sGam[c8 + 2 * e], d1 = bf16_hi(w4[e]) * sGam[c8 + 2 * e + 1];
+                    o4[e] = pack_bf16x2(d0, d1);
+                    gpart[2 * e] += bf16_lo(s4[e]) * d0;
+                    gpart[2 * e + 1] += bf16_hi(s4[e]) * d1;
+                }
                 *(uint4 *)(sdS + r * KS + c8) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
             }
             const int r = tid >> 2, c8 = 8 * (tid & 3);
-            uint4 vv = make_uint4(0u, 0u, 0u, 0u), dd = vv;
-            if (r < m) {
-                const size_t off = ((size_t)(tok0 + r) * H + h) * DV + j0 + c8;
-                vv = *(const uint4 *)(p.v + off);
-                dd = *(const uint4 *)(p.dO + off);
-            }
-            *(uint4 *)(sV + r * VS + c8) = vv;
-            *(uint4 *)(sdO + r * VS + c8) = dd;
+            const uint32_t keep = 0u - (uint32_t)(r < m);
+            *(uint4 *)(sV + r * VS + c8) = make_uint4(pf.v.x & keep, pf.v.y & keep, pf.v.z & keep, pf.v.w & keep);
+            *(uint4 *)(sdO + r * VS + c8) = make_uint4(pf.o.x & keep, pf.o.y & keep, pf.o.z & keep, pf.o.w & keep);
         }
+        if (j0 + 32 < DV) issue(j0 + 32);
         lds_barrier();
         // V_new = Ab V - W S_p^T and dV_new = K-> dSg^T + A_qk^T dO, rows R0..R0+15
         {
@@ -354,10 +485,10 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             const int k1 = R0 + 16 <= 32 ? 32 : 64;
 #pragma unroll
             for (int tn = 0; tn < 2; ++tn) {
-                f32x4 u = mma_tile<false, false>(sAb, CS, sV, VS, R0, 16 * tn, 0, k1, z, lane);
-                const f32x4 ws = mma_tile<false, true>(sW, KS, sSp, KS, R0, 16 * tn, 0, DK, z, lane);
-                f32x4 dv = mma_tile<false, true>(sKr, KS, sdS, KS, R0, 16 * tn, 0, DK, z, lane);
-                dv = mma_tile<true, false>(sAqk, CS, sdO, VS, R0, 16 * tn, lo_k, kC, dv, lane);
+                f32x4 u = mma_tile<false, false, kC>(sAb, CS, sV, VS, R0, 16 * tn, 0, k1, z, lane);
+                const f32x4 ws = mma_tile<false, true, DK>(sW, KS, sSp, KS, R0, 16 * tn, 0, DK, z, lane);
+                f32x4 dv = mma_tile<false, true, DK>(sKr, KS, sdS, KS, R0, 16 * tn, 0, DK, z, lane);
+                dv = mma_tile<true, false, kC>(sAqk, CS, sdO, VS, R0, 16 * tn, lo_k, kC, dv, lane);
                 store4(sVn + (R0 + r16) * VS + 16 * tn + 4 * g4, u[0] - ws[0], u[1] - ws[1],
                        u[2] - ws[2], u[3] - ws[3]);
                 store4(sdVn + (R0 + r16) * VS + 16 * tn + 4 * g4, dv[0], dv[1], dv[2], dv[3]);
@@ -371,7 +502,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             // dV = Diag(beta) At^T dV_new
 #pragma unroll
             for (int tn = 0; tn < 2; ++tn) {
-                const f32x4 d = mma_tile<true, false>(sA, CS, sdVn, VS, R0, 16 * tn, lo_k, kC, z, lane);
+                const f32x4 d = mma_tile<true, false, kC>(sA, CS, sdVn, VS, R0, 16 * tn, lo_k, kC, z, lane);
                 if (row < m) {
                     uint2 o;
                     o.x = pack_bf16x2(br * d[0], br * d[1]);
@@ -397,13 +528,6 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
                 if (tj <= wave) aA[tj] = mfma(frag(sVn, 16 * tj + r16, VS, 8 * g4), fdo, aA[tj]);
                 aY[tj] = mfma(frag(sV, 16 * tj + r16, VS, 8 * g4), fdv, aY[tj]);
             }
-            // sum_i S_p[i][j] dSg[i][j] over the tile's 32 rows
-            {
-                const int col = tid % DK, half = tid / DK;  // DK = 128: 2 halves; DK = 64: 4
-                constexpr int NH = kThreads / DK;
-                for (int r = half; r < 32; r += NH)
-                    gpart += bf16_lo(sSp[r * KS + col]) * bf16_lo(sdS[r * KS + col]);
-            }
         }
         lds_barrier();  // the tile buffers are reloaded
     }
@@ -424,14 +548,21 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             for (int e = 0; e < 4; ++e) d[e] = (16 * tj + 4 * g4 + e <= row) ? aA[tj][e] : 0.f;
             store4(sdA + row * CS + 16 * tj + 4 * g4, d[0], d[1], d[2], d[3]);
         }
-        atomicAdd(&sDg[tid % DK], gpart);
+        // lanes l, l + DK/8, ... of a wave hold the same columns: sum them first
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = gpart[e];
+#pragma unroll
+            for (int off = DK / 8; off < 64; off <<= 1) x += __shfl_xor(x, off);
+            if (lane < DK / 8) atomicAdd(&sDg[8 * lane + e], x);
+        }
     }
     lds_barrier();
     {
         const int row = R0 + r16;
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {
-            aY[tj] = mma_tile<false, true>(sdW, KS, sKl, KS, R0, 16 * tj, 0, DK, aY[tj], lane);
+            aY[tj] = mma_tile<false, true, DK>(sdW, KS, sKl, KS, R0, 16 * tj, 0, DK, aY[tj], lane);
             store4(sY + row * CS + 16 * tj + 4 * g4, aY[tj][0], aY[tj][1], aY[tj][2], aY[tj][3]);
         }
     }
@@ -441,7 +572,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         const int row = R0 + r16;
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {
-            const f32x4 zt = mma_tile<true, false>(sA, CS, sY, CS, R0, 16 * tj, lo_k, kC, z, lane);
+            const f32x4 zt = mma_tile<true, false, kC>(sA, CS, sY, CS, R0, 16 * tj, lo_k, kC, z, lane);
             store4(sZ + row * CS + 16 * tj + 4 * g4, zt[0], zt[1], zt[2], zt[3]);
             if (tj == wave && (r16 >> 2) == g4) sDb[row] = zt[r16 & 3];  // diag(Z)
         }
@@ -456,8 +587,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         for (int tj = 0; tj < 4; ++tj) {
             f32x4 dx = z;
             if (tj <= wave) {
-                dx = mma_tile<false, true>(sZ, CS, sAb, CS, R0, 16 * tj, 0, kC, z, lane);
-                const f32x4 kk = mma_tile<false, true>(sKl, KS, sKr, KS, R0, 16 * tj, 0, DK, z, lane);
+                dx = mma_tile<false, true, kC>(sZ, CS, sAb, CS, R0, 16 * tj, 0, kC, z, lane);
+                const f32x4 kk = mma_tile<false, true, DK>(sKl, KS, sKr, KS, R0, 16 * tj, 0, DK, z, lane);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int col = 16 * tj + 4 * g4 + e;
@@ -484,13 +615,13 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         float dgp[NT][4];
 #pragma unroll
         for (int tn = 0; tn < NT; ++tn) {
-            f32x4 a = mma_tile<true, false>(sA, CS, sdW, KS, R0, 16 * tn, lo_k, kC, z, lane);
+            f32x4 a = mma_tile<true, false, kC>(sA, CS, sdW, KS, R0, 16 * tn, lo_k, kC, z, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) a[e] *= br;
-            gKl[tn] = mma_tile<false, false>(sdXm, CS, sKr, KS, R0, 16 * tn, 0, kC, a, lane);
-            f32x4 b = mma_tile<true, false>(sdA, CS, sQl, KS, R0, 16 * tn, lo_k, kC, aKg[tn], lane);
-            gKr[tn] = mma_tile<true, false>(sdXm, CS, sKl, KS, R0, 16 * tn, lo_k, kC, b, lane);
-            gQl[tn] = mma_tile<false, false>(sdA, CS, sKr, KS, R0, 16 * tn, 0, kC, aQ[tn], lane);
+            gKl[tn] = mma_tile<false, false, kC>(sdXm, CS, sKr, KS, R0, 16 * tn, 0, kC, a, lane);
+            f32x4 b = mma_tile<true, false, kC>(sdA, CS, sQl, KS, R0, 16 * tn, lo_k, kC, aKg[tn], lane);
+            gKr[tn] = mma_tile<true, false, kC>(sdXm, CS, sKl, KS, R0, 16 * tn, lo_k, kC, b, lane);
+            gQl[tn] = mma_tile<false, false, kC>(sdA, CS, sKr, KS, R0, 16 * tn, 0, kC, aQ[tn], lane);
             // last-row term: sum over rows of K-> dKg, per column
             const uint2 kr = *(const uint2 *)(sKr + row * KS + 16 * tn + 4 * g4);
             dgp[tn][0] = bf16_lo(kr.x) * aKg[tn][0];
@@ -511,34 +642,34 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     // ---- stage 7: chain rule through Gamma, suffix sums ------------------------------
     float *sGm = (float *)(smem + L::oQl);  // fp32 [64][DK] Gamma
     float *sDl = (float *)sT;               // fp32 [64][DK] dg
-    {
-        float g[8][CPT];
-        gate(g);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int e = 0; e < CPT; ++e) sGm[(8 * rg + i) * DK + c0 + e] = g[i][e];
-    }
+        for (int e = 0; e < CPT; ++e) sGm[(8 * rg + i) * DK + c0 + e] = g[i][e];
     lds_barrier();
     {
         const int row = R0 + r16;
         const bool ok = row < m;
         const size_t th = (size_t)(tok0 + (ok ? row : 0)) * H + h;
+        uint2 qw[NT], kw[NT];  // all loads first
+#pragma unroll
+        for (int tn = 0; tn < NT; ++tn) {
+            qw[tn] = *(const uint2 *)(p.q + th * DK + 16 * tn + 4 * g4);
+            kw[tn] = *(const uint2 *)(p.k + th * DK + 16 * tn + 4 * g4);
+        }
 #pragma unroll
         for (int tn = 0; tn < NT; ++tn) {
             const int col = 16 * tn + 4 * g4;
-            float qv[4] = {0.f, 0.f, 0.f, 0.f}, kv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (ok) {
-                const uint2 qw = *(const uint2 *)(p.q + th * DK + col);
-                const uint2 kw = *(const uint2 *)(p.k + th * DK + col);
-                qv[0] = bf16_lo(qw.x); qv[1] = bf16_hi(qw.x); qv[2] = bf16_lo(qw.y); qv[3] = bf16_hi(qw.y);
-                kv[0] = bf16_lo(kw.x); kv[1] = bf16_hi(kw.x); kv[2] = bf16_lo(kw.y); kv[3] = bf16_hi(kw.y);
-            }
+            const uint32_t keep = ok ? 0xffffffffu : 0u;
+            const float qv[4] = {bf16_lo(qw[tn].x & keep), bf16_hi(qw[tn].x & keep),
+                                 bf16_lo(qw[tn].y & keep), bf16_hi(qw[tn].y & keep)};
+            const float kv[4] = {bf16_lo(kw[tn].x & keep), bf16_hi(kw[tn].x & keep),
+                                 bf16_lo(kw[tn].y & keep), bf16_hi(kw[tn].y & keep)};
             float dq4[4], dk4[4], dl4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float gv = sGm[row * DK + col + e];
-                const float G = expf(gv), iG = expf(-gv);
+                const float gv = sGm[row * DK + col + e] * kLog2e;
+                const float G = exp2_fast(gv), iG = exp2_fast(-gv);
                 dq4[e] = gQl[tn][e] * G;
                 dk4[e] = gKl[tn][e] * G + gKr[tn][e] * iG;
                 dl4[e] = gQl[tn][e] * qv[e] * G + gKl[tn][e] * kv[e] * G - gKr[tn][e] * kv[e] * iG;
@@ -558,29 +689,42 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     }
     lds_barrier();
     if (GATE == kGateChannel) {
-        for (int col = tid; col < DK; col += kThreads) {
-            float acc = sDg[col];  // the last-row term
-            for (int r = kC - 1; r >= 0; --r) {
-                acc += sDl[r * DK + col];
-                if (r < m) p.dla[((size_t)(tok0 + r) * H + h) * DK + col] = acc;
-            }
+        // suffix sums over the 64 rows, per column: kThreads / DK parts of rows, part
+        // totals through LDS, then each part walks its rows backwards
+        constexpr int NP = kThreads / DK, RP = kC / NP;
+        const int col = tid % DK, part = tid / DK;
+        float ps = 0.f;
+        for (int r = part * RP; r < (part + 1) * RP; ++r) ps += sDl[r * DK + col];
+        sGp[part * DK + col] = ps;
+        lds_barrier();
+        float acc = sDg[col];  // the last-row term
+        for (int p2 = part + 1; p2 < NP; ++p2) acc += sGp[p2 * DK + col];
+        for (int r = (part + 1) * RP - 1; r >= part * RP; --r) {
+            acc += sDl[r * DK + col];
+            if (r < m) p.dla[((size_t)(tok0 + r) * H + h) * DK + col] = acc;
         }
     } else if (GATE == kGateHead) {
-        // row sums (and the last-row term) into sGp, then the suffix sum by one thread
-        if (tid < kC) {
+        // row sums (four threads per row), the last-row term on row 63, then a suffix
+        // scan over the rows in wave 0
+        {
+            const int row = tid >> 2, q = tid & 3;
             float s = 0.f;
-            for (int col = 0; col < DK; ++col) s += sDl[tid * DK + col];
-            if (tid == kC - 1)
-                for (int col = 0; col < DK; ++col) s += sDg[col];
-            sGp[tid] = s;
+            for (int col = q; col < DK; col += 4) s += sDl[row * DK + col];
+            if (row == kC - 1)
+                for (int col = q; col < DK; col += 4) s += sDg[col];
+            s += dpp<kDppXor1>(s);
+            s += dpp<kDppXor2>(s);
+            if (q == 0) sGp[row] = s;
         }
         lds_barrier();
-        if (tid == 0) {
-            float acc = 0.f;
-            for (int r = kC - 1; r >= 0; --r) {
-                acc += sGp[r];
-                if (r < m) p.dla[(size_t)(tok0 + r) * H + h] = acc;
+        if (wave == 0) {
+            float x = sGp[lane];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_down(x, off, 64);
+                if (lane + off < 64) x += y;
             }
+            if (lane < m) p.dla[(size_t)(tok0 + lane) * H + h] = x;
         }
     }
 }
