@@ -608,6 +608,16 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
 
     // ---- stage 6: dK<-, dK->, dQ<- ------------------------------------------------------
     f32x4 gKl[NT], gKr[NT], gQl[NT];
+    // q, k of this lane's rows and columns for the chain rule at the end, loaded now so
+    // that they arrive during the products below
+    uint2 qw[NT], kw[NT];
+    const bool ok_row = R0 + r16 < m;
+    const size_t th_row = (size_t)(tok0 + (ok_row ? R0 + r16 : 0)) * H + h;
+#pragma unroll
+    for (int tn = 0; tn < NT; ++tn) {
+        qw[tn] = *(const uint2 *)(p.q + th_row * DK + 16 * tn + 4 * g4);
+        kw[tn] = *(const uint2 *)(p.k + th_row * DK + 16 * tn + 4 * g4);
+    }
     {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         const int row = R0 + r16;
@@ -649,14 +659,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     lds_barrier();
     {
         const int row = R0 + r16;
-        const bool ok = row < m;
-        const size_t th = (size_t)(tok0 + (ok ? row : 0)) * H + h;
-        uint2 qw[NT], kw[NT];  // all loads first
-#pragma unroll
-        for (int tn = 0; tn < NT; ++tn) {
-            qw[tn] = *(const uint2 *)(p.q + th * DK + 16 * tn + 4 * g4);
-            kw[tn] = *(const uint2 *)(p.k + th * DK + 16 * tn + 4 * g4);
-        }
+        const bool ok = ok_row;
+        const size_t th = th_row;
 #pragma unroll
         for (int tn = 0; tn < NT; ++tn) {
             const int col = 16 * tn + 4 * g4;
