@@ -117,7 +117,9 @@ def chunk_forward(q, k, v, beta, log_alpha=None, a=None, b=None, S0=None, cu_seq
 def chunk_bwd(q, k, v, beta, dO, log_alpha=None, S0=None, dS_final=None, cu_seqlens=None,
               C: int = 64, a=None, b=None):
     """Gradients of <dO, O> + <dS_final, S_final> by the chunk-form backward of the
-    "Kimi Delta Attention backward" notes (KDA form only: a = k, b = beta k), fp64.
+    "Kimi Delta Attention backward" notes (KDA form: a = k, b = beta k), fp64; with a and
+    b given, by the gated DPLR backward of the "Diagonal Plus Low Rank" notes (section 3),
+    see ``_chunk_bwd_dplr``.
 
     Notation as above, with the notes' state convention S_[t] = S_[t-1] Diag(gamma_C)
     + V_new^T K-> Diag(gamma_C).  Per chunk, with dS = dL/dS_[t] at its end:
@@ -138,7 +140,8 @@ def chunk_bwd(q, k, v, beta, dO, log_alpha=None, S0=None, dS_final=None, cu_seql
     out: the notes' diag(At^T dAt) / beta is written as the diagonal of the first
     line of their derivation, which is the same number and is defined at beta = 0.
     """
-    assert a is None and b is None, "chunk_bwd covers the KDA form only"
+    if a is not None:
+        return _chunk_bwd_dplr(q, k, v, beta, dO, log_alpha, a, b, S0, dS_final, cu_seqlens, C)
     q, k, v, beta, dO = (np.asarray(x, dtype=np.float64) for x in (q, k, v, beta, dO))
     la = None if log_alpha is None else np.asarray(log_alpha, dtype=np.float64)
     B, T, H, dk = q.shape
@@ -207,6 +210,109 @@ def chunk_bwd(q, k, v, beta, dO, log_alpha=None, S0=None, dS_final=None, cu_seql
                     suffix = np.cumsum(dlg[::-1], axis=0)[::-1]
                     out["dlog_alpha"][sl, h] = suffix if la.ndim == 4 else suffix.sum(axis=1)
                 dS = dS * gC[None, :] + G.T @ Ql - dU.T @ W
+            out["dS0"][n, h] = dS
+    res = {key: val.reshape((B, T) + val.shape[1:]) for key, val in out.items() if key != "dS0"}
+    res["dS0"] = out["dS0"]
+    return res
+
+
+def _chunk_bwd_dplr(q, k, v, beta, dO, log_alpha, a, b, S0, dS_final, cu_seqlens, C):
+    """Gated DPLR backward ("Diagonal Plus Low Rank" notes, section 3), fp64, with the
+    write term scaled by beta (V' = Diag(beta) V, the notes' V).  Per chunk, with
+    F = I + (B<- A->^T * M_1), E = F^-1, W = E B<-, Cm = -E (B<- K->^T * M_1) V',
+    N = Cm - W S_p^T (the notes' V_2), and dS = dL/dS_[t]:
+      dN = dCm = A-> Diag(gamma_C) dS^T + (Q<- A->^T * M)^T dO
+      dV'1 = K-> Diag(gamma_C) dS^T + (Q<- K->^T * M)^T dO
+      dW = -dN S_p
+      dE = -dCm V'^T (B<- K->^T * M_1)^T + dW B<-^T,    dF = -E^T dE E^T
+      dQ<- = dO S_p + (dO V'^T * M) K-> + (dO N^T * M) A->
+      dB<- = E^T dW - (E^T dCm V'^T * M_1) K-> + (dF * M_1) A->
+      dK-> = (dO V'^T * M)^T Q<- - (E^T dCm V'^T * M_1)^T B<- + V' dS Diag(gamma_C)
+      dA-> = (dO N^T * M)^T Q<- + (dF * M_1)^T B<- + N dS Diag(gamma_C)
+      dV' = dV'1 - (B<- K->^T * M_1)^T E^T dCm,          dV = Diag(beta) dV', dbeta = rowsum(dV' * V)
+      dlog Gamma = dQ<- Q<- + dB<- B<- - dK-> K-> - dA-> A->, plus diag(S_[t]^T dS) on the last row
+      dS_[t-1] = dS Diag(gamma_C) + dO^T Q<- - dCm^T W
+    The notes write dW with S_[t] and list dK->, dA-> without their state-update terms;
+    the forward definitions fix both (N uses S_[t-1]; V'^T K-> Diag(gamma_C) and
+    N^T A-> Diag(gamma_C) enter the state), and the pins against the token reverse pass
+    confirm that reading.
+    """
+    q, k, v, beta, dO, a, b = (np.asarray(x, dtype=np.float64) for x in (q, k, v, beta, dO, a, b))
+    la = None if log_alpha is None else np.asarray(log_alpha, dtype=np.float64)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    flat = lambda x: None if x is None else x.reshape((B * T,) + x.shape[2:])
+    qf, kf, vf, bf, laf, dOf, af, bbf = map(flat, (q, k, v, beta, la, dO, a, b))
+    if cu_seqlens is None:
+        bounds = [(n * T, (n + 1) * T) for n in range(B)]
+    else:
+        cu = list(np.asarray(cu_seqlens).tolist())
+        bounds = [(cu[i], cu[i + 1]) for i in range(len(cu) - 1)]
+    N_ = len(bounds)
+    out = {key: np.zeros((B * T, H, dk)) for key in ("dq", "dk", "da", "db")}
+    out["dv"] = np.zeros((B * T, H, dv))
+    out["dbeta"] = np.zeros((B * T, H))
+    out["dS0"] = np.zeros((N_, H, dv, dk))
+    if la is not None:
+        out["dlog_alpha"] = np.zeros((B * T,) + la.shape[2:])
+    M = np.tril(np.ones((C, C)))
+    M1 = np.tril(np.ones((C, C)), -1)
+    for n, (t0, t1) in enumerate(bounds):
+        for h in range(H):
+            S = np.zeros((dv, dk)) if S0 is None else np.array(S0[n, h], dtype=np.float64)
+            chunks = []
+            for c0 in range(t0, t1, C):
+                c1 = min(c0 + C, t1)
+                m = c1 - c0
+                Mm, M1m = M[:m, :m], M1[:m, :m]
+                Q, K, A_, B_ = qf[c0:c1, h], kf[c0:c1, h], af[c0:c1, h], bbf[c0:c1, h]
+                bet = bf[c0:c1, h]
+                Vp = bet[:, None] * vf[c0:c1, h]
+                Gam = np.exp(_g(None if laf is None else laf[c0:c1, h], m, dk))
+                gC = Gam[-1]
+                Ql, Kr, Ar, Bl = Q * Gam, K / Gam, A_ / Gam, B_ * Gam
+                E = _unit_lower_inverse(np.eye(m) + (Bl @ Ar.T) * M1m)
+                W = E @ Bl
+                BK = (Bl @ Kr.T) * M1m
+                Cm = -E @ (BK @ Vp)
+                Nn = Cm - W @ S.T
+                Sn = (S + Vp.T @ Kr + Nn.T @ Ar) * gC[None, :]
+                chunks.append(dict(c0=c0, c1=c1, m=m, Ql=Ql, Kr=Kr, Ar=Ar, Bl=Bl, Gam=Gam, gC=gC,
+                                   E=E, W=W, BK=BK, Nn=Nn, Vp=Vp, bet=bet, V=vf[c0:c1, h],
+                                   dO=dOf[c0:c1, h], Sp=S, Sn=Sn))
+                S = Sn
+            dS = np.zeros((dv, dk)) if dS_final is None else np.array(dS_final[n, h], dtype=np.float64)
+            for ch in reversed(chunks):
+                m = ch["m"]
+                Mm, M1m = M[:m, :m], M1[:m, :m]
+                Ql, Kr, Ar, Bl, Gam, gC = ch["Ql"], ch["Kr"], ch["Ar"], ch["Bl"], ch["Gam"], ch["gC"]
+                E, W, BK, Nn, Vp, Sp, G = ch["E"], ch["W"], ch["BK"], ch["Nn"], ch["Vp"], ch["Sp"], ch["dO"]
+                dC = (Ar * gC[None, :]) @ dS.T + ((Ql @ Ar.T) * Mm).T @ G
+                dV1 = (Kr * gC[None, :]) @ dS.T + ((Ql @ Kr.T) * Mm).T @ G
+                dW = -dC @ Sp
+                dE = -dC @ Vp.T @ BK.T + dW @ Bl.T
+                dF = -E.T @ dE @ E.T
+                dOV = (G @ Vp.T) * Mm
+                dON = (G @ Nn.T) * Mm
+                X = (E.T @ dC @ Vp.T) * M1m
+                dQl = G @ Sp + dOV @ Kr + dON @ Ar
+                dBl = E.T @ dW - X @ Kr + (dF * M1m) @ Ar
+                dKr = dOV.T @ Ql - X.T @ Bl + Vp @ dS * gC[None, :]
+                dAr = dON.T @ Ql + (dF * M1m).T @ Bl + Nn @ dS * gC[None, :]
+                dVp = dV1 - BK.T @ (E.T @ dC)
+                dlg = dQl * Ql + dBl * Bl - dKr * Kr - dAr * Ar
+                dlg[-1] += np.sum(ch["Sn"] * dS, axis=0)
+                sl = slice(ch["c0"], ch["c1"])
+                out["dq"][sl, h] = dQl * Gam
+                out["db"][sl, h] = dBl * Gam
+                out["dk"][sl, h] = dKr / Gam
+                out["da"][sl, h] = dAr / Gam
+                out["dv"][sl, h] = ch["bet"][:, None] * dVp
+                out["dbeta"][sl, h] = np.sum(dVp * ch["V"], axis=1)
+                if la is not None:
+                    suffix = np.cumsum(dlg[::-1], axis=0)[::-1]
+                    out["dlog_alpha"][sl, h] = suffix if la.ndim == 4 else suffix.sum(axis=1)
+                dS = dS * gC[None, :] + G.T @ Ql - dC.T @ W
             out["dS0"][n, h] = dS
     res = {key: val.reshape((B, T) + val.shape[1:]) for key, val in out.items() if key != "dS0"}
     res["dS0"] = out["dS0"]

@@ -126,3 +126,19 @@ def test_chunk_backward_of_the_notes_matches(C, gate):
     m = chunk_mirror.chunk_bwd(dO=dO, dS_final=dSf, C=C, **c)
     for key in ["dq", "dk", "dv", "dbeta", "dS0"] + (["dlog_alpha"] if gate else []):
         np.testing.assert_allclose(m[key], g[key], rtol=0, atol=1e-10, err_msg=key)
+
+
+@pytest.mark.parametrize("C", [1, 5, 16])
+@pytest.mark.parametrize("gate", [0, 1, 2])
+def test_dplr_chunk_backward_of_the_notes_matches(C, gate):
+    """The gated DPLR chunk backward of the DPLR notes (section 3; numpy, fp64) against
+    the token-level reverse pass: every gradient, a and b included."""
+    rng = np.random.default_rng(560 + C + 7 * gate)
+    cu = [0, 23, 23, 40, 61]
+    c = _case(rng, B=1, T=61, H=2, dk=5, dv=4, gate=gate, dplr=True, cu=cu)
+    dO = rng.standard_normal(c["v"].shape)
+    dSf = rng.standard_normal(c["S0"].shape)
+    g = oracle.recurrence_bwd(dO=dO, dS_final=dSf, **c)
+    m = chunk_mirror.chunk_bwd(dO=dO, dS_final=dSf, C=C, **c)
+    for key in ["dq", "dk", "dv", "da", "db", "dbeta", "dS0"] + (["dlog_alpha"] if gate else []):
+        np.testing.assert_allclose(m[key], g[key], rtol=0, atol=1e-10, err_msg=key)
