@@ -153,7 +153,7 @@ int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
 }
 
 size_t gdr_chunk_bwd_workspace(int B, int H, int T, int dk, int dv, int C, int n_seq, int dtype,
-                               int gate) {
+                               int gate, int has_ab) {
     const bool varlen = n_seq > 0;
     if (!shape_ok(B, H, T, dk, dv, n_seq, varlen)) return 0;
     gdr::BwdArgs a;
@@ -161,18 +161,23 @@ size_t gdr_chunk_bwd_workspace(int B, int H, int T, int dk, int dv, int C, int n
     a.B = B; a.H = H; a.T = T; a.dk = dk; a.dv = dv; a.C = C; a.n_seq = n_seq;
     a.dtype = dtype; a.gate = gate;
     static const int32_t dummy_cu = 0;
+    static const char dummy = 0;
     if (varlen) a.cu_seqlens = &dummy_cu;
+    if (has_ab) a.a = a.b = &dummy;
     if (!gdr::kda_bwd_supported(a)) return 0;
     return gdr::kda_bwd_workspace_bytes(a, varlen ? n_seq : B);
 }
 
-int gdr_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
-                  const float *beta, const float *S0, const void *dO, const float *dS_final,
-                  void *dq, void *dk, void *dv, float *dlog_alpha, float *dbeta, float *dS0,
-                  const int32_t *cu_seqlens, int n_seq, int B, int H, int T, int dk_, int dv_,
-                  int C, int dtype, int gate, void *workspace, size_t workspace_bytes,
-                  void *stream) {
+int gdr_chunk_bwd(const void *q, const void *k, const void *v, const void *a_, const void *b_,
+                  const float *log_alpha, const float *beta, const float *S0, const void *dO,
+                  const float *dS_final, void *dq, void *dk, void *dv, void *da, void *db,
+                  float *dlog_alpha, float *dbeta, float *dS0, const int32_t *cu_seqlens,
+                  int n_seq, int B, int H, int T, int dk_, int dv_, int C, int dtype, int gate,
+                  void *workspace, size_t workspace_bytes, void *stream) {
     if (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta) return GDR_ERR_NULL;
+    const bool has_ab = a_ != nullptr;
+    if ((a_ == nullptr) != (b_ == nullptr)) return GDR_ERR_NULL;
+    if ((da == nullptr) != !has_ab || (db == nullptr) != !has_ab) return GDR_ERR_NULL;
     if (!gate_ok(gate)) return GDR_ERR_SHAPE;
     if (gate & GDR_GATE_CLIP) return GDR_ERR_UNSUPPORTED;
     if ((gate == GDR_GATE_NONE) != (log_alpha == nullptr)) return GDR_ERR_NULL;
@@ -181,9 +186,11 @@ int gdr_chunk_bwd(const void *q, const void *k, const void *v, const float *log_
     if (!shape_ok(B, H, T, dk_, dv_, n_seq, varlen)) return GDR_ERR_SHAPE;
     gdr::BwdArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.q = q; a.k = k; a.v = v; a.dO = dO; a.log_alpha = log_alpha; a.beta = beta; a.S0 = S0;
-    a.dS_final = dS_final; a.grad_q = dq; a.grad_k = dk; a.grad_v = dv; a.grad_la = dlog_alpha;
-    a.grad_beta = dbeta; a.grad_S0 = dS0; a.cu_seqlens = cu_seqlens; a.n_seq = varlen ? n_seq : 0;
+    a.q = q; a.k = k; a.v = v; a.a = a_; a.b = b_; a.dO = dO; a.log_alpha = log_alpha;
+    a.beta = beta; a.S0 = S0; a.dS_final = dS_final;
+    a.grad_q = dq; a.grad_k = dk; a.grad_v = dv; a.grad_a = da; a.grad_b = db;
+    a.grad_la = dlog_alpha; a.grad_beta = dbeta; a.grad_S0 = dS0; a.cu_seqlens = cu_seqlens;
+    a.n_seq = varlen ? n_seq : 0;
     a.B = B; a.H = H; a.T = T; a.dk = dk_; a.dv = dv_; a.C = C; a.dtype = dtype; a.gate = gate;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     if (!gdr::kda_bwd_supported(a)) return GDR_ERR_UNSUPPORTED;
@@ -192,18 +199,22 @@ int gdr_chunk_bwd(const void *q, const void *k, const void *v, const float *log_
     const size_t tokens = (size_t)B * T, es = elem_size(dtype);
     const size_t la_elems = gate == GDR_GATE_CHANNEL ? tokens * H * dk_ : (gate == GDR_GATE_HEAD ? tokens * H : 0);
     const size_t sbytes = (size_t)N * H * dv_ * dk_ * 4;
-    const Range inputs[] = {range(q, tokens * H * dk_ * es), range(k, tokens * H * dk_ * es),
-                            range(v, tokens * H * dv_ * es), range(log_alpha, la_elems * 4),
-                            range(beta, tokens * H * 4), range(S0, S0 ? sbytes : 0),
-                            range(dO, tokens * H * dv_ * es), range(dS_final, dS_final ? sbytes : 0),
+    const size_t kbytes = tokens * H * dk_ * es, vbytes = tokens * H * dv_ * es;
+    const Range inputs[] = {range(q, kbytes), range(k, kbytes), range(v, vbytes),
+                            range(a_, has_ab ? kbytes : 0), range(b_, has_ab ? kbytes : 0),
+                            range(log_alpha, la_elems * 4), range(beta, tokens * H * 4),
+                            range(S0, S0 ? sbytes : 0), range(dO, vbytes),
+                            range(dS_final, dS_final ? sbytes : 0),
                             range(cu_seqlens, varlen ? (size_t)(n_seq + 1) * 4 : 0)};
-    const Range outputs[] = {range(dq, tokens * H * dk_ * es), range(dk, tokens * H * dk_ * es),
-                             range(dv, tokens * H * dv_ * es), range(dlog_alpha, la_elems * 4),
-                             range(dbeta, tokens * H * 4), range(dS0, dS0 ? sbytes : 0)};
+    const Range outputs[] = {range(dq, kbytes), range(dk, kbytes), range(dv, vbytes),
+                             range(da, has_ab ? kbytes : 0), range(db, has_ab ? kbytes : 0),
+                             range(dlog_alpha, la_elems * 4), range(dbeta, tokens * H * 4),
+                             range(dS0, dS0 ? sbytes : 0)};
+    constexpr int kOut = sizeof(outputs) / sizeof(outputs[0]);
     const size_t need = gdr::kda_bwd_workspace_bytes(a, N);
     if (!workspace || workspace_bytes < need) return GDR_ERR_WORKSPACE;
     const Range rws = range(workspace, need);
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < kOut; ++i) {
         for (const Range &r : inputs)
             if (overlaps(outputs[i], r)) return GDR_ERR_ALIAS;
         for (int j = 0; j < i; ++j)
@@ -213,8 +224,8 @@ int gdr_chunk_bwd(const void *q, const void *k, const void *v, const float *log_
     for (const Range &r : inputs)
         if (overlaps(rws, r)) return GDR_ERR_ALIAS;
     if (trace_enabled())
-        std::fprintf(stderr, "[gdr] kda_bwd B=%d H=%d T=%d N=%d dk=%d dv=%d gate=%d ws=%zu\n", B, H, T,
-                     N, dk_, dv_, gate, need);
+        std::fprintf(stderr, "[gdr] %s B=%d H=%d T=%d N=%d dk=%d dv=%d gate=%d ws=%zu\n",
+                     has_ab ? "dplr_bwd" : "kda_bwd", B, H, T, N, dk_, dv_, gate, need);
     const int rc = gdr::launch_kda_bwd(a, N, (hipStream_t)stream);
     return rc == 0 ? GDR_OK : GDR_ERR_HIP;
 }

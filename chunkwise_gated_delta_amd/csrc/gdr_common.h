@@ -114,11 +114,11 @@ struct FwdArgs {
     size_t workspace_bytes;
 };
 
-// Arguments of the backward pass (KDA form: a = k, b = beta k).
+// Arguments of the backward pass (a, b NULL: the KDA form a = k, b = beta k).
 struct BwdArgs {
-    const void *q, *k, *v, *dO;
+    const void *q, *k, *v, *a, *b, *dO;
     const float *log_alpha, *beta, *S0, *dS_final;
-    void *grad_q, *grad_k, *grad_v;            // dL/dq, dL/dk, dL/dv
+    void *grad_q, *grad_k, *grad_v, *grad_a, *grad_b;  // dL/dq, dL/dk, dL/dv, dL/da, dL/db
     float *grad_la, *grad_beta, *grad_S0;      // dL/dlog_alpha, dL/dbeta, dL/dS0
     const int32_t *cu_seqlens;
     int n_seq, B, H, T, dk, dv, C, dtype, gate;

@@ -53,9 +53,9 @@ __device__ __forceinline__ int tr_off(int d, int t) {
 // Backward block of job j: W' slot <- K^ (natural layout), A^ slot <- W' (transposed),
 // K^b slot <- Q~ (transposed), gamma_C copied.  One workgroup per block; the other
 // slots are left as they are (the reverse pass does not use them).
-template <int DK>
+template <int DK, bool DP>
 __global__ __launch_bounds__(kThreads) void kda_bwd_reorder_kernel(const char *fwd, char *bwd, int nblk) {
-    using F = Blk<DK, false>;
+    using F = Blk<DK, DP>;  // forward blocks (DPLR: the K^ slot holds A^)
     using R = Blk<DK, true>;
     const int j = blockIdx.x;
     if (j >= nblk) return;
@@ -97,9 +97,11 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_reorder_kernel(const char *f
 // ---------------------------------------------------------------------------------
 struct BwdParams {
     const bf16 *q, *k, *v, *dO;
+    const bf16 *a, *b;  // DPLR only
     const float *la, *beta;
     const uint16_t *S, *dS;  // bf16 [chunk][head][dv][dk]: S_p, dS_n
     bf16 *dq, *dk, *dv;
+    bf16 *da, *db;      // DPLR only
     float *dla, *dbeta;
     const int32_t *cu;
     const int32_t *coff;
@@ -719,6 +721,649 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             s += dpp<kDppXor1>(s);
             s += dpp<kDppXor2>(s);
             if (q == 0) sGp[row] = s;
+        }
+        lds_barrier();
+        if (wave == 0) {
+            float x = sGp[lane];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_down(x, off, 64);
+                if (lane + off < 64) x += y;
+            }
+            if (lane < m) p.dla[(size_t)(tok0 + lane) * H + h] = x;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Per-chunk gradients of the gated DPLR form ("Diagonal Plus Low Rank" notes,
+// section 3), with the write term scaled by beta (V' = Diag(beta) V):
+//   F = I + (B<- A->^T strictly lower), E = F^-1, W = E B<-, BK = B<- K->^T strictly lower,
+//   A_qk = Q<- K->^T, A_qa = Q<- A->^T (both on and below the diagonal),
+//   N = -E BK V' - W S_p^T,  S_n = (S_p + V'^T K-> + N^T A->) Diag(gamma_C)
+// and, with dSg = dS_n Diag(gamma_C):
+//   dN = A-> dSg^T + A_qa^T dO,     dV'1 = K-> dSg^T + A_qk^T dO
+//   dV' = dV'1 - (E BK)^T dN,       dV = Diag(beta) dV',  dbeta = rowsum(dV' V)
+//   dW = -dN S_p,  Yc = dN V'^T,    dE = -Yc BK^T + dW B<-^T,  dF = -E^T dE E^T (strictly lower)
+//   X = E^T Yc (strictly lower),    dOV = dO V'^T, dON = dO N^T (on and below the diagonal)
+//   dQ<- = dO S_p + dOV K-> + dON A->
+//   dB<- = E^T dW - X K-> + dF A->
+//   dK-> = V' dSg + dOV^T Q<- - X^T B<-
+//   dA-> = N dSg + dON^T Q<- + dF^T B<-
+//   dg = dQ<- Q<- + dB<- B<- - dK-> K-> - dA-> A->, plus on the last row
+//        sum_i S_n dS_n = sum_i S_p dSg + sum_r K-> (V' dSg) + sum_r A-> (N dSg)
+// (the notes print dW with S_[t] and leave the state terms out of dK->, dA->; the
+// forward definitions fix both).  V' is never stored: beta scales the fragments of V
+// where they are read, and E BK is kept unscaled.
+// ---------------------------------------------------------------------------------
+template <int DK>
+struct BwdDpSmem {
+    static constexpr int KS = DK + 8, CS = kC + 8, VS = 32;
+    static constexpr int QK = kC * KS * 2, CC = kC * CS * 2;
+    static constexpr int oKr = 0;            // K->
+    static constexpr int oAr = oKr + QK;     // A->
+    static constexpr int oW = oAr + QK;      // W, then dW; before W: the inverse's temporaries
+    static constexpr int oEBK = oW + QK;     // E BK (unscaled); then dON
+    static constexpr int oQB = oEBK + CC;    // Q<-, B<-; during the dv loop the tile buffers
+    static constexpr int oE = oQB + 2 * QK;  // E
+    static constexpr int oBK = oE + CC;      // BK; then dE, then X
+    static constexpr int oAqk = oBK + CC;    // A_qk; then Yc, Z, dF
+    static constexpr int oAqa = oAqk + CC;   // A_qa; then dOV
+    //   dv tile: S_p [32][KS], dSg [32][KS], V, dO, N, dN [64][VS]; over Q<-, B<- when it
+    //   fits there (dk = 128), else in a region of its own
+    static constexpr int tSp = 0, tdS = tSp + 32 * KS * 2, tV = tdS + 32 * KS * 2;
+    static constexpr int tdO = tV + kC * VS * 2, tN = tdO + kC * VS * 2, tdN = tN + kC * VS * 2;
+    static constexpr int tEnd = tdN + kC * VS * 2;
+    //   the inverse: diagonal blocks of F fp32 [64][20], L, middle factor; over W and E BK
+    //   when they fit there, else in a region of its own
+    static constexpr int iKd = 0, iL = kC * 20 * 4, iTm = iL + CC, iEnd = iTm + CC;
+    static constexpr bool kTileOverQB = tEnd <= 2 * QK, kInvOverW = iEnd <= QK + CC;
+    static constexpr int oExtra = oAqa + CC;
+    static constexpr int oTile = kTileOverQB ? oQB : oExtra;
+    static constexpr int oInv = kInvOverW ? oW : oExtra + (kTileOverQB ? 0 : tEnd);
+    static constexpr int oBeta = oExtra + (kTileOverQB ? 0 : tEnd) + (kInvOverW ? 0 : iEnd);
+    static constexpr int oGam = oBeta + kC * 4;
+    static constexpr int oGp = oGam + DK * 4;
+    static constexpr int oDb = oGp + 8 * DK * 4;
+    static constexpr int oDg = oDb + kC * 4;
+    static constexpr int bytes = oDg + DK * 4;
+    static_assert(kC * DK * 4 <= 2 * QK, "Gamma / dg fit over K->, A-> and over Q<-, B<-");
+    static_assert(bytes <= 160 * 1024, "LDS");
+};
+
+template <int DK, int GATE>
+__global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParams p) {
+    using L = BwdDpSmem<DK>;
+    constexpr int KS = L::KS, CS = L::CS, VS = L::VS;
+    constexpr int NT = DK / 16, CPT = DK / 32, WPR = CPT / 2;
+    __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+    uint16_t *sKr = (uint16_t *)(smem + L::oKr), *sAr = (uint16_t *)(smem + L::oAr);
+    uint16_t *sW = (uint16_t *)(smem + L::oW), *sEBK = (uint16_t *)(smem + L::oEBK);
+    uint16_t *sQl = (uint16_t *)(smem + L::oQB), *sBl = sQl + kC * KS;
+    uint16_t *sE = (uint16_t *)(smem + L::oE), *sBK = (uint16_t *)(smem + L::oBK);
+    uint16_t *sAqk = (uint16_t *)(smem + L::oAqk), *sAqa = (uint16_t *)(smem + L::oAqa);
+    char *sT = smem + L::oTile;
+    uint16_t *sSp = (uint16_t *)(sT + L::tSp), *sdS = (uint16_t *)(sT + L::tdS);
+    uint16_t *sV = (uint16_t *)(sT + L::tV), *sdO = (uint16_t *)(sT + L::tdO);
+    uint16_t *sN = (uint16_t *)(sT + L::tN), *sdN = (uint16_t *)(sT + L::tdN);
+    float *sKd = (float *)(smem + L::oInv + L::iKd);
+    uint16_t *sL = (uint16_t *)(smem + L::oInv + L::iL), *sTm = (uint16_t *)(smem + L::oInv + L::iTm);
+    float *sBeta = (float *)(smem + L::oBeta), *sGam = (float *)(smem + L::oGam);
+    float *sGp = (float *)(smem + L::oGp), *sDb = (float *)(smem + L::oDb);
+    float *sDg = (float *)(smem + L::oDg);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int H = p.H, DV = p.dv_;
+    const int job = blockIdx.x;
+    const int h = job % H;
+    int n = 0, c = 0;
+    if (!chunk_of(p, job / H, n, c)) return;  // workgroup-uniform
+    long t0, t1;
+    seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
+    const long tok0 = t0 + (long)c * kC;
+    const int m = (int)((t1 - tok0) < kC ? (t1 - tok0) : kC);
+    const size_t sbase = (size_t)(job / H) * H + h;
+    const int R0 = 16 * wave;
+    const int lo_k = R0 >= 32 ? 32 : 0;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+
+    constexpr int kSPT = 32 * DK / 8 / kThreads;
+    struct Tile {
+        uint4 s[kSPT], d[kSPT], v, o;
+    } pf;
+    auto issue = [&](int j0) {
+        const uint16_t *ps = p.S + (sbase * DV + j0) * DK;
+        const uint16_t *pd = p.dS + (sbase * DV + j0) * DK;
+#pragma unroll
+        for (int i = 0; i < kSPT; ++i) {
+            const int idx = tid + kThreads * i, r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+            pf.s[i] = *(const uint4 *)(ps + (size_t)r * DK + c8);
+            pf.d[i] = *(const uint4 *)(pd + (size_t)r * DK + c8);
+        }
+        const int r = tid >> 2, c8 = 8 * (tid & 3);
+        const size_t off = ((size_t)(tok0 + (r < m ? r : 0)) * H + h) * DV + j0 + c8;
+        pf.v = *(const uint4 *)(p.v + off);
+        pf.o = *(const uint4 *)(p.dO + off);
+    };
+    issue(0);
+
+    // ---- gate (rows 8rg + i, channels c0 + e) ------------------------------------------
+    const int rg = tid >> 5, c0 = CPT * (tid & 31);
+    float g[8][CPT];
+    {
+        float la[8][CPT];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * rg + i;
+            const size_t th = (size_t)(tok0 + (r < m ? r : 0)) * H + h;
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) la[i][e] = 0.f;
+            if (GATE == kGateChannel) {
+                if constexpr (CPT == 4) {
+                    const float4 x = *(const float4 *)(p.la + th * DK + c0);
+                    la[i][0] = x.x; la[i][CPT > 1 ? 1 : 0] = x.y;
+                    la[i][CPT > 2 ? 2 : 0] = x.z; la[i][CPT > 3 ? 3 : 0] = x.w;
+                } else {
+                    const float2 x = *(const float2 *)(p.la + th * DK + c0);
+                    la[i][0] = x.x; la[i][CPT > 1 ? 1 : 0] = x.y;
+                }
+            } else if (GATE == kGateHead) {
+                const float x = p.la[th];
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) la[i][e] = x;
+            }
+            if (r >= m)
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) la[i][e] = 0.f;
+        }
+        float run[CPT];
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) run[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) {
+                run[e] += la[i][e];
+                g[i][e] = run[e];
+            }
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) sGp[rg * DK + c0 + e] = run[e];
+        lds_barrier();
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+            float carry = 0.f;
+            for (int r2 = 0; r2 < rg; ++r2) carry += sGp[r2 * DK + c0 + e];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) g[i][e] += carry;
+        }
+    }
+    // Q<-, B<- (scale e^g) or K->, A-> (scale e^-g) of two inputs, bf16 into LDS
+    auto scaled = [&](const bf16 *x, const bf16 *y, uint16_t *dx, uint16_t *dy, bool up) {
+        uint32_t xw[8][WPR], yw[8][WPR];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * rg + i;
+            const size_t th = (size_t)(tok0 + (r < m ? r : 0)) * H + h;
+            if constexpr (WPR == 2) {
+                const uint2 a2 = *(const uint2 *)(x + th * DK + c0), b2 = *(const uint2 *)(y + th * DK + c0);
+                xw[i][0] = a2.x; xw[i][WPR - 1] = a2.y; yw[i][0] = b2.x; yw[i][WPR - 1] = b2.y;
+            } else {
+                xw[i][0] = *(const uint32_t *)(x + th * DK + c0);
+                yw[i][0] = *(const uint32_t *)(y + th * DK + c0);
+            }
+            if (r >= m)
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) xw[i][w] = yw[i][w] = 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * rg + i;
+            uint32_t ox[WPR], oy[WPR];
+#pragma unroll
+            for (int w = 0; w < WPR; ++w) {
+                const float s0 = up ? g[i][2 * w] : -g[i][2 * w], s1 = up ? g[i][2 * w + 1] : -g[i][2 * w + 1];
+                const float e0 = exp2_fast(s0 * kLog2e), e1 = exp2_fast(s1 * kLog2e);
+                ox[w] = pack_bf16x2(bf16_lo(xw[i][w]) * e0, bf16_hi(xw[i][w]) * e1);
+                oy[w] = pack_bf16x2(bf16_lo(yw[i][w]) * e0, bf16_hi(yw[i][w]) * e1);
+            }
+            if constexpr (WPR == 2) {
+                *(uint2 *)(dx + r * KS + c0) = make_uint2(ox[0], ox[WPR - 1]);
+                *(uint2 *)(dy + r * KS + c0) = make_uint2(oy[0], oy[WPR - 1]);
+            } else {
+                *(uint32_t *)(dx + r * KS + c0) = ox[0];
+                *(uint32_t *)(dy + r * KS + c0) = oy[0];
+            }
+        }
+    };
+    scaled(p.q, p.b, sQl, sBl, true);
+    scaled(p.k, p.a, sKr, sAr, false);
+    if (rg == 7)
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) sGam[c0 + e] = exp2_fast(g[7][e] * kLog2e);
+    if (tid < kC) sBeta[tid] = tid < m ? p.beta[(size_t)(tok0 + tid) * H + h] : 0.f;
+    for (int i = tid; i < kC; i += kThreads) sDb[i] = 0.f;
+    for (int i = tid; i < DK; i += kThreads) sDg[i] = 0.f;
+    for (int idx = tid; idx < kC * CS / 8; idx += kThreads) ((uint4 *)sE)[idx] = make_uint4(0u, 0u, 0u, 0u);
+    lds_barrier();
+
+    // ---- C x C products: F's strictly lower part (fp32 diagonal blocks, bf16 L), BK, A_qk, A_qa
+    for (int tj = 0; tj < 4; ++tj) {
+        f32x4 ba = z, bk = z, aq = z, aa = z;
+        if (tj <= wave) {
+            ba = mma_tile<false, true, DK>(sBl, KS, sAr, KS, R0, 16 * tj, 0, DK, z, lane);
+            bk = mma_tile<false, true, DK>(sBl, KS, sKr, KS, R0, 16 * tj, 0, DK, z, lane);
+            aq = mma_tile<false, true, DK>(sQl, KS, sKr, KS, R0, 16 * tj, 0, DK, z, lane);
+            aa = mma_tile<false, true, DK>(sQl, KS, sAr, KS, R0, 16 * tj, 0, DK, z, lane);
+        }
+        const int row = R0 + r16;
+        float vba[4], vbk[4], vaq[4], vaa[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int col = 16 * tj + 4 * g4 + e;
+            vba[e] = col < row ? ba[e] : 0.f;
+            vbk[e] = col < row ? bk[e] : 0.f;
+            vaq[e] = col <= row ? aq[e] : 0.f;
+            vaa[e] = col <= row ? aa[e] : 0.f;
+            if (tj == wave) sKd[row * 20 + 4 * g4 + e] = vba[e];
+        }
+        const int o = row * CS + 16 * tj + 4 * g4;
+        store4(sL + o, vba[0], vba[1], vba[2], vba[3]);
+        store4(sBK + o, vbk[0], vbk[1], vbk[2], vbk[3]);
+        store4(sAqk + o, vaq[0], vaq[1], vaq[2], vaq[3]);
+        store4(sAqa + o, vaa[0], vaa[1], vaa[2], vaa[3]);
+    }
+    lds_barrier();
+
+    // ---- E = F^-1: diagonal blocks by forward substitution, then two doubling levels ----
+    {
+        const int jl = lane >> 2, s4 = lane & 3, j = R0 + jl;
+        float xs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float acc = 0.f;
+#pragma unroll
+            for (int u = 0; u < (i + 3) / 4; ++u) acc += sKd[(R0 + i) * 20 + 4 * u + s4] * xs[u];
+            acc += dpp<kDppXor1>(acc);
+            acc += dpp<kDppXor2>(acc);
+            const float xi = (i == jl ? 1.f : 0.f) - acc;
+            if (s4 == (i & 3)) xs[i >> 2] = xi;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sE[(R0 + 4 * u + s4) * CS + j] = __builtin_bit_cast(uint16_t, (__bf16)xs[u]);
+    }
+    lds_barrier();
+    if (wave == 0 || wave == 2) {
+        const int o = wave == 0 ? 0 : 32;
+        f32x4 t = mfma16(frag4_tr(sE + o, o, CS, 0, lane), frag4(sL + o, o + 16 + r16, CS, 4 * g4), z);
+        store4(sTm + (o + 16 + r16) * CS + o + 4 * g4, t[0], t[1], t[2], t[3]);
+        asm volatile("" ::: "memory");
+        t = mfma16(frag4_tr(sTm + o, o + 16, CS, 0, lane), frag4(sE + o + 16, o + 16 + r16, CS, 4 * g4), z);
+        store4(sE + (o + 16 + r16) * CS + o + 4 * g4, -t[0], -t[1], -t[2], -t[3]);
+    }
+    lds_barrier();
+    {
+        const int m0 = 32 + 16 * (wave >> 1), n0 = 16 * (wave & 1);
+        const f32x4 t = mma_tile<false, false, kC>(sL, CS, sE, CS, m0, n0, 0, 32, z, lane);
+        store4(sTm + (m0 + r16) * CS + n0 + 4 * g4, t[0], t[1], t[2], t[3]);
+        lds_barrier();
+        const f32x4 cc = mma_tile<false, false, kC>(sE + 32, CS, sTm + 32 * CS, CS, m0, n0, 0, 32, z, lane);
+        lds_barrier();
+        store4(sE + (m0 + r16) * CS + n0 + 4 * g4, -cc[0], -cc[1], -cc[2], -cc[3]);
+    }
+    lds_barrier();
+
+    // ---- W = E B<-, E BK -------------------------------------------------------------------
+    {
+        const int k1 = R0 + 16 <= 32 ? 32 : 64;  // E is lower triangular
+        f32x4 wv[NT], eb[4];
+#pragma unroll
+        for (int tn = 0; tn < NT; ++tn) wv[tn] = mma_tile<false, false, kC>(sE, CS, sBl, KS, R0, 16 * tn, 0, k1, z, lane);
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) eb[tj] = mma_tile<false, false, kC>(sE, CS, sBK, CS, R0, 16 * tj, 0, k1, z, lane);
+        lds_barrier();  // the inverse's temporaries under W and E BK are read
+#pragma unroll
+        for (int tn = 0; tn < NT; ++tn)
+            store4(sW + (R0 + r16) * KS + 16 * tn + 4 * g4, wv[tn][0], wv[tn][1], wv[tn][2], wv[tn][3]);
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj)
+            store4(sEBK + (R0 + r16) * CS + 16 * tj + 4 * g4, eb[tj][0], eb[tj][1], eb[tj][2], eb[tj][3]);
+    }
+    lds_barrier();  // Q<-, B<- are not read again before they are rebuilt after the dv loop
+
+    // ---- the dv tiles (buffers over Q<-, B<-) -----------------------------------------
+    f32x4 aQ[NT], aW[NT], aKs[NT], aAs[NT], aOV[4], aON[4], aY[4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) aQ[t] = aW[t] = aKs[t] = aAs[t] = z;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) aOV[t] = aON[t] = aY[t] = z;
+    float gpart[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float dbp = 0.f;  // rowsum of dV' V for this lane's row and columns
+    const float brow = sBeta[R0 + r16];
+    // beta of the 8 rows 8(lane/16) + k0 + 0..7 (the contraction index of a transposed
+    // fragment over the chunk's rows), to scale V into V' where it is read
+    auto bscale8 = [&](bf16x8 f, int k0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (__bf16)((float)f[i] * sBeta[k0 + 8 * g4 + i]);
+        return f;
+    };
+    auto bscale = [&](bf16x8 f, float bs) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (__bf16)((float)f[i] * bs);
+        return f;
+    };
+    for (int j0 = 0; j0 < DV; j0 += 32) {
+        {
+#pragma unroll
+            for (int i = 0; i < kSPT; ++i) {
+                const int idx = tid + kThreads * i, r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+                *(uint4 *)(sSp + r * KS + c8) = pf.s[i];
+                const uint32_t w4[4] = {pf.d[i].x, pf.d[i].y, pf.d[i].z, pf.d[i].w};
+                const uint32_t s4[4] = {pf.s[i].x, pf.s[i].y, pf.s[i].z, pf.s[i].w};
+                uint32_t o4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float d0 = bf16_lo(w4[e]) * sGam[c8 + 2 * e], d1 = bf16_hi(w4[e]) * sGam[c8 + 2 * e + 1];
+                    o4[e] = pack_bf16x2(d0, d1);
+                    gpart[2 * e] += bf16_lo(s4[e]) * d0;
+                    gpart[2 * e + 1] += bf16_hi(s4[e]) * d1;
+                }
+                *(uint4 *)(sdS + r * KS + c8) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+            }
+            const int r = tid >> 2, c8 = 8 * (tid & 3);
+            const uint32_t keep = 0u - (uint32_t)(r < m);
+            *(uint4 *)(sV + r * VS + c8) = make_uint4(pf.v.x & keep, pf.v.y & keep, pf.v.z & keep, pf.v.w & keep);
+            *(uint4 *)(sdO + r * VS + c8) = make_uint4(pf.o.x & keep, pf.o.y & keep, pf.o.z & keep, pf.o.w & keep);
+        }
+        if (j0 + 32 < DV) issue(j0 + 32);
+        lds_barrier();
+        // N = -(E BK) V' - W S_p^T,  dN = A-> dSg^T + A_qa^T dO
+        {
+            const int k1 = R0 + 16 <= 32 ? 32 : 64;
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn) {
+                const int n0 = 16 * tn;
+                f32x4 cm = z;
+                for (int k = 0; k < k1; k += 32)
+                    cm = mfma(bscale8(frag_tr(sV, k, VS, n0, lane), k), frag(sEBK, R0 + r16, CS, k + 8 * g4), cm);
+                const f32x4 ws = mma_tile<false, true, DK>(sW, KS, sSp, KS, R0, n0, 0, DK, z, lane);
+                f32x4 dn = mma_tile<false, true, DK>(sAr, KS, sdS, KS, R0, n0, 0, DK, z, lane);
+                dn = mma_tile<true, false, kC>(sAqa, CS, sdO, VS, R0, n0, lo_k, kC, dn, lane);
+                store4(sN + (R0 + r16) * VS + n0 + 4 * g4, -cm[0] - ws[0], -cm[1] - ws[1], -cm[2] - ws[2], -cm[3] - ws[3]);
+                store4(sdN + (R0 + r16) * VS + n0 + 4 * g4, dn[0], dn[1], dn[2], dn[3]);
+            }
+        }
+        lds_barrier();
+        {
+            const int row = R0 + r16;
+            // dV' = K-> dSg^T + A_qk^T dO - (E BK)^T dN; dV = Diag(beta) dV'; dbeta += dV' . V
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn) {
+                const int n0 = 16 * tn;
+                f32x4 d = mma_tile<false, true, DK>(sKr, KS, sdS, KS, R0, n0, 0, DK, z, lane);
+                d = mma_tile<true, false, kC>(sAqk, CS, sdO, VS, R0, n0, lo_k, kC, d, lane);
+                const f32x4 e2 = mma_tile<true, false, kC>(sEBK, CS, sdN, VS, R0, n0, lo_k, kC, z, lane);
+                const uint2 vw = *(const uint2 *)(sV + row * VS + n0 + 4 * g4);
+                const float vv[4] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    d[e] -= e2[e];
+                    dbp += d[e] * vv[e];
+                }
+                if (row < m) {
+                    uint2 o;
+                    o.x = pack_bf16x2(brow * d[0], brow * d[1]);
+                    o.y = pack_bf16x2(brow * d[2], brow * d[3]);
+                    *(uint2 *)(p.dv + ((size_t)(tok0 + row) * H + h) * DV + j0 + n0 + 4 * g4) = o;
+                }
+            }
+            // contractions over the tile: dQ<- += dO S_p, dW += dN S_p, dK->s += V' dSg, dA->s += N dSg
+            const bf16x8 fdo = frag(sdO, row, VS, 8 * g4);
+            const bf16x8 fdn = frag(sdN, row, VS, 8 * g4);
+            const bf16x8 fvp = bscale(frag(sV, row, VS, 8 * g4), brow);
+            const bf16x8 fn = frag(sN, row, VS, 8 * g4);
+#pragma unroll
+            for (int tn = 0; tn < NT; ++tn) {
+                const bf16x8 fs = frag_tr(sSp, 0, KS, 16 * tn, lane);
+                const bf16x8 fd = frag_tr(sdS, 0, KS, 16 * tn, lane);
+                aQ[tn] = mfma(fs, fdo, aQ[tn]);
+                aW[tn] = mfma(fs, fdn, aW[tn]);
+                aKs[tn] = mfma(fd, fvp, aKs[tn]);
+                aAs[tn] = mfma(fd, fn, aAs[tn]);
+            }
+            // dOV += dO V'^T, dON += dO N^T (lower tiles); Yc += dN V'^T
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj) {
+                const bf16x8 fv = bscale(frag(sV, 16 * tj + r16, VS, 8 * g4), sBeta[16 * tj + r16]);
+                if (tj <= wave) {
+                    aOV[tj] = mfma(fv, fdo, aOV[tj]);
+                    aON[tj] = mfma(frag(sN, 16 * tj + r16, VS, 8 * g4), fdo, aON[tj]);
+                }
+                aY[tj] = mfma(fv, fdn, aY[tj]);
+            }
+        }
+        lds_barrier();
+    }
+
+    // ---- after the dv loop: dW, dOV, dON, Yc to LDS; Q<-, B<- rebuilt ---------------------
+    uint16_t *sdW = sW, *sOV = sAqa, *sON = sEBK, *sY = sAqk;
+    {
+        const int row = R0 + r16;
+#pragma unroll
+        for (int tn = 0; tn < NT; ++tn)
+            store4(sdW + row * KS + 16 * tn + 4 * g4, -aW[tn][0], -aW[tn][1], -aW[tn][2], -aW[tn][3]);
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+            float ov[4], on[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool lo = 16 * tj + 4 * g4 + e <= row;
+                ov[e] = lo ? aOV[tj][e] : 0.f;
+                on[e] = lo ? aON[tj][e] : 0.f;
+            }
+            const int o = row * CS + 16 * tj + 4 * g4;
+            store4(sOV + o, ov[0], ov[1], ov[2], ov[3]);
+            store4(sON + o, on[0], on[1], on[2], on[3]);
+            store4(sY + o, aY[tj][0], aY[tj][1], aY[tj][2], aY[tj][3]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = gpart[e];
+#pragma unroll
+            for (int off = DK / 8; off < 64; off <<= 1) x += __shfl_xor(x, off);
+            if (lane < DK / 8) atomicAdd(&sDg[8 * lane + e], x);
+        }
+        dbp += __shfl_xor(dbp, 16);
+        dbp += __shfl_xor(dbp, 32);
+        if (g4 == 0) sDb[row] = dbp;
+    }
+    scaled(p.q, p.b, sQl, sBl, true);
+    lds_barrier();
+    // dE = -Yc BK^T + dW B<-^T;  X = E^T Yc (strictly lower)
+    f32x4 vdE[4], vX[4];
+    {
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+            f32x4 d = mma_tile<false, true, kC>(sY, CS, sBK, CS, R0, 16 * tj, 0, kC, z, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[e] = -d[e];
+            vdE[tj] = mma_tile<false, true, DK>(sdW, KS, sBl, KS, R0, 16 * tj, 0, DK, d, lane);
+            vX[tj] = mma_tile<true, false, kC>(sE, CS, sY, CS, R0, 16 * tj, lo_k, kC, z, lane);
+        }
+    }
+    lds_barrier();  // Yc and BK are read
+    uint16_t *sdE = sBK;
+    {
+        const int row = R0 + r16;
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj)
+            store4(sdE + row * CS + 16 * tj + 4 * g4, vdE[tj][0], vdE[tj][1], vdE[tj][2], vdE[tj][3]);
+    }
+    lds_barrier();
+    // Z = E^T dE
+    f32x4 vZ[4];
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) vZ[tj] = mma_tile<true, false, kC>(sE, CS, sdE, CS, R0, 16 * tj, lo_k, kC, z, lane);
+    lds_barrier();  // dE is read
+    uint16_t *sZ = sAqk, *sX = sBK;
+    {
+        const int row = R0 + r16;
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+            float xv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xv[e] = 16 * tj + 4 * g4 + e < row ? vX[tj][e] : 0.f;
+            const int o = row * CS + 16 * tj + 4 * g4;
+            store4(sZ + o, vZ[tj][0], vZ[tj][1], vZ[tj][2], vZ[tj][3]);
+            store4(sX + o, xv[0], xv[1], xv[2], xv[3]);
+        }
+    }
+    lds_barrier();
+    // dF = -Z E^T (strictly lower)
+    f32x4 vF[4];
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+        vF[tj] = z;
+        if (tj <= wave) vF[tj] = mma_tile<false, true, kC>(sZ, CS, sE, CS, R0, 16 * tj, 0, kC, z, lane);
+    }
+    lds_barrier();  // Z is read
+    uint16_t *sdF = sAqk;
+    {
+        const int row = R0 + r16;
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+            float fv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) fv[e] = 16 * tj + 4 * g4 + e < row ? -vF[tj][e] : 0.f;
+            store4(sdF + row * CS + 16 * tj + 4 * g4, fv[0], fv[1], fv[2], fv[3]);
+        }
+    }
+    lds_barrier();
+
+    // ---- final products -------------------------------------------------------------------
+    const bool ok_row = R0 + r16 < m;
+    const size_t th_row = (size_t)(tok0 + (ok_row ? R0 + r16 : 0)) * H + h;
+    uint2 xq[NT], xk[NT], xa[NT], xb[NT];
+#pragma unroll
+    for (int tn = 0; tn < NT; ++tn) {
+        const size_t o = th_row * DK + 16 * tn + 4 * g4;
+        xq[tn] = *(const uint2 *)(p.q + o);
+        xk[tn] = *(const uint2 *)(p.k + o);
+        xa[tn] = *(const uint2 *)(p.a + o);
+        xb[tn] = *(const uint2 *)(p.b + o);
+    }
+    f32x4 gQ[NT], gB[NT], gK[NT], gA[NT];
+    {
+        const int row = R0 + r16;
+        float dgp[NT][4];
+#pragma unroll
+        for (int tn = 0; tn < NT; ++tn) {
+            const int n0 = 16 * tn;
+            f32x4 q2 = mma_tile<false, false, kC>(sOV, CS, sKr, KS, R0, n0, 0, kC, aQ[tn], lane);
+            gQ[tn] = mma_tile<false, false, kC>(sON, CS, sAr, KS, R0, n0, 0, kC, q2, lane);
+            f32x4 b2 = mma_tile<true, false, kC>(sE, CS, sdW, KS, R0, n0, lo_k, kC, z, lane);
+            const f32x4 xk2 = mma_tile<false, false, kC>(sX, CS, sKr, KS, R0, n0, 0, kC, z, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b2[e] -= xk2[e];
+            gB[tn] = mma_tile<false, false, kC>(sdF, CS, sAr, KS, R0, n0, 0, kC, b2, lane);
+            f32x4 k2 = mma_tile<true, false, kC>(sOV, CS, sQl, KS, R0, n0, lo_k, kC, aKs[tn], lane);
+            const f32x4 xb2 = mma_tile<true, false, kC>(sX, CS, sBl, KS, R0, n0, lo_k, kC, z, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) k2[e] -= xb2[e];
+            gK[tn] = k2;
+            f32x4 a2 = mma_tile<true, false, kC>(sON, CS, sQl, KS, R0, n0, lo_k, kC, aAs[tn], lane);
+            gA[tn] = mma_tile<true, false, kC>(sdF, CS, sBl, KS, R0, n0, lo_k, kC, a2, lane);
+            // last-row term: sum over rows of K-> (V' dSg) + A-> (N dSg)
+            const uint2 kr = *(const uint2 *)(sKr + row * KS + n0 + 4 * g4);
+            const uint2 ar = *(const uint2 *)(sAr + row * KS + n0 + 4 * g4);
+            dgp[tn][0] = bf16_lo(kr.x) * aKs[tn][0] + bf16_lo(ar.x) * aAs[tn][0];
+            dgp[tn][1] = bf16_hi(kr.x) * aKs[tn][1] + bf16_hi(ar.x) * aAs[tn][1];
+            dgp[tn][2] = bf16_lo(kr.y) * aKs[tn][2] + bf16_lo(ar.y) * aAs[tn][2];
+            dgp[tn][3] = bf16_hi(kr.y) * aKs[tn][3] + bf16_hi(ar.y) * aAs[tn][3];
+        }
+#pragma unroll
+        for (int tn = 0; tn < NT; ++tn)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float sgm = group_sum<16>(dgp[tn][e]);
+                if (r16 == 0) atomicAdd(&sDg[16 * tn + 4 * g4 + e], sgm);
+            }
+    }
+    lds_barrier();  // the operand arrays are free: Gamma over K->, A->, dg over Q<-, B<-
+
+    // ---- chain rule through Gamma, suffix sums -------------------------------------------
+    float *sGm = (float *)(smem + L::oKr);
+    float *sDl = (float *)(smem + L::oQB);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) sGm[(8 * rg + i) * DK + c0 + e] = g[i][e];
+    lds_barrier();
+    {
+        const int row = R0 + r16;
+        const uint32_t keep = ok_row ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int tn = 0; tn < NT; ++tn) {
+            const int col = 16 * tn + 4 * g4;
+            const uint2 w4[4] = {xq[tn], xk[tn], xa[tn], xb[tn]};
+            float iv[4][4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                iv[u][0] = bf16_lo(w4[u].x & keep); iv[u][1] = bf16_hi(w4[u].x & keep);
+                iv[u][2] = bf16_lo(w4[u].y & keep); iv[u][3] = bf16_hi(w4[u].y & keep);
+            }
+            float oq[4], ok4[4], oa[4], ob[4], dl[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float gv = sGm[row * DK + col + e] * kLog2e;
+                const float G = exp2_fast(gv), iG = exp2_fast(-gv);
+                oq[e] = gQ[tn][e] * G;
+                ob[e] = gB[tn][e] * G;
+                ok4[e] = gK[tn][e] * iG;
+                oa[e] = gA[tn][e] * iG;
+                dl[e] = oq[e] * iv[0][e] + ob[e] * iv[3][e] - ok4[e] * iv[1][e] - oa[e] * iv[2][e];
+            }
+            if (ok_row) {
+                const size_t o = th_row * DK + col;
+                uint2 w;
+                w.x = pack_bf16x2(oq[0], oq[1]); w.y = pack_bf16x2(oq[2], oq[3]);
+                *(uint2 *)(p.dq + o) = w;
+                w.x = pack_bf16x2(ok4[0], ok4[1]); w.y = pack_bf16x2(ok4[2], ok4[3]);
+                *(uint2 *)(p.dk + o) = w;
+                w.x = pack_bf16x2(oa[0], oa[1]); w.y = pack_bf16x2(oa[2], oa[3]);
+                *(uint2 *)(p.da + o) = w;
+                w.x = pack_bf16x2(ob[0], ob[1]); w.y = pack_bf16x2(ob[2], ob[3]);
+                *(uint2 *)(p.db + o) = w;
+            }
+            *(float4 *)(sDl + row * DK + col) = make_float4(dl[0], dl[1], dl[2], dl[3]);
+        }
+        if (tid < kC && tid < m) p.dbeta[(size_t)(tok0 + tid) * H + h] = sDb[tid];
+    }
+    lds_barrier();
+    if (GATE == kGateChannel) {
+        constexpr int NP = kThreads / DK, RP = kC / NP;
+        const int col = tid % DK, part = tid / DK;
+        float ps = 0.f;
+        for (int r = part * RP; r < (part + 1) * RP; ++r) ps += sDl[r * DK + col];
+        sGp[part * DK + col] = ps;
+        lds_barrier();
+        float acc = sDg[col];
+        for (int p2 = part + 1; p2 < NP; ++p2) acc += sGp[p2 * DK + col];
+        for (int r = (part + 1) * RP - 1; r >= part * RP; --r) {
+            acc += sDl[r * DK + col];
+            if (r < m) p.dla[((size_t)(tok0 + r) * H + h) * DK + col] = acc;
+        }
+    } else if (GATE == kGateHead) {
+        {
+            const int row = tid >> 2, q4 = tid & 3;
+            float sacc = 0.f;
+            for (int col = q4; col < DK; col += 4) sacc += sDl[row * DK + col];
+            if (row == kC - 1)
+                for (int col = q4; col < DK; col += 4) sacc += sDg[col];
+            sacc += dpp<kDppXor1>(sacc);
+            sacc += dpp<kDppXor2>(sacc);
+            if (q4 == 0) sGp[row] = sacc;
         }
         lds_barrier();
         if (wave == 0) {

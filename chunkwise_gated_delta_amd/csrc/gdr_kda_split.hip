@@ -1068,7 +1068,8 @@ namespace {
 FwdArgs fwd_view(const BwdArgs &b) {
     FwdArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.q = b.q; a.k = b.k; a.v = b.v; a.log_alpha = b.log_alpha; a.beta = b.beta; a.S0 = b.S0;
+    a.q = b.q; a.k = b.k; a.v = b.v; a.a = b.a; a.b = b.b;
+    a.log_alpha = b.log_alpha; a.beta = b.beta; a.S0 = b.S0;
     a.cu_seqlens = b.cu_seqlens;
     a.n_seq = b.n_seq; a.B = b.B; a.H = b.H; a.T = b.T; a.dk = b.dk; a.dv = b.dv; a.C = b.C;
     a.dtype = b.dtype; a.gate = b.gate;
@@ -1085,7 +1086,7 @@ struct BwdLayout {
 BwdLayout bwd_layout(const BwdArgs &b, int N) {
     BwdLayout L;
     const FwdArgs a = fwd_view(b);
-    L.fw = split_layout(a, N, blk_bytes(b.dk, false));
+    L.fw = split_layout(a, N, blk_bytes(b.dk, b.a != nullptr));
     const size_t nblk = (size_t)b.H * L.fw.max_chunks;
     L.bwd_off = L.fw.total;
     L.s_off = L.bwd_off + nblk * blk_bytes(b.dk, true);
@@ -1176,6 +1177,7 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
     SplitParams sp;
     std::memset(&sp, 0, sizeof(sp));
     sp.q = (const bf16 *)b.q; sp.k = (const bf16 *)b.k; sp.v = (const bf16 *)b.v;
+    sp.a = (const bf16 *)b.a; sp.b = (const bf16 *)b.b;
     sp.la = b.log_alpha; sp.beta = b.beta; sp.S0 = b.S0; sp.cu = b.cu_seqlens;
     sp.err = (int *)ws;
     sp.coff = varlen ? (int32_t *)(ws + lay.fw.coff_off) : nullptr;
@@ -1196,6 +1198,8 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
     std::memset(&bp, 0, sizeof(bp));
     bp.q = (const bf16 *)b.q; bp.k = (const bf16 *)b.k; bp.v = (const bf16 *)b.v;
     bp.dO = (const bf16 *)b.dO; bp.la = b.log_alpha; bp.beta = b.beta;
+    bp.a = (const bf16 *)b.a; bp.b = (const bf16 *)b.b;
+    bp.da = (bf16 *)b.grad_a; bp.db = (bf16 *)b.grad_b;
     bp.S = (const uint16_t *)(ws + lay.s_off); bp.dS = (const uint16_t *)(ws + lay.ds_off);
     bp.dq = (bf16 *)b.grad_q; bp.dk = (bf16 *)b.grad_k; bp.dv = (bf16 *)b.grad_v;
     bp.dla = b.grad_la; bp.dbeta = b.grad_beta;
@@ -1205,27 +1209,33 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
 
     if (varlen) hipLaunchKernelGGL((chunk_plan_kernel<SplitParams>), dim3(1), dim3(kPlanThreads), 0, s, sp);
     const long njobs = (long)b.H * max_chunks;
-    const long slots = 2L * compute_units();
+    const bool dp = b.a != nullptr;
+    const long slots = (dp ? 1L : 2L) * compute_units();  // resident prep workgroups per CU
     const dim3 grid_prep((unsigned)(njobs < slots ? njobs : slots));
     const dim3 grid_state((unsigned)(((n_seq_eff * b.H + 7) / 8) * 8 * sp.n_tiles));
     const dim3 grid_jobs((unsigned)njobs);
-#define GDR_BWD(DK, G)                                                                             \
+#define GDR_BWD(DK, G, D, POST)                                                                    \
     do {                                                                                           \
-        hipLaunchKernelGGL((kda_prep_kernel<DK, G, false, false>), grid_prep, dim3(kThreads), 0, s, sp); \
-        hipLaunchKernelGGL((kda_state_kernel<DK, false, kSaveStates>), grid_state, dim3(kThreads), 0, s, sp); \
-        hipLaunchKernelGGL((kda_bwd_reorder_kernel<DK>), grid_jobs, dim3(kThreads), 0, s,             \
+        hipLaunchKernelGGL((kda_prep_kernel<DK, G, D, false>), grid_prep, dim3(kThreads), 0, s, sp);  \
+        hipLaunchKernelGGL((kda_state_kernel<DK, D, kSaveStates>), grid_state, dim3(kThreads), 0, s, sp); \
+        hipLaunchKernelGGL((kda_bwd_reorder_kernel<DK, D>), grid_jobs, dim3(kThreads), 0, s,       \
                            (const char *)sp.blk, rp.blk, (int)njobs);                              \
         hipLaunchKernelGGL((kda_state_kernel<DK, true, kReverse>), grid_state, dim3(kThreads), 0, s, rp); \
-        hipLaunchKernelGGL((kda_bwd_post_kernel<DK, G>), grid_jobs, dim3(kThreads), 0, s, bp);      \
+        hipLaunchKernelGGL((POST<DK, G>), grid_jobs, dim3(kThreads), 0, s, bp);                   \
     } while (0)
-#define GDR_BWD_GATES(DK)                                            \
-    do {                                                             \
-        if (b.gate == kGateChannel) GDR_BWD(DK, kGateChannel);       \
-        else if (b.gate == kGateHead) GDR_BWD(DK, kGateHead);        \
-        else GDR_BWD(DK, kGateNone);                                 \
+#define GDR_BWD_GATES(DK, D, POST)                                        \
+    do {                                                                  \
+        if (b.gate == kGateChannel) GDR_BWD(DK, kGateChannel, D, POST);   \
+        else if (b.gate == kGateHead) GDR_BWD(DK, kGateHead, D, POST);    \
+        else GDR_BWD(DK, kGateNone, D, POST);                             \
     } while (0)
-    if (b.dk == 128) GDR_BWD_GATES(128);
-    else GDR_BWD_GATES(64);
+    if (dp) {
+        if (b.dk == 128) GDR_BWD_GATES(128, true, kda_bwd_post_dplr_kernel);
+        else GDR_BWD_GATES(64, true, kda_bwd_post_dplr_kernel);
+    } else {
+        if (b.dk == 128) GDR_BWD_GATES(128, false, kda_bwd_post_kernel);
+        else GDR_BWD_GATES(64, false, kda_bwd_post_kernel);
+    }
 #undef GDR_BWD_GATES
 #undef GDR_BWD
     return (int)hipGetLastError();

@@ -50,9 +50,9 @@ def load_library(path: str = LIB_PATH):
         lib.gdr_chunk_fwd_workspace.restype = Z
         lib.gdr_chunk_fwd_workspace.argtypes = [I] * 10
         lib.gdr_chunk_bwd.restype = I
-        lib.gdr_chunk_bwd.argtypes = [P] * 15 + [I] * 9 + [P, Z, P]
+        lib.gdr_chunk_bwd.argtypes = [P] * 19 + [I] * 9 + [P, Z, P]
         lib.gdr_chunk_bwd_workspace.restype = Z
-        lib.gdr_chunk_bwd_workspace.argtypes = [I] * 9
+        lib.gdr_chunk_bwd_workspace.argtypes = [I] * 10
         lib.gdr_workspace_error.restype = I
         lib.gdr_workspace_error.argtypes = [P, P]
         lib.gdr_status_string.restype = ctypes.c_char_p
@@ -189,22 +189,24 @@ def check_workspace_error(workspace: Optional[torch.Tensor] = None, device=None)
 
 
 def bwd_workspace_bytes(B, H, T, dk, dv, C=64, n_seq=0, dtype=torch.bfloat16,
-                        gate=GATE_CHANNEL) -> int:
+                        gate=GATE_CHANNEL, has_ab=False) -> int:
     """Workspace bytes of chunk_bwd for these arguments; 0 if unsupported."""
     lib = load_library()
-    return int(lib.gdr_chunk_bwd_workspace(B, H, T, dk, dv, C, n_seq, _dtype_code(dtype), gate))
+    return int(lib.gdr_chunk_bwd_workspace(B, H, T, dk, dv, C, n_seq, _dtype_code(dtype), gate,
+                                           int(bool(has_ab))))
 
 
 def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
               dO: torch.Tensor, log_alpha: Optional[torch.Tensor] = None,
+              a: Optional[torch.Tensor] = None, b: Optional[torch.Tensor] = None,
               S0: Optional[torch.Tensor] = None, dS_final: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
               want_dS0: bool = True, workspace: Optional[torch.Tensor] = None) -> dict:
-    """Gradients of <dO, O> + <dS_final, S_final> for chunk_fwd in its KDA form (a = b = None).
+    """Gradients of <dO, O> + <dS_final, S_final> for chunk_fwd.
 
     Shapes as in chunk_fwd; dO like O, dS_final like S_final (None: zero).
-    Returns a dict with dq, dk, dv (q's dtype), dbeta, dlog_alpha (when a gate is
-    given) and dS0 (fp32, when want_dS0).
+    Returns a dict with dq, dk, dv (q's dtype), dbeta, da and db (with a, b),
+    dlog_alpha (when a gate is given) and dS0 (fp32, when want_dS0).
     """
     lib = load_library()
     if not q.is_cuda:
@@ -212,7 +214,7 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q.dtype)
-    tensors = dict(q=q, k=k, v=v, beta=beta, dO=dO, log_alpha=log_alpha, S0=S0,
+    tensors = dict(q=q, k=k, v=v, a=a, b=b, beta=beta, dO=dO, log_alpha=log_alpha, S0=S0,
                    dS_final=dS_final, cu_seqlens=cu_seqlens)
     for name, t in tensors.items():
         if t is None:
@@ -221,8 +223,12 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
             raise ValueError(f"{name} is on {t.device}, q on {q.device}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if k.shape != q.shape or k.dtype != q.dtype:
-        raise ValueError("k must match q in shape and dtype")
+    for name in ("k", "a", "b"):
+        t = tensors[name]
+        if t is not None and (t.shape != q.shape or t.dtype != q.dtype):
+            raise ValueError(f"{name} must match q in shape and dtype")
+    if (a is None) != (b is None):
+        raise ValueError("give both a and b, or neither")
     if v.shape[:3] != q.shape[:3] or v.dtype != q.dtype:
         raise ValueError("v must be [B, T, H, dv] in q's dtype")
     if dO.shape != v.shape or dO.dtype != q.dtype:
@@ -248,23 +254,29 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     for name, t in (("S0", S0), ("dS_final", dS_final)):
         if t is not None and (t.shape != (N, H, dv, dk) or t.dtype != torch.float32):
             raise ValueError(f"{name} must be [{N}, {H}, {dv}, {dk}] float32")
-    need = int(lib.gdr_chunk_bwd_workspace(B, H, T, dk, dv, chunk_size, n_seq, dt, gate))
+    need = int(lib.gdr_chunk_bwd_workspace(B, H, T, dk, dv, chunk_size, n_seq, dt, gate,
+                                           int(a is not None)))
     if need == 0:
         raise GdrError(-3, f"no backward kernel for dtype={q.dtype} dk={dk} dv={dv} C={chunk_size}")
     if workspace is None:
         workspace = _workspace(q.device, need)
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
            "dbeta": torch.empty_like(beta)}
+    if a is not None:
+        out["da"] = torch.empty_like(a)
+        out["db"] = torch.empty_like(b)
     if log_alpha is not None:
         out["dlog_alpha"] = torch.empty_like(log_alpha)
     if want_dS0:
         out["dS0"] = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        rc = lib.gdr_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
-                               _ptr(dO), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]),
-                               _ptr(out["dv"]), _ptr(out.get("dlog_alpha")), _ptr(out["dbeta"]),
-                               _ptr(out.get("dS0")), _ptr(cu_seqlens), n_seq, B, H, T, dk, dv,
+        rc = lib.gdr_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha),
+                               _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]),
+                               _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out.get("da")),
+                               _ptr(out.get("db")), _ptr(out.get("dlog_alpha")),
+                               _ptr(out["dbeta"]), _ptr(out.get("dS0")), _ptr(cu_seqlens),
+                               n_seq, B, H, T, dk, dv,
                                chunk_size, dt, gate, _ptr(workspace), workspace.numel(),
                                ctypes.c_void_p(stream))
     if rc != 0:

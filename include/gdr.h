@@ -122,24 +122,26 @@ int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
                   size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace gdr_chunk_bwd needs (arguments as for
- * gdr_chunk_fwd_workspace, without a and b).  Returns 0 when the arguments are
- * invalid or unsupported.  Zero-fill a workspace before its first use. */
+ * gdr_chunk_fwd_workspace).  Returns 0 when the arguments are invalid or
+ * unsupported.  Zero-fill a workspace before its first use. */
 size_t gdr_chunk_bwd_workspace(int B, int H, int T, int dk, int dv, int C, int n_seq, int dtype,
-                               int gate);
+                               int gate, int has_ab);
 
-/* The backward pass of gdr_chunk_fwd in its KDA form (a = b = NULL: a = k,
- * b = beta k; KDA, Gated DeltaNet and DeltaNet by the gate layout): the
- * gradients of L = <dO, O> + <dS_final, S_final> with respect to every input,
- * by the chunk-form backward of the "Kimi Delta Attention backward" notes (a
- * reverse serial pass over the chunks for dL/dS, then the per-chunk gradients
- * of the WY factors, the triangular inverse, the gate and beta).  The forward
- * quantities it needs are recomputed from the inputs.
+/* The backward pass of gdr_chunk_fwd: the gradients of
+ * L = <dO, O> + <dS_final, S_final> with respect to every input.  Without a, b
+ * (KDA, Gated DeltaNet, DeltaNet) it follows the chunk-form backward of the
+ * "Kimi Delta Attention backward" notes; with a, b the gated DPLR backward of the
+ * "Diagonal Plus Low Rank" notes (section 3), beta scaling the write term as in
+ * the forward.  A reverse serial pass over the chunks gives dL/dS, then each
+ * chunk's gradients of the WY factors, the triangular inverse, beta and the gate.
+ * The forward quantities it needs are recomputed from the inputs.
  *
- *   q, k, v, log_alpha, beta, S0, cu_seqlens, n_seq, B, H, T, dk, dv, C, gate
+ *   q, k, v, a, b, log_alpha, beta, S0, cu_seqlens, n_seq, B, H, T, dk, dv, C, gate
  *               as for gdr_chunk_fwd (gate: a layout; GDR_GATE_CLIP is unsupported)
  *   dO          [B, T, H, dv]  dtype          dL/dO
  *   dS_final    [N, H, dv, dk] fp32 or NULL   dL/dS_final (NULL: zero)
  *   dq, dk, dv  shapes of q, k, v, dtype      outputs
+ *   da, db      shapes of a, b, dtype         outputs; NULL exactly when a, b are
  *   dlog_alpha  shape of log_alpha, fp32      output; NULL exactly when gate is NONE
  *   dbeta       [B, T, H]      fp32           output
  *   dS0         [N, H, dv, dk] fp32 or NULL   output dL/dS0
@@ -147,12 +149,12 @@ size_t gdr_chunk_bwd_workspace(int B, int H, int T, int dk, int dv, int C, int n
  * Supported: bf16, C = 64, dk in {64, 128}, dv a multiple of 32 up to 256.
  * Outputs may not overlap inputs, each other or the workspace.  Memory,
  * streams and errors as for gdr_chunk_fwd. */
-int gdr_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
-                  const float *beta, const float *S0, const void *dO, const float *dS_final,
-                  void *dq, void *dk, void *dv, float *dlog_alpha, float *dbeta, float *dS0,
-                  const int32_t *cu_seqlens, int n_seq, int B, int H, int T, int dk_, int dv_,
-                  int C, int dtype, int gate, void *workspace, size_t workspace_bytes,
-                  void *stream);
+int gdr_chunk_bwd(const void *q, const void *k, const void *v, const void *a, const void *b,
+                  const float *log_alpha, const float *beta, const float *S0, const void *dO,
+                  const float *dS_final, void *dq, void *dk, void *dv, void *da, void *db,
+                  float *dlog_alpha, float *dbeta, float *dS0, const int32_t *cu_seqlens,
+                  int n_seq, int B, int H, int T, int dk_, int dv_, int C, int dtype, int gate,
+                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* Synchronises `stream`, returns the sticky device error flag of `workspace`
  * (0: none; 1: malformed cu_seqlens were clamped) and clears it.  Returns

@@ -79,6 +79,17 @@ def _call(lib, q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), a=None, b=None,
                              P(cu), n_seq, B, H, T, dk, dv, C, dtype, gate, P(ws), ws_bytes, None)
 
 
+def test_backward_workspace_sizes(lib):
+    # bf16, C = 64 only; DPLR needs larger forward blocks than KDA
+    kda = lib.gdr_chunk_bwd_workspace(2, 4, 300, 128, 128, 64, 0, 1, 2, 0)
+    dplr = lib.gdr_chunk_bwd_workspace(2, 4, 300, 128, 128, 64, 0, 1, 2, 1)
+    assert kda > 0 and dplr > kda
+    assert lib.gdr_chunk_bwd_workspace(2, 4, 300, 128, 128, 32, 0, 1, 2, 0) == 0  # C
+    assert lib.gdr_chunk_bwd_workspace(2, 4, 300, 128, 128, 64, 0, 0, 2, 0) == 0  # fp32
+    assert lib.gdr_chunk_bwd_workspace(2, 4, 300, 96, 128, 64, 0, 1, 2, 0) == 0   # dk
+    assert lib.gdr_chunk_bwd_workspace(2, 4, 300, 128, 128, 64, 0, 1, 2 | gdr.GATE_CLIP, 0) == 0
+
+
 def test_clip_flag_accepted_with_every_layout(lib):
     # the clip flag changes no buffer size: same workspace as the plain layout
     for dt, C, ab in [(1, 64, 0), (1, 64, 1), (0, 32, 0), (1, 16, 1)]:

@@ -39,21 +39,22 @@ def _cotangents(P, seed, ds_scale=0.5):
 def _gpu_bwd(P, dO, dSf, device="cuda"):
     to = lambda t: None if t is None else t.to(device)
     g = gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), log_alpha=to(P.log_alpha),
-                      S0=to(P.S0), dS_final=to(dSf), cu_seqlens=to(P.cu_seqlens),
-                      chunk_size=P.chunk)
+                      a=to(P.a), b=to(P.b), S0=to(P.S0), dS_final=to(dSf),
+                      cu_seqlens=to(P.cu_seqlens), chunk_size=P.chunk)
     torch.cuda.synchronize()
     return {key: val.to(torch.float64).cpu().numpy() for key, val in g.items()}
 
 
 def _oracle_bwd(P, dO, dSf, chains=None):
     return oracle.recurrence_bwd(f64(P.q), f64(P.k), f64(P.v), f64(P.beta), f64(dO),
-                                 log_alpha=f64(P.log_alpha), S0=f64(P.S0), dS_final=f64(dSf),
+                                 log_alpha=f64(P.log_alpha), a=f64(P.a), b=f64(P.b),
+                                 S0=f64(P.S0), dS_final=f64(dSf),
                                  cu_seqlens=None if P.cu_seqlens is None else P.cu_seqlens.numpy(),
                                  chains=chains)
 
 
 def _check(P, got, ref, keys=None):
-    keys = keys or [k for k in ("dq", "dk", "dv", "dbeta", "dlog_alpha", "dS0") if k in ref]
+    keys = keys or [k for k in ("dq", "dk", "dv", "da", "db", "dbeta", "dlog_alpha", "dS0") if k in ref]
     errs = {}
     for key in keys:
         errs[key] = rel_err(got[key], ref[key])
@@ -94,18 +95,45 @@ def test_bwd_varlen_with_empty_and_short_sequences():
     _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))
 
 
-def test_bwd_full_size_sampled():
-    P = inputs.make_problem("kda")
+@pytest.mark.parametrize("kind", ["kda", "dplr"])
+def test_bwd_full_size_sampled(kind):
+    P = inputs.make_problem(kind)
     dO, dSf = _cotangents(P, 740, ds_scale=0.1)
-    chains = [(0, 0), (1, 31)]
+    chains = [(0, 0), (1, 31)] if kind == "kda" else [(0, 0), (0, 11)]
     got = _gpu_bwd(P, dO, dSf)
     ref = _oracle_bwd(P, dO, dSf, chains=chains)
     for key in got:
         assert np.isfinite(got[key]).all(), key
     sel = {}
-    for key in ("dq", "dk", "dv", "dbeta", "dlog_alpha"):
+    for key in [k for k in ("dq", "dk", "dv", "da", "db", "dbeta", "dlog_alpha") if k in got]:
         sel[key] = (np.concatenate([got[key][n, :, h].ravel() for n, h in chains]),
                     np.concatenate([ref[key][n, :, h].ravel() for n, h in chains]))
     sel["dS0"] = (np.concatenate([got["dS0"][n, h].ravel() for n, h in chains]),
                   np.concatenate([ref["dS0"][n, h].ravel() for n, h in chains]))
     _check(P, {k: v[0] for k, v in sel.items()}, {k: v[1] for k, v in sel.items()})
+
+
+# ---------------------------------------------------------------------------
+# Gated DPLR form (a, b given)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("gate", [0, 1, 2])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 96)])
+def test_bwd_dplr_gates_and_head_sizes(gate, dk, dv):
+    P = inputs.make_problem("dplr", B=2, H=2, T=200, dk=dk, dv=dv, gate=gate, s0_scale=0.3)
+    dO, dSf = _cotangents(P, 750 + gate + dk + dv)
+    _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))
+
+
+@pytest.mark.parametrize("T", [1, 17, 65, 130])
+def test_bwd_dplr_ragged_lengths(T):
+    P = inputs.make_problem("dplr", B=2, H=2, T=T, s0_scale=0.3)
+    dO, dSf = _cotangents(P, 760 + T)
+    _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))
+
+
+def test_bwd_dplr_varlen_gdn2_form():
+    # packed sequences down to an empty one, per-sequence initial state, GDN2-form inputs
+    P = inputs.make_problem("kda_varlen", n_seq=6, total=520, min_len=1, H=3, dplr=True)
+    P.cu_seqlens = torch.tensor([0, 1, 65, 65, 200, 329, 520], dtype=torch.int32)
+    dO, dSf = _cotangents(P, 770)
+    _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))
