@@ -223,7 +223,10 @@ def backward_counts(P):
     FLOP per token-head, the chunk products of the backward notes as full tiles:
     30*C*d + 10*d^2 + 4*C^2 (the per-chunk gradients: fifteen C x C x d and five
     C x d x d products, two C x C x C), 6*d^2 (the reverse state pass) and the
-    forward quantities it recomputes, 10*C*d + 6*d^2.
+    forward quantities it recomputes, 10*C*d + 6*d^2.  With a and b (DPLR) the call
+    also reads a, b and writes da, db (es*d each), and the per-chunk gradients are
+    44*C*d + 14*d^2 + 10*C^2 (twenty-two C x C x d, seven C x d x d and five
+    C x C x C products), plus the DPLR forward recompute, 18*C*d + 8*d^2.
     """
     th = P.B * P.T * P.H
     d, C = P.dk, P.chunk
@@ -232,6 +235,9 @@ def backward_counts(P):
     per_th = es * (2 * P.dk + 2 * P.dv) + es * (2 * P.dk + P.dv) + 2 * gate_bytes + 8
     state = P.n_seq * P.H * P.dv * P.dk * 4 * (2 + (P.S0 is not None))
     flops_th = 30 * C * d + 10 * d * d + 4 * C * C + 6 * d * d + 10 * C * d + 6 * d * d
+    if P.a is not None:
+        per_th += 4 * es * P.dk
+        flops_th = 44 * C * d + 14 * d * d + 10 * C * C + 6 * d * d + 18 * C * d + 8 * d * d
     return th * per_th + state, th * flops_th
 
 
@@ -247,9 +253,10 @@ def bench_backward(args):
     dev = torch.device("cuda", 0)
     to = lambda t: None if t is None else t.to(dev)
     q, k, v, beta, la = to(P.q), to(P.k), to(P.v), to(P.beta), to(P.log_alpha)
+    a, b = to(P.a), to(P.b)
     S0, cu, dOd, dSd = to(P.S0), to(P.cu_seqlens), to(dO), to(dSf)
-    call = lambda: gdr.chunk_bwd(q, k, v, beta, dOd, log_alpha=la, S0=S0, dS_final=dSd,
-                                 cu_seqlens=cu, chunk_size=P.chunk)
+    call = lambda: gdr.chunk_bwd(q, k, v, beta, dOd, log_alpha=la, a=a, b=b, S0=S0,
+                                 dS_final=dSd, cu_seqlens=cu, chunk_size=P.chunk)
     for _ in range(args.warmup):
         g = call()
     torch.cuda.synchronize()
@@ -295,7 +302,8 @@ def bench_backward(args):
         cu_np = None if P.cu_seqlens is None else P.cu_seqlens.numpy()
         t = time.perf_counter()
         ref = oracle.recurrence_bwd(f64(P.q), f64(P.k), f64(P.v), f64(P.beta), f64(dO),
-                                    log_alpha=f64(P.log_alpha), S0=f64(P.S0), dS_final=f64(dSf),
+                                    log_alpha=f64(P.log_alpha), a=f64(P.a), b=f64(P.b),
+                                    S0=f64(P.S0), dS_final=f64(dSf),
                                     cu_seqlens=cu_np, chains=chains, n_threads=2)
         dt = time.perf_counter() - t
         if cu_np is None:
