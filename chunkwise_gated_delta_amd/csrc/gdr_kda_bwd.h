@@ -237,7 +237,6 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         pf.v = *(const uint4 *)(p.v + off);  // rows past the end are zeroed when stored
         pf.o = *(const uint4 *)(p.dO + off);
     };
-    issue(0);
 
     // ---- gate: g for rows 8rg + i, channels c0 + e (natural log, inclusive prefix) ----
     const int rg = tid >> 5, c0 = CPT * (tid & 31);
@@ -294,8 +293,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     // ---- stage 0: scaled operands ---------------------------------------------------
     float g[8][CPT];  // kept for the chain rule at the end
     {
-        gate(g);
-        if (tid < kC) sBeta[tid] = tid < m ? p.beta[(size_t)(tok0 + tid) * H + h] : 0.f;
+        // q, k and then log alpha are loaded together (one memory round trip); the first
+        // dv tile is requested only after them, so that waiting for them does not wait
+        // for it
         constexpr int WPR = CPT / 2;  // bf16 words per row and thread
         uint32_t qw[8][WPR], kw[8][WPR];
 #pragma unroll
@@ -309,10 +309,15 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
                 qw[i][0] = *(const uint32_t *)(p.q + th * DK + c0);
                 kw[i][0] = *(const uint32_t *)(p.k + th * DK + c0);
             }
-            if (r >= m)
+        }
+        gate(g);
+        issue(0);
+        if (tid < kC) sBeta[tid] = tid < m ? p.beta[(size_t)(tok0 + tid) * H + h] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (8 * rg + i >= m)
 #pragma unroll
                 for (int w = 0; w < WPR; ++w) qw[i][w] = kw[i][w] = 0u;
-        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * rg + i;
@@ -695,19 +700,34 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     }
     lds_barrier();
     if (GATE == kGateChannel) {
-        // suffix sums over the 64 rows, per column: kThreads / DK parts of rows, part
-        // totals through LDS, then each part walks its rows backwards
-        constexpr int NP = kThreads / DK, RP = kC / NP;
-        const int col = tid % DK, part = tid / DK;
-        float ps = 0.f;
-        for (int r = part * RP; r < (part + 1) * RP; ++r) ps += sDl[r * DK + col];
-        sGp[part * DK + col] = ps;
+        // suffix sums over the 64 rows, four columns per thread: kThreads / (DK / 4) parts
+        // of rows, part totals through LDS, then each part walks its rows backwards
+        // (at most 8 parts: sGp holds 8 rows of DK)
+        constexpr int NP = kThreads / (DK / 4) < 8 ? kThreads / (DK / 4) : 8, RP = kC / NP;
+        const int col = 4 * (tid % (DK / 4)), part = tid / (DK / 4);
+        const bool act = part < NP;
+        if (act) {
+            float4 ps = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int r = part * RP; r < (part + 1) * RP; ++r) {
+                const float4 x = *(const float4 *)(sDl + r * DK + col);
+                ps.x += x.x; ps.y += x.y; ps.z += x.z; ps.w += x.w;
+            }
+            *(float4 *)(sGp + part * DK + col) = ps;
+        }
         lds_barrier();
-        float acc = sDg[col];  // the last-row term
-        for (int p2 = part + 1; p2 < NP; ++p2) acc += sGp[p2 * DK + col];
-        for (int r = (part + 1) * RP - 1; r >= part * RP; --r) {
-            acc += sDl[r * DK + col];
-            if (r < m) p.dla[((size_t)(tok0 + r) * H + h) * DK + col] = acc;
+        if (act) {
+            float4 acc = *(const float4 *)(sDg + col);  // the last-row term
+            for (int p2 = part + 1; p2 < NP; ++p2) {
+                const float4 x = *(const float4 *)(sGp + p2 * DK + col);
+                acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+            }
+#pragma unroll
+            for (int r = (part + 1) * RP - 1; r >= part * RP; --r) {
+                const float4 x = *(const float4 *)(sDl + r * DK + col);
+                acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+                if (r < m) *(float4 *)(p.dla + ((size_t)(tok0 + r) * H + h) * DK + col) = acc;
+            }
         }
     } else if (GATE == kGateHead) {
         // row sums (four threads per row), the last-row term on row 63, then a suffix
@@ -847,10 +867,28 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
         pf.v = *(const uint4 *)(p.v + off);
         pf.o = *(const uint4 *)(p.dO + off);
     };
-    issue(0);
 
-    // ---- gate (rows 8rg + i, channels c0 + e) ------------------------------------------
+    // ---- inputs: q, b, k, a of this thread's rows and channels, then log alpha (one
+    // memory round trip); the first dv tile is requested after them ------------------------
     const int rg = tid >> 5, c0 = CPT * (tid & 31);
+    auto load_rows = [&](const bf16 *x, uint32_t (&xw)[8][WPR]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * rg + i;
+            const size_t th = (size_t)(tok0 + (r < m ? r : 0)) * H + h;
+            if constexpr (WPR == 2) {
+                const uint2 a2 = *(const uint2 *)(x + th * DK + c0);
+                xw[i][0] = a2.x; xw[i][WPR - 1] = a2.y;
+            } else {
+                xw[i][0] = *(const uint32_t *)(x + th * DK + c0);
+            }
+        }
+    };
+    uint32_t iq[8][WPR], ib[8][WPR], ik[8][WPR], ia[8][WPR];
+    load_rows(p.q, iq);
+    load_rows(p.b, ib);
+    load_rows(p.k, ik);
+    load_rows(p.a, ia);
     float g[8][CPT];
     {
         float la[8][CPT];
@@ -899,34 +937,21 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
             for (int i = 0; i < 8; ++i) g[i][e] += carry;
         }
     }
-    // Q<-, B<- (scale e^g) or K->, A-> (scale e^-g) of two inputs, bf16 into LDS
-    auto scaled = [&](const bf16 *x, const bf16 *y, uint16_t *dx, uint16_t *dy, bool up) {
-        uint32_t xw[8][WPR], yw[8][WPR];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 8 * rg + i;
-            const size_t th = (size_t)(tok0 + (r < m ? r : 0)) * H + h;
-            if constexpr (WPR == 2) {
-                const uint2 a2 = *(const uint2 *)(x + th * DK + c0), b2 = *(const uint2 *)(y + th * DK + c0);
-                xw[i][0] = a2.x; xw[i][WPR - 1] = a2.y; yw[i][0] = b2.x; yw[i][WPR - 1] = b2.y;
-            } else {
-                xw[i][0] = *(const uint32_t *)(x + th * DK + c0);
-                yw[i][0] = *(const uint32_t *)(y + th * DK + c0);
-            }
-            if (r >= m)
-#pragma unroll
-                for (int w = 0; w < WPR; ++w) xw[i][w] = yw[i][w] = 0u;
-        }
+    issue(0);
+    // Q<-, B<- (scale e^g) or K->, A-> (scale e^-g) of two loaded inputs, bf16 into LDS
+    auto scaled = [&](const uint32_t (&xw)[8][WPR], const uint32_t (&yw)[8][WPR], uint16_t *dx,
+                      uint16_t *dy, bool up) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * rg + i;
             uint32_t ox[WPR], oy[WPR];
+            const uint32_t keep = 8 * rg + i < m ? 0xffffffffu : 0u;  // rows past the end are zero
 #pragma unroll
             for (int w = 0; w < WPR; ++w) {
                 const float s0 = up ? g[i][2 * w] : -g[i][2 * w], s1 = up ? g[i][2 * w + 1] : -g[i][2 * w + 1];
                 const float e0 = exp2_fast(s0 * kLog2e), e1 = exp2_fast(s1 * kLog2e);
-                ox[w] = pack_bf16x2(bf16_lo(xw[i][w]) * e0, bf16_hi(xw[i][w]) * e1);
-                oy[w] = pack_bf16x2(bf16_lo(yw[i][w]) * e0, bf16_hi(yw[i][w]) * e1);
+                ox[w] = pack_bf16x2(bf16_lo(xw[i][w] & keep) * e0, bf16_hi(xw[i][w] & keep) * e1);
+                oy[w] = pack_bf16x2(bf16_lo(yw[i][w] & keep) * e0, bf16_hi(yw[i][w] & keep) * e1);
             }
             if constexpr (WPR == 2) {
                 *(uint2 *)(dx + r * KS + c0) = make_uint2(ox[0], ox[WPR - 1]);
@@ -937,8 +962,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
             }
         }
     };
-    scaled(p.q, p.b, sQl, sBl, true);
-    scaled(p.k, p.a, sKr, sAr, false);
+    scaled(iq, ib, sQl, sBl, true);
+    scaled(ik, ia, sKr, sAr, false);
     if (rg == 7)
 #pragma unroll
         for (int e = 0; e < CPT; ++e) sGam[c0 + e] = exp2_fast(g[7][e] * kLog2e);
@@ -1178,7 +1203,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
         dbp += __shfl_xor(dbp, 32);
         if (g4 == 0) sDb[row] = dbp;
     }
-    scaled(p.q, p.b, sQl, sBl, true);
+    load_rows(p.q, iq);  // Q<-, B<- again, over the dv-tile buffers
+    load_rows(p.b, ib);
+    scaled(iq, ib, sQl, sBl, true);
     lds_barrier();
     // dE = -Yc BK^T + dW B<-^T;  X = E^T Yc (strictly lower)
     f32x4 vdE[4], vX[4];
@@ -1342,17 +1369,34 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
     }
     lds_barrier();
     if (GATE == kGateChannel) {
-        constexpr int NP = kThreads / DK, RP = kC / NP;
-        const int col = tid % DK, part = tid / DK;
-        float ps = 0.f;
-        for (int r = part * RP; r < (part + 1) * RP; ++r) ps += sDl[r * DK + col];
-        sGp[part * DK + col] = ps;
+        // suffix sums over the 64 rows, four columns per thread: kThreads / (DK / 4) parts
+        // of rows, part totals through LDS, then each part walks its rows backwards
+        // (at most 8 parts: sGp holds 8 rows of DK)
+        constexpr int NP = kThreads / (DK / 4) < 8 ? kThreads / (DK / 4) : 8, RP = kC / NP;
+        const int col = 4 * (tid % (DK / 4)), part = tid / (DK / 4);
+        const bool act = part < NP;
+        if (act) {
+            float4 ps = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int r = part * RP; r < (part + 1) * RP; ++r) {
+                const float4 x = *(const float4 *)(sDl + r * DK + col);
+                ps.x += x.x; ps.y += x.y; ps.z += x.z; ps.w += x.w;
+            }
+            *(float4 *)(sGp + part * DK + col) = ps;
+        }
         lds_barrier();
-        float acc = sDg[col];
-        for (int p2 = part + 1; p2 < NP; ++p2) acc += sGp[p2 * DK + col];
-        for (int r = (part + 1) * RP - 1; r >= part * RP; --r) {
-            acc += sDl[r * DK + col];
-            if (r < m) p.dla[((size_t)(tok0 + r) * H + h) * DK + col] = acc;
+        if (act) {
+            float4 acc = *(const float4 *)(sDg + col);  // the last-row term
+            for (int p2 = part + 1; p2 < NP; ++p2) {
+                const float4 x = *(const float4 *)(sGp + p2 * DK + col);
+                acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+            }
+#pragma unroll
+            for (int r = (part + 1) * RP - 1; r >= part * RP; --r) {
+                const float4 x = *(const float4 *)(sDl + r * DK + col);
+                acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+                if (r < m) *(float4 *)(p.dla + ((size_t)(tok0 + r) * H + h) * DK + col) = acc;
+            }
         }
     } else if (GATE == kGateHead) {
         {
