@@ -202,30 +202,46 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     float *sGp = (float *)(smem + L::oGp), *sDb = (float *)(smem + L::oDb);
     float *sDg = (float *)(smem + L::oDg);
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r16 = lane & 15, g4 = lane >> 4;
     const int H = p.H, DV = p.dv_;
-    const int job = blockIdx.x;
-    const int h = job % H;
-    int n = 0, c = 0;
-    if (!chunk_of(p, job / H, n, c)) return;  // workgroup-uniform
-    long t0, t1;
-    seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
-    const long tok0 = t0 + (long)c * kC;
-    const int m = (int)((t1 - tok0) < kC ? (t1 - tok0) : kC);
-    const size_t sbase = (size_t)(job / H) * H + h;  // (chunk, head) index of the state buffers
-    const int R0 = 16 * wave;                        // this wave's 16 rows of every row-block output
+    const int R0 = 16 * wave;  // this wave's 16 rows of every row-block output
+    const int rg = tid >> 5, c0 = CPT * (tid & 31);
+    constexpr int WPR = CPT / 2;  // bf16 words per row and thread in the gate layout
 
-    // Global loads of one dv tile (S_p and dS_n rows j0..j0+31, value and dO tiles),
-    // issued a tile ahead so that their latency overlaps the previous tile's products.
+    // The grid is persistent: workgroup w takes jobs (chunk, head) w, w + gridDim.x, ...
+    // While one job finishes, the next job's inputs are already being loaded.
+    struct Job {
+        int job, h, m;
+        long tok0;
+        size_t sbase;  // (chunk, head) index of the state buffers
+        bool ok;
+    };
+    auto decode = [&](int job) {
+        Job J;
+        J.job = job;
+        J.h = job % H;
+        J.m = 1;
+        J.tok0 = 0;
+        J.sbase = (size_t)job;
+        int n = 0, c = 0;
+        J.ok = job < p.H * p.max_chunks && chunk_of(p, job / H, n, c);
+        if (J.ok) {
+            long t0, t1;
+            seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
+            J.tok0 = t0 + (long)c * kC;
+            J.m = (int)((t1 - J.tok0) < kC ? (t1 - J.tok0) : kC);
+        }
+        return J;
+    };
+    // One dv tile's S_p and dS_n rows j0..j0+31, value and dO tiles, loaded a tile ahead.
     constexpr int kSPT = 32 * DK / 8 / kThreads;  // 16-byte pieces of a state tile per thread
     struct Tile {
         uint4 s[kSPT], d[kSPT], v, o;
     } pf;
-    auto issue = [&](int j0) {
-        const uint16_t *ps = p.S + (sbase * DV + j0) * DK;
-        const uint16_t *pd = p.dS + (sbase * DV + j0) * DK;
+    auto issue = [&](const Job &J, int j0) {
+        const uint16_t *ps = p.S + (J.sbase * DV + j0) * DK;
+        const uint16_t *pd = p.dS + (J.sbase * DV + j0) * DK;
 #pragma unroll
         for (int i = 0; i < kSPT; ++i) {
             const int idx = tid + kThreads * i, r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
@@ -233,40 +249,68 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             pf.d[i] = *(const uint4 *)(pd + (size_t)r * DK + c8);
         }
         const int r = tid >> 2, c8 = 8 * (tid & 3);
-        const size_t off = ((size_t)(tok0 + (r < m ? r : 0)) * H + h) * DV + j0 + c8;
+        const size_t off = ((size_t)(J.tok0 + (r < J.m ? r : 0)) * H + J.h) * DV + j0 + c8;
         pf.v = *(const uint4 *)(p.v + off);  // rows past the end are zeroed when stored
         pf.o = *(const uint4 *)(p.dO + off);
     };
-
-    // ---- gate: g for rows 8rg + i, channels c0 + e (natural log, inclusive prefix) ----
-    const int rg = tid >> 5, c0 = CPT * (tid & 31);
-    auto gate = [&](float (&g)[8][CPT]) {
-        // all eight rows' log alpha are loaded before the sums use them
+    // A job's q, k and log alpha in the gate layout (rows 8rg + i, channels c0 + e) and
+    // beta of row tid; rows past the end are zeroed where they are used.
+    struct In {
+        uint32_t qw[8][WPR], kw[8][WPR];
         float la[8][CPT];
+        float beta;
+    } in;
+    auto load_in = [&](const Job &J) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * rg + i;
-            const size_t th = (size_t)(tok0 + (r < m ? r : 0)) * H + h;
-#pragma unroll
-            for (int e = 0; e < CPT; ++e) la[i][e] = 0.f;
+            const size_t th = (size_t)(J.tok0 + (r < J.m ? r : 0)) * H + J.h;
+            if constexpr (WPR == 2) {
+                const uint2 qa = *(const uint2 *)(p.q + th * DK + c0), ka = *(const uint2 *)(p.k + th * DK + c0);
+                in.qw[i][0] = qa.x; in.qw[i][WPR - 1] = qa.y; in.kw[i][0] = ka.x; in.kw[i][WPR - 1] = ka.y;
+            } else {
+                in.qw[i][0] = *(const uint32_t *)(p.q + th * DK + c0);
+                in.kw[i][0] = *(const uint32_t *)(p.k + th * DK + c0);
+            }
             if (GATE == kGateChannel) {
                 if constexpr (CPT == 4) {
                     const float4 x = *(const float4 *)(p.la + th * DK + c0);
-                    la[i][0] = x.x; la[i][CPT > 1 ? 1 : 0] = x.y;
-                    la[i][CPT > 2 ? 2 : 0] = x.z; la[i][CPT > 3 ? 3 : 0] = x.w;
+                    in.la[i][0] = x.x; in.la[i][CPT > 1 ? 1 : 0] = x.y;
+                    in.la[i][CPT > 2 ? 2 : 0] = x.z; in.la[i][CPT > 3 ? 3 : 0] = x.w;
                 } else {
                     const float2 x = *(const float2 *)(p.la + th * DK + c0);
-                    la[i][0] = x.x; la[i][CPT > 1 ? 1 : 0] = x.y;
+                    in.la[i][0] = x.x; in.la[i][CPT > 1 ? 1 : 0] = x.y;
                 }
             } else if (GATE == kGateHead) {
                 const float x = p.la[th];
 #pragma unroll
-                for (int e = 0; e < CPT; ++e) la[i][e] = x;
-            }
-            if (r >= m)
+                for (int e = 0; e < CPT; ++e) in.la[i][e] = x;
+            } else {
 #pragma unroll
-                for (int e = 0; e < CPT; ++e) la[i][e] = 0.f;
+                for (int e = 0; e < CPT; ++e) in.la[i][e] = 0.f;
+            }
         }
+        in.beta = p.beta[(size_t)(J.tok0 + (tid < J.m ? tid : 0)) * H + J.h];
+    };
+
+    Job J = decode(blockIdx.x);
+    if (J.ok) {
+        load_in(J);
+        issue(J, 0);
+    }
+    while (J.ok) {  // workgroup-uniform
+    const Job Nx = decode(J.job + gridDim.x);  // the next job
+    // lane indices are re-derived each job so that the compiler keeps no per-lane
+    // addresses alive across jobs
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+    const int rg = tid >> 5, c0 = CPT * (tid & 31);  // the gate layout, as in load_in
+    const int h = J.h, m = J.m;
+    const long tok0 = J.tok0;
+
+    // ---- gate: g for rows 8rg + i, channels c0 + e (natural log, inclusive prefix) ----
+    auto gate = [&](float (&g)[8][CPT]) {
         float run[CPT];
 #pragma unroll
         for (int e = 0; e < CPT; ++e) run[e] = 0.f;
@@ -274,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int e = 0; e < CPT; ++e) {
-                run[e] += la[i][e];
+                run[e] += 8 * rg + i < m ? in.la[i][e] : 0.f;
                 g[i][e] = run[e];
             }
 #pragma unroll
@@ -293,31 +337,17 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     // ---- stage 0: scaled operands ---------------------------------------------------
     float g[8][CPT];  // kept for the chain rule at the end
     {
-        // q, k and then log alpha are loaded together (one memory round trip); the first
-        // dv tile is requested only after them, so that waiting for them does not wait
-        // for it
-        constexpr int WPR = CPT / 2;  // bf16 words per row and thread
+        gate(g);
+        if (tid < kC) sBeta[tid] = tid < m ? in.beta : 0.f;
         uint32_t qw[8][WPR], kw[8][WPR];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 8 * rg + i;
-            const size_t th = (size_t)(tok0 + (r < m ? r : 0)) * H + h;
-            if constexpr (WPR == 2) {
-                const uint2 a = *(const uint2 *)(p.q + th * DK + c0), b = *(const uint2 *)(p.k + th * DK + c0);
-                qw[i][0] = a.x; qw[i][WPR - 1] = a.y; kw[i][0] = b.x; kw[i][WPR - 1] = b.y;
-            } else {
-                qw[i][0] = *(const uint32_t *)(p.q + th * DK + c0);
-                kw[i][0] = *(const uint32_t *)(p.k + th * DK + c0);
-            }
-        }
-        gate(g);
-        issue(0);
-        if (tid < kC) sBeta[tid] = tid < m ? p.beta[(size_t)(tok0 + tid) * H + h] : 0.f;
-#pragma unroll
         for (int i = 0; i < 8; ++i)
-            if (8 * rg + i >= m)
 #pragma unroll
-                for (int w = 0; w < WPR; ++w) qw[i][w] = kw[i][w] = 0u;
+            for (int w = 0; w < WPR; ++w) {
+                const bool ok = 8 * rg + i < m;
+                qw[i][w] = ok ? in.qw[i][w] : 0u;
+                kw[i][w] = ok ? in.kw[i][w] : 0u;
+            }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * rg + i;
@@ -484,7 +514,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             *(uint4 *)(sV + r * VS + c8) = make_uint4(pf.v.x & keep, pf.v.y & keep, pf.v.z & keep, pf.v.w & keep);
             *(uint4 *)(sdO + r * VS + c8) = make_uint4(pf.o.x & keep, pf.o.y & keep, pf.o.z & keep, pf.o.w & keep);
         }
-        if (j0 + 32 < DV) issue(j0 + 32);
+        if (j0 + 32 < DV) issue(J, j0 + 32);
+        else if (Nx.ok) issue(Nx, 0);  // the next job's first tile
         lds_barrier();
         // V_new = Ab V - W S_p^T and dV_new = K-> dSg^T + A_qk^T dO, rows R0..R0+15
         {
@@ -698,6 +729,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         }
         if (tid < kC && tid < m) p.dbeta[(size_t)(tok0 + tid) * H + h] = sDb[tid];
     }
+    if (Nx.ok) load_in(Nx);  // the next job's q, k, log alpha, beta
     lds_barrier();
     if (GATE == kGateChannel) {
         // suffix sums over the 64 rows, four columns per thread: kThreads / (DK / 4) parts
@@ -752,6 +784,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             }
             if (lane < m) p.dla[(size_t)(tok0 + lane) * H + h] = x;
         }
+    }
+    lds_barrier();  // the next job overwrites LDS
+    J = Nx;
     }
 }
 

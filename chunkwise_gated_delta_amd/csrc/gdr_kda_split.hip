@@ -1214,6 +1214,9 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
     const dim3 grid_prep((unsigned)(njobs < slots ? njobs : slots));
     const dim3 grid_state((unsigned)(((n_seq_eff * b.H + 7) / 8) * 8 * sp.n_tiles));
     const dim3 grid_jobs((unsigned)njobs);
+    // the KDA gradient kernel is persistent: one workgroup per CU (its LDS allows no more)
+    const long cus = compute_units();
+    const dim3 grid_post(dp ? grid_jobs : dim3((unsigned)(njobs < cus ? njobs : cus)));
 #define GDR_BWD(DK, G, D, POST)                                                                    \
     do {                                                                                           \
         hipLaunchKernelGGL((kda_prep_kernel<DK, G, D, false>), grid_prep, dim3(kThreads), 0, s, sp);  \
@@ -1221,7 +1224,7 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
         hipLaunchKernelGGL((kda_bwd_reorder_kernel<DK, D>), grid_jobs, dim3(kThreads), 0, s,       \
                            (const char *)sp.blk, rp.blk, (int)njobs);                              \
         hipLaunchKernelGGL((kda_state_kernel<DK, true, kReverse>), grid_state, dim3(kThreads), 0, s, rp); \
-        hipLaunchKernelGGL((POST<DK, G>), grid_jobs, dim3(kThreads), 0, s, bp);                   \
+        hipLaunchKernelGGL((POST<DK, G>), grid_post, dim3(kThreads), 0, s, bp);                   \
     } while (0)
 #define GDR_BWD_GATES(DK, D, POST)                                        \
     do {                                                                  \
