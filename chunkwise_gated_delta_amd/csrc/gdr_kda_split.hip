@@ -37,6 +37,7 @@
 // S = (S + V'^T K-> + N^T A->) Diag(gamma_C), with V' = Diag(beta) V.  The prep kernel hands its results over in the
 // operand order of v_mfma_f32_32x32x16_bf16, so the state kernel loads them straight
 // into registers with whole-wave contiguous loads.
+#include <cstdlib>
 #include <cstring>
 #include <type_traits>
 
@@ -90,6 +91,14 @@ struct SplitParams {
     int C;           // chunk size (always kC here)
     int nc;          // chunks per sequence (fixed-length batch)
     int max_chunks;  // blocks per head in the workspace
+    // Segmented state pass (seg_n >= 3; 0 otherwise): each (sequence, head) chain is cut
+    // into seg_n runs of chunks.  The map a run applies to the state is affine,
+    // S_end = S_start P + R, so phase 1 runs run 0 as usual (its end state is the start
+    // of run 1) next to runs 1 .. seg_n-2 from a zero state (R) and from the identity
+    // with zero values (P); seg_combine_kernel chains the maps into the start states;
+    // phase 2 runs 1 .. seg_n-1 from those with the output.
+    int seg_n, seg_phase;
+    float *seg_ws;  // fp32 per chain: start states of runs 1..n-1, then R and P of runs 1..n-2
 };
 
 // ---------------------------------------------------------------------------------
@@ -821,19 +830,22 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, lh = lane >> 5;
     const int H = p.H, DV = p.dv;
-    // Workgroups go to the 8 XCDs round-robin by block index.  A (sequence, head)
-    // group is the n_tiles workgroups that read the same chunk operands, so they are
-    // kept on one XCD (one L2); groups, longest sequence first, are dealt to the XCDs
-    // in turn so that every XCD gets an equal share of the long ones.  The grid is
-    // padded to a multiple of 8 groups; the padding exits at once.
+    // Workgroups go to the 8 XCDs round-robin by block index.  A group is the workgroups
+    // that read the same chunk operands (the n_tiles dv tiles of a (sequence, head)
+    // chain, or of one run of it), so they are kept on one XCD (one L2); groups, longest
+    // sequence first, are dealt to the XCDs in turn so that every XCD gets an equal share
+    // of the long ones.  The grid is padded to a multiple of 8 groups; the padding exits
+    // at once.
+    const int runs = p.seg_n > 1 ? p.seg_n - 1 : 1;  // groups per chain
+    const int tpg = p.seg_phase == 1 ? p.n_tiles + NSW : p.n_tiles;  // workgroups per group
     const int pos = blockIdx.x >> 3;
-    const int grp = (pos / p.n_tiles) * 8 + (blockIdx.x & 7);
-    if (grp >= p.n_seq * H) return;
-    const int tile = pos % p.n_tiles;
-    const int h = grp % H;
-    const int rank = grp / H;
+    const int grp = (pos / tpg) * 8 + (blockIdx.x & 7);
+    if (grp >= p.n_seq * H * runs) return;
+    const int tile = pos % tpg;
+    const int chain = grp / runs;
+    const int h = chain % H;
+    const int rank = chain / H;
     const int n = p.order ? p.order[rank] : rank;
-    const int j0 = tile * kDVT;
     long t0, t1;
     seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
     int nck = (int)((t1 - t0 + kC - 1) / kC);
@@ -845,6 +857,50 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     } else {
         cbase = (long)n * p.nc;
     }
+
+    // What this workgroup computes: its rows j0.. of a state-like matrix, where it starts
+    // (s_in rows, the identity, or zero), where its end state goes, and whether the values
+    // are read and the output and per-step states are written.
+    int j0 = tile * kDVT;
+    const float *s_in = p.S0 ? p.S0 + ((size_t)n * H + h) * DV * DK : nullptr;
+    float *s_out = p.Sf ? p.Sf + ((size_t)n * H + h) * DV * DK : nullptr;
+    bool ident = false, vzero = false, emit = true;
+    if (p.seg_n > 1) {
+        const int G = p.seg_n;
+        const int g = grp % runs + (p.seg_phase == 1 ? 0 : 1);  // run of this group
+        const size_t mat = (size_t)DV * DK;
+        float *ws = p.seg_ws + ((size_t)n * H + h) * ((size_t)(2 * G - 3) * mat + (size_t)(G - 2) * DK * DK);
+        float *start = ws;                          // start state of run g at start + (g-1) mat
+        float *R = ws + (size_t)(G - 1) * mat;      // R of run g at R + (g-1) mat
+        float *P = ws + (size_t)(2 * G - 3) * mat;  // P of run g at P + (g-1) DK DK
+        if (p.seg_phase == 1) {
+            if (g == 0) {
+                if (tile >= p.n_tiles) return;
+                s_out = start;  // run 0 as usual; its end is the start of run 1
+            } else if (tile < p.n_tiles) {
+                s_in = nullptr;  // R: from zero
+                s_out = R + (size_t)(g - 1) * mat;
+                emit = false;
+            } else {
+                j0 = (tile - p.n_tiles) * kDVT;  // P: rows of the dk x dk map, from I
+                s_in = nullptr;
+                s_out = P + (size_t)(g - 1) * DK * DK;
+                ident = vzero = true;
+                emit = false;
+            }
+        } else {
+            s_in = start + (size_t)(g - 1) * mat;
+            if (g < G - 1) s_out = nullptr;
+        }
+        // chunks of run g (counted from the end in reverse mode)
+        const int len = (nck + G - 1) / G;
+        const int a0 = g * len < nck ? g * len : nck, a1 = (g + 1) * len < nck ? (g + 1) * len : nck;
+        const int lo = MODE == kReverse ? nck - a1 : a0;
+        cbase += lo;
+        t0 += (long)lo * kC;
+        nck = a1 - a0;
+    }
+    const int jv = vzero ? 0 : j0;  // dv column of the value loads (any, when unused)
 
     const int rt = wave & 1;      // 32-row tile of the chunk
     const bool vw = wave < 2;     // V_new waves (W', Ab); waves 2, 3: output (Q~, Ao)
@@ -860,7 +916,12 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
         for (int q = 0; q < 4; ++q) {
             const int dk = 32 * wave + 8 * q + 4 * lh;
             float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (p.S0) s4 = *(const float4 *)(p.S0 + (((size_t)n * H + h) * DV + j0 + l32) * DK + dk);
+            if (s_in) s4 = *(const float4 *)(s_in + (size_t)(j0 + l32) * DK + dk);
+            if (ident) {
+                const int r = j0 + l32;
+                s4 = make_float4(r == dk ? 1.f : 0.f, r == dk + 1 ? 1.f : 0.f, r == dk + 2 ? 1.f : 0.f,
+                                 r == dk + 3 ? 1.f : 0.f);
+            }
             ST[4 * q + 0] = s4.x; ST[4 * q + 1] = s4.y; ST[4 * q + 2] = s4.z; ST[4 * q + 3] = s4.w;
             store4(sS + l32 * KS + dk, s4.x, s4.y, s4.z, s4.w);
         }
@@ -895,7 +956,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
             }
         }
         const long tok = t0 + (long)cid(c) * kC + vr;
-        x.V = *(const uint4 *)(p.v + ((size_t)(tok < t1 ? tok : t1 - 1) * H + h) * DV + j0 + vc);
+        x.V = *(const uint4 *)(p.v + ((size_t)(tok < t1 ? tok : t1 - 1) * H + h) * DV + jv + vc);
         if (wave == 0 && lane < DK / 4) x.G = ((const float4 *)(bp + Bk::oG))[lane];
     };
 
@@ -907,7 +968,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
             const int r = 16 * i + (lane >> 2), q4 = lane & 3;
             const long tok = t0 + (long)c * kC + 32 * rt + r;
             const uint4 o = *(const uint4 *)(sO + r * kVS + 8 * q4);
-            if (tok < t1) *(uint4 *)(p.O + ((size_t)tok * H + h) * DV + j0 + 8 * q4) = o;
+            if (tok < t1 && emit) *(uint4 *)(p.O + ((size_t)tok * H + h) * DV + j0 + 8 * q4) = o;
         }
     };
 
@@ -917,14 +978,14 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
         if (wave == 0 && lane < DK / 4) ((float4 *)sG)[lane] = x.G;
         {
             // rows past the end of the sequence are zero (branch-free: a lane mask)
-            const uint32_t keep = 0u - (uint32_t)(t0 + (long)cid(c) * kC + vr < t1);
+            const uint32_t keep = 0u - (uint32_t)(t0 + (long)cid(c) * kC + vr < t1 && !vzero);
             *(uint4 *)(sV + vr * kVS + vc) = make_uint4(x.V.x & keep, x.V.y & keep, x.V.z & keep, x.V.w & keep);
         }
         if (MODE == kForward && !vw && c > 0) store_out(c - 1);
         const int cn = c + kDepth < nck ? c + kDepth : nck - 1;
         load_p(nx, cn);
         lds_barrier();  // value tile, gamma_C and S of chunk c visible
-        if constexpr (MODE != kForward) {
+        if (MODE != kForward && emit) {
             // the state entering this step, bf16, 16 bytes per thread and pass
             uint16_t *dst = p.states + (((size_t)(cbase + cid(c)) * H + h) * DV + j0) * DK;
 #pragma unroll
@@ -1027,14 +1088,52 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
         if (MODE == kForward && !vw) store_out(nck - 1);
     }
 
-    if (p.Sf && wave < NSW) {
+    if (s_out && wave < NSW) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int dk = 32 * wave + 8 * q + 4 * lh;
-            *(float4 *)(p.Sf + (((size_t)n * H + h) * DV + j0 + l32) * DK + dk) =
+            *(float4 *)(s_out + (size_t)(j0 + l32) * DK + dk) =
                 make_float4(ST[4 * q + 0], ST[4 * q + 1], ST[4 * q + 2], ST[4 * q + 3]);
         }
     }
+}
+
+// Start state of run g + 1 of a segmented state pass: S_start(g+1) = S_start(g) P_g + R_g
+// (fp32), one workgroup per (chain, 32 rows of dv, 32 columns of dk); launched for
+// g = 1 .. seg_n-2 in turn.
+template <int DK>
+__global__ __launch_bounds__(kThreads) void seg_combine_kernel(SplitParams p, int g) {
+    constexpr int XS = DK + 4, PS = 32 + 4;  // padded LDS rows
+    __shared__ __attribute__((aligned(16))) float sX[kDVT * XS];
+    __shared__ __attribute__((aligned(16))) float sP[DK * PS];
+    const int tid = threadIdx.x;
+    const int G = p.seg_n, DV = p.dv;
+    const int per_chain = p.n_tiles * (DK / 32);
+    const int chain = blockIdx.x / per_chain, rem = blockIdx.x % per_chain;
+    const int j0 = (rem / (DK / 32)) * kDVT, k0 = (rem % (DK / 32)) * 32;
+    if (chain >= p.n_seq * p.H) return;
+    const size_t mat = (size_t)DV * DK;
+    float *start = p.seg_ws + (size_t)chain * ((size_t)(2 * G - 3) * mat + (size_t)(G - 2) * DK * DK);
+    const float *Xg = start + (size_t)(g - 1) * mat;
+    const float *Rg = start + (size_t)(G - 1) * mat + (size_t)(g - 1) * mat;
+    const float *Pg = start + (size_t)(2 * G - 3) * mat + (size_t)(g - 1) * DK * DK;
+    for (int i = tid; i < kDVT * DK / 4; i += kThreads) {
+        const int row = i / (DK / 4), c4 = 4 * (i % (DK / 4));
+        *(float4 *)(sX + row * XS + c4) = *(const float4 *)(Xg + (size_t)(j0 + row) * DK + c4);
+    }
+    for (int i = tid; i < DK * 8; i += kThreads) {
+        const int row = i >> 3, c4 = 4 * (i & 7);
+        *(float4 *)(sP + row * PS + c4) = *(const float4 *)(Pg + (size_t)row * DK + k0 + c4);
+    }
+    __syncthreads();
+    const int r = tid >> 3, c = 4 * (tid & 7);
+    float4 acc = *(const float4 *)(Rg + (size_t)(j0 + r) * DK + k0 + c);
+    for (int k = 0; k < DK; ++k) {
+        const float x = sX[r * XS + k];
+        const float4 y = *(const float4 *)(sP + k * PS + c);
+        acc.x += x * y.x; acc.y += x * y.y; acc.z += x * y.z; acc.w += x * y.w;
+    }
+    *(float4 *)(start + (size_t)g * mat + (size_t)(j0 + r) * DK + k0 + c) = acc;
 }
 
 // Compute units of the current device (cached per device).
@@ -1049,6 +1148,59 @@ int compute_units() {
         cached[dev] = n;
     }
     return cached[dev];
+}
+
+// Runs per chain for a segmented state pass, or 0 for the plain pass.  A segmented pass
+// takes about 2/G of the plain pass's serial steps; it is used when the plain pass
+// leaves most CUs idle (its first phase, chains x (G-1) x (dv + dk) / 32 workgroups,
+// must fit on the device at once) and the chains are long enough to amortise the two
+// extra launches.  GDR_SEGMENTS=0 in the environment turns it off (the workspace is
+// sized for it either way).
+constexpr int kSegMinChunks = 8, kSegMaxRuns = 8;
+int seg_runs(int chains, int dk, int dv, long chunks_per_chain, bool honour_env) {
+    if (honour_env) {
+        const char *e = std::getenv("GDR_SEGMENTS");
+        if (e && e[0] == '0' && e[1] == 0) return 0;
+    }
+    const long per_group = dv / kDVT + dk / 32;
+    long G = 1 + compute_units() / ((long)chains * per_group);
+    if (chunks_per_chain / kSegMinChunks < G) G = chunks_per_chain / kSegMinChunks;
+    if (G > kSegMaxRuns) G = kSegMaxRuns;
+    return G >= 3 ? (int)G : 0;
+}
+
+// Longest chain in chunks (packed sequences: at most the whole token axis).
+long chunks_per_chain(const FwdArgs &a) { return (a.T + kC - 1) / kC; }
+
+// The segmented-pass area follows the other workspace contents (256-byte aligned).
+size_t seg_offset(size_t total) { return (total + 255) / 256 * 256; }
+
+size_t seg_bytes(int chains, int dk, int dv, int runs) {
+    if (runs < 3) return 0;
+    return (size_t)chains * ((size_t)(2 * runs - 3) * dv * dk + (size_t)(runs - 2) * dk * dk) * 4;
+}
+
+// One state pass: plain, or segmented (phase 1, the map combination, phase 2).
+template <int DK, bool DP, int MODE>
+void run_state(SplitParams sp, int runs, hipStream_t s) {
+    const long chains = (long)sp.n_seq * sp.H;
+    if (runs < 3) {
+        sp.seg_n = sp.seg_phase = 0;
+        const dim3 grid((unsigned)(((chains + 7) / 8) * 8 * sp.n_tiles));
+        hipLaunchKernelGGL((kda_state_kernel<DK, DP, MODE>), grid, dim3(kThreads), 0, s, sp);
+        return;
+    }
+    const long groups = chains * (runs - 1);
+    sp.seg_n = runs;
+    sp.seg_phase = 1;
+    hipLaunchKernelGGL((kda_state_kernel<DK, DP, MODE>), dim3((unsigned)(((groups + 7) / 8) * 8 * (sp.n_tiles + DK / 32))),
+                       dim3(kThreads), 0, s, sp);
+    for (int g = 1; g <= runs - 2; ++g)
+        hipLaunchKernelGGL((seg_combine_kernel<DK>), dim3((unsigned)(chains * sp.n_tiles * (DK / 32))),
+                           dim3(kThreads), 0, s, sp, g);
+    sp.seg_phase = 2;
+    hipLaunchKernelGGL((kda_state_kernel<DK, DP, MODE>), dim3((unsigned)(((groups + 7) / 8) * 8 * sp.n_tiles)),
+                       dim3(kThreads), 0, s, sp);
 }
 
 int blk_bytes(int dk, bool dp) {
@@ -1080,7 +1232,8 @@ FwdArgs fwd_view(const BwdArgs &b) {
 // [S_p states][dS_n states], the states bf16 [chunk][head][dv][dk].
 struct BwdLayout {
     SplitLayout fw;
-    size_t bwd_off, s_off, ds_off, total;
+    size_t bwd_off, s_off, ds_off, seg_off, total;
+    int runs;  // of the segmented state passes (0: plain)
 };
 
 BwdLayout bwd_layout(const BwdArgs &b, int N) {
@@ -1091,7 +1244,9 @@ BwdLayout bwd_layout(const BwdArgs &b, int N) {
     L.bwd_off = L.fw.total;
     L.s_off = L.bwd_off + nblk * blk_bytes(b.dk, true);
     L.ds_off = L.s_off + nblk * b.dv * b.dk * 2;
-    L.total = L.ds_off + nblk * b.dv * b.dk * 2;
+    L.seg_off = seg_offset(L.ds_off + nblk * b.dv * b.dk * 2);
+    L.runs = seg_runs(N * b.H, b.dk, b.dv, chunks_per_chain(a), false);
+    L.total = L.seg_off + seg_bytes(N * b.H, b.dk, b.dv, L.runs);  // shared by both passes
     return L;
 }
 
@@ -1103,7 +1258,10 @@ bool kda_split_supported(const FwdArgs &a) {
 }
 
 size_t kda_split_workspace_bytes(const FwdArgs &a, int n_seq_eff) {
-    return split_layout(a, n_seq_eff, blk_bytes(a.dk, a.a != nullptr)).total;
+    const int chains = n_seq_eff * a.H;
+    const int runs = seg_runs(chains, a.dk, a.dv, chunks_per_chain(a), false);
+    return seg_offset(split_layout(a, n_seq_eff, blk_bytes(a.dk, a.a != nullptr)).total) +
+           seg_bytes(chains, a.dk, a.dv, runs);
 }
 
 int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
@@ -1111,6 +1269,7 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     const SplitLayout lay = split_layout(a, n_seq_eff, blk_bytes(a.dk, a.a != nullptr));
     const int max_chunks = lay.max_chunks;
     SplitParams sp;
+    std::memset(&sp, 0, sizeof(sp));
     sp.q = (const bf16 *)a.q; sp.k = (const bf16 *)a.k; sp.v = (const bf16 *)a.v;
     sp.a = (const bf16 *)a.a; sp.b = (const bf16 *)a.b;
     const bool dp = a.a != nullptr;
@@ -1124,13 +1283,14 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     sp.total = (long)a.B * a.T;
     sp.H = a.H; sp.T = a.T; sp.dv = a.dv; sp.n_seq = n_seq_eff; sp.n_tiles = a.dv / kDVT;
     sp.nc = lay.nc; sp.max_chunks = max_chunks; sp.C = kC;
+    sp.seg_ws = (float *)(ws + seg_offset(lay.total));
+    const int runs = seg_runs(n_seq_eff * a.H, a.dk, a.dv, chunks_per_chain(a), true);
 
     if (varlen) hipLaunchKernelGGL((chunk_plan_kernel<SplitParams>), dim3(1), dim3(kPlanThreads), 0, s, sp);
     // persistent prep workgroups: two per CU (one with a, b: their LDS allows no more)
     const long njobs = (long)a.H * max_chunks;
     const long slots = (dp ? 1L : 2L) * compute_units();
     const dim3 grid_prep((unsigned)(njobs < slots ? njobs : slots));
-    const dim3 grid_state((unsigned)(((n_seq_eff * a.H + 7) / 8) * 8 * sp.n_tiles));
 #define GDR_PREP(DK, G, D, CL) \
     hipLaunchKernelGGL((kda_prep_kernel<DK, G, D, CL>), grid_prep, dim3(kThreads), 0, s, sp)
 #define GDR_GATES(DK, D, CL)                                 \
@@ -1143,7 +1303,7 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     do {                                                                                    \
         if (a.clip) GDR_GATES(DK, D, true);                                                 \
         else GDR_GATES(DK, D, false);                                                       \
-        hipLaunchKernelGGL((kda_state_kernel<DK, D>), grid_state, dim3(kThreads), 0, s, sp); \
+        run_state<DK, D, kForward>(sp, runs, s);                                            \
     } while (0)
     if (a.dk == 128) {
         if (dp) GDR_PATH(128, true);
@@ -1187,6 +1347,8 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
     sp.total = (long)b.B * b.T;
     sp.H = b.H; sp.T = b.T; sp.dv = b.dv; sp.n_seq = n_seq_eff; sp.n_tiles = b.dv / kDVT;
     sp.nc = lay.fw.nc; sp.max_chunks = max_chunks; sp.C = kC;
+    sp.seg_ws = (float *)(ws + lay.seg_off);
+    const int runs = lay.runs ? seg_runs(n_seq_eff * b.H, b.dk, b.dv, chunks_per_chain(fwd_view(b)), true) : 0;
     // the reverse pass: backward blocks, dO as the value tile, dS_final in, dS0 out
     SplitParams rp = sp;
     rp.blk = ws + lay.bwd_off;
@@ -1212,7 +1374,6 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
     const bool dp = b.a != nullptr;
     const long slots = (dp ? 1L : 2L) * compute_units();  // resident prep workgroups per CU
     const dim3 grid_prep((unsigned)(njobs < slots ? njobs : slots));
-    const dim3 grid_state((unsigned)(((n_seq_eff * b.H + 7) / 8) * 8 * sp.n_tiles));
     const dim3 grid_jobs((unsigned)njobs);
     // the KDA gradient kernel is persistent: one workgroup per CU (its LDS allows no more)
     const long cus = compute_units();
@@ -1220,10 +1381,10 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
 #define GDR_BWD(DK, G, D, POST)                                                                    \
     do {                                                                                           \
         hipLaunchKernelGGL((kda_prep_kernel<DK, G, D, false>), grid_prep, dim3(kThreads), 0, s, sp);  \
-        hipLaunchKernelGGL((kda_state_kernel<DK, D, kSaveStates>), grid_state, dim3(kThreads), 0, s, sp); \
+        run_state<DK, D, kSaveStates>(sp, runs, s);                                               \
         hipLaunchKernelGGL((kda_bwd_reorder_kernel<DK, D>), grid_jobs, dim3(kThreads), 0, s,       \
                            (const char *)sp.blk, rp.blk, (int)njobs);                              \
-        hipLaunchKernelGGL((kda_state_kernel<DK, true, kReverse>), grid_state, dim3(kThreads), 0, s, rp); \
+        run_state<DK, true, kReverse>(rp, runs, s);                                               \
         hipLaunchKernelGGL((POST<DK, G>), grid_post, dim3(kThreads), 0, s, bp);                   \
     } while (0)
 #define GDR_BWD_GATES(DK, D, POST)                                        \

@@ -54,8 +54,13 @@ def test_workspace_sizes(lib):
     # ... and, for packed sequences, the chunk offsets and room for every sequence
     # to end in a partial chunk
     assert ws(1, 32, 32768, 128, 128, n_seq=8) == 256 + 256 + 32 * (512 + 8) * 61952
-    # DPLR (bf16, distinct a, b, C = 64): the same blocks plus Diag(beta) K^ (16 KiB)
-    assert ws(1, 16, 16384, 128, 128, has_ab=True) == 256 + 16 * 256 * (61952 + 16384)
+    # DPLR (bf16, distinct a, b, C = 64): the same blocks plus Diag(beta) K^ (16 KiB).
+    # With 16 (sequence, head) chains the state pass is cut into 3 runs (on 256 CUs):
+    # start states of runs 1, 2, and R, P of run 1, fp32 [128][128] each, per chain
+    assert ws(1, 16, 16384, 128, 128, has_ab=True) == \
+        256 + 16 * 256 * (61952 + 16384) + 16 * 4 * 128 * 128 * 4
+    # two chains of 32 chunks: 4 runs (3 start states, 2 R, 2 P per chain)
+    assert ws(1, 2, 2048, 128, 128) == 256 + 2 * 32 * 61952 + 2 * 7 * 128 * 128 * 4
     assert ws(1, 2, 100, 64, 64, has_ab=True) == 256 + 2 * 2 * (37120 + 8192)
     # the fp32 kernels (fp32 inputs, or other chunk sizes with a, b) keep one fp32 block
     # per (chunk, head): W', Q~, K^ (+ Diag(beta) K^) [C][dk], two [C][C], gamma [dk],

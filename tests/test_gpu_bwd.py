@@ -137,3 +137,21 @@ def test_bwd_dplr_varlen_gdn2_form():
     P.cu_seqlens = torch.tensor([0, 1, 65, 65, 200, 329, 520], dtype=torch.int32)
     dO, dSf = _cotangents(P, 770)
     _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))
+
+
+# ---------------------------------------------------------------------------
+# Segmented state passes (few chains, many chunks): both the forward state pass and
+# the reverse one run as side-by-side runs joined through their affine maps
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kind,H,T", [("kda", 2, 1700), ("dplr", 2, 1700), ("dplr", 1, 2600)])
+def test_bwd_segmented_state_passes(kind, H, T):
+    P = inputs.make_problem(kind, B=1, H=H, T=T, s0_scale=0.3)
+    dO, dSf = _cotangents(P, 780 + T)
+    _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))
+
+
+def test_bwd_segmented_varlen():
+    P = inputs.make_problem("kda_varlen", n_seq=3, total=2000, min_len=1, H=2, dplr=True)
+    P.cu_seqlens = torch.tensor([0, 1500, 1500, 2000], dtype=torch.int32)
+    dO, dSf = _cotangents(P, 790)
+    _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))

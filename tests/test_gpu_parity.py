@@ -298,3 +298,40 @@ def test_clip_varlen_with_initial_state():
     P.cu_seqlens = torch.tensor([0, 1, 65, 66, 200, 329, 520], dtype=torch.int32)
     assert P.a is not None and P.S0 is not None
     _check_clip(P)
+
+
+# ---------------------------------------------------------------------------
+# Segmented state pass: with few (sequence, head) chains and many chunks the serial
+# pass is cut into runs that run side by side (the chunk map is affine in the
+# state).  These shapes take that path on a 256-CU device; GDR_SEGMENTS=0 forces
+# the plain pass for the comparison.
+# ---------------------------------------------------------------------------
+SEGMENTED = {
+    "kda": dict(B=1, H=2, T=2048),
+    "gdn": dict(B=1, H=2, T=2000, s0_scale=0.3),
+    "dplr": dict(B=1, H=2, T=2100, s0_scale=0.3),
+    "gdn2_clip": dict(B=1, H=1, T=3000),
+    "dplr_d64_96": dict(B=1, H=2, T=1900, dk=64, dv=96),
+}
+
+
+@pytest.mark.parametrize("case", list(SEGMENTED))
+def test_segmented_state_pass(case, monkeypatch):
+    kind = case.split("_d")[0]
+    P = inputs.make_problem(kind, **SEGMENTED[case])
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+    monkeypatch.setenv("GDR_SEGMENTS", "0")
+    O0, Sf0 = gpu_run(P)
+    _check(P, O0, Sf0)
+    # the two passes differ only in rounding
+    assert rel_err(O, O0) <= TOL[P.dtype] and rel_err(Sf, Sf0) <= TOL[P.dtype]
+
+
+def test_segmented_varlen_with_empty_and_initial_state():
+    P = inputs.make_problem("kda_varlen", n_seq=4, total=2600, min_len=1, H=2, dplr=True)
+    P.cu_seqlens = torch.tensor([0, 1700, 1700, 1765, 2600], dtype=torch.int32)
+    assert P.S0 is not None
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+    np.testing.assert_array_equal(Sf[1], P.S0[1].double().numpy())
