@@ -338,7 +338,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default=WORKLOAD, choices=["kda", "gdn", "dplr", "kda_varlen",
-                                                              "deltanet_f32", "gdn2_clip"],
+                                                              "deltanet_f32", "gdn2_clip", "kda_strong"],
                     help="the benchmark line is for kda; the others time the same call on the "
                          "other workloads (reported under the same keys, metric named per workload)")
     ap.add_argument("--steps", type=int, default=100)

@@ -99,12 +99,17 @@ struct SplitParams {
     // phase 2 runs 1 .. seg_n-1 from those with the output.
     int seg_n, seg_phase;
     float *seg_ws;  // fp32 per chain: start states of runs 1..n-1, then R and P of runs 1..n-2
+    // Per (chunk, head) job: 1 when the chunk's gate range is too wide for the scaled
+    // operands (see kSubGateRange); such jobs are redone by the log-domain prep variant.
+    // NULL: not recorded.
+    int *sub;
+    int wide_err;  // nonzero: OR this into *err when a chunk's gate range is too wide
 };
 
 // ---------------------------------------------------------------------------------
 // Prep kernel
 // ---------------------------------------------------------------------------------
-template <int DK, bool DP>
+template <int DK, bool DP, bool SUB = false>
 struct PrepSmem {
     static constexpr int KS = DK + 8;                   // bf16 row stride of [64][DK] arrays
     static constexpr int CCB = kC * kCS * 2;            // bytes of one bf16 [64][kCS] array
@@ -123,15 +128,21 @@ struct PrepSmem {
     static constexpr int oTot = oLd;                    // fp32 [8][DK] gate partial sums (before oLd is used)
     static constexpr int oBeta = oT + 32 * kTS * 2;     // fp32 [64]
     static constexpr int oG = oBeta + kC * 4;           // fp32 [65]: head-gate prefix sums and total
-    static constexpr int bytes = oG + 80 * 4;
+    static constexpr int GS = DK + 4;                   // SUB: fp32 row stride of the gate array
+    static constexpr int oGf = oG + 80 * 4;             // SUB only: fp32 [64][GS] gate (log2)
+    static constexpr int bytes = oGf + (SUB ? kC * GS * 4 : 0);
     static_assert(8 * DK * 4 <= oBeta - oLd, "gate partial sums fit");
-    static_assert(DP || bytes <= 80 * 1024, "two workgroups per CU");
+    static_assert(DP || SUB || bytes <= 80 * 1024, "two workgroups per CU");
     static_assert(bytes <= 160 * 1024, "one workgroup per CU");
 };
 
-template <int DK, int GATE, bool DP, bool CLIP>
-__global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitParams p) {
-    using L = PrepSmem<DK, DP>;
+// A chunk whose gate falls by more than this (log2 units, any channel) is redone by the
+// SUB variant: the scaled operands K e^-g would leave the bf16/fp32 exponent range.
+constexpr float kSubGateRange = 96.f;
+
+template <int DK, int GATE, bool DP, bool CLIP, bool SUB = false>
+__global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(SplitParams p) {
+    using L = PrepSmem<DK, DP, SUB>;
     using Bk = Blk<DK, DP>;
     constexpr int KS = L::KS;
     constexpr int CPT = DK / 32;  // gate stage: channels per thread
@@ -155,6 +166,7 @@ __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitPar
     float *sTot = (float *)(smem + L::oTot);
     float *sBeta = (float *)(smem + L::oBeta);
     float *sG = (float *)(smem + L::oG);
+    float *sGf = (float *)(smem + L::oGf);  // SUB only
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -318,7 +330,24 @@ __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitPar
         lds_barrier();
     };
 
-    Job cur = decode(blockIdx.x);
+    // SUB: this workgroup's next flagged job at or after g (stride gridDim.x), 64
+    // candidates per round trip; njobs when there is none.
+    auto next_job = [&](int g) {
+        if constexpr (SUB) {
+            while (g < njobs) {  // workgroup-uniform
+                const long gi = (long)g + (long)lane * gridDim.x;
+                const int f = gi < njobs ? p.sub[gi] : 0;
+                const unsigned long long b = __builtin_amdgcn_ballot_w64(f != 0);
+                if (b) return g + (int)__builtin_ctzll(b) * (int)gridDim.x;
+                g += 64 * (int)gridDim.x;
+            }
+            return njobs;
+        } else {
+            return g;
+        }
+    };
+
+    Job cur = decode(next_job(blockIdx.x));
     if (cur.ok) issue(cur);
     while (cur.ok) {  // workgroup-uniform
         // Thread-index values are re-derived from an opaque copy each job: otherwise the
@@ -472,6 +501,19 @@ __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitPar
                 for (int i = 0; i < 8; ++i) g[i][e] = GATE == kGateHead ? sG[8 * rg + i] : 0.f;
             }
         }
+        if constexpr (!SUB) {
+            // wave 0 holds gamma_C of every channel: flag the chunk for the SUB variant
+            if ((p.sub || p.wide_err) && wave == 0) {
+                bool wide = false;
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) wide = wide || !(gC[e] >= -kSubGateRange);
+                const bool any = __builtin_amdgcn_ballot_w64(wide) != 0;
+                if (lane == 0) {
+                    if (p.sub) p.sub[cur.g] = any ? 1 : 0;
+                    if (any && p.wide_err) atomicOr(p.err, p.wide_err);
+                }
+            }
+        }
 
         // ---- scaled operands: Q<-, K<-, K-> to LDS; K^ and gamma_C to the block ---------
         // (DP: Q<-, B<-, K->, A-> to LDS; A^, Diag(beta) K^ and gamma_C to the block)
@@ -495,16 +537,31 @@ __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitPar
                 }
 #pragma unroll
                 for (int e = 0; e < CPT; ++e) {
-                    const float eg = GATE == kGateNone && !CLIP ? 1.f : exp2_fast(g[i][e]);
-                    const float eig = GATE == kGateNone && !CLIP ? 1.f : exp2_fast(-g[i][e]);
-                    const float egc = eig * gam[e];  // e^(g_C - g)
-                    a[e] = (DP ? bv[e] : kv[e]) * eg;
-                    b[e] = kv[e] * eig;
-                    cq[e] = qv[e] * eg;
-                    kh[e][i] = (DP ? av[e] : kv[e]) * egc;
-                    if constexpr (DP) {
-                        ar[e] = av[e] * eig;
-                        kb[e][i] = br * kv[e] * egc;
+                    if constexpr (SUB) {
+                        // raw rows for the log-domain Gram (Q<- and B<- are formed after it);
+                        // e^(g_C - g) directly, since e^-g may overflow here
+                        const float egc = exp2_fast(gC[e] - g[i][e]);
+                        a[e] = DP ? bv[e] : kv[e] * exp2_fast(g[i][e]);
+                        b[e] = kv[e];
+                        cq[e] = qv[e];
+                        kh[e][i] = (DP ? av[e] : kv[e]) * egc;
+                        if constexpr (DP) {
+                            ar[e] = av[e];
+                            kb[e][i] = br * kv[e] * egc;
+                        }
+                        sGf[r * L::GS + c0 + e] = g[i][e];
+                    } else {
+                        const float eg = GATE == kGateNone && !CLIP ? 1.f : exp2_fast(g[i][e]);
+                        const float eig = GATE == kGateNone && !CLIP ? 1.f : exp2_fast(-g[i][e]);
+                        const float egc = eig * gam[e];  // e^(g_C - g)
+                        a[e] = (DP ? bv[e] : kv[e]) * eg;
+                        b[e] = kv[e] * eig;
+                        cq[e] = qv[e] * eg;
+                        kh[e][i] = (DP ? av[e] : kv[e]) * egc;
+                        if constexpr (DP) {
+                            ar[e] = av[e] * eig;
+                            kb[e][i] = br * kv[e] * egc;
+                        }
                     }
                 }
                 uint32_t wa[WPR], wb[WPR], wq[WPR], wr[WPR];
@@ -553,7 +610,7 @@ __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitPar
             }
         }
         // this job's raw inputs are consumed: the next job's start loading
-        const Job nxt = decode(cur.g + gridDim.x);
+        const Job nxt = decode(next_job(cur.g + gridDim.x));
         if (nxt.ok) issue(nxt);
         lds_barrier();
 
@@ -561,6 +618,110 @@ __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitPar
         // (DP: B<- A->^T, B<- K->^T, Q<- K->^T, Q<- A->^T; 40 jobs.)
         // Computed transposed, D[c][r] = K->[c] . (K<- or Q<-)[r], so that each lane holds
         // four consecutive columns of one row.
+        if constexpr (SUB) {
+            // Log-domain Gram (GLA notes, section 5.3, the diagonal sub-chunk form, used for
+            // every pair): x_r . (y_c e^(g_r - g_c)) summed over the channels in fp32 with
+            // the exponent formed as a difference, so nothing overflows however far the
+            // gate falls.  The 10 lower 16x16 tiles are cut into 4x4 blocks of pairs (160
+            // blocks); lanes 2b and 2b+1 sum the two halves of the channels of block b.
+            // Blocks above the diagonal inside a diagonal tile are written as zeros.
+            constexpr int NP = DP ? 4 : 2;  // products: DP: BA, BK, QK, QA; else KK, QK
+            for (int item = tid; item < 320; item += kThreads) {
+                const int bk = item >> 1, half = item & 1;
+                const int t = bk >> 4, u = (bk >> 2) & 3, v = bk & 3;
+                const int ti = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
+                const int tj = t - ti * (ti + 1) / 2;
+                const int r0 = 16 * ti + 4 * u, cb = 16 * tj + 4 * v;
+                const bool live = ti > tj || u >= v;
+                float acc[NP][4][4];
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[pp][i][j] = 0.f;
+                if (live) {
+                    // DP: rows b (sKl), q (sQl); columns a (sAr), k (sKr).  Else: rows k
+                    // (sKr), q (sQl); columns k (sKr).
+                    const uint16_t *rx = DP ? sKl : sKr;
+                    for (int d = half * (DK / 2); d < (half + 1) * (DK / 2); d += 4) {
+                        float gr[4][4], gc[4][4], xr[4][4], qr[4][4], kc[4][4], ac[4][4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float4 a4 = *(const float4 *)(sGf + (r0 + i) * L::GS + d);
+                            const float4 b4 = *(const float4 *)(sGf + (cb + i) * L::GS + d);
+                            gr[i][0] = a4.x; gr[i][1] = a4.y; gr[i][2] = a4.z; gr[i][3] = a4.w;
+                            gc[i][0] = b4.x; gc[i][1] = b4.y; gc[i][2] = b4.z; gc[i][3] = b4.w;
+                            const uint2 x2 = *(const uint2 *)(rx + (r0 + i) * KS + d);
+                            const uint2 q2 = *(const uint2 *)(sQl + (r0 + i) * KS + d);
+                            const uint2 k2 = *(const uint2 *)(sKr + (cb + i) * KS + d);
+                            xr[i][0] = bf16_lo(x2.x); xr[i][1] = bf16_hi(x2.x); xr[i][2] = bf16_lo(x2.y); xr[i][3] = bf16_hi(x2.y);
+                            qr[i][0] = bf16_lo(q2.x); qr[i][1] = bf16_hi(q2.x); qr[i][2] = bf16_lo(q2.y); qr[i][3] = bf16_hi(q2.y);
+                            kc[i][0] = bf16_lo(k2.x); kc[i][1] = bf16_hi(k2.x); kc[i][2] = bf16_lo(k2.y); kc[i][3] = bf16_hi(k2.y);
+                            if constexpr (DP) {
+                                const uint2 a2 = *(const uint2 *)(sAr + (cb + i) * KS + d);
+                                ac[i][0] = bf16_lo(a2.x); ac[i][1] = bf16_hi(a2.x); ac[i][2] = bf16_lo(a2.y); ac[i][3] = bf16_hi(a2.y);
+                            }
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) {
+                                    // pairs above the diagonal are discarded: keep them finite
+                                    const float x = exp2_fast(fminf(gr[i][e] - gc[j][e], 0.f));
+                                    const float xk = kc[j][e] * x;
+                                    if constexpr (DP) {
+                                        const float xa = ac[j][e] * x;
+                                        acc[0][i][j] += xr[i][e] * xa;
+                                        acc[1][i][j] += xr[i][e] * xk;
+                                        acc[2][i][j] += qr[i][e] * xk;
+                                        acc[3][i][j] += qr[i][e] * xa;
+                                    } else {
+                                        acc[0][i][j] += xr[i][e] * xk;
+                                        acc[1][i][j] += qr[i][e] * xk;
+                                    }
+                                }
+                    }
+                }
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[pp][i][j] += dpp<kDppXor1>(acc[pp][i][j]);
+                if (half == 0) {
+                    const float4 bc = *(const float4 *)(sBeta + cb);
+                    const float bcv[4] = {bc.x, bc.y, bc.z, bc.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = r0 + i;
+                        const float br = DP ? 1.f : sBeta[r];
+                        float lv[4], av[4], bkv[4], qav[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int c = cb + j;
+                            lv[j] = c < r ? br * acc[0][i][j] : 0.f;  // L (DP: B<- A->^T)
+                            if constexpr (DP) {
+                                bkv[j] = c < r ? bcv[j] * acc[1][i][j] : 0.f;
+                                av[j] = c <= r ? bcv[j] * acc[2][i][j] : 0.f;
+                                qav[j] = c <= r ? acc[3][i][j] : 0.f;
+                            } else {
+                                av[j] = c <= r ? acc[1][i][j] : 0.f;
+                            }
+                        }
+                        if (ti == tj) *(float4 *)(sLd + r * kDS + 4 * v) = make_float4(lv[0], lv[1], lv[2], lv[3]);
+                        else store4(sX + r * kCS + cb, lv[0], lv[1], lv[2], lv[3]);
+                        store4(sAqk + r * kCS + cb, av[0], av[1], av[2], av[3]);
+                        if constexpr (DP) {
+                            store4(sBK + r * kCS + cb, bkv[0], bkv[1], bkv[2], bkv[3]);
+                            store4(sAqa + r * kCS + cb, qav[0], qav[1], qav[2], qav[3]);
+                        }
+                    }
+                }
+            }
+        } else
         for (int jb = wave; jb < (DP ? 40 : 20); jb += 4) {
             const int pr = jb / 10;  // product
             const bool isA = !DP && pr == 1;
@@ -595,6 +756,24 @@ __global__ __launch_bounds__(kThreads, DP ? 1 : 2) void kda_prep_kernel(SplitPar
             }
         }
         lds_barrier();
+        if constexpr (SUB) {
+            // Q<- (DP: and B<-) from the raw rows, now that the Gram has read them; later
+            // stages read them after further barriers
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * rg + i;
+#pragma unroll
+                for (int e = 0; e < CPT; e += 2) {
+                    const float e0 = exp2_fast(g[i][e]), e1 = exp2_fast(g[i][e + 1]);
+                    uint32_t *pq = (uint32_t *)(sQl + r * KS + c0 + e);
+                    *pq = pack_bf16x2(bf16_lo(*pq) * e0, bf16_hi(*pq) * e1);
+                    if constexpr (DP) {
+                        uint32_t *pb = (uint32_t *)(sKl + r * KS + c0 + e);
+                        *pb = pack_bf16x2(bf16_lo(*pb) * e0, bf16_hi(*pb) * e1);
+                    }
+                }
+            }
+        }
 
         // ---- At, diagonal blocks: forward substitution (wave 0) ------------------------
         // Lane (block lg, column l16): x_r = [r == col] - sum_{i<r} L[r][i] x_i, which
@@ -1257,16 +1436,32 @@ bool kda_split_supported(const FwdArgs &a) {
            (a.dk == 64 || a.dk == 128) && a.dv % kDVT == 0;
 }
 
-size_t kda_split_workspace_bytes(const FwdArgs &a, int n_seq_eff) {
+// Forward workspace: the split layout, then the per-job flags of the log-domain prep
+// (gated forms only), then the segmented-pass area.
+struct KdaWs {
+    SplitLayout lay;
+    size_t sub_off, seg_off, total;
+    bool sub;
+    int runs;
+};
+KdaWs kda_ws(const FwdArgs &a, int n_seq_eff) {
+    KdaWs w;
+    w.lay = split_layout(a, n_seq_eff, blk_bytes(a.dk, a.a != nullptr));
+    w.sub = a.gate != kGateNone || a.clip;
+    w.sub_off = seg_offset(w.lay.total);
+    w.seg_off = seg_offset(w.sub_off + (w.sub ? (size_t)a.H * w.lay.max_chunks * 4 : 0));
     const int chains = n_seq_eff * a.H;
-    const int runs = seg_runs(chains, a.dk, a.dv, chunks_per_chain(a), false);
-    return seg_offset(split_layout(a, n_seq_eff, blk_bytes(a.dk, a.a != nullptr)).total) +
-           seg_bytes(chains, a.dk, a.dv, runs);
+    w.runs = seg_runs(chains, a.dk, a.dv, chunks_per_chain(a), false);
+    w.total = w.seg_off + seg_bytes(chains, a.dk, a.dv, w.runs);
+    return w;
 }
+
+size_t kda_split_workspace_bytes(const FwdArgs &a, int n_seq_eff) { return kda_ws(a, n_seq_eff).total; }
 
 int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     const bool varlen = a.cu_seqlens != nullptr;
-    const SplitLayout lay = split_layout(a, n_seq_eff, blk_bytes(a.dk, a.a != nullptr));
+    const KdaWs kw = kda_ws(a, n_seq_eff);
+    const SplitLayout lay = kw.lay;
     const int max_chunks = lay.max_chunks;
     SplitParams sp;
     std::memset(&sp, 0, sizeof(sp));
@@ -1283,16 +1478,24 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     sp.total = (long)a.B * a.T;
     sp.H = a.H; sp.T = a.T; sp.dv = a.dv; sp.n_seq = n_seq_eff; sp.n_tiles = a.dv / kDVT;
     sp.nc = lay.nc; sp.max_chunks = max_chunks; sp.C = kC;
-    sp.seg_ws = (float *)(ws + seg_offset(lay.total));
-    const int runs = seg_runs(n_seq_eff * a.H, a.dk, a.dv, chunks_per_chain(a), true);
+    sp.seg_ws = (float *)(ws + kw.seg_off);
+    sp.sub = kw.sub ? (int *)(ws + kw.sub_off) : nullptr;
+    const int runs = kw.runs ? seg_runs(n_seq_eff * a.H, a.dk, a.dv, chunks_per_chain(a), true) : 0;
 
     if (varlen) hipLaunchKernelGGL((chunk_plan_kernel<SplitParams>), dim3(1), dim3(kPlanThreads), 0, s, sp);
     // persistent prep workgroups: two per CU (one with a, b: their LDS allows no more)
     const long njobs = (long)a.H * max_chunks;
     const long slots = (dp ? 1L : 2L) * compute_units();
     const dim3 grid_prep((unsigned)(njobs < slots ? njobs : slots));
-#define GDR_PREP(DK, G, D, CL) \
-    hipLaunchKernelGGL((kda_prep_kernel<DK, G, D, CL>), grid_prep, dim3(kThreads), 0, s, sp)
+    const long cus = compute_units();
+    const dim3 grid_sub((unsigned)(njobs < cus ? njobs : cus));
+    // the log-domain variant redoes the jobs the first pass flagged (usually none)
+#define GDR_PREP(DK, G, D, CL)                                                                    \
+    do {                                                                                          \
+        hipLaunchKernelGGL((kda_prep_kernel<DK, G, D, CL>), grid_prep, dim3(kThreads), 0, s, sp); \
+        if (sp.sub)                                                                               \
+            hipLaunchKernelGGL((kda_prep_kernel<DK, G, D, CL, true>), grid_sub, dim3(kThreads), 0, s, sp); \
+    } while (0)
 #define GDR_GATES(DK, D, CL)                                 \
     do {                                                     \
         if (a.gate == kGateChannel) GDR_PREP(DK, kGateChannel, D, CL); \
@@ -1340,6 +1543,7 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
     sp.a = (const bf16 *)b.a; sp.b = (const bf16 *)b.b;
     sp.la = b.log_alpha; sp.beta = b.beta; sp.S0 = b.S0; sp.cu = b.cu_seqlens;
     sp.err = (int *)ws;
+    sp.wide_err = 2;  // the gradient kernels form K e^-g: no log-domain rescue here
     sp.coff = varlen ? (int32_t *)(ws + lay.fw.coff_off) : nullptr;
     sp.order = varlen ? sp.coff + n_seq_eff + 1 : nullptr;
     sp.blk = ws + lay.fw.blk_off;

@@ -3,7 +3,7 @@
 This module only draws random numbers and shapes them; it holds none of the
 method's arithmetic, so both the CPU oracle tests and the GPU tests can use it.
 
-Five workloads are defined, each a sampled stand-in for the shapes and value
+Seven workloads are defined, each a sampled stand-in for the shapes and value
 ranges used to study the method (the pages report no dataset for this path):
 
 1. ``deltanet_f32``  DeltaNet, no gate, fp32:   B=1  H=2  T=256   dk=dv=64
@@ -13,6 +13,9 @@ ranges used to study the method (the pages report no dataset for this path):
 5. ``kda_varlen``    KDA, 8 packed sequences:    32768 tokens, H=32, dk=dv=128
 6. ``gdn2_clip``     GDN2 form with the spectral gate clip: the ``dplr`` shapes, with
                      the write key tied to b (b = beta k, as in the GDN2 form)
+7. ``kda_strong``    the ``kda`` shapes with -log alpha log-uniform in [1e-3, 8] per
+                     (token, channel): chunks whose gate falls beyond the range of the
+                     scaled operands (the log-domain prep's workload)
 
 Draw order (fixed, so every consumer sees the same bytes): [lengths], q, k, v,
 beta, log_alpha, [a_raw, b_noise], [S0].  All draws are float32; q and k (and a,
@@ -126,19 +129,21 @@ def dirichlet_lengths(rng: np.random.Generator, n_seq: int, total: int, min_len:
 
 def make_problem(kind: str, *, seed: Optional[int] = None, B=None, H=None, T=None, dk=None,
                  dv=None, n_seq=None, total=None, min_len=None, dtype=None,
-                 s0_scale=None, gate=None, dplr=None, clip=None, chunk: int = 64) -> Problem:
+                 s0_scale=None, gate=None, dplr=None, clip=None, la_range=None,
+                 chunk: int = 64) -> Problem:
     """Build a seeded problem of workload ``kind`` (see module doc).
 
     Keyword overrides shrink or reshape a workload while keeping its value
     distributions, so small parity cases and the full-size workloads share one
     recipe.  ``gate`` swaps the gate mode (the log-decay range stays the
     workload's); ``dplr=True`` adds distinct a, b drawn as in the ``dplr`` workload;
-    ``clip`` turns the spectral gate clipping on or off.
+    ``clip`` turns the spectral gate clipping on or off; ``la_range`` replaces the
+    uniform range of log alpha.
     """
     spec = dict(WORKLOADS[kind])
     spec.update({k: v for k, v in dict(B=B, H=H, T=T, dk=dk, dv=dv, n_seq=n_seq, total=total,
                                         min_len=min_len, dtype=dtype, s0_scale=s0_scale,
-                                        gate=gate, dplr=dplr, clip=clip).items()
+                                        gate=gate, dplr=dplr, clip=clip, la_range=la_range).items()
                  if v is not None})
     if seed is None:
         seed = spec["seed"]
@@ -159,10 +164,13 @@ def make_problem(kind: str, *, seed: Optional[int] = None, B=None, H=None, T=Non
     beta = rng.random(shp, dtype=np.float32)
     gate = spec["gate"]
     log_alpha = None
-    if gate == GATE_HEAD:
-        log_alpha = rng.uniform(*spec["la_range"], size=shp).astype(np.float32)
-    elif gate == GATE_CHANNEL:
-        log_alpha = rng.uniform(*spec["la_range"], size=shp + (dk_,)).astype(np.float32)
+    gshape = shp if gate == GATE_HEAD else shp + (dk_,)
+    if gate != GATE_NONE and spec.get("la_loguniform") and la_range is None:
+        # decay rates spread over orders of magnitude: -log alpha log-uniform in [lo, hi]
+        lo, hi = spec["la_loguniform"]
+        log_alpha = (-np.exp(rng.uniform(np.log(lo), np.log(hi), size=gshape))).astype(np.float32)
+    elif gate != GATE_NONE:
+        log_alpha = rng.uniform(*spec["la_range"], size=gshape).astype(np.float32)
     a = b = None
     if spec.get("dplr"):
         a32 = _l2n(rng.standard_normal(shp + (dk_,), dtype=np.float32))
@@ -208,6 +216,11 @@ WORKLOADS = {
                        s0_scale=0.1),
     "gdn2_clip": dict(seed=6, B=1, H=16, T=16384, dk=128, dv=128, dtype=torch.bfloat16,
                       gate=GATE_CHANNEL, la_range=(-0.1, -0.001), dplr=True, gdn2=True, clip=True),
+    # KDA shapes with per-channel decay rates over four orders of magnitude, as a forget
+    # gate exp(-w softplus(x)) gives: most chunks hold channels whose gate falls by far more
+    # than the scaled operands' exponent range, so they take the log-domain prep
+    "kda_strong": dict(seed=7, B=2, H=32, T=8192, dk=128, dv=128, dtype=torch.bfloat16,
+                       gate=GATE_CHANNEL, la_range=(-0.2, -0.001), la_loguniform=(1e-3, 8.0)),
 }
 
 # The tolerance on max|X - X_ref| / max|X_ref| for O and for the final state.

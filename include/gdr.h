@@ -83,7 +83,9 @@ typedef enum {
  * when a and b are given).  Returns 0 when the arguments are invalid
  * or unsupported.  The first 256 bytes of a workspace hold a sticky device
  * error flag (see gdr_workspace_error); zero-fill a workspace before its first
- * use. */
+ * use.  The size depends on the current device's compute-unit count (with few
+ * (sequence, head) pairs the serial pass is split across more CUs and needs
+ * room for the partial states): query it for the device the call runs on. */
 size_t gdr_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int C, int n_seq,
                                int dtype, int gate, int has_ab);
 
@@ -156,8 +158,11 @@ int gdr_chunk_bwd(const void *q, const void *k, const void *v, const void *a, co
                   int n_seq, int B, int H, int T, int dk_, int dv_, int C, int dtype, int gate,
                   void *workspace, size_t workspace_bytes, void *stream);
 
-/* Synchronises `stream`, returns the sticky device error flag of `workspace`
- * (0: none; 1: malformed cu_seqlens were clamped) and clears it.  Returns
+/* Synchronises `stream`, returns the sticky device error flags of `workspace`
+ * (0: none; bit 1: malformed cu_seqlens were clamped; bit 2, gdr_chunk_bwd only: a
+ * chunk's gate falls by more than 2^96 in some channel, beyond the range the
+ * gradient kernels handle, and the gradients of that call are not valid; the
+ * forward pass handles such chunks in the log domain) and clears them.  Returns
  * GDR_ERR_NULL or GDR_ERR_HIP on failure. */
 int gdr_workspace_error(void *workspace, void *stream);
 

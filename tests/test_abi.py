@@ -44,24 +44,31 @@ def test_version_and_status_strings(lib):
     assert lib.gdr_status_string(-99).decode() == "unknown status"
 
 
+def _align(x):
+    return -(-x // 256) * 256
+
+
 def test_workspace_sizes(lib):
     ws = gdr.workspace_bytes
-    # KDA family (bf16): the error-flag header plus one 61952-byte block per
-    # (chunk, head) at dk = 128 (37120 at dk = 64) ...
-    assert ws(2, 32, 8192, 128, 128) == 256 + 32 * (2 * 128) * 61952
-    assert ws(4, 16, 4096, 128, 128, gate=gdr.GATE_HEAD) == 256 + 16 * (4 * 64) * 61952
+    # KDA family (bf16): the error-flag header plus one 61952-byte block per (chunk, head)
+    # at dk = 128 (37120 at dk = 64); with a gate, one int per (chunk, head) flags chunks
+    # for the log-domain prep; then, with few chains, the segmented-pass area
+    kda = lambda chains_chunks, blk, gated=True: _align(256 + chains_chunks * blk) + \
+        (chains_chunks * 4 if gated else 0)
+    assert ws(2, 32, 8192, 128, 128) == _align(kda(32 * 256, 61952))
+    assert ws(4, 16, 4096, 128, 128, gate=gdr.GATE_HEAD) == _align(kda(16 * 256, 61952))
     assert ws(1, 2, 100, 64, 64, gate=gdr.GATE_NONE) == 256 + 2 * 2 * 37120
     # ... and, for packed sequences, the chunk offsets and room for every sequence
     # to end in a partial chunk
-    assert ws(1, 32, 32768, 128, 128, n_seq=8) == 256 + 256 + 32 * (512 + 8) * 61952
+    assert ws(1, 32, 32768, 128, 128, n_seq=8) == _align(256 + 256 + 32 * 520 * 61952) + 32 * 520 * 4
     # DPLR (bf16, distinct a, b, C = 64): the same blocks plus Diag(beta) K^ (16 KiB).
     # With 16 (sequence, head) chains the state pass is cut into 3 runs (on 256 CUs):
     # start states of runs 1, 2, and R, P of run 1, fp32 [128][128] each, per chain
     assert ws(1, 16, 16384, 128, 128, has_ab=True) == \
-        256 + 16 * 256 * (61952 + 16384) + 16 * 4 * 128 * 128 * 4
+        _align(kda(16 * 256, 61952 + 16384)) + 16 * 4 * 128 * 128 * 4
+    assert ws(1, 2, 100, 64, 64, has_ab=True) == _align(kda(2 * 2, 37120 + 8192))
     # two chains of 32 chunks: 4 runs (3 start states, 2 R, 2 P per chain)
-    assert ws(1, 2, 2048, 128, 128) == 256 + 2 * 32 * 61952 + 2 * 7 * 128 * 128 * 4
-    assert ws(1, 2, 100, 64, 64, has_ab=True) == 256 + 2 * 2 * (37120 + 8192)
+    assert ws(1, 2, 2048, 128, 128) == _align(kda(2 * 32, 61952)) + 2 * 7 * 128 * 128 * 4
     # the fp32 kernels (fp32 inputs, or other chunk sizes with a, b) keep one fp32 block
     # per (chunk, head): W', Q~, K^ (+ Diag(beta) K^) [C][dk], two [C][C], gamma [dk],
     # rounded up to 64 floats
@@ -96,13 +103,18 @@ def test_backward_workspace_sizes(lib):
 
 
 def test_clip_flag_accepted_with_every_layout(lib):
-    # the clip flag changes no buffer size: same workspace as the plain layout
+    # the clip flag changes no buffer size, except that an ungated bf16 call gains the
+    # per-chunk flags of the log-domain prep (a clipped gate can fall far)
     for dt, C, ab in [(1, 64, 0), (1, 64, 1), (0, 32, 0), (1, 16, 1)]:
         for layout in (0, 1, 2):
             plain = lib.gdr_chunk_fwd_workspace(2, 4, 300, 128, 128, C, 0, dt, layout, ab)
             assert plain > 0
-            assert lib.gdr_chunk_fwd_workspace(2, 4, 300, 128, 128, C, 0, dt,
-                                               layout | gdr.GATE_CLIP, ab) == plain
+            clipped = lib.gdr_chunk_fwd_workspace(2, 4, 300, 128, 128, C, 0, dt,
+                                                  layout | gdr.GATE_CLIP, ab)
+            if dt == 1 and C == 64 and layout == 0:
+                assert clipped == _align(plain + 2 * 4 * 5 * 4)  # 40 (chunk, head) flags
+            else:
+                assert clipped == plain
     assert lib.gdr_chunk_fwd_workspace(2, 4, 300, 128, 128, 64, 0, 1, 3 | gdr.GATE_CLIP, 0) == 0
     assert lib.gdr_chunk_fwd_workspace(2, 4, 300, 128, 128, 64, 0, 1, 16, 0) == 0
 

@@ -155,3 +155,21 @@ def test_bwd_segmented_varlen():
     P.cu_seqlens = torch.tensor([0, 1500, 1500, 2000], dtype=torch.int32)
     dO, dSf = _cotangents(P, 790)
     _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))
+
+
+def test_bwd_flags_gates_beyond_its_range():
+    # the gradient kernels form K e^-g: a chunk whose gate falls beyond that range sets
+    # bit 2 of the workspace error flag (the forward redoes such chunks in the log domain)
+    P = inputs.make_problem("kda_strong", B=1, H=2, T=200)
+    dO, dSf = _cotangents(P, 795)
+    ws = torch.zeros(gdr.bwd_workspace_bytes(P.B, P.H, P.T, P.dk, P.dv, has_ab=False),
+                     dtype=torch.uint8, device="cuda")
+    to = lambda t: None if t is None else t.to("cuda")
+    gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), log_alpha=to(P.log_alpha),
+                  dS_final=to(dSf), workspace=ws)
+    assert gdr.check_workspace_error(ws) & 2
+    # an ordinary gate leaves it clear
+    P = inputs.make_problem("kda", B=1, H=2, T=200)
+    gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), log_alpha=to(P.log_alpha),
+                  dS_final=to(dSf), workspace=ws)
+    assert gdr.check_workspace_error(ws) == 0

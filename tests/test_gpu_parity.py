@@ -335,3 +335,51 @@ def test_segmented_varlen_with_empty_and_initial_state():
     O, Sf = gpu_run(P)
     _check(P, O, Sf)
     np.testing.assert_array_equal(Sf[1], P.S0[1].double().numpy())
+
+
+# ---------------------------------------------------------------------------
+# Gates that fall far inside one chunk: the scaled operands K e^-g would leave the
+# exponent range, so those chunks are redone by the log-domain prep (every Gram pair
+# formed from the gate difference).  Without it these cases give non-finite output.
+# ---------------------------------------------------------------------------
+STRONG = {
+    "kda": dict(kind="kda_strong", B=1, H=2, T=300),
+    "kda_d64": dict(kind="kda_strong", B=2, H=2, T=200, dk=64, dv=64, s0_scale=0.3),
+    "gdn": dict(kind="gdn", B=1, H=2, T=330, la_range=(-3.0, -1.0)),
+    "dplr": dict(kind="dplr", B=1, H=2, T=300, la_range=(-3.0, -0.5), s0_scale=0.3),
+    "dplr_d64": dict(kind="dplr", B=1, H=2, T=260, dk=64, dv=96, la_range=(-3.0, -0.5)),
+    "gdn2_clip": dict(kind="gdn2_clip", B=1, H=2, T=300, la_range=(-3.0, -0.5)),
+}
+
+
+@pytest.mark.parametrize("case", list(STRONG))
+def test_strong_gate_log_domain_prep(case):
+    spec = dict(STRONG[case])
+    P = inputs.make_problem(spec.pop("kind"), **spec)
+    O, Sf = gpu_run(P)
+    assert np.isfinite(O).all() and np.isfinite(Sf).all()
+    _check(P, O, Sf)
+
+
+def test_strong_gate_on_some_heads_only():
+    # head 1 decays 40x faster: only its chunks take the log-domain prep
+    P = inputs.make_problem("kda", B=2, H=3, T=400, s0_scale=0.3)
+    P.log_alpha[:, :, 1] *= 40.0
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+
+
+def test_strong_gate_varlen():
+    P = inputs.make_problem("kda_varlen", n_seq=4, total=700, min_len=1, H=2,
+                            la_range=(-4.0, -0.5))
+    P.cu_seqlens = torch.tensor([0, 1, 300, 300, 700], dtype=torch.int32)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+
+
+def test_strong_gate_full_size_sampled():
+    P = inputs.make_problem("kda_strong")
+    out = torch.full((P.B, P.T, P.H, P.dv), float("nan"), dtype=P.dtype, device="cuda")
+    O, Sf = gpu_run(P, out=out)
+    assert np.isfinite(O).all() and np.isfinite(Sf).all()
+    _check(P, O, Sf, chains=[(0, 0), (1, 31), (0, 17)])
