@@ -128,9 +128,13 @@ struct PrepSmem {
     static constexpr int oTot = oLd;                    // fp32 [8][DK] gate partial sums (before oLd is used)
     static constexpr int oBeta = oT + 32 * kTS * 2;     // fp32 [64]
     static constexpr int oG = oBeta + kC * 4;           // fp32 [65]: head-gate prefix sums and total
-    static constexpr int GS = DK + 4;                   // SUB: fp32 row stride of the gate array
-    static constexpr int oGf = oG + 80 * 4;             // SUB only: fp32 [64][GS] gate (log2)
-    static constexpr int bytes = oGf + (SUB ? kC * GS * 4 : 0);
+    // SUB only: the gate, fp32 [64][GS] (log2), whose space then holds the bf16 operands
+    // of the off-diagonal Gram tiles ([128][KS]: GS = KS makes the two the same size),
+    // and the gate of the first row of each 16-row tile, fp32 [4][DK]
+    static constexpr int GS = KS;
+    static constexpr int oGf = oG + 80 * 4;
+    static constexpr int oGref = oGf + (SUB ? kC * GS * 4 : 0);
+    static constexpr int bytes = oGref + (SUB ? 4 * DK * 4 : 0);
     static_assert(8 * DK * 4 <= oBeta - oLd, "gate partial sums fit");
     static_assert(DP || SUB || bytes <= 80 * 1024, "two workgroups per CU");
     static_assert(bytes <= 160 * 1024, "one workgroup per CU");
@@ -166,7 +170,9 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
     float *sTot = (float *)(smem + L::oTot);
     float *sBeta = (float *)(smem + L::oBeta);
     float *sG = (float *)(smem + L::oG);
-    float *sGf = (float *)(smem + L::oGf);  // SUB only
+    float *sGf = (float *)(smem + L::oGf);      // SUB only
+    float *sGref = (float *)(smem + L::oGref);  // SUB only
+    uint16_t *sVar = (uint16_t *)sGf;           // SUB only, after the diagonal tiles
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -550,6 +556,7 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
                             kb[e][i] = br * kv[e] * egc;
                         }
                         sGf[r * L::GS + c0 + e] = g[i][e];
+                        if ((r & 15) == 0) sGref[(r >> 4) * DK + c0 + e] = g[i][e];
                     } else {
                         const float eg = GATE == kGateNone && !CLIP ? 1.f : exp2_fast(g[i][e]);
                         const float eig = GATE == kGateNone && !CLIP ? 1.f : exp2_fast(-g[i][e]);
@@ -619,20 +626,51 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
         // Computed transposed, D[c][r] = K->[c] . (K<- or Q<-)[r], so that each lane holds
         // four consecutive columns of one row.
         if constexpr (SUB) {
-            // Log-domain Gram (GLA notes, section 5.3, the diagonal sub-chunk form, used for
-            // every pair): x_r . (y_c e^(g_r - g_c)) summed over the channels in fp32 with
-            // the exponent formed as a difference, so nothing overflows however far the
-            // gate falls.  The 10 lower 16x16 tiles are cut into 4x4 blocks of pairs (160
-            // blocks); lanes 2b and 2b+1 sum the two halves of the channels of block b.
-            // Blocks above the diagonal inside a diagonal tile are written as zeros.
+            // Log-domain Gram by 16-row sub-chunks (GLA notes, section 5.3): no operand
+            // carries e^-g, so nothing overflows however far the gate falls.
+            // (1) Diagonal tiles element-wise in fp32: x_r . (y_c 2^(g_r - g_c)) with the
+            //     exponent formed as a difference.  Each tile's 10 lower 4x4 blocks of
+            //     pairs, the channels split in quarters over the four lanes of a quad
+            //     (threads 0-159); threads 160-183 write the tiles' upper blocks as zeros.
+            // (2) Off-diagonal tiles (ti > tj) on MFMA with the gate referred to the first
+            //     row s of tile ti: rows x_r 2^(g_r - g_s), columns y_c 2^(g_s - g_c), both
+            //     factors at most 1 (rows r >= s, columns c < s).
             constexpr int NP = DP ? 4 : 2;  // products: DP: BA, BK, QK, QA; else KK, QK
-            for (int item = tid; item < 320; item += kThreads) {
-                const int bk = item >> 1, half = item & 1;
-                const int t = bk >> 4, u = (bk >> 2) & 3, v = bk & 3;
-                const int ti = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
-                const int tj = t - ti * (ti + 1) / 2;
-                const int r0 = 16 * ti + 4 * u, cb = 16 * tj + 4 * v;
-                const bool live = ti > tj || u >= v;
+            // results of one output row of four pairs (r, cb..cb+3), as the fast path
+            // stores them: L (DP: B<- A->^T) strictly lower, x beta_r (not for DP) ...
+            auto put = [&](const float (&acc)[NP][4], int r, int cb, bool diag) {
+                const float4 bc = *(const float4 *)(sBeta + cb);
+                const float bcv[4] = {bc.x, bc.y, bc.z, bc.w};
+                const float br = DP ? 1.f : sBeta[r];
+                float lv[4], av[4], bkv[4], qav[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = cb + j;
+                    lv[j] = c < r ? br * acc[0][j] : 0.f;
+                    if constexpr (DP) {
+                        bkv[j] = c < r ? bcv[j] * acc[1][j] : 0.f;  // B<- K->^T Diag(beta)
+                        av[j] = c <= r ? bcv[j] * acc[2][j] : 0.f;  // Q<- K->^T Diag(beta)
+                        qav[j] = c <= r ? acc[3][j] : 0.f;          // Q<- A->^T
+                    } else {
+                        av[j] = c <= r ? acc[1][j] : 0.f;           // A_qk
+                    }
+                }
+                if (diag) *(float4 *)(sLd + r * kDS + (cb & 15)) = make_float4(lv[0], lv[1], lv[2], lv[3]);
+                else store4(sX + r * kCS + cb, lv[0], lv[1], lv[2], lv[3]);
+                store4(sAqk + r * kCS + cb, av[0], av[1], av[2], av[3]);
+                if constexpr (DP) {
+                    store4(sBK + r * kCS + cb, bkv[0], bkv[1], bkv[2], bkv[3]);
+                    store4(sAqa + r * kCS + cb, qav[0], qav[1], qav[2], qav[3]);
+                }
+            };
+            // (1) rows x (DP: b, else k) and q; columns k (DP: and a), all raw
+            const uint16_t *rx = DP ? sKl : sKr;
+            if (tid < 160) {
+                const int blk = tid >> 2, qd = tid & 3;
+                const int t = blk / 10, lb = blk % 10;
+                const int u = lb >= 6 ? 3 : (lb >= 3 ? 2 : (lb >= 1 ? 1 : 0));
+                const int v = lb - u * (u + 1) / 2;
+                const int r0 = 16 * t + 4 * u, cb = 16 * t + 4 * v;
                 float acc[NP][4][4];
 #pragma unroll
                 for (int pp = 0; pp < NP; ++pp)
@@ -640,86 +678,142 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int j = 0; j < 4; ++j) acc[pp][i][j] = 0.f;
-                if (live) {
-                    // DP: rows b (sKl), q (sQl); columns a (sAr), k (sKr).  Else: rows k
-                    // (sKr), q (sQl); columns k (sKr).
-                    const uint16_t *rx = DP ? sKl : sKr;
-                    for (int d = half * (DK / 2); d < (half + 1) * (DK / 2); d += 4) {
-                        float gr[4][4], gc[4][4], xr[4][4], qr[4][4], kc[4][4], ac[4][4];
+                for (int d = qd * (DK / 4); d < (qd + 1) * (DK / 4); d += 4) {
+                    float gr[4][4], gc[4][4], xr[4][4], qr[4][4], kc[4][4], ac[4][4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float4 a4 = *(const float4 *)(sGf + (r0 + i) * L::GS + d);
-                            const float4 b4 = *(const float4 *)(sGf + (cb + i) * L::GS + d);
-                            gr[i][0] = a4.x; gr[i][1] = a4.y; gr[i][2] = a4.z; gr[i][3] = a4.w;
-                            gc[i][0] = b4.x; gc[i][1] = b4.y; gc[i][2] = b4.z; gc[i][3] = b4.w;
-                            const uint2 x2 = *(const uint2 *)(rx + (r0 + i) * KS + d);
-                            const uint2 q2 = *(const uint2 *)(sQl + (r0 + i) * KS + d);
-                            const uint2 k2 = *(const uint2 *)(sKr + (cb + i) * KS + d);
-                            xr[i][0] = bf16_lo(x2.x); xr[i][1] = bf16_hi(x2.x); xr[i][2] = bf16_lo(x2.y); xr[i][3] = bf16_hi(x2.y);
-                            qr[i][0] = bf16_lo(q2.x); qr[i][1] = bf16_hi(q2.x); qr[i][2] = bf16_lo(q2.y); qr[i][3] = bf16_hi(q2.y);
-                            kc[i][0] = bf16_lo(k2.x); kc[i][1] = bf16_hi(k2.x); kc[i][2] = bf16_lo(k2.y); kc[i][3] = bf16_hi(k2.y);
-                            if constexpr (DP) {
-                                const uint2 a2 = *(const uint2 *)(sAr + (cb + i) * KS + d);
-                                ac[i][0] = bf16_lo(a2.x); ac[i][1] = bf16_hi(a2.x); ac[i][2] = bf16_lo(a2.y); ac[i][3] = bf16_hi(a2.y);
-                            }
+                    for (int i = 0; i < 4; ++i) {
+                        const float4 a4 = *(const float4 *)(sGf + (r0 + i) * L::GS + d);
+                        const float4 b4 = *(const float4 *)(sGf + (cb + i) * L::GS + d);
+                        gr[i][0] = a4.x; gr[i][1] = a4.y; gr[i][2] = a4.z; gr[i][3] = a4.w;
+                        gc[i][0] = b4.x; gc[i][1] = b4.y; gc[i][2] = b4.z; gc[i][3] = b4.w;
+                        const uint2 x2 = *(const uint2 *)(rx + (r0 + i) * KS + d);
+                        const uint2 q2 = *(const uint2 *)(sQl + (r0 + i) * KS + d);
+                        const uint2 k2 = *(const uint2 *)(sKr + (cb + i) * KS + d);
+                        xr[i][0] = bf16_lo(x2.x); xr[i][1] = bf16_hi(x2.x); xr[i][2] = bf16_lo(x2.y); xr[i][3] = bf16_hi(x2.y);
+                        qr[i][0] = bf16_lo(q2.x); qr[i][1] = bf16_hi(q2.x); qr[i][2] = bf16_lo(q2.y); qr[i][3] = bf16_hi(q2.y);
+                        kc[i][0] = bf16_lo(k2.x); kc[i][1] = bf16_hi(k2.x); kc[i][2] = bf16_lo(k2.y); kc[i][3] = bf16_hi(k2.y);
+                        if constexpr (DP) {
+                            const uint2 a2 = *(const uint2 *)(sAr + (cb + i) * KS + d);
+                            ac[i][0] = bf16_lo(a2.x); ac[i][1] = bf16_hi(a2.x); ac[i][2] = bf16_lo(a2.y); ac[i][3] = bf16_hi(a2.y);
                         }
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                                for (int j = 0; j < 4; ++j) {
-                                    // pairs above the diagonal are discarded: keep them finite
-                                    const float x = exp2_fast(fminf(gr[i][e] - gc[j][e], 0.f));
-                                    const float xk = kc[j][e] * x;
-                                    if constexpr (DP) {
-                                        const float xa = ac[j][e] * x;
-                                        acc[0][i][j] += xr[i][e] * xa;
-                                        acc[1][i][j] += xr[i][e] * xk;
-                                        acc[2][i][j] += qr[i][e] * xk;
-                                        acc[3][i][j] += qr[i][e] * xa;
-                                    } else {
-                                        acc[0][i][j] += xr[i][e] * xk;
-                                        acc[1][i][j] += qr[i][e] * xk;
-                                    }
-                                }
                     }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                // pairs above the diagonal are discarded: keep them finite
+                                const float x = exp2_fast(fminf(gr[i][e] - gc[j][e], 0.f));
+                                const float xk = kc[j][e] * x;
+                                if constexpr (DP) {
+                                    const float xa = ac[j][e] * x;
+                                    acc[0][i][j] += xr[i][e] * xa;
+                                    acc[1][i][j] += xr[i][e] * xk;
+                                    acc[2][i][j] += qr[i][e] * xk;
+                                    acc[3][i][j] += qr[i][e] * xa;
+                                } else {
+                                    acc[0][i][j] += xr[i][e] * xk;
+                                    acc[1][i][j] += qr[i][e] * xk;
+                                }
+                            }
                 }
 #pragma unroll
                 for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) acc[pp][i][j] += dpp<kDppXor1>(acc[pp][i][j]);
-                if (half == 0) {
-                    const float4 bc = *(const float4 *)(sBeta + cb);
-                    const float bcv[4] = {bc.x, bc.y, bc.z, bc.w};
+                        for (int j = 0; j < 4; ++j) {
+                            acc[pp][i][j] += dpp<kDppXor1>(acc[pp][i][j]);
+                            acc[pp][i][j] += dpp<kDppXor2>(acc[pp][i][j]);
+                        }
+                if (qd == 0) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int r = r0 + i;
-                        const float br = DP ? 1.f : sBeta[r];
-                        float lv[4], av[4], bkv[4], qav[4];
+                        float row[NP][4];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int c = cb + j;
-                            lv[j] = c < r ? br * acc[0][i][j] : 0.f;  // L (DP: B<- A->^T)
-                            if constexpr (DP) {
-                                bkv[j] = c < r ? bcv[j] * acc[1][i][j] : 0.f;
-                                av[j] = c <= r ? bcv[j] * acc[2][i][j] : 0.f;
-                                qav[j] = c <= r ? acc[3][i][j] : 0.f;
-                            } else {
-                                av[j] = c <= r ? acc[1][i][j] : 0.f;
-                            }
+                        for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) row[pp][j] = acc[pp][i][j];
+                        put(row, r0 + i, cb, true);
+                    }
+                }
+            } else if (tid < 184) {
+                const int zb = tid - 160, t = zb / 6, k6 = zb % 6;
+                const int u = k6 < 3 ? 0 : (k6 < 5 ? 1 : 2);
+                const int v = u == 0 ? k6 + 1 : (u == 1 ? k6 - 1 : 3);
+                float zero[NP][4];
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) zero[pp][j] = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) put(zero, 16 * t + 4 * u + i, 16 * t + 4 * v, true);
+            }
+            lds_barrier();  // the gate array is free: the operands below go over it
+
+            // (2) scratch rows (bf16, stride KS): columns k' at 0..47 (DP: a' at 48..95),
+            //     rows x' at 96..111, q' at 112..127
+            for (int ti = 1; ti < 4; ++ti) {
+                if (rg < 2 * ti + 2) {  // owners of rows 0 .. 16 ti + 15
+                    const int s0 = 16 * ti;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int r = 8 * rg + i;
+                        float f[CPT];
+#pragma unroll
+                        for (int e = 0; e < CPT; ++e) {
+                            const float gs = sGref[ti * DK + c0 + e];
+                            f[e] = exp2_fast(r >= s0 ? g[i][e] - gs : gs - g[i][e]);
                         }
-                        if (ti == tj) *(float4 *)(sLd + r * kDS + 4 * v) = make_float4(lv[0], lv[1], lv[2], lv[3]);
-                        else store4(sX + r * kCS + cb, lv[0], lv[1], lv[2], lv[3]);
-                        store4(sAqk + r * kCS + cb, av[0], av[1], av[2], av[3]);
-                        if constexpr (DP) {
-                            store4(sBK + r * kCS + cb, bkv[0], bkv[1], bkv[2], bkv[3]);
-                            store4(sAqa + r * kCS + cb, qav[0], qav[1], qav[2], qav[3]);
+#pragma unroll
+                        for (int w = 0; w < WPR; ++w) {
+                            if (r >= s0) {
+                                const uint32_t xw = *(const uint32_t *)(rx + r * KS + c0 + 2 * w);
+                                const uint32_t qw2 = *(const uint32_t *)(sQl + r * KS + c0 + 2 * w);
+                                *(uint32_t *)(sVar + (96 + r - s0) * KS + c0 + 2 * w) =
+                                    pack_bf16x2(bf16_lo(xw) * f[2 * w], bf16_hi(xw) * f[2 * w + 1]);
+                                *(uint32_t *)(sVar + (112 + r - s0) * KS + c0 + 2 * w) =
+                                    pack_bf16x2(bf16_lo(qw2) * f[2 * w], bf16_hi(qw2) * f[2 * w + 1]);
+                            } else {
+                                const uint32_t kw2 = *(const uint32_t *)(sKr + r * KS + c0 + 2 * w);
+                                *(uint32_t *)(sVar + r * KS + c0 + 2 * w) =
+                                    pack_bf16x2(bf16_lo(kw2) * f[2 * w], bf16_hi(kw2) * f[2 * w + 1]);
+                                if constexpr (DP) {
+                                    const uint32_t aw2 = *(const uint32_t *)(sAr + r * KS + c0 + 2 * w);
+                                    *(uint32_t *)(sVar + (48 + r) * KS + c0 + 2 * w) =
+                                        pack_bf16x2(bf16_lo(aw2) * f[2 * w], bf16_hi(aw2) * f[2 * w + 1]);
+                                }
+                            }
                         }
                     }
                 }
+                lds_barrier();
+                // tiles (ti, tj < ti) of each product, one 16x16 tile per wave and turn,
+                // computed transposed like the fast path
+                for (int jb = wave; jb < NP * ti; jb += 4) {
+                    const int pr = jb / ti, tj = jb - pr * ti;
+                    const bool qrow = DP ? pr >= 2 : pr == 1;
+                    const bool acol = DP && (pr == 0 || pr == 3);
+                    const uint16_t *src = sVar + (qrow ? 112 : 96) * KS;
+                    const uint16_t *col = sVar + (acol ? 48 : 0) * KS;
+                    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < DK / 32; ++s)
+                        d = mfma(frag(col, 16 * tj + l16, KS, 32 * s + 8 * lg), frag(src, l16, KS, 32 * s + 8 * lg), d);
+                    const int r = 16 * ti + l16, cb = 16 * tj + 4 * lg;
+                    if (DP && pr > 0) {
+                        const float4 be = pr < 3 ? *(const float4 *)(sBeta + cb) : make_float4(1.f, 1.f, 1.f, 1.f);
+                        uint16_t *dst = pr == 1 ? sBK : (pr == 2 ? sAqk : sAqa);
+                        store4(dst + r * kCS + cb, be.x * d[0], be.y * d[1], be.z * d[2], be.w * d[3]);
+                    } else if (!DP && pr == 1) {
+                        store4(sAqk + r * kCS + cb, d[0], d[1], d[2], d[3]);
+                    } else {
+                        const float br = DP ? 1.f : sBeta[r];
+                        store4(sX + r * kCS + cb, br * d[0], br * d[1], br * d[2], br * d[3]);
+                    }
+                }
+                lds_barrier();  // the scratch rows are rewritten for the next ti
             }
         } else
         for (int jb = wave; jb < (DP ? 40 : 20); jb += 4) {
