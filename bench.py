@@ -6,7 +6,7 @@ state pass and the output in the state kernel), on seeded synthetic inputs alrea
 resident in HBM.  Prints one JSON line.
 
 Throughput is tokens/s (B*T / mean step time; a token carries all H heads).  The
-roofline entry treats the call (its two kernels) as the unit: algorithmic bytes
+roofline entry treats the call (all its launches) as the unit: algorithmic bytes
 per call (read q, k, v, log alpha, beta; write O and S_final) over the mean call
 duration measured with HIP events on the launch stream, against 8 TB/s.  HBM
 traffic and MFMA-busy figures come from the committed rocprofv3 counter summary,
@@ -414,8 +414,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": None if traffic is None else int(traffic),
-                     "kernel": ("gdr_chunk_fwd call: kda_prep_kernel<128, channel gate> + "
-                                "kda_state_kernel<128>" if headline else "gdr_chunk_fwd call"),
+                     "kernel": ("gdr_chunk_fwd call: kda_prep_kernel<128, channel gate> + its "
+                                "log-domain pass (flag scan) + kda_state_kernel<128>"
+                                if headline else "gdr_chunk_fwd call"),
                      "call_ms_mean": call_ms, "call_ms_median": pct(launch_ms, 0.5),
                      "call_ms_p10": pct(launch_ms, 0.1), "call_ms_p90": pct(launch_ms, 0.9),
                      "call_ms_cold_mean": float(np.mean(cold_ms)) if cold_ms else None,

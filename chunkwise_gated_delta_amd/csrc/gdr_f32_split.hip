@@ -32,6 +32,7 @@ namespace gdr {
 namespace {
 
 constexpr int kFT = 256;       // threads per workgroup, both kernels
+constexpr float kF32GateRange = 80.f;  // natural log
 constexpr int kDB = 64;        // dk channels per operand block of the prep kernel
 constexpr int kOS = kDB + 1;   // row stride (floats) of [C][kDB] operand arrays
 constexpr int kFDVT = 32;      // dv columns per state workgroup
@@ -211,7 +212,12 @@ __global__ __launch_bounds__(kFT) void f32_prep_kernel(F32Params p) {
                 if (DP) bp[B.oKb + r * dk + col] = sBeta[r] * kv[i] * egc;
             }
         }
-        if (first && rg == 0) bp[B.oG + col] = expf(gC);
+        if (first && rg == 0) {
+            bp[B.oG + col] = expf(gC);
+            // e^-g leaves the float range once a channel falls by e^80 inside the chunk:
+            // such a chunk's result is not valid, which the error word reports (bit 2)
+            if (!(gC >= -kF32GateRange)) atomicOr(p.err, 2);
+        }
         lds_barrier();
     };
 

@@ -383,3 +383,17 @@ def test_strong_gate_full_size_sampled():
     O, Sf = gpu_run(P, out=out)
     assert np.isfinite(O).all() and np.isfinite(Sf).all()
     _check(P, O, Sf, chains=[(0, 0), (1, 31), (0, 17)])
+
+
+def test_fp32_path_flags_gates_beyond_its_range():
+    # the fp32 kernels form K e^-g: a chunk falling by more than e^80 sets bit 2 of the
+    # workspace error word (the bf16 C = 64 path redoes such chunks instead)
+    P = inputs.make_problem("kda", B=1, H=2, T=130, dtype=torch.float32, la_range=(-3.0, -1.5))
+    ws = torch.zeros(gdr.workspace_bytes(P.B, P.H, P.T, P.dk, P.dv, dtype=torch.float32),
+                     dtype=torch.uint8, device="cuda")
+    to = lambda t: None if t is None else t.to("cuda")
+    gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), log_alpha=to(P.log_alpha), workspace=ws)
+    assert gdr.check_workspace_error(ws) & 2
+    P = inputs.make_problem("kda", B=1, H=2, T=130, dtype=torch.float32)
+    gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), log_alpha=to(P.log_alpha), workspace=ws)
+    assert gdr.check_workspace_error(ws) == 0
