@@ -397,3 +397,10 @@ def test_fp32_path_flags_gates_beyond_its_range():
     P = inputs.make_problem("kda", B=1, H=2, T=130, dtype=torch.float32)
     gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), log_alpha=to(P.log_alpha), workspace=ws)
     assert gdr.check_workspace_error(ws) == 0
+
+
+def test_strong_gate_with_segmented_state_pass():
+    # both mechanisms at once: log-domain chunks and a segmented serial pass
+    P = inputs.make_problem("dplr", B=1, H=2, T=2100, la_range=(-3.0, -0.2), s0_scale=0.3)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
