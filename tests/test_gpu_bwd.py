@@ -173,3 +173,10 @@ def test_bwd_flags_gates_beyond_its_range():
     gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), log_alpha=to(P.log_alpha),
                   dS_final=to(dSf), workspace=ws)
     assert gdr.check_workspace_error(ws) == 0
+
+
+def test_bwd_segmented_many_runs_long_sequence():
+    # 8 runs in both state passes of the backward
+    P = inputs.make_problem("kda", B=1, H=1, T=12000, s0_scale=0.3)
+    dO, dSf = _cotangents(P, 797)
+    _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))

@@ -404,3 +404,10 @@ def test_strong_gate_with_segmented_state_pass():
     P = inputs.make_problem("dplr", B=1, H=2, T=2100, la_range=(-3.0, -0.2), s0_scale=0.3)
     O, Sf = gpu_run(P)
     _check(P, O, Sf)
+
+
+def test_segmented_many_runs_long_sequence():
+    # one (sequence, head) chain of 256 chunks: 8 runs, six map combinations
+    P = inputs.make_problem("kda", B=1, H=1, T=16384, s0_scale=0.3)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
