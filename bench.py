@@ -74,7 +74,9 @@ def algorithmic_counts(P):
     FLOP per token-head: 10*C*d + 6*d^2 -- five C x C x d products (K<-K->^T,
     At K<-, At V, Q<-K->^T, A_qk V_new) and three C x d x d products (W S^T,
     V_new^T K^, Q<- S^T), counted as full tiles.  With a and b (DPLR) the call also
-    reads a, b (2*dk each) and does 18*C*d + 8*d^2.
+    reads a, b (2*dk each) and does 18*C*d + 8*d^2.  Counting only the lower triangles
+    of the C x C factors gives 5*(C+1)*d + 6*d^2 (DPLR: 9*(C+1)*d + 8*d^2), the third
+    value returned.
     """
     th = P.B * P.T * P.H
     d, C = P.dk, P.chunk
@@ -82,11 +84,13 @@ def algorithmic_counts(P):
     gate_bytes = {0: 0, 1: 4, 2: 4 * P.dk}[P.gate]
     per_th = es * (2 * P.dk + 2 * P.dv) + gate_bytes + 4
     flops_th = 10 * C * d + 6 * d * d
+    tri_th = 5 * (C + 1) * d + 6 * d * d
     if P.a is not None:
         per_th += 2 * es * P.dk
         flops_th = 18 * C * d + 8 * d * d
+        tri_th = 9 * (C + 1) * d + 8 * d * d
     state = P.n_seq * P.H * P.dv * P.dk * 4 * (1 + (P.S0 is not None))
-    return th * per_th + state, th * flops_th
+    return th * per_th + state, th * flops_th, th * tri_th
 
 
 def time_gpu(P, steps, warmup, cold_steps):
@@ -380,7 +384,7 @@ def main():
     from chunkwise_gated_delta_amd import inputs
 
     P = inputs.make_problem(args.workload)
-    alg_bytes, alg_flops = algorithmic_counts(P)
+    alg_bytes, alg_flops, tri_flops = algorithmic_counts(P)
     ms, launch_ms, cold_ms, out, fin = time_gpu(P, args.steps, args.warmup, args.cold_steps)
     call_ms = float(np.mean(launch_ms))
     tokens = P.B * P.T  # packed total for the varlen workload (B = 1)
@@ -423,6 +427,8 @@ def main():
                      "alg_bytes_per_launch": alg_bytes},
         "mfma": {"alg_flops_per_launch": alg_flops, "achieved_tflops": tflops,
                  "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "frac": tflops / BF16_MFMA_PEAK_TFLOPS,
+                 "lower_triangle_flops_per_launch": tri_flops,
+                 "frac_lower_triangle": tri_flops / (call_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                  "counter_busy_frac": cc.get("mfma_busy_frac")},
     }
     if not args.no_context:
