@@ -134,7 +134,8 @@ struct PrepSmem {
     static constexpr int GS = KS;
     static constexpr int oGf = oG + 80 * 4;
     static constexpr int oGref = oGf + (SUB ? kC * GS * 4 : 0);
-    static constexpr int bytes = oGref + (SUB ? 4 * DK * 4 : 0);
+    static constexpr int oWide = oGref + (SUB ? 4 * DK * 4 : 0);  // SUB only: int [4]
+    static constexpr int bytes = oWide + (SUB ? 16 : 0);
     static_assert(8 * DK * 4 <= oBeta - oLd, "gate partial sums fit");
     static_assert(DP || SUB || bytes <= 80 * 1024, "two workgroups per CU");
     static_assert(bytes <= 160 * 1024, "one workgroup per CU");
@@ -143,6 +144,9 @@ struct PrepSmem {
 // A chunk whose gate falls by more than this (log2 units, any channel) is redone by the
 // SUB variant: the scaled operands K e^-g would leave the bf16/fp32 exponent range.
 constexpr float kSubGateRange = 96.f;
+// In the SUB variant a diagonal 16x16 tile whose gate falls by at most this much goes on
+// MFMA with columns y_c 2^(g_s - g_c) (at most 2^64); a wider one is formed element-wise.
+constexpr float kSubTileRange = 64.f;
 
 template <int DK, int GATE, bool DP, bool CLIP, bool SUB = false>
 __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(SplitParams p) {
@@ -173,6 +177,7 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
     float *sGf = (float *)(smem + L::oGf);      // SUB only
     float *sGref = (float *)(smem + L::oGref);  // SUB only
     uint16_t *sVar = (uint16_t *)sGf;           // SUB only, after the diagonal tiles
+    int *sWide = (int *)(smem + L::oWide);      // SUB only
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -627,14 +632,15 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
         // four consecutive columns of one row.
         if constexpr (SUB) {
             // Log-domain Gram by 16-row sub-chunks (GLA notes, section 5.3): no operand
-            // carries e^-g, so nothing overflows however far the gate falls.
-            // (1) Diagonal tiles element-wise in fp32: x_r . (y_c 2^(g_r - g_c)) with the
-            //     exponent formed as a difference.  Each tile's 10 lower 4x4 blocks of
-            //     pairs, the channels split in quarters over the four lanes of a quad
-            //     (threads 0-159); threads 160-183 write the tiles' upper blocks as zeros.
-            // (2) Off-diagonal tiles (ti > tj) on MFMA with the gate referred to the first
-            //     row s of tile ti: rows x_r 2^(g_r - g_s), columns y_c 2^(g_s - g_c), both
-            //     factors at most 1 (rows r >= s, columns c < s).
+            // carries e^-g, so nothing overflows however far the gate falls.  Tile (ti, tj)
+            // takes the gate referred to the first row s of tile ti: rows x_r 2^(g_r - g_s)
+            // (at most 1), columns y_c 2^(g_s - g_c) (at most 1 for tj < ti; for the
+            // diagonal tile at most 2^(g_s - g_(s+15)), which is bounded by kSubTileRange
+            // there) on MFMA.  A diagonal tile whose gate falls further is formed
+            // element-wise in fp32, x_r . (y_c 2^(g_r - g_c)) with the exponent formed as
+            // a difference (the notes' form for diagonal sub-chunks), by the wave that owns
+            // its rows: ten lower 4x4 blocks of pairs on four lanes each (a quarter of the
+            // channels per lane), six upper blocks written as zeros.
             constexpr int NP = DP ? 4 : 2;  // products: DP: BA, BK, QK, QA; else KK, QK
             // results of one output row of four pairs (r, cb..cb+3), as the fast path
             // stores them: L (DP: B<- A->^T) strictly lower, x beta_r (not for DP) ...
@@ -663,11 +669,17 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
                     store4(sAqa + r * kCS + cb, qav[0], qav[1], qav[2], qav[3]);
                 }
             };
-            // (1) rows x (DP: b, else k) and q; columns k (DP: and a), all raw
+            // rows x (DP: b, else k) and q; columns k (DP: and a), all raw
             const uint16_t *rx = DP ? sKl : sKr;
-            if (tid < 160) {
-                const int blk = tid >> 2, qd = tid & 3;
-                const int t = blk / 10, lb = blk % 10;
+            // does the gate of this wave's tile fall further than kSubTileRange? (lanes
+            // 32-63 hold the tile's last row; sGref its first)
+            bool wide_t = false;
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) wide_t = wide_t || !(sGref[wave * DK + c0 + e] - g[7][e] <= kSubTileRange);
+            wide_t = __builtin_amdgcn_ballot_w64(wide_t && lane >= 32) != 0;
+            if (lane == 0) sWide[wave] = wide_t ? 1 : 0;
+            if (wide_t && lane < 40) {
+                const int qd = lane & 3, t = wave, lb = lane >> 2;
                 const int u = lb >= 6 ? 3 : (lb >= 3 ? 2 : (lb >= 1 ? 1 : 0));
                 const int v = lb - u * (u + 1) / 2;
                 const int r0 = 16 * t + 4 * u, cb = 16 * t + 4 * v;
@@ -738,8 +750,8 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
                         put(row, r0 + i, cb, true);
                     }
                 }
-            } else if (tid < 184) {
-                const int zb = tid - 160, t = zb / 6, k6 = zb % 6;
+            } else if (wide_t && lane < 46) {
+                const int t = wave, k6 = lane - 40;
                 const int u = k6 < 3 ? 0 : (k6 < 5 ? 1 : 2);
                 const int v = u == 0 ? k6 + 1 : (u == 1 ? k6 - 1 : 3);
                 float zero[NP][4];
@@ -752,10 +764,10 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
             }
             lds_barrier();  // the gate array is free: the operands below go over it
 
-            // (2) scratch rows (bf16, stride KS): columns k' at 0..47 (DP: a' at 48..95),
-            //     rows x' at 96..111, q' at 112..127
-            for (int ti = 1; ti < 4; ++ti) {
-                if (rg < 2 * ti + 2) {  // owners of rows 0 .. 16 ti + 15
+            // scratch rows (bf16, stride KS): columns k' at 0..47 (DP: a' at 48..95), rows x'
+            // at 96..111, q' at 112..127; the diagonal tile's columns at 0..15 (a' 48..63)
+            for (int ti = 0; ti < 4; ++ti) {
+                if (ti > 0 && rg < 2 * ti + 2) {  // owners of rows 0 .. 16 ti + 15
                     const int s0 = 16 * ti;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
@@ -811,6 +823,73 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
                     } else {
                         const float br = DP ? 1.f : sBeta[r];
                         store4(sX + r * kCS + cb, br * d[0], br * d[1], br * d[2], br * d[3]);
+                    }
+                }
+                if (ti > 0) lds_barrier();  // the column rows are rewritten below
+                // the diagonal tile (ti, ti), unless it was formed element-wise
+                const bool wide = sWide[ti] != 0;  // workgroup-uniform
+                if (!wide) {
+                    if (rg == 2 * ti || rg == 2 * ti + 1) {  // owners of tile ti's rows
+                        const int s0 = 16 * ti;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const int r = 8 * rg + i;
+                            float fc[CPT], fr[CPT];
+#pragma unroll
+                            for (int e = 0; e < CPT; ++e) {
+                                const float gs = sGref[ti * DK + c0 + e];
+                                fc[e] = exp2_fast(gs - g[i][e]);
+                                fr[e] = exp2_fast(g[i][e] - gs);
+                            }
+#pragma unroll
+                            for (int w = 0; w < WPR; ++w) {
+                                const uint32_t kw2 = *(const uint32_t *)(sKr + r * KS + c0 + 2 * w);
+                                *(uint32_t *)(sVar + (r - s0) * KS + c0 + 2 * w) =
+                                    pack_bf16x2(bf16_lo(kw2) * fc[2 * w], bf16_hi(kw2) * fc[2 * w + 1]);
+                                if constexpr (DP) {
+                                    const uint32_t aw2 = *(const uint32_t *)(sAr + r * KS + c0 + 2 * w);
+                                    *(uint32_t *)(sVar + (48 + r - s0) * KS + c0 + 2 * w) =
+                                        pack_bf16x2(bf16_lo(aw2) * fc[2 * w], bf16_hi(aw2) * fc[2 * w + 1]);
+                                }
+                                if (ti == 0) {  // the rows were not built above
+                                    const uint32_t xw = *(const uint32_t *)(rx + r * KS + c0 + 2 * w);
+                                    const uint32_t qw2 = *(const uint32_t *)(sQl + r * KS + c0 + 2 * w);
+                                    *(uint32_t *)(sVar + (96 + r - s0) * KS + c0 + 2 * w) =
+                                        pack_bf16x2(bf16_lo(xw) * fr[2 * w], bf16_hi(xw) * fr[2 * w + 1]);
+                                    *(uint32_t *)(sVar + (112 + r - s0) * KS + c0 + 2 * w) =
+                                        pack_bf16x2(bf16_lo(qw2) * fr[2 * w], bf16_hi(qw2) * fr[2 * w + 1]);
+                                }
+                            }
+                        }
+                    }
+                    lds_barrier();
+                    for (int pr = wave; pr < NP; pr += 4) {
+                        const bool qrow = DP ? pr >= 2 : pr == 1;
+                        const bool acol = DP && (pr == 0 || pr == 3);
+                        const uint16_t *src = sVar + (qrow ? 112 : 96) * KS;
+                        const uint16_t *col = sVar + (acol ? 48 : 0) * KS;
+                        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s = 0; s < DK / 32; ++s)
+                            d = mfma(frag(col, l16, KS, 32 * s + 8 * lg), frag(src, l16, KS, 32 * s + 8 * lg), d);
+                        const int r = 16 * ti + l16, cb = 16 * ti + 4 * lg;
+                        const float4 be = *(const float4 *)(sBeta + cb);
+                        const float bcv[4] = {be.x, be.y, be.z, be.w};
+                        float o[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int c = cb + j;
+                            const bool strict = DP ? pr < 2 : pr == 0;  // L, BA, BK: below the diagonal
+                            const bool keep = strict ? c < r : c <= r;
+                            const float sc = DP ? ((pr == 1 || pr == 2) ? bcv[j] : 1.f) : (pr == 0 ? sBeta[r] : 1.f);
+                            o[j] = keep ? sc * d[j] : 0.f;
+                        }
+                        if (pr == 0) {
+                            *(float4 *)(sLd + r * kDS + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
+                        } else {
+                            uint16_t *dst = DP ? (pr == 1 ? sBK : (pr == 2 ? sAqk : sAqa)) : sAqk;
+                            store4(dst + r * kCS + cb, o[0], o[1], o[2], o[3]);
+                        }
                     }
                 }
                 lds_barrier();  // the scratch rows are rewritten for the next ti

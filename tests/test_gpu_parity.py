@@ -411,3 +411,16 @@ def test_segmented_many_runs_long_sequence():
     P = inputs.make_problem("kda", B=1, H=1, T=16384, s0_scale=0.3)
     O, Sf = gpu_run(P)
     _check(P, O, Sf)
+
+
+@pytest.mark.parametrize("kind,dk,dv", [("kda", 128, 128), ("dplr", 128, 128), ("kda", 64, 64),
+                                        ("dplr", 64, 96), ("gdn", 128, 128)])
+def test_strong_gate_diagonal_tiles_mfma_and_elementwise(kind, dk, dv):
+    # head 0: every chunk flagged but each 16-row tile falls by less than 2^64 (its diagonal
+    # tiles on MFMA); head 1: four times steeper, its diagonal tiles formed element-wise
+    P = inputs.make_problem(kind, B=1, H=2, T=330, dk=dk, dv=dv, la_range=(-2.0, -1.0),
+                            s0_scale=0.3)
+    P.log_alpha[:, :, 1] *= 4.0
+    O, Sf = gpu_run(P)
+    assert np.isfinite(O).all() and np.isfinite(Sf).all()
+    _check(P, O, Sf)
