@@ -37,6 +37,15 @@
 // S = (S + V'^T K-> + N^T A->) Diag(gamma_C), with V' = Diag(beta) V.  The prep kernel hands its results over in the
 // operand order of v_mfma_f32_32x32x16_bf16, so the state kernel loads them straight
 // into registers with whole-wave contiguous loads.
+//
+// Two variants around these:
+//   - a chunk whose gate falls by more than 2^96 in a channel (K-> would leave the float
+//     range) is flagged by the prep kernel and redone by its SUB instantiation, which
+//     forms L and A_qk by 16-row sub-chunks in the log domain ("Gated Linear Attention"
+//     notes, section 5.3) and shares everything after them;
+//   - with few (sequence, head) chains the serial pass is cut into runs joined through
+//     the affine map of each run, S_end = S_start P + R (seg_combine_kernel between two
+//     launches of the state kernel), so that more CUs work at once.
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
