@@ -159,8 +159,9 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
         final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
     if not output_final_state:
         final_state = None
-    need = int(lib.gdr_chunk_fwd_workspace(B, H, T, dk, dv, chunk_size, n_seq, dt, gate,
-                                           int(a is not None)))
+    with torch.cuda.device(q.device):  # the size depends on the device's CU count
+        need = int(lib.gdr_chunk_fwd_workspace(B, H, T, dk, dv, chunk_size, n_seq, dt, gate,
+                                               int(a is not None)))
     if need == 0:
         raise GdrError(-3, f"no kernel for dtype={q.dtype} dk={dk} dv={dv} C={chunk_size}")
     if workspace is None:
@@ -254,8 +255,9 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     for name, t in (("S0", S0), ("dS_final", dS_final)):
         if t is not None and (t.shape != (N, H, dv, dk) or t.dtype != torch.float32):
             raise ValueError(f"{name} must be [{N}, {H}, {dv}, {dk}] float32")
-    need = int(lib.gdr_chunk_bwd_workspace(B, H, T, dk, dv, chunk_size, n_seq, dt, gate,
-                                           int(a is not None)))
+    with torch.cuda.device(q.device):  # the size depends on the device's CU count
+        need = int(lib.gdr_chunk_bwd_workspace(B, H, T, dk, dv, chunk_size, n_seq, dt, gate,
+                                               int(a is not None)))
     if need == 0:
         raise GdrError(-3, f"no backward kernel for dtype={q.dtype} dk={dk} dv={dv} C={chunk_size}")
     if workspace is None:
