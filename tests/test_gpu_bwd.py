@@ -180,3 +180,9 @@ def test_bwd_segmented_many_runs_long_sequence():
     P = inputs.make_problem("kda", B=1, H=1, T=12000, s0_scale=0.3)
     dO, dSf = _cotangents(P, 797)
     _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))
+
+
+def test_bwd_segmented_without_final_state_gradient():
+    P = inputs.make_problem("dplr", B=1, H=2, T=1800)
+    dO, _ = _cotangents(P, 799)
+    _check(P, _gpu_bwd(P, dO, None), _oracle_bwd(P, dO, None))

@@ -424,3 +424,18 @@ def test_strong_gate_diagonal_tiles_mfma_and_elementwise(kind, dk, dv):
     O, Sf = gpu_run(P)
     assert np.isfinite(O).all() and np.isfinite(Sf).all()
     _check(P, O, Sf)
+
+
+def test_segmented_without_final_state_and_in_place():
+    P = inputs.make_problem("kda", B=1, H=2, T=2048, s0_scale=0.3)
+    O, Sf = gpu_run(P, output_final_state=False)
+    assert Sf is None
+    _check(P, O, None)
+    # S_final written over S0 in place: the runs read S0 before the last one writes it
+    S = P.S0.to("cuda").clone()
+    to = lambda t: None if t is None else t.to("cuda")
+    O2, Sf2 = gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), log_alpha=to(P.log_alpha),
+                            S0=S, final_state=S)
+    torch.cuda.synchronize()
+    assert Sf2.data_ptr() == S.data_ptr()
+    _check(P, O2.double().cpu().numpy(), Sf2.double().cpu().numpy())
