@@ -439,3 +439,12 @@ def test_segmented_without_final_state_and_in_place():
     torch.cuda.synchronize()
     assert Sf2.data_ptr() == S.data_ptr()
     _check(P, O2.double().cpu().numpy(), Sf2.double().cpu().numpy())
+
+
+@pytest.mark.parametrize("kind", ["kda", "dplr", "gdn"])
+def test_total_forgetting_gate(kind):
+    # log alpha = -300 per token: each output is beta v (k . q) of its own token
+    P = inputs.make_problem(kind, B=1, H=2, T=150, la_range=(-300.0, -300.0), s0_scale=0.3)
+    O, Sf = gpu_run(P)
+    assert np.isfinite(O).all() and np.isfinite(Sf).all()
+    _check(P, O, Sf)

@@ -148,6 +148,23 @@ def test_single_token(gate, dplr):
         assert np.max(np.abs(other - S1)) > 1e-3
 
 
+@pytest.mark.parametrize("dplr", [False, True])
+@pytest.mark.parametrize("gate", [1, 2])
+def test_total_forgetting(gate, dplr):
+    """A gate that falls by e^-300 per token forgets everything before the current
+    token: S_t = beta_t v_t k_t^T and o_t = beta_t v_t (k_t . q_t), whatever S0 and the
+    rank-one factor (the recurrence with Diag(alpha) = 0 up to e^-300)."""
+    rng = np.random.default_rng(40 + gate + 3 * dplr)
+    c = _rand_case(rng, B=2, T=7, H=2, dk=5, dv=3, gate=gate, dplr=dplr)
+    c["log_alpha"] = np.full_like(c["log_alpha"], -300.0)
+    O, Sf = oracle.recurrence(**c)
+    bv = c["beta"][..., None] * c["v"]
+    kq = np.sum(c["k"] * c["q"], axis=-1)[..., None]
+    np.testing.assert_allclose(O, bv * kq, rtol=0, atol=1e-13)
+    last = np.einsum("bhi,bhj->bhij", bv[:, -1], c["k"][:, -1])
+    np.testing.assert_allclose(Sf, last, rtol=0, atol=1e-13)
+
+
 # ---------------------------------------------------------------------------
 # 3. WY representation of the transition product.
 # ---------------------------------------------------------------------------
