@@ -312,6 +312,7 @@ SEGMENTED = {
     "dplr": dict(B=1, H=2, T=2100, s0_scale=0.3),
     "gdn2_clip": dict(B=1, H=1, T=3000),
     "dplr_d64_96": dict(B=1, H=2, T=1900, dk=64, dv=96),
+    "kda_d128_64": dict(B=1, H=2, T=2048, dk=128, dv=64, s0_scale=0.3),  # P taller than R
 }
 
 
