@@ -259,8 +259,21 @@ def bench_backward(args):
     q, k, v, beta, la = to(P.q), to(P.k), to(P.v), to(P.beta), to(P.log_alpha)
     a, b = to(P.a), to(P.b)
     S0, cu, dOd, dSd = to(P.S0), to(P.cu_seqlens), to(dO), to(dSf)
+    ws = None
+    if args.forward_workspace:
+        # the backward of a training step: the forward call's workspace (its per-chunk
+        # factors) is handed to the backward, which then skips recomputing them
+        n_seq = 0 if cu is None else P.n_seq
+        gate = gdr.GATE_NONE if la is None else (gdr.GATE_HEAD if la.dim() == 3 else gdr.GATE_CHANNEL)
+        need = max(gdr.workspace_bytes(P.B, P.H, P.T, P.dk, P.dv, n_seq=n_seq, gate=gate, has_ab=a is not None),
+                   gdr.bwd_workspace_bytes(P.B, P.H, P.T, P.dk, P.dv, n_seq=n_seq, gate=gate,
+                                           has_ab=a is not None))
+        ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+        gdr.chunk_fwd(q, k, v, beta, log_alpha=la, a=a, b=b, S0=S0, cu_seqlens=cu,
+                      chunk_size=P.chunk, workspace=ws)
     call = lambda: gdr.chunk_bwd(q, k, v, beta, dOd, log_alpha=la, a=a, b=b, S0=S0,
-                                 dS_final=dSd, cu_seqlens=cu, chunk_size=P.chunk)
+                                 dS_final=dSd, cu_seqlens=cu, chunk_size=P.chunk, workspace=ws,
+                                 forward_workspace=args.forward_workspace)
     for _ in range(args.warmup):
         g = call()
     torch.cuda.synchronize()
@@ -285,7 +298,8 @@ def bench_backward(args):
     gbs = alg_bytes / (call_ms * 1e-3) / 1e9
     tflops = alg_flops / (call_ms * 1e-3) / 1e12
     result = {
-        "metric": f"tokens/s, {args.workload} chunk bwd (all input gradients), 1xMI355X",
+        "metric": f"tokens/s, {args.workload} chunk bwd (all input gradients"
+                  f"{', forward workspace reused' if args.forward_workspace else ''}), 1xMI355X",
         "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -353,6 +367,9 @@ def main():
                     help="skip the GEMM / copy context measurements")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (gdr_chunk_bwd) on the workload instead")
+    ap.add_argument("--forward-workspace", action="store_true",
+                    help="with --backward: hand the backward the workspace of a forward call on "
+                         "the same inputs (GDR_BWD_FORWARD_WORKSPACE), as a training step does")
     ap.add_argument("--copy-cal", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (calibrates the HBM "
                          "traffic counters: FETCH_SIZE/WRITE_SIZE per byte actually moved)")

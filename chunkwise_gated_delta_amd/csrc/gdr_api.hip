@@ -173,8 +173,9 @@ int gdr_chunk_bwd(const void *q, const void *k, const void *v, const void *a_, c
                   const float *dS_final, void *dq, void *dk, void *dv, void *da, void *db,
                   float *dlog_alpha, float *dbeta, float *dS0, const int32_t *cu_seqlens,
                   int n_seq, int B, int H, int T, int dk_, int dv_, int C, int dtype, int gate,
-                  void *workspace, size_t workspace_bytes, void *stream) {
+                  int flags, void *workspace, size_t workspace_bytes, void *stream) {
     if (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta) return GDR_ERR_NULL;
+    if (flags & ~GDR_BWD_FORWARD_WORKSPACE) return GDR_ERR_SHAPE;
     const bool has_ab = a_ != nullptr;
     if ((a_ == nullptr) != (b_ == nullptr)) return GDR_ERR_NULL;
     if ((da == nullptr) != !has_ab || (db == nullptr) != !has_ab) return GDR_ERR_NULL;
@@ -192,6 +193,7 @@ int gdr_chunk_bwd(const void *q, const void *k, const void *v, const void *a_, c
     a.grad_la = dlog_alpha; a.grad_beta = dbeta; a.grad_S0 = dS0; a.cu_seqlens = cu_seqlens;
     a.n_seq = varlen ? n_seq : 0;
     a.B = B; a.H = H; a.T = T; a.dk = dk_; a.dv = dv_; a.C = C; a.dtype = dtype; a.gate = gate;
+    a.reuse_fwd = (flags & GDR_BWD_FORWARD_WORKSPACE) != 0;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     if (!gdr::kda_bwd_supported(a)) return GDR_ERR_UNSUPPORTED;
     const int N = varlen ? n_seq : B;

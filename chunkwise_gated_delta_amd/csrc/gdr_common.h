@@ -122,6 +122,7 @@ struct BwdArgs {
     float *grad_la, *grad_beta, *grad_S0;      // dL/dlog_alpha, dL/dbeta, dL/dS0
     const int32_t *cu_seqlens;
     int n_seq, B, H, T, dk, dv, C, dtype, gate;
+    bool reuse_fwd;  // the workspace holds the forward's per-chunk blocks of the same inputs
     void *workspace;
     size_t workspace_bytes;
 };

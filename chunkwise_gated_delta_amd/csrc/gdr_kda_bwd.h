@@ -105,9 +105,25 @@ struct BwdParams {
     float *dla, *dbeta;
     const int32_t *cu;
     const int32_t *coff;
+    int *err;  // workspace error word: bit 2 when a chunk's gate falls beyond kBwdGateRange
     long total;
     int H, T, dv_, n_seq, nc, max_chunks, C;
 };
+
+// These kernels form K e^-g inside a chunk: a chunk whose gate falls by more than this
+// (natural log, 2^96) in some channel is beyond their range, which the error word reports.
+constexpr float kBwdGateRange = 66.54f;
+
+// Wave 3's lanes 32-63 hold the chunk's last row (rows 8 rg + i, rg = 7) of the in-chunk
+// gate sums; flag the call when any channel falls beyond kBwdGateRange.
+template <int CPT>
+__device__ __forceinline__ void flag_wide_gate(const float (&g)[8][CPT], int wave, int lane, int *err) {
+    if (wave != 3) return;
+    bool wide = false;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) wide = wide || !(g[7][e] >= -kBwdGateRange);
+    if (__builtin_amdgcn_ballot_w64(wide && lane >= 32) != 0 && lane == 0) atomicOr(err, 2);
+}
 
 // One 16x16 output tile of A B on the 16x16x32 MFMA: lane l ends with
 // D[m0 + l%16][n0 + 4(l/16) + e] in register e.  A is read from a row-major [m][k]
@@ -338,6 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     float g[8][CPT];  // kept for the chain rule at the end
     {
         gate(g);
+        flag_wide_gate(g, wave, lane, p.err);
         if (tid < kC) sBeta[tid] = tid < m ? in.beta : 0.f;
         uint32_t qw[8][WPR], kw[8][WPR];
 #pragma unroll
@@ -972,6 +989,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
             for (int i = 0; i < 8; ++i) g[i][e] += carry;
         }
     }
+    flag_wide_gate(g, wave, lane, p.err);
     issue(0);
     // Q<-, B<- (scale e^g) or K->, A-> (scale e^-g) of two loaded inputs, bf16 into LDS
     auto scaled = [&](const uint32_t (&xw)[8][WPR], const uint32_t (&yw)[8][WPR], uint16_t *dx,

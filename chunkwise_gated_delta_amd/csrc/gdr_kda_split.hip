@@ -112,7 +112,6 @@ struct SplitParams {
     // operands (see kSubGateRange); such jobs are redone by the log-domain prep variant.
     // NULL: not recorded.
     int *sub;
-    int wide_err;  // nonzero: OR this into *err when a chunk's gate range is too wide
 };
 
 // ---------------------------------------------------------------------------------
@@ -523,15 +522,12 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
         }
         if constexpr (!SUB) {
             // wave 0 holds gamma_C of every channel: flag the chunk for the SUB variant
-            if ((p.sub || p.wide_err) && wave == 0) {
+            if (p.sub && wave == 0) {
                 bool wide = false;
 #pragma unroll
                 for (int e = 0; e < CPT; ++e) wide = wide || !(gC[e] >= -kSubGateRange);
                 const bool any = __builtin_amdgcn_ballot_w64(wide) != 0;
-                if (lane == 0) {
-                    if (p.sub) p.sub[cur.g] = any ? 1 : 0;
-                    if (any && p.wide_err) atomicOr(p.err, p.wide_err);
-                }
+                if (lane == 0) p.sub[cur.g] = any ? 1 : 0;
             }
         }
 
@@ -1725,7 +1721,6 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
     sp.a = (const bf16 *)b.a; sp.b = (const bf16 *)b.b;
     sp.la = b.log_alpha; sp.beta = b.beta; sp.S0 = b.S0; sp.cu = b.cu_seqlens;
     sp.err = (int *)ws;
-    sp.wide_err = 2;  // the gradient kernels form K e^-g: no log-domain rescue here
     sp.coff = varlen ? (int32_t *)(ws + lay.fw.coff_off) : nullptr;
     sp.order = varlen ? sp.coff + n_seq_eff + 1 : nullptr;
     sp.blk = ws + lay.fw.blk_off;
@@ -1751,7 +1746,7 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
     bp.S = (const uint16_t *)(ws + lay.s_off); bp.dS = (const uint16_t *)(ws + lay.ds_off);
     bp.dq = (bf16 *)b.grad_q; bp.dk = (bf16 *)b.grad_k; bp.dv = (bf16 *)b.grad_v;
     bp.dla = b.grad_la; bp.dbeta = b.grad_beta;
-    bp.cu = b.cu_seqlens; bp.coff = sp.coff; bp.total = sp.total;
+    bp.cu = b.cu_seqlens; bp.coff = sp.coff; bp.total = sp.total; bp.err = (int *)ws;
     bp.H = b.H; bp.T = b.T; bp.dv_ = b.dv; bp.n_seq = n_seq_eff; bp.nc = lay.fw.nc;
     bp.max_chunks = max_chunks; bp.C = kC;
 
@@ -1766,7 +1761,8 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
     const dim3 grid_post(dp ? grid_jobs : dim3((unsigned)(njobs < cus ? njobs : cus)));
 #define GDR_BWD(DK, G, D, POST)                                                                    \
     do {                                                                                           \
-        hipLaunchKernelGGL((kda_prep_kernel<DK, G, D, false>), grid_prep, dim3(kThreads), 0, s, sp);  \
+        if (!b.reuse_fwd)  /* else the forward left its blocks in the workspace */              \
+            hipLaunchKernelGGL((kda_prep_kernel<DK, G, D, false>), grid_prep, dim3(kThreads), 0, s, sp); \
         run_state<DK, D, kSaveStates>(sp, runs, s);                                               \
         hipLaunchKernelGGL((kda_bwd_reorder_kernel<DK, D>), grid_jobs, dim3(kThreads), 0, s,       \
                            (const char *)sp.blk, rp.blk, (int)njobs);                              \

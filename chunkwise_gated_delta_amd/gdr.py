@@ -50,7 +50,7 @@ def load_library(path: str = LIB_PATH):
         lib.gdr_chunk_fwd_workspace.restype = Z
         lib.gdr_chunk_fwd_workspace.argtypes = [I] * 10
         lib.gdr_chunk_bwd.restype = I
-        lib.gdr_chunk_bwd.argtypes = [P] * 19 + [I] * 9 + [P, Z, P]
+        lib.gdr_chunk_bwd.argtypes = [P] * 19 + [I] * 10 + [P, Z, P]
         lib.gdr_chunk_bwd_workspace.restype = Z
         lib.gdr_chunk_bwd_workspace.argtypes = [I] * 10
         lib.gdr_workspace_error.restype = I
@@ -202,12 +202,17 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
               a: Optional[torch.Tensor] = None, b: Optional[torch.Tensor] = None,
               S0: Optional[torch.Tensor] = None, dS_final: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
-              want_dS0: bool = True, workspace: Optional[torch.Tensor] = None) -> dict:
+              want_dS0: bool = True, workspace: Optional[torch.Tensor] = None,
+              forward_workspace: bool = False) -> dict:
     """Gradients of <dO, O> + <dS_final, S_final> for chunk_fwd.
 
     Shapes as in chunk_fwd; dO like O, dS_final like S_final (None: zero).
     Returns a dict with dq, dk, dv (q's dtype), dbeta, da and db (with a, b),
     dlog_alpha (when a gate is given) and dS0 (fp32, when want_dS0).
+
+    forward_workspace=True: `workspace` is the one the chunk_fwd call on the same inputs
+    filled (sized for both, see bwd_workspace_bytes); its per-chunk factors are reused
+    (GDR_BWD_FORWARD_WORKSPACE).  The caller guarantees the inputs are the same.
     """
     lib = load_library()
     if not q.is_cuda:
@@ -260,6 +265,8 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
                                                int(a is not None)))
     if need == 0:
         raise GdrError(-3, f"no backward kernel for dtype={q.dtype} dk={dk} dv={dv} C={chunk_size}")
+    if forward_workspace and workspace is None:
+        raise ValueError("forward_workspace=True needs the workspace chunk_fwd used")
     if workspace is None:
         workspace = _workspace(q.device, need)
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
@@ -279,8 +286,8 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
                                _ptr(out.get("db")), _ptr(out.get("dlog_alpha")),
                                _ptr(out["dbeta"]), _ptr(out.get("dS0")), _ptr(cu_seqlens),
                                n_seq, B, H, T, dk, dv,
-                               chunk_size, dt, gate, _ptr(workspace), workspace.numel(),
-                               ctypes.c_void_p(stream))
+                               chunk_size, dt, gate, int(bool(forward_workspace)), _ptr(workspace),
+                               workspace.numel(), ctypes.c_void_p(stream))
     if rc != 0:
         raise GdrError(rc, lib.gdr_status_string(rc).decode())
     return out

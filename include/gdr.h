@@ -129,6 +129,16 @@ int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
 size_t gdr_chunk_bwd_workspace(int B, int H, int T, int dk, int dv, int C, int n_seq, int dtype,
                                int gate, int has_ab);
 
+/* Flags of gdr_chunk_bwd.
+ *   GDR_BWD_FORWARD_WORKSPACE  `workspace` is the one a gdr_chunk_fwd call on the same
+ *       q, k, v, a, b, log_alpha, beta, cu_seqlens, B, H, T, dk, dv, C and gate layout
+ *       filled, enqueued earlier and followed by no other call on that workspace; its
+ *       per-chunk factors are used instead of being recomputed (the forward's first
+ *       kernel is skipped).  The workspace must still hold gdr_chunk_bwd_workspace
+ *       bytes.  Nothing checks that the inputs are the same: when they differ the
+ *       gradients are wrong. */
+enum { GDR_BWD_FORWARD_WORKSPACE = 1 };
+
 /* The backward pass of gdr_chunk_fwd: the gradients of
  * L = <dO, O> + <dS_final, S_final> with respect to every input.  Without a, b
  * (KDA, Gated DeltaNet, DeltaNet) it follows the chunk-form backward of the
@@ -147,6 +157,7 @@ size_t gdr_chunk_bwd_workspace(int B, int H, int T, int dk, int dv, int C, int n
  *   dlog_alpha  shape of log_alpha, fp32      output; NULL exactly when gate is NONE
  *   dbeta       [B, T, H]      fp32           output
  *   dS0         [N, H, dv, dk] fp32 or NULL   output dL/dS0
+ *   flags       0 or GDR_BWD_FORWARD_WORKSPACE (other values: GDR_ERR_SHAPE)
  *
  * Supported: bf16, C = 64, dk in {64, 128}, dv a multiple of 32 up to 256.
  * Outputs may not overlap inputs, each other or the workspace.  Memory,
@@ -156,7 +167,7 @@ int gdr_chunk_bwd(const void *q, const void *k, const void *v, const void *a, co
                   const float *dS_final, void *dq, void *dk, void *dv, void *da, void *db,
                   float *dlog_alpha, float *dbeta, float *dS0, const int32_t *cu_seqlens,
                   int n_seq, int B, int H, int T, int dk_, int dv_, int C, int dtype, int gate,
-                  void *workspace, size_t workspace_bytes, void *stream);
+                  int flags, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Synchronises `stream`, returns the sticky device error flags of `workspace`
  * (0: none; bit 1: malformed cu_seqlens were clamped; bit 2: a chunk's gate falls

@@ -158,3 +158,15 @@ def test_aliasing_rejected(lib):
     assert _call(lib, Sf=FAKE + (2 << 30)) == -5          # S_final on top of v
     assert _call(lib, S0=FAKE + (10 << 30), Sf=FAKE + (10 << 30) + 64) == -5  # partial overlap
     assert _call(lib, ws=FAKE + (5 << 30)) == -5          # workspace on top of O
+
+
+def test_backward_flags_validated(lib):
+    # pointers are never dereferenced: validation fails before any launch
+    ptrs = [P(FAKE + (i << 30)) for i in range(19)]
+    ptrs[3] = ptrs[4] = ptrs[13] = ptrs[14] = P(None)  # no a, b (and no da, db)
+    ptrs[18] = P(None)                                  # no cu_seqlens
+    args = ptrs + [0, 1, 2, 64, 128, 128, 64, 1, 2]
+    for flags, want in [(2, -2), (4, -2), (-1, -2)]:
+        assert lib.gdr_chunk_bwd(*args, flags, P(FAKE + (30 << 30)), 16, None) == want
+    # a valid flag gets past that check (and then fails on the too-small workspace)
+    assert lib.gdr_chunk_bwd(*args, 1, P(FAKE + (30 << 30)), 16, None) == -4

@@ -168,6 +168,12 @@ def test_bwd_flags_gates_beyond_its_range():
     gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), log_alpha=to(P.log_alpha),
                   dS_final=to(dSf), workspace=ws)
     assert gdr.check_workspace_error(ws) & 2
+    # the same through the forward's workspace (the gradient kernels raise it themselves)
+    gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), log_alpha=to(P.log_alpha), workspace=ws)
+    assert gdr.check_workspace_error(ws) == 0  # the forward handles the chunk
+    gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), log_alpha=to(P.log_alpha),
+                  dS_final=to(dSf), workspace=ws, forward_workspace=True)
+    assert gdr.check_workspace_error(ws) & 2
     # an ordinary gate leaves it clear
     P = inputs.make_problem("kda", B=1, H=2, T=200)
     gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), log_alpha=to(P.log_alpha),
@@ -186,3 +192,38 @@ def test_bwd_segmented_without_final_state_gradient():
     P = inputs.make_problem("dplr", B=1, H=2, T=1800)
     dO, _ = _cotangents(P, 799)
     _check(P, _gpu_bwd(P, dO, None), _oracle_bwd(P, dO, None))
+
+
+# ---------------------------------------------------------------------------
+# GDR_BWD_FORWARD_WORKSPACE: the backward reuses the per-chunk factors the forward call
+# left in its workspace instead of recomputing them
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kind,spec", [("kda", dict(B=2, H=2, T=300)), ("gdn", dict(B=1, H=3, T=200)),
+                                       ("dplr", dict(B=1, H=2, T=300)),
+                                       ("kda", dict(B=1, H=2, T=2048)),  # segmented passes
+                                       ("kda_varlen", dict(n_seq=3, total=700, min_len=1, H=2))])
+def test_bwd_reuses_forward_workspace(kind, spec):
+    P = inputs.make_problem(kind, s0_scale=0.3, **spec)
+    dO, dSf = _cotangents(P, 810)
+    to = lambda t: None if t is None else t.to("cuda")
+    n_seq = 0 if P.cu_seqlens is None else P.n_seq
+    gate = (gdr.GATE_NONE if P.log_alpha is None else
+            gdr.GATE_HEAD if P.log_alpha.dim() == 3 else gdr.GATE_CHANNEL)
+    ab = P.a is not None
+    need = max(gdr.workspace_bytes(P.B, P.H, P.T, P.dk, P.dv, n_seq=n_seq, gate=gate, has_ab=ab),
+               gdr.bwd_workspace_bytes(P.B, P.H, P.T, P.dk, P.dv, n_seq=n_seq, gate=gate, has_ab=ab))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    args = dict(log_alpha=to(P.log_alpha), a=to(P.a), b=to(P.b), S0=to(P.S0),
+                cu_seqlens=to(P.cu_seqlens))
+    gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), workspace=ws, **args)
+    g1 = gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), dS_final=to(dSf),
+                       workspace=ws, forward_workspace=True, **args)
+    g2 = gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), dS_final=to(dSf), **args)
+    torch.cuda.synchronize()
+    for key in g1:  # the same factors: the same bits, except for the order of the fp32
+        # LDS atomics that gather the gate gradient's last-row term
+        if key == "dlog_alpha":
+            assert rel_err(g1[key].cpu().numpy(), g2[key].cpu().numpy()) <= 1e-5, key
+        else:
+            assert torch.equal(g1[key], g2[key]), key
+    _check(P, {k: v.to(torch.float64).cpu().numpy() for k, v in g1.items()}, _oracle_bwd(P, dO, dSf))
