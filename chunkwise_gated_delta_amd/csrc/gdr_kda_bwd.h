@@ -110,12 +110,41 @@ struct BwdParams {
     int H, T, dv_, n_seq, nc, max_chunks, C;
 };
 
-// These kernels form K e^-g inside a chunk: a chunk whose gate falls by more than this
-// (natural log, 2^96) in some channel is beyond their range, which the error word reports.
+// The gate inside a chunk, referred to the middle of its range: g' = g - r with
+// r = n ln 2, n the integer nearest g_C / (2 ln 2).  Every factor these kernels form from
+// it (Q<-, K<-, K->, Gamma) is e^g' or its inverse, which stays within about e^(|g_C|/2)
+// both ways; the products they enter (K<- K->^T, Q<- K->^T, ...) are unchanged by the
+// shift, and the terms with the states take S_p 2^n and dS_n e^(g_C - r) per column:
+// (S_p 2^n)(W' 2^-n)^T = S_p W^T, and dS_n Diag(gamma_C) 2^-n pairs with K-> 2^n.  The
+// gradients of the shifted operands map back through the shifted Gamma in the same way,
+// and the gate gradient (elementwise products of an operand and its gradient) is
+// unchanged.  A power of two keeps the bf16 S_p exact when scaled.
+//
+// g[i][e] holds the prefix of the thread's row-group (rows 8 rg + i); part[8 r2 * DK]
+// (r2 < 8) holds each row-group's total for the same channel; row-group 0 writes 2^n to
+// *spf.
+template <int CPT>
+__device__ __forceinline__ void g_shift(float (&g)[8][CPT], int e, const float *part, int rg,
+                                        float *spf) {
+    constexpr int DKP = CPT * 32;
+    float carry = 0.f;
+    for (int r2 = 0; r2 < rg; ++r2) carry += part[r2 * DKP];
+    float total = carry;
+    for (int r2 = rg; r2 < 8; ++r2) total += part[r2 * DKP];
+    const float n = rintf(0.5f * total * kLog2e);
+    const float shift = carry - n * kLn2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g[i][e] += shift;
+    if (rg == 0) *spf = exp2f(n);
+}
+
+// With the shift above, a chunk whose gate falls by more than twice this in some channel
+// (natural log; e^66.54 = 2^96) is beyond the kernels' float range, which the error word
+// reports.
 constexpr float kBwdGateRange = 66.54f;
 
-// Wave 3's lanes 32-63 hold the chunk's last row (rows 8 rg + i, rg = 7) of the in-chunk
-// gate sums; flag the call when any channel falls beyond kBwdGateRange.
+// Wave 3's lanes 32-63 hold the chunk's last row (rows 8 rg + i, rg = 7) of the shifted
+// gate, g_C/2; flag the call when any channel falls beyond 2 kBwdGateRange.
 template <int CPT>
 __device__ __forceinline__ void flag_wide_gate(const float (&g)[8][CPT], int wave, int lane, int *err) {
     if (wave != 3) return;
@@ -192,7 +221,8 @@ struct BwdSmem {
     static constexpr int oGp = oGam + DK * 4;   // fp32 [8][DK] gate partial sums
     static constexpr int oDb = oGp + 8 * DK * 4;  // fp32 [64] dbeta
     static constexpr int oDg = oDb + kC * 4;    // fp32 [DK] last-row term of dg
-    static constexpr int bytes = oDg + DK * 4;
+    static constexpr int oSpf = oDg + DK * 4;   // fp32 [DK] 2^n, the state's scale
+    static constexpr int bytes = oSpf + DK * 4;
     // final stage: Gamma fp32 [64][DK] over Q<-..K-> (free by then), dg fp32 [64][DK] over T
     static_assert(kC * DK * 4 <= 3 * QK, "Gamma fits over the operand arrays");
     static_assert(kC * DK * 4 <= Tbytes, "dg fits over the tile region");
@@ -217,6 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     float *sBeta = (float *)(smem + L::oBeta), *sGam = (float *)(smem + L::oGam);
     float *sGp = (float *)(smem + L::oGp), *sDb = (float *)(smem + L::oDb);
     float *sDg = (float *)(smem + L::oDg);
+    float *sSpf = (float *)(smem + L::oSpf);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -341,12 +372,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         for (int e = 0; e < CPT; ++e) sGp[rg * DK + c0 + e] = run[e];
         lds_barrier();
 #pragma unroll
-        for (int e = 0; e < CPT; ++e) {
-            float carry = 0.f;
-            for (int r2 = 0; r2 < rg; ++r2) carry += sGp[r2 * DK + c0 + e];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) g[i][e] += carry;
-        }
+        for (int e = 0; e < CPT; ++e) g_shift(g, e, sGp + c0 + e, rg, sSpf + c0 + e);
         lds_barrier();  // sGp may be reused
     };
 
@@ -513,17 +539,19 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
 #pragma unroll
             for (int i = 0; i < kSPT; ++i) {
                 const int idx = tid + kThreads * i, r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
-                *(uint4 *)(sSp + r * KS + c8) = pf.s[i];
                 const uint32_t w4[4] = {pf.d[i].x, pf.d[i].y, pf.d[i].z, pf.d[i].w};
                 const uint32_t s4[4] = {pf.s[i].x, pf.s[i].y, pf.s[i].z, pf.s[i].w};
-                uint32_t o4[4];
+                uint32_t o4[4], p4[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float d0 = bf16_lo(w4[e]) * sGam[c8 + 2 * e], d1 = bf16_hi(w4[e]) * sGam[c8 + 2 * e + 1];
+                    const float s0 = bf16_lo(s4[e]) * sSpf[c8 + 2 * e], s1 = bf16_hi(s4[e]) * sSpf[c8 + 2 * e + 1];
                     o4[e] = pack_bf16x2(d0, d1);
-                    gpart[2 * e] += bf16_lo(s4[e]) * d0;
-                    gpart[2 * e + 1] += bf16_hi(s4[e]) * d1;
+                    p4[e] = pack_bf16x2(s0, s1);
+                    gpart[2 * e] += s0 * d0;
+                    gpart[2 * e + 1] += s1 * d1;
                 }
+                *(uint4 *)(sSp + r * KS + c8) = make_uint4(p4[0], p4[1], p4[2], p4[3]);
                 *(uint4 *)(sdS + r * KS + c8) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
             }
             const int r = tid >> 2, c8 = 8 * (tid & 3);
@@ -858,7 +886,8 @@ struct BwdDpSmem {
     static constexpr int oGp = oGam + DK * 4;
     static constexpr int oDb = oGp + 8 * DK * 4;
     static constexpr int oDg = oDb + kC * 4;
-    static constexpr int bytes = oDg + DK * 4;
+    static constexpr int oSpf = oDg + DK * 4;
+    static constexpr int bytes = oSpf + DK * 4;
     static_assert(kC * DK * 4 <= 2 * QK, "Gamma / dg fit over K->, A-> and over Q<-, B<-");
     static_assert(bytes <= 160 * 1024, "LDS");
 };
@@ -883,6 +912,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
     float *sBeta = (float *)(smem + L::oBeta), *sGam = (float *)(smem + L::oGam);
     float *sGp = (float *)(smem + L::oGp), *sDb = (float *)(smem + L::oDb);
     float *sDg = (float *)(smem + L::oDg);
+    float *sSpf = (float *)(smem + L::oSpf);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -982,12 +1012,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
         for (int e = 0; e < CPT; ++e) sGp[rg * DK + c0 + e] = run[e];
         lds_barrier();
 #pragma unroll
-        for (int e = 0; e < CPT; ++e) {
-            float carry = 0.f;
-            for (int r2 = 0; r2 < rg; ++r2) carry += sGp[r2 * DK + c0 + e];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) g[i][e] += carry;
-        }
+        for (int e = 0; e < CPT; ++e) g_shift(g, e, sGp + c0 + e, rg, sSpf + c0 + e);
     }
     flag_wide_gate(g, wave, lane, p.err);
     issue(0);
@@ -1136,17 +1161,19 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
 #pragma unroll
             for (int i = 0; i < kSPT; ++i) {
                 const int idx = tid + kThreads * i, r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
-                *(uint4 *)(sSp + r * KS + c8) = pf.s[i];
                 const uint32_t w4[4] = {pf.d[i].x, pf.d[i].y, pf.d[i].z, pf.d[i].w};
                 const uint32_t s4[4] = {pf.s[i].x, pf.s[i].y, pf.s[i].z, pf.s[i].w};
-                uint32_t o4[4];
+                uint32_t o4[4], p4[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float d0 = bf16_lo(w4[e]) * sGam[c8 + 2 * e], d1 = bf16_hi(w4[e]) * sGam[c8 + 2 * e + 1];
+                    const float s0 = bf16_lo(s4[e]) * sSpf[c8 + 2 * e], s1 = bf16_hi(s4[e]) * sSpf[c8 + 2 * e + 1];
                     o4[e] = pack_bf16x2(d0, d1);
-                    gpart[2 * e] += bf16_lo(s4[e]) * d0;
-                    gpart[2 * e + 1] += bf16_hi(s4[e]) * d1;
+                    p4[e] = pack_bf16x2(s0, s1);
+                    gpart[2 * e] += s0 * d0;
+                    gpart[2 * e + 1] += s1 * d1;
                 }
+                *(uint4 *)(sSp + r * KS + c8) = make_uint4(p4[0], p4[1], p4[2], p4[3]);
                 *(uint4 *)(sdS + r * KS + c8) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
             }
             const int r = tid >> 2, c8 = 8 * (tid & 3);

@@ -64,6 +64,7 @@ constexpr int kDS = 20;        // fp32 row stride of the 16x16 diagonal blocks
 constexpr int kTS = 32 + 8;    // bf16 row stride of the 32x32 level temporary
 constexpr int kVS = kDVT + 8;  // bf16 row stride of the value tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // One (chunk, head) block of the workspace.  A "fragment tile" of 32 rows and K
 // contraction columns is stored as K/16 steps x 64 lanes x 16 bytes; lane l of
@@ -1585,11 +1586,14 @@ FwdArgs fwd_view(const BwdArgs &b) {
     return a;
 }
 
-// Backward workspace: [header][packed-sequence plan][forward blocks][backward blocks]
-// [S_p states][dS_n states], the states bf16 [chunk][head][dv][dk].
+// Backward workspace: [header][packed-sequence plan][forward blocks][log-domain job
+// flags (gated forms)][backward blocks][S_p states][dS_n states], the states bf16
+// [chunk][head][dv][dk].  Everything up to the flags sits where the forward workspace
+// has it, so that a forward call's workspace can stand in for the first kernel.
 struct BwdLayout {
     SplitLayout fw;
-    size_t bwd_off, s_off, ds_off, seg_off, total;
+    size_t sub_off, bwd_off, s_off, ds_off, seg_off, total;
+    bool sub;
     int runs;  // of the segmented state passes (0: plain)
 };
 
@@ -1598,7 +1602,9 @@ BwdLayout bwd_layout(const BwdArgs &b, int N) {
     const FwdArgs a = fwd_view(b);
     L.fw = split_layout(a, N, blk_bytes(b.dk, b.a != nullptr));
     const size_t nblk = (size_t)b.H * L.fw.max_chunks;
-    L.bwd_off = L.fw.total;
+    L.sub = b.gate != kGateNone;
+    L.sub_off = seg_offset(L.fw.total);
+    L.bwd_off = seg_offset(L.sub_off + (L.sub ? nblk * 4 : 0));
     L.s_off = L.bwd_off + nblk * blk_bytes(b.dk, true);
     L.ds_off = L.s_off + nblk * b.dv * b.dk * 2;
     L.seg_off = seg_offset(L.ds_off + nblk * b.dv * b.dk * 2);
@@ -1729,6 +1735,7 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
     sp.H = b.H; sp.T = b.T; sp.dv = b.dv; sp.n_seq = n_seq_eff; sp.n_tiles = b.dv / kDVT;
     sp.nc = lay.fw.nc; sp.max_chunks = max_chunks; sp.C = kC;
     sp.seg_ws = (float *)(ws + lay.seg_off);
+    sp.sub = lay.sub ? (int *)(ws + lay.sub_off) : nullptr;
     const int runs = lay.runs ? seg_runs(n_seq_eff * b.H, b.dk, b.dv, chunks_per_chain(fwd_view(b)), true) : 0;
     // the reverse pass: backward blocks, dO as the value tile, dS_final in, dS0 out
     SplitParams rp = sp;
@@ -1737,6 +1744,7 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
     rp.S0 = b.dS_final;
     rp.Sf = b.grad_S0;
     rp.states = (uint16_t *)(ws + lay.ds_off);
+    rp.sub = nullptr;
     BwdParams bp;
     std::memset(&bp, 0, sizeof(bp));
     bp.q = (const bf16 *)b.q; bp.k = (const bf16 *)b.k; bp.v = (const bf16 *)b.v;
@@ -1758,11 +1766,15 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
     const dim3 grid_jobs((unsigned)njobs);
     // the KDA gradient kernel is persistent: one workgroup per CU (its LDS allows no more)
     const long cus = compute_units();
+    const dim3 grid_sub((unsigned)(njobs < cus ? njobs : cus));
     const dim3 grid_post(dp ? grid_jobs : dim3((unsigned)(njobs < cus ? njobs : cus)));
 #define GDR_BWD(DK, G, D, POST)                                                                    \
     do {                                                                                           \
-        if (!b.reuse_fwd)  /* else the forward left its blocks in the workspace */              \
+        if (!b.reuse_fwd) { /* else the forward left its blocks in the workspace */             \
             hipLaunchKernelGGL((kda_prep_kernel<DK, G, D, false>), grid_prep, dim3(kThreads), 0, s, sp); \
+            if (sp.sub)                                                                            \
+                hipLaunchKernelGGL((kda_prep_kernel<DK, G, D, false, true>), grid_sub, dim3(kThreads), 0, s, sp); \
+        }                                                                                          \
         run_state<DK, D, kSaveStates>(sp, runs, s);                                               \
         hipLaunchKernelGGL((kda_bwd_reorder_kernel<DK, D>), grid_jobs, dim3(kThreads), 0, s,       \
                            (const char *)sp.blk, rp.blk, (int)njobs);                              \

@@ -172,8 +172,8 @@ int gdr_chunk_bwd(const void *q, const void *k, const void *v, const void *a, co
 /* Synchronises `stream`, returns the sticky device error flags of `workspace`
  * (0: none; bit 1: malformed cu_seqlens were clamped; bit 2: a chunk's gate falls
  * further than the kernels that ran can represent, so that call's results are
- * not valid -- gdr_chunk_bwd when a channel falls by more than 2^96 within a
- * chunk, and the fp32 kernels (fp32 inputs, or C < 64) by more than e^80; the
+ * not valid -- gdr_chunk_bwd when a channel falls by more than 2^192 (e^133)
+ * within a chunk, and the fp32 kernels (fp32 inputs, or C < 64) by more than e^80; the
  * bf16 forward with C = 64 handles such chunks in the log domain and never sets
  * it) and clears them.  Returns GDR_ERR_NULL or GDR_ERR_HIP on failure. */
 int gdr_workspace_error(void *workspace, void *stream);

@@ -157,10 +157,69 @@ def test_bwd_segmented_varlen():
     _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))
 
 
+# Gates whose chunk decay lies between the forward's plain range (66.5 in natural log per
+# channel and chunk) and twice it: the forward takes the log-domain prep, the gradient
+# kernels refer the gate to the middle of the chunk's range.  -log alpha is log-uniform
+# (the strong-gate workload's recipe: most tokens keep their memory, some forget fast).
+BWD_STRONG = {
+    "kda": dict(kind="kda_strong", B=1, H=2, T=300),
+    "kda_d64": dict(kind="kda_strong", B=2, H=2, T=200, dk=64, dv=64, s0_scale=0.3),
+    "gdn": dict(kind="gdn", B=1, H=2, T=330, loguniform=(1e-2, 8.0)),
+    "dplr": dict(kind="dplr", B=1, H=2, T=300, loguniform=(1e-2, 8.0), s0_scale=0.3),
+}
+
+
+def _chunk_decays(P):
+    """Largest and smallest per-channel decay -sum(log alpha) over the chunks of P."""
+    la = P.log_alpha.double()
+    if la.dim() == 3:
+        la = la.unsqueeze(-1)
+    sums = []
+    for bi in range(P.B):
+        for c0 in range(0, P.T, 64):
+            sums.append(-la[bi, c0:c0 + 64].sum(0))
+    s = torch.stack(sums)
+    return float(s.max()), float(s.min())
+
+
+@pytest.mark.parametrize("case", list(BWD_STRONG))
+def test_bwd_strong_gates(case):
+    spec = dict(BWD_STRONG[case])
+    lu = spec.pop("loguniform", None)
+    P = inputs.make_problem(spec.pop("kind"), **spec)
+    if lu is not None:
+        rng = np.random.default_rng(31)
+        x = np.exp(rng.uniform(np.log(lu[0]), np.log(lu[1]), size=tuple(P.log_alpha.shape)))
+        P.log_alpha = torch.from_numpy(-x.astype(np.float32))
+    hi, _ = _chunk_decays(P)
+    assert 66.6 < hi < 133.0  # beyond the plain range, within the shifted one
+    dO, dSf = _cotangents(P, 795)
+    to = lambda t: None if t is None else t.to("cuda")
+    n_seq = 0 if P.cu_seqlens is None else P.n_seq
+    gate = gdr.GATE_HEAD if P.log_alpha.dim() == 3 else gdr.GATE_CHANNEL
+    ab = P.a is not None
+    need = max(gdr.workspace_bytes(P.B, P.H, P.T, P.dk, P.dv, n_seq=n_seq, gate=gate, has_ab=ab),
+               gdr.bwd_workspace_bytes(P.B, P.H, P.T, P.dk, P.dv, n_seq=n_seq, gate=gate, has_ab=ab))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    args = dict(log_alpha=to(P.log_alpha), a=to(P.a), b=to(P.b), S0=to(P.S0))
+    ref = _oracle_bwd(P, dO, dSf)
+    g = gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), dS_final=to(dSf),
+                      workspace=ws, **args)
+    assert gdr.check_workspace_error(ws) == 0
+    _check(P, {k: v.to(torch.float64).cpu().numpy() for k, v in g.items()}, ref)
+    # the same through the forward call's workspace
+    gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), workspace=ws, **args)
+    g = gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), dS_final=to(dSf),
+                      workspace=ws, forward_workspace=True, **args)
+    assert gdr.check_workspace_error(ws) == 0
+    _check(P, {k: v.to(torch.float64).cpu().numpy() for k, v in g.items()}, ref)
+
+
 def test_bwd_flags_gates_beyond_its_range():
-    # the gradient kernels form K e^-g: a chunk whose gate falls beyond that range sets
-    # bit 2 of the workspace error flag (the forward redoes such chunks in the log domain)
-    P = inputs.make_problem("kda_strong", B=1, H=2, T=200)
+    # a chunk whose gate falls by more than twice the plain range (about e^133 per channel)
+    # sets bit 2 of the workspace error flag; the forward still handles it
+    P = inputs.make_problem("kda", B=1, H=2, T=200, la_range=(-4.5, -3.5))
+    assert _chunk_decays(P)[0] > 140.0
     dO, dSf = _cotangents(P, 795)
     ws = torch.zeros(gdr.bwd_workspace_bytes(P.B, P.H, P.T, P.dk, P.dv, has_ab=False),
                      dtype=torch.uint8, device="cuda")
@@ -168,7 +227,6 @@ def test_bwd_flags_gates_beyond_its_range():
     gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), log_alpha=to(P.log_alpha),
                   dS_final=to(dSf), workspace=ws)
     assert gdr.check_workspace_error(ws) & 2
-    # the same through the forward's workspace (the gradient kernels raise it themselves)
     gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), log_alpha=to(P.log_alpha), workspace=ws)
     assert gdr.check_workspace_error(ws) == 0  # the forward handles the chunk
     gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), log_alpha=to(P.log_alpha),
