@@ -93,7 +93,7 @@ def algorithmic_counts(P):
     return th * per_th + state, th * flops_th, th * tri_th
 
 
-def time_gpu(P, steps, warmup, cold_steps):
+def time_gpu(P, steps, warmup, cold_steps, for_backward=False):
     import torch
 
     from chunkwise_gated_delta_amd import gdr
@@ -104,8 +104,16 @@ def time_gpu(P, steps, warmup, cold_steps):
     a, b, S0, cu = to(P.a), to(P.b), to(P.S0), to(P.cu_seqlens)
     out = torch.empty((P.B, P.T, P.H, P.dv), dtype=P.dtype, device=dev)
     fin = torch.empty((P.n_seq, P.H, P.dv, P.dk), dtype=torch.float32, device=dev)
+    ws = None
+    if for_backward:
+        # the forward of a training step: it also keeps the per-chunk states for the backward
+        n_seq = 0 if cu is None else P.n_seq
+        gate = gdr.GATE_NONE if la is None else (gdr.GATE_HEAD if la.dim() == 3 else gdr.GATE_CHANNEL)
+        ws = torch.zeros(gdr.bwd_workspace_bytes(P.B, P.H, P.T, P.dk, P.dv, n_seq=n_seq, gate=gate,
+                                                 has_ab=a is not None), dtype=torch.uint8, device=dev)
     call = lambda: gdr.chunk_fwd(q, k, v, beta, log_alpha=la, a=a, b=b, S0=S0, cu_seqlens=cu,
-                                 chunk_size=P.chunk, out=out, final_state=fin, clip=P.clip)
+                                 chunk_size=P.chunk, out=out, final_state=fin, clip=P.clip,
+                                 workspace=ws, for_backward=for_backward)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -260,6 +268,8 @@ def bench_backward(args):
     a, b = to(P.a), to(P.b)
     S0, cu, dOd, dSd = to(P.S0), to(P.cu_seqlens), to(dO), to(dSf)
     ws = None
+    if args.forward_states:
+        args.forward_workspace = True
     if args.forward_workspace:
         # the backward of a training step: the forward call's workspace (its per-chunk
         # factors) is handed to the backward, which then skips recomputing them
@@ -270,10 +280,11 @@ def bench_backward(args):
                                            has_ab=a is not None))
         ws = torch.zeros(need, dtype=torch.uint8, device=dev)
         gdr.chunk_fwd(q, k, v, beta, log_alpha=la, a=a, b=b, S0=S0, cu_seqlens=cu,
-                      chunk_size=P.chunk, workspace=ws)
+                      chunk_size=P.chunk, workspace=ws, for_backward=args.forward_states)
     call = lambda: gdr.chunk_bwd(q, k, v, beta, dOd, log_alpha=la, a=a, b=b, S0=S0,
                                  dS_final=dSd, cu_seqlens=cu, chunk_size=P.chunk, workspace=ws,
-                                 forward_workspace=args.forward_workspace)
+                                 forward_workspace=args.forward_workspace,
+                                 forward_states=args.forward_states)
     for _ in range(args.warmup):
         g = call()
     torch.cuda.synchronize()
@@ -299,7 +310,7 @@ def bench_backward(args):
     tflops = alg_flops / (call_ms * 1e-3) / 1e12
     result = {
         "metric": f"tokens/s, {args.workload} chunk bwd (all input gradients"
-                  f"{', forward workspace reused' if args.forward_workspace else ''}), 1xMI355X",
+                  f"{', forward states reused' if args.forward_states else (', forward workspace reused' if args.forward_workspace else '')}), 1xMI355X",
         "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -370,6 +381,12 @@ def main():
     ap.add_argument("--forward-workspace", action="store_true",
                     help="with --backward: hand the backward the workspace of a forward call on "
                          "the same inputs (GDR_BWD_FORWARD_WORKSPACE), as a training step does")
+    ap.add_argument("--for-backward", action="store_true",
+                    help="forward only: time gdr_chunk_fwd_for_bwd (the forward of a training "
+                         "step, which also keeps the per-chunk states for the backward)")
+    ap.add_argument("--forward-states", action="store_true",
+                    help="with --backward: the forward call also kept its per-chunk states "
+                         "(gdr_chunk_fwd_for_bwd, GDR_BWD_FORWARD_STATES)")
     ap.add_argument("--copy-cal", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (calibrates the HBM "
                          "traffic counters: FETCH_SIZE/WRITE_SIZE per byte actually moved)")
@@ -402,19 +419,21 @@ def main():
 
     P = inputs.make_problem(args.workload)
     alg_bytes, alg_flops, tri_flops = algorithmic_counts(P)
-    ms, launch_ms, cold_ms, out, fin = time_gpu(P, args.steps, args.warmup, args.cold_steps)
+    ms, launch_ms, cold_ms, out, fin = time_gpu(P, args.steps, args.warmup, args.cold_steps,
+                                                for_backward=args.for_backward)
     call_ms = float(np.mean(launch_ms))
     tokens = P.B * P.T  # packed total for the varlen workload (B = 1)
     achieved_gbs = alg_bytes / (call_ms * 1e-3) / 1e9
     tflops = alg_flops / (call_ms * 1e-3) / 1e12
-    headline = args.workload == WORKLOAD
+    headline = args.workload == WORKLOAD and not args.for_backward
     cc = committed_counters() if headline else {}
     traffic = cc.get("traffic_bytes_per_launch")
     pct = lambda xs, f: xs[min(len(xs) - 1, int(f * len(xs)))]
 
     result = {
         "metric": ("tokens/s + MFMA util % for KDA chunk fwd, T=8192 H=32 d=128, 1xMI355X"
-                   if headline else f"tokens/s, {args.workload} chunk fwd, 1xMI355X"),
+                   if headline else f"tokens/s, {args.workload} chunk fwd"
+                   f"{' keeping the states for the backward' if args.for_backward else ''}, 1xMI355X"),
         "value": tokens / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,

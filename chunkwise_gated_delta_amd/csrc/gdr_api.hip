@@ -3,6 +3,7 @@
 #include "../../include/gdr.h"
 #include "gdr_common.h"
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -88,11 +89,11 @@ size_t gdr_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int C, int n
     return workspace_for(a, varlen ? n_seq : B);
 }
 
-int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, const void *b,
-                  const float *log_alpha, const float *beta, const float *S0, void *O,
-                  float *S_final, const int32_t *cu_seqlens, int n_seq, int B, int H, int T,
-                  int dk, int dv, int C, int dtype, int gate, void *workspace,
-                  size_t workspace_bytes, void *stream) {
+namespace {
+int chunk_fwd(const void *q, const void *k, const void *v, const void *a, const void *b,
+              const float *log_alpha, const float *beta, const float *S0, void *O, float *S_final,
+              const int32_t *cu_seqlens, int n_seq, int B, int H, int T, int dk, int dv, int C,
+              int dtype, int gate, void *workspace, size_t workspace_bytes, void *stream, bool keep) {
     if (!q || !k || !v || !beta || !O) return GDR_ERR_NULL;
     if ((a == nullptr) != (b == nullptr)) return GDR_ERR_NULL;
     if (!gate_ok(gate)) return GDR_ERR_SHAPE;
@@ -134,7 +135,14 @@ int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
     args.log_alpha = log_alpha; args.beta = beta; args.S0 = S0;
     args.O = O; args.S_final = S_final; args.cu_seqlens = cu_seqlens;
     args.workspace = workspace; args.workspace_bytes = workspace_bytes;
-    const size_t need = workspace_for(args, N);
+    size_t need = workspace_for(args, N);
+    if (keep) {
+        // the states go where gdr_chunk_bwd reads them: its workspace layout and limits
+        const gdr::BwdArgs bv = gdr::bwd_view(args);
+        if (args.clip || !gdr::kda_bwd_supported(bv)) return GDR_ERR_UNSUPPORTED;
+        args.keep_states = true;
+        need = std::max(need, gdr::kda_bwd_workspace_bytes(bv, N));
+    }
     if (!workspace || workspace_bytes < need) return GDR_ERR_WORKSPACE;
     const Range rws = range(workspace, need);
     for (const Range &r : inputs)
@@ -150,6 +158,25 @@ int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
     if (!split && !gdr::f32_split_supported(args)) return GDR_ERR_UNSUPPORTED;
     const int rc = split ? gdr::launch_kda_split(args, N, s) : gdr::launch_f32_split(args, N, s);
     return rc == 0 ? GDR_OK : GDR_ERR_HIP;
+}
+}  // namespace
+
+int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, const void *b,
+                  const float *log_alpha, const float *beta, const float *S0, void *O,
+                  float *S_final, const int32_t *cu_seqlens, int n_seq, int B, int H, int T,
+                  int dk, int dv, int C, int dtype, int gate, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    return chunk_fwd(q, k, v, a, b, log_alpha, beta, S0, O, S_final, cu_seqlens, n_seq, B, H, T,
+                     dk, dv, C, dtype, gate, workspace, workspace_bytes, stream, false);
+}
+
+int gdr_chunk_fwd_for_bwd(const void *q, const void *k, const void *v, const void *a,
+                          const void *b, const float *log_alpha, const float *beta,
+                          const float *S0, void *O, float *S_final, const int32_t *cu_seqlens,
+                          int n_seq, int B, int H, int T, int dk, int dv, int C, int dtype,
+                          int gate, void *workspace, size_t workspace_bytes, void *stream) {
+    return chunk_fwd(q, k, v, a, b, log_alpha, beta, S0, O, S_final, cu_seqlens, n_seq, B, H, T,
+                     dk, dv, C, dtype, gate, workspace, workspace_bytes, stream, true);
 }
 
 size_t gdr_chunk_bwd_workspace(int B, int H, int T, int dk, int dv, int C, int n_seq, int dtype,
@@ -175,7 +202,7 @@ int gdr_chunk_bwd(const void *q, const void *k, const void *v, const void *a_, c
                   int n_seq, int B, int H, int T, int dk_, int dv_, int C, int dtype, int gate,
                   int flags, void *workspace, size_t workspace_bytes, void *stream) {
     if (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta) return GDR_ERR_NULL;
-    if (flags & ~GDR_BWD_FORWARD_WORKSPACE) return GDR_ERR_SHAPE;
+    if (flags & ~(GDR_BWD_FORWARD_WORKSPACE | GDR_BWD_FORWARD_STATES)) return GDR_ERR_SHAPE;
     const bool has_ab = a_ != nullptr;
     if ((a_ == nullptr) != (b_ == nullptr)) return GDR_ERR_NULL;
     if ((da == nullptr) != !has_ab || (db == nullptr) != !has_ab) return GDR_ERR_NULL;
@@ -193,7 +220,8 @@ int gdr_chunk_bwd(const void *q, const void *k, const void *v, const void *a_, c
     a.grad_la = dlog_alpha; a.grad_beta = dbeta; a.grad_S0 = dS0; a.cu_seqlens = cu_seqlens;
     a.n_seq = varlen ? n_seq : 0;
     a.B = B; a.H = H; a.T = T; a.dk = dk_; a.dv = dv_; a.C = C; a.dtype = dtype; a.gate = gate;
-    a.reuse_fwd = (flags & GDR_BWD_FORWARD_WORKSPACE) != 0;
+    a.reuse_states = (flags & GDR_BWD_FORWARD_STATES) != 0;
+    a.reuse_fwd = a.reuse_states || (flags & GDR_BWD_FORWARD_WORKSPACE) != 0;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     if (!gdr::kda_bwd_supported(a)) return GDR_ERR_UNSUPPORTED;
     const int N = varlen ? n_seq : B;

@@ -110,6 +110,7 @@ struct FwdArgs {
     const int32_t *cu_seqlens;
     int n_seq, B, H, T, dk, dv, C, dtype, gate;  // gate: the layout only (kGate*)
     bool clip;  // spectral clipping of the gate, alpha <- min(alpha, 1 / ||I - b a^T||_2)
+    bool keep_states;  // also leave the per-chunk states for the backward (its workspace layout)
     void *workspace;
     size_t workspace_bytes;
 };
@@ -123,6 +124,7 @@ struct BwdArgs {
     const int32_t *cu_seqlens;
     int n_seq, B, H, T, dk, dv, C, dtype, gate;
     bool reuse_fwd;  // the workspace holds the forward's per-chunk blocks of the same inputs
+    bool reuse_states;  // ... and the states entering each chunk (keep_states forward)
     void *workspace;
     size_t workspace_bytes;
 };
@@ -137,5 +139,6 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t stream);
 bool kda_bwd_supported(const BwdArgs &a);
 size_t kda_bwd_workspace_bytes(const BwdArgs &a, int n_seq_eff);
 int launch_kda_bwd(const BwdArgs &a, int n_seq_eff, hipStream_t stream);
+BwdArgs bwd_view(const FwdArgs &a);  // the backward arguments that share a's shapes
 
 }  // namespace gdr

@@ -1169,7 +1169,8 @@ constexpr int kDepth = 2;
 // writing the state entering each step to p.states; with the slots of a backward
 // block (W' slot: K^, A^ slot: W', K^b slot: Q~, value tile: dO) and DP set this is
 // the backward state pass dS <- dS Diag(gamma_C) + (K^ dS^T)^T W' + dO^T Q~.
-constexpr int kForward = 0, kSaveStates = 1, kReverse = 2;
+// kForwardSave: the forward pass that also stores the states (both of the first two)
+constexpr int kForward = 0, kSaveStates = 1, kReverse = 2, kForwardSave = 3;
 
 template <int DK, bool DP, int MODE = kForward>
 __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
@@ -1177,6 +1178,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     using Bk = Blk<DK, DP>;
     constexpr int KS = L::KS;
     constexpr int NSW = DK / 32;  // waves owning a 32x32 S^T tile
+    constexpr bool kOut = MODE == kForward || MODE == kForwardSave;  // writes O
 
     __shared__ __attribute__((aligned(16))) char smem[L::bytes];
     uint16_t *sS = (uint16_t *)(smem + L::oS);
@@ -1339,11 +1341,11 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
             const uint32_t keep = 0u - (uint32_t)(t0 + (long)cid(c) * kC + vr < t1 && !vzero);
             *(uint4 *)(sV + vr * kVS + vc) = make_uint4(x.V.x & keep, x.V.y & keep, x.V.z & keep, x.V.w & keep);
         }
-        if (MODE == kForward && !vw && c > 0) store_out(c - 1);
+        if (kOut && !vw && c > 0) store_out(c - 1);
         const int cn = c + kDepth < nck ? c + kDepth : nck - 1;
         load_p(nx, cn);
         lds_barrier();  // value tile, gamma_C and S of chunk c visible
-        if (MODE != kForward && emit) {
+        if (MODE != kForward && emit) {  // kSaveStates, kReverse, kForwardSave
             // the state entering this step, bf16, 16 bytes per thread and pass
             uint16_t *dst = p.states + (((size_t)(cbase + cid(c)) * H + h) * DV + j0) * DK;
 #pragma unroll
@@ -1377,7 +1379,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
             for (int q = 0; q < 4; ++q)
                 store4(sVn + l32 * kCS + 32 * rt + 8 * q + 4 * lh, acc[4 * q + 0], acc[4 * q + 1],
                        acc[4 * q + 2], acc[4 * q + 3]);
-        } else if constexpr (MODE == kForward) {
+        } else if constexpr (kOut) {
             // O^T = V^T Ao^T + S Q~^T (operands swapped); register 4q+e is
             // O[row 32rt + l32][dv 8q + 4lh + e]
             acc = mfma32x32(fv[0], as_bf16x8(x.A[0]), acc);
@@ -1443,7 +1445,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
             step(c, buf[0], buf[2]);
             if (c + 1 < nck) step(c + 1, buf[1], buf[0]);
         }
-        if (MODE == kForward && !vw) store_out(nck - 1);
+        if (kOut && !vw) store_out(nck - 1);
     }
 
     if (s_out && wave < NSW) {
@@ -1642,6 +1644,17 @@ KdaWs kda_ws(const FwdArgs &a, int n_seq_eff) {
 
 size_t kda_split_workspace_bytes(const FwdArgs &a, int n_seq_eff) { return kda_ws(a, n_seq_eff).total; }
 
+BwdArgs bwd_view(const FwdArgs &a) {
+    BwdArgs b;
+    std::memset(&b, 0, sizeof(b));
+    b.q = a.q; b.k = a.k; b.v = a.v; b.a = a.a; b.b = a.b;
+    b.log_alpha = a.log_alpha; b.beta = a.beta; b.S0 = a.S0;
+    b.cu_seqlens = a.cu_seqlens;
+    b.n_seq = a.n_seq; b.B = a.B; b.H = a.H; b.T = a.T; b.dk = a.dk; b.dv = a.dv; b.C = a.C;
+    b.dtype = a.dtype; b.gate = a.gate;
+    return b;
+}
+
 int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     const bool varlen = a.cu_seqlens != nullptr;
     const KdaWs kw = kda_ws(a, n_seq_eff);
@@ -1664,7 +1677,15 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     sp.nc = lay.nc; sp.max_chunks = max_chunks; sp.C = kC;
     sp.seg_ws = (float *)(ws + kw.seg_off);
     sp.sub = kw.sub ? (int *)(ws + kw.sub_off) : nullptr;
-    const int runs = kw.runs ? seg_runs(n_seq_eff * a.H, a.dk, a.dv, chunks_per_chain(a), true) : 0;
+    int runs = kw.runs ? seg_runs(n_seq_eff * a.H, a.dk, a.dv, chunks_per_chain(a), true) : 0;
+    if (a.keep_states) {
+        // the backward's layout: the same header, plan, blocks and flags, then the states
+        // entering each chunk where gdr_chunk_bwd reads them, and its segmented-pass area
+        const BwdLayout bl = bwd_layout(bwd_view(a), n_seq_eff);
+        sp.states = (uint16_t *)(ws + bl.s_off);
+        sp.seg_ws = (float *)(ws + bl.seg_off);
+        runs = bl.runs ? seg_runs(n_seq_eff * a.H, a.dk, a.dv, chunks_per_chain(a), true) : 0;
+    }
 
     if (varlen) hipLaunchKernelGGL((chunk_plan_kernel<SplitParams>), dim3(1), dim3(kPlanThreads), 0, s, sp);
     // persistent prep workgroups: two per CU (one with a, b: their LDS allows no more)
@@ -1690,7 +1711,8 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     do {                                                                                    \
         if (a.clip) GDR_GATES(DK, D, true);                                                 \
         else GDR_GATES(DK, D, false);                                                       \
-        run_state<DK, D, kForward>(sp, runs, s);                                            \
+        if (a.keep_states) run_state<DK, D, kForwardSave>(sp, runs, s);                     \
+        else run_state<DK, D, kForward>(sp, runs, s);                                       \
     } while (0)
     if (a.dk == 128) {
         if (dp) GDR_PATH(128, true);
@@ -1775,7 +1797,7 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
             if (sp.sub)                                                                            \
                 hipLaunchKernelGGL((kda_prep_kernel<DK, G, D, false, true>), grid_sub, dim3(kThreads), 0, s, sp); \
         }                                                                                          \
-        run_state<DK, D, kSaveStates>(sp, runs, s);                                               \
+        if (!b.reuse_states) run_state<DK, D, kSaveStates>(sp, runs, s);                          \
         hipLaunchKernelGGL((kda_bwd_reorder_kernel<DK, D>), grid_jobs, dim3(kThreads), 0, s,       \
                            (const char *)sp.blk, rp.blk, (int)njobs);                              \
         run_state<DK, true, kReverse>(rp, runs, s);                                               \

@@ -21,7 +21,8 @@ GATE_NONE, GATE_HEAD, GATE_CHANNEL = 0, 1, 2
 GATE_CLIP = 4  # flag: spectral clipping of the gate, alpha <- min(alpha, 1/||I - b a^T||_2)
 STATUS = {0: "GDR_OK", -1: "GDR_ERR_NULL", -2: "GDR_ERR_SHAPE", -3: "GDR_ERR_UNSUPPORTED",
           -4: "GDR_ERR_WORKSPACE", -5: "GDR_ERR_ALIAS", -6: "GDR_ERR_HIP"}
-EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_workspace", "gdr_chunk_bwd", "gdr_chunk_bwd_workspace",
+EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_for_bwd", "gdr_chunk_fwd_workspace", "gdr_chunk_bwd",
+           "gdr_chunk_bwd_workspace",
            "gdr_workspace_error", "gdr_status_string", "gdr_version")
 
 _lib = None
@@ -47,6 +48,8 @@ def load_library(path: str = LIB_PATH):
         P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         lib.gdr_chunk_fwd.restype = I
         lib.gdr_chunk_fwd.argtypes = [P] * 11 + [I] * 9 + [P, Z, P]
+        lib.gdr_chunk_fwd_for_bwd.restype = I
+        lib.gdr_chunk_fwd_for_bwd.argtypes = [P] * 11 + [I] * 9 + [P, Z, P]
         lib.gdr_chunk_fwd_workspace.restype = Z
         lib.gdr_chunk_fwd_workspace.argtypes = [I] * 10
         lib.gdr_chunk_bwd.restype = I
@@ -99,11 +102,15 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
               output_final_state: bool = True, out: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None,
-              clip: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              clip: bool = False, for_backward: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise forward of S_t = S_{t-1} Diag(alpha_t)(I - b_t a_t^T) + beta_t v_t k_t^T, o_t = S_t q_t.
 
     clip=True clips the gate per token to min(alpha_t, 1/||I - b_t a_t^T||_2)
     (spectral clipping of the GDN2 stability notes, eq. 7; GATE_CLIP in the C ABI).
+
+    for_backward=True (gdr_chunk_fwd_for_bwd): also leave the per-chunk states in
+    `workspace` (required, sized by bwd_workspace_bytes) for a chunk_bwd call with
+    forward_states=True on the same inputs.
 
     q, k, (a, b): [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H] fp32;
     log_alpha: None, [B, T, H] (head gate) or [B, T, H, dk] (channel gate), fp32;
@@ -165,10 +172,13 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     if need == 0:
         raise GdrError(-3, f"no kernel for dtype={q.dtype} dk={dk} dv={dv} C={chunk_size}")
     if workspace is None:
+        if for_backward:
+            raise ValueError("for_backward=True needs the workspace the backward will use")
         workspace = _workspace(q.device, need)
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    entry = lib.gdr_chunk_fwd_for_bwd if for_backward else lib.gdr_chunk_fwd
     with torch.cuda.device(q.device):
-        rc = lib.gdr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha),
+        rc = entry(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha),
                                _ptr(beta), _ptr(S0), _ptr(out), _ptr(final_state),
                                _ptr(cu_seqlens), n_seq, B, H, T, dk, dv, chunk_size, dt, gate,
                                _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
@@ -203,7 +213,7 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
               S0: Optional[torch.Tensor] = None, dS_final: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
               want_dS0: bool = True, workspace: Optional[torch.Tensor] = None,
-              forward_workspace: bool = False) -> dict:
+              forward_workspace: bool = False, forward_states: bool = False) -> dict:
     """Gradients of <dO, O> + <dS_final, S_final> for chunk_fwd.
 
     Shapes as in chunk_fwd; dO like O, dS_final like S_final (None: zero).
@@ -213,6 +223,8 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     forward_workspace=True: `workspace` is the one the chunk_fwd call on the same inputs
     filled (sized for both, see bwd_workspace_bytes); its per-chunk factors are reused
     (GDR_BWD_FORWARD_WORKSPACE).  The caller guarantees the inputs are the same.
+    forward_states=True: the same for a workspace chunk_fwd(for_backward=True) filled; its
+    per-chunk states are reused too (GDR_BWD_FORWARD_STATES).
     """
     lib = load_library()
     if not q.is_cuda:
@@ -265,8 +277,9 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
                                                int(a is not None)))
     if need == 0:
         raise GdrError(-3, f"no backward kernel for dtype={q.dtype} dk={dk} dv={dv} C={chunk_size}")
-    if forward_workspace and workspace is None:
-        raise ValueError("forward_workspace=True needs the workspace chunk_fwd used")
+    if (forward_workspace or forward_states) and workspace is None:
+        raise ValueError("forward_workspace / forward_states need the workspace chunk_fwd used")
+    flags = 2 if forward_states else (1 if forward_workspace else 0)
     if workspace is None:
         workspace = _workspace(q.device, need)
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
@@ -286,7 +299,7 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
                                _ptr(out.get("db")), _ptr(out.get("dlog_alpha")),
                                _ptr(out["dbeta"]), _ptr(out.get("dS0")), _ptr(cu_seqlens),
                                n_seq, B, H, T, dk, dv,
-                               chunk_size, dt, gate, int(bool(forward_workspace)), _ptr(workspace),
+                               chunk_size, dt, gate, flags, _ptr(workspace),
                                workspace.numel(), ctypes.c_void_p(stream))
     if rc != 0:
         raise GdrError(rc, lib.gdr_status_string(rc).decode())

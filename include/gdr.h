@@ -123,6 +123,22 @@ int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
                   int dk, int dv, int C, int dtype, int gate, void *workspace,
                   size_t workspace_bytes, void *stream);
 
+/* gdr_chunk_fwd for a training step: the same computation (the same O and
+ * S_final, bit for bit), which also leaves in `workspace` the state entering
+ * every chunk (bf16, where gdr_chunk_bwd reads it), so that the backward call
+ * with GDR_BWD_FORWARD_STATES skips both its first kernel and its forward state
+ * pass.  The state pass of the chunk form ("Kimi Delta Attention" notes,
+ * forward recap; DPLR notes, section 2) already walks those states; storing
+ * them costs the extra writes only.  Arguments and errors as gdr_chunk_fwd,
+ * plus: the workspace must hold gdr_chunk_bwd_workspace bytes, and only what
+ * gdr_chunk_bwd supports is accepted (else GDR_ERR_UNSUPPORTED; no gate
+ * clipping). */
+int gdr_chunk_fwd_for_bwd(const void *q, const void *k, const void *v, const void *a,
+                          const void *b, const float *log_alpha, const float *beta,
+                          const float *S0, void *O, float *S_final, const int32_t *cu_seqlens,
+                          int n_seq, int B, int H, int T, int dk, int dv, int C, int dtype,
+                          int gate, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace gdr_chunk_bwd needs (arguments as for
  * gdr_chunk_fwd_workspace).  Returns 0 when the arguments are invalid or
  * unsupported.  Zero-fill a workspace before its first use. */
@@ -136,8 +152,11 @@ size_t gdr_chunk_bwd_workspace(int B, int H, int T, int dk, int dv, int C, int n
  *       per-chunk factors are used instead of being recomputed (the forward's first
  *       kernel is skipped).  The workspace must still hold gdr_chunk_bwd_workspace
  *       bytes.  Nothing checks that the inputs are the same: when they differ the
- *       gradients are wrong. */
-enum { GDR_BWD_FORWARD_WORKSPACE = 1 };
+ *       gradients are wrong.
+ *   GDR_BWD_FORWARD_STATES  as GDR_BWD_FORWARD_WORKSPACE (implies it), for a workspace
+ *       that gdr_chunk_fwd_for_bwd filled: its per-chunk states are used as well, and
+ *       the backward's forward state pass is skipped. */
+enum { GDR_BWD_FORWARD_WORKSPACE = 1, GDR_BWD_FORWARD_STATES = 2 };
 
 /* The backward pass of gdr_chunk_fwd: the gradients of
  * L = <dO, O> + <dS_final, S_final> with respect to every input.  Without a, b
@@ -157,7 +176,8 @@ enum { GDR_BWD_FORWARD_WORKSPACE = 1 };
  *   dlog_alpha  shape of log_alpha, fp32      output; NULL exactly when gate is NONE
  *   dbeta       [B, T, H]      fp32           output
  *   dS0         [N, H, dv, dk] fp32 or NULL   output dL/dS0
- *   flags       0 or GDR_BWD_FORWARD_WORKSPACE (other values: GDR_ERR_SHAPE)
+ *   flags       0, GDR_BWD_FORWARD_WORKSPACE or GDR_BWD_FORWARD_STATES (other bits:
+ *               GDR_ERR_SHAPE)
  *
  * Supported: bf16, C = 64, dk in {64, 128}, dv a multiple of 32 up to 256.
  * Outputs may not overlap inputs, each other or the workspace.  Memory,

@@ -166,7 +166,36 @@ def test_backward_flags_validated(lib):
     ptrs[3] = ptrs[4] = ptrs[13] = ptrs[14] = P(None)  # no a, b (and no da, db)
     ptrs[18] = P(None)                                  # no cu_seqlens
     args = ptrs + [0, 1, 2, 64, 128, 128, 64, 1, 2]
-    for flags, want in [(2, -2), (4, -2), (-1, -2)]:
+    for flags, want in [(4, -2), (8, -2), (-1, -2)]:
         assert lib.gdr_chunk_bwd(*args, flags, P(FAKE + (30 << 30)), 16, None) == want
-    # a valid flag gets past that check (and then fails on the too-small workspace)
-    assert lib.gdr_chunk_bwd(*args, 1, P(FAKE + (30 << 30)), 16, None) == -4
+    # valid flags get past that check (and then fail on the too-small workspace)
+    for flags in (1, 2, 3):
+        assert lib.gdr_chunk_bwd(*args, flags, P(FAKE + (30 << 30)), 16, None) == -4
+
+
+def _call_for_bwd(lib, **kw):
+    """gdr_chunk_fwd_for_bwd with _call's defaults (B=1, H=2, T=64, channel gate)."""
+    d = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), a=None, b=None,
+             la=FAKE + (3 << 30), beta=FAKE + (4 << 30), S0=None, O=FAKE + (5 << 30),
+             Sf=FAKE + (6 << 30), cu=None, n_seq=0, B=1, H=2, T=64, dk=128, dv=128, C=64,
+             dtype=1, gate=2, ws=FAKE + (7 << 30), ws_bytes=1 << 20)
+    d.update(kw)
+    return lib.gdr_chunk_fwd_for_bwd(P(d["q"]), P(d["k"]), P(d["v"]), P(d["a"]), P(d["b"]),
+                                     P(d["la"]), P(d["beta"]), P(d["S0"]), P(d["O"]), P(d["Sf"]),
+                                     P(d["cu"]), d["n_seq"], d["B"], d["H"], d["T"], d["dk"],
+                                     d["dv"], d["C"], d["dtype"], d["gate"], P(d["ws"]),
+                                     d["ws_bytes"], None)
+
+
+def test_forward_for_backward_validated(lib):
+    # the forward that keeps its states for the backward takes only what the backward
+    # supports, and the backward's workspace; every case fails before any launch
+    fwd = lib.gdr_chunk_fwd_workspace(1, 2, 64, 128, 128, 64, 0, 1, 2, 0)
+    bwd = lib.gdr_chunk_bwd_workspace(1, 2, 64, 128, 128, 64, 0, 1, 2, 0)
+    assert bwd > fwd > 0
+    assert _call_for_bwd(lib, ws_bytes=fwd) == -4               # the forward's size is short
+    assert _call_for_bwd(lib, ws=None) == -4
+    assert _call_for_bwd(lib, gate=2 | gdr.GATE_CLIP) == -3     # no clipped backward
+    assert _call_for_bwd(lib, dtype=0, C=32) == -3              # fp32: forward only
+    assert _call_for_bwd(lib, q=None) == -1
+    assert _call_for_bwd(lib, O=FAKE) == -5

@@ -260,7 +260,10 @@ def test_bwd_segmented_without_final_state_gradient():
                                        ("dplr", dict(B=1, H=2, T=300)),
                                        ("kda", dict(B=1, H=2, T=2048)),  # segmented passes
                                        ("kda_varlen", dict(n_seq=3, total=700, min_len=1, H=2))])
-def test_bwd_reuses_forward_workspace(kind, spec):
+@pytest.mark.parametrize("states", [False, True])
+def test_bwd_reuses_forward_workspace(kind, spec, states):
+    # states=True: the forward also kept the per-chunk states (gdr_chunk_fwd_for_bwd), and
+    # the backward skips its own forward state pass as well
     P = inputs.make_problem(kind, s0_scale=0.3, **spec)
     dO, dSf = _cotangents(P, 810)
     to = lambda t: None if t is None else t.to("cuda")
@@ -273,9 +276,12 @@ def test_bwd_reuses_forward_workspace(kind, spec):
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     args = dict(log_alpha=to(P.log_alpha), a=to(P.a), b=to(P.b), S0=to(P.S0),
                 cu_seqlens=to(P.cu_seqlens))
-    gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), workspace=ws, **args)
+    O1, S1 = gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), workspace=ws,
+                           for_backward=states, **args)
+    O2, S2 = gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), **args)
+    assert torch.equal(O1, O2) and torch.equal(S1, S2)  # the same forward, bit for bit
     g1 = gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), dS_final=to(dSf),
-                       workspace=ws, forward_workspace=True, **args)
+                       workspace=ws, forward_workspace=True, forward_states=states, **args)
     g2 = gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), dS_final=to(dSf), **args)
     torch.cuda.synchronize()
     for key in g1:  # the same factors: the same bits, except for the order of the fp32
