@@ -268,6 +268,8 @@ def bench_backward(args):
     a, b = to(P.a), to(P.b)
     S0, cu, dOd, dSd = to(P.S0), to(P.cu_seqlens), to(dO), to(dSf)
     ws = None
+    if args.train_step:
+        args.forward_states = True
     if args.forward_states:
         args.forward_workspace = True
     if args.forward_workspace:
@@ -281,10 +283,18 @@ def bench_backward(args):
         ws = torch.zeros(need, dtype=torch.uint8, device=dev)
         gdr.chunk_fwd(q, k, v, beta, log_alpha=la, a=a, b=b, S0=S0, cu_seqlens=cu,
                       chunk_size=P.chunk, workspace=ws, for_backward=args.forward_states)
-    call = lambda: gdr.chunk_bwd(q, k, v, beta, dOd, log_alpha=la, a=a, b=b, S0=S0,
-                                 dS_final=dSd, cu_seqlens=cu, chunk_size=P.chunk, workspace=ws,
-                                 forward_workspace=args.forward_workspace,
-                                 forward_states=args.forward_states)
+    bwd = lambda: gdr.chunk_bwd(q, k, v, beta, dOd, log_alpha=la, a=a, b=b, S0=S0,
+                                dS_final=dSd, cu_seqlens=cu, chunk_size=P.chunk, workspace=ws,
+                                forward_workspace=args.forward_workspace,
+                                forward_states=args.forward_states)
+    if args.train_step:
+        # one training step of the layer: the forward that keeps its states, then the backward
+        def call():
+            gdr.chunk_fwd(q, k, v, beta, log_alpha=la, a=a, b=b, S0=S0, cu_seqlens=cu,
+                          chunk_size=P.chunk, workspace=ws, for_backward=True)
+            return bwd()
+    else:
+        call = bwd
     for _ in range(args.warmup):
         g = call()
     torch.cuda.synchronize()
@@ -305,12 +315,17 @@ def bench_backward(args):
     launch_ms = sorted(a.elapsed_time(b) for a, b in per)
     call_ms = float(np.mean(launch_ms))
     alg_bytes, alg_flops = backward_counts(P)
+    if args.train_step:
+        fb, ff, _ = algorithmic_counts(P)
+        alg_bytes, alg_flops = alg_bytes + fb, alg_flops + ff
     tokens = P.B * P.T
     gbs = alg_bytes / (call_ms * 1e-3) / 1e9
     tflops = alg_flops / (call_ms * 1e-3) / 1e12
     result = {
-        "metric": f"tokens/s, {args.workload} chunk bwd (all input gradients"
-                  f"{', forward states reused' if args.forward_states else (', forward workspace reused' if args.forward_workspace else '')}), 1xMI355X",
+        "metric": (f"tokens/s, {args.workload} chunk training step (forward keeping its states, "
+                   "then all input gradients), 1xMI355X" if args.train_step else
+                   f"tokens/s, {args.workload} chunk bwd (all input gradients"
+                   f"{', forward states reused' if args.forward_states else (', forward workspace reused' if args.forward_workspace else '')}), 1xMI355X"),
         "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -384,6 +399,9 @@ def main():
     ap.add_argument("--for-backward", action="store_true",
                     help="forward only: time gdr_chunk_fwd_for_bwd (the forward of a training "
                          "step, which also keeps the per-chunk states for the backward)")
+    ap.add_argument("--train-step", action="store_true",
+                    help="with --backward: time a whole training step of the layer "
+                         "(gdr_chunk_fwd_for_bwd, then gdr_chunk_bwd on its states)")
     ap.add_argument("--forward-states", action="store_true",
                     help="with --backward: the forward call also kept its per-chunk states "
                          "(gdr_chunk_fwd_for_bwd, GDR_BWD_FORWARD_STATES)")

@@ -213,6 +213,12 @@ def test_bwd_strong_gates(case):
                       workspace=ws, forward_workspace=True, **args)
     assert gdr.check_workspace_error(ws) == 0
     _check(P, {k: v.to(torch.float64).cpu().numpy() for k, v in g.items()}, ref)
+    # and through the forward that keeps its per-chunk states
+    gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), workspace=ws, for_backward=True, **args)
+    g = gdr.chunk_bwd(to(P.q), to(P.k), to(P.v), to(P.beta), to(dO), dS_final=to(dSf),
+                      workspace=ws, forward_states=True, **args)
+    assert gdr.check_workspace_error(ws) == 0
+    _check(P, {k: v.to(torch.float64).cpu().numpy() for k, v in g.items()}, ref)
 
 
 def test_bwd_flags_gates_beyond_its_range():
