@@ -264,6 +264,7 @@ def test_bwd_segmented_without_final_state_gradient():
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("kind,spec", [("kda", dict(B=2, H=2, T=300)), ("gdn", dict(B=1, H=3, T=200)),
                                        ("dplr", dict(B=1, H=2, T=300)),
+                                       ("kda", dict(B=1, H=2, T=300, gate=gdr.GATE_NONE)),
                                        ("kda", dict(B=1, H=2, T=2048)),  # segmented passes
                                        ("kda_varlen", dict(n_seq=3, total=700, min_len=1, H=2))])
 @pytest.mark.parametrize("states", [False, True])
