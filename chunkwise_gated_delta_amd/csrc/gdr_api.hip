@@ -4,6 +4,7 @@
 #include "gdr_common.h"
 
 #include <algorithm>
+#include <initializer_list>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -32,6 +33,14 @@ Range range(const void *p, size_t bytes) {
 }
 
 bool overlaps(Range a, Range b) { return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+// Every tensor and the workspace must start on a 16-byte boundary: the kernels move
+// them with 16-byte vector loads and stores.  NULL pointers pass.
+bool aligned16(std::initializer_list<const void *> ptrs) {
+    for (const void *p : ptrs)
+        if (((uintptr_t)p & 15u) != 0) return false;
+    return true;
+}
 
 bool shape_ok(int B, int H, int T, int dk, int dv, int n_seq, bool varlen) {
     if (B < 1 || H < 1 || T < 1) return false;
@@ -104,6 +113,8 @@ int chunk_fwd(const void *q, const void *k, const void *v, const void *a, const 
     const bool has_ab = a != nullptr;
     const int sup = supported(dtype, dk, dv, C, has_ab);
     if (sup != GDR_OK) return sup;
+    if (!aligned16({q, k, v, a, b, log_alpha, beta, S0, O, S_final, cu_seqlens, workspace}))
+        return GDR_ERR_ALIGN;
     const int N = varlen ? n_seq : B;
 
     // Bytes of every tensor, for the alias check.
@@ -224,6 +235,9 @@ int gdr_chunk_bwd(const void *q, const void *k, const void *v, const void *a_, c
     a.reuse_fwd = a.reuse_states || (flags & GDR_BWD_FORWARD_WORKSPACE) != 0;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     if (!gdr::kda_bwd_supported(a)) return GDR_ERR_UNSUPPORTED;
+    if (!aligned16({q, k, v, a_, b_, log_alpha, beta, S0, dO, dS_final, dq, dk, dv, da, db,
+                    dlog_alpha, dbeta, dS0, cu_seqlens, workspace}))
+        return GDR_ERR_ALIGN;
     const int N = varlen ? n_seq : B;
 
     const size_t tokens = (size_t)B * T, es = elem_size(dtype);
@@ -283,6 +297,7 @@ const char *gdr_status_string(int status) {
         case GDR_ERR_WORKSPACE: return "workspace missing or too small";
         case GDR_ERR_ALIAS: return "output overlaps an input or the workspace";
         case GDR_ERR_HIP: return "HIP launch failed";
+        case GDR_ERR_ALIGN: return "a tensor or the workspace is not 16-byte aligned";
         default: return "unknown status";
     }
 }

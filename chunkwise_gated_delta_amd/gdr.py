@@ -20,7 +20,7 @@ GDR_F32, GDR_BF16 = 0, 1
 GATE_NONE, GATE_HEAD, GATE_CHANNEL = 0, 1, 2
 GATE_CLIP = 4  # flag: spectral clipping of the gate, alpha <- min(alpha, 1/||I - b a^T||_2)
 STATUS = {0: "GDR_OK", -1: "GDR_ERR_NULL", -2: "GDR_ERR_SHAPE", -3: "GDR_ERR_UNSUPPORTED",
-          -4: "GDR_ERR_WORKSPACE", -5: "GDR_ERR_ALIAS", -6: "GDR_ERR_HIP"}
+          -4: "GDR_ERR_WORKSPACE", -5: "GDR_ERR_ALIAS", -6: "GDR_ERR_HIP", -7: "GDR_ERR_ALIGN"}
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_for_bwd", "gdr_chunk_fwd_workspace", "gdr_chunk_bwd",
            "gdr_chunk_bwd_workspace",
            "gdr_workspace_error", "gdr_status_string", "gdr_version")
@@ -86,8 +86,19 @@ def workspace_bytes(B, H, T, dk, dv, C=64, n_seq=0, dtype=torch.bfloat16, gate=G
                                            int(bool(has_ab))))
 
 
+def _ws_key(device: torch.device):
+    return (device.type, device.index, torch.cuda.current_stream(device).cuda_stream)
+
+
 def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    key = (device.type, device.index)
+    """The default workspace of the current stream on `device` (grown on demand).
+
+    One buffer per (device, stream): calls that pass no workspace on different
+    streams never share one.  The buffer is allocated on that stream and used only
+    there, so when it is replaced by a larger one the caching allocator hands the old
+    memory out again only to work ordered after everything already enqueued on it.
+    """
+    key = _ws_key(device)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -192,7 +203,7 @@ def check_workspace_error(workspace: Optional[torch.Tensor] = None, device=None)
     lib = load_library()
     if workspace is None:
         dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
-        workspace = _ws_cache.get((dev.type, dev.index))
+        workspace = _ws_cache.get(_ws_key(dev))
         if workspace is None:
             return 0
     stream = torch.cuda.current_stream(workspace.device).cuda_stream

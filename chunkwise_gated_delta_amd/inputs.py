@@ -9,7 +9,8 @@ ranges used to study the method (the pages report no dataset for this path):
 1. ``deltanet_f32``  DeltaNet, no gate, fp32:   B=1  H=2  T=256   dk=dv=64
 2. ``gdn``           Gated DeltaNet, head gate:  B=4  H=16 T=4096  dk=dv=128
 3. ``kda``           KDA, per-channel gate:      B=2  H=32 T=8192  dk=dv=128
-4. ``dplr``          gated DPLR, distinct a, b:  B=1  H=16 T=16384 dk=dv=128
+4. ``dplr``          gated DPLR, distinct a, b:  B=1  H=16 T=16384 dk=dv=128; the drawn
+                     beta scales b only and the write term is unscaled (beta = 1 is passed)
 5. ``kda_varlen``    KDA, 8 packed sequences:    32768 tokens, H=32, dk=dv=128
 6. ``gdn2_clip``     GDN2 form with the spectral gate clip: the ``dplr`` shapes, with
                      the write key tied to b (b = beta k, as in the GDN2 form)
@@ -180,6 +181,9 @@ def make_problem(kind: str, *, seed: Optional[int] = None, B=None, H=None, T=Non
         a, b = _cast(a32, dt), _cast(b32, dt)
         if spec.get("gdn2"):
             k = kb
+        if spec.get("unit_write"):
+            # the drawn beta lives on in b only: the write term is v k^T, unscaled
+            beta = np.ones_like(beta)
     S0 = None
     if spec.get("s0_scale"):
         n = len(cu) - 1 if cu is not None else B_
@@ -209,8 +213,10 @@ WORKLOADS = {
                 gate=GATE_HEAD, la_range=(-0.1, -0.001)),
     "kda": dict(seed=3, B=2, H=32, T=8192, dk=128, dv=128, dtype=torch.bfloat16,
                 gate=GATE_CHANNEL, la_range=(-0.2, -0.001)),
+    # the DPLR notes' form (section 2): b = beta unit(a + 0.1 noise), write term v k^T
+    # unscaled, so the library's write scale is 1
     "dplr": dict(seed=4, B=1, H=16, T=16384, dk=128, dv=128, dtype=torch.bfloat16,
-                 gate=GATE_CHANNEL, la_range=(-0.1, -0.001), dplr=True),
+                 gate=GATE_CHANNEL, la_range=(-0.1, -0.001), dplr=True, unit_write=True),
     "kda_varlen": dict(seed=5, varlen=True, n_seq=8, total=32768, min_len=256, H=32, dk=128,
                        dv=128, dtype=torch.bfloat16, gate=GATE_CHANNEL, la_range=(-0.2, -0.001),
                        s0_scale=0.1),

@@ -53,7 +53,8 @@ typedef enum {
     GDR_ERR_UNSUPPORTED = -3, /* valid, but no kernel for this dtype/shape/chunk size */
     GDR_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than gdr_chunk_fwd_workspace() */
     GDR_ERR_ALIAS = -5,       /* O or S_final overlaps an input it must not overwrite */
-    GDR_ERR_HIP = -6          /* a HIP runtime call failed */
+    GDR_ERR_HIP = -6,         /* a HIP runtime call failed */
+    GDR_ERR_ALIGN = -7        /* a tensor pointer or the workspace is not 16-byte aligned */
 } gdr_status;
 
 /* Element type of q, k, v, a, b and O.  log_alpha, beta, S0 and S_final are

@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.gdr_version() >= 100
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         s = lib.gdr_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.gdr_status_string(-99).decode() == "unknown status"
@@ -158,6 +158,25 @@ def test_aliasing_rejected(lib):
     assert _call(lib, Sf=FAKE + (2 << 30)) == -5          # S_final on top of v
     assert _call(lib, S0=FAKE + (10 << 30), Sf=FAKE + (10 << 30) + 64) == -5  # partial overlap
     assert _call(lib, ws=FAKE + (5 << 30)) == -5          # workspace on top of O
+
+
+def test_misaligned_pointers_rejected(lib):
+    # every tensor and the workspace must start on a 16-byte boundary: a contiguous view
+    # with a storage offset (here 2 bytes: one bf16 element) is refused before any launch
+    assert _call(lib, q=FAKE + 2) == -7
+    assert _call(lib, v=FAKE + (2 << 30) + 8) == -7
+    assert _call(lib, beta=FAKE + (4 << 30) + 4) == -7
+    assert _call(lib, O=FAKE + (5 << 30) + 2) == -7
+    assert _call(lib, ws=FAKE + (7 << 30) + 2) == -7
+    assert _call_for_bwd(lib, q=FAKE + 2) == -7
+    assert lib.gdr_status_string(-7).decode() != "unknown status"
+    # the backward: dq offset by one bf16 element
+    ptrs = [P(FAKE + (i << 30)) for i in range(19)]
+    ptrs[3] = ptrs[4] = ptrs[13] = ptrs[14] = P(None)  # no a, b (and no da, db)
+    ptrs[18] = P(None)                                  # no cu_seqlens
+    ptrs[10] = P(FAKE + (10 << 30) + 2)
+    args = ptrs + [0, 1, 2, 64, 128, 128, 64, 1, 2]
+    assert lib.gdr_chunk_bwd(*args, 0, P(FAKE + (30 << 30)), 1 << 40, None) == -7
 
 
 def test_backward_flags_validated(lib):

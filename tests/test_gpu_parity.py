@@ -56,27 +56,17 @@ def test_small_full_compare(kind):
     _check(P, O, Sf)
 
 
-FULL_CHAINS = {
-    "gdn": [(0, 0), (3, 15), (1, 7)],
-    "kda": [(0, 0), (1, 31), (0, 17)],
-    "dplr": [(0, 0), (0, 11)],
-    "kda_varlen": None,  # filled in: shortest and longest sequence
-    "gdn2_clip": [(0, 0), (0, 13)],
-}
-
-
 @pytest.mark.parametrize("kind", ["gdn", "kda", "dplr", "kda_varlen", "gdn2_clip"])
-def test_full_size_sampled(kind):
+def test_full_size_all_chains(kind):
+    # the workload exactly as the benchmark launches it, every (sequence, head) chain
+    # against the oracle (all host threads): this pins the chain-dependent parts at full
+    # size -- the XCD deal, the longest-first order of packed sequences, the segmented runs
     P = inputs.make_problem(kind)
-    chains = FULL_CHAINS[kind]
-    if chains is None:
-        lens = np.diff(P.cu_seqlens.numpy())
-        chains = [(int(np.argmin(lens)), 0), (int(np.argmax(lens)), 31), (3, 9)]
     # NaN canary: every output element must be written.
     out = torch.full((P.B, P.T, P.H, P.dv), float("nan"), dtype=P.dtype, device="cuda")
     O, Sf = gpu_run(P, out=out)
     assert np.isfinite(O).all() and np.isfinite(Sf).all()
-    _check(P, O, Sf, chains=chains)
+    _check(P, O, Sf)
 
 
 # ---------------------------------------------------------------------------
@@ -378,12 +368,12 @@ def test_strong_gate_varlen():
     _check(P, O, Sf)
 
 
-def test_strong_gate_full_size_sampled():
+def test_strong_gate_full_size_all_chains():
     P = inputs.make_problem("kda_strong")
     out = torch.full((P.B, P.T, P.H, P.dv), float("nan"), dtype=P.dtype, device="cuda")
     O, Sf = gpu_run(P, out=out)
     assert np.isfinite(O).all() and np.isfinite(Sf).all()
-    _check(P, O, Sf, chains=[(0, 0), (1, 31), (0, 17)])
+    _check(P, O, Sf)
 
 
 def test_fp32_path_flags_gates_beyond_its_range():
