@@ -125,7 +125,13 @@ def test_generators_are_deterministic_and_shaped():
     nq = torch.linalg.vector_norm(P1.q.float(), dim=-1)
     assert torch.all((nq - 1).abs() < 1e-2)
     assert float(P1.log_alpha.max()) <= -0.001 and float(P1.log_alpha.min()) >= -0.1
-    assert float(P1.beta.min()) >= 0 and float(P1.beta.max()) < 1
+    # the DPLR workload's write term is unscaled (beta = 1); the drawn beta in [0, 1)
+    # scales b = beta unit(a + 0.1 noise), so |b| < 1
+    assert torch.all(P1.beta == 1)
+    nb = torch.linalg.vector_norm(P1.b.float(), dim=-1)
+    assert float(nb.max()) < 1 + 1e-2 and float(nb.min()) >= 0
+    P3 = inputs.make_problem("kda", T=64, H=4)
+    assert float(P3.beta.min()) >= 0 and float(P3.beta.max()) < 1
 
 
 def test_dirichlet_split_full_size():
