@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <mutex>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -86,6 +87,33 @@ size_t workspace_for(const FwdArgs &a, int n_seq_eff) {
 
 }  // namespace
 
+// Scratch of gdr_chunk_fwd_noalloc: the forward's workspace in a fixed device array,
+// one per GPU (each device that loads the library holds its own copy until the process
+// ends).  Host code never uses the array's name as an address: the device address of
+// the current device's copy comes from hipGetSymbolAddress, once per device, and is
+// kept in scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)GDR_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (NULL on failure).
+void *scratch_of_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        scratch_ptr[dev] = ptr;
+    }
+    return scratch_ptr[dev];
+}
+}  // namespace
+
 extern "C" {
 
 size_t gdr_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int C, int n_seq, int dtype,
@@ -102,7 +130,8 @@ namespace {
 int chunk_fwd(const void *q, const void *k, const void *v, const void *a, const void *b,
               const float *log_alpha, const float *beta, const float *S0, void *O, float *S_final,
               const int32_t *cu_seqlens, int n_seq, int B, int H, int T, int dk, int dv, int C,
-              int dtype, int gate, void *workspace, size_t workspace_bytes, void *stream, bool keep) {
+              int dtype, int gate, void *workspace, size_t workspace_bytes, void *stream, bool keep,
+              int *err_word = nullptr, bool use_scratch = false) {
     if (!q || !k || !v || !beta || !O) return GDR_ERR_NULL;
     if ((a == nullptr) != (b == nullptr)) return GDR_ERR_NULL;
     if (!gate_ok(gate)) return GDR_ERR_SHAPE;
@@ -113,7 +142,8 @@ int chunk_fwd(const void *q, const void *k, const void *v, const void *a, const 
     const bool has_ab = a != nullptr;
     const int sup = supported(dtype, dk, dv, C, has_ab);
     if (sup != GDR_OK) return sup;
-    if (!aligned16({q, k, v, a, b, log_alpha, beta, S0, O, S_final, cu_seqlens, workspace}))
+    if (!aligned16({q, k, v, a, b, log_alpha, beta, S0, O, S_final, cu_seqlens, workspace}) ||
+        ((uintptr_t)err_word & 3u) != 0)
         return GDR_ERR_ALIGN;
     const int N = varlen ? n_seq : B;
 
@@ -146,6 +176,7 @@ int chunk_fwd(const void *q, const void *k, const void *v, const void *a, const 
     args.log_alpha = log_alpha; args.beta = beta; args.S0 = S0;
     args.O = O; args.S_final = S_final; args.cu_seqlens = cu_seqlens;
     args.workspace = workspace; args.workspace_bytes = workspace_bytes;
+    args.err = err_word;
     size_t need = workspace_for(args, N);
     if (keep) {
         // the states go where gdr_chunk_bwd reads them: its workspace layout and limits
@@ -154,11 +185,25 @@ int chunk_fwd(const void *q, const void *k, const void *v, const void *a, const 
         args.keep_states = true;
         need = std::max(need, gdr::kda_bwd_workspace_bytes(bv, N));
     }
+    if (use_scratch) {
+        // the fixed per-GPU array stands in for the workspace (set up on first use)
+        if (need > kScratchBytes) return GDR_ERR_WORKSPACE;
+        workspace = scratch_of_current_device();
+        if (workspace == nullptr) return GDR_ERR_HIP;
+        workspace_bytes = kScratchBytes;
+        args.workspace = workspace; args.workspace_bytes = workspace_bytes;
+    }
     if (!workspace || workspace_bytes < need) return GDR_ERR_WORKSPACE;
     const Range rws = range(workspace, need);
     for (const Range &r : inputs)
         if (overlaps(rws, r)) return GDR_ERR_ALIAS;
     if (overlaps(rws, rO) || overlaps(rws, rsf)) return GDR_ERR_ALIAS;
+    if (err_word) {
+        const Range rerr = range(err_word, sizeof(int));
+        for (const Range &r : inputs)
+            if (overlaps(rerr, r)) return GDR_ERR_ALIAS;
+        if (overlaps(rerr, rO) || overlaps(rerr, rsf) || overlaps(rerr, rws)) return GDR_ERR_ALIAS;
+    }
 
     hipStream_t s = (hipStream_t)stream;
     const bool split = gdr::kda_split_supported(args);
@@ -179,6 +224,15 @@ int gdr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
                   size_t workspace_bytes, void *stream) {
     return chunk_fwd(q, k, v, a, b, log_alpha, beta, S0, O, S_final, cu_seqlens, n_seq, B, H, T,
                      dk, dv, C, dtype, gate, workspace, workspace_bytes, stream, false);
+}
+
+int gdr_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *a,
+                          const void *b, const float *log_alpha, const float *beta,
+                          const float *S0, void *O, float *S_final, const int32_t *cu_seqlens,
+                          int n_seq, int B, int H, int T, int dk, int dv, int C, int dtype,
+                          int gate, int *flags, void *stream) {
+    return chunk_fwd(q, k, v, a, b, log_alpha, beta, S0, O, S_final, cu_seqlens, n_seq, B, H, T,
+                     dk, dv, C, dtype, gate, nullptr, 0, stream, false, flags, true);
 }
 
 int gdr_chunk_fwd_for_bwd(const void *q, const void *k, const void *v, const void *a,

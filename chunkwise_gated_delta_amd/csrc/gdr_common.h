@@ -113,6 +113,7 @@ struct FwdArgs {
     bool keep_states;  // also leave the per-chunk states for the backward (its workspace layout)
     void *workspace;
     size_t workspace_bytes;
+    int *err;  // device error word; NULL: the one in the workspace header
 };
 
 // Arguments of the backward pass (a, b NULL: the KDA form a = k, b = beta k).

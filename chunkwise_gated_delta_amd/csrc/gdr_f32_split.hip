@@ -774,7 +774,7 @@ int launch_f32_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     fp.la = a.log_alpha; fp.beta = a.beta; fp.S0 = a.S0;
     fp.O = a.O; fp.Sf = a.S_final; fp.cu = a.cu_seqlens;
     char *ws = (char *)a.workspace;
-    fp.err = (int *)ws;
+    fp.err = a.err ? a.err : (int *)ws;
     const bool varlen = a.cu_seqlens != nullptr;
     fp.coff = varlen ? (int32_t *)(ws + lay.coff_off) : nullptr;
     fp.order = varlen ? fp.coff + n_seq_eff + 1 : nullptr;

@@ -1668,7 +1668,7 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     sp.la = a.log_alpha; sp.beta = a.beta; sp.S0 = a.S0;
     sp.O = (bf16 *)a.O; sp.Sf = a.S_final; sp.cu = a.cu_seqlens;
     char *ws = (char *)a.workspace;
-    sp.err = (int *)ws;
+    sp.err = a.err ? a.err : (int *)ws;
     sp.coff = varlen ? (int32_t *)(ws + lay.coff_off) : nullptr;
     sp.order = varlen ? sp.coff + n_seq_eff + 1 : nullptr;
     sp.blk = ws + lay.blk_off;

@@ -21,7 +21,9 @@ GATE_NONE, GATE_HEAD, GATE_CHANNEL = 0, 1, 2
 GATE_CLIP = 4  # flag: spectral clipping of the gate, alpha <- min(alpha, 1/||I - b a^T||_2)
 STATUS = {0: "GDR_OK", -1: "GDR_ERR_NULL", -2: "GDR_ERR_SHAPE", -3: "GDR_ERR_UNSUPPORTED",
           -4: "GDR_ERR_WORKSPACE", -5: "GDR_ERR_ALIAS", -6: "GDR_ERR_HIP", -7: "GDR_ERR_ALIGN"}
-EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_for_bwd", "gdr_chunk_fwd_workspace", "gdr_chunk_bwd",
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GDR_NOALLOC_SCRATCH_BYTES
+EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_for_bwd", "gdr_chunk_fwd_noalloc",
+           "gdr_chunk_fwd_workspace", "gdr_chunk_bwd",
            "gdr_chunk_bwd_workspace",
            "gdr_workspace_error", "gdr_status_string", "gdr_version")
 
@@ -50,6 +52,8 @@ def load_library(path: str = LIB_PATH):
         lib.gdr_chunk_fwd.argtypes = [P] * 11 + [I] * 9 + [P, Z, P]
         lib.gdr_chunk_fwd_for_bwd.restype = I
         lib.gdr_chunk_fwd_for_bwd.argtypes = [P] * 11 + [I] * 9 + [P, Z, P]
+        lib.gdr_chunk_fwd_noalloc.restype = I
+        lib.gdr_chunk_fwd_noalloc.argtypes = [P] * 11 + [I] * 9 + [P, P]
         lib.gdr_chunk_fwd_workspace.restype = Z
         lib.gdr_chunk_fwd_workspace.argtypes = [I] * 10
         lib.gdr_chunk_bwd.restype = I
@@ -113,7 +117,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
               output_final_state: bool = True, out: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None,
-              clip: bool = False, for_backward: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              clip: bool = False, for_backward: bool = False, no_alloc: bool = False,
+              flags: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise forward of S_t = S_{t-1} Diag(alpha_t)(I - b_t a_t^T) + beta_t v_t k_t^T, o_t = S_t q_t.
 
     clip=True clips the gate per token to min(alpha_t, 1/||I - b_t a_t^T||_2)
@@ -122,6 +127,12 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
     for_backward=True (gdr_chunk_fwd_for_bwd): also leave the per-chunk states in
     `workspace` (required, sized by bwd_workspace_bytes) for a chunk_bwd call with
     forward_states=True on the same inputs.
+
+    no_alloc=True (gdr_chunk_fwd_noalloc): the library's fixed per-GPU scratch array
+    replaces the workspace (no workspace argument; at most NOALLOC_SCRATCH_BYTES of it);
+    `flags`, a zeroed int32 device tensor of one element or None, receives the device
+    error bits.  Calls that overlap on one GPU race on that array.  Pass `out` and
+    `final_state` to keep the call free of allocations altogether.
 
     q, k, (a, b): [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H] fp32;
     log_alpha: None, [B, T, H] (head gate) or [B, T, H, dk] (channel gate), fp32;
@@ -182,11 +193,24 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Ten
                                                int(a is not None)))
     if need == 0:
         raise GdrError(-3, f"no kernel for dtype={q.dtype} dk={dk} dv={dv} C={chunk_size}")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    if no_alloc:
+        if for_backward or workspace is not None:
+            raise ValueError("no_alloc=True takes neither a workspace nor for_backward")
+        if flags is not None and (flags.dtype != torch.int32 or flags.device != q.device):
+            raise ValueError("flags must be an int32 tensor on q's device")
+        with torch.cuda.device(q.device):
+            rc = lib.gdr_chunk_fwd_noalloc(
+                _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha), _ptr(beta),
+                _ptr(S0), _ptr(out), _ptr(final_state), _ptr(cu_seqlens), n_seq, B, H, T, dk, dv,
+                chunk_size, dt, gate, _ptr(flags), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise GdrError(rc, lib.gdr_status_string(rc).decode())
+        return out, final_state
     if workspace is None:
         if for_backward:
             raise ValueError("for_backward=True needs the workspace the backward will use")
         workspace = _workspace(q.device, need)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
     entry = lib.gdr_chunk_fwd_for_bwd if for_backward else lib.gdr_chunk_fwd
     with torch.cuda.device(q.device):
         rc = entry(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha),

@@ -140,6 +140,34 @@ int gdr_chunk_fwd_for_bwd(const void *q, const void *k, const void *v, const voi
                           int n_seq, int B, int H, int T, int dk, int dv, int C, int dtype,
                           int gate, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Size of the fixed scratch array behind gdr_chunk_fwd_noalloc, per GPU (64 MiB). */
+#define GDR_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* gdr_chunk_fwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The same kernels and the same results, bit for bit.
+ * The workspace is a fixed device array of GDR_NOALLOC_SCRATCH_BYTES that every
+ * GPU the library runs on holds from the first such call until the process
+ * ends; the call itself allocates nothing (no hipMalloc, no library allocator).
+ *
+ *   q ... C, dtype, gate, stream   as for gdr_chunk_fwd
+ *   flags   NULL, or a device int (4-byte aligned, owned by the caller) into which
+ *           the call ORs the device error bits gdr_workspace_error would report
+ *           (bit 1: malformed cu_seqlens were clamped); zero it before its first use
+ *
+ * Limits and errors: as gdr_chunk_fwd, plus GDR_ERR_WORKSPACE when the call would
+ * need more than the array holds (gdr_chunk_fwd_workspace(...) >
+ * GDR_NOALLOC_SCRATCH_BYTES; at dk = 128 roughly H * T <= 64K token-heads), and
+ * GDR_ERR_HIP when the array's address cannot be obtained.  Every call on one GPU
+ * uses that GPU's single array, which keeps the last call's contents: calls that
+ * overlap in time on one GPU (on different streams, or from several threads
+ * without ordering) race and give wrong results; serialise them on one stream. */
+int gdr_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *a,
+                          const void *b, const float *log_alpha, const float *beta,
+                          const float *S0, void *O, float *S_final, const int32_t *cu_seqlens,
+                          int n_seq, int B, int H, int T, int dk, int dv, int C, int dtype,
+                          int gate, int *flags, void *stream);
+
 /* Bytes of device workspace gdr_chunk_bwd needs (arguments as for
  * gdr_chunk_fwd_workspace).  Returns 0 when the arguments are invalid or
  * unsupported.  Zero-fill a workspace before its first use. */

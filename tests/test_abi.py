@@ -179,6 +179,38 @@ def test_misaligned_pointers_rejected(lib):
     assert lib.gdr_chunk_bwd(*args, 0, P(FAKE + (30 << 30)), 1 << 40, None) == -7
 
 
+def _call_noalloc(lib, **kw):
+    """gdr_chunk_fwd_noalloc with _call's defaults (B=1, H=2, T=64, channel gate)."""
+    d = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), a=None, b=None,
+             la=FAKE + (3 << 30), beta=FAKE + (4 << 30), S0=None, O=FAKE + (5 << 30),
+             Sf=FAKE + (6 << 30), cu=None, n_seq=0, B=1, H=2, T=64, dk=128, dv=128, C=64,
+             dtype=1, gate=2, flags=None)
+    d.update(kw)
+    return lib.gdr_chunk_fwd_noalloc(P(d["q"]), P(d["k"]), P(d["v"]), P(d["a"]), P(d["b"]),
+                                     P(d["la"]), P(d["beta"]), P(d["S0"]), P(d["O"]), P(d["Sf"]),
+                                     P(d["cu"]), d["n_seq"], d["B"], d["H"], d["T"], d["dk"],
+                                     d["dv"], d["C"], d["dtype"], d["gate"], P(d["flags"]), None)
+
+
+def test_noalloc_validated_before_any_setup(lib):
+    # the host checks of gdr_chunk_fwd, in the same order, then the scratch size: none of
+    # these calls reaches the device (the scratch is set up only after them)
+    assert _call_noalloc(lib, q=None) == -1
+    assert _call_noalloc(lib, T=0) == -2
+    assert _call_noalloc(lib, C=32) == -3
+    assert _call_noalloc(lib, q=FAKE + 2) == -7
+    assert _call_noalloc(lib, flags=FAKE + (8 << 30) + 2) == -7   # an int: 4-byte aligned
+    assert _call_noalloc(lib, O=FAKE) == -5
+    # more than the fixed array holds: refused, whatever the inputs
+    big = dict(B=2, H=32, T=8192)
+    assert lib.gdr_chunk_fwd_workspace(2, 32, 8192, 128, 128, 64, 0, 1, 2, 0) > gdr.NOALLOC_SCRATCH_BYTES
+    assert _call_noalloc(lib, **big) == -4
+    # the documented size of the array matches the binding's constant
+    text = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    m = re.search(r"#define GDR_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == gdr.NOALLOC_SCRATCH_BYTES
+
+
 def test_backward_flags_validated(lib):
     # pointers are never dereferenced: validation fails before any launch
     ptrs = [P(FAKE + (i << 30)) for i in range(19)]
