@@ -220,8 +220,8 @@ struct BwdSmem {
     static constexpr int oGam = oBeta + kC * 4; // fp32 [DK] gamma_C
     static constexpr int oGp = oGam + DK * 4;   // fp32 [8][DK] gate partial sums
     static constexpr int oDb = oGp + 8 * DK * 4;  // fp32 [64] dbeta
-    static constexpr int oDg = oDb + kC * 4;    // fp32 [DK] last-row term of dg
-    static constexpr int oSpf = oDg + DK * 4;   // fp32 [DK] 2^n, the state's scale
+    static constexpr int oDg = oDb + kC * 4;    // fp32 [4][DK] last-row term of dg, per wave
+    static constexpr int oSpf = oDg + 4 * DK * 4;  // fp32 [DK] 2^n, the state's scale
     static constexpr int bytes = oSpf + DK * 4;
     // final stage: Gamma fp32 [64][DK] over Q<-..K-> (free by then), dg fp32 [64][DK] over T
     static_assert(kC * DK * 4 <= 3 * QK, "Gamma fits over the operand arrays");
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             }
         }
         for (int i = tid; i < kC; i += kThreads) sDb[i] = 0.f;
-        for (int i = tid; i < DK; i += kThreads) sDg[i] = 0.f;
+        for (int i = tid; i < 4 * DK; i += kThreads) sDg[i] = 0.f;
     }
     lds_barrier();
 
@@ -637,7 +637,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             float x = gpart[e];
 #pragma unroll
             for (int off = DK / 8; off < 64; off <<= 1) x += __shfl_xor(x, off);
-            if (lane < DK / 8) atomicAdd(&sDg[8 * lane + e], x);
+            if (lane < DK / 8) sDg[wave * DK + 8 * lane + e] += x;  // this wave's slot
         }
     }
     lds_barrier();
@@ -691,16 +691,16 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
 
     // ---- stage 6: dK<-, dK->, dQ<- ------------------------------------------------------
     f32x4 gKl[NT], gKr[NT], gQl[NT];
-    // q, k of this lane's rows and columns for the chain rule at the end, loaded now so
-    // that they arrive during the products below
-    uint2 qw[NT], kw[NT];
+    // dg of this lane's row and columns: dQ<- Q<- + dK<- K<- - dK-> K->, each operand the
+    // bf16 value the products above used.  Every pair (r, c) of a Gram product then enters
+    // the row-r and row-c terms as the same product of the same rounded numbers, so the
+    // pairs inside a suffix cancel exactly in the suffix sums below, as they do in exact
+    // arithmetic (with the operands rebuilt from q, k and e^g, both copies differ by the
+    // bf16 rounding of the operands, and those residues swamp dlog alpha wherever the gate
+    // decays fast enough to make it small).
+    float dgl[NT][4];
     const bool ok_row = R0 + r16 < m;
     const size_t th_row = (size_t)(tok0 + (ok_row ? R0 + r16 : 0)) * H + h;
-#pragma unroll
-    for (int tn = 0; tn < NT; ++tn) {
-        qw[tn] = *(const uint2 *)(p.q + th_row * DK + 16 * tn + 4 * g4);
-        kw[tn] = *(const uint2 *)(p.k + th_row * DK + 16 * tn + 4 * g4);
-    }
     {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         const int row = R0 + r16;
@@ -717,17 +717,23 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             gQl[tn] = mma_tile<false, false, kC>(sdA, CS, sKr, KS, R0, 16 * tn, 0, kC, aQ[tn], lane);
             // last-row term: sum over rows of K-> dKg, per column
             const uint2 kr = *(const uint2 *)(sKr + row * KS + 16 * tn + 4 * g4);
-            dgp[tn][0] = bf16_lo(kr.x) * aKg[tn][0];
-            dgp[tn][1] = bf16_hi(kr.x) * aKg[tn][1];
-            dgp[tn][2] = bf16_lo(kr.y) * aKg[tn][2];
-            dgp[tn][3] = bf16_hi(kr.y) * aKg[tn][3];
+            const uint2 ql = *(const uint2 *)(sQl + row * KS + 16 * tn + 4 * g4);
+            const uint2 kl = *(const uint2 *)(sKl + row * KS + 16 * tn + 4 * g4);
+            const float vr[4] = {bf16_lo(kr.x), bf16_hi(kr.x), bf16_lo(kr.y), bf16_hi(kr.y)};
+            const float vq[4] = {bf16_lo(ql.x), bf16_hi(ql.x), bf16_lo(ql.y), bf16_hi(ql.y)};
+            const float vl[4] = {bf16_lo(kl.x), bf16_hi(kl.x), bf16_lo(kl.y), bf16_hi(kl.y)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dgp[tn][e] = vr[e] * aKg[tn][e];
+                dgl[tn][e] = gQl[tn][e] * vq[e] + gKl[tn][e] * vl[e] - gKr[tn][e] * vr[e];
+            }
         }
 #pragma unroll
         for (int tn = 0; tn < NT; ++tn)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float s = group_sum<16>(dgp[tn][e]);
-                if (r16 == 0) atomicAdd(&sDg[16 * tn + 4 * g4 + e], s);
+                if (r16 == 0) sDg[wave * DK + 16 * tn + 4 * g4 + e] += s;
             }
     }
     lds_barrier();  // the operand arrays are free: Gamma goes over them
@@ -747,19 +753,13 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
 #pragma unroll
         for (int tn = 0; tn < NT; ++tn) {
             const int col = 16 * tn + 4 * g4;
-            const uint32_t keep = ok ? 0xffffffffu : 0u;
-            const float qv[4] = {bf16_lo(qw[tn].x & keep), bf16_hi(qw[tn].x & keep),
-                                 bf16_lo(qw[tn].y & keep), bf16_hi(qw[tn].y & keep)};
-            const float kv[4] = {bf16_lo(kw[tn].x & keep), bf16_hi(kw[tn].x & keep),
-                                 bf16_lo(kw[tn].y & keep), bf16_hi(kw[tn].y & keep)};
-            float dq4[4], dk4[4], dl4[4];
+            float dq4[4], dk4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float gv = sGm[row * DK + col + e] * kLog2e;
                 const float G = exp2_fast(gv), iG = exp2_fast(-gv);
                 dq4[e] = gQl[tn][e] * G;
                 dk4[e] = gKl[tn][e] * G + gKr[tn][e] * iG;
-                dl4[e] = gQl[tn][e] * qv[e] * G + gKl[tn][e] * kv[e] * G - gKr[tn][e] * kv[e] * iG;
             }
             if (ok) {
                 uint2 o;
@@ -770,7 +770,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
                 o.y = pack_bf16x2(dk4[2], dk4[3]);
                 *(uint2 *)(p.dk + th * DK + col) = o;
             }
-            *(float4 *)(sDl + row * DK + col) = make_float4(dl4[0], dl4[1], dl4[2], dl4[3]);
+            *(float4 *)(sDl + row * DK + col) = make_float4(dgl[tn][0], dgl[tn][1], dgl[tn][2], dgl[tn][3]);
         }
         if (tid < kC && tid < m) p.dbeta[(size_t)(tok0 + tid) * H + h] = sDb[tid];
     }
@@ -794,7 +794,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         }
         lds_barrier();
         if (act) {
-            float4 acc = *(const float4 *)(sDg + col);  // the last-row term
+            float4 acc = *(const float4 *)(sDg + col);  // the last-row term, waves in order
+            for (int w = 1; w < 4; ++w) {
+                const float4 x = *(const float4 *)(sDg + w * DK + col);
+                acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+            }
             for (int p2 = part + 1; p2 < NP; ++p2) {
                 const float4 x = *(const float4 *)(sGp + p2 * DK + col);
                 acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
@@ -814,7 +818,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             float s = 0.f;
             for (int col = q; col < DK; col += 4) s += sDl[row * DK + col];
             if (row == kC - 1)
-                for (int col = q; col < DK; col += 4) s += sDg[col];
+                for (int col = q; col < DK; col += 4)
+                    s += ((sDg[col] + sDg[DK + col]) + sDg[2 * DK + col]) + sDg[3 * DK + col];
             s += dpp<kDppXor1>(s);
             s += dpp<kDppXor2>(s);
             if (q == 0) sGp[row] = s;
@@ -885,8 +890,8 @@ struct BwdDpSmem {
     static constexpr int oGam = oBeta + kC * 4;
     static constexpr int oGp = oGam + DK * 4;
     static constexpr int oDb = oGp + 8 * DK * 4;
-    static constexpr int oDg = oDb + kC * 4;
-    static constexpr int oSpf = oDg + DK * 4;
+    static constexpr int oDg = oDb + kC * 4;      // fp32 [4][DK] last-row term of dg, per wave
+    static constexpr int oSpf = oDg + 4 * DK * 4;
     static constexpr int bytes = oSpf + DK * 4;
     static_assert(kC * DK * 4 <= 2 * QK, "Gamma / dg fit over K->, A-> and over Q<-, B<-");
     static_assert(bytes <= 160 * 1024, "LDS");
@@ -1047,7 +1052,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
         for (int e = 0; e < CPT; ++e) sGam[c0 + e] = exp2_fast(g[7][e] * kLog2e);
     if (tid < kC) sBeta[tid] = tid < m ? p.beta[(size_t)(tok0 + tid) * H + h] : 0.f;
     for (int i = tid; i < kC; i += kThreads) sDb[i] = 0.f;
-    for (int i = tid; i < DK; i += kThreads) sDg[i] = 0.f;
+    for (int i = tid; i < 4 * DK; i += kThreads) sDg[i] = 0.f;
     for (int idx = tid; idx < kC * CS / 8; idx += kThreads) ((uint4 *)sE)[idx] = make_uint4(0u, 0u, 0u, 0u);
     lds_barrier();
 
@@ -1277,7 +1282,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
             float x = gpart[e];
 #pragma unroll
             for (int off = DK / 8; off < 64; off <<= 1) x += __shfl_xor(x, off);
-            if (lane < DK / 8) atomicAdd(&sDg[8 * lane + e], x);
+            if (lane < DK / 8) sDg[wave * DK + 8 * lane + e] += x;  // this wave's slot
         }
         dbp += __shfl_xor(dbp, 16);
         dbp += __shfl_xor(dbp, 32);
@@ -1351,16 +1356,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
     // ---- final products -------------------------------------------------------------------
     const bool ok_row = R0 + r16 < m;
     const size_t th_row = (size_t)(tok0 + (ok_row ? R0 + r16 : 0)) * H + h;
-    uint2 xq[NT], xk[NT], xa[NT], xb[NT];
-#pragma unroll
-    for (int tn = 0; tn < NT; ++tn) {
-        const size_t o = th_row * DK + 16 * tn + 4 * g4;
-        xq[tn] = *(const uint2 *)(p.q + o);
-        xk[tn] = *(const uint2 *)(p.k + o);
-        xa[tn] = *(const uint2 *)(p.a + o);
-        xb[tn] = *(const uint2 *)(p.b + o);
-    }
     f32x4 gQ[NT], gB[NT], gK[NT], gA[NT];
+    // dg of this lane's row and columns, dQ<- Q<- + dB<- B<- - dK-> K-> - dA-> A->, from
+    // the bf16 operands the products used, so that the pairs of every Gram product cancel
+    // exactly inside the suffix sums (as in the KDA kernel)
+    float dgl[NT][4];
     {
         const int row = R0 + r16;
         float dgp[NT][4];
@@ -1384,17 +1384,24 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
             // last-row term: sum over rows of K-> (V' dSg) + A-> (N dSg)
             const uint2 kr = *(const uint2 *)(sKr + row * KS + n0 + 4 * g4);
             const uint2 ar = *(const uint2 *)(sAr + row * KS + n0 + 4 * g4);
-            dgp[tn][0] = bf16_lo(kr.x) * aKs[tn][0] + bf16_lo(ar.x) * aAs[tn][0];
-            dgp[tn][1] = bf16_hi(kr.x) * aKs[tn][1] + bf16_hi(ar.x) * aAs[tn][1];
-            dgp[tn][2] = bf16_lo(kr.y) * aKs[tn][2] + bf16_lo(ar.y) * aAs[tn][2];
-            dgp[tn][3] = bf16_hi(kr.y) * aKs[tn][3] + bf16_hi(ar.y) * aAs[tn][3];
+            const uint2 ql = *(const uint2 *)(sQl + row * KS + n0 + 4 * g4);
+            const uint2 bl = *(const uint2 *)(sBl + row * KS + n0 + 4 * g4);
+            const float vk[4] = {bf16_lo(kr.x), bf16_hi(kr.x), bf16_lo(kr.y), bf16_hi(kr.y)};
+            const float va[4] = {bf16_lo(ar.x), bf16_hi(ar.x), bf16_lo(ar.y), bf16_hi(ar.y)};
+            const float vq[4] = {bf16_lo(ql.x), bf16_hi(ql.x), bf16_lo(ql.y), bf16_hi(ql.y)};
+            const float vb[4] = {bf16_lo(bl.x), bf16_hi(bl.x), bf16_lo(bl.y), bf16_hi(bl.y)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dgp[tn][e] = vk[e] * aKs[tn][e] + va[e] * aAs[tn][e];
+                dgl[tn][e] = gQ[tn][e] * vq[e] + gB[tn][e] * vb[e] - gK[tn][e] * vk[e] - gA[tn][e] * va[e];
+            }
         }
 #pragma unroll
         for (int tn = 0; tn < NT; ++tn)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float sgm = group_sum<16>(dgp[tn][e]);
-                if (r16 == 0) atomicAdd(&sDg[16 * tn + 4 * g4 + e], sgm);
+                if (r16 == 0) sDg[wave * DK + 16 * tn + 4 * g4 + e] += sgm;
             }
     }
     lds_barrier();  // the operand arrays are free: Gamma over K->, A->, dg over Q<-, B<-
@@ -1409,18 +1416,10 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
     lds_barrier();
     {
         const int row = R0 + r16;
-        const uint32_t keep = ok_row ? 0xffffffffu : 0u;
 #pragma unroll
         for (int tn = 0; tn < NT; ++tn) {
             const int col = 16 * tn + 4 * g4;
-            const uint2 w4[4] = {xq[tn], xk[tn], xa[tn], xb[tn]};
-            float iv[4][4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                iv[u][0] = bf16_lo(w4[u].x & keep); iv[u][1] = bf16_hi(w4[u].x & keep);
-                iv[u][2] = bf16_lo(w4[u].y & keep); iv[u][3] = bf16_hi(w4[u].y & keep);
-            }
-            float oq[4], ok4[4], oa[4], ob[4], dl[4];
+            float oq[4], ok4[4], oa[4], ob[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float gv = sGm[row * DK + col + e] * kLog2e;
@@ -1429,7 +1428,6 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
                 ob[e] = gB[tn][e] * G;
                 ok4[e] = gK[tn][e] * iG;
                 oa[e] = gA[tn][e] * iG;
-                dl[e] = oq[e] * iv[0][e] + ob[e] * iv[3][e] - ok4[e] * iv[1][e] - oa[e] * iv[2][e];
             }
             if (ok_row) {
                 const size_t o = th_row * DK + col;
@@ -1443,7 +1441,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
                 w.x = pack_bf16x2(ob[0], ob[1]); w.y = pack_bf16x2(ob[2], ob[3]);
                 *(uint2 *)(p.db + o) = w;
             }
-            *(float4 *)(sDl + row * DK + col) = make_float4(dl[0], dl[1], dl[2], dl[3]);
+            *(float4 *)(sDl + row * DK + col) = make_float4(dgl[tn][0], dgl[tn][1], dgl[tn][2], dgl[tn][3]);
         }
         if (tid < kC && tid < m) p.dbeta[(size_t)(tok0 + tid) * H + h] = sDb[tid];
     }
@@ -1466,7 +1464,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
         }
         lds_barrier();
         if (act) {
-            float4 acc = *(const float4 *)(sDg + col);  // the last-row term
+            float4 acc = *(const float4 *)(sDg + col);  // the last-row term, waves in order
+            for (int w = 1; w < 4; ++w) {
+                const float4 x = *(const float4 *)(sDg + w * DK + col);
+                acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+            }
             for (int p2 = part + 1; p2 < NP; ++p2) {
                 const float4 x = *(const float4 *)(sGp + p2 * DK + col);
                 acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
@@ -1484,7 +1486,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
             float sacc = 0.f;
             for (int col = q4; col < DK; col += 4) sacc += sDl[row * DK + col];
             if (row == kC - 1)
-                for (int col = q4; col < DK; col += 4) sacc += sDg[col];
+                for (int col = q4; col < DK; col += 4)
+                    sacc += ((sDg[col] + sDg[DK + col]) + sDg[2 * DK + col]) + sDg[3 * DK + col];
             sacc += dpp<kDppXor1>(sacc);
             sacc += dpp<kDppXor2>(sacc);
             if (q4 == 0) sGp[row] = sacc;
