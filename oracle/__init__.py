@@ -27,7 +27,9 @@ _LIB = None
 def _lib():
     global _LIB
     if _LIB is None:
-        path = os.path.join(_HERE, "libgdr_ref.so")
+        # GDR_ORACLE_LIB names another build of the same sources (the sanitizer build
+        # of the CPU test suite); by default the one oracle/build.py makes
+        path = os.environ.get("GDR_ORACLE_LIB") or os.path.join(_HERE, "libgdr_ref.so")
         if not os.path.exists(path):
             from . import build as _b
             _b.build()
