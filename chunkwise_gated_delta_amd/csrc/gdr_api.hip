@@ -56,7 +56,8 @@ int supported(int dtype, int dk, int dv, int C, bool has_ab) {
     if (dtype != GDR_F32 && dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
     if (dk != 64 && dk != 128) return GDR_ERR_UNSUPPORTED;
     if (dv % 32 != 0 || dv > 256) return GDR_ERR_UNSUPPORTED;
-    if (dtype == GDR_BF16 && !has_ab) return C == 64 ? GDR_OK : GDR_ERR_UNSUPPORTED;
+    if (dtype == GDR_BF16 && !has_ab)
+        return (C == 64 || (C == 128 && dk == 128)) ? GDR_OK : GDR_ERR_UNSUPPORTED;
     return (C == 16 || C == 32 || C == 64) ? GDR_OK : GDR_ERR_UNSUPPORTED;
 }
 

@@ -57,6 +57,7 @@ namespace gdr {
 namespace {
 
 constexpr int kC = 64;         // chunk size
+constexpr int kC2 = 128;       // chunk size of the 128-token path (two halves of kC)
 constexpr int kDVT = 32;       // dv columns per state workgroup
 constexpr int kThreads = 256;  // 4 waves, both kernels
 constexpr int kCS = kC + 8;    // bf16 row stride of [*][64] arrays
@@ -82,6 +83,22 @@ struct Blk {
     static constexpr int oKb = oG + 4 * DK;     // DP only: Diag(beta) K^ transposed, as oK
     static constexpr int bytes = oKb + (DP ? 128 * DK : 0);
     static_assert(bytes % 256 == 0, "block alignment");
+};
+
+// One (128-token chunk, head) block of the C = 128 path (KDA form, dk = 128), in the
+// same fragment order: 4 row tiles of W'' and Q~'', K^'' tiles of dk rows with K = 128
+// tokens, and the 10 lower 32x32 tiles of Ab'' and Ao'' (tile (rt, ct) at index
+// rt (rt + 1) / 2 + ct, K = 32 each).  Rows 0-63 are those of the first 64-token half;
+// the second half's rows are re-expressed against the state entering the whole chunk.
+template <int DK>
+struct Blk128 {
+    static constexpr int oW = 0;                 // W'': row tiles 0-3, K = DK
+    static constexpr int oQ = oW + 256 * DK;     // Q~'': same
+    static constexpr int oK = oQ + 256 * DK;     // K^'' transposed: DK/32 tiles, K = 128 tokens
+    static constexpr int oAb = oK + 256 * DK;    // Ab'': 10 tiles
+    static constexpr int oAo = oAb + 10 * 2048;  // Ao'': 10 tiles
+    static constexpr int oG = oAo + 10 * 2048;   // gamma of the whole chunk [DK] fp32
+    static constexpr int bytes = (oG + 4 * DK + 255) / 256 * 256;
 };
 
 struct SplitParams {
@@ -157,10 +174,15 @@ constexpr float kSubGateRange = 96.f;
 // MFMA with columns y_c 2^(g_s - g_c) (at most 2^64); a wider one is formed element-wise.
 constexpr float kSubTileRange = 64.f;
 
-template <int DK, int GATE, bool DP, bool CLIP, bool SUB = false>
+template <int DK, int GATE, bool DP, bool CLIP, bool SUB = false, bool PAIR = false>
 __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(SplitParams p) {
     using L = PrepSmem<DK, DP, SUB>;
     using Bk = Blk<DK, DP>;
+    // PAIR: chunks of 128 tokens.  Each job runs the 64-token code on the two halves in
+    // turn and merges them into one Blk128 block (see the end of the job loop).
+    using B2 = Blk128<DK>;
+    static_assert(!PAIR || (!DP && !SUB && DK == 128), "the 128-token path covers the KDA form at dk = 128");
+    constexpr int kBlkBytes = PAIR ? B2::bytes : Bk::bytes;
     constexpr int KS = L::KS;
     constexpr int CPT = DK / 32;  // gate stage: channels per thread
     constexpr int WPR = CPT / 2;  // 32-bit words of bf16 per row per thread
@@ -201,19 +223,29 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
         int g, m;
         long tok0;
         bool ok;
+        int half;  // PAIR: which 64-token half of the 128-token chunk g
     };
-    auto decode = [&](int g) {
+    auto decode = [&](int g, int half = 0) {
         Job J;
         J.g = g;
         J.tok0 = 0;
         J.m = 1;
+        J.half = half;
         int n = 0, c = 0;
         J.ok = g < njobs && chunk_of(p, g / H, n, c);
         if (J.ok) {
             long t0, t1;
             seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
-            J.tok0 = t0 + (long)c * kC;
-            J.m = (int)((t1 - J.tok0) < kC ? (t1 - J.tok0) : kC);  // >= 1
+            if constexpr (PAIR) {
+                const long base = t0 + (long)c * kC2;
+                const int m2 = (int)((t1 - base) < kC2 ? (t1 - base) : kC2);  // >= 1
+                J.m = half ? (m2 > kC ? m2 - kC : 0) : (m2 < kC ? m2 : kC);
+                // an empty second half reads (and zeroes) rows of the first
+                J.tok0 = half && J.m > 0 ? base + kC : base;
+            } else {
+                J.tok0 = t0 + (long)c * kC;
+                J.m = (int)((t1 - J.tok0) < kC ? (t1 - J.tok0) : kC);  // >= 1
+            }
         }
         return J;
     };
@@ -233,9 +265,10 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
         const float *lb = p.la + ((size_t)J.tok0 * H + h) * DK + c0;
         const bf16 *ab = DP ? p.a + ((size_t)J.tok0 * H + h) * DK + c0 : nullptr;
         const bf16 *bb = DP ? p.b + ((size_t)J.tok0 * H + h) * DK + c0 : nullptr;
+        const int last = J.m > 0 ? J.m - 1 : 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int r = 8 * rg + i, rr = r < J.m ? r : J.m - 1;
+            const int r = 8 * rg + i, rr = r < J.m ? r : last;
             if constexpr (WPR == 2) {
                 const uint2 xk = *(const uint2 *)(kb + rr * rs), xq = *(const uint2 *)(qb + rr * rs);
                 kw[i][0] = xk.x; kw[i][WPR - 1] = xk.y;
@@ -265,9 +298,9 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
                 lw[i][0] = p.la[(size_t)(J.tok0 + rr) * H + h];
             }
         }
-        const int rb0 = tid < kC ? (tid < J.m ? tid : J.m - 1) : 0;
+        const int rb0 = tid < kC ? (tid < J.m ? tid : last) : 0;
         beta_r = p.beta[(size_t)(J.tok0 + rb0) * H + h];
-        if (GATE == kGateHead && !CLIP) lah = p.la[(size_t)(J.tok0 + (lane < J.m ? lane : J.m - 1)) * H + h];
+        if (GATE == kGateHead && !CLIP) lah = p.la[(size_t)(J.tok0 + (lane < J.m ? lane : last)) * H + h];
     };
 
     // DPLR after the inverse (E in sX as bf16, unit diagonal, zero above it):
@@ -369,6 +402,9 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
 
     Job cur = decode(next_job(blockIdx.x));
     if (cur.ok) issue(cur);
+    // PAIR: the first half's K^ (before its scaling by the second half's gamma) and its
+    // gamma, carried to the merge; the second half's gamma
+    float kha[CPT][8], gama[CPT], gamb[CPT];
     while (cur.ok) {  // workgroup-uniform
         // Thread-index values are re-derived from an opaque copy each job: otherwise the
         // compiler hoists every per-lane LDS address of the body out of the loop and
@@ -381,7 +417,7 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
         const int l16 = lane & 15, lg = lane >> 4;
         const int rg = tid >> 5, cg = tid & 31, c0 = CPT * cg;
         const int m = cur.m;
-        char *bp = p.blk + (size_t)cur.g * Bk::bytes;
+        char *bp = p.blk + (size_t)cur.g * kBlkBytes;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             if (8 * rg + i >= m) {
@@ -521,7 +557,16 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
                 for (int i = 0; i < 8; ++i) g[i][e] = GATE == kGateHead ? sG[8 * rg + i] : 0.f;
             }
         }
-        if constexpr (!SUB) {
+        if constexpr (PAIR) {
+            // no log-domain variant on this path: a half whose gate falls beyond the
+            // scaled operands' range makes the call's result invalid (error bit 2)
+            if (wave == 0) {
+                bool wide = false;
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) wide = wide || !(gC[e] >= -kSubGateRange);
+                if (__builtin_amdgcn_ballot_w64(wide) != 0 && lane == 0) atomicOr(p.err, 2);
+            }
+        } else if constexpr (!SUB) {
             // wave 0 holds gamma_C of every channel: flag the chunk for the SUB variant
             if (p.sub && wave == 0) {
                 bool wide = false;
@@ -603,32 +648,50 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
                 }
             }
             // K^ transposed: channel cc is row cc%32 of fragment tile cc/32; this thread's
-            // 8 rows are one 16-byte piece (step rg/2, lane half rg%2).
+            // 8 rows are one 16-byte piece (step rg/2, lane half rg%2).  PAIR: the first
+            // half's waits in registers for the second half's gamma; the second half's
+            // takes steps 4-7 of the 8 the 128-token tiles have.
+            if (PAIR && cur.half == 0) {
 #pragma unroll
-            for (int e = 0; e < CPT; ++e) {
-                const int cc = c0 + e;
-                const int pc = (cc >> 5) * 4 * 64 + (rg >> 1) * 64 + (cc & 31) + 32 * (rg & 1);
-                uint4 w;
-                w.x = pack_bf16x2(kh[e][0], kh[e][1]);
-                w.y = pack_bf16x2(kh[e][2], kh[e][3]);
-                w.z = pack_bf16x2(kh[e][4], kh[e][5]);
-                w.w = pack_bf16x2(kh[e][6], kh[e][7]);
-                ((uint4 *)(bp + Bk::oK))[pc] = w;
-                if constexpr (DP) {
-                    w.x = pack_bf16x2(kb[e][0], kb[e][1]);
-                    w.y = pack_bf16x2(kb[e][2], kb[e][3]);
-                    w.z = pack_bf16x2(kb[e][4], kb[e][5]);
-                    w.w = pack_bf16x2(kb[e][6], kb[e][7]);
-                    ((uint4 *)(bp + Bk::oKb))[pc] = w;
+                for (int e = 0; e < CPT; ++e) {
+                    gama[e] = gam[e];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) kha[e][i] = kh[e][i];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) {
+                    const int cc = c0 + e;
+                    const int pc = PAIR ? (cc >> 5) * 8 * 64 + (4 + (rg >> 1)) * 64 + (cc & 31) + 32 * (rg & 1)
+                                        : (cc >> 5) * 4 * 64 + (rg >> 1) * 64 + (cc & 31) + 32 * (rg & 1);
+                    uint4 w;
+                    w.x = pack_bf16x2(kh[e][0], kh[e][1]);
+                    w.y = pack_bf16x2(kh[e][2], kh[e][3]);
+                    w.z = pack_bf16x2(kh[e][4], kh[e][5]);
+                    w.w = pack_bf16x2(kh[e][6], kh[e][7]);
+                    ((uint4 *)(bp + (PAIR ? B2::oK : Bk::oK)))[pc] = w;
+                    if constexpr (DP) {
+                        w.x = pack_bf16x2(kb[e][0], kb[e][1]);
+                        w.y = pack_bf16x2(kb[e][2], kb[e][3]);
+                        w.z = pack_bf16x2(kb[e][4], kb[e][5]);
+                        w.w = pack_bf16x2(kb[e][6], kb[e][7]);
+                        ((uint4 *)(bp + Bk::oKb))[pc] = w;
+                    }
                 }
             }
-            if (rg == 0) {
+            if (PAIR && cur.half == 1) {
 #pragma unroll
-                for (int e = 0; e < CPT; ++e) ((float *)(bp + Bk::oG))[c0 + e] = gam[e];
+                for (int e = 0; e < CPT; ++e) gamb[e] = gam[e];
+            }
+            if (rg == 0 && !(PAIR && cur.half == 0)) {
+#pragma unroll
+                for (int e = 0; e < CPT; ++e)
+                    ((float *)(bp + (PAIR ? B2::oG : Bk::oG)))[c0 + e] = PAIR ? gama[e] * gam[e] : gam[e];
             }
         }
-        // this job's raw inputs are consumed: the next job's start loading
-        const Job nxt = decode(next_job(cur.g + gridDim.x));
+        // this job's raw inputs are consumed: the next job's start loading (PAIR: the
+        // second half of this chunk, then the next chunk)
+        const Job nxt = PAIR && cur.half == 0 ? decode(cur.g, 1) : decode(next_job(cur.g + gridDim.x));
         if (nxt.ok) issue(nxt);
         lds_barrier();
 
@@ -1101,18 +1164,167 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
         }
 
         // ---- fragment tiles out: W', Q~ (2 row tiles x DK/16 steps), Ab, Ao (3 tiles) ---
+        // (PAIR, first half: the same tiles are rows 0-63 of the 128-token block)
         constexpr int NPW = 2 * (DK / 16) * 64;
-        for (int pc = tid; pc < NPW; pc += kThreads) {
-            const int t = pc / ((DK / 16) * 64), s = (pc >> 6) % (DK / 16), ln = pc & 63;
-            const int r = 32 * t + (ln & 31), cc = 16 * s + 8 * (ln >> 5);
-            ((uint4 *)(bp + Bk::oW))[pc] = *(const uint4 *)(sKr + r * KS + cc);
-            ((uint4 *)(bp + Bk::oQ))[pc] = *(const uint4 *)(sQl + r * KS + cc);
-        }
-        for (int pc = tid; pc < 3 * 128; pc += kThreads) {
-            const int tau = pc >> 7, s = (pc >> 6) & 1, ln = pc & 63;
-            const int r = (tau ? 32 : 0) + (ln & 31), cc = (tau == 2 ? 32 : 0) + 16 * s + 8 * (ln >> 5);
-            ((uint4 *)(bp + Bk::oAb))[pc] = *(const uint4 *)((DP ? sEc : sX) + r * kCS + cc);
-            ((uint4 *)(bp + Bk::oAo))[pc] = *(const uint4 *)(sAqk + r * kCS + cc);
+        if (!PAIR || cur.half == 0) {
+            for (int pc = tid; pc < NPW; pc += kThreads) {
+                const int t = pc / ((DK / 16) * 64), s = (pc >> 6) % (DK / 16), ln = pc & 63;
+                const int r = 32 * t + (ln & 31), cc = 16 * s + 8 * (ln >> 5);
+                ((uint4 *)(bp + (PAIR ? B2::oW : Bk::oW)))[pc] = *(const uint4 *)(sKr + r * KS + cc);
+                ((uint4 *)(bp + (PAIR ? B2::oQ : Bk::oQ)))[pc] = *(const uint4 *)(sQl + r * KS + cc);
+            }
+            for (int pc = tid; pc < 3 * 128; pc += kThreads) {
+                const int tau = pc >> 7, s = (pc >> 6) & 1, ln = pc & 63;
+                const int r = (tau ? 32 : 0) + (ln & 31), cc = (tau == 2 ? 32 : 0) + 16 * s + 8 * (ln >> 5);
+                ((uint4 *)(bp + (PAIR ? B2::oAb : Bk::oAb)))[pc] = *(const uint4 *)((DP ? sEc : sX) + r * kCS + cc);
+                ((uint4 *)(bp + (PAIR ? B2::oAo : Bk::oAo)))[pc] = *(const uint4 *)(sAqk + r * kCS + cc);
+            }
+        } else if constexpr (PAIR) {
+            // ---- merge of the two halves into one 128-token chunk --------------------------
+            // With a, b the halves, the state entering b is S_a = S Diag(gamma_a) + V_a^T K^_a
+            // (V_a = Ab_a V + W'_a S^T), so b's rows against the state entering the chunk are
+            //   V_b = [M Ab_a, Ab_b] V + (W'_b Diag(gamma_a) + M W'_a) S^T,     M = W'_b K^_a^T
+            //   O_b = [N Ab_a, Ao_b] V + (Q~_b Diag(gamma_a) + N W'_a) S^T,     N = Q~_b K^_a^T
+            // and the chunk's state update is S Diag(gamma_a gamma_b) + V_a^T (K^_a Diag(gamma_b))
+            // + V_b^T K^_b: the WY factors of the 128-token chunk, built from those of its
+            // 64-token sub-chunks (secondary chunking, "Gated Linear Attention" notes,
+            // section 5.3).  W'_b, Q~_b, Ab_b, Ao_b are in LDS; W'_a and Ab_a are read back
+            // from the first half's tiles of this block; K^_a is in registers.
+            //
+            // (1) Ab_b, Ao_b -> tiles (2,2), (3,2), (3,3) of Ab'', Ao''
+            for (int pc = tid; pc < 3 * 128; pc += kThreads) {
+                const int tau = pc >> 7, s = (pc >> 6) & 1, ln = pc & 63;
+                const int r = (tau ? 32 : 0) + (ln & 31), cc = (tau == 2 ? 32 : 0) + 16 * s + 8 * (ln >> 5);
+                const int dt = tau == 0 ? 5 : (tau == 1 ? 8 : 9);
+                ((uint4 *)(bp + B2::oAb))[dt * 128 + (pc & 127)] = *(const uint4 *)(sX + r * kCS + cc);
+                ((uint4 *)(bp + B2::oAo))[dt * 128 + (pc & 127)] = *(const uint4 *)(sAqk + r * kCS + cc);
+            }
+            // (2) K^_a as rows [64 tokens][KS] over K<- (free since W'_b, Q~_b were formed);
+            //     gamma_a over the gate scratch
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * rg + i;
+                uint32_t wk[WPR];
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) wk[w] = pack_bf16x2(kha[2 * w][i], kha[2 * w + 1][i]);
+                if constexpr (WPR == 2) *(uint2 *)(sKl + r * KS + c0) = make_uint2(wk[0], wk[WPR - 1]);
+                else *(uint32_t *)(sKl + r * KS + c0) = wk[0];
+            }
+            if (rg == 0) {
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) sTot[c0 + e] = gama[e];
+            }
+            __syncthreads();  // also completes the first half's stores, which are read back below
+            // (3) M -> X array, N -> A_qk array (64 x 64 each; transposed products as for the
+            //     Gram, so that each lane holds four consecutive columns of one row)
+            for (int jb = wave; jb < 32; jb += 4) {
+                const int pr = jb >> 4, t = jb & 15, ti = t >> 2, tj = t & 3;
+                const uint16_t *src = pr ? sQl : sKr;
+                f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < DK / 32; ++s)
+                    d = mfma(frag(sKl, 16 * tj + l16, KS, 32 * s + 8 * lg), frag(src, 16 * ti + l16, KS, 32 * s + 8 * lg), d);
+                store4((pr ? sAqk : sX) + (16 * ti + l16) * kCS + 16 * tj + 4 * lg, d[0], d[1], d[2], d[3]);
+            }
+            lds_barrier();
+            // (4) W'_a, row-major over K<- (from the first half's fragment tiles)
+            for (int pc = tid; pc < NPW; pc += kThreads) {
+                const int t = pc / ((DK / 16) * 64), s = (pc >> 6) % (DK / 16), ln = pc & 63;
+                const int r = 32 * t + (ln & 31), cc = 16 * s + 8 * (ln >> 5);
+                *(uint4 *)(sKl + r * KS + cc) = ((const uint4 *)(bp + B2::oW))[pc];
+            }
+            lds_barrier();
+            //     W''_b = W'_b Diag(gamma_a) + M W'_a, Q~''_b = Q~_b Diag(gamma_a) + N W'_a, in place
+            {
+                bf16x8 fm[4][2], fn[4][2];
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        fm[ti][s] = frag(sX, 16 * ti + l16, kCS, 32 * s + 8 * lg);
+                        fn[ti][s] = frag(sAqk, 16 * ti + l16, kCS, 32 * s + 8 * lg);
+                    }
+#pragma unroll
+                for (int tt = 0; tt < DK / 64; ++tt) {
+                    const int tn = wave * (DK / 64) + tt;
+                    const bf16x8 w0 = frag_tr(sKl, 0, KS, 16 * tn, lane);
+                    const bf16x8 w1 = frag_tr(sKl, 32, KS, 16 * tn, lane);
+                    const float4 ga = *(const float4 *)(sTot + 16 * tn + 4 * lg);
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) {
+                        const int r = 16 * ti + l16, cc = 16 * tn + 4 * lg;
+                        const uint2 wv = *(const uint2 *)(sKr + r * KS + cc);
+                        const uint2 qv = *(const uint2 *)(sQl + r * KS + cc);
+                        f32x4 w = {bf16_lo(wv.x) * ga.x, bf16_hi(wv.x) * ga.y, bf16_lo(wv.y) * ga.z, bf16_hi(wv.y) * ga.w};
+                        f32x4 o = {bf16_lo(qv.x) * ga.x, bf16_hi(qv.x) * ga.y, bf16_lo(qv.y) * ga.z, bf16_hi(qv.y) * ga.w};
+                        w = mfma(w0, fm[ti][0], w);
+                        w = mfma(w1, fm[ti][1], w);
+                        o = mfma(w0, fn[ti][0], o);
+                        o = mfma(w1, fn[ti][1], o);
+                        store4(sKr + r * KS + cc, w[0], w[1], w[2], w[3]);
+                        store4(sQl + r * KS + cc, o[0], o[1], o[2], o[3]);
+                    }
+                }
+            }
+            lds_barrier();
+            // (5) W''_b, Q~''_b -> row tiles 2, 3; Ab_a, row-major over K<- (zero where the
+            //     tiles are: rows 0-31, columns 32-63)
+            for (int pc = tid; pc < NPW; pc += kThreads) {
+                const int t = pc / ((DK / 16) * 64), s = (pc >> 6) % (DK / 16), ln = pc & 63;
+                const int r = 32 * t + (ln & 31), cc = 16 * s + 8 * (ln >> 5);
+                ((uint4 *)(bp + B2::oW))[NPW + pc] = *(const uint4 *)(sKr + r * KS + cc);
+                ((uint4 *)(bp + B2::oQ))[NPW + pc] = *(const uint4 *)(sQl + r * KS + cc);
+            }
+            for (int pc = tid; pc < 3 * 128; pc += kThreads) {
+                const int tau = pc >> 7, s = (pc >> 6) & 1, ln = pc & 63;
+                const int r = (tau ? 32 : 0) + (ln & 31), cc = (tau == 2 ? 32 : 0) + 16 * s + 8 * (ln >> 5);
+                *(uint4 *)(sKl + r * kCS + cc) = ((const uint4 *)(bp + B2::oAb))[pc];
+            }
+            for (int i = tid; i < 128; i += kThreads)
+                *(uint4 *)(sKl + (i >> 2) * kCS + 32 + 8 * (i & 3)) = make_uint4(0u, 0u, 0u, 0u);
+            lds_barrier();
+            //     M Ab_a, N Ab_a: wave w owns rows 16w..16w+15, four 16-column tiles
+            f32x4 vm[4], vn[4];
+            {
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                const bf16x8 m0 = frag(sX, 16 * wave + l16, kCS, 8 * lg), m1 = frag(sX, 16 * wave + l16, kCS, 32 + 8 * lg);
+                const bf16x8 n0 = frag(sAqk, 16 * wave + l16, kCS, 8 * lg), n1 = frag(sAqk, 16 * wave + l16, kCS, 32 + 8 * lg);
+#pragma unroll
+                for (int tn = 0; tn < 4; ++tn) {
+                    const bf16x8 a0 = frag_tr(sKl, 0, kCS, 16 * tn, lane), a1 = frag_tr(sKl, 32, kCS, 16 * tn, lane);
+                    vm[tn] = mfma(a1, m1, mfma(a0, m0, zero));
+                    vn[tn] = mfma(a1, n1, mfma(a0, n0, zero));
+                }
+            }
+            lds_barrier();  // M, N are read
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn) {
+                const int o = (16 * wave + l16) * kCS + 16 * tn + 4 * lg;
+                store4(sX + o, vm[tn][0], vm[tn][1], vm[tn][2], vm[tn][3]);
+                store4(sAqk + o, vn[tn][0], vn[tn][1], vn[tn][2], vn[tn][3]);
+            }
+            lds_barrier();
+            // (6) M Ab_a, N Ab_a -> tiles (2,0), (2,1), (3,0), (3,1) of Ab'', Ao'';
+            //     K^_a Diag(gamma_b) -> steps 0-3 of the K^'' tiles
+            for (int pc = tid; pc < 4 * 128; pc += kThreads) {
+                const int tq = pc >> 7, s = (pc >> 6) & 1, ln = pc & 63;
+                const int r = 32 * (tq >> 1) + (ln & 31), cc = 32 * (tq & 1) + 16 * s + 8 * (ln >> 5);
+                const int dt = (tq >> 1) ? 6 + (tq & 1) : 3 + (tq & 1);
+                ((uint4 *)(bp + B2::oAb))[dt * 128 + (pc & 127)] = *(const uint4 *)(sX + r * kCS + cc);
+                ((uint4 *)(bp + B2::oAo))[dt * 128 + (pc & 127)] = *(const uint4 *)(sAqk + r * kCS + cc);
+            }
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) {
+                const int cc = c0 + e;
+                const int pc = (cc >> 5) * 8 * 64 + (rg >> 1) * 64 + (cc & 31) + 32 * (rg & 1);
+                const float gb = gamb[e];
+                uint4 w;
+                w.x = pack_bf16x2(kha[e][0] * gb, kha[e][1] * gb);
+                w.y = pack_bf16x2(kha[e][2] * gb, kha[e][3] * gb);
+                w.z = pack_bf16x2(kha[e][4] * gb, kha[e][5] * gb);
+                w.w = pack_bf16x2(kha[e][6] * gb, kha[e][7] * gb);
+                ((uint4 *)(bp + B2::oK))[pc] = w;
+            }
         }
         lds_barrier();  // every LDS array is free for the next job
         cur = nxt;
@@ -1458,6 +1670,219 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------------
+// State kernel for chunks of 128 tokens (KDA form, dk = 128, forward pass): one
+// workgroup of 8 waves per (sequence, head, 32-wide dv tile), serial over the chunks.
+//   waves 0-3 (w)      V_new rows 32w..+31 = Ab'' V + W'' S^T, then the S^T rows 32w..+31
+//                      of dk: S <- S Diag(gamma) + V_new^T K^''
+//   waves 4-7 (w - 4)  O rows 32(w-4)..+31 = Ao'' V + Q~'' S^T
+// A chunk's rows, row tiles, value tile and gamma are loaded one chunk ahead (a step is
+// twice as long as at C = 64); the K^'' tile, read only after the V_new products, is
+// loaded at the start of its own step.
+// ---------------------------------------------------------------------------------
+constexpr int kThreads2 = 512;          // 8 waves
+constexpr int kC2S = kC2 + 8;           // bf16 row stride of [*][128] arrays
+struct State128Smem {
+    static constexpr int KS = 128 + 8;
+    static constexpr int oS = 0;                       // S bf16 [32 dv][KS]
+    static constexpr int oV = oS + kDVT * KS * 2;      // V bf16 [128][kVS]
+    static constexpr int oVn = oV + kC2 * kVS * 2;     // V_new^T bf16 [32 dv][kC2S]
+    static constexpr int oO = oVn + kDVT * kC2S * 2;   // output staging, 4 x bf16 [32][kVS]
+    static constexpr int oG = oO + 4 * 32 * kVS * 2;   // gamma, 2 x fp32 [128] (chunk parity)
+    static constexpr int bytes = oG + 2 * 128 * 4;
+};
+
+struct Pre128 {
+    uint4 P[8];  // W'' (waves 0-3) or Q~'' (waves 4-7): this wave's 32 rows, K = 128
+    uint4 A[8];  // Ab'' or Ao'' tiles (r, 0..r) of row tile r: 2 (r + 1) steps
+    uint4 V;     // one 16-byte piece of the value tile
+    float4 G;    // wave 0, lanes 0..31: gamma[4 lane..+3]
+};
+
+// vmcnt(N) with N chosen at run time among the counts a row tile can leave in flight.
+__device__ __forceinline__ void wait_vmcnt_rows(int rt) {
+    switch (rt) {  // wave-uniform
+        case 0: wait_vmcnt<8 + 2 + 1>(); break;
+        case 1: wait_vmcnt<8 + 4 + 1>(); break;
+        case 2: wait_vmcnt<8 + 6 + 1>(); break;
+        default: wait_vmcnt<8 + 8 + 1>(); break;
+    }
+}
+
+__global__ __launch_bounds__(kThreads2) void kda_state128_kernel(SplitParams p) {
+    constexpr int DK = 128;
+    using L = State128Smem;
+    using Bk = Blk128<DK>;
+    constexpr int KS = L::KS;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+    uint16_t *sS = (uint16_t *)(smem + L::oS);
+    uint16_t *sV = (uint16_t *)(smem + L::oV);
+    uint16_t *sVn = (uint16_t *)(smem + L::oVn);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int H = p.H, DV = p.dv;
+    // XCD-aware placement as in kda_state_kernel: the dv tiles of a chain on one XCD,
+    // chains (longest packed sequence first) dealt to the XCDs in turn.
+    const int tpg = p.n_tiles;
+    const int pos = blockIdx.x >> 3;
+    const int chain = (pos / tpg) * 8 + (blockIdx.x & 7);
+    if (chain >= p.n_seq * H) return;
+    const int j0 = (pos % tpg) * kDVT;
+    const int h = chain % H;
+    const int rank = chain / H;
+    const int n = p.order ? p.order[rank] : rank;
+    long t0, t1;
+    seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
+    int nck = (int)((t1 - t0 + kC2 - 1) / kC2);
+    long cbase;
+    if (p.coff) {
+        cbase = p.coff[n];
+        const long room = p.max_chunks - cbase;  // only short of nck for malformed offsets
+        nck = (int)(room < 0 ? 0 : (room < nck ? room : nck));
+    } else {
+        cbase = (long)n * p.nc;
+    }
+    const float *s_in = p.S0 ? p.S0 + ((size_t)n * H + h) * DV * DK : nullptr;
+    float *s_out = p.Sf ? p.Sf + ((size_t)n * H + h) * DV * DK : nullptr;
+
+    const bool vw = wave < 4;  // V_new and state waves; waves 4-7: output
+    const int rt = wave & 3;   // 32-row tile of the chunk
+    uint16_t *sO = (uint16_t *)(smem + L::oO) + rt * 32 * kVS;
+
+    // state (waves 0-3): wave w holds S^T[dk 32w..+31][dv 0..31]; register 4q+e is
+    // S[dv l32][dk 32w + 8q + 4lh + e]
+    f32x16 ST = {};
+    if (vw) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int dk = 32 * rt + 8 * q + 4 * lh;
+            float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (s_in) s4 = *(const float4 *)(s_in + (size_t)(j0 + l32) * DK + dk);
+            ST[4 * q + 0] = s4.x; ST[4 * q + 1] = s4.y; ST[4 * q + 2] = s4.z; ST[4 * q + 3] = s4.w;
+            store4(sS + l32 * KS + dk, s4.x, s4.y, s4.z, s4.w);
+        }
+    }
+
+    const int vr = tid >> 2, vc = 8 * (tid & 3);  // value tile: token vr, columns vc..vc+7
+    const int na = 2 * (rt + 1);                  // A steps of this row tile
+    auto load = [&](Pre128 &x, int c) {
+        const char *bp = p.blk + ((size_t)(cbase + c) * H + h) * Bk::bytes;
+        const uint4 *pw = (const uint4 *)(bp + (vw ? Bk::oW : Bk::oQ)) + rt * (DK / 16) * 64 + lane;
+#pragma unroll
+        for (int s = 0; s < DK / 16; ++s) x.P[s] = pw[s * 64];
+        // tiles (rt, 0..rt) are consecutive: index rt (rt + 1) / 2 + ct, two steps each
+        const uint4 *pa = (const uint4 *)(bp + (vw ? Bk::oAb : Bk::oAo)) + (rt * (rt + 1) / 2) * 128 + lane;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < na) x.A[i] = pa[i * 64];
+        const long tok = t0 + (long)c * kC2 + vr;
+        x.V = *(const uint4 *)(p.v + ((size_t)(tok < t1 ? tok : t1 - 1) * H + h) * DV + j0 + vc);
+        if (wave == 0 && lane < DK / 4) x.G = ((const float4 *)(bp + Bk::oG))[lane];
+    };
+    uint4 K[8];  // K^'' tile of dk rows 32w.. (waves 0-3), chunk of the current step
+    auto load_k = [&](int c) {
+        const char *bp = p.blk + ((size_t)(cbase + c) * H + h) * Bk::bytes;
+        const uint4 *pk = (const uint4 *)(bp + Bk::oK) + rt * 512 + lane;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) K[s] = pk[s * 64];
+    };
+
+    auto store_out = [&](int c) {  // output rows of chunk c, staged by this O wave
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = 16 * i + (lane >> 2), q4 = lane & 3;
+            const long tok = t0 + (long)c * kC2 + 32 * rt + r;
+            const uint4 o = *(const uint4 *)(sO + r * kVS + 8 * q4);
+            if (tok < t1) *(uint4 *)(p.O + ((size_t)tok * H + h) * DV + j0 + 8 * q4) = o;
+        }
+    };
+
+    auto step = [&](int c, Pre128 &x, Pre128 &nx) {
+        wait_vmcnt<0>();  // chunk c's operands have arrived (issued one step ago)
+        if (vw) load_k(c);
+        float *sG = (float *)(smem + L::oG) + (c & 1) * 128;
+        if (wave == 0 && lane < DK / 4) ((float4 *)sG)[lane] = x.G;
+        {
+            const uint32_t keep = 0u - (uint32_t)(t0 + (long)c * kC2 + vr < t1);
+            *(uint4 *)(sV + vr * kVS + vc) = make_uint4(x.V.x & keep, x.V.y & keep, x.V.z & keep, x.V.w & keep);
+        }
+        if (!vw && c > 0) store_out(c - 1);
+        load(nx, c + 1 < nck ? c + 1 : nck - 1);
+        lds_barrier();  // value tile, gamma and S of chunk c visible
+
+        f32x16 acc = {};
+        if (vw) {
+            // V_new rows 32rt.. = Ab'' V + W'' S^T; register 4q+e is V_new[32rt + 8q + 4lh + e][dv l32]
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (i < na) acc = mfma32x32(as_bf16x8(x.A[i]), frag_tr32(sV, 16 * i, kVS, 0, lane), acc);
+#pragma unroll
+            for (int s = 0; s < DK / 16; ++s)
+                acc = mfma32x32(as_bf16x8(x.P[s]), frag(sS, l32, KS, 16 * s + 8 * lh), acc);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                store4(sVn + l32 * kC2S + 32 * rt + 8 * q + 4 * lh, acc[4 * q + 0], acc[4 * q + 1],
+                       acc[4 * q + 2], acc[4 * q + 3]);
+        } else {
+            // O^T = V^T Ao''^T + S Q~''^T; register 4q+e is O[row 32rt + l32][dv 8q + 4lh + e]
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (i < na) acc = mfma32x32(frag_tr32(sV, 16 * i, kVS, 0, lane), as_bf16x8(x.A[i]), acc);
+#pragma unroll
+            for (int s = 0; s < DK / 16; ++s)
+                acc = mfma32x32(frag(sS, l32, KS, 16 * s + 8 * lh), as_bf16x8(x.P[s]), acc);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                store4(sO + l32 * kVS + 8 * q + 4 * lh, acc[4 * q + 0], acc[4 * q + 1], acc[4 * q + 2],
+                       acc[4 * q + 3]);
+        }
+        lds_barrier();  // V_new^T visible; every read of S is done
+
+        if (vw) {
+            // S <- S Diag(gamma) + V_new^T K^'' (transposed: S^T tile = K^''^T-tile V_new)
+            wait_vmcnt_rows(rt);  // this step's K^'' tile has arrived (the next chunk's loads may not)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 g = *(const float4 *)(sG + 32 * rt + 8 * q + 4 * lh);
+                ST[4 * q + 0] *= g.x; ST[4 * q + 1] *= g.y;
+                ST[4 * q + 2] *= g.z; ST[4 * q + 3] *= g.w;
+            }
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                ST = mfma32x32(as_bf16x8(K[s]), frag(sVn, l32, kC2S, 16 * s + 8 * lh), ST);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                store4(sS + l32 * KS + 32 * rt + 8 * q + 4 * lh, ST[4 * q + 0], ST[4 * q + 1],
+                       ST[4 * q + 2], ST[4 * q + 3]);
+        }
+    };
+
+    if (nck > 0) {
+        Pre128 buf[2];
+        load(buf[0], 0);
+        int c = 0;
+        for (; c + 2 <= nck; c += 2) {
+            step(c, buf[0], buf[1]);
+            step(c + 1, buf[1], buf[0]);
+        }
+        if (c < nck) step(c, buf[0], buf[1]);
+        if (!vw) store_out(nck - 1);
+    }
+
+    if (s_out && vw) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int dk = 32 * rt + 8 * q + 4 * lh;
+            *(float4 *)(s_out + (size_t)(j0 + l32) * DK + dk) =
+                make_float4(ST[4 * q + 0], ST[4 * q + 1], ST[4 * q + 2], ST[4 * q + 3]);
+        }
+    }
+}
+
 // Start state of run g + 1 of a segmented state pass: S_start(g+1) = S_start(g) P_g + R_g
 // (fp32), one workgroup per (chain, 32 rows of dv, 32 columns of dk); launched for
 // g = 1 .. seg_n-2 in turn.
@@ -1618,8 +2043,10 @@ BwdLayout bwd_layout(const BwdArgs &b, int N) {
 }  // namespace
 
 bool kda_split_supported(const FwdArgs &a) {
-    return a.dtype == 1 && (a.a == nullptr) == (a.b == nullptr) && a.C == kC &&
-           (a.dk == 64 || a.dk == 128) && a.dv % kDVT == 0;
+    if (a.dtype != 1 || (a.a == nullptr) != (a.b == nullptr) || a.dv % kDVT != 0) return false;
+    if (a.C == kC2)  // 128-token chunks: the KDA form at dk = 128, forward only
+        return a.a == nullptr && a.dk == 128 && !a.keep_states;
+    return a.C == kC && (a.dk == 64 || a.dk == 128);
 }
 
 // Forward workspace: the split layout, then the per-job flags of the log-domain prep
@@ -1632,6 +2059,13 @@ struct KdaWs {
 };
 KdaWs kda_ws(const FwdArgs &a, int n_seq_eff) {
     KdaWs w;
+    if (a.C == kC2) {  // blocks of 128-token chunks; no log-domain flags, plain state pass
+        w.lay = split_layout(a, n_seq_eff, Blk128<128>::bytes);
+        w.sub = false;
+        w.sub_off = w.seg_off = w.total = seg_offset(w.lay.total);
+        w.runs = 0;
+        return w;
+    }
     w.lay = split_layout(a, n_seq_eff, blk_bytes(a.dk, a.a != nullptr));
     w.sub = a.gate != kGateNone || a.clip;
     w.sub_off = seg_offset(w.lay.total);
@@ -1674,7 +2108,7 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     sp.blk = ws + lay.blk_off;
     sp.total = (long)a.B * a.T;
     sp.H = a.H; sp.T = a.T; sp.dv = a.dv; sp.n_seq = n_seq_eff; sp.n_tiles = a.dv / kDVT;
-    sp.nc = lay.nc; sp.max_chunks = max_chunks; sp.C = kC;
+    sp.nc = lay.nc; sp.max_chunks = max_chunks; sp.C = a.C;
     sp.seg_ws = (float *)(ws + kw.seg_off);
     sp.sub = kw.sub ? (int *)(ws + kw.sub_off) : nullptr;
     int runs = kw.runs ? seg_runs(n_seq_eff * a.H, a.dk, a.dv, chunks_per_chain(a), true) : 0;
@@ -1690,6 +2124,25 @@ int launch_kda_split(const FwdArgs &a, int n_seq_eff, hipStream_t s) {
     if (varlen) hipLaunchKernelGGL((chunk_plan_kernel<SplitParams>), dim3(1), dim3(kPlanThreads), 0, s, sp);
     // persistent prep workgroups: two per CU (one with a, b: their LDS allows no more)
     const long njobs = (long)a.H * max_chunks;
+    if (a.C == kC2) {
+        // 128-token chunks: the prep merges each chunk's two halves, then the 128-row pass
+        const dim3 grid((unsigned)(njobs < 2L * compute_units() ? njobs : 2L * compute_units()));
+#define GDR_PREP2(G, CL) hipLaunchKernelGGL((kda_prep_kernel<128, G, false, CL, false, true>), grid, dim3(kThreads), 0, s, sp)
+        if (a.clip) {
+            if (a.gate == kGateChannel) GDR_PREP2(kGateChannel, true);
+            else if (a.gate == kGateHead) GDR_PREP2(kGateHead, true);
+            else GDR_PREP2(kGateNone, true);
+        } else {
+            if (a.gate == kGateChannel) GDR_PREP2(kGateChannel, false);
+            else if (a.gate == kGateHead) GDR_PREP2(kGateHead, false);
+            else GDR_PREP2(kGateNone, false);
+        }
+#undef GDR_PREP2
+        const long chains = (long)n_seq_eff * a.H;
+        hipLaunchKernelGGL(kda_state128_kernel, dim3((unsigned)(((chains + 7) / 8) * 8 * sp.n_tiles)),
+                           dim3(kThreads2), 0, s, sp);
+        return (int)hipGetLastError();
+    }
     const long slots = (dp ? 1L : 2L) * compute_units();
     const dim3 grid_prep((unsigned)(njobs < slots ? njobs : slots));
     const long cus = compute_units();

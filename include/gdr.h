@@ -109,7 +109,11 @@ size_t gdr_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int C, int n
  *               n_seq is ignored when cu_seqlens is NULL.
  *   C           chunk size (tokens per chunk).  The result does not depend on it
  *               beyond rounding.  Supported: 64 for bf16 without a, b; 16, 32 or
- *               64 for fp32 inputs and for bf16 with a, b (DPLR).
+ *               64 for fp32 inputs and for bf16 with a, b (DPLR); and 128 for bf16
+ *               without a, b at dk = 128 (each 128-token chunk's factors built from
+ *               those of its two 64-token halves, "Gated Linear Attention" notes,
+ *               section 5.3, secondary chunking; no log-domain rescue: a half whose
+ *               gate falls by more than 2^96 in a channel raises error bit 2).
  *   dk, dv      head sizes; dk in {64, 128}; dv a multiple of 32 up to 256.
  *
  * S_final may equal S0 (in-place state update).  O must not overlap any input.
@@ -222,9 +226,10 @@ int gdr_chunk_bwd(const void *q, const void *k, const void *v, const void *a, co
  * (0: none; bit 1: malformed cu_seqlens were clamped; bit 2: a chunk's gate falls
  * further than the kernels that ran can represent, so that call's results are
  * not valid -- gdr_chunk_bwd when a channel falls by more than 2^192 (e^133)
- * within a chunk, and the fp32 kernels (fp32 inputs, or C < 64) by more than e^80; the
- * bf16 forward with C = 64 handles such chunks in the log domain and never sets
- * it) and clears them.  Returns GDR_ERR_NULL or GDR_ERR_HIP on failure. */
+ * within a chunk, the fp32 kernels (fp32 inputs, or C < 64) by more than e^80, and the
+ * bf16 forward with C = 128 when a 64-token half falls by more than 2^96; the bf16
+ * forward with C = 64 handles such chunks in the log domain and never sets it) and
+ * clears them.  Returns GDR_ERR_NULL or GDR_ERR_HIP on failure. */
 int gdr_workspace_error(void *workspace, void *stream);
 
 /* Human-readable text for a gdr_status value (static storage). */

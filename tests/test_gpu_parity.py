@@ -439,3 +439,82 @@ def test_total_forgetting_gate(kind):
     O, Sf = gpu_run(P)
     assert np.isfinite(O).all() and np.isfinite(Sf).all()
     _check(P, O, Sf)
+
+
+# ---------------------------------------------------------------------------
+# Chunks of 128 tokens (bf16, a = k, b = beta k, dk = 128): the prep kernel forms each
+# chunk's factors from those of its two 64-token halves (secondary chunking) and a
+# 128-row serial pass applies them.  Ragged lengths cover a partial second half and an
+# empty one (T = 65, 129, 191, 200), a single token and exact multiples.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 127, 128, 129, 191, 200, 333])
+def test_c128_ragged_lengths(T):
+    P = inputs.make_problem("kda", B=2, H=2, T=T, chunk=128, s0_scale=0.3)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+
+
+@pytest.mark.parametrize("kind", ["deltanet_f32", "gdn", "kda"])
+@pytest.mark.parametrize("dv", [128, 64, 96])
+def test_c128_gates_and_value_sizes(kind, dv):
+    P = inputs.make_problem(kind, B=2, H=3, T=300, dk=128, dv=dv, dtype=torch.bfloat16, chunk=128,
+                            s0_scale=0.3)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+
+
+def test_c128_varlen_with_empty_and_short_sequences():
+    P = inputs.make_problem("kda_varlen", n_seq=6, total=700, min_len=1, H=3, chunk=128)
+    P.cu_seqlens = torch.tensor([0, 1, 129, 129, 300, 365, 700], dtype=torch.int32)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+    np.testing.assert_array_equal(Sf[2], P.S0[2].double().numpy())
+
+
+def test_c128_clip_and_in_place_state():
+    P = _kda_form("kda", B=2, H=2, T=250, chunk=128, s0_scale=0.3)
+    _check_clip(P)
+    S = P.S0.to("cuda").clone()
+    to = lambda t: None if t is None else t.to("cuda")
+    O, Sf = gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), log_alpha=to(P.log_alpha),
+                          S0=S, final_state=S, chunk_size=128, clip=True)
+    torch.cuda.synchronize()
+    assert Sf.data_ptr() == S.data_ptr()
+    _check(P, O.double().cpu().numpy(), Sf.double().cpu().numpy())
+
+
+def test_c128_matches_c64_and_is_deterministic():
+    P = inputs.make_problem("kda", B=1, H=4, T=777, s0_scale=0.3)
+    O64, S64 = gpu_run(P)
+    P.chunk = 128
+    O1, S1 = gpu_run(P)
+    O2, S2 = gpu_run(P)
+    np.testing.assert_array_equal(O1, O2)
+    np.testing.assert_array_equal(S1, S2)
+    # the two chunkings differ only in rounding
+    assert rel_err(O1, O64) <= TOL[P.dtype] and rel_err(S1, S64) <= TOL[P.dtype]
+
+
+def test_c128_flags_gates_beyond_its_range():
+    # no log-domain variant at C = 128: a half whose gate falls past the scaled operands'
+    # range raises bit 2 of the error word (the C = 64 path redoes such chunks instead)
+    P = inputs.make_problem("kda", B=1, H=2, T=260, la_range=(-4.0, -3.0), chunk=128)
+    ws = torch.zeros(gdr.workspace_bytes(P.B, P.H, P.T, P.dk, P.dv, C=128), dtype=torch.uint8,
+                     device="cuda")
+    to = lambda t: None if t is None else t.to("cuda")
+    gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), log_alpha=to(P.log_alpha), workspace=ws,
+                  chunk_size=128)
+    assert gdr.check_workspace_error(ws) & 2
+    P = inputs.make_problem("kda", B=1, H=2, T=260, chunk=128)
+    gdr.chunk_fwd(to(P.q), to(P.k), to(P.v), to(P.beta), log_alpha=to(P.log_alpha), workspace=ws,
+                  chunk_size=128)
+    assert gdr.check_workspace_error(ws) == 0
+
+
+@pytest.mark.parametrize("kind", ["kda", "gdn", "kda_varlen"])
+def test_c128_full_size_all_chains(kind):
+    P = inputs.make_problem(kind, chunk=128)
+    out = torch.full((P.B, P.T, P.H, P.dv), float("nan"), dtype=P.dtype, device="cuda")
+    O, Sf = gpu_run(P, out=out)
+    assert np.isfinite(O).all() and np.isfinite(Sf).all()
+    _check(P, O, Sf)
