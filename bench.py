@@ -12,6 +12,10 @@ duration measured with HIP events on the launch stream, against 8 TB/s.  HBM
 traffic and MFMA-busy figures come from the committed rocprofv3 counter summary,
 and only while the kernel source still matches the one it was measured on.  The
 CPU baseline is the fp64 oracle on the host cores.
+
+Before the W warm-up steps the call is repeated untimed for at least --settle-ms of
+device time (60 by default; the count is reported under "settle"), so that the timed
+steps do not fall in the GPU's power-management transient after idle.
 """
 import argparse
 import hashlib
@@ -93,7 +97,33 @@ def algorithmic_counts(P):
     return th * per_th + state, th * flops_th, th * tri_th
 
 
-def time_gpu(P, steps, warmup, cold_steps, for_backward=False):
+def settle(call, settle_ms):
+    """Repeat `call` untimed until `settle_ms` of device time have passed; returns the count.
+
+    A GPU that has been idle runs the first ~30 ms of this load through a power-management
+    transient: per-call times rise by ~15% around the tenth call and return to the steady
+    value by about the fiftieth (kernel traces of the first 400 calls on MI355X).  A short
+    warm-up followed by a short timed window would measure that transient, not the kernels;
+    the settle phase precedes the warm-up steps, which are then run and timed as asked.
+    """
+    import torch
+
+    if settle_ms <= 0:
+        return 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n, batch = 0, 8
+    e0.record()
+    while True:
+        for _ in range(batch):
+            call()
+        n += batch
+        e1.record()
+        e1.synchronize()
+        if e0.elapsed_time(e1) >= settle_ms:
+            return n
+
+
+def time_gpu(P, steps, warmup, cold_steps, for_backward=False, settle_ms=0.0):
     import torch
 
     from chunkwise_gated_delta_amd import gdr
@@ -114,6 +144,7 @@ def time_gpu(P, steps, warmup, cold_steps, for_backward=False):
     call = lambda: gdr.chunk_fwd(q, k, v, beta, log_alpha=la, a=a, b=b, S0=S0, cu_seqlens=cu,
                                  chunk_size=P.chunk, out=out, final_state=fin, clip=P.clip,
                                  workspace=ws, for_backward=for_backward)
+    n_settle = settle(call, settle_ms)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -145,7 +176,7 @@ def time_gpu(P, steps, warmup, cold_steps, for_backward=False):
     torch.cuda.synchronize()
     cold_ms = sorted(a.elapsed_time(b) for a, b in cold)
     del scrub
-    return total_ms / steps, launch_ms, cold_ms, out, fin
+    return total_ms / steps, launch_ms, cold_ms, out, fin, n_settle
 
 
 def machine_context():
@@ -295,6 +326,7 @@ def bench_backward(args):
             return bwd()
     else:
         call = bwd
+    n_settle = settle(call, args.settle_ms)
     for _ in range(args.warmup):
         g = call()
     torch.cuda.synchronize()
@@ -337,6 +369,8 @@ def bench_backward(args):
                      "alg_bytes_per_launch": alg_bytes},
         "mfma": {"alg_flops_per_launch": alg_flops, "achieved_tflops": tflops,
                  "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "frac": tflops / BF16_MFMA_PEAK_TFLOPS},
+        "settle": {"calls": n_settle, "device_ms_min": args.settle_ms,
+                   "note": "untimed calls before the warm-up steps (power-management transient)"},
     }
     if not args.no_cpu:
         import oracle
@@ -388,6 +422,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cold-steps", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="before the warm-up steps, repeat the call untimed until this much device "
+                         "time has passed (the GPU's power-management transient after idle); 0: off")
     ap.add_argument("--chunk", type=int, default=64, choices=[64, 128],
                     help="forward chunk size C (128: bf16 without a, b at dk = 128 only)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
@@ -442,8 +479,9 @@ def main():
 
     P = inputs.make_problem(args.workload, chunk=args.chunk)
     alg_bytes, alg_flops, tri_flops = algorithmic_counts(P)
-    ms, launch_ms, cold_ms, out, fin = time_gpu(P, args.steps, args.warmup, args.cold_steps,
-                                                for_backward=args.for_backward)
+    ms, launch_ms, cold_ms, out, fin, n_settle = time_gpu(
+        P, args.steps, args.warmup, args.cold_steps, for_backward=args.for_backward,
+        settle_ms=args.settle_ms)
     call_ms = float(np.mean(launch_ms))
     tokens = P.B * P.T  # packed total for the varlen workload (B = 1)
     achieved_gbs = alg_bytes / (call_ms * 1e-3) / 1e9
@@ -490,6 +528,8 @@ def main():
                  "lower_triangle_flops_per_launch": tri_flops,
                  "frac_lower_triangle": tri_flops / (call_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                  "counter_busy_frac": cc.get("mfma_busy_frac")},
+        "settle": {"calls": n_settle, "device_ms_min": args.settle_ms,
+                   "note": "untimed calls before the warm-up steps (power-management transient)"},
     }
     if not args.no_context:
         result["context"] = machine_context()
