@@ -11,7 +11,8 @@
 // Three passes produce the states the per-chunk gradients need:
 //   forward   the forward state kernel, saving S_p (the state entering each chunk)
 //   reverse   dS_p = dS_n Diag(gamma_C) + (K^ dS_n^T)^T W' + dO^T Q~ over the chunks in
-//             reverse order (the forward state kernel on a reordered block), saving
+//             reverse order (the forward state kernel on a reordered block, which the
+//             forward state pass writes as it reads each forward block), saving
 //             dS_n (the gradient of the state leaving each chunk); K^ = K-> gamma_C,
 //             W' = -W and Q~ = Q<- - A_qk W come from the forward prep blocks
 //   post      one workgroup per (chunk, head), with dSg = dS_n Diag(gamma_C):
@@ -33,64 +34,6 @@
 
 namespace gdr {
 namespace {
-
-// ---------------------------------------------------------------------------------
-// Reordering of the forward blocks into the slots the reverse state pass reads.
-// ---------------------------------------------------------------------------------
-// Byte offset of element (row r, contraction column d) in a row-tile fragment slot
-// (W', Q~: rows = tokens, K = DK), and of element (dk row d, token t) in a
-// transposed slot (K^: rows = dk, K = 64 tokens).  See Blk.
-template <int DK>
-__device__ __forceinline__ int nat_off(int r, int d) {
-    const int rt = r >> 5, s = d >> 4, l = (r & 31) + 32 * ((d & 15) >> 3);
-    return (((rt * (DK / 16) + s) * 64 + l) * 8 + (d & 7)) * 2;
-}
-__device__ __forceinline__ int tr_off(int d, int t) {
-    const int w = d >> 5, s = t >> 4, l = (d & 31) + 32 * ((t & 15) >> 3);
-    return (((w * 4 + s) * 64 + l) * 8 + (t & 7)) * 2;
-}
-
-// Backward block of job j: W' slot <- K^ (natural layout), A^ slot <- W' (transposed),
-// K^b slot <- Q~ (transposed), gamma_C copied.  One workgroup per block; the other
-// slots are left as they are (the reverse pass does not use them).
-template <int DK, bool DP>
-__global__ __launch_bounds__(kThreads) void kda_bwd_reorder_kernel(const char *fwd, char *bwd, int nblk) {
-    using F = Blk<DK, DP>;  // forward blocks (DPLR: the K^ slot holds A^)
-    using R = Blk<DK, true>;
-    const int j = blockIdx.x;
-    if (j >= nblk) return;
-    const char *src = fwd + (size_t)j * F::bytes;
-    char *dst = bwd + (size_t)j * R::bytes;
-    constexpr int kPieces = 8 * DK;  // 16-byte pieces per slot
-    for (int u = threadIdx.x; u < 3 * kPieces; u += kThreads) {
-        const int slot = u / kPieces, pc = u % kPieces;
-        const int l = pc & 63, st = pc >> 6;
-        uint16_t v[8];
-        if (slot == 0) {
-            // destination natural (row r, cols d..d+7); source K^ transposed (d + e, r)
-            const int rt = st / (DK / 16), s = st % (DK / 16);
-            const int r = 32 * rt + (l & 31), d = 16 * s + 8 * (l >> 5);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = *(const uint16_t *)(src + F::oK + tr_off(d + e, r));
-        } else {
-            // destination transposed (dk row d, tokens t..t+7); source natural (t + e, d)
-            const int w = st >> 2, s = st & 3;
-            const int d = 32 * w + (l & 31), t = 16 * s + 8 * (l >> 5);
-            const int so = slot == 1 ? F::oW : F::oQ;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = *(const uint16_t *)(src + so + nat_off<DK>(t + e, d));
-        }
-        const int dso = slot == 0 ? R::oW : (slot == 1 ? R::oK : R::oKb);
-        uint4 o;
-        o.x = v[0] | ((uint32_t)v[1] << 16);
-        o.y = v[2] | ((uint32_t)v[3] << 16);
-        o.z = v[4] | ((uint32_t)v[5] << 16);
-        o.w = v[6] | ((uint32_t)v[7] << 16);
-        ((uint4 *)(dst + dso))[pc] = o;
-    }
-    for (int i = threadIdx.x; i < DK; i += kThreads)
-        ((float *)(dst + R::oG))[i] = ((const float *)(src + F::oG))[i];
-}
 
 // ---------------------------------------------------------------------------------
 // Per-chunk gradients.

@@ -113,6 +113,7 @@ struct SplitParams {
     int *err;
     char *blk;      // (chunk, head) blocks
     uint16_t *states;  // state kernel modes 1, 2: bf16 [chunk][head][dv][dk], the state entering each step
+    int fblk;  // state kernel mode 2: byte stride of the forward blocks it reads
     long total;
     int H, T, dv, n_seq, n_tiles;
     int C;           // chunk size (always kC here)
@@ -1343,6 +1344,13 @@ struct StateSmem {
     static constexpr int oO = oVn + kDVT * kCS * 2;  // output staging, 2 x bf16 [32][kVS]
     static constexpr int oG = oO + 2 * 32 * kVS * 2;  // gamma_C, 2 x fp32 [DK] (chunk parity)
     static constexpr int bytes = oG + 2 * DK * 4;
+    // The reverse pass reads the forward blocks and transposes their operands here: K^ as
+    // K^T row-major [DK][kCS]; W' and Q~ row-major [64 tokens][KS], two of each (chunk
+    // parity: they are read after the step's second barrier).
+    static constexpr int oRt = bytes;
+    static constexpr int oRw = oRt + DK * kCS * 2;
+    static constexpr int oRq = oRw + 2 * kC * KS * 2;
+    static constexpr int bytes_rev = oRq + 2 * kC * KS * 2;
 };
 
 // Operands of one chunk for one wave, loaded two chunks ahead.
@@ -1377,10 +1385,11 @@ constexpr int kDepth = 2;
 
 // Modes of the state kernel.  Forward: the forward pass.  SaveStates: the forward
 // recurrence without the output, writing the state that enters each chunk (bf16)
-// to p.states.  Reverse: the chunks in reverse order, no output and no Ab V term,
-// writing the state entering each step to p.states; with the slots of a backward
-// block (W' slot: K^, A^ slot: W', K^b slot: Q~, value tile: dO) and DP set this is
-// the backward state pass dS <- dS Diag(gamma_C) + (K^ dS^T)^T W' + dO^T Q~.
+// to p.states.  Reverse (DP set): the chunks in reverse order on the forward blocks
+// (byte stride p.fblk), no output and no Ab V term, writing the state entering each
+// step to p.states: with K^ (DPLR: A^) in place of W', W'^T in place of the K^ tile
+// and Q~^T in place of K^b, all three transposed in LDS, and dO as the value tile,
+// this is the backward state pass dS <- dS Diag(gamma_C) + (K^ dS^T)^T W' + dO^T Q~.
 // kForwardSave: the forward pass that also stores the states (both of the first two)
 constexpr int kForward = 0, kSaveStates = 1, kReverse = 2, kForwardSave = 3;
 
@@ -1391,8 +1400,12 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     constexpr int KS = L::KS;
     constexpr int NSW = DK / 32;  // waves owning a 32x32 S^T tile
     constexpr bool kOut = MODE == kForward || MODE == kForwardSave;  // writes O
+    // The reverse pass runs on the forward blocks: it loads what the forward loads (no
+    // K^b) and takes the transposes it needs from LDS.
+    constexpr bool kRev = MODE == kReverse;
+    constexpr bool kLoadKb = DP && !kRev;
 
-    __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+    __shared__ __attribute__((aligned(16))) char smem[kRev ? L::bytes_rev : L::bytes];
     uint16_t *sS = (uint16_t *)(smem + L::oS);
     uint16_t *sV = (uint16_t *)(smem + L::oV);
     uint16_t *sVn = (uint16_t *)(smem + L::oVn);
@@ -1502,14 +1515,15 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     const int vr = tid >> 2, vc = 8 * (tid & 3);
     // Loads of one chunk in two batches: the W'/Q~ tile first, the rest later in the
     // step, so that the memory pipeline is fed while the wave computes.
+    const size_t bstride = kRev ? (size_t)p.fblk : (size_t)Bk::bytes;
     auto load_p = [&](Pre<DK> &x, int c) {
-        const char *bp = p.blk + ((size_t)(cbase + cid(c)) * H + h) * Bk::bytes;
+        const char *bp = p.blk + ((size_t)(cbase + cid(c)) * H + h) * bstride;
         const uint4 *pw = (const uint4 *)(bp + (vw ? Bk::oW : Bk::oQ)) + rt * (DK / 16) * 64 + lane;
 #pragma unroll
         for (int s = 0; s < DK / 16; ++s) x.P[s] = pw[s * 64];
     };
     auto load_rest = [&](Pre<DK> &x, int c) {
-        const char *bp = p.blk + ((size_t)(cbase + cid(c)) * H + h) * Bk::bytes;
+        const char *bp = p.blk + ((size_t)(cbase + cid(c)) * H + h) * bstride;
         const uint4 *pa = (const uint4 *)(bp + (vw ? Bk::oAb : Bk::oAo)) + rt * 128 + lane;
         x.A[0] = pa[0];
         x.A[1] = pa[64];
@@ -1521,7 +1535,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
             const uint4 *pk = (const uint4 *)(bp + Bk::oK) + wave * 256 + lane;
 #pragma unroll
             for (int s = 0; s < 4; ++s) x.K[s] = pk[s * 64];
-            if constexpr (DP) {
+            if constexpr (kLoadKb) {
                 const uint4 *pkb = (const uint4 *)(bp + Bk::oKb) + wave * 256 + lane;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) x.Kb[s] = pkb[s * 64];
@@ -1545,7 +1559,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     };
 
     auto step = [&](int c, Pre<DK> &x, Pre<DK> &nx) {
-        wait_vmcnt<(kDepth - 1) * kMinLoadsPerChunk<DK, DP>>();  // operands of chunk c have arrived
+        wait_vmcnt<(kDepth - 1) * kMinLoadsPerChunk<DK, kLoadKb>>();  // operands of chunk c have arrived
         float *sG = (float *)(smem + L::oG) + (c & 1) * DK;
         if (wave == 0 && lane < DK / 4) ((float4 *)sG)[lane] = x.G;
         {
@@ -1556,7 +1570,26 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
         if (kOut && !vw && c > 0) store_out(c - 1);
         const int cn = c + kDepth < nck ? c + kDepth : nck - 1;
         load_p(nx, cn);
-        lds_barrier();  // value tile, gamma_C and S of chunk c visible
+        // reverse pass: this chunk's K^ tiles (as K^T) and W', Q~ rows, row-major in LDS
+        uint16_t *sRt = kRev ? (uint16_t *)(smem + L::oRt) : nullptr;
+        const uint16_t *sRw = kRev ? (const uint16_t *)(smem + L::oRw) + (c & 1) * kC * KS : nullptr;
+        const uint16_t *sRq = kRev ? (const uint16_t *)(smem + L::oRq) + (c & 1) * kC * KS : nullptr;
+        if constexpr (kRev) {
+            // (through registers: as a plain copy the compiler would keep the operand sets
+            // in scratch memory)
+            auto put = [](uint16_t *d, uint4 u) {
+                asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+                *(uint4 *)d = u;
+            };
+            if (wave < NSW) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) put(sRt + (32 * wave + l32) * kCS + 16 * s + 8 * lh, x.K[s]);
+            }
+            uint16_t *sR = (uint16_t *)(vw ? sRw : sRq);
+#pragma unroll
+            for (int s = 0; s < DK / 16; ++s) put(sR + (32 * rt + l32) * KS + 16 * s + 8 * lh, x.P[s]);
+        }
+        lds_barrier();  // value tile, gamma_C and S of chunk c visible (reverse: and its operands)
         if (MODE != kForward && emit) {  // kSaveStates, kReverse, kForwardSave
             // the state entering this step, bf16, 16 bytes per thread and pass
             uint16_t *dst = p.states + (((size_t)(cbase + cid(c)) * H + h) * DV + j0) * DK;
@@ -1574,6 +1607,11 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
             if (i < 2 || rt || DP) fv[i] = frag_tr32(sV, 16 * i, kVS, 0, lane);
 #pragma unroll
         for (int s = 0; s < DK / 16; ++s) fs[s] = frag(sS, l32, KS, 16 * s + 8 * lh);
+        // reverse: the row tile of K^ (natural layout) in place of W'
+        bf16x8 fp[DK / 16];
+#pragma unroll
+        for (int s = 0; s < DK / 16; ++s)
+            fp[s] = kRev ? frag_tr32(sRt, 16 * s, kCS, 32 * rt, lane) : as_bf16x8(x.P[s]);
         f32x16 acc = {};
         if (vw) {
             // V_new = Ab V + W' S^T; register 4q+e is V_new[row 32rt + 8q + 4lh + e][dv l32]
@@ -1586,7 +1624,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
                 }
             }
 #pragma unroll
-            for (int s = 0; s < DK / 16; ++s) acc = mfma32x32(as_bf16x8(x.P[s]), fs[s], acc);
+            for (int s = 0; s < DK / 16; ++s) acc = mfma32x32(fp[s], fs[s], acc);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 store4(sVn + l32 * kCS + 32 * rt + 8 * q + 4 * lh, acc[4 * q + 0], acc[4 * q + 1],
@@ -1619,14 +1657,21 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
                 ST[4 * q + 0] *= g.x; ST[4 * q + 1] *= g.y;
                 ST[4 * q + 2] *= g.z; ST[4 * q + 3] *= g.w;
             }
+            // reverse: W'^T and Q~^T tiles of dk rows 32w.. in place of the K^ and K^b tiles
+            bf16x8 fk[4], fb[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                fk[s] = kRev ? frag_tr32(sRw, 16 * s, KS, 32 * wave, lane) : as_bf16x8(x.K[s]);
+                if constexpr (DP) fb[s] = kRev ? frag_tr32(sRq, 16 * s, KS, 32 * wave, lane) : as_bf16x8(x.Kb[s]);
+            }
             bf16x8 fn[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) fn[s] = frag(sVn, l32, kCS, 16 * s + 8 * lh);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) ST = mfma32x32(as_bf16x8(x.K[s]), fn[s], ST);
+            for (int s = 0; s < 4; ++s) ST = mfma32x32(fk[s], fn[s], ST);
             if constexpr (DP) {  // + V^T Diag(beta) K^
 #pragma unroll
-                for (int s = 0; s < 4; ++s) ST = mfma32x32(as_bf16x8(x.Kb[s]), fv[s], ST);
+                for (int s = 0; s < 4; ++s) ST = mfma32x32(fb[s], fv[s], ST);
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -2019,7 +2064,7 @@ FwdArgs fwd_view(const BwdArgs &b) {
 // has it, so that a forward call's workspace can stand in for the first kernel.
 struct BwdLayout {
     SplitLayout fw;
-    size_t sub_off, bwd_off, s_off, ds_off, seg_off, total;
+    size_t sub_off, s_off, ds_off, seg_off, total;
     bool sub;
     int runs;  // of the segmented state passes (0: plain)
 };
@@ -2031,8 +2076,7 @@ BwdLayout bwd_layout(const BwdArgs &b, int N) {
     const size_t nblk = (size_t)b.H * L.fw.max_chunks;
     L.sub = b.gate != kGateNone;
     L.sub_off = seg_offset(L.fw.total);
-    L.bwd_off = seg_offset(L.sub_off + (L.sub ? nblk * 4 : 0));
-    L.s_off = L.bwd_off + nblk * blk_bytes(b.dk, true);
+    L.s_off = seg_offset(L.sub_off + (L.sub ? nblk * 4 : 0));
     L.ds_off = L.s_off + nblk * b.dv * b.dk * 2;
     L.seg_off = seg_offset(L.ds_off + nblk * b.dv * b.dk * 2);
     L.runs = seg_runs(N * b.H, b.dk, b.dv, chunks_per_chain(a), false);
@@ -2213,8 +2257,8 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
     sp.sub = lay.sub ? (int *)(ws + lay.sub_off) : nullptr;
     const int runs = lay.runs ? seg_runs(n_seq_eff * b.H, b.dk, b.dv, chunks_per_chain(fwd_view(b)), true) : 0;
     // the reverse pass: backward blocks, dO as the value tile, dS_final in, dS0 out
-    SplitParams rp = sp;
-    rp.blk = ws + lay.bwd_off;
+    SplitParams rp = sp;  // on the forward blocks
+    rp.fblk = blk_bytes(b.dk, b.a != nullptr);
     rp.v = (const bf16 *)b.dO;
     rp.S0 = b.dS_final;
     rp.Sf = b.grad_S0;
@@ -2251,9 +2295,7 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
                 hipLaunchKernelGGL((kda_prep_kernel<DK, G, D, false, true>), grid_sub, dim3(kThreads), 0, s, sp); \
         }                                                                                          \
         if (!b.reuse_states) run_state<DK, D, kSaveStates>(sp, runs, s);                          \
-        hipLaunchKernelGGL((kda_bwd_reorder_kernel<DK, D>), grid_jobs, dim3(kThreads), 0, s,       \
-                           (const char *)sp.blk, rp.blk, (int)njobs);                              \
-        run_state<DK, true, kReverse>(rp, runs, s);                                               \
+        run_state<DK, true, kReverse>(rp, runs, s); /* on the forward blocks */                    \
         hipLaunchKernelGGL((POST<DK, G>), grid_post, dim3(kThreads), 0, s, bp);                   \
     } while (0)
 #define GDR_BWD_GATES(DK, D, POST)                                        \
