@@ -123,6 +123,36 @@ __device__ __forceinline__ f32x4 mma_tile(const uint16_t *A, int lda, const uint
     return acc;
 }
 
+// The same product split in two, for a row block whose A fragments serve several output
+// tiles: load_a reads them once, mma_b multiplies them by one B tile (same steps, same
+// order, same result as mma_tile).
+template <bool AT, int KMAX>
+__device__ __forceinline__ void load_a(bf16x8 (&fa)[KMAX / 32], const uint16_t *A, int lda, int m0,
+                                       int k0, int k1, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int st = 0; st < KMAX / 32; ++st) {
+        const int k = k0 + 32 * st;
+        if (k < k1) fa[st] = AT ? frag_tr(A, k, lda, m0, lane) : frag(A, m0 + r, lda, k + 8 * g);
+    }
+}
+template <bool BT, int KMAX>
+__device__ __forceinline__ f32x4 mma_b(const bf16x8 (&fa)[KMAX / 32], const uint16_t *B, int ldb, int n0,
+                                       int k0, int k1, f32x4 acc, int lane) {
+    constexpr int NS = KMAX / 32;
+    const int r = lane & 15, g = lane >> 4;
+    bf16x8 fb[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        const int k = k0 + 32 * st;
+        if (k < k1) fb[st] = BT ? frag(B, n0 + r, ldb, k + 8 * g) : frag_tr(B, k, ldb, n0, lane);
+    }
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+        if (k0 + 32 * st < k1) acc = mfma(fb[st], fa[st], acc);
+    return acc;
+}
+
 // Operand fragments of v_mfma_f32_16x16x16_bf16 (lane l: index l%16, contraction
 // 4(l/16)+0..3): from a row-major [m][k] array (8-byte read) or, gathered with one
 // LDS transpose read, from an array whose rows run along the contraction.
@@ -163,8 +193,10 @@ struct BwdSmem {
     static constexpr int oGam = oBeta + kC * 4; // fp32 [DK] gamma_C
     static constexpr int oGp = oGam + DK * 4;   // fp32 [8][DK] gate partial sums
     static constexpr int oDb = oGp + 8 * DK * 4;  // fp32 [64] dbeta
-    static constexpr int oDg = oDb + kC * 4;    // fp32 [4][DK] last-row term of dg, per wave
-    static constexpr int oSpf = oDg + 4 * DK * 4;  // fp32 [DK] 2^n, the state's scale
+    // fp32 [8][DK] last-row term of dg: slot w the S_p dSg part of wave w, slot 4 + w its
+    // K-> dKg part (each written once per job: no clearing, no read-modify-write)
+    static constexpr int oDg = oDb + kC * 4;
+    static constexpr int oSpf = oDg + 8 * DK * 4;  // fp32 [DK] 2^n, the state's scale
     static constexpr int bytes = oSpf + DK * 4;
     // final stage: Gamma fp32 [64][DK] over Q<-..K-> (free by then), dg fp32 [64][DK] over T
     static_assert(kC * DK * 4 <= 3 * QK, "Gamma fits over the operand arrays");
@@ -362,7 +394,6 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             }
         }
         for (int i = tid; i < kC; i += kThreads) sDb[i] = 0.f;
-        for (int i = tid; i < 4 * DK; i += kThreads) sDg[i] = 0.f;
     }
     lds_barrier();
 
@@ -371,19 +402,20 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     for (int idx = tid; idx < kC * CS / 8; idx += kThreads) ((uint4 *)sA)[idx] = make_uint4(0u, 0u, 0u, 0u);
     {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        bf16x8 fkl[NT / 2], fql[NT / 2];  // K<-, Q<- rows R0.. (K = DK)
+        load_a<false, DK>(fkl, sKl, KS, R0, 0, DK, lane);
+        load_a<false, DK>(fql, sQl, KS, R0, 0, DK, lane);
         for (int tj = 0; tj < 4; ++tj) {
             f32x4 kk = z, aq = z;
             if (tj <= wave) {
-                kk = mma_tile<false, true, DK>(sKl, KS, sKr, KS, R0, 16 * tj, 0, DK, z, lane);
-                aq = mma_tile<false, true, DK>(sQl, KS, sKr, KS, R0, 16 * tj, 0, DK, z, lane);
+                kk = mma_b<true, DK>(fkl, sKr, KS, 16 * tj, 0, DK, z, lane);
+                aq = mma_b<true, DK>(fql, sKr, KS, 16 * tj, 0, DK, z, lane);
             }
-            const int row = R0 + r16;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int col = 16 * tj + 4 * g4 + e;
-                sKK[row * 68 + col] = col < row ? kk[e] : 0.f;
-                sAqk[row * CS + col] = __builtin_bit_cast(uint16_t, (__bf16)(col <= row ? aq[e] : 0.f));
-            }
+            const int row = R0 + r16, col = 16 * tj + 4 * g4;
+            *(float4 *)(sKK + row * 68 + col) = make_float4(col < row ? kk[0] : 0.f, col + 1 < row ? kk[1] : 0.f,
+                                                         col + 2 < row ? kk[2] : 0.f, col + 3 < row ? kk[3] : 0.f);
+            store4(sAqk + row * CS + col, col <= row ? aq[0] : 0.f, col + 1 <= row ? aq[1] : 0.f,
+                   col + 2 <= row ? aq[2] : 0.f, col + 3 <= row ? aq[3] : 0.f);
         }
     }
     lds_barrier();
@@ -412,9 +444,12 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) sA[(R0 + 4 * u + s) * CS + j] = __builtin_bit_cast(uint16_t, (__bf16)xs[u]);
-        for (int idx = tid; idx < kC * kC; idx += kThreads) {
-            const int i = idx >> 6, k2 = idx & 63;
-            sL[i * CS + k2] = __builtin_bit_cast(uint16_t, (__bf16)(sBeta[i] * sKK[i * 68 + k2]));
+        for (int idx = tid; idx < kC * kC / 8; idx += kThreads) {  // eight columns per piece
+            const int i = idx >> 3, k8 = 8 * (idx & 7);
+            const float bi = sBeta[i];
+            const float4 a = *(const float4 *)(sKK + i * 68 + k8), b = *(const float4 *)(sKK + i * 68 + k8 + 4);
+            *(uint4 *)(sL + i * CS + k8) = make_uint4(pack_bf16x2(bi * a.x, bi * a.y), pack_bf16x2(bi * a.z, bi * a.w),
+                                                      pack_bf16x2(bi * b.x, bi * b.y), pack_bf16x2(bi * b.z, bi * b.w));
         }
     }
     lds_barrier();
@@ -445,9 +480,13 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         store4(sA + (m0 + r16) * CS + n0 + 4 * g4, -c[0], -c[1], -c[2], -c[3]);
     }
     lds_barrier();
-    for (int idx = tid; idx < kC * kC; idx += kThreads) {
-        const int i = idx >> 6, j = idx & 63;
-        sAb[i * CS + j] = __builtin_bit_cast(uint16_t, (__bf16)(bf16_lo(sA[i * CS + j]) * sBeta[j]));
+    for (int idx = tid; idx < kC * kC / 8; idx += kThreads) {  // eight columns per piece
+        const int i = idx >> 3, j8 = 8 * (idx & 7);
+        const uint4 a = *(const uint4 *)(sA + i * CS + j8);
+        const float4 b0 = *(const float4 *)(sBeta + j8), b1 = *(const float4 *)(sBeta + j8 + 4);
+        *(uint4 *)(sAb + i * CS + j8) =
+            make_uint4(pack_bf16x2(bf16_lo(a.x) * b0.x, bf16_hi(a.x) * b0.y), pack_bf16x2(bf16_lo(a.y) * b0.z, bf16_hi(a.y) * b0.w),
+                       pack_bf16x2(bf16_lo(a.z) * b1.x, bf16_hi(a.z) * b1.y), pack_bf16x2(bf16_lo(a.w) * b1.z, bf16_hi(a.w) * b1.w));
     }
     lds_barrier();
 
@@ -455,8 +494,10 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         const int k1 = R0 + 16 <= 32 ? 32 : 64;  // Ab is lower triangular
+        bf16x8 fab[2];
+        load_a<false, kC>(fab, sAb, CS, R0, 0, k1, lane);
         for (int tn = 0; tn < NT; ++tn) {
-            const f32x4 w = mma_tile<false, false, kC>(sAb, CS, sKl, KS, R0, 16 * tn, 0, k1, z, lane);
+            const f32x4 w = mma_b<false, kC>(fab, sKl, KS, 16 * tn, 0, k1, z, lane);
             store4(sW + (R0 + r16) * KS + 16 * tn + 4 * g4, w[0], w[1], w[2], w[3]);
         }
     }
@@ -509,15 +550,35 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         {
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
             const int k1 = R0 + 16 <= 32 ? 32 : 64;
+            // each product's A fragments (rows R0..) read once for both 16-column tiles
+            f32x4 u[2], dv[2];
+            {
+                bf16x8 fa[2];
+                load_a<false, kC>(fa, sAb, CS, R0, 0, k1, lane);
 #pragma unroll
-            for (int tn = 0; tn < 2; ++tn) {
-                f32x4 u = mma_tile<false, false, kC>(sAb, CS, sV, VS, R0, 16 * tn, 0, k1, z, lane);
-                const f32x4 ws = mma_tile<false, true, DK>(sW, KS, sSp, KS, R0, 16 * tn, 0, DK, z, lane);
-                f32x4 dv = mma_tile<false, true, DK>(sKr, KS, sdS, KS, R0, 16 * tn, 0, DK, z, lane);
-                dv = mma_tile<true, false, kC>(sAqk, CS, sdO, VS, R0, 16 * tn, lo_k, kC, dv, lane);
-                store4(sVn + (R0 + r16) * VS + 16 * tn + 4 * g4, u[0] - ws[0], u[1] - ws[1],
-                       u[2] - ws[2], u[3] - ws[3]);
-                store4(sdVn + (R0 + r16) * VS + 16 * tn + 4 * g4, dv[0], dv[1], dv[2], dv[3]);
+                for (int tn = 0; tn < 2; ++tn) u[tn] = mma_b<false, kC>(fa, sV, VS, 16 * tn, 0, k1, z, lane);
+            }
+            {
+                bf16x8 fa[NT / 2];
+                load_a<false, DK>(fa, sW, KS, R0, 0, DK, lane);
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn) {
+                    const f32x4 ws = mma_b<true, DK>(fa, sSp, KS, 16 * tn, 0, DK, z, lane);
+                    store4(sVn + (R0 + r16) * VS + 16 * tn + 4 * g4, u[tn][0] - ws[0], u[tn][1] - ws[1],
+                           u[tn][2] - ws[2], u[tn][3] - ws[3]);
+                }
+                load_a<false, DK>(fa, sKr, KS, R0, 0, DK, lane);
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn) dv[tn] = mma_b<true, DK>(fa, sdS, KS, 16 * tn, 0, DK, z, lane);
+            }
+            {
+                bf16x8 fa[2];
+                load_a<true, kC>(fa, sAqk, CS, R0, lo_k, kC, lane);
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn) {
+                    dv[tn] = mma_b<false, kC>(fa, sdO, VS, 16 * tn, lo_k, kC, dv[tn], lane);
+                    store4(sdVn + (R0 + r16) * VS + 16 * tn + 4 * g4, dv[tn][0], dv[tn][1], dv[tn][2], dv[tn][3]);
+                }
             }
         }
         lds_barrier();
@@ -526,9 +587,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             const int row = R0 + r16;
             const float br = sBeta[row];
             // dV = Diag(beta) At^T dV_new
+            bf16x8 fat[2];
+            load_a<true, kC>(fat, sA, CS, R0, lo_k, kC, lane);
 #pragma unroll
             for (int tn = 0; tn < 2; ++tn) {
-                const f32x4 d = mma_tile<true, false, kC>(sA, CS, sdVn, VS, R0, 16 * tn, lo_k, kC, z, lane);
+                const f32x4 d = mma_b<false, kC>(fat, sdVn, VS, 16 * tn, lo_k, kC, z, lane);
                 if (row < m) {
                     uint2 o;
                     o.x = pack_bf16x2(br * d[0], br * d[1]);
@@ -580,15 +643,17 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             float x = gpart[e];
 #pragma unroll
             for (int off = DK / 8; off < 64; off <<= 1) x += __shfl_xor(x, off);
-            if (lane < DK / 8) sDg[wave * DK + 8 * lane + e] += x;  // this wave's slot
+            if (lane < DK / 8) sDg[wave * DK + 8 * lane + e] = x;  // this wave's slot
         }
     }
     lds_barrier();
     {
         const int row = R0 + r16;
+        bf16x8 fdw[NT / 2];
+        load_a<false, DK>(fdw, sdW, KS, R0, 0, DK, lane);
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {
-            aY[tj] = mma_tile<false, true, DK>(sdW, KS, sKl, KS, R0, 16 * tj, 0, DK, aY[tj], lane);
+            aY[tj] = mma_b<true, DK>(fdw, sKl, KS, 16 * tj, 0, DK, aY[tj], lane);
             store4(sY + row * CS + 16 * tj + 4 * g4, aY[tj][0], aY[tj][1], aY[tj][2], aY[tj][3]);
         }
     }
@@ -596,9 +661,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
     {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         const int row = R0 + r16;
+        bf16x8 fat[2];
+        load_a<true, kC>(fat, sA, CS, R0, lo_k, kC, lane);
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {
-            const f32x4 zt = mma_tile<true, false, kC>(sA, CS, sY, CS, R0, 16 * tj, lo_k, kC, z, lane);
+            const f32x4 zt = mma_b<false, kC>(fat, sY, CS, 16 * tj, lo_k, kC, z, lane);
             store4(sZ + row * CS + 16 * tj + 4 * g4, zt[0], zt[1], zt[2], zt[3]);
             if (tj == wave && (r16 >> 2) == g4) sDb[row] = zt[r16 & 3];  // diag(Z)
         }
@@ -609,12 +676,15 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         const int row = R0 + r16;
         const float br = sBeta[row];
         float db2 = 0.f;
+        bf16x8 fz[2], fkl[NT / 2];  // Z, K<- rows R0..
+        load_a<false, kC>(fz, sZ, CS, R0, 0, kC, lane);
+        load_a<false, DK>(fkl, sKl, KS, R0, 0, DK, lane);
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {
             f32x4 dx = z;
             if (tj <= wave) {
-                dx = mma_tile<false, true, kC>(sZ, CS, sAb, CS, R0, 16 * tj, 0, kC, z, lane);
-                const f32x4 kk = mma_tile<false, true, DK>(sKl, KS, sKr, KS, R0, 16 * tj, 0, DK, z, lane);
+                dx = mma_b<true, kC>(fz, sAb, CS, 16 * tj, 0, kC, z, lane);
+                const f32x4 kk = mma_b<true, DK>(fkl, sKr, KS, 16 * tj, 0, DK, z, lane);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int col = 16 * tj + 4 * g4 + e;
@@ -649,15 +719,37 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         const int row = R0 + r16;
         const float br = sBeta[row];
         float dgp[NT][4];
+        // one product at a time, its row block's A fragments read once for all NT tiles
+        {
+            bf16x8 fat[2], fdx[2];  // At^T and dXm rows R0..
+            load_a<true, kC>(fat, sA, CS, R0, lo_k, kC, lane);
+            load_a<false, kC>(fdx, sdXm, CS, R0, 0, kC, lane);
+#pragma unroll
+            for (int tn = 0; tn < NT; ++tn) {
+                f32x4 a = mma_b<false, kC>(fat, sdW, KS, 16 * tn, lo_k, kC, z, lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] *= br;
+                gKl[tn] = mma_b<false, kC>(fdx, sKr, KS, 16 * tn, 0, kC, a, lane);
+            }
+        }
+        {
+            bf16x8 fda[2], fdx[2];  // dA^T and dXm^T rows R0..
+            load_a<true, kC>(fda, sdA, CS, R0, lo_k, kC, lane);
+            load_a<true, kC>(fdx, sdXm, CS, R0, lo_k, kC, lane);
+#pragma unroll
+            for (int tn = 0; tn < NT; ++tn) {
+                const f32x4 b = mma_b<false, kC>(fda, sQl, KS, 16 * tn, lo_k, kC, aKg[tn], lane);
+                gKr[tn] = mma_b<false, kC>(fdx, sKl, KS, 16 * tn, lo_k, kC, b, lane);
+            }
+        }
+        {
+            bf16x8 fda[2];  // dA rows R0..
+            load_a<false, kC>(fda, sdA, CS, R0, 0, kC, lane);
+#pragma unroll
+            for (int tn = 0; tn < NT; ++tn) gQl[tn] = mma_b<false, kC>(fda, sKr, KS, 16 * tn, 0, kC, aQ[tn], lane);
+        }
 #pragma unroll
         for (int tn = 0; tn < NT; ++tn) {
-            f32x4 a = mma_tile<true, false, kC>(sA, CS, sdW, KS, R0, 16 * tn, lo_k, kC, z, lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) a[e] *= br;
-            gKl[tn] = mma_tile<false, false, kC>(sdXm, CS, sKr, KS, R0, 16 * tn, 0, kC, a, lane);
-            f32x4 b = mma_tile<true, false, kC>(sdA, CS, sQl, KS, R0, 16 * tn, lo_k, kC, aKg[tn], lane);
-            gKr[tn] = mma_tile<true, false, kC>(sdXm, CS, sKl, KS, R0, 16 * tn, lo_k, kC, b, lane);
-            gQl[tn] = mma_tile<false, false, kC>(sdA, CS, sKr, KS, R0, 16 * tn, 0, kC, aQ[tn], lane);
             // last-row term: sum over rows of K-> dKg, per column
             const uint2 kr = *(const uint2 *)(sKr + row * KS + 16 * tn + 4 * g4);
             const uint2 ql = *(const uint2 *)(sQl + row * KS + 16 * tn + 4 * g4);
@@ -672,12 +764,12 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             }
         }
 #pragma unroll
-        for (int tn = 0; tn < NT; ++tn)
+        for (int tn = 0; tn < NT; ++tn) {
+            float s4[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float s = group_sum<16>(dgp[tn][e]);
-                if (r16 == 0) sDg[wave * DK + 16 * tn + 4 * g4 + e] += s;
-            }
+            for (int e = 0; e < 4; ++e) s4[e] = group_sum<16>(dgp[tn][e]);
+            if (r16 == 0) *(float4 *)(sDg + (4 + wave) * DK + 16 * tn + 4 * g4) = make_float4(s4[0], s4[1], s4[2], s4[3]);
+        }
     }
     lds_barrier();  // the operand arrays are free: Gamma goes over them
 
@@ -697,9 +789,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         for (int tn = 0; tn < NT; ++tn) {
             const int col = 16 * tn + 4 * g4;
             float dq4[4], dk4[4];
+            const float4 g4v = *(const float4 *)(sGm + row * DK + col);
+            const float gr[4] = {g4v.x, g4v.y, g4v.z, g4v.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float gv = sGm[row * DK + col + e] * kLog2e;
+                const float gv = gr[e] * kLog2e;
                 const float G = exp2_fast(gv), iG = exp2_fast(-gv);
                 dq4[e] = gQl[tn][e] * G;
                 dk4[e] = gKl[tn][e] * G + gKr[tn][e] * iG;
@@ -737,9 +831,14 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         }
         lds_barrier();
         if (act) {
-            float4 acc = *(const float4 *)(sDg + col);  // the last-row term, waves in order
+            // the last-row term: each wave's two parts, then the waves in order
+            auto slot = [&](int w) {
+                const float4 a = *(const float4 *)(sDg + w * DK + col), b = *(const float4 *)(sDg + (4 + w) * DK + col);
+                return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+            };
+            float4 acc = slot(0);
             for (int w = 1; w < 4; ++w) {
-                const float4 x = *(const float4 *)(sDg + w * DK + col);
+                const float4 x = slot(w);
                 acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
             }
             for (int p2 = part + 1; p2 < NP; ++p2) {
@@ -762,7 +861,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
             for (int col = q; col < DK; col += 4) s += sDl[row * DK + col];
             if (row == kC - 1)
                 for (int col = q; col < DK; col += 4)
-                    s += ((sDg[col] + sDg[DK + col]) + sDg[2 * DK + col]) + sDg[3 * DK + col];
+                    s += (((sDg[col] + sDg[4 * DK + col]) + (sDg[DK + col] + sDg[5 * DK + col])) +
+                          (sDg[2 * DK + col] + sDg[6 * DK + col])) + (sDg[3 * DK + col] + sDg[7 * DK + col]);
             s += dpp<kDppXor1>(s);
             s += dpp<kDppXor2>(s);
             if (q == 0) sGp[row] = s;
@@ -833,8 +933,8 @@ struct BwdDpSmem {
     static constexpr int oGam = oBeta + kC * 4;
     static constexpr int oGp = oGam + DK * 4;
     static constexpr int oDb = oGp + 8 * DK * 4;
-    static constexpr int oDg = oDb + kC * 4;      // fp32 [4][DK] last-row term of dg, per wave
-    static constexpr int oSpf = oDg + 4 * DK * 4;
+    static constexpr int oDg = oDb + kC * 4;      // fp32 [8][DK] last-row term of dg, as above
+    static constexpr int oSpf = oDg + 8 * DK * 4;
     static constexpr int bytes = oSpf + DK * 4;
     static_assert(kC * DK * 4 <= 2 * QK, "Gamma / dg fit over K->, A-> and over Q<-, B<-");
     static_assert(bytes <= 160 * 1024, "LDS");
@@ -995,7 +1095,6 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
         for (int e = 0; e < CPT; ++e) sGam[c0 + e] = exp2_fast(g[7][e] * kLog2e);
     if (tid < kC) sBeta[tid] = tid < m ? p.beta[(size_t)(tok0 + tid) * H + h] : 0.f;
     for (int i = tid; i < kC; i += kThreads) sDb[i] = 0.f;
-    for (int i = tid; i < 4 * DK; i += kThreads) sDg[i] = 0.f;
     for (int idx = tid; idx < kC * CS / 8; idx += kThreads) ((uint4 *)sE)[idx] = make_uint4(0u, 0u, 0u, 0u);
     lds_barrier();
 
@@ -1225,7 +1324,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
             float x = gpart[e];
 #pragma unroll
             for (int off = DK / 8; off < 64; off <<= 1) x += __shfl_xor(x, off);
-            if (lane < DK / 8) sDg[wave * DK + 8 * lane + e] += x;  // this wave's slot
+            if (lane < DK / 8) sDg[wave * DK + 8 * lane + e] = x;  // this wave's slot
         }
         dbp += __shfl_xor(dbp, 16);
         dbp += __shfl_xor(dbp, 32);
@@ -1340,12 +1439,12 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
             }
         }
 #pragma unroll
-        for (int tn = 0; tn < NT; ++tn)
+        for (int tn = 0; tn < NT; ++tn) {
+            float s4[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float sgm = group_sum<16>(dgp[tn][e]);
-                if (r16 == 0) sDg[wave * DK + 16 * tn + 4 * g4 + e] += sgm;
-            }
+            for (int e = 0; e < 4; ++e) s4[e] = group_sum<16>(dgp[tn][e]);
+            if (r16 == 0) *(float4 *)(sDg + (4 + wave) * DK + 16 * tn + 4 * g4) = make_float4(s4[0], s4[1], s4[2], s4[3]);
+        }
     }
     lds_barrier();  // the operand arrays are free: Gamma over K->, A->, dg over Q<-, B<-
 
@@ -1407,9 +1506,14 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
         }
         lds_barrier();
         if (act) {
-            float4 acc = *(const float4 *)(sDg + col);  // the last-row term, waves in order
+            // the last-row term: each wave's two parts, then the waves in order
+            auto slot = [&](int w) {
+                const float4 a = *(const float4 *)(sDg + w * DK + col), b = *(const float4 *)(sDg + (4 + w) * DK + col);
+                return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+            };
+            float4 acc = slot(0);
             for (int w = 1; w < 4; ++w) {
-                const float4 x = *(const float4 *)(sDg + w * DK + col);
+                const float4 x = slot(w);
                 acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
             }
             for (int p2 = part + 1; p2 < NP; ++p2) {
@@ -1430,7 +1534,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
             for (int col = q4; col < DK; col += 4) sacc += sDl[row * DK + col];
             if (row == kC - 1)
                 for (int col = q4; col < DK; col += 4)
-                    sacc += ((sDg[col] + sDg[DK + col]) + sDg[2 * DK + col]) + sDg[3 * DK + col];
+                    sacc += (((sDg[col] + sDg[4 * DK + col]) + (sDg[DK + col] + sDg[5 * DK + col])) +
+                             (sDg[2 * DK + col] + sDg[6 * DK + col])) + (sDg[3 * DK + col] + sDg[7 * DK + col]);
             sacc += dpp<kDppXor1>(sacc);
             sacc += dpp<kDppXor2>(sacc);
             if (q4 == 0) sGp[row] = sacc;
