@@ -63,22 +63,40 @@ struct BwdParams {
 // and the gate gradient (elementwise products of an operand and its gradient) is
 // unchanged.  A power of two keeps the bf16 S_p exact when scaled.
 //
-// g[i][e] holds the prefix of the thread's row-group (rows 8 rg + i); part[8 r2 * DK]
+// g[i][e] holds the prefix of the thread's row-group (rows 8 rg + i); part[r2 * DK + e]
 // (r2 < 8) holds each row-group's total for the same channel; row-group 0 writes 2^n to
-// *spf.
+// spf[e].  part and spf point at the thread's first channel (one vector read per
+// row-group; the sums run in row-group order).
 template <int CPT>
-__device__ __forceinline__ void g_shift(float (&g)[8][CPT], int e, const float *part, int rg,
-                                        float *spf) {
+__device__ __forceinline__ void g_shift_all(float (&g)[8][CPT], const float *part, int rg, float *spf) {
     constexpr int DKP = CPT * 32;
-    float carry = 0.f;
-    for (int r2 = 0; r2 < rg; ++r2) carry += part[r2 * DKP];
-    float total = carry;
-    for (int r2 = rg; r2 < 8; ++r2) total += part[r2 * DKP];
-    const float n = rintf(0.5f * total * kLog2e);
-    const float shift = carry - n * kLn2;
+    float acc[CPT], carry[CPT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) g[i][e] += shift;
-    if (rg == 0) *spf = exp2f(n);
+    for (int e = 0; e < CPT; ++e) acc[e] = carry[e] = 0.f;
+#pragma unroll
+    for (int r2 = 0; r2 < 8; ++r2) {
+        float v[CPT];
+        if constexpr (CPT == 4) {
+            const float4 x = *(const float4 *)(part + r2 * DKP);
+            v[0] = x.x; v[CPT > 1 ? 1 : 0] = x.y; v[CPT > 2 ? 2 : 0] = x.z; v[CPT > 3 ? 3 : 0] = x.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) v[e] = part[r2 * DKP + e];
+        }
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+            if (r2 == rg) carry[e] = acc[e];  // the sum of the row-groups before this one
+            acc[e] += v[e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+        const float n = rintf(0.5f * acc[e] * kLog2e);
+        const float shift = carry[e] - n * kLn2;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g[i][e] += shift;
+        if (rg == 0) spf[e] = exp2f(n);
+    }
 }
 
 // With the shift above, a chunk whose gate falls by more than twice this in some channel
@@ -151,6 +169,27 @@ __device__ __forceinline__ f32x4 mma_b(const bf16x8 (&fa)[KMAX / 32], const uint
     for (int st = 0; st < NS; ++st)
         if (k0 + 32 * st < k1) acc = mfma(fb[st], fa[st], acc);
     return acc;
+}
+
+// Two row blocks against one B tile over the same range: the B fragments read once.
+template <bool BT, int KMAX>
+__device__ __forceinline__ void mma_b2(const bf16x8 (&fa)[KMAX / 32], const bf16x8 (&fa2)[KMAX / 32],
+                                       const uint16_t *B, int ldb, int n0, int k0, int k1, f32x4 &acc,
+                                       f32x4 &acc2, int lane) {
+    constexpr int NS = KMAX / 32;
+    const int r = lane & 15, g = lane >> 4;
+    bf16x8 fb[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        const int k = k0 + 32 * st;
+        if (k < k1) fb[st] = BT ? frag(B, n0 + r, ldb, k + 8 * g) : frag_tr(B, k, ldb, n0, lane);
+    }
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+        if (k0 + 32 * st < k1) {
+            acc = mfma(fb[st], fa[st], acc);
+            acc2 = mfma(fb[st], fa2[st], acc2);
+        }
 }
 
 // Operand fragments of v_mfma_f32_16x16x16_bf16 (lane l: index l%16, contraction
@@ -346,8 +385,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
 #pragma unroll
         for (int e = 0; e < CPT; ++e) sGp[rg * DK + c0 + e] = run[e];
         lds_barrier();
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) g_shift(g, e, sGp + c0 + e, rg, sSpf + c0 + e);
+        g_shift_all(g, sGp + c0, rg, sSpf + c0);
         lds_barrier();  // sGp may be reused
     };
 
@@ -721,15 +759,19 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
         float dgp[NT][4];
         // one product at a time, its row block's A fragments read once for all NT tiles
         {
-            bf16x8 fat[2], fdx[2];  // At^T and dXm rows R0..
+            bf16x8 fat[2], fdx[2], fda[2];  // At^T, dXm and dA rows R0..
             load_a<true, kC>(fat, sA, CS, R0, lo_k, kC, lane);
             load_a<false, kC>(fdx, sdXm, CS, R0, 0, kC, lane);
+            load_a<false, kC>(fda, sdA, CS, R0, 0, kC, lane);
 #pragma unroll
             for (int tn = 0; tn < NT; ++tn) {
                 f32x4 a = mma_b<false, kC>(fat, sdW, KS, 16 * tn, lo_k, kC, z, lane);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) a[e] *= br;
-                gKl[tn] = mma_b<false, kC>(fdx, sKr, KS, 16 * tn, 0, kC, a, lane);
+                // dK<- = (Diag(beta) At^T dW) + dXm K->, dQ<- = dO S_p + dA K->: one K-> tile
+                gKl[tn] = a;
+                gQl[tn] = aQ[tn];
+                mma_b2<false, kC>(fdx, fda, sKr, KS, 16 * tn, 0, kC, gKl[tn], gQl[tn], lane);
             }
         }
         {
@@ -741,12 +783,6 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
                 const f32x4 b = mma_b<false, kC>(fda, sQl, KS, 16 * tn, lo_k, kC, aKg[tn], lane);
                 gKr[tn] = mma_b<false, kC>(fdx, sKl, KS, 16 * tn, lo_k, kC, b, lane);
             }
-        }
-        {
-            bf16x8 fda[2];  // dA rows R0..
-            load_a<false, kC>(fda, sdA, CS, R0, 0, kC, lane);
-#pragma unroll
-            for (int tn = 0; tn < NT; ++tn) gQl[tn] = mma_b<false, kC>(fda, sKr, KS, 16 * tn, 0, kC, aQ[tn], lane);
         }
 #pragma unroll
         for (int tn = 0; tn < NT; ++tn) {
@@ -1059,8 +1095,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
 #pragma unroll
         for (int e = 0; e < CPT; ++e) sGp[rg * DK + c0 + e] = run[e];
         lds_barrier();
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) g_shift(g, e, sGp + c0 + e, rg, sSpf + c0 + e);
+        g_shift_all(g, sGp + c0, rg, sSpf + c0);
     }
     flag_wide_gate(g, wave, lane, p.err);
     issue(0);
