@@ -564,10 +564,15 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_kernel(BwdParams p) 
                 const uint32_t w4[4] = {pf.d[i].x, pf.d[i].y, pf.d[i].z, pf.d[i].w};
                 const uint32_t s4[4] = {pf.s[i].x, pf.s[i].y, pf.s[i].z, pf.s[i].w};
                 uint32_t o4[4], p4[4];
+                // the eight columns' gamma_C and 2^n, two vector reads each
+                const float4 ga = *(const float4 *)(sGam + c8), gb = *(const float4 *)(sGam + c8 + 4);
+                const float4 fa = *(const float4 *)(sSpf + c8), fb = *(const float4 *)(sSpf + c8 + 4);
+                const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+                const float sf[8] = {fa.x, fa.y, fa.z, fa.w, fb.x, fb.y, fb.z, fb.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float d0 = bf16_lo(w4[e]) * sGam[c8 + 2 * e], d1 = bf16_hi(w4[e]) * sGam[c8 + 2 * e + 1];
-                    const float s0 = bf16_lo(s4[e]) * sSpf[c8 + 2 * e], s1 = bf16_hi(s4[e]) * sSpf[c8 + 2 * e + 1];
+                    const float d0 = bf16_lo(w4[e]) * gm[2 * e], d1 = bf16_hi(w4[e]) * gm[2 * e + 1];
+                    const float s0 = bf16_lo(s4[e]) * sf[2 * e], s1 = bf16_hi(s4[e]) * sf[2 * e + 1];
                     o4[e] = pack_bf16x2(d0, d1);
                     p4[e] = pack_bf16x2(s0, s1);
                     gpart[2 * e] += s0 * d0;
@@ -1246,10 +1251,15 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_post_dplr_kernel(BwdParam
                 const uint32_t w4[4] = {pf.d[i].x, pf.d[i].y, pf.d[i].z, pf.d[i].w};
                 const uint32_t s4[4] = {pf.s[i].x, pf.s[i].y, pf.s[i].z, pf.s[i].w};
                 uint32_t o4[4], p4[4];
+                // the eight columns' gamma_C and 2^n, two vector reads each
+                const float4 ga = *(const float4 *)(sGam + c8), gb = *(const float4 *)(sGam + c8 + 4);
+                const float4 fa = *(const float4 *)(sSpf + c8), fb = *(const float4 *)(sSpf + c8 + 4);
+                const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+                const float sf[8] = {fa.x, fa.y, fa.z, fa.w, fb.x, fb.y, fb.z, fb.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float d0 = bf16_lo(w4[e]) * sGam[c8 + 2 * e], d1 = bf16_hi(w4[e]) * sGam[c8 + 2 * e + 1];
-                    const float s0 = bf16_lo(s4[e]) * sSpf[c8 + 2 * e], s1 = bf16_hi(s4[e]) * sSpf[c8 + 2 * e + 1];
+                    const float d0 = bf16_lo(w4[e]) * gm[2 * e], d1 = bf16_hi(w4[e]) * gm[2 * e + 1];
+                    const float s0 = bf16_lo(s4[e]) * sf[2 * e], s1 = bf16_hi(s4[e]) * sf[2 * e + 1];
                     o4[e] = pack_bf16x2(d0, d1);
                     p4[e] = pack_bf16x2(s0, s1);
                     gpart[2 * e] += s0 * d0;
