@@ -11,8 +11,8 @@
 // Three passes produce the states the per-chunk gradients need:
 //   forward   the forward state kernel, saving S_p (the state entering each chunk)
 //   reverse   dS_p = dS_n Diag(gamma_C) + (K^ dS_n^T)^T W' + dO^T Q~ over the chunks in
-//             reverse order (the forward state kernel on a reordered block, which the
-//             forward state pass writes as it reads each forward block), saving
+//             reverse order (the forward state kernel on the forward blocks, with K^,
+//             W' and Q~ transposed in LDS as it reads them), saving
 //             dS_n (the gradient of the state leaving each chunk); K^ = K-> gamma_C,
 //             W' = -W and Q~ = Q<- - A_qk W come from the forward prep blocks
 //   post      one workgroup per (chunk, head), with dSg = dS_n Diag(gamma_C):
