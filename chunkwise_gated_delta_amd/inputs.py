@@ -196,6 +196,42 @@ def make_problem(kind: str, *, seed: Optional[int] = None, B=None, H=None, T=Non
         clip=bool(spec.get("clip", False)))
 
 
+def make_problem_on_device(kind: str, device, *, seed: Optional[int] = None, B=None, H=None,
+                           T=None) -> Problem:
+    """A workload's recipe drawn on ``device`` with a seeded torch generator, for sizes
+    whose host copy would be too large (tensors beyond 2^31 elements).
+
+    The bf16 forms without a, b and without packing only (kda, gdn): q, k ~ N(0, 1)
+    L2-normalised per token, v ~ N(0, 1), beta ~ U(0, 1), log alpha ~ U(la_range), drawn
+    in that order, one tensor at a time.  Same distributions as ``make_problem``, other
+    values (another generator).  The returned Problem holds device tensors.
+    """
+    spec = dict(WORKLOADS[kind])
+    assert not spec.get("varlen") and not spec.get("dplr") and spec["dtype"] == torch.bfloat16
+    spec.update({k: v for k, v in dict(B=B, H=H, T=T).items() if v is not None})
+    gen = torch.Generator(device=device)
+    gen.manual_seed(spec["seed"] if seed is None else seed)
+    shp = (spec["B"], spec["T"], spec["H"])
+    dt = spec["dtype"]
+
+    def unit_rows(d):
+        x = torch.randn(shp + (d,), generator=gen, device=device, dtype=torch.float32)
+        x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+        return x.to(dt)
+
+    q = unit_rows(spec["dk"])
+    k = unit_rows(spec["dk"])
+    v = torch.randn(shp + (spec["dv"],), generator=gen, device=device, dtype=torch.float32).to(dt)
+    beta = torch.rand(shp, generator=gen, device=device, dtype=torch.float32)
+    gate = spec["gate"]
+    gshape = shp if gate == GATE_HEAD else shp + (spec["dk"],)
+    lo, hi = spec["la_range"]
+    log_alpha = torch.rand(gshape, generator=gen, device=device, dtype=torch.float32)
+    log_alpha.mul_(hi - lo).add_(lo)
+    return Problem(name=kind, q=q, k=k, v=v, beta=beta, log_alpha=log_alpha, a=None, b=None,
+                   S0=None, cu_seqlens=None, gate=gate)
+
+
 def make_cotangents(P: Problem, seed: int, ds_scale: float = 0.1):
     """Seeded dO (P's dtype, shape of O) and dS_final (fp32, shape of S_final) for the
     backward pass: dO ~ N(0, 1), dS_final ~ ds_scale N(0, 1), drawn in that order."""
