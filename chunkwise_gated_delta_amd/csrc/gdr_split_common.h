@@ -12,17 +12,50 @@ namespace gdr {
 namespace {
 
 constexpr int kPlanThreads = 256;
+constexpr int kPlanBins = 4096;
+
+// Bin of a sequence's chunk count for the longest-first order: the count itself below
+// 2048; from 2048 on, its power of two and the six bits below the leading one (so the
+// bins are monotone in the count, and counts in one bin differ by less than 1/64).
+__device__ __forceinline__ int plan_bin(int c) {
+    if (c < 2048) return c;
+    const int e = 31 - __builtin_clz((unsigned)c);  // 11 .. 30
+    return 2048 + ((e - 11) << 6) + ((c >> (e - 6)) & 63);
+}
+
+// Exclusive prefix sum of x over the workgroup's kPlanThreads threads (buf: kPlanThreads
+// ints of LDS); *total receives the sum of all of them.
+__device__ __forceinline__ int plan_scan(int x, int *buf, int *total) {
+    const int tid = threadIdx.x;
+    buf[tid] = x;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+        const int y = tid >= off ? buf[tid - off] : 0;
+        __syncthreads();
+        buf[tid] += y;
+        __syncthreads();
+    }
+    const int incl = buf[tid];
+    *total = buf[kPlanThreads - 1];
+    __syncthreads();  // buf may be reused
+    return incl - x;
+}
 
 // Chunk offsets of packed sequences: coff[n] = sum over m < n of ceil(len_m / C);
 // and the sequences ordered longest first (ties by index), so that a state kernel,
 // whose work per sequence is serial, starts the longest ones first when there are
-// more workgroups than slots.  Malformed offsets are clamped here (and flagged)
-// exactly as the other kernels clamp them, so all of them agree on every
-// sequence's bounds.  P provides cu, T, total, err, coff, order, n_seq and C.
+// more workgroups than slots.  The order is a stable counting sort over plan_bin of
+// the chunk counts (exact below 2048 chunks): O(n_seq) work, one workgroup.  Malformed
+// offsets are clamped here (and flagged) exactly as the other kernels clamp them, so
+// all of them agree on every sequence's bounds.  P provides cu, T, total, err, coff,
+// order, n_seq and C.
 template <class P>
 __global__ __launch_bounds__(kPlanThreads) void chunk_plan_kernel(P p) {
-    __shared__ int part[kPlanThreads];
+    __shared__ int buf[kPlanThreads];
+    __shared__ int bins[kPlanBins];  // per bin: its count, then its next free rank
+    __shared__ int tkey[kPlanThreads];
     const int tid = threadIdx.x, N = p.n_seq, C = p.C;
+    // (1) chunk offsets: each thread sums a contiguous range of sequences
     const int per = (N + kPlanThreads - 1) / kPlanThreads;
     const int a = min(N, tid * per), b = min(N, a + per);
     int s = 0;
@@ -31,35 +64,52 @@ __global__ __launch_bounds__(kPlanThreads) void chunk_plan_kernel(P p) {
         seq_bounds(p.cu, n, p.T, p.total, t0, t1, p.err);
         s += (int)((t1 - t0 + C - 1) / C);
     }
-    part[tid] = s;
-    __syncthreads();
-    if (tid == 0) {
-        int acc = 0;
-        for (int i = 0; i < kPlanThreads; ++i) {
-            const int x = part[i];
-            part[i] = acc;
-            acc += x;
-        }
-        p.coff[N] = acc;
-    }
-    __syncthreads();
-    s = part[tid];
+    int all = 0;
+    s = plan_scan(s, buf, &all);
+    if (tid == 0) p.coff[N] = all;
     for (int n = a; n < b; ++n) {
         p.coff[n] = s;
         long t0, t1;
         seq_bounds(p.cu, n, p.T, p.total, t0, t1, nullptr);
         s += (int)((t1 - t0 + C - 1) / C);
     }
+    // (2) histogram of the bins
+    for (int i = tid; i < kPlanBins; i += kPlanThreads) bins[i] = 0;
+    __syncthreads();  // also orders the coff writes above before the reads below
+    for (int n = tid; n < N; n += kPlanThreads) atomicAdd(&bins[plan_bin(p.coff[n + 1] - p.coff[n])], 1);
     __syncthreads();
-    // rank of sequence n: how many sequences are longer, or as long with a lower index
-    for (int n = tid; n < N; n += kPlanThreads) {
-        const int cn = p.coff[n + 1] - p.coff[n];
-        int rank = 0;
-        for (int m2 = 0; m2 < N; ++m2) {
-            const int cm = p.coff[m2 + 1] - p.coff[m2];
-            rank += (cm > cn) || (cm == cn && m2 < n);
+    // (3) first rank of each bin = the number of sequences in higher bins: thread t owns
+    // bins [BPT t, BPT t + BPT), sums them from the top, and adds the totals of the
+    // threads above it
+    constexpr int BPT = kPlanBins / kPlanThreads;
+    int loc[BPT];
+    s = 0;
+#pragma unroll
+    for (int i = BPT - 1; i >= 0; --i) {
+        loc[i] = s;
+        s += bins[BPT * tid + i];
+    }
+    const int below = plan_scan(s, buf, &all);  // sequences in the bins below this thread's
+    const int above = all - below - s;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) bins[BPT * tid + i] = above + loc[i];
+    __syncthreads();
+    // (4) ranks, kPlanThreads sequences at a time in index order: a sequence goes after
+    // those of its bin in earlier tiles and in this tile before it
+    for (int base = 0; base < N; base += kPlanThreads) {
+        const int n = base + tid;
+        const int key = n < N ? plan_bin(p.coff[n + 1] - p.coff[n]) : -1;
+        tkey[tid] = key;
+        __syncthreads();
+        int same = 0;
+        for (int j = 0; j < tid; ++j) same += tkey[j] == key;
+        if (n < N) {
+            const int r = bins[key] + same;
+            if (r < N) p.order[r] = n;
         }
-        p.order[rank] = n;
+        __syncthreads();
+        if (n < N) atomicAdd(&bins[key], 1);
+        __syncthreads();
     }
 }
 

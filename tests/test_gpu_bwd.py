@@ -96,6 +96,32 @@ def test_bwd_varlen_with_empty_and_short_sequences():
     _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))
 
 
+def test_bwd_varlen_many_sequences():
+    # 700 packed sequences (three tiles of the plan kernel's ranking, empty ones among
+    # them) and one of 5000 tokens; sampled chains against the oracle
+    rng = np.random.default_rng(31)
+    lens = [int(x) for x in rng.integers(0, 150, 700)] + [5000]
+    rng.shuffle(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    P = inputs.make_problem("kda_varlen", n_seq=8, total=int(cu[-1]), min_len=1, H=2, dk=64, dv=64)
+    P.cu_seqlens = torch.from_numpy(cu)
+    P.S0 = None
+    dO, dSf = _cotangents(P, 735)
+    got = _gpu_bwd(P, dO, dSf)
+    for key in got:
+        assert np.isfinite(got[key]).all(), key
+    picks = sorted(set([int(np.argmax(lens))] + [int(n) for n in rng.choice(len(lens), 24, replace=False)]))
+    chains = [(n, h) for n in picks for h in range(P.H)]
+    ref = _oracle_bwd(P, dO, dSf, chains=chains)
+    sel = {}
+    for key in ("dq", "dk", "dv", "dbeta", "dlog_alpha"):
+        sel[key] = (np.concatenate([got[key][0, cu[n]:cu[n + 1], h].ravel() for n, h in chains]),
+                    np.concatenate([ref[key][0, cu[n]:cu[n + 1], h].ravel() for n, h in chains]))
+    sel["dS0"] = (np.concatenate([got["dS0"][n, h].ravel() for n, h in chains]),
+                  np.concatenate([ref["dS0"][n, h].ravel() for n, h in chains]))
+    _check(P, {k: v[0] for k, v in sel.items()}, {k: v[1] for k, v in sel.items()})
+
+
 # Chains compared at full size.  The state passes deal chain c = n H + h to XCD c % 8,
 # so KDA's first eight chains of each batch row cover every XCD slot (twice over);
 # DPLR (16 chains, segmented state passes) is compared on all of them.  The fp64

@@ -176,6 +176,28 @@ def test_varlen_with_empty_and_short_sequences():
     np.testing.assert_array_equal(Sf[1], P.S0[1].double().numpy())
 
 
+def test_varlen_many_sequences_and_very_long_ones():
+    # 3000 packed sequences (empty ones among them) and two longer than 2048 chunks: the
+    # plan's longest-first order spans many of its 256-sequence tiles and both kinds of
+    # length bins (exact counts; power of two and six bits).  Every output row must be
+    # written (NaN canary); sampled chains against the oracle.
+    rng = np.random.default_rng(21)
+    lens = [int(x) for x in rng.integers(0, 120, 3000)] + [140_000, 200_000]
+    rng.shuffle(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    P = inputs.make_problem("kda_varlen", n_seq=8, total=int(cu[-1]), min_len=1, H=2, dk=64, dv=64)
+    P.cu_seqlens = torch.from_numpy(cu)
+    P.S0 = None
+    out = torch.full((1, P.T, P.H, P.dv), float("nan"), dtype=P.dtype, device="cuda")
+    O, Sf = gpu_run(P, out=out)
+    assert np.isfinite(O).all() and np.isfinite(Sf).all()
+    longest = sorted(range(len(lens)), key=lambda n: -lens[n])[:2]
+    empty = [n for n in range(len(lens)) if lens[n] == 0][:1]
+    sample = [int(n) for n in rng.choice(len(lens), 40, replace=False)]
+    chains = [(n, h) for n in sorted(set(longest + empty + sample)) for h in range(P.H)]
+    _check(P, O, Sf, chains=chains)
+
+
 def test_state_passing_on_gpu():
     """Splitting a sequence and carrying S_final into S0 equals one call."""
     P = inputs.make_problem("kda", B=1, H=2, T=256)
