@@ -23,22 +23,29 @@ __device__ __forceinline__ int plan_bin(int c) {
     return 2048 + ((e - 11) << 6) + ((c >> (e - 6)) & 63);
 }
 
-// Exclusive prefix sum of x over the workgroup's kPlanThreads threads (buf: kPlanThreads
-// ints of LDS); *total receives the sum of all of them.
+// Exclusive prefix sum of x over the workgroup's kPlanThreads threads: a scan inside
+// each wave, then the wave totals through LDS (buf: one int per wave); *total receives
+// the sum of all of them.
 __device__ __forceinline__ int plan_scan(int x, int *buf, int *total) {
-    const int tid = threadIdx.x;
-    buf[tid] = x;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        const int y = tid >= off ? buf[tid - off] : 0;
-        __syncthreads();
-        buf[tid] += y;
-        __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int incl = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
     }
-    const int incl = buf[tid];
-    *total = buf[kPlanThreads - 1];
+    if (lane == 63) buf[w] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < kPlanThreads / 64; ++i) {
+        const int t = buf[i];
+        before += i < w ? t : 0;
+        all += t;
+    }
+    *total = all;
     __syncthreads();  // buf may be reused
-    return incl - x;
+    return before + incl - x;
 }
 
 // Chunk offsets of packed sequences: coff[n] = sum over m < n of ceil(len_m / C);
@@ -51,7 +58,7 @@ __device__ __forceinline__ int plan_scan(int x, int *buf, int *total) {
 // order, n_seq and C.
 template <class P>
 __global__ __launch_bounds__(kPlanThreads) void chunk_plan_kernel(P p) {
-    __shared__ int buf[kPlanThreads];
+    __shared__ int buf[kPlanThreads / 64];
     __shared__ int bins[kPlanBins];  // per bin: its count, then its next free rank
     __shared__ int tkey[kPlanThreads];
     const int tid = threadIdx.x, N = p.n_seq, C = p.C;
@@ -101,9 +108,9 @@ __global__ __launch_bounds__(kPlanThreads) void chunk_plan_kernel(P p) {
         const int key = n < N ? plan_bin(p.coff[n + 1] - p.coff[n]) : -1;
         tkey[tid] = key;
         __syncthreads();
-        int same = 0;
-        for (int j = 0; j < tid; ++j) same += tkey[j] == key;
         if (n < N) {
+            int same = 0;
+            for (int j = 0; j < tid; ++j) same += tkey[j] == key;
             const int r = bins[key] + same;
             if (r < N) p.order[r] = n;
         }

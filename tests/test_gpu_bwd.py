@@ -5,7 +5,7 @@ max|X - X_ref| / max|X_ref| <= 1e-2, the bar the bf16 forward is held to; the
 oracle runs on the exact bf16 input values and the same seeded dO, dS_final.
 Small cases compare every element over several chunks with a ragged tail; the
 full-size DPLR workload is compared on every chain, KDA on 16 chains that cover
-every XCD slot of the state passes.
+every XCD slot of the state passes, the packed workload on one chain of every sequence.
 """
 import sys
 
@@ -146,6 +146,26 @@ def test_bwd_full_size_chains(kind):
     for key in [k for k in ("dq", "dk", "dv", "da", "db", "dbeta", "dlog_alpha") if k in got]:
         sel[key] = (np.concatenate([got[key][n, :, h].ravel() for n, h in chains]),
                     np.concatenate([ref[key][n, :, h].ravel() for n, h in chains]))
+    sel["dS0"] = (np.concatenate([got["dS0"][n, h].ravel() for n, h in chains]),
+                  np.concatenate([ref["dS0"][n, h].ravel() for n, h in chains]))
+    _check(P, {k: v[0] for k, v in sel.items()}, {k: v[1] for k, v in sel.items()})
+
+
+def test_bwd_full_size_varlen_every_sequence():
+    # the packed workload at full size (8 sequences, 32768 tokens, 32 heads, per-sequence
+    # S0): one chain of every sequence, each on another head and so another XCD slot
+    P = inputs.make_problem("kda_varlen")
+    dO, dSf = _cotangents(P, 745, ds_scale=0.1)
+    got = _gpu_bwd(P, dO, dSf)
+    for key in got:
+        assert np.isfinite(got[key]).all(), key
+    cu = P.cu_seqlens.numpy()
+    chains = [(n, (5 * n + 3) % P.H) for n in range(P.n_seq)]
+    ref = _oracle_bwd(P, dO, dSf, chains=chains)
+    sel = {}
+    for key in ("dq", "dk", "dv", "dbeta", "dlog_alpha"):
+        sel[key] = (np.concatenate([got[key][0, cu[n]:cu[n + 1], h].ravel() for n, h in chains]),
+                    np.concatenate([ref[key][0, cu[n]:cu[n + 1], h].ravel() for n, h in chains]))
     sel["dS0"] = (np.concatenate([got["dS0"][n, h].ravel() for n, h in chains]),
                   np.concatenate([ref["dS0"][n, h].ravel() for n, h in chains]))
     _check(P, {k: v[0] for k, v in sel.items()}, {k: v[1] for k, v in sel.items()})
