@@ -216,6 +216,42 @@ def test_state_passing_on_gpu():
     assert np.max(np.abs(S2 - Sf)) <= 1e-2 * np.max(np.abs(Sf))
 
 
+def test_concurrent_calls_on_two_streams():
+    # two calls in flight at once on two streams (default priority), each with the default
+    # workspace of its own stream, and a backward beside a forward: the same bits as the
+    # calls made one after the other
+    dev = "cuda"
+    to = lambda t: None if t is None else t.to(dev)
+    P1 = inputs.make_problem("kda", B=2, H=4, T=1000)
+    P2 = inputs.make_problem("gdn", B=3, H=4, T=700)
+    a1 = [to(getattr(P1, n)) for n in ("q", "k", "v", "beta", "log_alpha")]
+    a2 = [to(getattr(P2, n)) for n in ("q", "k", "v", "beta", "log_alpha")]
+    dO, dSf = inputs.make_cotangents(P1, seed=55)
+    dO, dSf = to(dO), to(dSf)
+    fwd = lambda a: gdr.chunk_fwd(*a[:4], log_alpha=a[4])
+    bwd = lambda a: gdr.chunk_bwd(*a[:4], dO, log_alpha=a[4], dS_final=dSf)
+    O1, S1 = fwd(a1)
+    O2, S2 = fwd(a2)
+    G1 = bwd(a1)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            O1b, S1b = fwd(a1)
+            G1b = bwd(a1)
+        with torch.cuda.stream(s2):
+            O2b, S2b = fwd(a2)
+        torch.cuda.synchronize()
+        assert torch.equal(O1, O1b) and torch.equal(S1, S1b)
+        assert torch.equal(O2, O2b) and torch.equal(S2, S2b)
+        for key in G1:
+            assert torch.equal(G1[key], G1b[key]), key
+    for st in (s1, s2):
+        with torch.cuda.stream(st):
+            assert gdr.check_workspace_error() == 0
+
+
 def test_deterministic():
     P = inputs.make_problem("kda", B=1, H=4, T=300)
     O1, S1 = gpu_run(P)
