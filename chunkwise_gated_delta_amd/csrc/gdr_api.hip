@@ -44,12 +44,11 @@ bool aligned16(std::initializer_list<const void *> ptrs) {
 }
 
 bool shape_ok(int B, int H, int T, int dk, int dv, int n_seq, bool varlen) {
-    if (B < 1 || H < 1 || T < 1) return false;
+    if (B < 1 || H < 1 || T < 1 || dk < 1 || dv < 1) return false;
     if (varlen && (B != 1 || n_seq < 1)) return false;
-    const long long tokens = (long long)B * T;
-    if (tokens * H * (long long)(dk > dv ? dk : dv) >= (1LL << 40)) return false;
-    if (dk < 1 || dv < 1) return false;
-    return true;
+    // elements per tensor below 2^40 (the product of four ints needs more than 64 bits)
+    const __int128 elems = (__int128)B * T * H * (dk > dv ? dk : dv);
+    return elems < ((__int128)1 << 40);
 }
 
 int supported(int dtype, int dk, int dv, int C, bool has_ab) {

@@ -141,6 +141,18 @@ def test_bad_shapes_rejected(lib):
     assert _call(lib, cu=FAKE + (8 << 30), n_seq=0) == -2
 
 
+def test_size_bound(lib):
+    # tokens x H x max(dk, dv) must stay below 2^40 elements per tensor (every global
+    # offset is 64-bit; job and chain indices stay 32-bit inside that bound)
+    ws = gdr.workspace_bytes
+    assert ws(1, 1 << 10, (1 << 23) - 64, 128, 128) > 0
+    assert ws(1, 1 << 10, 1 << 23, 128, 128) == 0
+    assert ws(1 << 10, 1 << 10, 1 << 13, 64, 128) == 0      # the larger head size counts
+    assert ws(1 << 20, 1 << 20, 1 << 20, 64, 64) == 0       # no 32-bit wrap in the check
+    assert _call(lib, B=1, H=1 << 10, T=1 << 23) == -2
+    assert gdr.bwd_workspace_bytes(1, 1 << 10, 1 << 23, 128, 128) == 0
+
+
 def test_unsupported_rejected(lib):
     assert _call(lib, dk=96) == -3
     assert _call(lib, dv=40) == -3
