@@ -48,7 +48,10 @@ bool shape_ok(int B, int H, int T, int dk, int dv, int n_seq, bool varlen) {
     if (varlen && (B != 1 || n_seq < 1)) return false;
     // elements per tensor below 2^40 (the product of four ints needs more than 64 bits)
     const __int128 elems = (__int128)B * T * H * (dk > dv ? dk : dv);
-    return elems < ((__int128)1 << 40);
+    if (elems >= ((__int128)1 << 40)) return false;
+    // (sequence, head) chains below 2^27: the serial kernels number their workgroups
+    // (chains x tiles x runs) in 32 bits
+    return (long long)(varlen ? n_seq : B) * H < (1LL << 27);
 }
 
 int supported(int dtype, int dk, int dv, int C, bool has_ab) {

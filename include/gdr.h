@@ -115,6 +115,8 @@ size_t gdr_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int C, int n
  *               section 5.3, secondary chunking; no log-domain rescue: a half whose
  *               gate falls by more than 2^96 in a channel raises error bit 2).
  *   dk, dv      head sizes; dk in {64, 128}; dv a multiple of 32 up to 256.
+ *   Sizes: B, H, T >= 1, B * T * H * max(dk, dv) < 2^40 (elements of the largest
+ *   tensor) and N * H < 2^27 ((sequence, head) pairs); otherwise GDR_ERR_SHAPE.
  *
  * S_final may equal S0 (in-place state update).  O must not overlap any input.
  * cu_seqlens lives in device memory and is not read on the host: malformed

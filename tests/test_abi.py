@@ -151,6 +151,12 @@ def test_size_bound(lib):
     assert ws(1 << 20, 1 << 20, 1 << 20, 64, 64) == 0       # no 32-bit wrap in the check
     assert _call(lib, B=1, H=1 << 10, T=1 << 23) == -2
     assert gdr.bwd_workspace_bytes(1, 1 << 10, 1 << 23, 128, 128) == 0
+    # and fewer than 2^27 (sequence, head) chains (the serial kernels count workgroups in
+    # 32 bits)
+    assert ws((1 << 17) - 1, 1 << 10, 1, 64, 64) > 0
+    assert ws(1 << 17, 1 << 10, 1, 64, 64) == 0
+    assert ws(1, 1 << 10, 1 << 20, 64, 64, n_seq=1 << 17) == 0
+    assert ws(1, 1 << 10, 1 << 20, 64, 64, n_seq=(1 << 17) - 1) > 0
 
 
 def test_unsupported_rejected(lib):
