@@ -1380,7 +1380,10 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("" ::: "memory");
 }
 
-// Chunks whose operands are in flight ahead of the one being computed.
+// Chunks whose operands are in flight ahead of the one being computed: two, in three
+// rotating register sets (one workgroup per CU); or one, in two sets, which fits 256
+// registers so that two workgroups share a CU and one's first loads and last stores
+// overlap the other's steps (for passes with more workgroups than CUs).
 constexpr int kDepth = 2;
 
 // Modes of the state kernel.  Forward: the forward pass.  SaveStates: the forward
@@ -1393,8 +1396,8 @@ constexpr int kDepth = 2;
 // kForwardSave: the forward pass that also stores the states (both of the first two)
 constexpr int kForward = 0, kSaveStates = 1, kReverse = 2, kForwardSave = 3;
 
-template <int DK, bool DP, int MODE = kForward>
-__global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
+template <int DK, bool DP, int MODE = kForward, int DEPTH = kDepth>
+__global__ __launch_bounds__(kThreads, DEPTH == 1 ? 2 : 1) void kda_state_kernel(SplitParams p) {
     using L = StateSmem<DK>;
     using Bk = Blk<DK, DP>;
     constexpr int KS = L::KS;
@@ -1559,7 +1562,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     };
 
     auto step = [&](int c, Pre<DK> &x, Pre<DK> &nx) {
-        wait_vmcnt<(kDepth - 1) * kMinLoadsPerChunk<DK, kLoadKb>>();  // operands of chunk c have arrived
+        wait_vmcnt<(DEPTH - 1) * kMinLoadsPerChunk<DK, kLoadKb>>();  // operands of chunk c have arrived
         float *sG = (float *)(smem + L::oG) + (c & 1) * DK;
         if (wave == 0 && lane < DK / 4) ((float4 *)sG)[lane] = x.G;
         {
@@ -1568,7 +1571,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
             *(uint4 *)(sV + vr * kVS + vc) = make_uint4(x.V.x & keep, x.V.y & keep, x.V.z & keep, x.V.w & keep);
         }
         if (kOut && !vw && c > 0) store_out(c - 1);
-        const int cn = c + kDepth < nck ? c + kDepth : nck - 1;
+        const int cn = c + DEPTH < nck ? c + DEPTH : nck - 1;
         load_p(nx, cn);
         // reverse pass: this chunk's K^ tiles (as K^T) and W', Q~ rows, row-major in LDS
         uint16_t *sRt = kRev ? (uint16_t *)(smem + L::oRt) : nullptr;
@@ -1681,26 +1684,34 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(SplitParams p) {
     };
 
     if (nck > 0) {
-        Pre<DK> buf[kDepth + 1];
+        Pre<DK> buf[DEPTH + 1];
 #pragma unroll
-        for (int u = 0; u < kDepth; ++u) {
+        for (int u = 0; u < DEPTH; ++u) {
             load_p(buf[u], u < nck ? u : nck - 1);
             load_rest(buf[u], u < nck ? u : nck - 1);
             asm volatile("" ::: "memory");  // keep the chunks' loads in chunk order
         }
-        static_assert(kDepth == 2, "the unrolled loop below rotates three operand sets");
-        // Whole triples of steps, then the tail: every path through this code runs the
-        // steps in order with nothing skipped, so the compiler's count of memory
-        // operations in flight stays exact and the waits above are the only ones.
+        // Whole rounds of steps (one per operand set), then the tail: every path through
+        // this code runs the steps in order with nothing skipped, so the compiler's count
+        // of memory operations in flight stays exact and the waits above are the only ones.
         int c = 0;
-        for (; c + 3 <= nck; c += 3) {
-            step(c, buf[0], buf[2]);
-            step(c + 1, buf[1], buf[0]);
-            step(c + 2, buf[2], buf[1]);
-        }
-        if (c < nck) {
-            step(c, buf[0], buf[2]);
-            if (c + 1 < nck) step(c + 1, buf[1], buf[0]);
+        if constexpr (DEPTH == 2) {
+            for (; c + 3 <= nck; c += 3) {
+                step(c, buf[0], buf[2]);
+                step(c + 1, buf[1], buf[0]);
+                step(c + 2, buf[2], buf[1]);
+            }
+            if (c < nck) {
+                step(c, buf[0], buf[2]);
+                if (c + 1 < nck) step(c + 1, buf[1], buf[0]);
+            }
+        } else {
+            static_assert(DEPTH == 1, "one or two chunks ahead");
+            for (; c + 2 <= nck; c += 2) {
+                step(c, buf[0], buf[1]);
+                step(c + 1, buf[1], buf[0]);
+            }
+            if (c < nck) step(c, buf[0], buf[1]);
         }
         if (kOut && !vw) store_out(nck - 1);
     }
@@ -2017,6 +2028,13 @@ void run_state(SplitParams sp, int runs, hipStream_t s) {
     if (runs < 3) {
         sp.seg_n = sp.seg_phase = 0;
         const dim3 grid((unsigned)(((chains + 7) / 8) * 8 * sp.n_tiles));
+        // (the state-keeping forward spills in the smaller register budget at dk = 128)
+        if constexpr (!DP && (MODE == kForward || MODE == kSaveStates)) {
+            if (chains * sp.n_tiles > compute_units()) {  // more than one round of workgroups
+                hipLaunchKernelGGL((kda_state_kernel<DK, DP, MODE, 1>), grid, dim3(kThreads), 0, s, sp);
+                return;
+            }
+        }
         hipLaunchKernelGGL((kda_state_kernel<DK, DP, MODE>), grid, dim3(kThreads), 0, s, sp);
         return;
     }

@@ -82,6 +82,15 @@ def test_bwd_ragged_lengths(T):
     _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))
 
 
+@pytest.mark.parametrize("T", [64, 130])
+def test_bwd_serial_pass_two_workgroups_per_cu(T):
+    # more workgroups than CUs in the forward state pass of the backward (one chunk ahead,
+    # two workgroups per CU)
+    P = inputs.make_problem("kda", B=1, H=80, T=T, s0_scale=0.3)
+    dO, dSf = _cotangents(P, 715 + T)
+    _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))
+
+
 def test_bwd_no_final_state_gradient():
     P = inputs.make_problem("kda", B=1, H=3, T=150)
     dO, _ = _cotangents(P, 720)

@@ -216,6 +216,25 @@ def test_state_passing_on_gpu():
     assert np.max(np.abs(S2 - Sf)) <= 1e-2 * np.max(np.abs(Sf))
 
 
+@pytest.mark.parametrize("T", [64, 130, 200])
+@pytest.mark.parametrize("kind,dk,dv", [("kda", 128, 128), ("gdn", 128, 64), ("kda", 64, 64)])
+def test_serial_pass_two_workgroups_per_cu(kind, dk, dv, T):
+    # more (sequence, head, dv tile) workgroups than CUs: the serial pass loads one chunk
+    # ahead and fits two workgroups per CU; one, odd and even chunk counts
+    H = 330 * 32 // dv  # at least 330 workgroups
+    P = inputs.make_problem(kind, B=1, H=H, T=T, dk=dk, dv=dv, s0_scale=0.3)
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+
+
+def test_serial_pass_two_workgroups_per_cu_varlen():
+    P = inputs.make_problem("kda_varlen", n_seq=5, total=900, min_len=1, H=70)
+    P.cu_seqlens = torch.tensor([0, 1, 65, 65, 400, 900], dtype=torch.int32)
+    P.S0 = P.S0[:5]
+    O, Sf = gpu_run(P)
+    _check(P, O, Sf)
+
+
 def test_concurrent_calls_on_two_streams():
     # two calls in flight at once on two streams (default priority), each with the default
     # workspace of its own stream, and a backward beside a forward: the same bits as the
