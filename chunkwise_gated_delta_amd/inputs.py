@@ -197,18 +197,19 @@ def make_problem(kind: str, *, seed: Optional[int] = None, B=None, H=None, T=Non
 
 
 def make_problem_on_device(kind: str, device, *, seed: Optional[int] = None, B=None, H=None,
-                           T=None) -> Problem:
+                           T=None, dk=None, dv=None, dtype=None) -> Problem:
     """A workload's recipe drawn on ``device`` with a seeded torch generator, for sizes
     whose host copy would be too large (tensors beyond 2^31 elements).
 
-    The bf16 forms without a, b and without packing only (kda, gdn): q, k ~ N(0, 1)
+    The forms without a, b and without packing only (kda, gdn): q, k ~ N(0, 1)
     L2-normalised per token, v ~ N(0, 1), beta ~ U(0, 1), log alpha ~ U(la_range), drawn
     in that order, one tensor at a time.  Same distributions as ``make_problem``, other
     values (another generator).  The returned Problem holds device tensors.
     """
     spec = dict(WORKLOADS[kind])
-    assert not spec.get("varlen") and not spec.get("dplr") and spec["dtype"] == torch.bfloat16
-    spec.update({k: v for k, v in dict(B=B, H=H, T=T).items() if v is not None})
+    assert not spec.get("varlen") and not spec.get("dplr") and "la_range" in spec
+    spec.update({k: v for k, v in dict(B=B, H=H, T=T, dk=dk, dv=dv, dtype=dtype).items()
+                 if v is not None})
     gen = torch.Generator(device=device)
     gen.manual_seed(spec["seed"] if seed is None else seed)
     shp = (spec["B"], spec["T"], spec["H"])

@@ -1,11 +1,13 @@
 """Parity beyond 2^31 elements per tensor (every global offset of the HIP path is 64-bit).
 
-KDA form, B = 1, H = 1024, T = 16448 (257 chunks, the last one ragged), dk = dv = 128:
-q, k, v, log alpha, O and every input gradient hold 2,155,872,256 elements (> 2^31), the
-forward blocks 16.3 GB and each per-chunk state buffer 8.6 GB of the workspace.  The
-inputs are drawn on the device; the oracle recomputes the first, a middle and the last
-head (the largest offsets) from the same values, to the bf16 bar 1e-2.  Every element
-of O and of the gradients is checked to have been written (NaN canaries).
+KDA form in bf16, B = 1, H = 1024, T = 16448 (257 chunks, the last one ragged), dk = dv =
+128: q, k, v, log alpha, O and every input gradient hold 2,155,872,256 elements (> 2^31),
+the forward blocks 16.3 GB and each per-chunk state buffer 8.6 GB of the workspace.  The
+fp32 kernels the same way: GDN form, H = 1024, T = 32832 (513 chunks), dk = dv = 64, 2^31
++ 2^23 elements per tensor.  The inputs are drawn on the device; the oracle recomputes the
+first, a middle and the last head (the largest offsets) from the same values, to the bar
+of the input precision (1e-2 bf16, 1e-4 fp32).  Every element of O and of the gradients
+is checked to have been written (NaN canaries).
 """
 import sys
 
@@ -89,4 +91,28 @@ def test_backward_beyond_2_31_elements(big):
               file=sys.__stderr__, flush=True)
         assert max(errs.values()) <= TOL, errs
     del g, dO, dSf
+    torch.cuda.empty_cache()
+
+
+def test_fp32_forward_beyond_2_31_elements():
+    T32 = 32832
+    P = inputs.make_problem_on_device("gdn", "cuda", B=1, H=H, T=T32, dk=64, dv=64,
+                                      dtype=torch.float32, seed=13)
+    assert P.q.numel() > 2**31
+    ws = torch.zeros(gdr.workspace_bytes(1, H, T32, 64, 64, dtype=torch.float32, gate=gdr.GATE_HEAD),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.full((1, T32, H, 64), float("nan"), dtype=torch.float32, device="cuda")
+    O, Sf = gdr.chunk_fwd(P.q, P.k, P.v, P.beta, log_alpha=P.log_alpha, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert gdr.check_workspace_error(ws) == 0
+    assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(Sf).all())
+    del ws
+    for h in HEADS:
+        Oref, Sref = oracle.recurrence(_head(P.q, h), _head(P.k, h), _head(P.v, h), _head(P.beta, h),
+                                       log_alpha=_head(P.log_alpha, h))
+        eo = rel_err(_head(O, h), Oref)
+        es = rel_err(Sf[:, h:h + 1].to(torch.float64).cpu().numpy(), Sref)
+        print(f"[gpu-case] fp32 head {h}: rel err O {eo:.3e} S_final {es:.3e}", file=sys.__stderr__, flush=True)
+        assert eo <= 1e-4 and es <= 1e-4
+    del O, Sf, out, P
     torch.cuda.empty_cache()
