@@ -1353,7 +1353,7 @@ struct StateSmem {
     static constexpr int bytes_rev = oRq + 2 * kC * KS * 2;
 };
 
-// Operands of one chunk for one wave, loaded two chunks ahead.
+// Operands of one chunk for one wave, loaded one or two chunks ahead (DEPTH).
 template <int DK>
 struct Pre {
     uint4 P[DK / 16];  // W' (waves 0, 1) or Q~ (waves 2, 3): this wave's 32 rows
@@ -2077,9 +2077,10 @@ FwdArgs fwd_view(const BwdArgs &b) {
 }
 
 // Backward workspace: [header][packed-sequence plan][forward blocks][log-domain job
-// flags (gated forms)][backward blocks][S_p states][dS_n states], the states bf16
+// flags (gated forms)][S_p states][dS_n states][segmented-pass area], the states bf16
 // [chunk][head][dv][dk].  Everything up to the flags sits where the forward workspace
-// has it, so that a forward call's workspace can stand in for the first kernel.
+// has it, so that a forward call's workspace can stand in for the first kernel; the
+// reverse pass reads the forward blocks too.
 struct BwdLayout {
     SplitLayout fw;
     size_t sub_off, s_off, ds_off, seg_off, total;
@@ -2274,8 +2275,8 @@ int launch_kda_bwd(const BwdArgs &b, int n_seq_eff, hipStream_t s) {
     sp.seg_ws = (float *)(ws + lay.seg_off);
     sp.sub = lay.sub ? (int *)(ws + lay.sub_off) : nullptr;
     const int runs = lay.runs ? seg_runs(n_seq_eff * b.H, b.dk, b.dv, chunks_per_chain(fwd_view(b)), true) : 0;
-    // the reverse pass: backward blocks, dO as the value tile, dS_final in, dS0 out
-    SplitParams rp = sp;  // on the forward blocks
+    // the reverse pass: the forward blocks, dO as the value tile, dS_final in, dS0 out
+    SplitParams rp = sp;
     rp.fblk = blk_bytes(b.dk, b.a != nullptr);
     rp.v = (const bf16 *)b.dO;
     rp.S0 = b.dS_final;
