@@ -91,6 +91,22 @@ def test_bwd_serial_pass_two_workgroups_per_cu(T):
     _check(P, _gpu_bwd(P, dO, dSf), _oracle_bwd(P, dO, dSf))
 
 
+def test_bwd_chain_gradients_independent_of_the_other_chains():
+    # the forward state pass of the backward in its one-chunk-ahead form (80 heads) and in
+    # its two-chunks-ahead form (the first four heads alone): the same bits
+    P = inputs.make_problem("kda", B=1, H=80, T=130, s0_scale=0.3)
+    dO, dSf = _cotangents(P, 717)
+    g = _gpu_bwd(P, dO, dSf)
+    P4 = inputs.make_problem("kda", B=1, H=80, T=130, s0_scale=0.3)
+    for name in ("q", "k", "v", "beta", "log_alpha"):
+        setattr(P4, name, getattr(P, name)[:, :, :4].contiguous())
+    P4.S0 = P.S0[:, :4].contiguous()
+    g4 = _gpu_bwd(P4, dO[:, :, :4].contiguous(), dSf[:, :4].contiguous())
+    for key in g4:
+        ref = g[key][:, :4] if key == "dS0" else g[key][:, :, :4]
+        np.testing.assert_array_equal(ref, g4[key], err_msg=key)
+
+
 def test_bwd_no_final_state_gradient():
     P = inputs.make_problem("kda", B=1, H=3, T=150)
     dO, _ = _cotangents(P, 720)

@@ -227,6 +227,21 @@ def test_serial_pass_two_workgroups_per_cu(kind, dk, dv, T):
     _check(P, O, Sf)
 
 
+def test_chain_result_independent_of_the_other_chains():
+    # 82 heads (328 workgroups: the one-chunk-ahead serial pass, two workgroups per CU)
+    # against the first four heads alone (16 workgroups: the two-chunks-ahead form): the
+    # same arithmetic in the same order, so the four chains agree bit for bit
+    P = inputs.make_problem("kda", B=1, H=82, T=200, s0_scale=0.3)
+    O, Sf = gpu_run(P)
+    P4 = inputs.make_problem("kda", B=1, H=82, T=200, s0_scale=0.3)
+    for name in ("q", "k", "v", "beta", "log_alpha"):
+        setattr(P4, name, getattr(P, name)[:, :, :4].contiguous())
+    P4.S0 = P.S0[:, :4].contiguous()
+    O4, Sf4 = gpu_run(P4)
+    np.testing.assert_array_equal(O[:, :, :4], O4)
+    np.testing.assert_array_equal(Sf[:, :4], Sf4)
+
+
 def test_serial_pass_two_workgroups_per_cu_varlen():
     P = inputs.make_problem("kda_varlen", n_seq=5, total=900, min_len=1, H=70)
     P.cu_seqlens = torch.tensor([0, 1, 65, 65, 400, 900], dtype=torch.int32)
