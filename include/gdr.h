@@ -1,6 +1,7 @@
 /*
  * gdr.h -- C ABI of libgdr.so: the chunkwise-parallel forward pass of the
- * gated delta-rule family of linear attention on AMD MI355X (gfx950).
+ * gated delta-rule family of linear attention on AMD MI355X (gfx950), and the
+ * backward pass of its KDA and gated DPLR forms.
  *
  * The operation (per sequence n and head h; "Diagonal Plus Low Rank" notes,
  * section 2, the original gated DPLR formula, with the write term scaled by
@@ -30,8 +31,9 @@
  * and keeps no pointer after a call returns.  All work is enqueued on
  * `stream` (a hipStream_t; NULL is the default stream) and the call returns
  * without synchronising: buffers must stay valid until that work completes.
- * The library keeps no state; concurrent calls on different streams with
- * disjoint outputs and workspaces are safe.
+ * Apart from the per-GPU scratch array of gdr_chunk_fwd_noalloc (see there), the
+ * library keeps no state; concurrent calls on different streams with disjoint
+ * outputs and workspaces are safe.
  */
 #ifndef GDR_H
 #define GDR_H
