@@ -198,6 +198,41 @@ def test_varlen_many_sequences_and_very_long_ones():
     _check(P, O, Sf, chains=chains)
 
 
+def _plan_bin(c):
+    # the plan's length bins: the chunk count below 2048, then its power of two and the
+    # six bits below the leading one
+    if c < 2048:
+        return c
+    e = c.bit_length() - 1
+    return 2048 + ((e - 11) << 6) + ((c >> (e - 6)) & 63)
+
+
+def test_packed_sequence_plan_exact():
+    # the plan kernel's integer outputs, read back from the workspace: chunk offsets
+    # coff[n] = sum over m < n of ceil(len_m / 64) (and the total at coff[N]), and the
+    # order longest first by length bin, ties by index -- exact counts below 2048 chunks,
+    # three sequences beyond them, empty ones, several of the kernel's 256-sequence tiles
+    rng = np.random.default_rng(41)
+    lens = [int(x) for x in rng.integers(0, 400, 700)] + [0, 0, 140_000, 180_000, 200_000, 64, 65]
+    rng.shuffle(lens)
+    N = len(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    P = inputs.make_problem("kda_varlen", n_seq=8, total=int(cu[-1]), min_len=1, H=1, dk=64, dv=64)
+    P.cu_seqlens = torch.from_numpy(cu)
+    P.S0 = None
+    ws = torch.zeros(gdr.workspace_bytes(1, 1, P.T, 64, 64, n_seq=N), dtype=torch.uint8, device="cuda")
+    gpu_run(P, workspace=ws)
+    words = ws[256:256 + 4 * (2 * N + 1)].cpu().view(torch.int32).numpy()
+    coff, order = words[:N + 1], words[N + 1:]
+    counts = [(x + 63) // 64 for x in lens]
+    np.testing.assert_array_equal(coff, np.concatenate([[0], np.cumsum(counts)]))
+    expect = sorted(range(N), key=lambda n: (-_plan_bin(counts[n]), n))
+    np.testing.assert_array_equal(order, expect)
+    # exact longest-first wherever the counts are below 2048
+    short = [n for n in order if counts[n] < 2048]
+    assert short == sorted(short, key=lambda n: (-counts[n], n))
+
+
 def test_state_passing_on_gpu():
     """Splitting a sequence and carrying S_final into S0 equals one call."""
     P = inputs.make_problem("kda", B=1, H=2, T=256)
