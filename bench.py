@@ -33,11 +33,13 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 WORKLOAD = "kda"
-# The headline kernels' source: the kernel file and the device headers it includes.
+# The headline kernels' source: the kernel file, the device headers it includes and the
+# build script (its compiler flags shape the code as much as the source does).
 KERNEL_SOURCES = ["chunkwise_gated_delta_amd/csrc/gdr_kda_split.hip",
                   "chunkwise_gated_delta_amd/csrc/gdr_mfma.h",
                   "chunkwise_gated_delta_amd/csrc/gdr_split_common.h",
-                  "chunkwise_gated_delta_amd/csrc/gdr_common.h"]
+                  "chunkwise_gated_delta_amd/csrc/gdr_common.h",
+                  "chunkwise_gated_delta_amd/build.py"]
 COUNTERS_FILE = "profiles/kda_split__kda_B2_H32_T8192_d128__counters.md"
 
 

@@ -12,8 +12,12 @@ LIB = os.path.join(HERE, "libgdr.so")
 SOURCES = ["gdr_api.hip", "gdr_f32_split.hip", "gdr_kda_split.hip"]
 
 # Packed fp32 ops stay off: the compiler must not form v_pk_* fp32 instructions.
+# MFMA accumulators are placed in ordinary vector registers where they fit
+# (-amdgpu-mfma-vgpr-form): the kernels scale, convert and store them with vector
+# instructions, which otherwise copy them out of the accumulator registers first.
 HIPCC_FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-std=c++17",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form",
                "-Wall", "-Wno-unused-function"]
 NOISE = "'-packed-fp32-ops' is not a recognized feature"
 
