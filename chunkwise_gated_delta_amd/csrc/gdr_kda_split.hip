@@ -168,8 +168,10 @@ struct PrepSmem {
     static_assert(bytes <= 160 * 1024, "one workgroup per CU");
 };
 
-// A chunk whose gate falls by more than this (log2 units, any channel) is redone by the
-// SUB variant: the scaled operands K e^-g would leave the bf16/fp32 exponent range.
+// Gate ranges of the scaled operands (log2 units, any channel).  Up to kSubGateRange the
+// operands K e^-g stay in the bf16/fp32 exponent range; up to twice that the prep refers
+// the gate of a channel to the middle of the chunk (sh below); a chunk whose gate falls
+// further is redone by the SUB variant.
 constexpr float kSubGateRange = 96.f;
 // In the SUB variant a diagonal 16x16 tile whose gate falls by at most this much goes on
 // MFMA with columns y_c 2^(g_s - g_c) (at most 2^64); a wider one is formed element-wise.
@@ -568,14 +570,31 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
                 if (__builtin_amdgcn_ballot_w64(wide) != 0 && lane == 0) atomicOr(p.err, 2);
             }
         } else if constexpr (!SUB) {
-            // wave 0 holds gamma_C of every channel: flag the chunk for the SUB variant
+            // wave 0 holds gamma_C of every channel: flag the chunk for the SUB variant when
+            // it falls beyond what the shifted operands below cover
             if (p.sub && wave == 0) {
                 bool wide = false;
 #pragma unroll
-                for (int e = 0; e < CPT; ++e) wide = wide || !(gC[e] >= -kSubGateRange);
+                for (int e = 0; e < CPT; ++e) wide = wide || !(gC[e] >= -2.f * kSubGateRange);
                 const bool any = __builtin_amdgcn_ballot_w64(wide) != 0;
                 if (lane == 0) p.sub[cur.g] = any ? 1 : 0;
             }
+        }
+
+        // Gate reference of the Gram operands.  A channel whose gate falls by more than
+        // 2^kSubGateRange within the chunk would take K-> = K e^-g out of range; its operands
+        // are formed with the gate referred to sh = round(g_C / 2) (a power of two) instead,
+        // K<-' = K e^(g - sh), K->' = K e^(sh - g), Q<-' = Q e^(g - sh), so every factor stays
+        // within 2^(|g_C| / 2) either way and a chunk may fall by up to 2^(2 kSubGateRange).
+        // Their products (the Gram and A_qk) are unchanged; K<- and Q<- (DP: B<- and Q<-)
+        // are multiplied back by 2^sh in LDS before the stages that need them (exact in bf16),
+        // so the block holds the same quantities either way.  Other channels: sh = 0.
+        float sh[CPT];
+        [[maybe_unused]] bool shifted = false;
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+            sh[e] = !SUB && !PAIR && gC[e] < -kSubGateRange ? rintf(0.5f * gC[e]) : 0.f;
+            shifted = shifted || sh[e] != 0.f;
         }
 
         // ---- scaled operands: Q<-, K<-, K-> to LDS; K^ and gamma_C to the block ---------
@@ -584,6 +603,11 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
             float kh[CPT][8], kb[CPT][8], gam[CPT];
 #pragma unroll
             for (int e = 0; e < CPT; ++e) gam[e] = GATE == kGateNone && !CLIP ? 1.f : exp2_fast(gC[e]);
+            // e^(g_C - g) = e^(sh - g) e^(g_C - sh): one exp2 per channel, and neither factor
+            // leaves the range (sh = 0: gamma_C itself)
+            float gsh[CPT];
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) gsh[e] = sh[e] != 0.f ? exp2_fast(gC[e] - sh[e]) : gam[e];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int r = 8 * rg + i;
@@ -615,9 +639,10 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
                         sGf[r * L::GS + c0 + e] = g[i][e];
                         if ((r & 15) == 0) sGref[(r >> 4) * DK + c0 + e] = g[i][e];
                     } else {
-                        const float eg = GATE == kGateNone && !CLIP ? 1.f : exp2_fast(g[i][e]);
-                        const float eig = GATE == kGateNone && !CLIP ? 1.f : exp2_fast(-g[i][e]);
-                        const float egc = eig * gam[e];  // e^(g_C - g)
+                        const float gs = g[i][e] - sh[e];  // (sh = 0: g itself)
+                        const float eg = GATE == kGateNone && !CLIP ? 1.f : exp2_fast(gs);
+                        const float eig = GATE == kGateNone && !CLIP ? 1.f : exp2_fast(-gs);
+                        const float egc = eig * gsh[e];  // e^(g_C - g)
                         a[e] = (DP ? bv[e] : kv[e]) * eg;
                         b[e] = kv[e] * eig;
                         cq[e] = qv[e] * eg;
@@ -999,6 +1024,26 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
             }
         }
         lds_barrier();
+        if constexpr (!SUB && !PAIR && (GATE != kGateNone || CLIP)) {
+            // shifted channels: K<-' 2^sh = K<-, Q<-' 2^sh = Q<- (DP: B<-, Q<-), now that the
+            // Gram has read them; later stages read them after further barriers
+            if (shifted) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 8 * rg + i;
+#pragma unroll
+                    for (int e = 0; e < CPT; e += 2) {
+                        const int n0 = (int)sh[e], n1 = (int)sh[e + 1];
+                        uint32_t *pq = (uint32_t *)(sQl + r * KS + c0 + e);
+                        uint32_t *pk = (uint32_t *)(sKl + r * KS + c0 + e);
+                        *pq = pack_bf16x2(__builtin_amdgcn_ldexpf(bf16_lo(*pq), n0),
+                                          __builtin_amdgcn_ldexpf(bf16_hi(*pq), n1));
+                        *pk = pack_bf16x2(__builtin_amdgcn_ldexpf(bf16_lo(*pk), n0),
+                                          __builtin_amdgcn_ldexpf(bf16_hi(*pk), n1));
+                    }
+                }
+            }
+        }
         if constexpr (SUB) {
             // Q<- (DP: and B<-) from the raw rows, now that the Gram has read them; later
             // stages read them after further barriers

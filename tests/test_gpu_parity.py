@@ -534,11 +534,33 @@ def test_segmented_many_runs_long_sequence():
 @pytest.mark.parametrize("kind,dk,dv", [("kda", 128, 128), ("dplr", 128, 128), ("kda", 64, 64),
                                         ("dplr", 64, 96), ("gdn", 128, 128)])
 def test_strong_gate_diagonal_tiles_mfma_and_elementwise(kind, dk, dv):
-    # head 0: every chunk flagged but each 16-row tile falls by less than 2^64 (its diagonal
-    # tiles on MFMA); head 1: four times steeper, its diagonal tiles formed element-wise
-    P = inputs.make_problem(kind, B=1, H=2, T=330, dk=dk, dv=dv, la_range=(-2.0, -1.0),
+    # head 0: every chunk falls by more than 2^192 (past the shifted operands' range: the
+    # log-domain prep) but each 16-row tile by less than 2^64 (its diagonal tiles on MFMA);
+    # head 1: four times steeper, its diagonal tiles formed element-wise
+    P = inputs.make_problem(kind, B=1, H=2, T=330, dk=dk, dv=dv, la_range=(-2.7, -2.2),
                             s0_scale=0.3)
     P.log_alpha[:, :, 1] *= 4.0
+    O, Sf = gpu_run(P)
+    assert np.isfinite(O).all() and np.isfinite(Sf).all()
+    _check(P, O, Sf)
+
+
+# Every chunk falls by 2^120 .. 2^176 in every channel: past the plain scaled operands'
+# range, within that of the operands referred to the middle of the chunk (no log-domain pass).
+SHIFTED = {
+    "kda": dict(kind="kda", B=2, H=2, T=333, la_range=(-1.9, -1.3), s0_scale=0.3),
+    "kda_d64": dict(kind="kda", B=1, H=3, T=200, dk=64, dv=64, la_range=(-1.9, -1.3)),
+    "gdn": dict(kind="gdn", B=2, H=2, T=300, la_range=(-1.9, -1.3), s0_scale=0.3),
+    "dplr": dict(kind="dplr", B=1, H=2, T=300, la_range=(-1.9, -1.3), s0_scale=0.3),
+    "dplr_d64": dict(kind="dplr", B=1, H=2, T=260, dk=64, dv=96, la_range=(-1.9, -1.3)),
+    "gdn2_clip": dict(kind="gdn2_clip", B=1, H=2, T=300, la_range=(-1.9, -1.3)),
+}
+
+
+@pytest.mark.parametrize("case", list(SHIFTED))
+def test_gate_within_the_shifted_range(case):
+    spec = dict(SHIFTED[case])
+    P = inputs.make_problem(spec.pop("kind"), **spec)
     O, Sf = gpu_run(P)
     assert np.isfinite(O).all() and np.isfinite(Sf).all()
     _check(P, O, Sf)
