@@ -561,12 +561,12 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
             }
         }
         if constexpr (PAIR) {
-            // no log-domain variant on this path: a half whose gate falls beyond the
-            // scaled operands' range makes the call's result invalid (error bit 2)
+            // no log-domain variant on this path: a half whose gate falls beyond the shifted
+            // operands' range (below) makes the call's result invalid (error bit 2)
             if (wave == 0) {
                 bool wide = false;
 #pragma unroll
-                for (int e = 0; e < CPT; ++e) wide = wide || !(gC[e] >= -kSubGateRange);
+                for (int e = 0; e < CPT; ++e) wide = wide || !(gC[e] >= -2.f * kSubGateRange);
                 if (__builtin_amdgcn_ballot_w64(wide) != 0 && lane == 0) atomicOr(p.err, 2);
             }
         } else if constexpr (!SUB) {
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
         [[maybe_unused]] bool shifted = false;
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
-            sh[e] = !SUB && !PAIR && gC[e] < -kSubGateRange ? rintf(0.5f * gC[e]) : 0.f;
+            sh[e] = !SUB && gC[e] < -kSubGateRange ? rintf(0.5f * gC[e]) : 0.f;
             shifted = shifted || sh[e] != 0.f;
         }
 
@@ -1024,7 +1024,7 @@ __global__ __launch_bounds__(kThreads, DP || SUB ? 1 : 2) void kda_prep_kernel(S
             }
         }
         lds_barrier();
-        if constexpr (!SUB && !PAIR && (GATE != kGateNone || CLIP)) {
+        if constexpr (!SUB && (GATE != kGateNone || CLIP)) {
             // shifted channels: K<-' 2^sh = K<-, Q<-' 2^sh = Q<- (DP: B<-, Q<-), now that the
             // Gram has read them; later stages read them after further barriers
             if (shifted) {

@@ -115,7 +115,7 @@ size_t gdr_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int C, int n
  *               without a, b at dk = 128 (each 128-token chunk's factors built from
  *               those of its two 64-token halves, "Gated Linear Attention" notes,
  *               section 5.3, secondary chunking; no log-domain rescue: a half whose
- *               gate falls by more than 2^96 in a channel raises error bit 2).
+ *               gate falls by more than 2^192 in a channel raises error bit 2).
  *   dk, dv      head sizes; dk in {64, 128}; dv a multiple of 32 up to 256.
  *   Sizes: B, H, T >= 1, B * T * H * max(dk, dv) < 2^40 (elements of the largest
  *   tensor) and N * H < 2^27 ((sequence, head) pairs); otherwise GDR_ERR_SHAPE.
@@ -231,7 +231,7 @@ int gdr_chunk_bwd(const void *q, const void *k, const void *v, const void *a, co
  * further than the kernels that ran can represent, so that call's results are
  * not valid -- gdr_chunk_bwd when a channel falls by more than 2^192 (e^133)
  * within a chunk, the fp32 kernels (fp32 inputs, or C < 64) by more than e^80, and the
- * bf16 forward with C = 128 when a 64-token half falls by more than 2^96; the bf16
+ * bf16 forward with C = 128 when a 64-token half falls by more than 2^192; the bf16
  * forward with C = 64 handles such chunks in the log domain and never sets it) and
  * clears them.  Returns GDR_ERR_NULL or GDR_ERR_HIP on failure. */
 int gdr_workspace_error(void *workspace, void *stream);

@@ -644,9 +644,20 @@ def test_c128_matches_c64_and_is_deterministic():
     assert rel_err(O1, O64) <= TOL[P.dtype] and rel_err(S1, S64) <= TOL[P.dtype]
 
 
+def test_c128_gate_within_the_shifted_range():
+    # every 64-token half falls by 2^120 .. 2^176: the shifted Gram operands, no error bit
+    P = inputs.make_problem("kda", B=2, H=2, T=333, la_range=(-1.9, -1.3), chunk=128, s0_scale=0.3)
+    ws = torch.zeros(gdr.workspace_bytes(P.B, P.H, P.T, P.dk, P.dv, C=128), dtype=torch.uint8,
+                     device="cuda")
+    O, Sf = gpu_run(P, workspace=ws)
+    assert gdr.check_workspace_error(ws) == 0
+    assert np.isfinite(O).all() and np.isfinite(Sf).all()
+    _check(P, O, Sf)
+
+
 def test_c128_flags_gates_beyond_its_range():
-    # no log-domain variant at C = 128: a half whose gate falls past the scaled operands'
-    # range raises bit 2 of the error word (the C = 64 path redoes such chunks instead)
+    # no log-domain variant at C = 128: a half whose gate falls past the shifted operands'
+    # range (2^192) raises bit 2 of the error word (the C = 64 path redoes such chunks instead)
     P = inputs.make_problem("kda", B=1, H=2, T=260, la_range=(-4.0, -3.0), chunk=128)
     ws = torch.zeros(gdr.workspace_bytes(P.B, P.H, P.T, P.dk, P.dv, C=128), dtype=torch.uint8,
                      device="cuda")
