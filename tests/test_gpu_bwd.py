@@ -410,3 +410,45 @@ def test_bwd_bitwise_deterministic(kind):
     g2 = _gpu_bwd(P, dO, dSf)
     for key in g1:
         np.testing.assert_array_equal(g1[key], g2[key], err_msg=key)
+
+
+@pytest.mark.parametrize("kind", ["kda", "dplr"])
+def test_bwd_graph_capture_replays(kind):
+    # the backward inside a captured HIP graph (its gradient buffers from the capture's
+    # memory pool), replayed on new inputs copied into the captured tensors: each replay
+    # gives the bits of an eager call on the same inputs
+    problems = [inputs.make_problem(kind, seed=50 + i, B=1, H=2, T=300, s0_scale=0.3) for i in range(3)]
+    cots = [inputs.make_cotangents(P, 60 + i) for i, P in enumerate(problems)]
+    P0 = problems[0]
+    names = ("q", "k", "v", "beta", "log_alpha", "a", "b", "S0")
+    dev = {n: None if getattr(P0, n) is None else getattr(P0, n).to("cuda").clone() for n in names}
+    dO, dSf = (t.to("cuda").clone() for t in cots[0])
+    ws = torch.zeros(gdr.bwd_workspace_bytes(P0.B, P0.H, P0.T, P0.dk, P0.dv, has_ab=P0.a is not None),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        return gdr.chunk_bwd(dev["q"], dev["k"], dev["v"], dev["beta"], dO, log_alpha=dev["log_alpha"],
+                             a=dev["a"], b=dev["b"], S0=dev["S0"], dS_final=dSf, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g = call()
+    for P, (o, s) in list(zip(problems, cots))[1:] + [(problems[0], cots[0])]:
+        for n in names:
+            if dev[n] is not None:
+                dev[n].copy_(getattr(P, n).to("cuda"))
+        dO.copy_(o.to("cuda"))
+        dSf.copy_(s.to("cuda"))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = _gpu_bwd(P, o, s)
+        for key in ref:
+            np.testing.assert_array_equal(g[key].to(torch.float64).cpu().numpy(), ref[key], err_msg=key)
+    got = {key: val.to(torch.float64).cpu().numpy() for key, val in g.items()}
+    _check(P0, got, _oracle_bwd(P0, cots[0][0], cots[0][1]))

@@ -678,3 +678,51 @@ def test_c128_full_size_all_chains(kind):
     O, Sf = gpu_run(P, out=out)
     assert np.isfinite(O).all() and np.isfinite(Sf).all()
     _check(P, O, Sf)
+
+
+# ---------------------------------------------------------------------------
+# The forward inside a captured HIP graph: no allocation, no memset and no host
+# synchronisation in the call, so one capture serves any number of replays on new
+# inputs copied into the captured tensors.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kind", ["kda", "gdn", "dplr", "kda_varlen"])
+def test_graph_capture_replays(kind):
+    spec = dict(B=1, H=2, T=300) if kind != "kda_varlen" else dict(n_seq=3, total=420, min_len=1, H=2)
+    problems = [inputs.make_problem(kind, seed=40 + i, s0_scale=0.3, **spec) for i in range(4)]
+    P0 = problems[0]
+    names = ("q", "k", "v", "beta", "log_alpha", "a", "b", "S0", "cu_seqlens")
+    dev = {n: None if getattr(P0, n) is None else getattr(P0, n).to("cuda").clone() for n in names}
+    if kind == "kda_varlen":  # one packing for every replay: the cu_seqlens of the first
+        for P in problems[1:]:
+            P.cu_seqlens = P0.cu_seqlens
+    N = P0.S0.shape[0]
+    out = torch.empty((P0.B, P0.T, P0.H, P0.dv), dtype=P0.dtype, device="cuda")
+    fs = torch.empty((N, P0.H, P0.dv, P0.dk), dtype=torch.float32, device="cuda")
+    nbytes = gdr.workspace_bytes(P0.B, P0.H, P0.T, P0.dk, P0.dv, n_seq=N if kind == "kda_varlen" else 0,
+                                 gate=P0.gate, has_ab=P0.a is not None)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+
+    def call():
+        gdr.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["beta"], log_alpha=dev["log_alpha"],
+                      a=dev["a"], b=dev["b"], S0=dev["S0"], cu_seqlens=dev["cu_seqlens"],
+                      out=out, final_state=fs, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for P in problems[1:] + problems[:1]:
+        for n in names:
+            if dev[n] is not None:
+                dev[n].copy_(getattr(P, n).to("cuda"))
+        graph.replay()
+        torch.cuda.synchronize()
+        O_ref, S_ref = gpu_run(P)  # the same call, eager, on fresh buffers
+        np.testing.assert_array_equal(out.double().cpu().numpy(), O_ref)
+        np.testing.assert_array_equal(fs.double().cpu().numpy(), S_ref)
+    _check(problems[0], out.double().cpu().numpy(), fs.double().cpu().numpy())
