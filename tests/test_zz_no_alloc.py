@@ -78,3 +78,37 @@ def test_noalloc_rejects_what_the_scratch_cannot_hold():
     with pytest.raises(gdr.GdrError) as e:
         gdr.chunk_fwd(q, q, v, beta, log_alpha=la, no_alloc=True)
     assert e.value.code == -4
+
+
+def test_noalloc_graph_capture_replays():
+    # captured in a HIP graph and replayed on new inputs copied into the captured tensors:
+    # every replay gives the bits of the workspace entry point on the same inputs
+    problems = [inputs.make_problem("kda", seed=70 + i, B=1, H=2, T=300, s0_scale=0.3) for i in range(3)]
+    P0 = problems[0]
+    names = ("q", "k", "v", "beta", "log_alpha", "S0")
+    dev = {n: getattr(P0, n).to("cuda").clone() for n in names}
+    out = torch.empty_like(dev["v"])
+    fs = torch.empty_like(dev["S0"])
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def call():
+        gdr.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["beta"], log_alpha=dev["log_alpha"],
+                      S0=dev["S0"], no_alloc=True, flags=flags, out=out, final_state=fs)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for P in problems[1:] + problems[:1]:
+        for n in names:
+            dev[n].copy_(getattr(P, n).to("cuda"))
+        graph.replay()
+        torch.cuda.synchronize()
+        O1, S1 = _run(P, no_alloc=False)
+        assert torch.equal(out, O1) and torch.equal(fs, S1)
+    assert int(flags.item()) == 0
