@@ -685,10 +685,12 @@ def test_c128_full_size_all_chains(kind):
 # synchronisation in the call, so one capture serves any number of replays on new
 # inputs copied into the captured tensors.
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("kind", ["kda", "gdn", "dplr", "kda_varlen"])
+@pytest.mark.parametrize("kind", ["kda", "gdn", "dplr", "dplr_segmented", "kda_varlen"])
 def test_graph_capture_replays(kind):
-    spec = dict(B=1, H=2, T=300) if kind != "kda_varlen" else dict(n_seq=3, total=420, min_len=1, H=2)
-    problems = [inputs.make_problem(kind, seed=40 + i, s0_scale=0.3, **spec) for i in range(4)]
+    spec = {"kda_varlen": dict(n_seq=3, total=420, min_len=1, H=2),
+            "dplr_segmented": dict(B=1, H=4, T=2100)}.get(kind, dict(B=1, H=2, T=300))  # (4 chains: runs)
+    base = "dplr" if kind == "dplr_segmented" else kind
+    problems = [inputs.make_problem(base, seed=40 + i, s0_scale=0.3, **spec) for i in range(4)]
     P0 = problems[0]
     names = ("q", "k", "v", "beta", "log_alpha", "a", "b", "S0", "cu_seqlens")
     dev = {n: None if getattr(P0, n) is None else getattr(P0, n).to("cuda").clone() for n in names}
